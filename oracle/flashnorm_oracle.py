@@ -1,0 +1,173 @@
+"""Plain float64 CPU oracle for fused RMSNorm + projection (FlashNorm).
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import or call this module.  The product path (the HIP
+library and its Python binding) never does, and shares no code with it.
+
+What it computes, and where the pages state it
+----------------------------------------------
+Sources (web pages; cited by title and section):
+
+* [FlashNorm digest] "RMS norm는 연산량 1할인데 왜 33번 호출로 속도를 갉아먹나"
+  (news.juniverse.app feature, 2026-09-20), summary bullets:
+  - proposal 1, weightless normalisation: the norm's gain is folded offline
+    into the projection weights, leaving a single matrix;
+  - proposal 2, deferred normalisation: the per-row scalar division is moved
+    after the matrix product so matrix and vector units can run together;
+  - proposal 3, double-norm removal: scale invariance makes the second of two
+    back-to-back RMS norms redundant.
+* [FlashInfer #5521] "MiniMax-H3 Fused FC1 + SwiGLU" analysis, sections
+  "Segmented Chain" (norm -> GEMM -> silu_and_mul as separate steps) and
+  "Design" item 2 (SwiGLU applied to the GEMM accumulators in registers).
+* [FlashInfer #4040] "Fused SwiGLU 및 NVFP4 양자화", section "하드웨어 최적화"
+  (fp32 -> bf16 conversion rounds to nearest, ties to even).
+* [FlashInfer #5668] "Kimi-K3 TP12 LatentMoE Tail", section on K23_LADDER
+  (keep fp32 through the whole sum and round to bf16 once; judge accuracy
+  against a float64 reference).
+
+The pages never write the RMSNorm formula.  Every proposal above presupposes
+standard RMSNorm with a gain, so the oracle takes the plain reading
+
+    r[m]      = sqrt( (1/K) * sum_k x[m,k]^2 + eps )
+    xhat[m,k] = x[m,k] / r[m] * g[k]
+    y[m,n]    = sum_k xhat[m,k] * W[k,n]
+
+with eps inside the square root and the mean over the hidden size K.  The
+SwiGLU variant computes a = xhat @ W_gate, b = xhat @ W_up and
+out = a * sigmoid(a) * b (the gate is the operand inside the SiLU).  Folding
+and deferral are exact in real arithmetic, so the oracle computes the
+unfolded definition directly; the folded/deferred form exists only to pin
+that equality.
+
+All arithmetic is float64.  Inputs are the stored (bf16 or fp32) values,
+up-cast exactly.  eps is taken as float64(float32(eps)), the exact value a
+GPU kernel receives as a float argument.
+
+Pins (see tests/test_oracle.py): hand-derived worked cases, brute force on
+tiny inputs, torch's float64 rms_norm followed by a float64 matmul, the fold
+identity, scale invariance, norm-after-weightless-norm, row permutation and
+column concatenation, and library round-to-nearest-even conversions.  Every
+function here is pinned; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def eps_as_received(eps: float) -> float:
+    """eps as a float32 kernel argument carries it, widened to float64."""
+    return float(np.float32(eps))
+
+
+def rms(x, eps: float) -> np.ndarray:
+    """Per-row root mean square with eps inside the root (the plain RMSNorm
+    reading of [FlashNorm digest] proposals 1-3): r[m] = sqrt(mean_k x^2 + eps)."""
+    x = _f64(x)
+    K = x.shape[-1]
+    mean_sq = np.sum(x * x, axis=-1) / K
+    return np.sqrt(mean_sq + eps_as_received(eps))
+
+
+def rmsnorm(x, g, eps: float) -> np.ndarray:
+    """xhat = x / r * g, row by row ([FlashNorm digest]: the norm the proposals
+    act on; g is the gain that proposal 1 folds away)."""
+    x = _f64(x)
+    g = _f64(g)
+    return x / rms(x, eps)[..., None] * g
+
+
+def norm_proj(x, g, W, eps: float) -> np.ndarray:
+    """Unfolded definition y = RMSNorm_g(x) @ W: the norm followed by the
+    projection that [FlashNorm digest] fuses."""
+    return rmsnorm(x, g, eps) @ _f64(W)
+
+
+def silu(a) -> np.ndarray:
+    """SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a)) ([FlashInfer #5521]
+    silu_and_mul step of the segmented chain)."""
+    a = _f64(a)
+    return a / (1.0 + np.exp(-a))
+
+
+def norm_proj_swiglu(x, g, W_gate, W_up, eps: float) -> np.ndarray:
+    """SwiGLU after the normalised gate and up projections:
+    out = silu(xhat @ W_gate) * (xhat @ W_up) ([FlashInfer #5521], chain
+    steps "GEMM" then "silu_and_mul"; the fused kernel's register epilogue
+    computes the same function).  Both products see the normalised xhat, so
+    the 1/r factor reaches a before the nonlinearity."""
+    xhat = rmsnorm(x, g, eps)
+    a = xhat @ _f64(W_gate)
+    b = xhat @ _f64(W_up)
+    return silu(a) * b
+
+
+def fold_exact(g, W) -> np.ndarray:
+    """Weightless normalisation, before storage rounding: W'[k,n] = g[k]*W[k,n]
+    ([FlashNorm digest] proposal 1).  For bf16 or fp32 operands the float64
+    product is exact."""
+    return _f64(g)[:, None] * _f64(W)
+
+
+def round_to_bf16(a) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even
+    ([FlashInfer #4040]: the fp32 -> bf16 conversion is round-to-nearest-even).
+
+    bf16 keeps 8 significant bits and fp32's exponent range: the quantum of a
+    value m*2^e (0.5 <= |m| < 1) is 2^(e-8), held at 2^-133 below the
+    smallest normal 2^-126.  Results of magnitude 2^128 or more overflow to
+    infinity.  NaN stays NaN."""
+    a = _f64(a)
+    with np.errstate(invalid="ignore", over="ignore"):
+        _, e = np.frexp(a)
+        e = np.maximum(e, -125)
+        q = np.ldexp(np.rint(np.ldexp(a, 8 - e)), e - 8)   # np.rint: half to even
+        q = np.where(np.abs(q) >= 2.0 ** 128, np.copysign(np.inf, a), q)
+    return q
+
+
+def round_to_f32(a) -> np.ndarray:
+    """Round float64 values to the nearest float32 (numpy's cast is IEEE
+    round-to-nearest-even)."""
+    return _f64(a).astype(np.float32).astype(np.float64)
+
+
+def round_to(a, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_to_bf16(a)
+    if dtype == "f32":
+        return round_to_f32(a)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def fold_weights(g, W, dtype: str) -> np.ndarray:
+    """Stored folded weights: W' = round_dtype(g[k] * W[k,n]), one rounding of
+    the exact product ([FlashNorm digest] proposal 1; single rounding as in
+    [FlashInfer #5668]).  Returned as float64 holding the stored values."""
+    return round_to(fold_exact(g, W), dtype)
+
+
+def norm_proj_folded(x, W_folded, eps: float) -> np.ndarray:
+    """Deferred normalisation on folded weights: y = (x @ W') / r, the scalar
+    division moved after the product ([FlashNorm digest] proposal 2).  Used
+    only to pin that this equals the unfolded definition."""
+    x = _f64(x)
+    return (x @ _f64(W_folded)) / rms(x, eps)[:, None]
+
+
+def norm_proj_swiglu_folded(x, Wg_folded, Wu_folded, eps: float) -> np.ndarray:
+    """Deferred form of the SwiGLU variant: a = (x @ W'_g)/r, b = (x @ W'_u)/r,
+    out = silu(a) * b.  Used only to pin equality with the unfolded form."""
+    x = _f64(x)
+    r = rms(x, eps)[:, None]
+    a = (x @ _f64(Wg_folded)) / r
+    b = (x @ _f64(Wu_folded)) / r
+    return silu(a) * b
+
+
+__all__ = ["rms", "rmsnorm", "norm_proj", "silu", "norm_proj_swiglu", "fold_exact",
+           "round_to_bf16", "round_to_f32", "round_to", "fold_weights", "norm_proj_folded",
+           "norm_proj_swiglu_folded", "eps_as_received"]

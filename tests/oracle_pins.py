@@ -1,0 +1,266 @@
+"""Pins for the float64 oracle: checks that tie it to something other than
+itself (hand-derived cases, brute force, a library routine, algebraic
+invariants of the method).
+
+Each check takes the oracle module as an argument so the same checks can be
+run against deliberately broken copies of the oracle (see
+test_oracle.py::test_pins_catch_planted_mistakes).  A check raises
+AssertionError (or any exception) when the oracle disagrees.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def load_golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _case_W(case):
+    W = case["W"]
+    if W == "diag_then_2diag":
+        K = len(case["g"])
+        W = np.zeros((K, 2 * K))
+        for k in range(K):
+            W[k, k] = 1.0
+            W[k, k + K] = 2.0
+    return np.asarray(W, dtype=np.float64)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    err = np.max(np.abs(a - b) / (np.abs(b) + 1.0)) if a.size else 0.0
+    assert err <= tol, f"{what}: max rel err {err:.3e} > {tol:.1e}\n{a}\nvs\n{b}"
+
+
+# --------------------------------------------------------------------------
+# hand-derived worked cases (tests/golden/hand_cases.json)
+# --------------------------------------------------------------------------
+def check_hand_cases(o):
+    from scipy.special import expit
+    for case in load_golden()["cases"]:
+        x = np.asarray(case["x"], dtype=np.float64)
+        g = np.asarray(case["g"], dtype=np.float64)
+        W = _case_W(case)
+        eps = case["eps"]
+        name = case["name"]
+        _close(o.rms(x, eps), case["r"], 1e-15, f"{name}: r")
+        _close(o.norm_proj(x, g, W, eps), case["y"], 1e-14, f"{name}: y")
+        if "W_folded" in case:
+            _close(o.fold_exact(g, W), case["W_folded"], 0.0, f"{name}: W'")
+            _close(o.norm_proj_folded(x, case["W_folded"], eps), case["y"], 1e-14, f"{name}: folded y")
+        if "W_up" in case:
+            a = np.asarray(case["swiglu_a"], dtype=np.float64)
+            b = np.asarray(case["swiglu_b"], dtype=np.float64)
+            expected = a * expit(a) * b       # SiLU via scipy's logistic function
+            _close(o.norm_proj_swiglu(x, g, W, case["W_up"], eps), expected, 1e-14, f"{name}: swiglu")
+
+
+def check_silu_closed_forms(o):
+    from scipy.special import expit
+    t = np.array([-30.0, -2.5, -1.0, 0.0, 0.5, 1.5, 2.0, 30.0])
+    _close(o.silu(t), t * expit(t), 1e-15, "silu vs t*expit(t)")
+    # sigmoid(ln 3) = 3/4 exactly in real arithmetic
+    _close(o.silu(np.log(3.0)), 0.75 * np.log(3.0), 1e-15, "silu(ln 3)")
+    assert o.silu(np.array([0.0]))[0] == 0.0
+
+
+# --------------------------------------------------------------------------
+# brute force on tiny inputs: scalar loops over Python floats
+# --------------------------------------------------------------------------
+def _brute_norm_proj(x, g, W, eps, W_up=None):
+    M, K = len(x), len(x[0])
+    N = len(W[0])
+    eps = float(np.float32(eps))
+    out = []
+    for m in range(M):
+        s = 0.0
+        for k in range(K):
+            s += x[m][k] * x[m][k]
+        r = math.sqrt(s / K + eps)
+        xh = [x[m][k] / r * g[k] for k in range(K)]
+        row = []
+        for n in range(N):
+            a = 0.0
+            for k in range(K):
+                a += xh[k] * W[k][n]
+            if W_up is None:
+                row.append(a)
+            else:
+                b = 0.0
+                for k in range(K):
+                    b += xh[k] * W_up[k][n]
+                row.append(a / (1.0 + math.exp(-a)) * b)
+        out.append(row)
+    return out
+
+
+def check_brute_force(o, seed=11):
+    rng = np.random.default_rng(seed)
+    for (M, K, N, eps) in [(1, 1, 1, 0.0), (3, 5, 4, 1e-6), (2, 7, 3, 0.5), (4, 6, 6, 0.0)]:
+        x = rng.standard_normal((M, K))
+        g = rng.uniform(0.5, 1.5, K)
+        W = rng.standard_normal((K, N))
+        Wu = rng.standard_normal((K, N))
+        ref = _brute_norm_proj(x.tolist(), g.tolist(), W.tolist(), eps)
+        _close(o.norm_proj(x, g, W, eps), ref, 1e-13, f"brute norm_proj {M}x{K}x{N}")
+        ref = _brute_norm_proj(x.tolist(), g.tolist(), W.tolist(), eps, Wu.tolist())
+        _close(o.norm_proj_swiglu(x, g, W, Wu, eps), ref, 1e-13, f"brute swiglu {M}x{K}x{N}")
+
+
+# --------------------------------------------------------------------------
+# library special case: torch's float64 rms_norm, then a float64 matmul
+# --------------------------------------------------------------------------
+def check_torch_rms_norm(o, seed=12):
+    import torch
+    rng = np.random.default_rng(seed)
+    for (M, K, N, eps) in [(5, 64, 24, 1e-6), (3, 40, 9, 0.25), (2, 16, 16, 0.0)]:
+        x = rng.standard_normal((M, K))
+        g = rng.uniform(0.5, 1.5, K)
+        W = rng.standard_normal((K, N))
+        eps32 = float(np.float32(eps))
+        xt = torch.from_numpy(x)
+        ref = torch.nn.functional.rms_norm(xt, (K,), torch.from_numpy(g), eps32) @ torch.from_numpy(W)
+        _close(o.norm_proj(x, g, W, eps), ref.numpy(), 1e-13, f"torch rms_norm@W {M}x{K}x{N}")
+        # g = 1: plain rms_norm without weight
+        ref1 = torch.nn.functional.rms_norm(xt, (K,), None, eps32).numpy() @ W
+        _close(o.norm_proj(x, np.ones(K), W, eps), ref1, 1e-13, "g=1 rms_norm@W")
+    # rows pre-scaled to RMS 1 with eps = 0: the norm is the identity, y = x @ W
+    x = rng.standard_normal((4, 32))
+    x = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True))
+    W = rng.standard_normal((32, 8))
+    _close(o.norm_proj(x, np.ones(32), W, 0.0), x @ W, 1e-13, "unit-RMS rows give x@W")
+
+
+# --------------------------------------------------------------------------
+# algebraic invariants of the method
+# --------------------------------------------------------------------------
+def check_fold_identity(o, seed=13):
+    """Proposal 1 + 2: folded + deferred equals the unfolded definition."""
+    rng = np.random.default_rng(seed)
+    M, K, N = 6, 48, 20
+    x = rng.standard_normal((M, K))
+    g = rng.uniform(0.5, 1.5, K)
+    W = rng.standard_normal((K, N))
+    Wu = rng.standard_normal((K, N))
+    for eps in (0.0, 1e-6, 0.3):
+        _close(o.norm_proj_folded(x, o.fold_exact(g, W), eps), o.norm_proj(x, g, W, eps), 1e-13, "I1 fold")
+        _close(o.norm_proj_swiglu_folded(x, o.fold_exact(g, W), o.fold_exact(g, Wu), eps),
+               o.norm_proj_swiglu(x, g, W, Wu, eps), 1e-13, "I1 fold swiglu")
+
+
+def check_scale_invariance(o, seed=14):
+    """RMSNorm(c x) = RMSNorm(x) for c > 0 at eps = 0 (proposal 3's premise)."""
+    rng = np.random.default_rng(seed)
+    M, K, N = 5, 40, 12
+    x = rng.standard_normal((M, K))
+    g = rng.uniform(0.5, 1.5, K)
+    W = rng.standard_normal((K, N))
+    base = o.norm_proj(x, g, W, 0.0)
+    for p in (-3, 5):
+        assert np.array_equal(o.norm_proj(x * 2.0 ** p, g, W, 0.0), base), f"I2 bit-exact for 2^{p}"
+    for c in (0.3, 7.1):
+        _close(o.norm_proj(c * x, g, W, 0.0), base, 1e-14, f"I2 c={c}")
+    # with eps > 0 the difference is bounded by about eps / mean(x^2)
+    eps = 1e-3
+    d = np.max(np.abs(o.norm_proj(10.0 * x, g, W, eps) - o.norm_proj(x, g, W, eps)))
+    scale = np.max(np.abs(base))
+    assert 0 < d <= 2 * eps / np.min(np.mean(x * x, axis=1)) * scale, "I2 eps>0 bound"
+    # and scaling x down must change y when eps dominates (eps really enters)
+    small = o.norm_proj(1e-6 * x, g, W, 1.0)
+    assert np.max(np.abs(small)) < 1e-5 * scale
+
+
+def check_double_norm(o, seed=15):
+    """A gain-free norm followed by RMSNorm_g equals RMSNorm_g alone at eps=0
+    (proposal 3, double-norm removal)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((7, 33))
+    g = rng.uniform(0.5, 1.5, 33)
+    once = o.rmsnorm(x, g, 0.0)
+    twice = o.rmsnorm(o.rmsnorm(x, np.ones(33), 0.0), g, 0.0)
+    _close(twice, once, 1e-15, "I3 double norm")
+    _close(o.rms(o.rmsnorm(x, np.ones(33), 0.0), 0.0), np.ones(7), 1e-15, "I3 unit rms")
+
+
+def check_rows_and_columns(o, seed=16):
+    """Rows are independent (permutation, NaN isolation); columns are
+    independent and the map is linear in W (concatenation, scaling)."""
+    rng = np.random.default_rng(seed)
+    M, K, N = 8, 24, 10
+    x = rng.standard_normal((M, K))
+    g = rng.uniform(0.5, 1.5, K)
+    W1 = rng.standard_normal((K, N))
+    W2 = rng.standard_normal((K, 3))
+    y = o.norm_proj(x, g, W1, 1e-6)
+    perm = rng.permutation(M)
+    assert np.array_equal(o.norm_proj(x[perm], g, W1, 1e-6), y[perm]), "I6 permutation"
+    xn = x.copy()
+    xn[3, 5] = np.nan
+    yn = o.norm_proj(xn, g, W1, 1e-6)
+    assert np.all(np.isnan(yn[3])), "I6 NaN row"
+    assert np.array_equal(np.delete(yn, 3, 0), np.delete(y, 3, 0)), "I6 NaN isolated"
+    cat = o.norm_proj(x, g, np.concatenate([W1, W2], axis=1), 1e-6)
+    _close(cat, np.concatenate([y, o.norm_proj(x, g, W2, 1e-6)], axis=1), 1e-14, "I7 concat")
+    _close(o.norm_proj(x, g, 2.5 * W1, 1e-6), 2.5 * y, 1e-14, "I7 linear")
+
+
+# --------------------------------------------------------------------------
+# storage rounding
+# --------------------------------------------------------------------------
+def check_rounding(o, seed=17):
+    import torch
+    gold = load_golden()
+    for desc, v, want in gold["rne_bf16"]["pairs"]:
+        got = o.round_to_bf16(np.array([v]))[0]
+        assert got == want, f"bf16 RNE {desc}: {got!r} != {want!r}"
+    for desc, v, want in gold["rne_f32"]["pairs"]:
+        got = o.round_to_f32(np.array([v]))[0]
+        assert got == want, f"f32 RNE {desc}: {got!r} != {want!r}"
+    # library cross-check: torch's CPU float32 -> bfloat16 conversion (RNE)
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    ties = (rng.integers(0, 2 ** 16, size=5000).astype(np.uint32) << 16) | np.uint32(0x8000)
+    f = np.concatenate([f, ties.view(np.float32)])
+    f = f[np.isfinite(f)]
+    ref = torch.from_numpy(f).to(torch.bfloat16).to(torch.float64).numpy()
+    got = o.round_to_bf16(f.astype(np.float64))
+    assert np.array_equal(got, ref), "bf16 RNE vs torch"
+    assert np.isnan(o.round_to_bf16(np.array([np.nan]))[0])
+    assert o.round_to_bf16(np.array([3.5e38]))[0] == np.inf
+
+
+def check_fold_rounding(o, seed=18):
+    """W' = one rounding of the exact product: bf16 against torch's conversion
+    of the (exact) fp32 product, fp32 against numpy's IEEE fp32 multiply."""
+    import torch
+    rng = np.random.default_rng(seed)
+    K, N = 64, 48
+    g32 = torch.from_numpy(rng.uniform(0.5, 1.5, K).astype(np.float32)).to(torch.bfloat16).float()
+    W32 = torch.from_numpy(rng.standard_normal((K, N)).astype(np.float32)).to(torch.bfloat16).float()
+    ref = (g32[:, None] * W32).to(torch.bfloat16).double().numpy()
+    got = o.fold_weights(g32.double().numpy(), W32.double().numpy(), "bf16")
+    assert np.array_equal(got, ref), "fold bf16"
+    gf = rng.uniform(0.5, 1.5, K).astype(np.float32)
+    Wf = rng.standard_normal((K, N)).astype(np.float32)
+    ref = (gf[:, None] * Wf).astype(np.float64)
+    got = o.fold_weights(gf.astype(np.float64), Wf.astype(np.float64), "f32")
+    assert np.array_equal(got, ref), "fold f32"
+    ones = np.ones(K)
+    assert np.array_equal(o.fold_weights(ones, W32.double().numpy(), "bf16"), W32.double().numpy()), "g=1 fold"
+
+
+ALL_CHECKS = [check_hand_cases, check_silu_closed_forms, check_brute_force, check_torch_rms_norm,
+              check_fold_identity, check_scale_invariance, check_double_norm,
+              check_rows_and_columns, check_rounding, check_fold_rounding]

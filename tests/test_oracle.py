@@ -1,0 +1,71 @@
+"""The float64 oracle against its pins (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle.flashnorm_oracle as O
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("check", P.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pin(check):
+    check(O)
+
+
+def _K(x):
+    return np.asarray(x).shape[-1]
+
+
+# Plausible mistakes, planted in the oracle module; every one must be caught
+# by at least one pin.
+MUTANTS = {
+    "eps outside the root": ("rms", lambda x, eps: np.sqrt(np.sum(np.asarray(x, float) ** 2, -1) / _K(x)) + eps),
+    "mean over K-1": ("rms", lambda x, eps: np.sqrt(np.sum(np.asarray(x, float) ** 2, -1) / (_K(x) - 1) + eps)),
+    "eps dropped": ("rms", lambda x, eps: np.sqrt(np.sum(np.asarray(x, float) ** 2, -1) / _K(x))),
+    "root dropped": ("rms", lambda x, eps: np.sum(np.asarray(x, float) ** 2, -1) / _K(x) + eps),
+    "gain dropped": ("rmsnorm", lambda x, g, eps: np.asarray(x, float) / O.rms(x, eps)[..., None]),
+    "multiply by r": ("rmsnorm", lambda x, g, eps: np.asarray(x, float) * O.rms(x, eps)[..., None] * g),
+    "gain reversed": ("rmsnorm", lambda x, g, eps: np.asarray(x, float) / O.rms(x, eps)[..., None]
+                      * np.asarray(g, float)[::-1]),
+    "W transposed": ("norm_proj", lambda x, g, W, eps: O.rmsnorm(x, g, eps) @ np.asarray(W, float).T),
+    "sigmoid sign": ("silu", lambda a: np.asarray(a, float) / (1.0 + np.exp(np.asarray(a, float)))),
+    "gate/up swapped": ("norm_proj_swiglu", lambda x, g, Wg, Wu, eps:
+                        O.silu(O.rmsnorm(x, g, eps) @ np.asarray(Wu, float))
+                        * (O.rmsnorm(x, g, eps) @ np.asarray(Wg, float))),
+    "up not normalised": ("norm_proj_swiglu", lambda x, g, Wg, Wu, eps:
+                          O.silu(O.rmsnorm(x, g, eps) @ np.asarray(Wg, float))
+                          * ((np.asarray(x, float) * g) @ np.asarray(Wu, float))),
+    "scale after silu": ("norm_proj_swiglu", lambda x, g, Wg, Wu, eps:
+                         O.silu((np.asarray(x, float) * g) @ np.asarray(Wg, float))
+                         * (O.rmsnorm(x, g, eps) @ np.asarray(Wu, float))),
+    "bf16 truncation": ("round_to_bf16", lambda a: np.trunc(np.ldexp(np.asarray(a, float),
+                        8 - np.maximum(np.frexp(np.asarray(a, float))[1], -125)))
+                        * np.ldexp(1.0, np.maximum(np.frexp(np.asarray(a, float))[1], -125) - 8)),
+    "bf16 ties away": ("round_to_bf16", lambda a: np.sign(a) * np.floor(np.ldexp(np.abs(np.asarray(a, float)),
+                       8 - np.maximum(np.frexp(np.asarray(a, float))[1], -125)) + 0.5)
+                       * np.ldexp(1.0, np.maximum(np.frexp(np.asarray(a, float))[1], -125) - 8)),
+    "fold on the output axis": ("fold_exact", lambda g, W: np.asarray(W, float) * np.asarray(g, float)[None, :]),
+    "deferred multiply": ("norm_proj_folded", lambda x, Wf, eps: (np.asarray(x, float) @ np.asarray(Wf, float))
+                          * O.rms(x, eps)[:, None]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistakes(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    original = {k: getattr(O, k) for k in ("rms", "rmsnorm", "silu")}
+    monkeypatch.setattr(O, attr, fn)
+    # mutants that call O.rms / O.rmsnorm / O.silu must see the unmutated
+    # helpers unless the helper itself is the mutant
+    caught = []
+    for check in P.ALL_CHECKS:
+        try:
+            check(O)
+        except Exception as e:  # noqa: BLE001 - any failure counts as detection
+            caught.append(f"{check.__name__}: {type(e).__name__}")
+    assert caught, f"no pin caught planted mistake {name!r}"
+    assert original  # keep reference for readability
+
+
+def test_eps_is_the_float32_value():
+    assert O.eps_as_received(1e-6) == float(np.float32(1e-6))
+    assert O.eps_as_received(1e-6) != 1e-6
