@@ -1,0 +1,378 @@
+#!/usr/bin/env python3
+"""Benchmark of fused RMSNorm + projection (libflashnorm) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch: one fused call for the
+single-call workloads, or the 65 calls of the 32-layer decode step.  Inputs
+are seeded synthetics already resident in HBM when timing starts.  Decode
+workloads rotate distinct copies of the folded weights (>= 1 GiB in total)
+so the 256 MB Infinity Cache cannot serve repeated calls ("cold", the
+headline); the single-buffer ("hot") figure is reported beside it.
+
+Prints ONE JSON line.  Default workload: the QKV decode projection,
+x[16,4096] bf16 -> W'[4096,12288].
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused RMSNorm+proj: decode µs/call & HBM GB/s; prefill TFLOP/s; % roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+F32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
+ROTATE_BYTES = 1 << 30
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="qkv_decode",
+                   choices=["tiny", "qkv_decode", "ffn_decode", "prefill_qkv", "decode_step"])
+    p.add_argument("--no-chain", action="store_true", help="skip the unfused chain baselines")
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
+    p.add_argument("--hot", action="store_true", help="time a single weight buffer only (no rotation)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run 1 GiB device-to-device copies (counter calibration) and exit")
+    return p.parse_args(argv)
+
+
+# ----------------------------------------------------------------- timing --
+def time_region(torch, launch, steps, warmup):
+    """Average ms per step over `steps` back-to-back steps (events on the
+    current stream, which is the stream every launch uses)."""
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_each(torch, launch, count):
+    """Per-step durations (ms) with an event pair around every step."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(count)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        launch(i)
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in evs)
+
+
+def pct(sorted_vals, q):
+    i = min(len(sorted_vals) - 1, max(0, int(round(q * (len(sorted_vals) - 1)))))
+    return sorted_vals[i]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rmsnorm_projection_gemm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------ CPU oracle --
+def cpu_baseline(call, inp, budget_s, metric_unit):
+    """The float64 oracle as it stands, on the host cores, on a bounded sample
+    of the same workload; scaled to the metric's unit."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    rows = call.M
+    # keep one oracle call to a few seconds at most: sample rows for big M
+    if call.M * call.K * call.N * call.mats > 2e10:
+        rows = max(1, int(2e10 // (call.K * call.N * call.mats)))
+    x = inp.x[:rows]
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        if call.swiglu:
+            oracle.norm_proj_swiglu(x, inp.g, inp.W, inp.W_up, call.eps)
+        else:
+            oracle.norm_proj(x, inp.g, inp.W, call.eps)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_call = el / calls * (call.M / rows)       # seconds per full call
+    if metric_unit == "TFLOP/s":
+        value = call.flops() / per_call / 1e12
+    elif metric_unit == "GB/s":
+        value = call.algorithmic_bytes() / per_call / 1e9
+    else:
+        value = per_call * 1e6
+    sample = (f"{calls} oracle call(s) on x[{rows},{call.K}] (of M={call.M}) x W[{call.K},{call.N}]"
+              f"{' x2 (gate, up)' if call.swiglu else ''}, float64, {el:.1f} s; scaled by M/{rows}")
+    return {"value": round(value, 4), "unit": metric_unit, "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds_per_call": per_call}
+
+
+# ---------------------------------------------------------- single calls --
+def to_dev(torch, a, dtype):
+    t = torch.from_numpy(a)
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
+
+
+def run_single(args, torch, fn, workloads):
+    call = workloads.WORKLOADS[args.workload]
+    inp = workloads.make_inputs(call)
+    x = to_dev(torch, inp.x, call.dtype)
+    g = to_dev(torch, inp.g, call.dtype)
+    Wg = to_dev(torch, inp.W, call.dtype)
+    Wu = to_dev(torch, inp.W_up, call.dtype) if call.swiglu else None
+    Pg = fn.fold_weights(g, Wg)
+    Pu = fn.fold_weights(g, Wu) if call.swiglu else None
+    wbytes = Pg.data.numel() * call.mats
+    rot = 1 if args.hot else max(1, math.ceil(ROTATE_BYTES / wbytes))
+    pgs = [Pg] + [fn.PackedWeights(Pg.data.clone(), Pg.K, Pg.N, Pg.dtype) for _ in range(rot - 1)]
+    pus = ([Pu] + [fn.PackedWeights(Pu.data.clone(), Pu.K, Pu.N, Pu.dtype) for _ in range(rot - 1)]
+           if call.swiglu else None)
+    y = torch.empty((call.M, call.N), dtype=x.dtype, device="cuda")
+    eps = call.eps
+
+    if call.swiglu:
+        def fused(i):
+            fn.norm_proj_swiglu(x, pgs[i % rot], pus[i % rot], eps, out=y)
+    else:
+        def fused(i):
+            fn.norm_proj(x, pgs[i % rot], eps, out=y)
+
+    ms = time_region(torch, fused, args.steps, args.warmup)
+    each = time_each(torch, fused, min(args.steps, 200))
+    hot_ms = time_region(torch, lambda i: (fn.norm_proj_swiglu(x, Pg, Pu, eps, out=y) if call.swiglu
+                                           else fn.norm_proj(x, Pg, eps, out=y)), args.steps, args.warmup)
+    result = {"ms": ms, "each": each, "hot_ms": hot_ms, "rot": rot, "wbytes": wbytes}
+
+    if not args.no_chain:
+        # unfused chains on row-major weights, same rotation
+        Wcat = torch.cat([Wg, Wu], dim=1).contiguous() if call.swiglu else Wg
+        ws = [Wcat] + [Wcat.clone() for _ in range(rot - 1)]
+        xhat = torch.empty_like(x)
+        N = call.N
+
+        def chain_own(i):
+            fn.rmsnorm(x, g, eps, out=xhat)
+            h = torch.matmul(xhat, ws[i % rot])
+            if call.swiglu:
+                fn.silu_mul(h, out=y)
+
+        def chain_torch(i):
+            xn = torch.nn.functional.rms_norm(x, (call.K,), g, eps)
+            h = torch.matmul(xn, ws[i % rot])
+            if call.swiglu:
+                torch.mul(torch.nn.functional.silu(h[:, :N]), h[:, N:], out=y)
+
+        result["chain_own_ms"] = time_region(torch, chain_own, args.steps, args.warmup)
+        result["chain_torch_ms"] = time_region(torch, chain_torch, args.steps, args.warmup)
+        del ws
+    return call, inp, result
+
+
+def run_decode_step(args, torch, fn, workloads):
+    calls = workloads.decode_step_calls()
+    items = []
+    for c in calls:
+        x, g, Wg, Wu = workloads.make_inputs_device(c)
+        Pg = fn.fold_weights(g, Wg)
+        Pu = fn.fold_weights(g, Wu) if c.swiglu else None
+        item = {"call": c, "x": x, "g": g, "Pg": Pg, "Pu": Pu,
+                "y": torch.empty((c.M, c.N), dtype=x.dtype, device="cuda")}
+        if not args.no_chain:
+            item["Wcat"] = torch.cat([Wg, Wu], dim=1).contiguous() if c.swiglu else Wg
+            item["xhat"] = torch.empty_like(x)
+        del Wg, Wu
+        items.append(item)
+
+    def fused(_):
+        for it in items:
+            c = it["call"]
+            if c.swiglu:
+                fn.norm_proj_swiglu(it["x"], it["Pg"], it["Pu"], c.eps, out=it["y"])
+            else:
+                fn.norm_proj(it["x"], it["Pg"], c.eps, out=it["y"])
+
+    ms = time_region(torch, fused, args.steps, args.warmup)
+    each = time_each(torch, fused, min(args.steps, 20))
+    result = {"ms": ms, "each": each, "hot_ms": None, "rot": 1,
+              "wbytes": sum(it["Pg"].data.numel() * it["call"].mats for it in items)}
+    if not args.no_chain:
+        def chain_own(_):
+            for it in items:
+                c = it["call"]
+                fn.rmsnorm(it["x"], it["g"], c.eps, out=it["xhat"])
+                h = torch.matmul(it["xhat"], it["Wcat"])
+                if c.swiglu:
+                    fn.silu_mul(h, out=it["y"])
+
+        def chain_torch(_):
+            for it in items:
+                c = it["call"]
+                xn = torch.nn.functional.rms_norm(it["x"], (c.K,), it["g"], c.eps)
+                h = torch.matmul(xn, it["Wcat"])
+                if c.swiglu:
+                    torch.mul(torch.nn.functional.silu(h[:, :c.N]), h[:, c.N:], out=it["y"])
+
+        result["chain_own_ms"] = time_region(torch, chain_own, args.steps, args.warmup)
+        result["chain_torch_ms"] = time_region(torch, chain_torch, args.steps, args.warmup)
+    return calls, result
+
+
+def calibrate_copy(torch):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: libflashnorm runs on one GPU; "
+              "the multi-GPU column split is a design note, not a measured path.", file=sys.stderr)
+        return 2
+    import torch
+    import rmsnorm_projection_gemm_amd as fn
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    fn.load()
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return 0
+
+    if args.workload == "decode_step":
+        calls, r = run_decode_step(args, torch, fn, workloads)
+        bytes_step = sum(c.algorithmic_bytes() for c in calls)
+        flops_step = sum(c.flops() for c in calls)
+        name = "32-layer decode step, M=8: 32 x (norm+QKV 4096->12288, norm+gate/up SwiGLU 4096->2x11008) + norm+head 4096->32000"
+        config = {"workload": name, "calls_per_step": len(calls), "M": 8, "K": 4096,
+                  "weights_bytes": r["wbytes"], "cache": "cold (9.3 GB of distinct weights per step)"}
+        kernel = fn.kernel_name(8, 4096, 12288, False, torch.bfloat16)
+        cpu_call, cpu_inp = calls[-1], None
+        unit = "GB/s"
+        value = bytes_step / (r["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": counter_traffic("decode_step")}
+        dtype = "bf16"
+        per_unit = {"algorithmic_bytes_per_step": bytes_step, "flops_per_step": flops_step}
+    else:
+        call, inp, r = run_single(args, torch, fn, workloads)
+        bytes_call = call.algorithmic_bytes()
+        flops_call = call.flops()
+        kernel = fn.kernel_name(call.M, call.K, call.N, call.swiglu,
+                                torch.bfloat16 if call.dtype == "bf16" else torch.float32)
+        config = {"workload": call.name, "M": call.M, "K": call.K, "N": call.N, "mats": call.mats,
+                  "eps": call.eps, "kernel": kernel,
+                  "cache": (f"cold ({r['rot']} rotated W' copies, {r['rot'] * r['wbytes'] / 2**30:.2f} GiB)"
+                            if r["rot"] > 1 else "hot (one weight buffer)")}
+        cpu_call, cpu_inp = call, inp
+        dtype = call.dtype
+        per_unit = {"algorithmic_bytes_per_call": bytes_call, "flops_per_call": flops_call}
+        if args.workload == "prefill_qkv":
+            unit = "TFLOP/s"
+            value = flops_call / (r["ms"] * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(value, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(value / BF16_PEAK_TFLOPS, 4), "traffic": counter_traffic(args.workload)}
+        elif args.workload == "tiny":
+            unit = "us/call"
+            value = r["ms"] * 1e3
+            gbs = bytes_call / (r["ms"] * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": counter_traffic(args.workload),
+                    "note": "launch-latency bound; the fraction is not meaningful here"}
+        else:
+            unit = "GB/s"
+            value = bytes_call / (r["ms"] * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(value / HBM_PEAK_GBS, 4), "traffic": counter_traffic(args.workload)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 6),
+        "higher_is_better": unit != "us/call",
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; random-init weights of the named shapes)",
+        "config": config,
+        "roofline": roof,
+        "us_per_step": round(r["ms"] * 1e3, 3),
+        "us_p10_p50_p90": [round(pct(r["each"], q) * 1e3, 3) for q in (0.1, 0.5, 0.9)],
+        "hot_us_per_step": None if r["hot_ms"] is None else round(r["hot_ms"] * 1e3, 3),
+        "kernel": kernel,
+        **per_unit,
+    }
+    if "chain_own_ms" in r:
+        out["chain"] = {
+            "own_rmsnorm_then_hipblaslt_us": round(r["chain_own_ms"] * 1e3, 3),
+            "torch_rms_norm_then_matmul_us": round(r["chain_torch_ms"] * 1e3, 3),
+            "fused_speedup_vs_own_chain": round(r["chain_own_ms"] / r["ms"], 3),
+            "fused_speedup_vs_torch_chain": round(r["chain_torch_ms"] / r["ms"], 3),
+        }
+    if not args.no_cpu_baseline:
+        if cpu_inp is None:
+            cpu_inp = workloads.make_inputs(cpu_call)
+        cb = cpu_baseline(cpu_call, cpu_inp, args.cpu_seconds, unit if unit != "us/call" else "us/call")
+        if args.workload == "decode_step":
+            # one head call sampled; scale to the whole step by algorithmic bytes
+            per_call = cb.pop("seconds_per_call")
+            step_s = per_call * bytes_step / cpu_call.algorithmic_bytes()
+            cb["value"] = round(bytes_step / step_s / 1e9, 4)
+            cb["sample"] += "; scaled to the 65-call step by algorithmic bytes"
+        else:
+            cb.pop("seconds_per_call")
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

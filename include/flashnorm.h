@@ -1,0 +1,151 @@
+/*
+ * libflashnorm: fused RMSNorm + linear projection for AMD Instinct MI355X
+ * (gfx950), after FlashNorm.
+ *
+ * The method ([FlashNorm digest] "RMS norm는 연산량 1할인데 왜 33번 호출로
+ * 속도를 갉아먹나", news.juniverse.app, summary bullets proposal 1-3):
+ *   - weightless normalisation: the RMSNorm gain g is folded offline into the
+ *     projection, W' = diag(g) * W, so the run-time norm has no weights;
+ *   - deferred normalisation: the per-row division by RMS(x) moves after the
+ *     product, y = (x * W') / RMS(x), so the sum of squares (vector units)
+ *     and the contraction (matrix units) proceed together.
+ * With RMS(x) = sqrt(mean_k x^2 + eps), the result equals the unfolded
+ * definition y = (x / RMS(x) * g) * W.  The SwiGLU variant
+ * ([FlashInfer #5521] "MiniMax-H3 Fused FC1 + SwiGLU", section "Design",
+ * register-level SwiGLU) computes silu(a) * b with a and b the normalised
+ * gate and up projections, applied to the accumulators before the store.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory:   every data pointer is device memory owned by the caller.  The
+ *           library allocates nothing, frees nothing and never synchronises;
+ *           each call enqueues its work on `stream` (0 = the null stream)
+ *           and returns.  Results are ready when the stream reaches them.
+ * Layouts:  x[M,K], y[M,N], W[K,N] are dense row-major (leading dimensions
+ *           K, N and N).  g[K] is a vector.  All tensors of one call share
+ *           the storage dtype `dt`; y and out use it too.
+ * Packed weights: the folded weights W' live in the library's packed,
+ *           fragment-major layout (fn_fold_weights writes it, the fused
+ *           calls read it).  With e the element size, V = 16/e values per
+ *           lane (8 for bf16, 4 for fp32) and KB = 4*V rows per k-block
+ *           (32 for bf16, 16 for fp32), element W'[k][n] sits at byte
+ *             (((n/16) * ceil(K/KB) + k/KB) * 64 + ((k%KB)/V) * 16 + n%16) * 16
+ *               + (k%V) * e
+ *           and padding elements (k >= K or n >= N) are zero.  Its size is
+ *           fn_packed_weight_bytes(K, N, dt).
+ * Rounding: sums of squares and products accumulate in fp32.  A bf16 result
+ *           is rounded once, to nearest with ties to even, from the fp32
+ *           value ([FlashInfer #4040] "Fused SwiGLU 및 NVFP4 양자화", section
+ *           "하드웨어 최적화"; [FlashInfer #5668] "Kimi-K3 TP12 LatentMoE
+ *           Tail", round once after an fp32 sum).
+ * Errors:   arguments are checked before any HIP call; on failure nothing is
+ *           enqueued and a status other than FN_OK is returned, with detail
+ *           in fn_last_error() (per thread).  Launch failures return
+ *           FN_ERR_HIP.  No C++ exception crosses this interface.
+ * Limits:   1 <= K <= 2^20 with K % 8 == 0; 0 <= M <= 2^22; 0 <= N <= 2^24.
+ *           M == 0 or N == 0 is a valid empty call: nothing is launched and
+ *           no pointer is read.  x, W', y, out must be 16-byte aligned; g, W
+ *           and h (the unfused helpers) need the alignment of their dtype.
+ *           eps must be finite and >= 0.  An output may not overlap an input.
+ * Threads:  the library holds no state between calls beyond the per-thread
+ *           error text; calls on different streams may run concurrently.
+ */
+#ifndef FLASHNORM_H
+#define FLASHNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fn_status {
+  FN_OK = 0,
+  FN_ERR_NULL = 1,   /* a required pointer is NULL                        */
+  FN_ERR_SHAPE = 2,  /* M, K or N outside the limits above                 */
+  FN_ERR_ALIGN = 3,  /* a pointer lacks the required alignment             */
+  FN_ERR_DTYPE = 4,  /* dt is not a member of fn_dtype                     */
+  FN_ERR_EPS = 5,    /* eps is negative, NaN or infinite                   */
+  FN_ERR_ALIAS = 6,  /* an output buffer overlaps an input buffer          */
+  FN_ERR_HIP = 7     /* the HIP runtime rejected a launch                  */
+} fn_status;
+
+typedef enum fn_dtype {
+  FN_F32 = 0,        /* IEEE binary32                                      */
+  FN_BF16 = 1        /* bfloat16 (8 significant bits, fp32 exponent range) */
+} fn_dtype;
+
+/* Bytes of the packed folded weights for a [K,N] matrix; 0 if K, N or dt is
+ * outside the limits. */
+size_t fn_packed_weight_bytes(int64_t K, int64_t N, fn_dtype dt);
+
+/* Weightless normalisation, offline ([FlashNorm digest] proposal 1):
+ *   W'[k][n] = round_dt(g[k] * W[k][n])
+ * computed as one fp32 product (exact for bf16 operands; the correctly
+ * rounded product for fp32) rounded once to dt, written in the packed layout.
+ * g:        [K] device vector, or NULL to pack W unchanged (W' = W).
+ * W:        [K,N] row-major device matrix.
+ * W_packed: device buffer of fn_packed_weight_bytes(K, N, dt) bytes, fully
+ *           overwritten (padding included).  Must not overlap g or W.
+ * Not on the per-token path: run once per weight matrix. */
+fn_status fn_fold_weights(const void* g, const void* W, void* W_packed,
+                          int64_t K, int64_t N, fn_dtype dt, hipStream_t stream);
+
+/* Fused RMSNorm + projection, one launch ([FlashNorm digest] proposals 1-2):
+ *   y[m][n] = round_dt( (sum_k x[m][k] * W'[k][n]) / sqrt(sum_k x[m][k]^2 / K + eps) )
+ * x:        [M,K] row-major.
+ * W_packed: folded weights from fn_fold_weights for this K and N.
+ * y:        [M,N] row-major output, fully overwritten.
+ * eps:      added to the mean square inside the root.
+ * Rows are independent: a non-finite value in row m affects row m only. */
+fn_status fn_norm_proj(const void* x, const void* W_packed, void* y,
+                       int64_t M, int64_t K, int64_t N, float eps,
+                       fn_dtype dt, hipStream_t stream);
+
+/* Fused RMSNorm + gate/up projections + SwiGLU, one launch
+ * ([FlashNorm digest] proposals 1-2; [FlashInfer #5521] section "Design",
+ * register-level SwiGLU):
+ *   a = (x * W'_gate)[m][n] / r[m],  b = (x * W'_up)[m][n] / r[m],
+ *   out[m][n] = round_dt( a / (1 + exp(-a)) * b ),
+ *   r[m] = sqrt(sum_k x[m][k]^2 / K + eps).
+ * The 1/r factor reaches a and b before the SiLU (it cannot be moved past a
+ * nonlinearity).  W_gate_packed and W_up_packed are two packed [K,N]
+ * matrices; out is [M,N] row-major. */
+fn_status fn_norm_proj_swiglu(const void* x, const void* W_gate_packed,
+                              const void* W_up_packed, void* out,
+                              int64_t M, int64_t K, int64_t N, float eps,
+                              fn_dtype dt, hipStream_t stream);
+
+/* Unfused baseline, step 1 of the segmented chain ([FlashInfer #5521],
+ * section "Segmented Chain"): xhat[m][k] = round_dt(x[m][k] / r[m] * g[k]),
+ * written to HBM for a following GEMM.  x, xhat: [M,K]; g: [K]. */
+fn_status fn_rmsnorm(const void* x, const void* g, void* xhat,
+                     int64_t M, int64_t K, float eps, fn_dtype dt,
+                     hipStream_t stream);
+
+/* Unfused baseline, last step of the segmented chain (silu_and_mul over a
+ * [M, 2N] product whose first N columns are the gate and last N the up
+ * projection): out[m][n] = round_dt(silu(h[m][n]) * h[m][N + n]).
+ * h: [M, 2N] row-major; out: [M, N].  K is not involved (pass any valid
+ * shape: only M and N are checked, with N >= 1 and M >= 0). */
+fn_status fn_silu_mul(const void* h, void* out, int64_t M, int64_t N,
+                      fn_dtype dt, hipStream_t stream);
+
+/* Name of the kernel instance fn_norm_proj (swiglu == 0) or
+ * fn_norm_proj_swiglu (swiglu != 0) would launch for this shape, e.g.
+ * "decode_bf16_m16_n1_w4"; a static string, "invalid" for bad shapes. */
+const char* fn_kernel_name(int64_t M, int64_t K, int64_t N, int swiglu, fn_dtype dt);
+
+/* Static description of a status code. */
+const char* fn_status_string(fn_status s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* fn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHNORM_H */

@@ -1,0 +1,213 @@
+"""Python binding of libflashnorm: fused RMSNorm + projection on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of libflashnorm.so; PyTorch provides device memory and the current
+stream.  There is no CPU fallback: if the library is not built, every call
+raises.
+
+    import rmsnorm_projection_gemm_amd as fn
+    Wp = fn.fold_weights(g, W)           # offline: W' = diag(g) W, packed
+    y = fn.norm_proj(x, Wp, eps=1e-6)    # y = (x W') / rms(x), one launch
+    out = fn.norm_proj_swiglu(x, Wg, Wu) # silu(a) * b, one launch
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import re
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libflashnorm.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "flashnorm.h")
+
+FN_F32 = 0
+FN_BF16 = 1
+
+STATUS = {0: "FN_OK", 1: "FN_ERR_NULL", 2: "FN_ERR_SHAPE", 3: "FN_ERR_ALIGN", 4: "FN_ERR_DTYPE",
+          5: "FN_ERR_EPS", 6: "FN_ERR_ALIAS", 7: "FN_ERR_HIP"}
+
+_lib = None
+
+
+class FlashNormError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+def header_functions():
+    """Names of the functions include/flashnorm.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fn_[a-z_]+)\s*\(", text)))
+
+
+def load():
+    """Load libflashnorm.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m rmsnorm_projection_gemm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    sigs = {
+        "fn_packed_weight_bytes": (ctypes.c_size_t, [i64, i64, i32]),
+        "fn_fold_weights": (i32, [vp, vp, vp, i64, i64, i32, vp]),
+        "fn_norm_proj": (i32, [vp, vp, vp, i64, i64, i64, f32, i32, vp]),
+        "fn_norm_proj_swiglu": (i32, [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp]),
+        "fn_rmsnorm": (i32, [vp, vp, vp, i64, i64, f32, i32, vp]),
+        "fn_silu_mul": (i32, [vp, vp, i64, i64, i32, vp]),
+        "fn_kernel_name": (ctypes.c_char_p, [i64, i64, i64, i32, i32]),
+        "fn_status_string": (ctypes.c_char_p, [i32]),
+        "fn_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise FlashNormError(status, load().fn_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return FN_BF16
+    if dtype == torch.float32:
+        return FN_F32
+    raise ValueError(f"dtype must be torch.bfloat16 or torch.float32, got {dtype}")
+
+
+def _stream(t) -> int:
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def _need_cuda(name, t):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor, got device {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclasses.dataclass
+class PackedWeights:
+    """Folded weights W' = diag(g) W in libflashnorm's packed layout."""
+    data: "object"      # torch.uint8 tensor on the device, packed bytes
+    K: int
+    N: int
+    dtype: "object"     # torch.bfloat16 or torch.float32
+
+
+def packed_weight_bytes(K: int, N: int, dtype) -> int:
+    n = load().fn_packed_weight_bytes(K, N, _dt(dtype))
+    if n == 0 and N > 0:
+        raise ValueError(f"K={K} must be in [1, 2^20] and a multiple of 8; N={N} in [0, 2^24]")
+    return n
+
+
+def fold_weights(g, W, out: Optional[PackedWeights] = None) -> PackedWeights:
+    """W'[k, n] = round(g[k] * W[k, n]) in the packed layout (g=None packs W)."""
+    torch = _torch()
+    _need_cuda("W", W)
+    if W.dim() != 2:
+        raise ValueError(f"W must be [K, N], got shape {tuple(W.shape)}")
+    K, N = W.shape
+    dt = _dt(W.dtype)
+    if g is not None:
+        _need_cuda("g", g)
+        if g.dtype != W.dtype or tuple(g.shape) != (K,):
+            raise ValueError(f"g must be [{K}] of dtype {W.dtype}, got {tuple(g.shape)} {g.dtype}")
+    nbytes = packed_weight_bytes(K, N, W.dtype)
+    if out is None:
+        out = PackedWeights(torch.empty(nbytes, dtype=torch.uint8, device=W.device), K, N, W.dtype)
+    elif (out.K, out.N, out.dtype) != (K, N, W.dtype) or out.data.numel() != nbytes:
+        raise ValueError("out does not match W's shape and dtype")
+    _check(load().fn_fold_weights(None if g is None else g.data_ptr(), W.data_ptr(), out.data.data_ptr(),
+                                  K, N, dt, _stream(W)))
+    return out
+
+
+def _check_x(x, Wp: PackedWeights):
+    _need_cuda("x", x)
+    if x.dim() != 2 or x.shape[1] != Wp.K:
+        raise ValueError(f"x must be [M, {Wp.K}], got {tuple(x.shape)}")
+    if x.dtype != Wp.dtype:
+        raise ValueError(f"x dtype {x.dtype} must match the folded weights' {Wp.dtype}")
+    if x.device != Wp.data.device:
+        raise ValueError("x and the folded weights must be on the same device")
+
+
+def _out(out, M, N, x):
+    torch = _torch()
+    if out is None:
+        return torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _need_cuda("out", out)
+    if tuple(out.shape) != (M, N) or out.dtype != x.dtype:
+        raise ValueError(f"out must be [{M}, {N}] of dtype {x.dtype}")
+    return out
+
+
+def norm_proj(x, Wp: PackedWeights, eps: float = 1e-6, out=None):
+    """y = (x @ W') / sqrt(mean(x^2) + eps), one fused launch."""
+    _check_x(x, Wp)
+    M, N = x.shape[0], Wp.N
+    y = _out(out, M, N, x)
+    _check(load().fn_norm_proj(x.data_ptr(), Wp.data.data_ptr(), y.data_ptr(), M, Wp.K, N, eps,
+                               _dt(x.dtype), _stream(x)))
+    return y
+
+
+def norm_proj_swiglu(x, Wg: PackedWeights, Wu: PackedWeights, eps: float = 1e-6, out=None):
+    """out = silu(a) * b with a, b the normalised gate/up projections, one launch."""
+    _check_x(x, Wg)
+    if (Wu.K, Wu.N, Wu.dtype) != (Wg.K, Wg.N, Wg.dtype):
+        raise ValueError("gate and up weights must have the same K, N and dtype")
+    M, N = x.shape[0], Wg.N
+    y = _out(out, M, N, x)
+    _check(load().fn_norm_proj_swiglu(x.data_ptr(), Wg.data.data_ptr(), Wu.data.data_ptr(), y.data_ptr(),
+                                      M, Wg.K, N, eps, _dt(x.dtype), _stream(x)))
+    return y
+
+
+def rmsnorm(x, g, eps: float = 1e-6, out=None):
+    """Unfused chain step: xhat = x / rms(x) * g written to memory."""
+    _need_cuda("x", x)
+    _need_cuda("g", g)
+    M, K = x.shape
+    y = _out(out, M, K, x)
+    _check(load().fn_rmsnorm(x.data_ptr(), g.data_ptr(), y.data_ptr(), M, K, eps, _dt(x.dtype), _stream(x)))
+    return y
+
+
+def silu_mul(h, out=None):
+    """Unfused chain step: out = silu(h[:, :N]) * h[:, N:] for h of shape [M, 2N]."""
+    _need_cuda("h", h)
+    M, N2 = h.shape
+    if N2 % 2:
+        raise ValueError("h must have an even number of columns")
+    y = _out(out, M, N2 // 2, h)
+    _check(load().fn_silu_mul(h.data_ptr(), y.data_ptr(), M, N2 // 2, _dt(h.dtype), _stream(h)))
+    return y
+
+
+def kernel_name(M: int, K: int, N: int, swiglu: bool, dtype) -> str:
+    return load().fn_kernel_name(M, K, N, int(swiglu), _dt(dtype)).decode()
+
+
+__all__ = ["load", "fold_weights", "norm_proj", "norm_proj_swiglu", "rmsnorm", "silu_mul",
+           "packed_weight_bytes", "kernel_name", "PackedWeights", "FlashNormError", "header_functions",
+           "LIB_PATH", "FN_F32", "FN_BF16"]

@@ -1,0 +1,202 @@
+// libflashnorm C ABI: argument checks, kernel-instance choice, launches.
+// The contract of every function is documented in include/flashnorm.h.
+#include "../../include/flashnorm.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "fn_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxK = int64_t(1) << 20;
+constexpr int64_t kMaxM = int64_t(1) << 22;
+constexpr int64_t kMaxN = int64_t(1) << 24;
+
+thread_local char g_last_error[256] = "";
+
+fn_status fail(fn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool dtype_ok(fn_dtype dt) { return dt == FN_F32 || dt == FN_BF16; }
+fn::DType to_dt(fn_dtype dt) { return dt == FN_F32 ? fn::DType::F32 : fn::DType::BF16; }
+int64_t esize(fn_dtype dt) { return dt == FN_F32 ? 4 : 2; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (a == nullptr || b == nullptr || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int64_t packed_bytes(int64_t K, int64_t N, fn_dtype dt) {
+  const int64_t kb = dt == FN_F32 ? 16 : 32;
+  return ((N + 15) / 16) * ((K + kb - 1) / kb) * 1024;
+}
+
+fn_status check_k(int64_t K) {
+  if (K < 1 || K > kMaxK) return fail(FN_ERR_SHAPE, "K=%lld must be in [1, %lld]", (long long)K, (long long)kMaxK);
+  if (K % 8 != 0) return fail(FN_ERR_SHAPE, "K=%lld must be a multiple of 8", (long long)K);
+  return FN_OK;
+}
+
+fn_status check_mn(int64_t M, int64_t N) {
+  if (M < 0 || M > kMaxM) return fail(FN_ERR_SHAPE, "M=%lld must be in [0, %lld]", (long long)M, (long long)kMaxM);
+  if (N < 0 || N > kMaxN) return fail(FN_ERR_SHAPE, "N=%lld must be in [0, %lld]", (long long)N, (long long)kMaxN);
+  return FN_OK;
+}
+
+fn_status check_eps(float eps) {
+  if (!std::isfinite(eps) || eps < 0.f) return fail(FN_ERR_EPS, "eps=%g must be finite and >= 0", (double)eps);
+  return FN_OK;
+}
+
+fn_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return FN_OK;
+}
+
+#define FN_TRY(expr)                  \
+  do {                                \
+    const fn_status s_ = (expr);      \
+    if (s_ != FN_OK) return s_;       \
+  } while (0)
+
+fn_status fused_common(const void* x, const void* wg, const void* wu, void* y, int64_t M, int64_t K,
+                       int64_t N, float eps, fn_dtype dt, hipStream_t stream, bool swiglu) {
+  g_last_error[0] = '\0';
+  if (!dtype_ok(dt)) return fail(FN_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(M, N));
+  FN_TRY(check_eps(eps));
+  if (M == 0 || N == 0) return FN_OK;
+  if (x == nullptr) return fail(FN_ERR_NULL, "x is NULL");
+  if (wg == nullptr) return fail(FN_ERR_NULL, swiglu ? "W_gate_packed is NULL" : "W_packed is NULL");
+  if (swiglu && wu == nullptr) return fail(FN_ERR_NULL, "W_up_packed is NULL");
+  if (y == nullptr) return fail(FN_ERR_NULL, swiglu ? "out is NULL" : "y is NULL");
+  if (!aligned(x, 16)) return fail(FN_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(wg, 16) || (swiglu && !aligned(wu, 16)))
+    return fail(FN_ERR_ALIGN, "packed weights must be 16-byte aligned");
+  if (!aligned(y, 16)) return fail(FN_ERR_ALIGN, "output must be 16-byte aligned");
+  const int64_t e = esize(dt);
+  const int64_t xb = M * K * e, yb = M * N * e, wb = packed_bytes(K, N, dt);
+  if (overlap(y, yb, x, xb) || overlap(y, yb, wg, wb) || (swiglu && overlap(y, yb, wu, wb)))
+    return fail(FN_ERR_ALIAS, "output overlaps an input");
+  const fn::DType t = to_dt(dt);
+  const fn::FusedPlan plan = fn::plan_fused(t, M, K, N, swiglu);
+  return hip_status(fn::launch_fused(t, plan, x, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, eps, stream),
+                    plan.name);
+}
+
+}  // namespace
+
+namespace fn {
+
+FusedPlan plan_fused(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
+  return plan_decode(dt, M, K, N, swiglu);
+}
+
+hipError_t launch_fused(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
+                        const void* w_up, void* y, int M, int K, int N, float eps, hipStream_t stream) {
+  return launch_decode(dt, plan, x, w_gate, w_up, y, M, K, N, eps, stream);
+}
+
+}  // namespace fn
+
+extern "C" {
+
+size_t fn_packed_weight_bytes(int64_t K, int64_t N, fn_dtype dt) {
+  if (!dtype_ok(dt) || K < 1 || K > kMaxK || K % 8 != 0 || N < 0 || N > kMaxN) return 0;
+  return (size_t)packed_bytes(K, N, dt);
+}
+
+fn_status fn_fold_weights(const void* g, const void* W, void* W_packed, int64_t K, int64_t N, fn_dtype dt,
+                          hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!dtype_ok(dt)) return fail(FN_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(0, N));
+  if (N == 0) return FN_OK;
+  if (W == nullptr) return fail(FN_ERR_NULL, "W is NULL");
+  if (W_packed == nullptr) return fail(FN_ERR_NULL, "W_packed is NULL");
+  const int64_t e = esize(dt);
+  if ((g != nullptr && !aligned(g, (uintptr_t)e)) || !aligned(W, (uintptr_t)e))
+    return fail(FN_ERR_ALIGN, "g and W must be aligned to their element size");
+  if (!aligned(W_packed, 16)) return fail(FN_ERR_ALIGN, "W_packed must be 16-byte aligned");
+  const int64_t pb = packed_bytes(K, N, dt);
+  if (overlap(W_packed, pb, W, K * N * e) || overlap(W_packed, pb, g, K * e))
+    return fail(FN_ERR_ALIAS, "W_packed overlaps g or W");
+  return hip_status(fn::launch_fold(to_dt(dt), g, W, W_packed, (int)K, (int)N, stream), "fold_weights");
+}
+
+fn_status fn_norm_proj(const void* x, const void* W_packed, void* y, int64_t M, int64_t K, int64_t N, float eps,
+                       fn_dtype dt, hipStream_t stream) {
+  return fused_common(x, W_packed, nullptr, y, M, K, N, eps, dt, stream, false);
+}
+
+fn_status fn_norm_proj_swiglu(const void* x, const void* W_gate_packed, const void* W_up_packed, void* out,
+                              int64_t M, int64_t K, int64_t N, float eps, fn_dtype dt, hipStream_t stream) {
+  return fused_common(x, W_gate_packed, W_up_packed, out, M, K, N, eps, dt, stream, true);
+}
+
+fn_status fn_rmsnorm(const void* x, const void* g, void* xhat, int64_t M, int64_t K, float eps, fn_dtype dt,
+                     hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!dtype_ok(dt)) return fail(FN_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(M, 0));
+  FN_TRY(check_eps(eps));
+  if (M == 0) return FN_OK;
+  if (x == nullptr || g == nullptr || xhat == nullptr) return fail(FN_ERR_NULL, "x, g and xhat must be non-NULL");
+  const int64_t e = esize(dt);
+  if (!aligned(x, (uintptr_t)e) || !aligned(g, (uintptr_t)e) || !aligned(xhat, (uintptr_t)e))
+    return fail(FN_ERR_ALIGN, "x, g and xhat must be aligned to their element size");
+  if (overlap(xhat, M * K * e, x, M * K * e) || overlap(xhat, M * K * e, g, K * e))
+    return fail(FN_ERR_ALIAS, "xhat overlaps x or g");
+  return hip_status(fn::launch_rmsnorm(to_dt(dt), x, g, xhat, (int)M, (int)K, eps, stream), "rmsnorm");
+}
+
+fn_status fn_silu_mul(const void* h, void* out, int64_t M, int64_t N, fn_dtype dt, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!dtype_ok(dt)) return fail(FN_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  FN_TRY(check_mn(M, N));
+  if (M == 0 || N == 0) return FN_OK;
+  if (h == nullptr || out == nullptr) return fail(FN_ERR_NULL, "h and out must be non-NULL");
+  const int64_t e = esize(dt);
+  if (!aligned(h, (uintptr_t)e) || !aligned(out, (uintptr_t)e))
+    return fail(FN_ERR_ALIGN, "h and out must be aligned to their element size");
+  if (overlap(out, M * N * e, h, M * 2 * N * e)) return fail(FN_ERR_ALIAS, "out overlaps h");
+  return hip_status(fn::launch_silu_mul(to_dt(dt), h, out, (int)M, (int)N, stream), "silu_mul");
+}
+
+const char* fn_kernel_name(int64_t M, int64_t K, int64_t N, int swiglu, fn_dtype dt) {
+  if (!dtype_ok(dt) || K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN)
+    return "invalid";
+  return fn::plan_fused(to_dt(dt), M, K, N, swiglu != 0).name;
+}
+
+const char* fn_status_string(fn_status s) {
+  switch (s) {
+    case FN_OK: return "ok";
+    case FN_ERR_NULL: return "null pointer";
+    case FN_ERR_SHAPE: return "shape out of range";
+    case FN_ERR_ALIGN: return "misaligned pointer";
+    case FN_ERR_DTYPE: return "unknown dtype";
+    case FN_ERR_EPS: return "eps must be finite and non-negative";
+    case FN_ERR_ALIAS: return "output overlaps an input";
+    case FN_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* fn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

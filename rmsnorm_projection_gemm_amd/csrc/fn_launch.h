@@ -1,0 +1,44 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fn {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+inline int elem_bytes(DType t) { return t == DType::F32 ? 4 : 2; }
+inline int k_per_block(DType t) { return t == DType::F32 ? 16 : 32; }   // KB of the packed layout
+
+// Kernel instance chosen for one fused call.
+struct FusedPlan {
+  int kind;           // 0 = decode (skinny M), 1 = prefill (tiled)
+  int mf;             // 16-row fragments per workgroup (decode)
+  int nf;             // 16-column fragments per workgroup (decode)
+  int waves;          // waves per workgroup
+  dim3 grid;
+  dim3 block;
+  const char* name;   // static string
+};
+
+FusedPlan plan_fused(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu);
+FusedPlan plan_decode(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu);
+hipError_t launch_decode(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
+                         const void* w_up, void* y, int M, int K, int N, float eps,
+                         hipStream_t stream);
+
+hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
+                       int K, int N, hipStream_t stream);
+
+hipError_t launch_fused(DType dt, const FusedPlan& plan, const void* x,
+                        const void* w_gate, const void* w_up, void* y,
+                        int M, int K, int N, float eps, hipStream_t stream);
+
+hipError_t launch_rmsnorm(DType dt, const void* x, const void* g, void* xhat,
+                          int M, int K, float eps, hipStream_t stream);
+
+hipError_t launch_silu_mul(DType dt, const void* h, void* out, int M, int N,
+                           hipStream_t stream);
+
+}  // namespace fn

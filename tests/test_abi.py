@@ -1,0 +1,142 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/flashnorm.h declares, sizes the packed layout, picks kernel instances
+by the M-ladder, and rejects bad arguments before any HIP call."""
+import ctypes
+import math
+
+import pytest
+
+import rmsnorm_projection_gemm_amd as fn
+
+F32, BF16 = fn.FN_F32, fn.FN_BF16
+OK, NULL, SHAPE, ALIGN, DTYPE, EPS, ALIAS = 0, 1, 2, 3, 4, 5, 6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fn.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = fn.header_functions()
+    assert set(declared) >= {"fn_fold_weights", "fn_norm_proj", "fn_norm_proj_swiglu"}
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in flashnorm.h but not exported"
+    # the raw symbol table as well (not only the ctypes wrappers)
+    handle = ctypes.CDLL(fn.LIB_PATH)
+    for name in declared:
+        ctypes.cast(getattr(handle, name), ctypes.c_void_p)
+
+
+@pytest.mark.parametrize("K,N,dt", [(8, 1, BF16), (4096, 12288, BF16), (40, 37, BF16), (256, 768, F32),
+                                    (24, 17, F32), (4096, 0, BF16)])
+def test_packed_weight_bytes(lib, K, N, dt):
+    kb = 16 if dt == F32 else 32
+    assert lib.fn_packed_weight_bytes(K, N, dt) == math.ceil(N / 16) * math.ceil(K / kb) * 1024
+
+
+@pytest.mark.parametrize("K,N,dt", [(0, 16, BF16), (12, 16, BF16), ((1 << 20) + 8, 16, BF16),
+                                    (16, -1, BF16), (16, (1 << 24) + 1, F32), (16, 16, 9)])
+def test_packed_weight_bytes_invalid(lib, K, N, dt):
+    assert lib.fn_packed_weight_bytes(K, N, dt) == 0
+
+
+@pytest.mark.parametrize("M,name", [(1, "m16"), (8, "m16"), (16, "m16"), (17, "m32"), (32, "m32"),
+                                    (33, "m64"), (64, "m64")])
+def test_m_ladder(lib, M, name):
+    got = lib.fn_kernel_name(M, 4096, 12288, 0, BF16).decode()
+    assert name in got and got.startswith("decode_bf16"), got
+    assert lib.fn_kernel_name(M, 4096, 11008, 1, BF16).decode().startswith("decode_swiglu_bf16")
+
+
+def test_kernel_name_invalid(lib):
+    assert lib.fn_kernel_name(0, 4096, 16, 0, BF16) == b"invalid"
+    assert lib.fn_kernel_name(4, 12, 16, 0, BF16) == b"invalid"
+
+
+def _np(lib, x=0x1000, w=0x20000, y=0x40000, M=4, K=16, N=16, eps=1e-6, dt=BF16):
+    return lib.fn_norm_proj(x, w, y, M, K, N, eps, dt, None)
+
+
+def _sw(lib, x=0x1000, wg=0x20000, wu=0x30000, y=0x40000, M=4, K=16, N=16, eps=1e-6, dt=BF16):
+    return lib.fn_norm_proj_swiglu(x, wg, wu, y, M, K, N, eps, dt, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(x=None), NULL, "x is NULL"),
+    (dict(w=None), NULL, "W_packed"),
+    (dict(y=None), NULL, "y is NULL"),
+    (dict(K=12), SHAPE, "multiple of 8"),
+    (dict(K=0), SHAPE, "K=0"),
+    (dict(K=(1 << 20) + 8), SHAPE, "K="),
+    (dict(M=-1), SHAPE, "M=-1"),
+    (dict(M=(1 << 22) + 1), SHAPE, "M="),
+    (dict(N=-5), SHAPE, "N=-5"),
+    (dict(x=0x1008), ALIGN, "x must be 16-byte aligned"),
+    (dict(w=0x20004), ALIGN, "packed weights"),
+    (dict(y=0x40002), ALIGN, "output"),
+    (dict(eps=-1.0), EPS, "eps"),
+    (dict(eps=float("nan")), EPS, "eps"),
+    (dict(eps=float("inf")), EPS, "eps"),
+    (dict(dt=3), DTYPE, "dtype"),
+    (dict(y=0x1000), ALIAS, "overlaps"),
+    (dict(y=0x1040), ALIAS, "overlaps"),
+    (dict(y=0x20000), ALIAS, "overlaps"),
+])
+def test_norm_proj_rejects(lib, kwargs, status, needle):
+    assert _np(lib, **kwargs) == status
+    assert needle in lib.fn_last_error().decode()
+
+
+def test_swiglu_rejects(lib):
+    assert _sw(lib, wu=None) == NULL
+    assert "W_up_packed" in lib.fn_last_error().decode()
+    assert _sw(lib, wg=None) == NULL
+    assert _sw(lib, wu=0x30008) == ALIGN
+    assert _sw(lib, y=0x30000) == ALIAS
+    assert _sw(lib, dt=-1) == DTYPE
+
+
+def test_empty_calls_touch_nothing(lib):
+    # M == 0 or N == 0 is a valid no-op: nothing is launched, pointers unread
+    assert _np(lib, x=None, w=None, y=None, M=0) == OK
+    assert _np(lib, x=None, w=None, y=None, N=0) == OK
+    assert _sw(lib, x=None, wg=None, wu=None, y=None, M=0) == OK
+    assert lib.fn_last_error() == b""
+    # but shapes are still validated for empty calls
+    assert _np(lib, M=0, K=12) == SHAPE
+
+
+def test_fold_rejects(lib):
+    f = lib.fn_fold_weights
+    assert f(0x100, None, 0x10000, 16, 16, BF16, None) == NULL
+    assert f(0x100, 0x1000, None, 16, 16, BF16, None) == NULL
+    assert f(0x101, 0x1000, 0x10000, 16, 16, BF16, None) == ALIGN
+    assert f(0x100, 0x1000, 0x10008, 16, 16, BF16, None) == ALIGN
+    assert f(0x100, 0x1000, 0x1000, 16, 16, BF16, None) == ALIAS
+    assert f(0x100, 0x1000, 0x10000, 20, 16, BF16, None) == SHAPE
+    assert f(0x100, 0x1000, 0x10000, 16, 16, 5, None) == DTYPE
+    assert f(None, None, None, 16, 0, BF16, None) == OK
+
+
+def test_chain_helpers_reject(lib):
+    assert lib.fn_rmsnorm(None, 0x100, 0x1000, 2, 16, 1e-6, BF16, None) == NULL
+    assert lib.fn_rmsnorm(0x1000, 0x100, 0x1000, 2, 16, 1e-6, BF16, None) == ALIAS
+    assert lib.fn_rmsnorm(0x1000, 0x100, 0x2000, 2, 16, -1.0, BF16, None) == EPS
+    assert lib.fn_silu_mul(0x1000, 0x1000, 2, 8, BF16, None) == ALIAS
+    assert lib.fn_silu_mul(0x1001, 0x4000, 2, 8, BF16, None) == ALIGN
+    assert lib.fn_silu_mul(None, None, 0, 8, BF16, None) == OK
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.fn_status_string(s)
+    assert lib.fn_status_string(99) == b"unknown status"
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    """No CPU fallback: a missing library is an error, not a silent path."""
+    monkeypatch.setattr(fn, "_lib", None)
+    monkeypatch.setattr(fn, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        fn.load()

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs.  Tolerance per element: |gpu - oracle| <=
+2e-2 * (|oracle| + 1) for bf16 storage with fp32 accumulation, 1e-5 * (|oracle| + 1)
+for fp32; bit-exact for the fold and for invariants that the kernel's fixed
+accumulation order preserves exactly."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests import oracle_pins
+from tests.gpu_helpers import TOL, assert_close, pack_host, to_dev, to_f64, tdtype
+
+pytestmark = pytest.mark.gpu
+
+
+def fused(fn, inp: W.Inputs, eps=None):
+    """Fold on the device, then one fused call; returns (y float64, gpu tensors)."""
+    c = inp.call
+    eps = c.eps if eps is None else eps
+    x = to_dev(inp.x, c.dtype)
+    g = to_dev(inp.g, c.dtype)
+    Wg = fn.fold_weights(g, to_dev(inp.W, c.dtype))
+    if c.swiglu:
+        Wu = fn.fold_weights(g, to_dev(inp.W_up, c.dtype))
+        y = fn.norm_proj_swiglu(x, Wg, Wu, eps)
+    else:
+        y = fn.norm_proj(x, Wg, eps)
+    return to_f64(y)
+
+
+def reference(inp: W.Inputs, rows=None, cols=None, eps=None):
+    c = inp.call
+    eps = c.eps if eps is None else eps
+    x = inp.x if rows is None else inp.x[rows]
+    Wm = inp.W if cols is None else inp.W[:, cols]
+    if c.swiglu:
+        Wu = inp.W_up if cols is None else inp.W_up[:, cols]
+        return oracle.norm_proj_swiglu(x, inp.g, Wm, Wu, eps)
+    return oracle.norm_proj(x, inp.g, Wm, eps)
+
+
+# ---------------------------------------------------------------- fold ----
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("K,N", [(8, 1), (40, 37), (256, 768), (4096, 1000)])
+def test_fold_bit_exact(gpu_lib, dtype, K, N):
+    inp = W.random_inputs(1, K, N, dtype, seed=100 + K + N)
+    ref = oracle.fold_weights(inp.g, inp.W, dtype)
+    Wp = gpu_lib.fold_weights(to_dev(inp.g, dtype), to_dev(inp.W, dtype))
+    got = Wp.data.cpu().numpy()
+    want = pack_host(ref, dtype)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), f"fold differs in {np.count_nonzero(got != want)} bytes"
+    # g omitted: the weights are packed unchanged
+    Wp1 = gpu_lib.fold_weights(None, to_dev(inp.W, dtype))
+    assert np.array_equal(Wp1.data.cpu().numpy(), pack_host(inp.W, dtype))
+
+
+# ------------------------------------------------------ hand-derived case --
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hand_case_exact(gpu_lib, dtype):
+    case = [c for c in oracle_pins.load_golden()["cases"] if c["name"] == "bf16_exact_k8"][0]
+    x = np.asarray(case["x"], np.float32)
+    g = np.asarray(case["g"], np.float32)
+    Wm = oracle_pins._case_W(case).astype(np.float32)
+    Wp = gpu_lib.fold_weights(to_dev(g, dtype), to_dev(Wm, dtype))
+    y = to_f64(gpu_lib.norm_proj(to_dev(x, dtype), Wp, 0.0))
+    assert np.array_equal(y, np.asarray(case["y"], np.float64))
+
+
+# ------------------------------------------------------ workload configs --
+def test_tiny_f32(gpu_lib):
+    inp = W.make_inputs(W.TINY)
+    assert_close(fused(gpu_lib, inp), reference(inp), "f32", "tiny")
+
+
+def test_qkv_decode_full(gpu_lib):
+    inp = W.make_inputs(W.QKV_DECODE)
+    assert_close(fused(gpu_lib, inp), reference(inp), "bf16", "qkv decode")
+
+
+def test_ffn_decode_swiglu_full(gpu_lib):
+    inp = W.make_inputs(W.FFN_DECODE)
+    assert_close(fused(gpu_lib, inp), reference(inp), "bf16", "ffn swiglu decode")
+
+
+def test_prefill_qkv_sampled(gpu_lib):
+    inp = W.make_inputs(W.PREFILL_QKV)
+    y = fused(gpu_lib, inp)
+    rows = W.sample_indices(inp.call.M, 96, seed=41)
+    cols = W.sample_indices(inp.call.N, 768, seed=42)
+    assert_close(y[np.ix_(rows, cols)], reference(inp, rows, cols), "bf16", "prefill sampled")
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("index", [0, 1, 30, 31, 62, 63, 64])
+def test_decode_step_calls(gpu_lib, index):
+    call = W.decode_step_calls()[index]
+    inp = W.make_inputs(call)
+    assert_close(fused(gpu_lib, inp), reference(inp), "bf16", call.name)
+
+
+# ---------------------------------------------------- ragged and edges ---
+RAGGED = [(1, 8, 16), (3, 40, 37), (17, 256, 48), (16, 64, 200), (33, 96, 100), (63, 128, 17),
+          (64, 72, 64), (65, 256, 160), (100, 40, 33), (130, 512, 260), (257, 64, 31)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("M,K,N", RAGGED)
+def test_ragged(gpu_lib, dtype, swiglu, M, K, N):
+    inp = W.random_inputs(M, K, N, dtype, seed=M * 7 + K * 3 + N + int(swiglu), swiglu=swiglu)
+    assert_close(fused(gpu_lib, inp), reference(inp), dtype, f"ragged {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.5])
+def test_eps_values(gpu_lib, eps):
+    inp = W.random_inputs(5, 64, 48, "f32", seed=7)
+    assert_close(fused(gpu_lib, inp, eps), reference(inp, eps=eps), "f32", f"eps={eps}")
+
+
+def test_empty_calls(gpu_lib):
+    import torch
+    Wp = gpu_lib.fold_weights(None, torch.zeros((64, 32), dtype=torch.bfloat16, device="cuda"))
+    y = gpu_lib.norm_proj(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), Wp)
+    assert tuple(y.shape) == (0, 32)
+    Wz = gpu_lib.fold_weights(None, torch.zeros((64, 0), dtype=torch.bfloat16, device="cuda"))
+    y = gpu_lib.norm_proj(torch.ones((3, 64), dtype=torch.bfloat16, device="cuda"), Wz)
+    assert tuple(y.shape) == (3, 0)
+
+
+def test_zero_row_with_eps(gpu_lib):
+    inp = W.random_inputs(4, 64, 32, "bf16", seed=9)
+    inp.x[2] = 0.0
+    y = fused(gpu_lib, inp, 1e-6)
+    assert np.all(y[2] == 0.0)
+    assert_close(y, reference(inp, eps=1e-6), "bf16", "zero row")
+
+
+def test_nan_row_isolated(gpu_lib):
+    inp = W.random_inputs(20, 128, 64, "bf16", seed=10)
+    inp.x[5, 17] = np.nan
+    c = inp.call
+    x = to_dev(inp.x, c.dtype)
+    Wp = gpu_lib.fold_weights(to_dev(inp.g, c.dtype), to_dev(inp.W, c.dtype))
+    y = to_f64(gpu_lib.norm_proj(x, Wp, c.eps))
+    assert np.all(np.isnan(y[5]))
+    ref = reference(inp)
+    keep = [i for i in range(20) if i != 5]
+    assert_close(y[keep], ref[keep], "bf16", "rows beside a NaN row")
+
+
+# ----------------------------------------------------------- invariants --
+def _fold_and_run(fn, x_np, g_np, W_np, dtype, eps):
+    Wp = fn.fold_weights(to_dev(g_np, dtype), to_dev(W_np, dtype))
+    return to_f64(fn.norm_proj(to_dev(x_np, dtype), Wp, eps))
+
+
+@pytest.mark.parametrize("p", [-3, 5])
+def test_scale_invariance_bit_exact(gpu_lib, p):
+    """RMSNorm(2^p x) = RMSNorm(x) at eps=0: the kernel scales every partial
+    sum by a power of two, so the outputs agree bit for bit."""
+    inp = W.random_inputs(16, 512, 96, "bf16", seed=12)
+    base = _fold_and_run(gpu_lib, inp.x, inp.g, inp.W, "bf16", 0.0)
+    scaled = _fold_and_run(gpu_lib, inp.x * np.float32(2.0 ** p), inp.g, inp.W, "bf16", 0.0)
+    assert np.array_equal(base, scaled)
+
+
+def test_row_permutation_bit_exact(gpu_lib):
+    inp = W.random_inputs(48, 256, 80, "bf16", seed=13)
+    perm = np.random.default_rng(1).permutation(48)
+    base = _fold_and_run(gpu_lib, inp.x, inp.g, inp.W, "bf16", 1e-6)
+    permd = _fold_and_run(gpu_lib, inp.x[perm], inp.g, inp.W, "bf16", 1e-6)
+    assert np.array_equal(permd, base[perm])
+
+
+def test_column_concatenation_bit_exact(gpu_lib):
+    inp = W.random_inputs(8, 256, 96, "bf16", seed=14)
+    full = _fold_and_run(gpu_lib, inp.x, inp.g, inp.W, "bf16", 1e-6)
+    left = _fold_and_run(gpu_lib, inp.x, inp.g, np.ascontiguousarray(inp.W[:, :64]), "bf16", 1e-6)
+    right = _fold_and_run(gpu_lib, inp.x, inp.g, np.ascontiguousarray(inp.W[:, 64:]), "bf16", 1e-6)
+    assert np.array_equal(full, np.concatenate([left, right], axis=1))
+
+
+def test_rne_store(gpu_lib):
+    """Outputs that are exact fp32 ties round to even in bf16: x = ones(8)
+    gives r = 1 and y[n] = sum_k W[k, n] exactly in fp32."""
+    K = 8
+    cols = [[1.0, 2.0 ** -8], [1.0, 2.0 ** -7, 2.0 ** -8], [-1.0, -2.0 ** -8],
+            [255.0, 0.5], [1.0, 2.0 ** -8, 2.0 ** -20], [3.0, 2.0 ** -7]]
+    Wm = np.zeros((K, 16), np.float32)
+    for n, vals in enumerate(cols):
+        Wm[:len(vals), n] = vals
+    x = np.ones((1, K), np.float32)
+    y = _fold_and_run(gpu_lib, x, np.ones(K, np.float32), Wm, "bf16", 0.0)
+    want = oracle.round_to_bf16(Wm.astype(np.float64).sum(axis=0))
+    assert np.array_equal(y[0], want)
+
+
+# ------------------------------------------------------ staleness (T5) --
+def test_back_to_back_calls_not_stale(gpu_lib):
+    """256 consecutive calls with distinct x into one reused, NaN-poisoned y:
+    every output must match its own input's oracle, and differ from the
+    previous call's oracle by more than the tolerance (so a one-step-stale
+    result would be caught; the failure mode of the two-stream FlashNorm
+    bug)."""
+    import torch
+    M, K, N, T = 16, 1024, 512, 256
+    base = W.random_inputs(M, K, N, "bf16", seed=15)
+    Wp = gpu_lib.fold_weights(to_dev(base.g, "bf16"), to_dev(base.W, "bf16"))
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xs = [W.make_x(M, K, "bf16", seed=1000 + t) for t in range(T)]
+    xd = [to_dev(x, "bf16") for x in xs]
+    outs = []
+    for t in range(T):
+        gpu_lib.norm_proj(xd[t], Wp, 1e-6, out=y)
+        outs.append(y.clone())
+    torch.cuda.synchronize()
+    prev_ref = None
+    for t in range(T):
+        ref = oracle.norm_proj(xs[t], base.g, base.W, 1e-6)
+        got = to_f64(outs[t])
+        assert_close(got, ref, "bf16", f"call {t}")
+        if prev_ref is not None:
+            stale = np.max(np.abs(got - prev_ref) / (np.abs(prev_ref) + 1.0))
+            assert stale > TOL["bf16"], f"call {t} indistinguishable from call {t - 1}"
+        prev_ref = ref
+
+
+# ------------------------------------------------------ unfused chain ---
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chain_rmsnorm(gpu_lib, dtype):
+    inp = W.random_inputs(9, 264, 8, dtype, seed=16)
+    xhat = to_f64(gpu_lib.rmsnorm(to_dev(inp.x, dtype), to_dev(inp.g, dtype), 1e-6))
+    assert_close(xhat, oracle.rmsnorm(inp.x, inp.g, 1e-6), dtype, "rmsnorm")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chain_silu_mul(gpu_lib, dtype):
+    rng = np.random.default_rng(17)
+    h = rng.standard_normal((7, 2 * 45)).astype(np.float32)
+    hd = to_dev(h, dtype)
+    hs = to_f64(hd)
+    out = to_f64(gpu_lib.silu_mul(hd))
+    assert_close(out, oracle.silu(hs[:, :45]) * hs[:, 45:], dtype, "silu_mul")
+
+
+def test_python_binding_rejects_bad_arguments(gpu_lib):
+    import torch
+    Wp = gpu_lib.fold_weights(None, torch.zeros((64, 32), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        gpu_lib.norm_proj(torch.zeros((4, 32), dtype=torch.bfloat16, device="cuda"), Wp)
+    with pytest.raises(ValueError):
+        gpu_lib.norm_proj(torch.zeros((4, 64), dtype=torch.float32, device="cuda"), Wp)
+    with pytest.raises(gpu_lib.FlashNormError):
+        gpu_lib.norm_proj(torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda"), Wp, eps=-1.0)
+    assert tdtype("bf16") == torch.bfloat16

@@ -154,6 +154,32 @@ def make_x(M: int, K: int, dtype: str, seed: int) -> np.ndarray:
     return _to_storage(rng.standard_normal((M, K), dtype=np.float32), dtype)
 
 
+def make_inputs_device(call: Call, device="cuda"):
+    """The same distributions drawn by torch's generator on the device, for
+    benchmark-only inputs too large to draw on the host quickly (the 32-layer
+    decode step holds 9.3 GB of weights).  Seeded by ``call.seed``; values
+    differ from make_inputs (different generator) and are rounded to bf16 by
+    torch's round-to-nearest-even conversion.  Returns (x, g, W, W_up)
+    tensors of the storage dtype."""
+    import torch
+    tdt = torch.bfloat16 if call.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed(call.seed)
+    M, K, N = call.M, call.K, call.N
+    x = torch.randn((M, K), generator=gen, device=device, dtype=torch.float32)
+    if call.outlier_fraction > 0:
+        n_out = int(round(call.outlier_fraction * K))
+        idx = torch.randperm(K, generator=gen, device=device)[:n_out]
+        x[:, idx] *= call.outlier_factor
+    g = torch.rand((K,), generator=gen, device=device, dtype=torch.float32) + 0.5
+    std = 1.0 / float(np.sqrt(K))
+    W = torch.randn((K, N), generator=gen, device=device, dtype=torch.float32).mul_(std).to(tdt)
+    W_up = None
+    if call.swiglu:
+        W_up = torch.randn((K, N), generator=gen, device=device, dtype=torch.float32).mul_(std).to(tdt)
+    return x.to(tdt), g.to(tdt), W, W_up
+
+
 def sample_indices(n: int, count: int, seed: int) -> np.ndarray:
     """Seeded sorted subset of range(n), always including the first and last index."""
     if count >= n:
@@ -164,5 +190,5 @@ def sample_indices(n: int, count: int, seed: int) -> np.ndarray:
 
 
 __all__ = ["Call", "Inputs", "EPS", "TINY", "QKV_DECODE", "FFN_DECODE", "PREFILL_QKV",
-           "WORKLOADS", "decode_step_calls", "make_inputs", "random_inputs", "make_x",
+           "WORKLOADS", "decode_step_calls", "make_inputs", "make_inputs_device", "random_inputs", "make_x",
            "sample_indices", "DECODE_STEP_LAYERS", "DECODE_STEP_M"]
