@@ -22,6 +22,10 @@ ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in any kernel.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source extras.  The decode kernels keep their few accumulators in
+# VGPRs (the AGPR form made the compiler shuffle accumulators every
+# iteration); the prefill kernel needs the AGPR file for its 256.
+FILE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
                 "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
 
@@ -39,7 +43,8 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-c", src, "-o", obj] + COMMON_FLAGS + DEVICE_FLAGS
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc(), "-c", src, "-o", obj] + COMMON_FLAGS + DEVICE_FLAGS + extra
     if src.endswith(".cpp"):
         cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + COMMON_FLAGS + DEVICE_FLAGS
     if verbose:

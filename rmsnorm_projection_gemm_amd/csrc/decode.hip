@@ -1,21 +1,33 @@
 // Fused RMSNorm + projection (+ SwiGLU) for small row counts (decode).
 //
-// One launch computes, per output tile, the contraction x * W' on the MFMA
-// units and the per-row sum of squares of x on the VALU from the very same
-// x registers, then applies the deferred 1/RMS scale (and SiLU * up) to the
-// fp32 accumulators and stores the tile once ([FlashNorm digest] proposals
-// 1-2; [FlashInfer #5521] "Design" item 2, register-level SwiGLU).  Nothing
-// intermediate is written to memory and there is no second stream to join,
-// so the stale-buffer race the FlashNorm talk describes (a post-scale step
-// reading a product that another stream had not finished) cannot occur.
+// One launch computes, per output tile, the contraction x * W' and the
+// per-row sum of squares of x from the very same x registers, then applies
+// the deferred 1/RMS scale (and SiLU * up) to the fp32 accumulators and
+// stores the tile once ([FlashNorm digest] proposals 1-2; [FlashInfer #5521]
+// "Design" item 2, register-level SwiGLU).  Nothing intermediate is written
+// to memory and there is no second stream to join, so the stale-buffer race
+// the FlashNorm talk describes (a post-scale step reading a product another
+// stream had not finished) cannot occur.
 //
-// Decomposition: a workgroup owns NF 16-column blocks of W' (for SwiGLU the
-// same columns of W'_gate and W'_up) and MF 16-row blocks of x; its WAVES
-// waves split the k-blocks between them and stream their share of W' from
-// HBM exactly once.  Partial accumulators and sums of squares meet in LDS,
-// where the epilogue finishes them.  W' uses the packed fragment layout, so
-// each lane's weight operand is one 16-byte load and a wave reads 1 KiB of
-// contiguous memory per fragment.
+// Decomposition: a workgroup owns WN*NF 16-column blocks of W' (for SwiGLU
+// the same columns of W'_gate and W'_up) and MF 16-row blocks of x.  Its
+// WN*WK waves form WN column groups of NF blocks each and WK k-splits; every
+// wave streams its share of W' from HBM exactly once, with non-temporal
+// loads so W' does not evict x from the caches.  The WN waves of one k-split
+// read the same x addresses at nearly the same time, so x crosses from L2 to
+// the CU once per workgroup rather than once per wave: x traffic out of L2,
+// not HBM, is what limits this kernel once M reaches 64.  W' uses the packed fragment layout: each lane's weight operand is
+// one 16-byte load and a wave reads 1 KiB of contiguous memory per fragment.
+//
+// In this regime the matrix cores idle while W' streams in, and every VALU
+// instruction costs four cycles per wave on the critical path.  So the sum of
+// squares is taken on the matrix cores too: an MFMA with the x fragment as
+// both operands yields the 16x16 Gram block x x^T whose diagonal holds each
+// row's partial sum of squares (fp32 products of bf16 values are exact).
+// Rows past M and columns past N are clamped to the last valid one instead
+// of masked: their results are never stored, and rows do not mix in the
+// product (nor on the Gram diagonal), so the clamped lanes cannot disturb
+// valid outputs.  Only the ragged last k-block (K % KB != 0) is masked.
 #include "fn_device.h"
 #include "fn_launch.h"
 
@@ -32,90 +44,143 @@ struct DecodeArgs {
   float eps;
 };
 
-template <typename T, int MF, int NF, bool SW, int WAVES, int U>
-__global__ __launch_bounds__(kWave * WAVES) void decode_kernel(DecodeArgs a) {
+template <typename T, int MF, int NF, bool SW, int WN, int WK, int U>
+__global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
   constexpr int V = Geo<T>::V;
   constexpr int KB = Geo<T>::KB;
   constexpr int NMAT = SW ? 2 : 1;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  // wave-uniform: loop bounds and weight offsets stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wn = wave % WN;         // column group of this wave
+  const int wk = wave / WN;         // k split of this wave
   const int lrow = lane & 15;       // operand row (x) / column (W') of this lane
   const int lgrp = lane >> 4;       // k group of this lane
-  const int nb0 = blockIdx.x * NF;
+  const int nb0 = (blockIdx.x * WN + wn) * NF;
   const int m0 = blockIdx.y * 16 * MF;
-  const int kb_begin = (int)((int64_t)a.kblocks * wave / WAVES);
-  const int kb_end = (int)((int64_t)a.kblocks * (wave + 1) / WAVES);
+  const int kb_begin = (int)((int64_t)a.kblocks * wk / WK);
+  const int kb_end = (int)((int64_t)a.kblocks * (wk + 1) / WK);
+  const int kb_full = a.K / KB;     // k-blocks with no ragged tail
 
   const T* xrow[MF];
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf) {
-    const int row = m0 + 16 * mf + lrow;
-    xrow[mf] = row < a.M ? static_cast<const T*>(a.x) + (size_t)row * a.K + lgrp * V : nullptr;
+    const int row = min(m0 + 16 * mf + lrow, a.M - 1);
+    xrow[mf] = static_cast<const T*>(a.x) + (size_t)row * a.K + lgrp * V;
   }
   const u32x4* wp[NMAT][NF];
-  bool wok[NF];
 #pragma unroll
   for (int nf = 0; nf < NF; ++nf) {
-    const int nb = nb0 + nf;
-    wok[nf] = nb < a.nblocks;
-    const size_t base = ((size_t)(wok[nf] ? nb : 0) * a.kblocks) * kWave + lane;
+    const size_t base = (size_t)min(nb0 + nf, a.nblocks - 1) * a.kblocks * kWave + lane;
     wp[0][nf] = a.wg + base;
     if (SW) wp[NMAT - 1][nf] = a.wu + base;
   }
 
   f32x4 acc[NMAT][MF][NF];
+  f32x4 gram[MF];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
+  for (int mf = 0; mf < MF; ++mf) {
+    gram[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf)
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) acc[m][mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ss[MF];
-#pragma unroll
-  for (int mf = 0; mf < MF; ++mf) ss[mf] = 0.f;
+  }
 
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int kb = kb_begin; kb < kb_end; kb += U) {
-    u32x4 xv[U][MF];
-    u32x4 wv[U][NMAT][NF];
+  // One stage = U k-blocks of operands in registers.
+  struct Stage {
+    u32x4 x[U][MF];
+    u32x4 w[U][NMAT][NF];
+  };
+  auto load = [&](Stage& s, int kb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = kb + u;
-      const bool kin = k < kb_end;
 #pragma unroll
-      for (int mf = 0; mf < MF; ++mf) {
-        const bool ok = kin && xrow[mf] != nullptr && (k * KB + lgrp * V) < a.K;
-        xv[u][mf] = ok ? *reinterpret_cast<const u32x4*>(xrow[mf] + (size_t)k * KB) : zero;
-      }
+      for (int mf = 0; mf < MF; ++mf)
+        s.x[u][mf] = *reinterpret_cast<const u32x4*>(xrow[mf] + (size_t)(kb + u) * KB);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf)
-          wv[u][m][nf] = (kin && wok[nf]) ? wp[m][nf][(size_t)k * kWave] : zero;
+          s.w[u][m][nf] = __builtin_nontemporal_load(wp[m][nf] + (size_t)(kb + u) * kWave);
     }
+  };
+  auto load1 = [&](Stage& s, int kb) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int mf = 0; mf < MF; ++mf) s.x[0][mf] = *reinterpret_cast<const u32x4*>(xrow[mf] + (size_t)kb * KB);
 #pragma unroll
-      for (int mf = 0; mf < MF; ++mf) {
-        ss[mf] += sumsq16<T>(xv[u][mf]);
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
+      for (int nf = 0; nf < NF; ++nf) s.w[0][m][nf] = __builtin_nontemporal_load(wp[m][nf] + (size_t)kb * kWave);
+  };
+  auto step = [&](const u32x4 (&xv)[MF], const u32x4 (&wv)[NMAT][NF]) {
 #pragma unroll
-          for (int nf = 0; nf < NF; ++nf)
-            acc[m][mf][nf] = mfma_chunk<T>(xv[u][mf], wv[u][m][nf], acc[m][mf][nf]);
+    for (int mf = 0; mf < MF; ++mf) {
+      gram[mf] = mfma_chunk<T>(xv[mf], xv[mf], gram[mf]);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) acc[m][mf][nf] = mfma_chunk<T>(xv[mf], wv[m][nf], acc[m][mf][nf]);
+    }
+  };
+  auto compute = [&](const Stage& s) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) step(s.x[u], s.w[u]);
+  };
+
+  // Double-buffered stream: the loads of the next stage are in flight while
+  // the current one is consumed.  The scheduling barriers keep the compiler
+  // from sinking loads below the matrix instructions that do not need them.
+  auto stream_range = [&](int lo, int hi) {
+    int kb = lo;
+    if (kb + 2 * U <= hi) {
+      Stage s0, s1;
+      load(s0, kb);
+      for (; kb + 4 * U <= hi; kb += 2 * U) {
+        load(s1, kb + U);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(s0, kb + 2 * U);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s1);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      load(s1, kb + U);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(s0);
+      compute(s1);
+      kb += 2 * U;
     }
-  }
+    for (; kb < hi; ++kb) {
+      Stage s;
+      load1(s, kb);
+      step(s.x[0], s.w[0]);
+    }
+  };
 
-  // Each row's partial sum of squares is spread over the four k groups.
+  const int kb_main_end = min(kb_end, kb_full);
+  stream_range(kb_begin, kb_main_end);
+  // The ragged last k-block (K % KB != 0): x is masked past K.
+  for (int kb = max(kb_main_end, kb_begin); kb < kb_end; ++kb) {
+    u32x4 xv[MF];
+    u32x4 wv[NMAT][NF];
+    const bool kin = kb * KB + lgrp * V < a.K;
 #pragma unroll
-  for (int mf = 0; mf < MF; ++mf) {
-    ss[mf] += __shfl_xor(ss[mf], 16);
-    ss[mf] += __shfl_xor(ss[mf], 32);
+    for (int mf = 0; mf < MF; ++mf)
+      xv[mf] = kin ? *reinterpret_cast<const u32x4*>(xrow[mf] + (size_t)kb * KB) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) wv[m][nf] = __builtin_nontemporal_load(wp[m][nf] + (size_t)kb * kWave);
+    step(xv, wv);
   }
 
-  __shared__ float red_acc[WAVES][NMAT][MF][NF][4][kWave];
-  __shared__ float red_ss[WAVES][MF][16];
+  // Partials meet in LDS.  Accumulator element r of lane l is row
+  // 4*(l/16) + r, column l%16 of its 16x16 tile; the Gram diagonal (row ==
+  // column) therefore sits in lanes whose l%16 / 4 == l/16, element l%4.
+  __shared__ float red_acc[WK][WN][NMAT][MF][NF][4][kWave];
+  __shared__ float red_ss[WK][WN][MF][16];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -123,17 +188,20 @@ __global__ __launch_bounds__(kWave * WAVES) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red_acc[wave][m][mf][nf][r][lane] = acc[m][mf][nf][r];
-  if (lgrp == 0) {
+        for (int r = 0; r < 4; ++r) red_acc[wk][wn][m][mf][nf][r][lane] = acc[m][mf][nf][r];
+  if ((lrow >> 2) == lgrp) {
+    const int r = lrow & 3;
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf) red_ss[wave][mf][lrow] = ss[mf];
+    for (int mf = 0; mf < MF; ++mf) {
+      const f32x4 gv = gram[mf];
+      red_ss[wk][wn][mf][lrow] = r == 0 ? gv[0] : (r == 1 ? gv[1] : (r == 2 ? gv[2] : gv[3]));
+    }
   }
   __syncthreads();
 
-  // Epilogue: wave w finishes tiles w, w + WAVES, ...  Accumulator element r
-  // of lane l is row 4*(l/16) + r, column l%16 of the 16x16 tile.
+  // Epilogue: the WK waves of column group wn finish its tiles wk, wk + WK, ...
   const float kf = (float)a.K;
-  for (int t = wave; t < MF * NF; t += WAVES) {
+  for (int t = wk; t < MF * NF; t += WK) {
     const int mf = t / NF, nf = t % NF;
     const int col = (nb0 + nf) * 16 + lrow;
 #pragma unroll
@@ -142,10 +210,10 @@ __global__ __launch_bounds__(kWave * WAVES) void decode_kernel(DecodeArgs a) {
       const int row = m0 + 16 * mf + i;
       float sum_sq = 0.f, p0 = 0.f, p1 = 0.f;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) {
-        sum_sq += red_ss[w][mf][i];
-        p0 += red_acc[w][0][mf][nf][r][lane];
-        if (SW) p1 += red_acc[w][NMAT - 1][mf][nf][r][lane];
+      for (int w = 0; w < WK; ++w) {
+        sum_sq += red_ss[w][wn][mf][i];
+        p0 += red_acc[w][wn][0][mf][nf][r][lane];
+        if (SW) p1 += red_acc[w][wn][NMAT - 1][mf][nf][r][lane];
       }
       if (row < a.M && col < a.N) {
         const float inv = inv_rms(sum_sq, kf, a.eps);
@@ -156,68 +224,69 @@ __global__ __launch_bounds__(kWave * WAVES) void decode_kernel(DecodeArgs a) {
   }
 }
 
-namespace {
+// Kernel instances.  The table maps (dtype, row capacity, SwiGLU) to a tile
+// configuration; launch_decode looks the instance up by the same key.
+struct DecodeInstance {
+  const void* fn;
+  DType dt;
+  int mf, nf, wn, wk, u;
+  bool sw;
+  const char* name;
+};
 
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeUnroll = 4;
-
-template <typename T, int MF, int NF, bool SW>
-const void* decode_fn() {
-  return reinterpret_cast<const void*>(&decode_kernel<T, MF, NF, SW, kDecodeWaves, kDecodeUnroll>);
-}
-
-template <typename T, bool SW>
-const void* pick(int mf, int nf) {
-  if (nf == 1) {
-    if (mf == 1) return decode_fn<T, 1, 1, SW>();
-    if (mf == 2) return decode_fn<T, 2, 1, SW>();
-    return decode_fn<T, 4, 1, SW>();
+#define FN_DECODE(TT, DT, MF, NF, SW, WN, WK, U, NAME)                                                    \
+  DecodeInstance {                                                                                        \
+    reinterpret_cast<const void*>(&decode_kernel<TT, MF, NF, SW, WN, WK, U>), DT, MF, NF, WN, WK, U, SW, NAME \
   }
-  if (mf == 1) return decode_fn<T, 1, 2, SW>();
-  if (mf == 2) return decode_fn<T, 2, 2, SW>();
-  return decode_fn<T, 4, 2, SW>();
-}
 
-const char* decode_name(DType dt, int mf, int nf, bool sw) {
-  static const char* names[2][2][3][2] = {
-      {{{"decode_f32_m16_n16_w4", "decode_f32_m16_n32_w4"},
-        {"decode_f32_m32_n16_w4", "decode_f32_m32_n32_w4"},
-        {"decode_f32_m64_n16_w4", "decode_f32_m64_n32_w4"}},
-       {{"decode_swiglu_f32_m16_n16_w4", "decode_swiglu_f32_m16_n32_w4"},
-        {"decode_swiglu_f32_m32_n16_w4", "decode_swiglu_f32_m32_n32_w4"},
-        {"decode_swiglu_f32_m64_n16_w4", "decode_swiglu_f32_m64_n32_w4"}}},
-      {{{"decode_bf16_m16_n16_w4", "decode_bf16_m16_n32_w4"},
-        {"decode_bf16_m32_n16_w4", "decode_bf16_m32_n32_w4"},
-        {"decode_bf16_m64_n16_w4", "decode_bf16_m64_n32_w4"}},
-       {{"decode_swiglu_bf16_m16_n16_w4", "decode_swiglu_bf16_m16_n32_w4"},
-        {"decode_swiglu_bf16_m32_n16_w4", "decode_swiglu_bf16_m32_n32_w4"},
-        {"decode_swiglu_bf16_m64_n16_w4", "decode_swiglu_bf16_m64_n32_w4"}}}};
-  const int mi = mf == 1 ? 0 : (mf == 2 ? 1 : 2);
-  return names[(int)dt][sw ? 1 : 0][mi][nf - 1];
-}
+// Tile choices measured on MI355X (cold weights, >= 1 GiB rotation): at one
+// row block a single wave per workgroup streaming the whole k range with
+// two 4-k-block stages in flight beats splitting k across waves; at four row
+// blocks (M <= 64) wider column groups cut the x traffic out of L2.
+static const DecodeInstance kDecode[] = {
+    FN_DECODE(__bf16, DType::BF16, 1, 1, false, 1, 1, 4, "decode_bf16_m16_n16_k1_u4"),
+    FN_DECODE(__bf16, DType::BF16, 2, 1, false, 1, 2, 2, "decode_bf16_m32_n16_k2_u2"),
+    FN_DECODE(__bf16, DType::BF16, 4, 2, false, 1, 4, 2, "decode_bf16_m64_n32_k4_u2"),
+    FN_DECODE(__bf16, DType::BF16, 1, 1, true, 1, 1, 2, "decode_swiglu_bf16_m16_n16_k1_u2"),
+    FN_DECODE(__bf16, DType::BF16, 2, 1, true, 1, 2, 2, "decode_swiglu_bf16_m32_n16_k2_u2"),
+    FN_DECODE(__bf16, DType::BF16, 4, 2, true, 2, 4, 2, "decode_swiglu_bf16_m64_n64_k4_u2"),
+    FN_DECODE(float, DType::F32, 1, 1, false, 1, 4, 2, "decode_f32_m16_n16_k4_u2"),
+    FN_DECODE(float, DType::F32, 2, 1, false, 1, 4, 2, "decode_f32_m32_n16_k4_u2"),
+    FN_DECODE(float, DType::F32, 4, 1, false, 1, 4, 2, "decode_f32_m64_n16_k4_u2"),
+    FN_DECODE(float, DType::F32, 1, 1, true, 1, 4, 2, "decode_swiglu_f32_m16_n16_k4_u2"),
+    FN_DECODE(float, DType::F32, 2, 1, true, 1, 4, 2, "decode_swiglu_f32_m32_n16_k4_u2"),
+    FN_DECODE(float, DType::F32, 4, 1, true, 1, 4, 2, "decode_swiglu_f32_m64_n16_k4_u2"),
+};
 
-}  // namespace
+static const DecodeInstance* find_decode(DType dt, int mf, bool sw) {
+  for (const DecodeInstance& d : kDecode)
+    if (d.dt == dt && d.mf == mf && d.sw == sw) return &d;
+  return nullptr;
+}
 
 // M-ladder: the smallest row capacity in {16, 32, 64} that holds M (the
 // ladder idea of [FlashInfer #5668], K23_LADDER, without its upper bound:
-// larger M tiles the rows over grid.y).
+// a larger M tiles the rows over grid.y).
 FusedPlan plan_decode(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
   (void)K;
+  const int mf = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const DecodeInstance* d = find_decode(dt, mf, swiglu);
   FusedPlan p{};
   p.kind = 0;
-  p.mf = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  p.nf = 1;
-  p.waves = kDecodeWaves;
+  p.mf = d->mf;
+  p.nf = d->nf * d->wn;
+  p.waves = d->wn * d->wk;
   const int64_t nblocks = ceil_div(N, 16);
   p.grid = dim3((unsigned)ceil_div(nblocks, p.nf), (unsigned)ceil_div(M, 16 * p.mf), 1);
-  p.block = dim3(kWave * kDecodeWaves, 1, 1);
-  p.name = decode_name(dt, p.mf, p.nf, swiglu);
+  p.block = dim3(kWave * p.waves, 1, 1);
+  p.name = d->name;
   return p;
 }
 
-hipError_t launch_decode(DType dt, const FusedPlan& p, const void* x, const void* wg,
-                         const void* wu, void* y, int M, int K, int N, float eps,
-                         hipStream_t stream) {
+hipError_t launch_decode(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
+                         int M, int K, int N, float eps, hipStream_t stream) {
+  const DecodeInstance* d = find_decode(dt, p.mf, wu != nullptr);
+  if (d == nullptr) return hipErrorInvalidValue;
   DecodeArgs a;
   a.x = x;
   a.wg = static_cast<const u32x4*>(wg);
@@ -229,14 +298,8 @@ hipError_t launch_decode(DType dt, const FusedPlan& p, const void* x, const void
   a.kblocks = (int)ceil_div(K, k_per_block(dt));
   a.nblocks = (int)ceil_div(N, 16);
   a.eps = eps;
-  const bool sw = wu != nullptr;
-  const void* fn;
-  if (dt == DType::BF16)
-    fn = sw ? pick<__bf16, true>(p.mf, p.nf) : pick<__bf16, false>(p.mf, p.nf);
-  else
-    fn = sw ? pick<float, true>(p.mf, p.nf) : pick<float, false>(p.mf, p.nf);
   void* args[] = {&a};
-  return hipLaunchKernel(fn, p.grid, p.block, args, 0, stream);
+  return hipLaunchKernel(d->fn, p.grid, p.block, args, 0, stream);
 }
 
 }  // namespace fn

@@ -28,6 +28,11 @@ hipError_t launch_decode(DType dt, const FusedPlan& plan, const void* x, const v
                          const void* w_up, void* y, int M, int K, int N, float eps,
                          hipStream_t stream);
 
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu);
+hipError_t launch_prefill(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
+                          const void* w_up, void* y, int M, int K, int N, float eps,
+                          hipStream_t stream);
+
 hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
                        int K, int N, hipStream_t stream);
 

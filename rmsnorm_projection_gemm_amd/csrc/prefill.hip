@@ -1,0 +1,264 @@
+// Fused RMSNorm + projection (+ SwiGLU) for many rows (prefill): the
+// compute-bound regime, one launch.
+//
+// A workgroup computes a BM x BN output tile (BM = 16*FM*WM rows, BN =
+// 16*FN*WN columns per weight matrix) with WM x WN waves, each owning a
+// 16*FM x 16*FN sub-tile whose fp32 accumulators stay in registers for the
+// whole k loop.  Operands stream through an NS-stage LDS ring, one 32-wide
+// k-block per stage, filled by direct global-to-LDS buffer loads (no
+// register staging).  Every operand lands in LDS already in MFMA fragment
+// order -- W' because the packed layout is fragment-major, x because each
+// lane of the loading wave fetches exactly the 16 bytes its MFMA lane will
+// own -- so each fragment read is one conflict-free ds_read_b128 at lane*16.
+// Loads past the matrix edges (rows >= M, columns past the packed width,
+// k >= K) use out-of-range buffer offsets, which read as zero.
+//
+// The per-row sum of squares rides along on the VALU from the x fragments
+// already in registers: each of the WN waves that share a row block sums a
+// 1/WN share of its row fragments, and the shares meet in LDS before the
+// epilogue applies 1/RMS (and SiLU * up) to the accumulators and stores
+// ([FlashNorm digest] proposals 1-2; [FlashInfer #5521] "Design" items 1-2,
+// tiles kept resident across the k loop and the SwiGLU applied to the
+// accumulators in registers).
+#include "fn_device.h"
+#include "fn_launch.h"
+
+namespace fn {
+
+struct PrefillArgs {
+  const void* x;
+  const void* wg;    // packed W' (gate for SwiGLU)
+  const void* wu;    // packed W'_up, SwiGLU only
+  void* y;
+  int M, K, N;
+  int kblocks;       // ceil(K / 32)
+  int nblocks;       // ceil(N / 16)
+  float eps;
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Raw buffer descriptor over [base, base + bytes); reads past the end return 0.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+template <int FM, int FN, int WM, int WN, bool SW, int NS>
+__global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a) {
+  constexpr int NW = WM * WN;
+  constexpr int NMAT = SW ? 2 : 1;
+  constexpr int BMF = FM * WM;                   // 16-row fragments per tile
+  constexpr int BNF = FN * WN;                   // 16-column fragments per tile and matrix
+  constexpr int SFR = BMF + NMAT * BNF;          // fragments per stage (one k-block)
+  constexpr int LPW = SFR / NW;                  // loads per wave per stage
+  constexpr int ALPW = BMF / NW;                 // of which x fragments
+  constexpr int SSF = FM / WN;                   // row fragments whose squares this wave sums
+  static_assert(SFR % NW == 0 && BMF % NW == 0 && FM % WN == 0, "tile shape");
+  static_assert(NS >= 2 && NS <= 4 && (NS - 2) * LPW < 64, "stage count");
+
+  // One LDS array per ring slot: the compiler can then tell a read of slot s
+  // from the direct-to-LDS loads still filling the other slots, instead of
+  // waiting for all of them before every read.
+  constexpr int SLOT = SFR * kFragBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[NS > 2 ? SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[NS > 3 ? SLOT : 16];
+  __shared__ float ssbuf[BMF * 16];
+  // slot s is a literal at every call site, so this folds to one array
+  auto slot_ptr = [&](int s) -> uint8_t* { return s == 0 ? ring0 : (s == 1 ? ring1 : (s == 2 ? ring2 : ring3)); };
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / WN, wn = wave % WN;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int m0 = blockIdx.y * BMF * 16;
+  const int nb0 = blockIdx.x * BNF;
+  const int64_t kfrag = (int64_t)a.kblocks * kFragBytes;   // bytes of one packed column block
+
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(static_cast<const __bf16*>(a.x) + (size_t)m0 * a.K, (int64_t)min(BMF * 16, a.M - m0) * a.K * 2);
+  // (two named descriptors: an array of this opaque type would make the
+  // host compilation pass drop the kernel's launch stub)
+  const int64_t wbytes = (int64_t)min(BNF, a.nblocks - nb0) * kfrag;
+  const __amdgpu_buffer_rsrc_t wr0 = make_rsrc(static_cast<const uint8_t*>(a.wg) + nb0 * kfrag, wbytes);
+  const __amdgpu_buffer_rsrc_t wr1 = make_rsrc(static_cast<const uint8_t*>(SW ? a.wu : a.wg) + nb0 * kfrag, wbytes);
+
+  // Fragments this wave loads each stage: f = wave + NW * i.  The first ALPW
+  // are x fragments (row block f), the rest W' fragments.
+  uint32_t xoff[ALPW];    // byte offset of this lane's x chunk at k-block 0
+#pragma unroll
+  for (int i = 0; i < ALPW; ++i) {
+    const int row = 16 * (wave + NW * i) + lrow;
+    xoff[i] = (uint32_t)(row * a.K + lgrp * 8) * 2u;
+  }
+  auto issue = [&](uint8_t* base, int kb) {
+    const bool kin = kb * 32 + lgrp * 8 < a.K;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int f = wave + NW * i;
+      lds_ptr dst = (lds_ptr)(base + f * kFragBytes);
+      if (i < ALPW) {
+        const uint32_t off = kin ? xoff[i] + (uint32_t)kb * 64u : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
+      } else {
+        const int g = f - BMF;
+        const int m = g / BNF, ni = g % BNF;
+        const uint32_t off = kb < a.kblocks ? (uint32_t)((ni * a.kblocks + kb) * kFragBytes + lane * 16) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(m == 0 ? wr0 : wr1, dst, 16, off, 0, 0, 0);
+      }
+    }
+  };
+
+  f32x4 acc[NMAT][FM][FN];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss[SSF];
+#pragma unroll
+  for (int i = 0; i < SSF; ++i) ss[i] = 0.f;
+
+  auto stage = [&](int s, int t) {
+    // k-block t has landed for this wave once at most the NS-2 younger ones
+    // are still in flight; the barrier extends that to every wave and also
+    // retires every wave's reads of the slot about to be refilled.
+    wait_vmcnt<(NS - 2) * LPW>();
+    __builtin_amdgcn_s_barrier();
+    const uint8_t* base = slot_ptr(s);
+    u32x4 av[FM], bv[NMAT][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      av[i] = *reinterpret_cast<const u32x4*>(base + (wm * FM + i) * kFragBytes + lane * 16);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bv[m][j] = *reinterpret_cast<const u32x4*>(base + (BMF + m * BNF + wn * FN + j) * kFragBytes + lane * 16);
+    // refill the slot every wave finished reading before the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    issue(slot_ptr((s + NS - 1) % NS), t + NS - 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      if (i / SSF == wn) ss[i % SSF] += sumsq16<__bf16>(av[i]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[m][i][j] = mfma_chunk<__bf16>(av[i], bv[m][j], acc[m][i][j]);
+    // the slot read here is refilled after the next barrier
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+  };
+
+  issue(ring0, 0);
+  if constexpr (NS > 2) issue(ring1, 1);
+  if constexpr (NS > 3) issue(ring2, 2);
+  const int T = a.kblocks;
+  for (int t0 = 0; t0 < T; t0 += NS) {
+    stage(0, t0);
+    if (t0 + 1 < T) stage(1, t0 + 1);
+    if (NS > 2 && t0 + 2 < T) stage(2, t0 + 2);
+    if (NS > 3 && t0 + 3 < T) stage(3, t0 + 3);
+  }
+  wait_vmcnt<0>();   // retire the zero-filled loads issued past the last k-block
+
+  // Sums of squares: lanes l, l^16, l^32, l^48 hold parts of row l%16.
+#pragma unroll
+  for (int i = 0; i < SSF; ++i) {
+    ss[i] += __shfl_xor(ss[i], 16);
+    ss[i] += __shfl_xor(ss[i], 32);
+    if (lgrp == 0) ssbuf[(wm * FM + wn * SSF + i) * 16 + lrow] = ss[i];
+  }
+  __syncthreads();
+
+  const float kf = (float)a.K;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rl = (wm * FM + i) * 16 + 4 * lgrp + r;   // row within the tile
+      const int row = m0 + rl;
+      const float inv = inv_rms(ssbuf[rl], kf, a.eps);
+      if (row < a.M) {
+        __bf16* yrow = static_cast<__bf16*>(a.y) + (size_t)row * a.N;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = (nb0 + wn * FN + j) * 16 + lrow;
+          if (col < a.N) {
+            const float v = SW ? silu_times(acc[0][i][j][r] * inv, acc[NMAT - 1][i][j][r] * inv)
+                               : acc[0][i][j][r] * inv;
+            Store<__bf16>::one(yrow + col, v);
+          }
+        }
+      }
+    }
+  }
+}
+
+struct PrefillInstance {
+  const void* fn;
+  int fm, fn_, wm, wn, ns;
+  bool sw;
+  const char* name;
+};
+
+#define FN_PREFILL(FM, FN_, WM, WN, SW, NS, NAME) \
+  PrefillInstance{reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, NS>), FM, FN_, WM, WN, NS, SW, NAME}
+
+static const PrefillInstance kPrefill[] = {
+    FN_PREFILL(8, 8, 2, 2, false, 4, "prefill_bf16_256x256_s4"),
+    FN_PREFILL(8, 4, 2, 2, true, 4, "prefill_swiglu_bf16_256x128_s4"),
+};
+
+static const PrefillInstance& pick(bool sw) { return kPrefill[sw ? 1 : 0]; }
+
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
+  (void)dt;
+  (void)K;
+  const PrefillInstance& d = pick(swiglu);
+  FusedPlan p{};
+  p.kind = 1;
+  p.mf = d.fm * d.wm;
+  p.nf = d.fn_ * d.wn;
+  p.waves = d.wm * d.wn;
+  p.grid = dim3((unsigned)ceil_div(ceil_div(N, 16), p.nf), (unsigned)ceil_div(M, 16 * p.mf), 1);
+  p.block = dim3(kWave * p.waves, 1, 1);
+  p.name = d.name;
+  return p;
+}
+
+hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
+                          int M, int K, int N, float eps, hipStream_t stream) {
+  if (dt != DType::BF16) return hipErrorInvalidValue;
+  const PrefillInstance& d = pick(wu != nullptr);
+  PrefillArgs a;
+  a.x = x;
+  a.wg = wg;
+  a.wu = wu;
+  a.y = y;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.kblocks = (int)ceil_div(K, 32);
+  a.nblocks = (int)ceil_div(N, 16);
+  a.eps = eps;
+  void* args[] = {&a};
+  (void)p;
+  return hipLaunchKernel(d.fn, p.grid, p.block, args, 0, stream);
+}
+
+}  // namespace fn

@@ -102,7 +102,8 @@ def test_decode_step_calls(gpu_lib, index):
 
 # ---------------------------------------------------- ragged and edges ---
 RAGGED = [(1, 8, 16), (3, 40, 37), (17, 256, 48), (16, 64, 200), (33, 96, 100), (63, 128, 17),
-          (64, 72, 64), (65, 256, 160), (100, 40, 33), (130, 512, 260), (257, 64, 31)]
+          (64, 72, 64), (65, 256, 160), (100, 40, 33), (130, 512, 260), (257, 64, 31),
+          (300, 136, 530), (513, 1032, 270), (777, 264, 1100)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -175,11 +176,14 @@ def test_row_permutation_bit_exact(gpu_lib):
 
 
 def test_column_concatenation_bit_exact(gpu_lib):
-    inp = W.random_inputs(8, 256, 96, "bf16", seed=14)
+    """Columns are independent: splitting W' by columns splits y, bit for bit
+    (the split sits at 1536 columns, a multiple of every workgroup width)."""
+    inp = W.random_inputs(8, 256, 1632, "bf16", seed=14)
     full = _fold_and_run(gpu_lib, inp.x, inp.g, inp.W, "bf16", 1e-6)
-    left = _fold_and_run(gpu_lib, inp.x, inp.g, np.ascontiguousarray(inp.W[:, :64]), "bf16", 1e-6)
-    right = _fold_and_run(gpu_lib, inp.x, inp.g, np.ascontiguousarray(inp.W[:, 64:]), "bf16", 1e-6)
+    left = _fold_and_run(gpu_lib, inp.x, inp.g, np.ascontiguousarray(inp.W[:, :1536]), "bf16", 1e-6)
+    right = _fold_and_run(gpu_lib, inp.x, inp.g, np.ascontiguousarray(inp.W[:, 1536:]), "bf16", 1e-6)
     assert np.array_equal(full, np.concatenate([left, right], axis=1))
+    assert_close(full, oracle.norm_proj(inp.x, inp.g, inp.W, 1e-6), "bf16", "concat")
 
 
 def test_rne_store(gpu_lib):
