@@ -44,15 +44,36 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     p.add_argument("--hot", action="store_true", help="time a single weight buffer only (no rotation)")
+    p.add_argument("--clock-warmup-s", type=float, default=0.5,
+                   help="untimed seconds of steps before warmup (clock ramp-up); 0 under a profiler")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run 1 GiB device-to-device copies (counter calibration) and exit")
     return p.parse_args(argv)
 
 
 # ----------------------------------------------------------------- timing --
+CLOCK_WARMUP_S = 0.5
+
+
+def clock_warmup(torch, launch):
+    """Run the step untimed for CLOCK_WARMUP_S so the GPU leaves its idle
+    power state before anything is timed (the first ~second runs at lower
+    clocks on MI355X)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while CLOCK_WARMUP_S > 0 and time.perf_counter() - t0 < CLOCK_WARMUP_S:
+        for _ in range(8):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def time_region(torch, launch, steps, warmup):
     """Average ms per step over `steps` back-to-back steps (events on the
-    current stream, which is the stream every launch uses)."""
+    current stream, which is the stream every launch uses), after a clock
+    warm-up and `warmup` untimed steps."""
+    clock_warmup(torch, launch)
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -83,10 +104,15 @@ def pct(sorted_vals, q):
     return sorted_vals[i]
 
 
-def kernel_source_hash():
+# Sources each workload's dominant kernel is built from.
+KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h")}
+DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
+
+
+def kernel_source_hash(workload):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rmsnorm_projection_gemm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES.get(workload, DEFAULT_KERNEL_SOURCES):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -94,13 +120,13 @@ def kernel_source_hash():
 
 def counter_traffic(workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
+    it was taken on the current sources of the workload's kernel; else None."""
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -268,6 +294,8 @@ def calibrate_copy(torch):
 
 def main(argv=None):
     args = parse_args(argv)
+    global CLOCK_WARMUP_S
+    CLOCK_WARMUP_S = args.clock_warmup_s
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: libflashnorm runs on one GPU; "
               "the multi-GPU column split is a design note, not a measured path.", file=sys.stderr)

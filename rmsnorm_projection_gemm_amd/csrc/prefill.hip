@@ -4,7 +4,10 @@
 // A workgroup computes a BM x BN output tile (BM = 16*FM*WM rows, BN =
 // 16*FN*WN columns per weight matrix) with WM x WN waves, each owning a
 // 16*FM x 16*FN sub-tile whose fp32 accumulators stay in registers for the
-// whole k loop.  Operands stream through an NS-stage LDS ring, one 32-wide
+// whole k loop.  The instances use 256x256 tiles (256x128 per matrix for
+// SwiGLU) with eight waves of 64x128, two waves per SIMD, and a 3-slot ring:
+// measured on MI355X this beats four waves of 128x128 by ~40%, the second
+// wave hiding the barrier and LDS latency of the first.  Operands stream through an NS-stage LDS ring, one 32-wide
 // k-block per stage, filled by direct global-to-LDS buffer loads (no
 // register staging).  Every operand lands in LDS already in MFMA fragment
 // order -- W' because the packed layout is fragment-major, x because each
@@ -13,9 +16,12 @@
 // Loads past the matrix edges (rows >= M, columns past the packed width,
 // k >= K) use out-of-range buffer offsets, which read as zero.
 //
-// The per-row sum of squares rides along on the VALU from the x fragments
-// already in registers: each of the WN waves that share a row block sums a
-// 1/WN share of its row fragments, and the shares meet in LDS before the
+// The per-row sum of squares comes from the x fragments already in
+// registers: each of the WN waves that share a row block takes a 1/WN share
+// of its row fragments, either on the VALU (convert and FMA) or, in the
+// instances, as the diagonal of an x x^T MFMA (GRAM), which measured faster
+// than the VALU form once the MFMA pipe is the bottleneck only 1/16 of the
+// time it spends on the projection.  The shares meet in LDS before the
 // epilogue applies 1/RMS (and SiLU * up) to the accumulators and stores
 // ([FlashNorm digest] proposals 1-2; [FlashInfer #5521] "Design" items 1-2,
 // tiles kept resident across the k loop and the SwiGLU applied to the
@@ -53,7 +59,7 @@ __device__ inline void wait_vmcnt() {
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int FM, int FN, int WM, int WN, bool SW, int NS>
+template <int FM, int FN, int WM, int WN, bool SW, int NS, bool GRAM>
 __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = SW ? 2 : 1;
@@ -128,8 +134,12 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss[SSF];
+  f32x4 gram[SSF];
 #pragma unroll
-  for (int i = 0; i < SSF; ++i) ss[i] = 0.f;
+  for (int i = 0; i < SSF; ++i) {
+    ss[i] = 0.f;
+    gram[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto stage = [&](int s, int t) {
     // k-block t has landed for this wave once at most the NS-2 younger ones
@@ -153,7 +163,10 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      if (i / SSF == wn) ss[i % SSF] += sumsq16<__bf16>(av[i]);
+      if (i / SSF == wn) {
+        if (GRAM) gram[i % SSF] = mfma_chunk<__bf16>(av[i], av[i], gram[i % SSF]);
+        else ss[i % SSF] += sumsq16<__bf16>(av[i]);
+      }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -176,12 +189,22 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   }
   wait_vmcnt<0>();   // retire the zero-filled loads issued past the last k-block
 
-  // Sums of squares: lanes l, l^16, l^32, l^48 hold parts of row l%16.
+  // Sums of squares.  VALU form: lanes l, l^16, l^32, l^48 hold parts of
+  // row l%16.  Gram form: the diagonal of x x^T, element l%4 of the lanes
+  // whose (l%16)/4 == l/16.
 #pragma unroll
   for (int i = 0; i < SSF; ++i) {
-    ss[i] += __shfl_xor(ss[i], 16);
-    ss[i] += __shfl_xor(ss[i], 32);
-    if (lgrp == 0) ssbuf[(wm * FM + wn * SSF + i) * 16 + lrow] = ss[i];
+    if (GRAM) {
+      if ((lrow >> 2) == lgrp) {
+        const int r = lrow & 3;
+        const f32x4 gv = gram[i];
+        ssbuf[(wm * FM + wn * SSF + i) * 16 + lrow] = r == 0 ? gv[0] : (r == 1 ? gv[1] : (r == 2 ? gv[2] : gv[3]));
+      }
+    } else {
+      ss[i] += __shfl_xor(ss[i], 16);
+      ss[i] += __shfl_xor(ss[i], 32);
+      if (lgrp == 0) ssbuf[(wm * FM + wn * SSF + i) * 16 + lrow] = ss[i];
+    }
   }
   __syncthreads();
 
@@ -216,12 +239,12 @@ struct PrefillInstance {
   const char* name;
 };
 
-#define FN_PREFILL(FM, FN_, WM, WN, SW, NS, NAME) \
-  PrefillInstance{reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, NS>), FM, FN_, WM, WN, NS, SW, NAME}
+#define FN_PREFILL(FM, FN_, WM, WN, SW, NS, GRAM, NAME) \
+  PrefillInstance{reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, NS, GRAM>), FM, FN_, WM, WN, NS, SW, NAME}
 
 static const PrefillInstance kPrefill[] = {
-    FN_PREFILL(8, 8, 2, 2, false, 4, "prefill_bf16_256x256_s4"),
-    FN_PREFILL(8, 4, 2, 2, true, 4, "prefill_swiglu_bf16_256x128_s4"),
+    FN_PREFILL(4, 8, 4, 2, false, 3, true, "prefill_bf16_256x256_w4x2_s3"),
+    FN_PREFILL(4, 4, 4, 2, true, 3, true, "prefill_swiglu_bf16_256x128_w4x2_s3"),
 };
 
 static const PrefillInstance& pick(bool sw) { return kPrefill[sw ? 1 : 0]; }
