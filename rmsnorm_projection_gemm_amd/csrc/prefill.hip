@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[NS > 3 ? SLOT : 16];
   __shared__ float ssbuf[BMF * 16];
   // slot s is a literal at every call site, so this folds to one array
-  auto slot_ptr = [&](int s) -> uint8_t* { return s == 0 ? ring0 : (s == 1 ? ring1 : (s == 2 ? ring2 : ring3)); };
+  auto slot_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* { return s == 0 ? ring0 : (s == 1 ? ring1 : (s == 2 ? ring2 : ring3)); };
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -108,19 +108,21 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     const int row = 16 * (wave + NW * i) + lrow;
     xoff[i] = (uint32_t)(row * a.K + lgrp * 8) * 2u;
   }
-  auto issue = [&](uint8_t* base, int kb) {
-    const bool kin = kb * 32 + lgrp * 8 < a.K;
+  auto issue = [&](uint8_t* base, int kb) __attribute__((always_inline)) {
+    // all-ones while in range, else zero: out-of-range offsets read as zero
+    const uint32_t xin = (uint32_t)((kb * 32 + lgrp * 8 - a.K) >> 31);
+    const uint32_t win = (uint32_t)((kb - a.kblocks) >> 31);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int f = wave + NW * i;
       lds_ptr dst = (lds_ptr)(base + f * kFragBytes);
       if (i < ALPW) {
-        const uint32_t off = kin ? xoff[i] + (uint32_t)kb * 64u : kOutOfRange;
+        const uint32_t off = ((xoff[i] + (uint32_t)kb * 64u) & xin) | (kOutOfRange & ~xin);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
       } else {
         const int g = f - BMF;
         const int m = g / BNF, ni = g % BNF;
-        const uint32_t off = kb < a.kblocks ? (uint32_t)((ni * a.kblocks + kb) * kFragBytes + lane * 16) : kOutOfRange;
+        const uint32_t off = ((uint32_t)((ni * a.kblocks + kb) * kFragBytes + lane * 16) & win) | (kOutOfRange & ~win);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(m == 0 ? wr0 : wr1, dst, 16, off, 0, 0, 0);
       }
     }
@@ -141,51 +143,101 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     gram[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto stage = [&](int s, int t) {
-    // k-block t has landed for this wave once at most the NS-2 younger ones
-    // are still in flight; the barrier extends that to every wave and also
-    // retires every wave's reads of the slot about to be refilled.
-    wait_vmcnt<(NS - 2) * LPW>();
-    __builtin_amdgcn_s_barrier();
-    const uint8_t* base = slot_ptr(s);
-    u32x4 av[FM], bv[NMAT][FN];
+  // Register plan: x fragments of two consecutive k-blocks (two sets), one
+  // set of W' fragments.  The MFMAs of k-block t run column by column, so the
+  // first half of the W' fragments is free by mid-step: there, after the
+  // barrier for k-block t+1, go the reads of t+1's x fragments and first W'
+  // half plus the refill of the slot t came from; t+1's second W' half is read
+  // once t's second half has been issued.  LDS latency and the barrier thus
+  // hide behind matrix work instead of stalling it.
+  constexpr int NB = NMAT * FN;            // W' fragments per wave and k-block
+  u32x4 av[2][FM], bv[NB];
+  auto read_a = [&](int r, const uint8_t* base) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      av[i] = *reinterpret_cast<const u32x4*>(base + (wm * FM + i) * kFragBytes + lane * 16);
+      av[r][i] = *reinterpret_cast<const u32x4*>(base + (wm * FM + i) * kFragBytes + lane * 16);
+  };
+  auto read_b = [&](int j0, int j1, const uint8_t* base) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int j = j0; j < j1; ++j) {
+      const int m = j / FN, jj = j % FN;
+      bv[j] = *reinterpret_cast<const u32x4*>(base + (BMF + m * BNF + wn * FN + jj) * kFragBytes + lane * 16);
+    }
+  };
+  auto mfma_cols = [&](int r, int j0, int j1) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bv[m][j] = *reinterpret_cast<const u32x4*>(base + (BMF + m * BNF + wn * FN + j) * kFragBytes + lane * 16);
-    // refill the slot every wave finished reading before the barrier
-    __builtin_amdgcn_sched_barrier(0);
-    issue(slot_ptr((s + NS - 1) % NS), t + NS - 1);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int j = j0; j < j1; ++j)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) acc[j / FN][i][j % FN] = mfma_chunk<__bf16>(av[r][i], bv[j], acc[j / FN][i][j % FN]);
+  };
+  auto squares = [&](int r) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
       if (i / SSF == wn) {
-        if (GRAM) gram[i % SSF] = mfma_chunk<__bf16>(av[i], av[i], gram[i % SSF]);
-        else ss[i % SSF] += sumsq16<__bf16>(av[i]);
+        if (GRAM) gram[i % SSF] = mfma_chunk<__bf16>(av[r][i], av[r][i], gram[i % SSF]);
+        else ss[i % SSF] += sumsq16<__bf16>(av[r][i]);
       }
+  };
+  // k-block t (in slot s, x operands in register set r).  Memory instructions
+  // are spread between the MFMAs (scheduling groups) instead of issued in
+  // bursts.  The body has no branches, so the compiler can tell the slot being
+  // read from the slots still being filled and adds no wait of its own.
+  auto step = [&](int s, int r, int t) __attribute__((always_inline)) {
+    const uint8_t* cur = slot_ptr(s);
+    const uint8_t* next = slot_ptr((s + 1) % NS);
+    // first half: W' columns 0..NB/2 of t, while t's other W' half is read
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_cols(r, 0, NB / 2);
+    read_b(NB / 2, NB, cur);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[m][i][j] = mfma_chunk<__bf16>(av[i], bv[m][j], acc[m][i][j]);
-    // the slot read here is refilled after the next barrier
+    for (int g = 0; g < NB / 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);       // FM MFMAs
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Every read of slot s has returned before the barrier; k-block t+1 has
+    // landed for this wave once at most the NS-2 younger ones are in flight,
+    // and the barrier extends both to every wave.
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    wait_vmcnt<(NS - 2) * LPW>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // second half: t's other W' columns and squares, while t+1's x fragments
+    // and first W' half are read and slot s is refilled with k-block t+NS
+    read_a(r ^ 1, next);
+    read_b(0, NB / 2, next);
+    mfma_cols(r, NB / 2, NB);
+    squares(r);
+    issue(slot_ptr(s), t + NS);
+#pragma unroll
+    for (int g = 0; g < FM + NB / 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+    }
+#pragma unroll
+    for (int g = 0; g < LPW; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);        // one global-to-LDS load
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        // two MFMAs
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
+  static_assert(NS == 4, "the unrolled schedule below assumes four ring slots");
   issue(ring0, 0);
-  if constexpr (NS > 2) issue(ring1, 1);
-  if constexpr (NS > 3) issue(ring2, 2);
-  const int T = a.kblocks;
-  for (int t0 = 0; t0 < T; t0 += NS) {
-    stage(0, t0);
-    if (t0 + 1 < T) stage(1, t0 + 1);
-    if (NS > 2 && t0 + 2 < T) stage(2, t0 + 2);
-    if (NS > 3 && t0 + 3 < T) stage(3, t0 + 3);
+  issue(ring1, 1);
+  issue(ring2, 2);
+  issue(ring3, 3);
+  wait_vmcnt<(NS - 1) * LPW>();
+  __builtin_amdgcn_s_barrier();
+  read_a(0, ring0);
+  read_b(0, NB / 2, ring0);
+  // k-blocks past the last one are zero-filled, so rounding the trip count up
+  // to whole rounds of the ring adds only zero products.
+  for (int t = 0; t < a.kblocks; t += 4) {
+    step(0, 0, t);
+    step(1, 1, t + 1);
+    step(2, 0, t + 2);
+    step(3, 1, t + 3);
   }
   wait_vmcnt<0>();   // retire the zero-filled loads issued past the last k-block
 
@@ -243,8 +295,8 @@ struct PrefillInstance {
   PrefillInstance{reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, NS, GRAM>), FM, FN_, WM, WN, NS, SW, NAME}
 
 static const PrefillInstance kPrefill[] = {
-    FN_PREFILL(4, 8, 4, 2, false, 3, true, "prefill_bf16_256x256_w4x2_s3"),
-    FN_PREFILL(4, 4, 4, 2, true, 3, true, "prefill_swiglu_bf16_256x128_w4x2_s3"),
+    FN_PREFILL(4, 8, 4, 2, false, 4, true, "prefill_bf16_256x256_w4x2_s4"),
+    FN_PREFILL(4, 4, 4, 2, true, 4, true, "prefill_swiglu_bf16_256x128_w4x2_s4"),
 };
 
 static const PrefillInstance& pick(bool sw) { return kPrefill[sw ? 1 : 0]; }
