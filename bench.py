@@ -105,7 +105,7 @@ def pct(sorted_vals, q):
 
 
 # Sources each workload's dominant kernel is built from.
-KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h")}
+KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": ("decode_x.hip", "fn_device.h")}
 DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
 
 

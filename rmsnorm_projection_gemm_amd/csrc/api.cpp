@@ -100,17 +100,21 @@ fn_status fused_common(const void* x, const void* wg, const void* wu, void* y, i
 
 namespace fn {
 
-// Rows up to 64 take the skinny decode kernel (weight streaming, HBM-bound);
-// more rows take the tiled prefill kernel (MFMA-bound), which has a bf16
-// instance only.  fp32 at any M stays on the decode kernel, tiled over rows.
+// The row ladder.  bf16: up to 16 rows the skinny decode kernel with x in
+// registers; 17..64 rows the decode kernel that shares x through LDS (both
+// weight streaming, HBM-bound); more rows the tiled prefill kernel
+// (MFMA-bound).  fp32 at any M stays on the register decode kernel, tiled
+// over rows.
 FusedPlan plan_fused(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
   if (dt == DType::BF16 && M > 64) return plan_prefill(dt, M, K, N, swiglu);
+  if (dt == DType::BF16 && M > 16) return plan_decode_x(dt, M, K, N, swiglu);
   return plan_decode(dt, M, K, N, swiglu);
 }
 
 hipError_t launch_fused(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
                         const void* w_up, void* y, int M, int K, int N, float eps, hipStream_t stream) {
   if (plan.kind == 1) return launch_prefill(dt, plan, x, w_gate, w_up, y, M, K, N, eps, stream);
+  if (plan.kind == 2) return launch_decode_x(dt, plan, x, w_gate, w_up, y, M, K, N, eps, stream);
   return launch_decode(dt, plan, x, w_gate, w_up, y, M, K, N, eps, stream);
 }
 

@@ -13,11 +13,12 @@
 // the same columns of W'_gate and W'_up) and MF 16-row blocks of x.  Its
 // WN*WK waves form WN column groups of NF blocks each and WK k-splits; every
 // wave streams its share of W' from HBM exactly once, with non-temporal
-// loads so W' does not evict x from the caches.  The WN waves of one k-split
-// read the same x addresses at nearly the same time, so x crosses from L2 to
-// the CU once per workgroup rather than once per wave: x traffic out of L2,
-// not HBM, is what limits this kernel once M reaches 64.  W' uses the packed fragment layout: each lane's weight operand is
-// one 16-byte load and a wave reads 1 KiB of contiguous memory per fragment.
+// loads so W' does not evict x from the caches, and loads the x fragments it
+// needs into its own registers.  That suits up to 16 rows, where x is a
+// small fraction of the bytes each CU moves; bf16 with more rows shares x
+// through LDS instead (decode_x.hip).  W' uses the packed fragment layout:
+// each lane's weight operand is one 16-byte load and a wave reads 1 KiB of
+// contiguous memory per fragment.
 //
 // In this regime the matrix cores idle while W' streams in, and every VALU
 // instruction costs four cycles per wave on the critical path.  So the sum of
@@ -241,15 +242,12 @@ struct DecodeInstance {
 
 // Tile choices measured on MI355X (cold weights, >= 1 GiB rotation): at one
 // row block a single wave per workgroup streaming the whole k range with
-// two 4-k-block stages in flight beats splitting k across waves; at four row
-// blocks (M <= 64) wider column groups cut the x traffic out of L2.
+// two 4-k-block stages in flight beats splitting k across waves.  bf16 with
+// more than 16 rows goes to the kernel that shares x through LDS
+// (decode_x.hip); fp32 keeps all three rungs here.
 static const DecodeInstance kDecode[] = {
     FN_DECODE(__bf16, DType::BF16, 1, 1, false, 1, 1, 4, "decode_bf16_m16_n16_k1_u4"),
-    FN_DECODE(__bf16, DType::BF16, 2, 1, false, 1, 2, 2, "decode_bf16_m32_n16_k2_u2"),
-    FN_DECODE(__bf16, DType::BF16, 4, 2, false, 1, 4, 2, "decode_bf16_m64_n32_k4_u2"),
     FN_DECODE(__bf16, DType::BF16, 1, 1, true, 1, 1, 2, "decode_swiglu_bf16_m16_n16_k1_u2"),
-    FN_DECODE(__bf16, DType::BF16, 2, 1, true, 1, 2, 2, "decode_swiglu_bf16_m32_n16_k2_u2"),
-    FN_DECODE(__bf16, DType::BF16, 4, 2, true, 2, 4, 2, "decode_swiglu_bf16_m64_n64_k4_u2"),
     FN_DECODE(float, DType::F32, 1, 1, false, 1, 4, 2, "decode_f32_m16_n16_k4_u2"),
     FN_DECODE(float, DType::F32, 2, 1, false, 1, 4, 2, "decode_f32_m32_n16_k4_u2"),
     FN_DECODE(float, DType::F32, 4, 1, false, 1, 4, 2, "decode_f32_m64_n16_k4_u2"),
@@ -271,6 +269,7 @@ FusedPlan plan_decode(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
   (void)K;
   const int mf = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   const DecodeInstance* d = find_decode(dt, mf, swiglu);
+  if (d == nullptr) d = find_decode(dt, 1, swiglu);   // bf16 above 16 rows: tiled over grid.y
   FusedPlan p{};
   p.kind = 0;
   p.mf = d->mf;

@@ -13,7 +13,7 @@ inline int k_per_block(DType t) { return t == DType::F32 ? 16 : 32; }   // KB of
 
 // Kernel instance chosen for one fused call.
 struct FusedPlan {
-  int kind;           // 0 = decode (skinny M), 1 = prefill (tiled)
+  int kind;           // 0 = decode (<= 16 rows, or fp32), 1 = prefill (tiled), 2 = decode with x in LDS
   int mf;             // 16-row fragments per workgroup (decode)
   int nf;             // 16-column fragments per workgroup (decode)
   int waves;          // waves per workgroup
@@ -27,6 +27,11 @@ FusedPlan plan_decode(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu);
 hipError_t launch_decode(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
                          const void* w_up, void* y, int M, int K, int N, float eps,
                          hipStream_t stream);
+
+FusedPlan plan_decode_x(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu);
+hipError_t launch_decode_x(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
+                           const void* w_up, void* y, int M, int K, int N, float eps,
+                           hipStream_t stream);
 
 FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu);
 hipError_t launch_prefill(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,

@@ -101,7 +101,8 @@ def test_decode_step_calls(gpu_lib, index):
 
 
 # ---------------------------------------------------- ragged and edges ---
-RAGGED = [(1, 8, 16), (3, 40, 37), (17, 256, 48), (16, 64, 200), (33, 96, 100), (63, 128, 17),
+RAGGED = [(1, 8, 16), (3, 40, 37), (17, 256, 48), (16, 64, 200), (24, 8, 1), (32, 1032, 270),
+          (33, 96, 100), (40, 1032, 270), (48, 520, 33), (61, 4104, 530), (63, 128, 17),
           (64, 72, 64), (65, 256, 160), (100, 40, 33), (130, 512, 260), (257, 64, 31),
           (300, 136, 530), (513, 1032, 270), (777, 264, 1100)]
 
