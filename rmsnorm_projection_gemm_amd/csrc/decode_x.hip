@@ -23,13 +23,12 @@
 // stage a few Gram MFMAs (x x^T of the fragments it loaded) whose diagonals
 // are partial sums of squares ([FlashNorm digest] proposal 2: the sum of
 // squares comes from the operands of the product, not from a second pass).
-// Partials of the k-splits and of the Gram diagonals meet in LDS for the
-// epilogue: 1/RMS, SiLU(gate) * up for SwiGLU ([FlashInfer #5521] "Design"
-// item 2), one RNE store.
+// The Gram diagonals meet in LDS for the epilogue: 1/RMS, SiLU(gate) * up
+// for SwiGLU ([FlashInfer #5521] "Design" item 2), one RNE store.
 //
 // Edges: rows past M and k past K read as zero (buffer offsets out of
-// range), and so do the k-blocks of a k-split past its range; column blocks
-// past N read as zero and are not stored.
+// range), and so do the stages past the last that fill the final round of
+// the ring; column blocks past N read as zero and are not stored.
 #include "fn_device.h"
 #include "fn_launch.h"
 
@@ -43,7 +42,7 @@ struct DecodeXArgs {
   int M, K, N;
   int kblocks;       // ceil(K / 32)
   int nblocks;       // ceil(N / 16)
-  int spg;           // stages per k-split, a multiple of the ring depth
+  int stages;        // ceil(kblocks / U)
   float eps;
 };
 
@@ -63,48 +62,38 @@ __device__ inline void wait_vmcnt_x() {
 constexpr uint32_t kOutOfRangeX = 0x80000000u;
 
 // MF: 16-row blocks of x.  NC: 16-column blocks per wave (for SwiGLU each
-// with its gate and up stream).  NWV: waves per k-split, sharing its x
-// fragments.  WK: k-splits.  U: k-blocks per stage.
-template <int MF, int NC, int NWV, int WK, bool SW, int U>
-__global__ __launch_bounds__(kWave * NWV * WK) void decode_x_kernel(DecodeXArgs a) {
+// with its gate and up stream).  NWV: waves, sharing the x fragments.  U:
+// k-blocks per stage.
+template <int MF, int NC, int NWV, bool SW, int U>
+__global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   constexpr int NS = 4;                    // LDS ring slots
   constexpr int D = NS - 1;                // stages in flight
   constexpr int NMAT = SW ? 2 : 1;
   constexpr int NST = NMAT * NC;           // weight streams per wave
-  constexpr int XF = U * MF;               // x fragments per stage
-  constexpr int XPW = XF / NWV;            // x fragments each wave loads per stage
+  constexpr int XF = U * MF;               // x loads (1 KiB each) per stage
+  constexpr int XPW = (XF + NWV - 1) / NWV;   // x loads each wave issues per stage
   constexpr int LPW = U * NST + XPW;       // vector-memory ops per wave per stage
-  constexpr int GR = MF > NWV ? MF / NWV : 1;   // Gram accumulators per wave
-  constexpr int SLOT = WK * XF * kFragBytes;
+  // Loads q >= XF (when NWV does not divide XF) fetch nothing and write
+  // zeros into the slot's padding, so every wave issues the same count.
+  constexpr int SLOT = XPW * NWV * kFragBytes;
   static_assert(U % 2 == 0, "each x load moves two k-blocks of 8 rows");
-  static_assert(XF % NWV == 0, "x fragments must split evenly across the waves");
-  static_assert(NWV % MF == 0 || MF % NWV == 0, "Gram row blocks must map statically");
   static_assert((D - 1) * LPW < 64, "vmcnt range");
-  static_assert(NS * SLOT + (WK - 1) * NWV * NST * MF * 4 * kWave * 4 + NWV * WK * GR * 16 * 4 <= 160 * 1024,
-                "LDS budget");
+  static_assert(NS * SLOT + NWV * XPW * 16 * 4 <= 160 * 1024, "LDS budget");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[SLOT];
-  __shared__ float red[(WK - 1) * NWV * NST * MF * 4 * kWave + 1];   // k-split partials
-  __shared__ float ssp[NWV * WK][GR][16];                              // Gram diagonals
+  __shared__ float ssp[NWV][XPW][16];      // Gram diagonals
   auto slot_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
     return s == 0 ? ring0 : (s == 1 ? ring1 : (s == 2 ? ring2 : ring3));
   };
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int w = wave % NWV;                // wave within the k-split
-  const int g = wave / NWV;                // k-split
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int nb0 = (blockIdx.x * NWV + w) * NC;   // first column block of this wave
-  const int st0 = g * a.spg;               // first stage of this k-split
-  const int goff = g * XF * kFragBytes;    // this k-split's part of a slot
   const int64_t kfrag = (int64_t)a.kblocks * kFragBytes;
-  auto red_at = [&](int h, int c, int i, int r) __attribute__((always_inline)) -> float& {
-    return red[((((h * NWV + w) * NST + c) * MF + i) * 4 + r) * kWave + lane];
-  };
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc_x(a.x, (int64_t)min(MF * 16, a.M) * a.K * 2);
   // weight stream c = m * NC + j: matrix m, column block nb0 + j (reads zero past N)
@@ -123,6 +112,8 @@ __global__ __launch_bounds__(kWave * NWV * WK) void decode_x_kernel(DecodeXArgs 
   // q = w + NWV*i issued by wave w.  Load q covers rows 8*(q%2) .. +7 of row
   // block (q/2) % MF and k-blocks 2*(q / (2*MF)) .. +1 of the stage; lane l
   // brings row l/8 of those, chunk (l%8) ^ (row/2) of its 8 16-byte chunks.
+  // The same numbering, q = u*MF + i, names the MFMA fragment (k-block u,
+  // row block i) whose Gram block wave q % NWV accumulates.
   uint32_t xoff[XPW];
   int xk[XPW];
 #pragma unroll
@@ -131,34 +122,39 @@ __global__ __launch_bounds__(kWave * NWV * WK) void decode_x_kernel(DecodeXArgs 
     const int lr = 8 * (q & 1) + (lane >> 3);
     const int c = (lane & 7) ^ (lr >> 1);
     const int row = 16 * ((q >> 1) % MF) + lr;
-    xk[i] = (2 * (q / (2 * MF)) + (c >> 2)) * 32 + (c & 3) * 8;
-    xoff[i] = (uint32_t)(row * a.K + xk[i]) * 2u;
+    xk[i] = q < XF ? (2 * (q / (2 * MF)) + (c >> 2)) * 32 + (c & 3) * 8 : 1 << 30;   // past XF: never in range
+    xoff[i] = (uint32_t)(row * a.K + (q < XF ? xk[i] : 0)) * 2u;
   }
   // LDS offset of this lane's MFMA operand (row lrow, chunk lgrp) for
   // k-block u, row block i of a stage
   auto x_at = [&](int u, int i) __attribute__((always_inline)) -> int {
-    const int p = ((u & 1) * 4 + lgrp) ^ (lrow >> 1);
-    return ((u >> 1) * 2 * MF + 2 * i + (lrow >> 3)) * kFragBytes + (lrow & 7) * 128 + p * 16;
+    const int c = ((u & 1) * 4 + lgrp) ^ (lrow >> 1);
+    return ((u >> 1) * 2 * MF + 2 * i + (lrow >> 3)) * kFragBytes + (lrow & 7) * 128 + c * 16;
   };
-  // Issue stage st (local to the k-split) into slot base; stages past the
-  // k-split's range, and k past K, read as zero without touching memory.
+  // LDS offset of fragment q of a stage (for the Gram blocks); past XF, the
+  // zero-filled padding
+  auto frag_at = [&](int q) __attribute__((always_inline)) -> int {
+    return q < XF ? x_at(q / MF, q % MF) : XF * kFragBytes + lane * 16;
+  };
+  // Issue stage st into slot base; stages past the last, and k past K, read
+  // as zero without touching memory.
   auto issue_x = [&](uint8_t* base, int st) __attribute__((always_inline)) {
-    const uint32_t live = (uint32_t)((st - a.spg) >> 31);
+    const uint32_t live = (uint32_t)((st - a.stages) >> 31);
+    const int k0 = st * U * 32;
 #pragma unroll
     for (int i = 0; i < XPW; ++i) {
-      const int q = w + NWV * i;
-      const int k0 = (st0 + st) * U * 32;
       const uint32_t in = live & (uint32_t)((k0 + xk[i] - a.K) >> 31);
       const uint32_t off = ((xoff[i] + (uint32_t)k0 * 2u) & in) | (kOutOfRangeX & ~in);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_x)(base + goff + q * kFragBytes), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_x)(base + (w + NWV * i) * kFragBytes), 16, off, 0, 0,
+                                               0);
     }
   };
   u32x4 wv[NS][U][NST];
   auto issue_w = [&](int b, int st) __attribute__((always_inline)) {
-    const uint32_t live = (uint32_t)((st - a.spg) >> 31);
+    const uint32_t live = (uint32_t)((st - a.stages) >> 31);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t off = (uint32_t)(((st0 + st) * U + u) * kFragBytes + lane * 16);
+      const uint32_t off = (uint32_t)((st * U + u) * kFragBytes + lane * 16);
 #pragma unroll
       for (int c = 0; c < NST; ++c)
         wv[b][u][c] = __builtin_bit_cast(
@@ -167,13 +163,13 @@ __global__ __launch_bounds__(kWave * NWV * WK) void decode_x_kernel(DecodeXArgs 
   };
 
   f32x4 acc[NST][MF];
-  f32x4 gram[GR];
+  f32x4 gram[XPW];
 #pragma unroll
   for (int c = 0; c < NST; ++c)
 #pragma unroll
     for (int i = 0; i < MF; ++i) acc[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int r = 0; r < GR; ++r) gram[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < XPW; ++j) gram[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Stage st lives in ring slot s and W' buffer s.
   auto step = [&](int s, int st) __attribute__((always_inline)) {
@@ -184,17 +180,15 @@ __global__ __launch_bounds__(kWave * NWV * WK) void decode_x_kernel(DecodeXArgs 
     wait_vmcnt_x<(D - 1) * LPW>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* base = slot_ptr(s) + goff;
+    const uint8_t* base = slot_ptr(s);
     u32x4 xv[U][MF];
     u32x4 xg[XPW];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < MF; ++i)
-        xv[u][i] = *reinterpret_cast<const u32x4*>(base + x_at(u, i));
+      for (int i = 0; i < MF; ++i) xv[u][i] = *reinterpret_cast<const u32x4*>(base + x_at(u, i));
 #pragma unroll
-    for (int j = 0; j < XPW; ++j)
-      xg[j] = *reinterpret_cast<const u32x4*>(base + x_at((w + NWV * j) / MF, (w + NWV * j) % MF));
+    for (int j = 0; j < XPW; ++j) xg[j] = *reinterpret_cast<const u32x4*>(base + frag_at(w + NWV * j));
     __builtin_amdgcn_sched_barrier(0);
     issue_w((s + D) % NS, st + D);
     issue_x(slot_ptr((s + D) % NS), st + D);
@@ -205,10 +199,8 @@ __global__ __launch_bounds__(kWave * NWV * WK) void decode_x_kernel(DecodeXArgs 
       for (int i = 0; i < MF; ++i)
 #pragma unroll
         for (int c = 0; c < NST; ++c) acc[c][i] = mfma_chunk<__bf16>(xv[u][i], wv[s][u][c], acc[c][i]);
-    // fragment w + NWV*j belongs to row block (w + NWV*j) % MF, which is
-    // w + NWV*(j % GR) when NWV divides MF and w % MF otherwise
 #pragma unroll
-    for (int j = 0; j < XPW; ++j) gram[j % GR] = mfma_chunk<__bf16>(xg[j], xg[j], gram[j % GR]);
+    for (int j = 0; j < XPW; ++j) gram[j] = mfma_chunk<__bf16>(xg[j], xg[j], gram[j]);
   };
 
 #pragma unroll
@@ -217,7 +209,8 @@ __global__ __launch_bounds__(kWave * NWV * WK) void decode_x_kernel(DecodeXArgs 
     issue_x(slot_ptr(p), p);
     __builtin_amdgcn_sched_barrier(0);   // keep the loop's load order: W', then x
   }
-  for (int st = 0; st < a.spg; st += NS) {
+  // whole rounds of the ring; stages past the last read as zero
+  for (int st = 0; st < a.stages; st += NS) {
     step(0, st);
     step(1, st + 1);
     step(2, st + 2);
@@ -225,32 +218,15 @@ __global__ __launch_bounds__(kWave * NWV * WK) void decode_x_kernel(DecodeXArgs 
   }
   wait_vmcnt_x<0>();
 
-  // Accumulator element r of lane l is row 4*(l/16) + r, column l%16 of its
+  // Accumulator element e of lane l is row 4*(l/16) + e, column l%16 of its
   // 16x16 tile, so the Gram diagonal sits in lanes with (l%16)/4 == l/16.
   if ((lrow >> 2) == lgrp) {
     const int e = lrow & 3;
 #pragma unroll
-    for (int r = 0; r < GR; ++r)
-      ssp[wave][r][lrow] = e == 0 ? gram[r][0] : (e == 1 ? gram[r][1] : (e == 2 ? gram[r][2] : gram[r][3]));
-  }
-  if (g > 0) {
-#pragma unroll
-    for (int c = 0; c < NST; ++c)
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red_at(g - 1, c, i, r) = acc[c][i][r];
+    for (int j = 0; j < XPW; ++j)
+      ssp[w][j][lrow] = e == 0 ? gram[j][0] : (e == 1 ? gram[j][1] : (e == 2 ? gram[j][2] : gram[j][3]));
   }
   __syncthreads();
-  if (g > 0) return;
-#pragma unroll
-  for (int h = 0; h < WK - 1; ++h)
-#pragma unroll
-    for (int c = 0; c < NST; ++c)
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[c][i][r] += red_at(h, c, i, r);
 
   const float kf = (float)a.K;
 #pragma unroll
@@ -259,14 +235,13 @@ __global__ __launch_bounds__(kWave * NWV * WK) void decode_x_kernel(DecodeXArgs 
     for (int e = 0; e < 4; ++e) {
       const int rr = 4 * lgrp + e;
       const int row = 16 * i + rr;
-      // Gram accumulator r of wave v (any k-split) covers row block
-      // (v % NWV + NWV * r) % MF
+      // Gram accumulator j of wave v holds fragment q = v + NWV*j, row block q % MF
       float ss = 0.f;
 #pragma unroll
-      for (int v = 0; v < NWV * WK; ++v)
+      for (int v = 0; v < NWV; ++v)
 #pragma unroll
-        for (int r = 0; r < GR; ++r)
-          if ((v % NWV + NWV * r) % MF == i) ss += ssp[v][r][rr];
+        for (int j = 0; j < XPW; ++j)
+          if (v + NWV * j < XF && (v + NWV * j) % MF == i) ss += ssp[v][j][rr];
       const float inv = inv_rms(ss, kf, a.eps);
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
@@ -282,37 +257,53 @@ __global__ __launch_bounds__(kWave * NWV * WK) void decode_x_kernel(DecodeXArgs 
 
 struct DecodeXInstance {
   const void* fn;
-  int mf, nc, nwv, wk, u;
+  int mf, nc, nwv, u;
   bool sw;
   const char* name;
 };
 
-#define FN_DECODE_X(MF, NC, NWV, WK, SW, U, NAME)                                                         \
-  DecodeXInstance {                                                                                      \
-    reinterpret_cast<const void*>(&decode_x_kernel<MF, NC, NWV, WK, SW, U>), MF, NC, NWV, WK, U, SW, NAME \
-  }
+#define FN_DECODE_X(MF, NC, NWV, SW, U, NAME) \
+  DecodeXInstance { reinterpret_cast<const void*>(&decode_x_kernel<MF, NC, NWV, SW, U>), MF, NC, NWV, U, SW, NAME }
 
-// Measured on MI355X (cold weights): four one-column-block waves per
-// workgroup sharing two-k-block stages beat wider waves, deeper stages,
-// more waves per workgroup and k-splits inside the workgroup, at both 32
-// and 64 rows.
+inline hipError_t launch_decode_x_instance(const DecodeXInstance& d, const void* x, const void* wg, const void* wu,
+                                           void* y, int M, int K, int N, float eps, hipStream_t stream) {
+  DecodeXArgs a;
+  a.x = x;
+  a.wg = wg;
+  a.wu = wu;
+  a.y = y;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.kblocks = (int)ceil_div(K, 32);
+  a.nblocks = (int)ceil_div(N, 16);
+  a.stages = (int)ceil_div(a.kblocks, d.u);
+  a.eps = eps;
+  void* args[] = {&a};
+  return hipLaunchKernel(d.fn, dim3((unsigned)ceil_div(a.nblocks, d.nc * d.nwv)), dim3(kWave * d.nwv), args, 0,
+                         stream);
+}
+
+#ifndef FN_DECODE_X_NO_TABLE
+// Measured on MI355X (cold weights): three one-column-block waves per
+// workgroup, two-k-block stages.  A skinny kernel is bounded by each CU's
+// vector-memory request rate, so what counts is the bytes each CU moves and
+// that every CU moves some: three column blocks per workgroup give 256
+// workgroups for 12288 columns (one per CU) and 230 for 11008, with each CU
+// fetching x once per three weight streams.  Four waves (192 and 172
+// workgroups) measured 10-15% slower, two waves slower still; wider waves,
+// deeper stages and k-splits inside the workgroup did not help.
 static const DecodeXInstance kDecodeX[] = {
-    FN_DECODE_X(2, 1, 4, 1, false, 2, "decode_bf16_m32_xlds_w4_u2"),
-    FN_DECODE_X(4, 1, 4, 1, false, 2, "decode_bf16_m64_xlds_w4_u2"),
-    FN_DECODE_X(2, 1, 4, 1, true, 2, "decode_swiglu_bf16_m32_xlds_w4_u2"),
-    FN_DECODE_X(4, 1, 4, 1, true, 2, "decode_swiglu_bf16_m64_xlds_w4_u2"),
+    FN_DECODE_X(2, 1, 3, false, 2, "decode_bf16_m32_xlds_w3_u2"),
+    FN_DECODE_X(4, 1, 3, false, 2, "decode_bf16_m64_xlds_w3_u2"),
+    FN_DECODE_X(2, 1, 3, true, 2, "decode_swiglu_bf16_m32_xlds_w3_u2"),
+    FN_DECODE_X(4, 1, 3, true, 2, "decode_swiglu_bf16_m64_xlds_w3_u2"),
 };
 
 static const DecodeXInstance* find_decode_x(int mf, bool sw) {
   for (const DecodeXInstance& d : kDecodeX)
     if (d.mf == mf && d.sw == sw) return &d;
   return nullptr;
-}
-
-// Stages per k-split, rounded up to whole ring rounds.
-static int decode_x_spg(int kblocks, int u, int wk) {
-  const int stages = (int)ceil_div(kblocks, u);
-  return (int)ceil_div(ceil_div(stages, wk), 4) * 4;
 }
 
 // Row ladder rungs 32 and 64; one workgroup row, NC*NWV column blocks each.
@@ -324,7 +315,7 @@ FusedPlan plan_decode_x(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) 
   p.kind = 2;
   p.mf = d->mf;
   p.nf = d->nc * d->nwv;
-  p.waves = d->nwv * d->wk;
+  p.waves = d->nwv;
   p.grid = dim3((unsigned)ceil_div(ceil_div(N, 16), p.nf), 1, 1);
   p.block = dim3(kWave * p.waves, 1, 1);
   p.name = d->name;
@@ -335,20 +326,8 @@ hipError_t launch_decode_x(DType dt, const FusedPlan& p, const void* x, const vo
                            int M, int K, int N, float eps, hipStream_t stream) {
   const DecodeXInstance* d = find_decode_x(p.mf, wu != nullptr);
   if (dt != DType::BF16 || d == nullptr || M > 16 * d->mf) return hipErrorInvalidValue;
-  DecodeXArgs a;
-  a.x = x;
-  a.wg = wg;
-  a.wu = wu;
-  a.y = y;
-  a.M = M;
-  a.K = K;
-  a.N = N;
-  a.kblocks = (int)ceil_div(K, 32);
-  a.nblocks = (int)ceil_div(N, 16);
-  a.spg = decode_x_spg(a.kblocks, d->u, d->wk);
-  a.eps = eps;
-  void* args[] = {&a};
-  return hipLaunchKernel(d->fn, p.grid, p.block, args, 0, stream);
+  return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream);
 }
+#endif
 
 }  // namespace fn
