@@ -43,11 +43,17 @@ All arithmetic is float64.  Inputs are the stored (bf16 or fp32) values,
 up-cast exactly.  eps is taken as float64(float32(eps)), the exact value a
 GPU kernel receives as a float argument.
 
+The fp8-weight functions at the end (E4M3 codes with one scale per output
+column) follow the reading stated in their section.
+
 Pins (see tests/test_oracle.py): hand-derived worked cases, brute force on
 tiny inputs, torch's float64 rms_norm followed by a float64 matmul, the fold
 identity, scale invariance, norm-after-weightless-norm, row permutation and
-column concatenation, and library round-to-nearest-even conversions.  Every
-function here is pinned; none is "parity unpinned".
+column concatenation, library round-to-nearest-even conversions (bf16, and
+torch's float8_e4m3fn for the E4M3 codes), hand-evaluated E4M3 codes, the
+quantisation error bound, and the exact reduction of the fp8 path to the
+deferred form when the weights are E4M3-exact.  Every function here is
+pinned; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -168,6 +174,104 @@ def norm_proj_swiglu_folded(x, Wg_folded, Wu_folded, eps: float) -> np.ndarray:
     return silu(a) * b
 
 
+# ------------------------------------------------------------ fp8 weights --
+# The pages state that folded weights stay valid for quantised models
+# ([FlashNorm digest], the compatibility bullet), carry an FP8 variant of the
+# fused FC1 + SwiGLU kernel ([FlashInfer #5521], "FP8 Variant" in the
+# results), and dequantise low-precision weights in registers right before
+# the matrix product ([Fused-kernel memory hierarchy] "Fused 커널은 왜 3~4배
+# 빠른가", section "트릭 2": in-register dequantisation).  They fix no format,
+# scale granularity or rounding.  The reading taken here:
+#
+# * format: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa
+#   bits; subnormals; no infinities; codes 0x7F/0xFF are NaN; largest finite
+#   magnitude 448), the FP8 format of the target's matrix cores;
+# * quantised operand: the folded, stored W' (fold first, as for bf16);
+# * one fp32 scale per output column: amax[n] = max_k |W'[k,n]|,
+#   r[n] = fp32(448 / amax[n]), codes q = RNE_e4m3(fp32(W'[k,n] * r[n])),
+#   dequantisation scale s[n] = fp32(amax[n] / 448); an all-zero column takes
+#   r = s = 1.  Every step is one IEEE fp32 operation, so the codes are a
+#   deterministic function of W' that a GPU reproduces bit for bit;
+# * the product: y[m,n] = s[n] * (sum_k x[m,k] * q[k,n]) / r_rms[m], i.e. the
+#   deferred form with the weight decoded exactly (every E4M3 value is a bf16
+#   value) and the column scale applied with 1/RMS after the sum.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each OCP E4M3 code (uint8): (-1)^s * 2^(e-7) * (1 + m/8) for
+    exponent field e > 0, (-1)^s * 2^-6 * (m/8) for e = 0; 0x7F and 0xFF are
+    NaN."""
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+def e4m3_encode(a) -> np.ndarray:
+    """Code of the E4M3 value nearest to a, ties to even (RNE on the 3-bit
+    mantissa, on the 2^-9 grid below the smallest normal 2^-6).  Magnitudes
+    at or past the rounding boundary above 448 saturate to 448; NaN gives
+    0x7F."""
+    a = _f64(a)
+    mag = np.abs(a)
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        _, e = np.frexp(mag)                     # mag = f * 2^e, 0.5 <= f < 1
+        e = np.maximum(e, -5)                    # below 2^-6: the subnormal quantum 2^-9
+        q = np.rint(np.ldexp(mag, 4 - e))        # units of the quantum 2^(e-4); half to even
+        val = np.ldexp(q, e - 4)
+    val = np.minimum(val, E4M3_MAX)
+    # exponent field and mantissa of the rounded magnitude
+    _, ev = np.frexp(np.where(val > 0, val, 1.0))
+    field = np.where(val >= 2.0 ** -6, ev + 6, 0)        # 2^(ev-1) = 2^(field-7)
+    mant = np.where(field > 0, np.ldexp(val, 4 - ev) - 8, np.ldexp(val, 9))
+    mant = np.where(np.isnan(mant), 0.0, mant)
+    code = (field.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    code = np.where(val == 0, 0, code)
+    code = code | np.where(np.signbit(a), 0x80, 0)
+    code = np.where(np.isnan(a), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_e4m3_columns(W_folded):
+    """Per-column E4M3 quantisation of stored folded weights (float values of
+    bf16 or fp32 storage).  Returns (codes uint8 [K,N], s float32 [N],
+    r float32 [N]) as described above."""
+    Wf = np.asarray(W_folded, dtype=np.float32)
+    amax = np.max(np.abs(Wf), axis=0) if Wf.shape[0] else np.zeros(Wf.shape[1], np.float32)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
+    r = np.where(zero, np.float32(1.0), np.float32(E4M3_MAX) / safe).astype(np.float32)
+    s = np.where(zero, np.float32(1.0), safe / np.float32(E4M3_MAX)).astype(np.float32)
+    scaled = (Wf * r[None, :]).astype(np.float32)             # one fp32 multiply
+    return e4m3_encode(scaled), s, r
+
+
+def fold_weights_fp8(g, W, dtype: str):
+    """Fold, store in dtype, then quantise per column: (codes, s)."""
+    codes, s, _ = quantize_e4m3_columns(fold_weights(g, W, dtype))
+    return codes, s
+
+
+def norm_proj_fp8(x, codes, s, eps: float) -> np.ndarray:
+    """Deferred normalisation with E4M3 weights: y = s[n] * (x @ q) / r."""
+    x = _f64(x)
+    return (x @ e4m3_decode(codes)) * _f64(s)[None, :] / rms(x, eps)[:, None]
+
+
+def norm_proj_swiglu_fp8(x, codes_gate, s_gate, codes_up, s_up, eps: float) -> np.ndarray:
+    """SwiGLU variant with E4M3 weights: a and b as in norm_proj_fp8, then
+    out = silu(a) * b."""
+    a = norm_proj_fp8(x, codes_gate, s_gate, eps)
+    b = norm_proj_fp8(x, codes_up, s_up, eps)
+    return silu(a) * b
+
+
 __all__ = ["rms", "rmsnorm", "norm_proj", "silu", "norm_proj_swiglu", "fold_exact",
            "round_to_bf16", "round_to_f32", "round_to", "fold_weights", "norm_proj_folded",
-           "norm_proj_swiglu_folded", "eps_as_received"]
+           "norm_proj_swiglu_folded", "eps_as_received", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
+           "quantize_e4m3_columns", "fold_weights_fp8", "norm_proj_fp8", "norm_proj_swiglu_fp8"]

@@ -264,3 +264,100 @@ def check_fold_rounding(o, seed=18):
 ALL_CHECKS = [check_hand_cases, check_silu_closed_forms, check_brute_force, check_torch_rms_norm,
               check_fold_identity, check_scale_invariance, check_double_norm,
               check_rows_and_columns, check_rounding, check_fold_rounding]
+
+
+# --------------------------------------------------------------------------
+# fp8 (E4M3) weights
+# --------------------------------------------------------------------------
+def check_e4m3_codes(o, seed=19):
+    """Decode and encode against hand-evaluated codes, the format's
+    structure, and torch's float8_e4m3fn conversion (RNE) as a library
+    cross-check."""
+    import torch
+    gold = load_golden()["e4m3"]
+    for desc, code, want in gold["decode"]:
+        got = o.e4m3_decode(np.array([code]))[0]
+        assert got == want and np.signbit(got) == np.signbit(want), f"decode {desc}: {got!r} != {want!r}"
+    for desc, v, want in gold["encode"]:
+        got = int(o.e4m3_encode(np.array([v]))[0])
+        assert got == want, f"encode {desc}: {got:#x} != {want:#x}"
+    codes = np.arange(256, dtype=np.uint8)
+    vals = o.e4m3_decode(codes)
+    finite = ~np.isnan(vals)
+    assert finite.sum() == 254 and not finite[0x7F] and not finite[0xFF]
+    pos = vals[:0x7F]
+    assert np.all(np.diff(pos) > 0), "positive codes are not increasing"
+    assert np.array_equal(vals[0x80:0xFF], -pos), "negative codes mirror the positive ones"
+    assert np.array_equal(o.e4m3_encode(vals[finite]), codes[finite]), "round trip"
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ref), np.isnan(vals)) and np.array_equal(ref[finite], vals[finite]), "decode vs torch"
+    # random fp32 values in range, plus every midpoint between neighbours
+    rng = np.random.default_rng(seed)
+    f = np.concatenate([rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 0.01,
+                        (pos[1:] + pos[:-1]) / 2, -(pos[1:] + pos[:-1]) / 2]).astype(np.float32)
+    ref = torch.from_numpy(f).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = o.e4m3_encode(f.astype(np.float64))
+    assert np.array_equal(got, ref), "encode vs torch"
+
+
+def check_e4m3_quantize(o, seed=20):
+    """Per-column quantisation: a hand-evaluated column, an all-zero column,
+    each column's largest magnitude landing on +-448, and the rounding error
+    bound (half a quantum of the scaled value)."""
+    gold = load_golden()["e4m3"]["quantize_column"]
+    W = np.zeros((4, 2))
+    W[:, 0] = gold["W"]
+    codes, s, r = o.quantize_e4m3_columns(W)
+    assert [int(c) for c in codes[:, 0]] == gold["codes"], codes[:, 0]
+    assert float(s[0]) == gold["s"], s[0]
+    assert np.all(codes[:, 1] == 0) and s[1] == 1.0 and r[1] == 1.0, "all-zero column"
+    rng = np.random.default_rng(seed)
+    Wf = (rng.standard_normal((96, 40)) / 8).astype(np.float32)
+    Wf[:, 3] *= 1e-3
+    codes, s, r = o.quantize_e4m3_columns(Wf)
+    vals = o.e4m3_decode(codes)
+    top = np.argmax(np.abs(Wf), axis=0)
+    assert np.all(np.abs(vals[top, np.arange(40)]) == 448.0), "column maximum maps to +-448"
+    scaled = Wf.astype(np.float64) * r.astype(np.float64)[None, :]
+    _, e = np.frexp(np.abs(scaled))
+    half_quantum = np.ldexp(1.0, np.maximum(e, -5) - 5)
+    assert np.all(np.abs(vals - scaled) <= half_quantum * (1 + 1e-6)), "E4M3 rounding error bound"
+    assert np.allclose(s.astype(np.float64) * r.astype(np.float64), 1.0, rtol=2e-7), "s = 1/r"
+
+
+def check_norm_proj_fp8(o, seed=21):
+    """With weights whose scaled values are exact E4M3 values the fp8 path is
+    the deferred bf16 path, exactly; brute force on a tiny case."""
+    rng = np.random.default_rng(seed)
+    K, N, M = 48, 24, 5
+    pool = o.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    pick = rng.choice(pool, size=(K, N)) * rng.choice([-1.0, 1.0], size=(K, N))
+    pick[0, :] = 448.0                          # each column's amax is 448 -> r = s = 1
+    Wf = (pick * np.ldexp(1.0, -6)).astype(np.float32)   # power-of-two rescale keeps exactness
+    codes, s, r = o.quantize_e4m3_columns(Wf)
+    assert np.all(r == 448.0 / (448.0 * 2.0 ** -6))
+    x = rng.standard_normal((M, K))
+    y = o.norm_proj_fp8(x, codes, s, 1e-6)
+    ref = o.norm_proj_folded(x, Wf.astype(np.float64), 1e-6)
+    _close(y, ref, 1e-12, "fp8 exact weights vs deferred form")
+    codes_u, s_u, _ = o.quantize_e4m3_columns(Wf[::-1].copy())
+    a = o.norm_proj_swiglu_fp8(x, codes, s, codes_u, s_u, 1e-6)
+    ref = o.norm_proj_swiglu_folded(x, Wf.astype(np.float64), Wf[::-1].astype(np.float64), 1e-6)
+    _close(a, ref, 1e-12, "fp8 SwiGLU exact weights vs deferred form")
+    # brute force, arbitrary weights
+    Wr = rng.standard_normal((6, 3)).astype(np.float32)
+    c2, s2, _ = o.quantize_e4m3_columns(Wr)
+    xs = rng.standard_normal((2, 6))
+    got = o.norm_proj_fp8(xs, c2, s2, 0.25)
+    for m in range(2):
+        ms = sum(float(v) ** 2 for v in xs[m]) / 6
+        rr = math.sqrt(ms + float(np.float32(0.25)))
+        for n in range(3):
+            acc = 0.0
+            for k in range(6):
+                acc += float(xs[m, k]) * float(o.e4m3_decode(np.array([c2[k, n]]))[0])
+            want = acc * float(s2[n]) / rr
+            assert abs(got[m, n] - want) <= 1e-12 * (abs(want) + 1), (m, n, got[m, n], want)
+
+
+ALL_CHECKS += [check_e4m3_codes, check_e4m3_quantize, check_norm_proj_fp8]

@@ -46,13 +46,53 @@ MUTANTS = {
     "fold on the output axis": ("fold_exact", lambda g, W: np.asarray(W, float) * np.asarray(g, float)[None, :]),
     "deferred multiply": ("norm_proj_folded", lambda x, Wf, eps: (np.asarray(x, float) @ np.asarray(Wf, float))
                           * O.rms(x, eps)[:, None]),
+    "e4m3 ties away": ("e4m3_encode", lambda a: _encode_with(a, lambda v: np.floor(v + 0.5))),
+    "e4m3 truncation": ("e4m3_encode", lambda a: _encode_with(a, np.floor)),
+    "e4m3 bias 8": ("e4m3_decode", lambda c: _decode_bias(c, 8)),
+    "fp8 scale dropped": ("norm_proj_fp8", lambda x, c, s, eps: (np.asarray(x, float) @ O.e4m3_decode(c))
+                          / O.rms(x, eps)[:, None]),
+    "fp8 scale inverted": ("norm_proj_fp8", lambda x, c, s, eps: (np.asarray(x, float) @ O.e4m3_decode(c))
+                           / np.asarray(s, float)[None, :] / O.rms(x, eps)[:, None]),
+    "fp8 scale per row": ("quantize_e4m3_columns", lambda W: _quantize_rows(W)),
 }
+
+
+_encode_ref = O.e4m3_encode
+_decode_ref = O.e4m3_decode
+_quantize_ref = O.quantize_e4m3_columns
+
+
+def _encode_with(a, rnd):
+    """E4M3 encoder with a different rounding of the scaled magnitude."""
+    a = np.asarray(a, float)
+    mag = np.abs(a)
+    with np.errstate(all="ignore"):
+        _, e = np.frexp(mag)
+        e = np.maximum(e, -5)
+        val = np.minimum(np.ldexp(rnd(np.ldexp(mag, 4 - e)), e - 4), 448.0)
+    return _encode_ref(np.copysign(val, a))
+
+
+def _decode_bias(c, bias):
+    c = np.asarray(c, dtype=np.int64) & 0xFF
+    e = (c >> 3) & 0xF
+    m = (c & 7) / 8.0
+    v = np.where(e == 0, np.ldexp(m, 1 - bias), np.ldexp(1 + m, e - bias))
+    v = np.where((c & 0x7F) == 0x7F, np.nan, v)
+    return np.where(c & 0x80, -v, v)
+
+
+def _quantize_rows(W):
+    Wt = np.asarray(W, dtype=np.float32).T.copy()
+    codes, s, r = _quantize_ref(Wt)
+    n = np.asarray(W).shape[1]
+    return codes.T.copy(), np.resize(s, n).astype(np.float32), np.resize(r, n).astype(np.float32)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistakes(name, monkeypatch):
     attr, fn = MUTANTS[name]
-    original = {k: getattr(O, k) for k in ("rms", "rmsnorm", "silu")}
+    original = {k: getattr(O, k) for k in ("rms", "rmsnorm", "silu", "e4m3_encode", "e4m3_decode")}
     monkeypatch.setattr(O, attr, fn)
     # mutants that call O.rms / O.rmsnorm / O.silu must see the unmutated
     # helpers unless the helper itself is the mutant
