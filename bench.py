@@ -40,6 +40,9 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qkv_decode",
                    choices=["tiny", "qkv_decode", "ffn_decode", "prefill_qkv", "decode_step"])
+    p.add_argument("--weights", default="native", choices=["native", "fp8"],
+                   help="weight storage: the activations' dtype, or E4M3 codes with per-column scales "
+                        "(bf16 decode workloads only)")
     p.add_argument("--no-chain", action="store_true", help="skip the unfused chain baselines")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
@@ -105,7 +108,9 @@ def pct(sorted_vals, q):
 
 
 # Sources each workload's dominant kernel is built from.
-KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": ("decode_x.hip", "fn_device.h")}
+KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": ("decode_x.hip", "fn_device.h"),
+                  "qkv_decode_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_fp8": ("decode_x.hip", "fn_device.h"),
+                  "decode_step_fp8": ("decode_x.hip", "fn_device.h")}
 DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
 
 
@@ -131,8 +136,14 @@ def counter_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
+def fp8_bytes(call):
+    """Algorithmic bytes of one call with fp8 weights: the codes and the
+    column scales once, x and y (bf16) once."""
+    return call.mats * (call.K * call.N + 4 * call.N) + 2 * (call.M * call.K + call.M * call.N)
+
+
 # ------------------------------------------------------------ CPU oracle --
-def cpu_baseline(call, inp, budget_s, metric_unit):
+def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False):
     """The float64 oracle as it stands, on the host cores, on a bounded sample
     of the same workload; scaled to the metric's unit."""
     import numpy as np
@@ -148,8 +159,17 @@ def cpu_baseline(call, inp, budget_s, metric_unit):
         rows = max(1, int(2e10 // (call.K * call.N * call.mats)))
     x = inp.x[:rows]
     calls, t0 = 0, time.perf_counter()
-    while True:
+    q8 = None
+    if fp8:
+        q8 = [oracle.fold_weights_fp8(inp.g, inp.W, call.dtype)]
         if call.swiglu:
+            q8.append(oracle.fold_weights_fp8(inp.g, inp.W_up, call.dtype))
+    while True:
+        if fp8 and call.swiglu:
+            oracle.norm_proj_swiglu_fp8(x, q8[0][0], q8[0][1], q8[1][0], q8[1][1], call.eps)
+        elif fp8:
+            oracle.norm_proj_fp8(x, q8[0][0], q8[0][1], call.eps)
+        elif call.swiglu:
             oracle.norm_proj_swiglu(x, inp.g, inp.W, inp.W_up, call.eps)
         else:
             oracle.norm_proj(x, inp.g, inp.W, call.eps)
@@ -161,11 +181,12 @@ def cpu_baseline(call, inp, budget_s, metric_unit):
     if metric_unit == "TFLOP/s":
         value = call.flops() / per_call / 1e12
     elif metric_unit == "GB/s":
-        value = call.algorithmic_bytes() / per_call / 1e9
+        value = (fp8_bytes(call) if fp8 else call.algorithmic_bytes()) / per_call / 1e9
     else:
         value = per_call * 1e6
     sample = (f"{calls} oracle call(s) on x[{rows},{call.K}] (of M={call.M}) x W[{call.K},{call.N}]"
-              f"{' x2 (gate, up)' if call.swiglu else ''}, float64, {el:.1f} s; scaled by M/{rows}")
+              f"{' x2 (gate, up)' if call.swiglu else ''}{' (E4M3 codes)' if fp8 else ''}, float64, {el:.1f} s;"
+              f" scaled by M/{rows}")
     return {"value": round(value, 4), "unit": metric_unit, "cores": cores, "kind": "oracle",
             "sample": sample, "seconds_per_call": per_call}
 
@@ -183,28 +204,54 @@ def run_single(args, torch, fn, workloads):
     g = to_dev(torch, inp.g, call.dtype)
     Wg = to_dev(torch, inp.W, call.dtype)
     Wu = to_dev(torch, inp.W_up, call.dtype) if call.swiglu else None
-    Pg = fn.fold_weights(g, Wg)
-    Pu = fn.fold_weights(g, Wu) if call.swiglu else None
-    wbytes = Pg.data.numel() * call.mats
+    fp8 = args.weights == "fp8"
+    if fp8:
+        Pg = fn.fold_weights_fp8(g, Wg)
+        Pu = fn.fold_weights_fp8(g, Wu) if call.swiglu else None
+        wbytes = (Pg.data.numel() + Pg.scales.numel() * 4) * call.mats
+
+        def clone(P):
+            return fn.PackedFp8(P.data.clone(), P.scales.clone(), P.K, P.N)
+        proj, proj_sw = fn.norm_proj_fp8, fn.norm_proj_swiglu_fp8
+    else:
+        Pg = fn.fold_weights(g, Wg)
+        Pu = fn.fold_weights(g, Wu) if call.swiglu else None
+        wbytes = Pg.data.numel() * call.mats
+
+        def clone(P):
+            return fn.PackedWeights(P.data.clone(), P.K, P.N, P.dtype)
+        proj, proj_sw = fn.norm_proj, fn.norm_proj_swiglu
     rot = 1 if args.hot else max(1, math.ceil(ROTATE_BYTES / wbytes))
-    pgs = [Pg] + [fn.PackedWeights(Pg.data.clone(), Pg.K, Pg.N, Pg.dtype) for _ in range(rot - 1)]
-    pus = ([Pu] + [fn.PackedWeights(Pu.data.clone(), Pu.K, Pu.N, Pu.dtype) for _ in range(rot - 1)]
-           if call.swiglu else None)
+    pgs = [Pg] + [clone(Pg) for _ in range(rot - 1)]
+    pus = ([Pu] + [clone(Pu) for _ in range(rot - 1)]) if call.swiglu else None
     y = torch.empty((call.M, call.N), dtype=x.dtype, device="cuda")
     eps = call.eps
 
     if call.swiglu:
         def fused(i):
-            fn.norm_proj_swiglu(x, pgs[i % rot], pus[i % rot], eps, out=y)
+            proj_sw(x, pgs[i % rot], pus[i % rot], eps, out=y)
     else:
         def fused(i):
-            fn.norm_proj(x, pgs[i % rot], eps, out=y)
+            proj(x, pgs[i % rot], eps, out=y)
 
     ms = time_region(torch, fused, args.steps, args.warmup)
     each = time_each(torch, fused, min(args.steps, 200))
-    hot_ms = time_region(torch, lambda i: (fn.norm_proj_swiglu(x, Pg, Pu, eps, out=y) if call.swiglu
-                                           else fn.norm_proj(x, Pg, eps, out=y)), args.steps, args.warmup)
+    hot_ms = time_region(torch, lambda i: (proj_sw(x, Pg, Pu, eps, out=y) if call.swiglu
+                                           else proj(x, Pg, eps, out=y)), args.steps, args.warmup)
     result = {"ms": ms, "each": each, "hot_ms": hot_ms, "rot": rot, "wbytes": wbytes}
+    if fp8:
+        # the same call with bf16 folded weights, same rotation rule, for comparison
+        del pgs, pus
+        Bg = fn.fold_weights(g, Wg)
+        Bu = fn.fold_weights(g, Wu) if call.swiglu else None
+        brot = max(1, math.ceil(ROTATE_BYTES / (Bg.data.numel() * call.mats)))
+        bgs = [Bg] + [fn.PackedWeights(Bg.data.clone(), Bg.K, Bg.N, Bg.dtype) for _ in range(brot - 1)]
+        bus = ([Bu] + [fn.PackedWeights(Bu.data.clone(), Bu.K, Bu.N, Bu.dtype) for _ in range(brot - 1)]
+               if call.swiglu else None)
+        result["bf16_ms"] = time_region(
+            torch, lambda i: (fn.norm_proj_swiglu(x, bgs[i % brot], bus[i % brot], eps, out=y) if call.swiglu
+                              else fn.norm_proj(x, bgs[i % brot], eps, out=y)), args.steps, args.warmup)
+        del bgs, bus
 
     if not args.no_chain:
         # unfused chains on row-major weights, same rotation
@@ -234,10 +281,14 @@ def run_single(args, torch, fn, workloads):
 def run_decode_step(args, torch, fn, workloads):
     calls = workloads.decode_step_calls()
     items = []
+    fp8 = args.weights == "fp8"
+    fold = fn.fold_weights_fp8 if fp8 else fn.fold_weights
+    proj = fn.norm_proj_fp8 if fp8 else fn.norm_proj
+    proj_sw = fn.norm_proj_swiglu_fp8 if fp8 else fn.norm_proj_swiglu
     for c in calls:
         x, g, Wg, Wu = workloads.make_inputs_device(c)
-        Pg = fn.fold_weights(g, Wg)
-        Pu = fn.fold_weights(g, Wu) if c.swiglu else None
+        Pg = fold(g, Wg)
+        Pu = fold(g, Wu) if c.swiglu else None
         item = {"call": c, "x": x, "g": g, "Pg": Pg, "Pu": Pu,
                 "y": torch.empty((c.M, c.N), dtype=x.dtype, device="cuda")}
         if not args.no_chain:
@@ -250,14 +301,15 @@ def run_decode_step(args, torch, fn, workloads):
         for it in items:
             c = it["call"]
             if c.swiglu:
-                fn.norm_proj_swiglu(it["x"], it["Pg"], it["Pu"], c.eps, out=it["y"])
+                proj_sw(it["x"], it["Pg"], it["Pu"], c.eps, out=it["y"])
             else:
-                fn.norm_proj(it["x"], it["Pg"], c.eps, out=it["y"])
+                proj(it["x"], it["Pg"], c.eps, out=it["y"])
 
     ms = time_region(torch, fused, args.steps, args.warmup)
     each = time_each(torch, fused, min(args.steps, 20))
     result = {"ms": ms, "each": each, "hot_ms": None, "rot": 1,
-              "wbytes": sum(it["Pg"].data.numel() * it["call"].mats for it in items)}
+              "wbytes": sum((it["Pg"].data.numel() + (it["Pg"].scales.numel() * 4 if fp8 else 0)) * it["call"].mats
+                            for it in items)}
     if not args.no_chain:
         def chain_own(_):
             for it in items:
@@ -310,28 +362,34 @@ def main(argv=None):
     if args.calibrate_copy:
         calibrate_copy(torch)
         return 0
+    fp8 = args.weights == "fp8"
+    if fp8 and args.workload in ("tiny", "prefill_qkv"):
+        print(f"bench.py: --weights fp8 applies to the bf16 decode workloads, not {args.workload}", file=sys.stderr)
+        return 2
+    suffix = "_fp8" if fp8 else ""
 
     if args.workload == "decode_step":
         calls, r = run_decode_step(args, torch, fn, workloads)
-        bytes_step = sum(c.algorithmic_bytes() for c in calls)
+        bytes_step = sum((fp8_bytes(c) if fp8 else c.algorithmic_bytes()) for c in calls)
         flops_step = sum(c.flops() for c in calls)
         name = "32-layer decode step, M=8: 32 x (norm+QKV 4096->12288, norm+gate/up SwiGLU 4096->2x11008) + norm+head 4096->32000"
         config = {"workload": name, "calls_per_step": len(calls), "M": 8, "K": 4096,
                   "weights_bytes": r["wbytes"], "cache": "cold (9.3 GB of distinct weights per step)"}
-        kernel = fn.kernel_name(8, 4096, 12288, False, torch.bfloat16)
+        kernel = fn.kernel_name_fp8(8, 4096, 12288, False) if fp8 else fn.kernel_name(8, 4096, 12288, False, torch.bfloat16)
         cpu_call, cpu_inp = calls[-1], None
         unit = "GB/s"
         value = bytes_step / (r["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": counter_traffic("decode_step")}
+                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": counter_traffic("decode_step" + suffix)}
         dtype = "bf16"
         per_unit = {"algorithmic_bytes_per_step": bytes_step, "flops_per_step": flops_step}
     else:
         call, inp, r = run_single(args, torch, fn, workloads)
-        bytes_call = call.algorithmic_bytes()
+        bytes_call = fp8_bytes(call) if fp8 else call.algorithmic_bytes()
         flops_call = call.flops()
-        kernel = fn.kernel_name(call.M, call.K, call.N, call.swiglu,
-                                torch.bfloat16 if call.dtype == "bf16" else torch.float32)
+        kernel = (fn.kernel_name_fp8(call.M, call.K, call.N, call.swiglu) if fp8 else
+                  fn.kernel_name(call.M, call.K, call.N, call.swiglu,
+                                 torch.bfloat16 if call.dtype == "bf16" else torch.float32))
         config = {"workload": call.name, "M": call.M, "K": call.K, "N": call.N, "mats": call.mats,
                   "eps": call.eps, "kernel": kernel,
                   "cache": (f"cold ({r['rot']} rotated W' copies, {r['rot'] * r['wbytes'] / 2**30:.2f} GiB)"
@@ -355,7 +413,9 @@ def main(argv=None):
             unit = "GB/s"
             value = bytes_call / (r["ms"] * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(value / HBM_PEAK_GBS, 4), "traffic": counter_traffic(args.workload)}
+                    "frac": round(value / HBM_PEAK_GBS, 4), "traffic": counter_traffic(args.workload + suffix)}
+        if fp8:
+            config["weights"] = "fp8 E4M3 codes + one fp32 scale per output column"
 
     out = {
         "metric": METRIC,
@@ -378,6 +438,9 @@ def main(argv=None):
         "kernel": kernel,
         **per_unit,
     }
+    if "bf16_ms" in r:
+        out["bf16_weights_us"] = round(r["bf16_ms"] * 1e3, 3)
+        out["speedup_vs_bf16_weights"] = round(r["bf16_ms"] / r["ms"], 3)
     if "chain_own_ms" in r:
         out["chain"] = {
             "own_rmsnorm_then_hipblaslt_us": round(r["chain_own_ms"] * 1e3, 3),
@@ -388,11 +451,11 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         if cpu_inp is None:
             cpu_inp = workloads.make_inputs(cpu_call)
-        cb = cpu_baseline(cpu_call, cpu_inp, args.cpu_seconds, unit if unit != "us/call" else "us/call")
+        cb = cpu_baseline(cpu_call, cpu_inp, args.cpu_seconds, unit if unit != "us/call" else "us/call", fp8=fp8)
         if args.workload == "decode_step":
             # one head call sampled; scale to the whole step by algorithmic bytes
             per_call = cb.pop("seconds_per_call")
-            step_s = per_call * bytes_step / cpu_call.algorithmic_bytes()
+            step_s = per_call * bytes_step / (fp8_bytes(cpu_call) if fp8 else cpu_call.algorithmic_bytes())
             cb["value"] = round(bytes_step / step_s / 1e9, 4)
             cb["sample"] += "; scaled to the 65-call step by algorithmic bytes"
         else:

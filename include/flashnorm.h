@@ -133,6 +133,70 @@ fn_status fn_rmsnorm(const void* x, const void* g, void* xhat,
 fn_status fn_silu_mul(const void* h, void* out, int64_t M, int64_t N,
                       fn_dtype dt, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * fp8 weights (E4M3, one scale per output column)
+ *
+ * Folded checkpoints stay valid for quantised models ([FlashNorm digest],
+ * compatibility bullet); the pages' fused FC1 + SwiGLU kernel has an FP8
+ * variant ([FlashInfer #5521], results, "FP8 Variant"), and low-precision
+ * weights are decoded in registers right before the matrix product
+ * ([Fused-kernel memory hierarchy] "Fused 커널은 왜 3~4배 빠른가", section
+ * "트릭 2").  Reading taken here: the folded, stored W' (as fn_fold_weights
+ * computes it in dt) is quantised per output column to OCP FP8 E4M3
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, largest
+ * finite 448), with every step one IEEE fp32 operation:
+ *   amax[n] = max_k |W'[k][n]|,  r[n] = 448 / amax[n],  s[n] = amax[n] / 448
+ *   (r = s = 1 for an all-zero column),
+ *   q[k][n] = RNE_E4M3(W'[k][n] * r[n])   (ties to even, saturating at 448).
+ * The fused calls then compute, in fp32,
+ *   y[m][n] = round_bf16( s[n] * (sum_k x[m][k] * q[k][n]) / RMS(x[m]) )
+ * decoding q exactly (every E4M3 value is a bf16 value).  Only bf16
+ * activations (x, y, out) are supported.
+ *
+ * Packed fp8 layout: fragment-major 1 KiB fragments of 16 columns x 64 rows;
+ * code q[k][n] sits at byte
+ *   (((n/16) * ceil(K/64) + k/64) * 64 + ((k%32)/8) * 16 + n%16) * 16
+ *     + (k%64 >= 32 ? 8 : 0) + k%8
+ * so one 16-byte lane load carries the lane's 8 values of two consecutive
+ * 32-row k-blocks.  Padding codes (k >= K or n >= N) are zero.  Weights must
+ * be finite; the codes of a column holding a NaN or an infinity are
+ * unspecified.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the packed fp8 weights for a [K,N] matrix; 0 if K or N is
+ * outside the limits. */
+size_t fn_packed_fp8_bytes(int64_t K, int64_t N);
+
+/* Fold (as fn_fold_weights, in dt), then quantise per column as above.
+ * g:         [K] device vector in dt, or NULL (W' = W).
+ * W:         [K,N] row-major device matrix in dt (FN_BF16 or FN_F32).
+ * W8_packed: device buffer of fn_packed_fp8_bytes(K, N) bytes, fully
+ *            overwritten (padding included).
+ * scales:    device buffer of N floats, receives s[n].
+ * The outputs may not overlap g, W or each other.  Offline, once per
+ * weight matrix. */
+fn_status fn_fold_weights_fp8(const void* g, const void* W, void* W8_packed, float* scales,
+                              int64_t K, int64_t N, fn_dtype dt, hipStream_t stream);
+
+/* Fused RMSNorm + projection with fp8 weights, one launch:
+ *   y[m][n] = round_bf16( s[n] * (sum_k x[m][k] * q[k][n]) / sqrt(sum_k x[m][k]^2 / K + eps) )
+ * x: [M,K] bf16; W8_packed, scales: from fn_fold_weights_fp8 for this K, N;
+ * y: [M,N] bf16, fully overwritten.  scales must be 4-byte aligned. */
+fn_status fn_norm_proj_fp8(const void* x, const void* W8_packed, const float* scales, void* y,
+                           int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream);
+
+/* Fused RMSNorm + gate/up projections + SwiGLU with fp8 weights:
+ *   a = s_gate[n] (x * q_gate)[m][n] / r[m],  b = s_up[n] (x * q_up)[m][n] / r[m],
+ *   out[m][n] = round_bf16( a / (1 + exp(-a)) * b ). */
+fn_status fn_norm_proj_swiglu_fp8(const void* x, const void* W8_gate, const float* s_gate,
+                                  const void* W8_up, const float* s_up, void* out,
+                                  int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream);
+
+/* Name of the kernel instance fn_norm_proj_fp8 (swiglu == 0) or
+ * fn_norm_proj_swiglu_fp8 (swiglu != 0) would launch for this shape; a
+ * static string, "invalid" for bad shapes. */
+const char* fn_kernel_name_fp8(int64_t M, int64_t K, int64_t N, int swiglu);
+
 /* Name of the kernel instance fn_norm_proj (swiglu == 0) or
  * fn_norm_proj_swiglu (swiglu != 0) would launch for this shape, e.g.
  * "decode_bf16_m16_n1_w4"; a static string, "invalid" for bad shapes. */

@@ -9,6 +9,8 @@ raises.
     Wp = fn.fold_weights(g, W)           # offline: W' = diag(g) W, packed
     y = fn.norm_proj(x, Wp, eps=1e-6)    # y = (x W') / rms(x), one launch
     out = fn.norm_proj_swiglu(x, Wg, Wu) # silu(a) * b, one launch
+    P8 = fn.fold_weights_fp8(g, W)       # W' quantised to E4M3 per column
+    y8 = fn.norm_proj_fp8(x, P8)         # y = s * (x q) / rms(x), one launch
 """
 from __future__ import annotations
 
@@ -42,7 +44,7 @@ def header_functions():
     with open(HEADER_PATH) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fn_[a-z0-9_]+)\s*\(", text)))
 
 
 def load():
@@ -62,6 +64,11 @@ def load():
         "fn_rmsnorm": (i32, [vp, vp, vp, i64, i64, f32, i32, vp]),
         "fn_silu_mul": (i32, [vp, vp, i64, i64, i32, vp]),
         "fn_kernel_name": (ctypes.c_char_p, [i64, i64, i64, i32, i32]),
+        "fn_packed_fp8_bytes": (ctypes.c_size_t, [i64, i64]),
+        "fn_fold_weights_fp8": (i32, [vp, vp, vp, vp, i64, i64, i32, vp]),
+        "fn_norm_proj_fp8": (i32, [vp, vp, vp, vp, i64, i64, i64, f32, vp]),
+        "fn_norm_proj_swiglu_fp8": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp]),
+        "fn_kernel_name_fp8": (ctypes.c_char_p, [i64, i64, i64, i32]),
         "fn_status_string": (ctypes.c_char_p, [i32]),
         "fn_last_error": (ctypes.c_char_p, []),
     }
@@ -208,6 +215,86 @@ def kernel_name(M: int, K: int, N: int, swiglu: bool, dtype) -> str:
     return load().fn_kernel_name(M, K, N, int(swiglu), _dt(dtype)).decode()
 
 
+# ------------------------------------------------------------ fp8 weights --
+@dataclasses.dataclass
+class PackedFp8:
+    """Folded weights quantised to E4M3 per output column: packed codes and
+    the column scales s (y = s * (x @ q) / rms(x))."""
+    data: "object"      # torch.uint8 tensor on the device, packed codes
+    scales: "object"    # torch.float32 tensor [N] on the device
+    K: int
+    N: int
+
+
+def packed_fp8_bytes(K: int, N: int) -> int:
+    n = load().fn_packed_fp8_bytes(K, N)
+    if n == 0 and N > 0:
+        raise ValueError(f"K={K} must be in [1, 2^20] and a multiple of 8; N={N} in [0, 2^24]")
+    return n
+
+
+def fold_weights_fp8(g, W, out: Optional[PackedFp8] = None) -> PackedFp8:
+    """Fold W' = round(g[k] * W[k, n]) in W's dtype, then quantise each column
+    to E4M3 with scale s[n] = max|W'[:, n]| / 448 (g=None quantises W)."""
+    torch = _torch()
+    _need_cuda("W", W)
+    if W.dim() != 2:
+        raise ValueError(f"W must be [K, N], got shape {tuple(W.shape)}")
+    K, N = W.shape
+    dt = _dt(W.dtype)
+    if g is not None:
+        _need_cuda("g", g)
+        if g.dtype != W.dtype or tuple(g.shape) != (K,):
+            raise ValueError(f"g must be [{K}] of dtype {W.dtype}, got {tuple(g.shape)} {g.dtype}")
+    nbytes = packed_fp8_bytes(K, N)
+    if out is None:
+        out = PackedFp8(torch.empty(nbytes, dtype=torch.uint8, device=W.device),
+                        torch.empty(N, dtype=torch.float32, device=W.device), K, N)
+    elif (out.K, out.N) != (K, N) or out.data.numel() != nbytes or out.scales.numel() != N:
+        raise ValueError("out does not match W's shape")
+    _check(load().fn_fold_weights_fp8(None if g is None else g.data_ptr(), W.data_ptr(), out.data.data_ptr(),
+                                      out.scales.data_ptr(), K, N, dt, _stream(W)))
+    return out
+
+
+def _check_x_fp8(x, P: PackedFp8):
+    torch = _torch()
+    _need_cuda("x", x)
+    if x.dim() != 2 or x.shape[1] != P.K:
+        raise ValueError(f"x must be [M, {P.K}], got {tuple(x.shape)}")
+    if x.dtype != torch.bfloat16:
+        raise ValueError(f"fp8-weight calls take bf16 activations, got {x.dtype}")
+    if x.device != P.data.device:
+        raise ValueError("x and the fp8 weights must be on the same device")
+
+
+def norm_proj_fp8(x, P: PackedFp8, eps: float = 1e-6, out=None):
+    """y = s * (x @ q) / sqrt(mean(x^2) + eps) with E4M3 weights, one launch."""
+    _check_x_fp8(x, P)
+    M, N = x.shape[0], P.N
+    y = _out(out, M, N, x)
+    _check(load().fn_norm_proj_fp8(x.data_ptr(), P.data.data_ptr(), P.scales.data_ptr(), y.data_ptr(), M, P.K, N,
+                                   eps, _stream(x)))
+    return y
+
+
+def norm_proj_swiglu_fp8(x, Pg: PackedFp8, Pu: PackedFp8, eps: float = 1e-6, out=None):
+    """out = silu(a) * b with E4M3 gate/up weights, one launch."""
+    _check_x_fp8(x, Pg)
+    if (Pu.K, Pu.N) != (Pg.K, Pg.N):
+        raise ValueError("gate and up weights must have the same K and N")
+    M, N = x.shape[0], Pg.N
+    y = _out(out, M, N, x)
+    _check(load().fn_norm_proj_swiglu_fp8(x.data_ptr(), Pg.data.data_ptr(), Pg.scales.data_ptr(), Pu.data.data_ptr(),
+                                          Pu.scales.data_ptr(), y.data_ptr(), M, Pg.K, N, eps, _stream(x)))
+    return y
+
+
+def kernel_name_fp8(M: int, K: int, N: int, swiglu: bool) -> str:
+    return load().fn_kernel_name_fp8(M, K, N, int(swiglu)).decode()
+
+
 __all__ = ["load", "fold_weights", "norm_proj", "norm_proj_swiglu", "rmsnorm", "silu_mul",
            "packed_weight_bytes", "kernel_name", "PackedWeights", "FlashNormError", "header_functions",
-           "LIB_PATH", "FN_F32", "FN_BF16"]
+           "LIB_PATH", "FN_F32", "FN_BF16", "PackedFp8", "packed_fp8_bytes", "fold_weights_fp8",
+           "norm_proj_fp8", "norm_proj_swiglu_fp8", "kernel_name_fp8"]

@@ -25,7 +25,8 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Per-source extras.  The decode kernels keep their few accumulators in
 # VGPRs (the AGPR form made the compiler shuffle accumulators every
 # iteration); the prefill kernel needs the AGPR file for its 256.
-FILE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+FILE_FLAGS = {"decode.hip": _VGPR_FORM, "decode_x.hip": _VGPR_FORM}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
                 "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
 

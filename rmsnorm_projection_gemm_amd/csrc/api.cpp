@@ -96,6 +96,35 @@ fn_status fused_common(const void* x, const void* wg, const void* wu, void* y, i
                     plan.name);
 }
 
+int64_t packed_fp8_bytes(int64_t K, int64_t N) { return ((N + 15) / 16) * ((K + 63) / 64) * 1024; }
+
+fn_status fp8_common(const void* x, const void* wg, const float* sg, const void* wu, const float* su, void* y,
+                     int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream, bool swiglu) {
+  g_last_error[0] = '\0';
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(M, N));
+  FN_TRY(check_eps(eps));
+  if (M == 0 || N == 0) return FN_OK;
+  if (x == nullptr) return fail(FN_ERR_NULL, "x is NULL");
+  if (wg == nullptr || sg == nullptr)
+    return fail(FN_ERR_NULL, swiglu ? "W8_gate or s_gate is NULL" : "W8_packed or scales is NULL");
+  if (swiglu && (wu == nullptr || su == nullptr)) return fail(FN_ERR_NULL, "W8_up or s_up is NULL");
+  if (y == nullptr) return fail(FN_ERR_NULL, swiglu ? "out is NULL" : "y is NULL");
+  if (!aligned(x, 16)) return fail(FN_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(wg, 16) || (swiglu && !aligned(wu, 16)))
+    return fail(FN_ERR_ALIGN, "packed fp8 weights must be 16-byte aligned");
+  if (!aligned(sg, 4) || (swiglu && !aligned(su, 4))) return fail(FN_ERR_ALIGN, "scales must be 4-byte aligned");
+  if (!aligned(y, 16)) return fail(FN_ERR_ALIGN, "output must be 16-byte aligned");
+  const int64_t xb = M * K * 2, yb = M * N * 2, wb = packed_fp8_bytes(K, N), sb = N * 4;
+  if (overlap(y, yb, x, xb) || overlap(y, yb, wg, wb) || overlap(y, yb, sg, sb) ||
+      (swiglu && (overlap(y, yb, wu, wb) || overlap(y, yb, su, sb))))
+    return fail(FN_ERR_ALIAS, "output overlaps an input");
+  const fn::FusedPlan plan = fn::plan_fp8(M, K, N, swiglu);
+  return hip_status(fn::launch_fp8(plan, x, wg, sg, swiglu ? wu : nullptr, swiglu ? su : nullptr, y, (int)M, (int)K,
+                                   (int)N, eps, stream),
+                    plan.name);
+}
+
 }  // namespace
 
 namespace fn {
@@ -184,6 +213,49 @@ fn_status fn_silu_mul(const void* h, void* out, int64_t M, int64_t N, fn_dtype d
     return fail(FN_ERR_ALIGN, "h and out must be aligned to their element size");
   if (overlap(out, M * N * e, h, M * 2 * N * e)) return fail(FN_ERR_ALIAS, "out overlaps h");
   return hip_status(fn::launch_silu_mul(to_dt(dt), h, out, (int)M, (int)N, stream), "silu_mul");
+}
+
+size_t fn_packed_fp8_bytes(int64_t K, int64_t N) {
+  if (K < 1 || K > kMaxK || K % 8 != 0 || N < 0 || N > kMaxN) return 0;
+  return (size_t)packed_fp8_bytes(K, N);
+}
+
+fn_status fn_fold_weights_fp8(const void* g, const void* W, void* W8_packed, float* scales, int64_t K, int64_t N,
+                              fn_dtype dt, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!dtype_ok(dt)) return fail(FN_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(0, N));
+  if (N == 0) return FN_OK;
+  if (W == nullptr) return fail(FN_ERR_NULL, "W is NULL");
+  if (W8_packed == nullptr || scales == nullptr) return fail(FN_ERR_NULL, "W8_packed or scales is NULL");
+  const int64_t e = esize(dt);
+  if ((g != nullptr && !aligned(g, (uintptr_t)e)) || !aligned(W, (uintptr_t)e))
+    return fail(FN_ERR_ALIGN, "g and W must be aligned to their element size");
+  if (!aligned(W8_packed, 16)) return fail(FN_ERR_ALIGN, "W8_packed must be 16-byte aligned");
+  if (!aligned(scales, 4)) return fail(FN_ERR_ALIGN, "scales must be 4-byte aligned");
+  const int64_t pb = packed_fp8_bytes(K, N);
+  if (overlap(W8_packed, pb, W, K * N * e) || overlap(W8_packed, pb, g, K * e) ||
+      overlap(scales, N * 4, W, K * N * e) || overlap(scales, N * 4, g, K * e) || overlap(scales, N * 4, W8_packed, pb))
+    return fail(FN_ERR_ALIAS, "W8_packed or scales overlaps an input or each other");
+  return hip_status(fn::launch_fold_fp8(to_dt(dt), g, W, W8_packed, scales, (int)K, (int)N, stream),
+                    "fold_weights_fp8");
+}
+
+fn_status fn_norm_proj_fp8(const void* x, const void* W8_packed, const float* scales, void* y, int64_t M, int64_t K,
+                           int64_t N, float eps, hipStream_t stream) {
+  return fp8_common(x, W8_packed, scales, nullptr, nullptr, y, M, K, N, eps, stream, false);
+}
+
+fn_status fn_norm_proj_swiglu_fp8(const void* x, const void* W8_gate, const float* s_gate, const void* W8_up,
+                                  const float* s_up, void* out, int64_t M, int64_t K, int64_t N, float eps,
+                                  hipStream_t stream) {
+  return fp8_common(x, W8_gate, s_gate, W8_up, s_up, out, M, K, N, eps, stream, true);
+}
+
+const char* fn_kernel_name_fp8(int64_t M, int64_t K, int64_t N, int swiglu) {
+  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
+  return fn::plan_fp8(M, K, N, swiglu != 0).name;
 }
 
 const char* fn_kernel_name(int64_t M, int64_t K, int64_t N, int swiglu, fn_dtype dt) {

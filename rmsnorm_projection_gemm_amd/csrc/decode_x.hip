@@ -1,23 +1,32 @@
-// Fused RMSNorm + projection (+ SwiGLU) for 17..64 rows (bf16), with x
-// shared through LDS.
+// Fused RMSNorm + projection (+ SwiGLU) with x shared through LDS: the bf16
+// path for 17..64 rows, and every row count with fp8 (E4M3) weights.
 //
 // Past 16 rows x stops being small next to W': at 64 rows it is 128 KiB per
 // 1024 k values, and a kernel that loads x into every wave's registers
 // (decode.hip) pushes about as many x bytes through each CU's vector memory
 // path as W' bytes, which is what bounds a skinny kernel on this chip (the
-// per-CU request rate, not HBM).  Here a workgroup owns NWV weight column
-// blocks -- one (or NC) per wave, for SwiGLU with both the gate and the up
-// stream -- and its waves walk the k range in lock step.  Per stage of U
-// k-blocks the x rows are fetched once for the workgroup, split across its
-// waves, straight into an LDS ring slot with direct global-to-LDS buffer
-// loads; every wave then reads its MFMA operands with ds_read_b128.  Each
-// wave streams its own W' fragments from HBM into registers with
-// non-temporal buffer loads, NS-1 stages ahead.
+// per-CU request rate, not HBM).  With fp8 weights the weight stream halves
+// and the same holds from a few rows on.  Here a workgroup owns NWV weight
+// column blocks -- one (or NC) per wave, for SwiGLU with both the gate and
+// the up stream -- and 16*MF rows (more rows tile over grid.y), and its waves
+// walk the k range in lock step.  Per stage of U k-blocks the x rows are
+// fetched once for the workgroup, split across its waves, straight into an
+// LDS ring slot with direct global-to-LDS buffer loads; every wave then reads
+// its MFMA operands with ds_read_b128.  Each wave streams its own weight
+// fragments from HBM into registers with non-temporal buffer loads, NS-1
+// stages ahead.
 //
 // x layout in a slot: each 1 KiB load carries 8 rows x 128 bytes (two
 // k-blocks), so every request is a whole cache line; the 16-byte chunks of
 // row r are stored permuted by r/2 so that the 16 lanes of each quarter
 // wave read 16 distinct bank groups.
+//
+// fp8 weights: one 16-byte lane load carries the lane's 8 codes of two
+// consecutive k-blocks, decoded in registers right before the MFMAs
+// ([Fused-kernel memory hierarchy] "Fused 커널은 왜 3~4배 빠른가", section
+// "트릭 2"); v_cvt_scalef32_pk_bf16_fp8 with scale 1 is exact (every E4M3
+// value is a bf16 value), and the column scale s[n] joins 1/RMS in the
+// epilogue ([FlashNorm digest] proposal 2, the deferred scale).
 //
 // Per k-block a wave runs MF projection MFMAs per weight stream, and per
 // stage a few Gram MFMAs (x x^T of the fragments it loaded) whose diagonals
@@ -44,6 +53,8 @@ struct DecodeXArgs {
   int nblocks;       // ceil(N / 16)
   int stages;        // ceil(kblocks / U)
   float eps;
+  const float* sg;   // fp8 weights: column scales of wg (else unused)
+  const float* su;   // fp8 weights: column scales of wu
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_x;
@@ -61,10 +72,24 @@ __device__ inline void wait_vmcnt_x() {
 
 constexpr uint32_t kOutOfRangeX = 0x80000000u;
 
+// 16 E4M3 codes (one 16-byte fp8 lane chunk) -> the lane's two bf16 B
+// operands: bytes 0..7 for the first k-block of the pair, 8..15 for the
+// second.  v_cvt_scalef32_pk_bf16_fp8 with scale 1 decodes two codes into
+// two bf16 exactly.
+__device__ inline void decode_e4m3x16(u32x4 w, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    lo[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+    lo[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+    hi[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, false));
+    hi[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, true));
+  }
+}
+
 // MF: 16-row blocks of x.  NC: 16-column blocks per wave (for SwiGLU each
 // with its gate and up stream).  NWV: waves, sharing the x fragments.  U:
 // k-blocks per stage.
-template <int MF, int NC, int NWV, bool SW, int U>
+template <int MF, int NC, int NWV, bool SW, int U, bool F8>
 __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   constexpr int NS = 4;                    // LDS ring slots
   constexpr int D = NS - 1;                // stages in flight
@@ -72,7 +97,8 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   constexpr int NST = NMAT * NC;           // weight streams per wave
   constexpr int XF = U * MF;               // x loads (1 KiB each) per stage
   constexpr int XPW = (XF + NWV - 1) / NWV;   // x loads each wave issues per stage
-  constexpr int LPW = U * NST + XPW;       // vector-memory ops per wave per stage
+  constexpr int WLD = F8 ? U / 2 : U;      // weight loads per stream per stage (fp8: one per k-block pair)
+  constexpr int LPW = WLD * NST + XPW;     // vector-memory ops per wave per stage
   // Loads q >= XF (when NWV does not divide XF) fetch nothing and write
   // zeros into the slot's padding, so every wave issues the same count.
   constexpr int SLOT = XPW * NWV * kFragBytes;
@@ -93,9 +119,13 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int nb0 = (blockIdx.x * NWV + w) * NC;   // first column block of this wave
-  const int64_t kfrag = (int64_t)a.kblocks * kFragBytes;
+  const int m0 = blockIdx.y * MF * 16;           // first row of this workgroup
+  // bytes of one packed column block: a fragment per k-block (bf16) or per
+  // pair of k-blocks (fp8)
+  const int64_t kfrag = (int64_t)(F8 ? (a.kblocks + 1) / 2 : a.kblocks) * kFragBytes;
 
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc_x(a.x, (int64_t)min(MF * 16, a.M) * a.K * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc_x(static_cast<const __bf16*>(a.x) + (size_t)m0 * a.K,
+                                                (int64_t)min(MF * 16, a.M - m0) * a.K * 2);
   // weight stream c = m * NC + j: matrix m, column block nb0 + j (reads zero past N)
   __amdgpu_buffer_rsrc_t wr[NST];
 #pragma unroll
@@ -149,12 +179,12 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
                                                0);
     }
   };
-  u32x4 wv[NS][U][NST];
+  u32x4 wv[NS][WLD][NST];
   auto issue_w = [&](int b, int st) __attribute__((always_inline)) {
     const uint32_t live = (uint32_t)((st - a.stages) >> 31);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t off = (uint32_t)((st * U + u) * kFragBytes + lane * 16);
+    for (int u = 0; u < WLD; ++u) {
+      const uint32_t off = (uint32_t)((st * WLD + u) * kFragBytes + lane * 16);
 #pragma unroll
       for (int c = 0; c < NST; ++c)
         wv[b][u][c] = __builtin_bit_cast(
@@ -193,12 +223,25 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     issue_w((s + D) % NS, st + D);
     issue_x(slot_ptr((s + D) % NS), st + D);
     __builtin_amdgcn_sched_barrier(0);
+    // B operands: the bf16 fragments as loaded, or the two halves of each
+    // fp8 fragment decoded exactly to bf16 (every E4M3 value is a bf16 value)
+    u32x4 bw[U][NST];
+#pragma unroll
+    for (int c = 0; c < NST; ++c) {
+      if constexpr (F8) {
+#pragma unroll
+        for (int p = 0; p < U / 2; ++p) decode_e4m3x16(wv[s][p][c], bw[2 * p][c], bw[2 * p + 1][c]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) bw[u][c] = wv[s][u][c];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
-        for (int c = 0; c < NST; ++c) acc[c][i] = mfma_chunk<__bf16>(xv[u][i], wv[s][u][c], acc[c][i]);
+        for (int c = 0; c < NST; ++c) acc[c][i] = mfma_chunk<__bf16>(xv[u][i], bw[u][c], acc[c][i]);
 #pragma unroll
     for (int j = 0; j < XPW; ++j) gram[j] = mfma_chunk<__bf16>(xg[j], xg[j], gram[j]);
   };
@@ -234,7 +277,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int rr = 4 * lgrp + e;
-      const int row = 16 * i + rr;
+      const int row = m0 + 16 * i + rr;
       // Gram accumulator j of wave v holds fragment q = v + NWV*j, row block q % MF
       float ss = 0.f;
 #pragma unroll
@@ -247,7 +290,10 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
       for (int j = 0; j < NC; ++j) {
         const int col = (nb0 + j) * 16 + lrow;
         if (row < a.M && col < a.N) {
-          const float val = SW ? silu_times(acc[j][i][e] * inv, acc[NC + j][i][e] * inv) : acc[j][i][e] * inv;
+          // fp8 weights: the column scale joins 1/RMS
+          const float ig = F8 ? a.sg[col] * inv : inv;
+          const float iu = F8 && SW ? a.su[col] * inv : inv;
+          const float val = SW ? silu_times(acc[j][i][e] * ig, acc[NC + j][i][e] * iu) : acc[j][i][e] * ig;
           Store<__bf16>::one(static_cast<__bf16*>(a.y) + (size_t)row * a.N + col, val);
         }
       }
@@ -258,16 +304,27 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 struct DecodeXInstance {
   const void* fn;
   int mf, nc, nwv, u;
-  bool sw;
+  bool sw, f8;
   const char* name;
 };
 
-#define FN_DECODE_X(MF, NC, NWV, SW, U, NAME) \
-  DecodeXInstance { reinterpret_cast<const void*>(&decode_x_kernel<MF, NC, NWV, SW, U>), MF, NC, NWV, U, SW, NAME }
+#define FN_DECODE_X(MF, NC, NWV, SW, U, NAME)                                                            \
+  DecodeXInstance {                                                                                     \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, NC, NWV, SW, U, false>), MF, NC, NWV, U, SW, false, NAME \
+  }
+#define FN_DECODE_X8(MF, NC, NWV, SW, U, NAME)                                                         \
+  DecodeXInstance {                                                                                   \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, NC, NWV, SW, U, true>), MF, NC, NWV, U, SW, true, NAME \
+  }
 
+// Rows tile over grid.y in blocks of 16*MF; sg and su are the fp8 column
+// scales (null for bf16 weights).
 inline hipError_t launch_decode_x_instance(const DecodeXInstance& d, const void* x, const void* wg, const void* wu,
-                                           void* y, int M, int K, int N, float eps, hipStream_t stream) {
+                                           void* y, int M, int K, int N, float eps, hipStream_t stream,
+                                           const float* sg = nullptr, const float* su = nullptr) {
   DecodeXArgs a;
+  a.sg = sg;
+  a.su = su;
   a.x = x;
   a.wg = wg;
   a.wu = wu;
@@ -280,8 +337,8 @@ inline hipError_t launch_decode_x_instance(const DecodeXInstance& d, const void*
   a.stages = (int)ceil_div(a.kblocks, d.u);
   a.eps = eps;
   void* args[] = {&a};
-  return hipLaunchKernel(d.fn, dim3((unsigned)ceil_div(a.nblocks, d.nc * d.nwv)), dim3(kWave * d.nwv), args, 0,
-                         stream);
+  return hipLaunchKernel(d.fn, dim3((unsigned)ceil_div(a.nblocks, d.nc * d.nwv), (unsigned)ceil_div(M, 16 * d.mf)),
+                         dim3(kWave * d.nwv), args, 0, stream);
 }
 
 #ifndef FN_DECODE_X_NO_TABLE
@@ -300,33 +357,63 @@ static const DecodeXInstance kDecodeX[] = {
     FN_DECODE_X(4, 1, 3, true, 2, "decode_swiglu_bf16_m64_xlds_w3_u2"),
 };
 
-static const DecodeXInstance* find_decode_x(int mf, bool sw) {
-  for (const DecodeXInstance& d : kDecodeX)
+// fp8 weights, measured the same way: with half the weight bytes per stage
+// the sixteen-row rungs want longer stages (eight k-blocks for a plain
+// projection, four with SwiGLU), the 64-row SwiGLU rung four waves.
+static const DecodeXInstance kDecodeF8[] = {
+    FN_DECODE_X8(1, 1, 3, false, 8, "decode_fp8_m16_xlds_w3_u8"),
+    FN_DECODE_X8(2, 1, 3, false, 4, "decode_fp8_m32_xlds_w3_u4"),
+    FN_DECODE_X8(4, 1, 3, false, 2, "decode_fp8_m64_xlds_w3_u2"),
+    FN_DECODE_X8(1, 1, 3, true, 4, "decode_swiglu_fp8_m16_xlds_w3_u4"),
+    FN_DECODE_X8(2, 1, 3, true, 4, "decode_swiglu_fp8_m32_xlds_w3_u4"),
+    FN_DECODE_X8(4, 1, 4, true, 2, "decode_swiglu_fp8_m64_xlds_w4_u2"),
+};
+
+template <size_t L>
+static const DecodeXInstance* find_instance(const DecodeXInstance (&t)[L], int mf, bool sw) {
+  for (const DecodeXInstance& d : t)
     if (d.mf == mf && d.sw == sw) return &d;
   return nullptr;
 }
 
-// Row ladder rungs 32 and 64; one workgroup row, NC*NWV column blocks each.
-FusedPlan plan_decode_x(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
-  (void)dt;
-  (void)K;
-  const DecodeXInstance* d = find_decode_x(M <= 32 ? 2 : 4, swiglu);
+static FusedPlan plan_of(const DecodeXInstance* d, int kind, int64_t M, int64_t N) {
   FusedPlan p{};
-  p.kind = 2;
+  p.kind = kind;
   p.mf = d->mf;
   p.nf = d->nc * d->nwv;
   p.waves = d->nwv;
-  p.grid = dim3((unsigned)ceil_div(ceil_div(N, 16), p.nf), 1, 1);
+  p.grid = dim3((unsigned)ceil_div(ceil_div(N, 16), p.nf), (unsigned)ceil_div(M, 16 * d->mf), 1);
   p.block = dim3(kWave * p.waves, 1, 1);
   p.name = d->name;
   return p;
 }
 
+// bf16 row ladder rungs 32 and 64 (one row of workgroups).
+FusedPlan plan_decode_x(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
+  (void)dt;
+  (void)K;
+  return plan_of(find_instance(kDecodeX, M <= 32 ? 2 : 4, swiglu), 2, M, N);
+}
+
 hipError_t launch_decode_x(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
                            int M, int K, int N, float eps, hipStream_t stream) {
-  const DecodeXInstance* d = find_decode_x(p.mf, wu != nullptr);
+  const DecodeXInstance* d = find_instance(kDecodeX, p.mf, wu != nullptr);
   if (dt != DType::BF16 || d == nullptr || M > 16 * d->mf) return hipErrorInvalidValue;
   return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream);
+}
+
+// fp8 row ladder 16 / 32 / 64; past 64 rows the 64-row tiles repeat over
+// grid.y (each row tile streams the weights again: a decode design).
+FusedPlan plan_fp8(int64_t M, int64_t K, int64_t N, bool swiglu) {
+  (void)K;
+  return plan_of(find_instance(kDecodeF8, M <= 16 ? 1 : (M <= 32 ? 2 : 4), swiglu), 3, M, N);
+}
+
+hipError_t launch_fp8(const FusedPlan& p, const void* x, const void* wg, const float* sg, const void* wu,
+                      const float* su, void* y, int M, int K, int N, float eps, hipStream_t stream) {
+  const DecodeXInstance* d = find_instance(kDecodeF8, p.mf, wu != nullptr);
+  if (d == nullptr) return hipErrorInvalidValue;
+  return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream, sg, su);
 }
 #endif
 

@@ -13,7 +13,8 @@ inline int k_per_block(DType t) { return t == DType::F32 ? 16 : 32; }   // KB of
 
 // Kernel instance chosen for one fused call.
 struct FusedPlan {
-  int kind;           // 0 = decode (<= 16 rows, or fp32), 1 = prefill (tiled), 2 = decode with x in LDS
+  int kind;           // 0 = decode (<= 16 rows, or fp32), 1 = prefill (tiled), 2 = decode with x in LDS,
+                      // 3 = fp8 weights (x in LDS, rows tiled over grid.y)
   int mf;             // 16-row fragments per workgroup (decode)
   int nf;             // 16-column fragments per workgroup (decode)
   int waves;          // waves per workgroup
@@ -40,6 +41,14 @@ hipError_t launch_prefill(DType dt, const FusedPlan& plan, const void* x, const 
 
 hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
                        int K, int N, hipStream_t stream);
+
+// fp8 (E4M3) weights: fold + quantise, and the fused calls (bf16 activations).
+hipError_t launch_fold_fp8(DType dt, const void* g, const void* W, void* W8, float* scales,
+                           int K, int N, hipStream_t stream);
+FusedPlan plan_fp8(int64_t M, int64_t K, int64_t N, bool swiglu);
+hipError_t launch_fp8(const FusedPlan& plan, const void* x, const void* wg, const float* sg,
+                      const void* wu, const float* su, void* y, int M, int K, int N, float eps,
+                      hipStream_t stream);
 
 hipError_t launch_fused(DType dt, const FusedPlan& plan, const void* x,
                         const void* w_gate, const void* w_up, void* y,

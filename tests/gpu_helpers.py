@@ -68,3 +68,17 @@ def pack_host(W_store: np.ndarray, dtype: str) -> np.ndarray:
     # [kb, grp, v, nb, j] -> [nb, kb, grp, j, v]
     p = pad.reshape(kbl, 4, V, nbl, 16).transpose(3, 0, 1, 4, 2)
     return np.ascontiguousarray(p).view(np.uint8).reshape(-1)
+
+
+def pack_fp8_host(codes: np.ndarray) -> np.ndarray:
+    """Packed fp8 layout of a [K,N] matrix of E4M3 codes, as raw bytes: code
+    (k, n) at fragment (n//16, k//64), lane ((k%32)//8)*16 + n%16, byte
+    (k%64 >= 32)*8 + k%8; padding zero."""
+    K, N = codes.shape
+    kp = -(-K // 64)
+    nbl = -(-N // 16)
+    pad = np.zeros((kp * 64, nbl * 16), dtype=np.uint8)
+    pad[:K, :N] = codes
+    # k = ((kp*2 + h)*4 + grp)*8 + j, n = nb*16 + c -> [nb, kp, grp, c, h, j]
+    p = pad.reshape(kp, 2, 4, 8, nbl, 16).transpose(4, 0, 2, 5, 1, 3)
+    return np.ascontiguousarray(p).reshape(-1)

@@ -140,3 +140,61 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fn, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         fn.load()
+
+
+# ------------------------------------------------------------ fp8 weights --
+@pytest.mark.parametrize("K,N,want", [(64, 16, 1024), (8, 1, 1024), (72, 17, 4096), (4096, 12288, 50331648)])
+def test_packed_fp8_bytes(lib, K, N, want):
+    assert lib.fn_packed_fp8_bytes(K, N) == want
+
+
+@pytest.mark.parametrize("K,N", [(0, 16), (12, 16), (16, -1), ((1 << 20) + 8, 16)])
+def test_packed_fp8_bytes_invalid(lib, K, N):
+    assert lib.fn_packed_fp8_bytes(K, N) == 0
+
+
+def test_fp8_kernel_names(lib):
+    assert lib.fn_kernel_name_fp8(16, 4096, 12288, 0).decode().startswith("decode_fp8_m16")
+    assert lib.fn_kernel_name_fp8(17, 4096, 12288, 0).decode().startswith("decode_fp8_m32")
+    assert lib.fn_kernel_name_fp8(64, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_m64")
+    assert lib.fn_kernel_name_fp8(4096, 4096, 12288, 1).decode().startswith("decode_swiglu_fp8_m64")
+    assert lib.fn_kernel_name_fp8(0, 4096, 16, 0) == b"invalid"
+
+
+def _np8(lib, x=0x1000, w=0x20000, s=0x30000, y=0x40000, M=4, K=16, N=16, eps=1e-6):
+    return lib.fn_norm_proj_fp8(x, w, s, y, M, K, N, eps, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(x=None), NULL, "x is NULL"),
+    (dict(w=None), NULL, "W8_packed"),
+    (dict(s=None), NULL, "scales"),
+    (dict(y=None), NULL, "y is NULL"),
+    (dict(K=12), SHAPE, "multiple of 8"),
+    (dict(x=0x1008), ALIGN, "x must be"),
+    (dict(w=0x20008), ALIGN, "fp8 weights"),
+    (dict(s=0x30002), ALIGN, "scales"),
+    (dict(eps=-1.0), EPS, "eps"),
+    (dict(y=0x30000), ALIAS, "overlaps"),
+    (dict(y=0x20000), ALIAS, "overlaps"),
+])
+def test_norm_proj_fp8_rejects(lib, kwargs, status, needle):
+    assert _np8(lib, **kwargs) == status
+    assert needle in lib.fn_last_error().decode()
+
+
+def test_fp8_swiglu_and_fold_reject(lib):
+    sw = lib.fn_norm_proj_swiglu_fp8
+    assert sw(0x1000, 0x20000, 0x30000, None, 0x31000, 0x40000, 4, 16, 16, 1e-6, None) == NULL
+    assert sw(0x1000, 0x20000, 0x30000, 0x21000, None, 0x40000, 4, 16, 16, 1e-6, None) == NULL
+    assert sw(0x1000, 0x20000, 0x30000, 0x21000, 0x31000, 0x31000, 4, 16, 16, 1e-6, None) == ALIAS
+    assert sw(None, None, None, None, None, None, 0, 16, 16, 1e-6, None) == OK
+    f = lib.fn_fold_weights_fp8
+    assert f(0x100, None, 0x10000, 0x20000, 16, 16, BF16, None) == NULL
+    assert f(0x100, 0x1000, 0x10000, None, 16, 16, BF16, None) == NULL
+    assert f(0x100, 0x1000, 0x10008, 0x20000, 16, 16, BF16, None) == ALIGN
+    assert f(0x100, 0x1000, 0x10000, 0x20002, 16, 16, BF16, None) == ALIGN
+    assert f(0x100, 0x1000, 0x10000, 0x10000, 16, 16, BF16, None) == ALIAS
+    assert f(0x100, 0x1000, 0x1000, 0x20000, 16, 16, BF16, None) == ALIAS
+    assert f(0x100, 0x1000, 0x10000, 0x20000, 16, 16, 9, None) == DTYPE
+    assert f(None, None, None, None, 16, 0, BF16, None) == OK
