@@ -202,6 +202,72 @@ const char* fn_kernel_name_fp8(int64_t M, int64_t K, int64_t N, int swiglu);
  * "decode_bf16_m16_n1_w4"; a static string, "invalid" for bad shapes. */
 const char* fn_kernel_name(int64_t M, int64_t K, int64_t N, int swiglu, fn_dtype dt);
 
+/* ---------------------------------------------------------------------------
+ * Recorded steps: a sequence of fused calls replayed with one launch
+ *
+ * A decode step starts the norm + projection once per layer, dozens of
+ * times, and on a GPU the starts and waits between small kernels cost more
+ * than their arithmetic ([FlashNorm digest], summary bullets "problem
+ * definition" and "GPU weakness"; [Fused kernels] closing summary, item 3:
+ * launch overhead matters for small units of work).  fn_step_create records
+ * the calls, in order, into a HIP graph once; fn_step_launch replays them
+ * with a single graph launch.
+ *
+ * Every pointer and size is fixed when the step is recorded: a replay reads
+ * whatever the x buffers hold at that time and overwrites the same outputs,
+ * so a caller refreshes its inputs in place between replays.  The calls of a
+ * step run in the order given, each after the previous one has finished
+ * (stream order), so a later call may read an earlier call's output.
+ * ------------------------------------------------------------------------- */
+
+typedef enum {
+  FN_CALL_NORM_PROJ = 0,            /* fn_norm_proj: w_gate = W_packed */
+  FN_CALL_NORM_PROJ_SWIGLU = 1,     /* fn_norm_proj_swiglu: w_gate, w_up */
+  FN_CALL_NORM_PROJ_FP8 = 2,        /* fn_norm_proj_fp8: w_gate = W8_packed, s_gate = scales */
+  FN_CALL_NORM_PROJ_SWIGLU_FP8 = 3  /* fn_norm_proj_swiglu_fp8: w_gate, s_gate, w_up, s_up */
+} fn_call_kind;
+
+/* One call of a step: the arguments of the entry point `kind` names.
+ * Fields a kind does not use are ignored (w_up for single projections,
+ * s_gate / s_up for bf16 and fp32 weights, dt for the fp8 kinds, which take
+ * bf16 activations). */
+typedef struct {
+  fn_call_kind kind;
+  const void* x;
+  const void* w_gate;
+  const void* w_up;
+  const float* s_gate;
+  const float* s_up;
+  void* y;
+  int64_t M, K, N;
+  float eps;
+  fn_dtype dt;
+} fn_call;
+
+typedef struct fn_step_s* fn_step;   /* opaque handle */
+
+/* Validate every call exactly as its entry point would (no HIP call is made
+ * before all of them pass), then record them into a HIP graph on a private
+ * stream and instantiate it.  calls: host array of n_calls >= 1 entries,
+ * copied; *out receives the handle.  Calls with M == 0 or N == 0 record
+ * nothing.  Unlike the per-call entry points this allocates: host memory
+ * for the handle and the HIP runtime's graph objects (freed by
+ * fn_step_destroy).  An invalid call returns its status with
+ * "call i: ..." in fn_last_error() and *out = NULL. */
+fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out);
+
+/* Replay the recorded calls on `stream` with one graph launch; allocates
+ * nothing.  A step must not be replayed on two streams at once (its
+ * replays share the outputs). */
+fn_status fn_step_launch(fn_step step, hipStream_t stream);
+
+/* Number of calls recorded (the calls with M, N >= 1); -1 for NULL. */
+int64_t fn_step_num_kernels(fn_step step);
+
+/* Release the graph and the handle; NULL is a no-op.  The caller makes
+ * sure no replay is still running (e.g. synchronises its stream). */
+fn_status fn_step_destroy(fn_step step);
+
 /* Static description of a status code. */
 const char* fn_status_string(fn_status s);
 

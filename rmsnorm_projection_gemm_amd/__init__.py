@@ -11,6 +11,8 @@ raises.
     out = fn.norm_proj_swiglu(x, Wg, Wu) # silu(a) * b, one launch
     P8 = fn.fold_weights_fp8(g, W)       # W' quantised to E4M3 per column
     y8 = fn.norm_proj_fp8(x, P8)         # y = s * (x q) / rms(x), one launch
+    st = fn.Step(); st.norm_proj(x, Wp, y); st.record()
+    st.launch()                          # every recorded call, one graph launch
 """
 from __future__ import annotations
 
@@ -69,6 +71,10 @@ def load():
         "fn_norm_proj_fp8": (i32, [vp, vp, vp, vp, i64, i64, i64, f32, vp]),
         "fn_norm_proj_swiglu_fp8": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp]),
         "fn_kernel_name_fp8": (ctypes.c_char_p, [i64, i64, i64, i32]),
+        "fn_step_create": (i32, [vp, i64, ctypes.POINTER(vp)]),
+        "fn_step_launch": (i32, [vp, vp]),
+        "fn_step_num_kernels": (i64, [vp]),
+        "fn_step_destroy": (i32, [vp]),
         "fn_status_string": (ctypes.c_char_p, [i32]),
         "fn_last_error": (ctypes.c_char_p, []),
     }
@@ -294,7 +300,96 @@ def kernel_name_fp8(M: int, K: int, N: int, swiglu: bool) -> str:
     return load().fn_kernel_name_fp8(M, K, N, int(swiglu)).decode()
 
 
+# ------------------------------------------------------- recorded steps --
+FN_CALL_NORM_PROJ, FN_CALL_NORM_PROJ_SWIGLU, FN_CALL_NORM_PROJ_FP8, FN_CALL_NORM_PROJ_SWIGLU_FP8 = 0, 1, 2, 3
+
+
+class FnCall(ctypes.Structure):
+    """struct fn_call of include/flashnorm.h."""
+    _fields_ = [("kind", ctypes.c_int), ("x", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("eps", ctypes.c_float), ("dt", ctypes.c_int)]
+
+
+class Step:
+    """A sequence of fused calls recorded once into a HIP graph and replayed
+    with one launch (fn_step_create / fn_step_launch).  Every call names its
+    output buffer; pointers are fixed at record() time, so refresh inputs in
+    place between replays.  The tensors stay referenced by the Step."""
+
+    def __init__(self):
+        self._calls = []
+        self._keep = []
+        self._handle = None
+
+    def _add(self, kind, x, wg, wu, sg, su, out, M, K, N, eps, dt, keep):
+        if self._handle is not None:
+            raise RuntimeError("the step is already recorded")
+        self._calls.append(FnCall(kind, x.data_ptr(), wg, wu, sg, su, out.data_ptr(), M, K, N, eps, dt))
+        self._keep.extend(keep)
+
+    def norm_proj(self, x, Wp: PackedWeights, out, eps: float = 1e-6):
+        _check_x(x, Wp)
+        _out(out, x.shape[0], Wp.N, x)
+        self._add(FN_CALL_NORM_PROJ, x, Wp.data.data_ptr(), None, None, None, out, x.shape[0], Wp.K, Wp.N, eps,
+                  _dt(x.dtype), (x, Wp.data, out))
+
+    def norm_proj_swiglu(self, x, Wg: PackedWeights, Wu: PackedWeights, out, eps: float = 1e-6):
+        _check_x(x, Wg)
+        if (Wu.K, Wu.N, Wu.dtype) != (Wg.K, Wg.N, Wg.dtype):
+            raise ValueError("gate and up weights must have the same K, N and dtype")
+        _out(out, x.shape[0], Wg.N, x)
+        self._add(FN_CALL_NORM_PROJ_SWIGLU, x, Wg.data.data_ptr(), Wu.data.data_ptr(), None, None, out,
+                  x.shape[0], Wg.K, Wg.N, eps, _dt(x.dtype), (x, Wg.data, Wu.data, out))
+
+    def norm_proj_fp8(self, x, P: PackedFp8, out, eps: float = 1e-6):
+        _check_x_fp8(x, P)
+        _out(out, x.shape[0], P.N, x)
+        self._add(FN_CALL_NORM_PROJ_FP8, x, P.data.data_ptr(), None, P.scales.data_ptr(), None, out,
+                  x.shape[0], P.K, P.N, eps, FN_BF16, (x, P.data, P.scales, out))
+
+    def norm_proj_swiglu_fp8(self, x, Pg: PackedFp8, Pu: PackedFp8, out, eps: float = 1e-6):
+        _check_x_fp8(x, Pg)
+        if (Pu.K, Pu.N) != (Pg.K, Pg.N):
+            raise ValueError("gate and up weights must have the same K and N")
+        _out(out, x.shape[0], Pg.N, x)
+        self._add(FN_CALL_NORM_PROJ_SWIGLU_FP8, x, Pg.data.data_ptr(), Pu.data.data_ptr(), Pg.scales.data_ptr(),
+                  Pu.scales.data_ptr(), out, x.shape[0], Pg.K, Pg.N, eps, FN_BF16,
+                  (x, Pg.data, Pg.scales, Pu.data, Pu.scales, out))
+
+    def record(self):
+        """Validate and record the calls (fn_step_create)."""
+        if self._handle is not None:
+            raise RuntimeError("the step is already recorded")
+        arr = (FnCall * len(self._calls))(*self._calls)
+        h = ctypes.c_void_p()
+        _check(load().fn_step_create(arr, len(self._calls), ctypes.byref(h)))
+        self._handle = h
+        return self
+
+    @property
+    def num_kernels(self) -> int:
+        return load().fn_step_num_kernels(self._handle)
+
+    def launch(self, stream=None):
+        """Replay every recorded call with one graph launch on `stream`
+        (default: the current stream of the first call's device)."""
+        if self._handle is None:
+            raise RuntimeError("record() the step first")
+        if stream is None:
+            stream = _stream(self._keep[0])
+        _check(load().fn_step_launch(self._handle, stream))
+
+    def close(self):
+        """Release the graph; the caller makes sure no replay is running."""
+        if self._handle is not None:
+            _check(load().fn_step_destroy(self._handle))
+            self._handle = None
+
+
 __all__ = ["load", "fold_weights", "norm_proj", "norm_proj_swiglu", "rmsnorm", "silu_mul",
            "packed_weight_bytes", "kernel_name", "PackedWeights", "FlashNormError", "header_functions",
            "LIB_PATH", "FN_F32", "FN_BF16", "PackedFp8", "packed_fp8_bytes", "fold_weights_fp8",
-           "norm_proj_fp8", "norm_proj_swiglu_fp8", "kernel_name_fp8"]
+           "norm_proj_fp8", "norm_proj_swiglu_fp8", "kernel_name_fp8", "Step", "FnCall", "FN_CALL_NORM_PROJ",
+           "FN_CALL_NORM_PROJ_SWIGLU", "FN_CALL_NORM_PROJ_FP8", "FN_CALL_NORM_PROJ_SWIGLU_FP8"]

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <new>
 
 #include "fn_launch.h"
 
@@ -70,8 +71,10 @@ fn_status hip_status(hipError_t e, const char* what) {
     if (s_ != FN_OK) return s_;       \
   } while (0)
 
+// check_only: validate and return without launching (recorded steps check
+// every call before recording any).
 fn_status fused_common(const void* x, const void* wg, const void* wu, void* y, int64_t M, int64_t K,
-                       int64_t N, float eps, fn_dtype dt, hipStream_t stream, bool swiglu) {
+                       int64_t N, float eps, fn_dtype dt, hipStream_t stream, bool swiglu, bool check_only = false) {
   g_last_error[0] = '\0';
   if (!dtype_ok(dt)) return fail(FN_ERR_DTYPE, "unknown dtype %d", (int)dt);
   FN_TRY(check_k(K));
@@ -90,6 +93,7 @@ fn_status fused_common(const void* x, const void* wg, const void* wu, void* y, i
   const int64_t xb = M * K * e, yb = M * N * e, wb = packed_bytes(K, N, dt);
   if (overlap(y, yb, x, xb) || overlap(y, yb, wg, wb) || (swiglu && overlap(y, yb, wu, wb)))
     return fail(FN_ERR_ALIAS, "output overlaps an input");
+  if (check_only) return FN_OK;
   const fn::DType t = to_dt(dt);
   const fn::FusedPlan plan = fn::plan_fused(t, M, K, N, swiglu);
   return hip_status(fn::launch_fused(t, plan, x, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, eps, stream),
@@ -99,7 +103,8 @@ fn_status fused_common(const void* x, const void* wg, const void* wu, void* y, i
 int64_t packed_fp8_bytes(int64_t K, int64_t N) { return ((N + 15) / 16) * ((K + 63) / 64) * 1024; }
 
 fn_status fp8_common(const void* x, const void* wg, const float* sg, const void* wu, const float* su, void* y,
-                     int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream, bool swiglu) {
+                     int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream, bool swiglu,
+                     bool check_only = false) {
   g_last_error[0] = '\0';
   FN_TRY(check_k(K));
   FN_TRY(check_mn(M, N));
@@ -119,13 +124,44 @@ fn_status fp8_common(const void* x, const void* wg, const float* sg, const void*
   if (overlap(y, yb, x, xb) || overlap(y, yb, wg, wb) || overlap(y, yb, sg, sb) ||
       (swiglu && (overlap(y, yb, wu, wb) || overlap(y, yb, su, sb))))
     return fail(FN_ERR_ALIAS, "output overlaps an input");
+  if (check_only) return FN_OK;
   const fn::FusedPlan plan = fn::plan_fp8(M, K, N, swiglu);
   return hip_status(fn::launch_fp8(plan, x, wg, sg, swiglu ? wu : nullptr, swiglu ? su : nullptr, y, (int)M, (int)K,
                                    (int)N, eps, stream),
                     plan.name);
 }
 
+// One recorded call: validate (check_only) or enqueue it on `stream`.
+fn_status run_call(const fn_call& c, hipStream_t stream, bool check_only) {
+  switch (c.kind) {
+    case FN_CALL_NORM_PROJ:
+      return fused_common(c.x, c.w_gate, nullptr, c.y, c.M, c.K, c.N, c.eps, c.dt, stream, false, check_only);
+    case FN_CALL_NORM_PROJ_SWIGLU:
+      return fused_common(c.x, c.w_gate, c.w_up, c.y, c.M, c.K, c.N, c.eps, c.dt, stream, true, check_only);
+    case FN_CALL_NORM_PROJ_FP8:
+      return fp8_common(c.x, c.w_gate, c.s_gate, nullptr, nullptr, c.y, c.M, c.K, c.N, c.eps, stream, false,
+                        check_only);
+    case FN_CALL_NORM_PROJ_SWIGLU_FP8:
+      return fp8_common(c.x, c.w_gate, c.s_gate, c.w_up, c.s_up, c.y, c.M, c.K, c.N, c.eps, stream, true,
+                        check_only);
+  }
+  return fail(FN_ERR_DTYPE, "unknown call kind %d", (int)c.kind);
+}
+
+// Prefix the current error text with the index of the failing call.
+fn_status call_failed(fn_status s, int64_t i) {
+  char detail[sizeof g_last_error];
+  std::memcpy(detail, g_last_error, sizeof detail);
+  return fail(s, "call %lld: %s", (long long)i, detail);
+}
+
 }  // namespace
+
+struct fn_step_s {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int64_t kernels = 0;
+};
 
 namespace fn {
 
@@ -251,6 +287,71 @@ fn_status fn_norm_proj_swiglu_fp8(const void* x, const void* W8_gate, const floa
                                   const float* s_up, void* out, int64_t M, int64_t K, int64_t N, float eps,
                                   hipStream_t stream) {
   return fp8_common(x, W8_gate, s_gate, W8_up, s_up, out, M, K, N, eps, stream, true);
+}
+
+fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out) {
+  g_last_error[0] = '\0';
+  if (out == nullptr) return fail(FN_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  if (calls == nullptr) return fail(FN_ERR_NULL, "calls is NULL");
+  if (n_calls < 1 || n_calls > (int64_t(1) << 20))
+    return fail(FN_ERR_SHAPE, "n_calls=%lld must be in [1, 2^20]", (long long)n_calls);
+  int64_t kernels = 0;
+  for (int64_t i = 0; i < n_calls; ++i) {
+    const fn_status s = run_call(calls[i], nullptr, true);
+    if (s != FN_OK) return call_failed(s, i);
+    if (calls[i].M > 0 && calls[i].N > 0) ++kernels;
+  }
+  // Record on a private stream (default priority), then instantiate.
+  hipStream_t cs = nullptr;
+  FN_TRY(hip_status(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "step: stream"));
+  fn_status st = hip_status(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal), "step: begin capture");
+  if (st == FN_OK) {
+    for (int64_t i = 0; i < n_calls && st == FN_OK; ++i) {
+      st = run_call(calls[i], cs, false);
+      if (st != FN_OK) st = call_failed(st, i);
+    }
+    hipGraph_t graph = nullptr;
+    const fn_status end = hip_status(hipStreamEndCapture(cs, &graph), "step: end capture");
+    if (st == FN_OK) st = end;
+    hipGraphExec_t exec = nullptr;
+    if (st == FN_OK) st = hip_status(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0), "step: instantiate");
+    if (st == FN_OK) {
+      fn_step h = new (std::nothrow) fn_step_s;
+      if (h == nullptr) {
+        st = fail(FN_ERR_HIP, "step: out of host memory");
+      } else {
+        h->graph = graph;
+        h->exec = exec;
+        h->kernels = kernels;
+        *out = h;
+      }
+    }
+    if (st != FN_OK) {
+      if (exec != nullptr) (void)hipGraphExecDestroy(exec);
+      if (graph != nullptr) (void)hipGraphDestroy(graph);
+    }
+  }
+  (void)hipStreamDestroy(cs);
+  return st;
+}
+
+fn_status fn_step_launch(fn_step step, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (step == nullptr) return fail(FN_ERR_NULL, "step is NULL");
+  return hip_status(hipGraphLaunch(step->exec, stream), "step: launch");
+}
+
+int64_t fn_step_num_kernels(fn_step step) { return step == nullptr ? -1 : step->kernels; }
+
+fn_status fn_step_destroy(fn_step step) {
+  g_last_error[0] = '\0';
+  if (step == nullptr) return FN_OK;
+  fn_status st = hip_status(hipGraphExecDestroy(step->exec), "step: destroy exec");
+  const fn_status s2 = hip_status(hipGraphDestroy(step->graph), "step: destroy graph");
+  if (st == FN_OK) st = s2;
+  delete step;
+  return st;
 }
 
 const char* fn_kernel_name_fp8(int64_t M, int64_t K, int64_t N, int swiglu) {

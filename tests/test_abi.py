@@ -198,3 +198,52 @@ def test_fp8_swiglu_and_fold_reject(lib):
     assert f(0x100, 0x1000, 0x1000, 0x20000, 16, 16, BF16, None) == ALIAS
     assert f(0x100, 0x1000, 0x10000, 0x20000, 16, 16, 9, None) == DTYPE
     assert f(None, None, None, None, 16, 0, BF16, None) == OK
+
+
+def _call(kind=fn.FN_CALL_NORM_PROJ, x=0x1000, wg=0x20000, wu=None, sg=None, su=None, y=0x40000, M=4, K=16, N=16,
+          eps=1e-6, dt=BF16):
+    return fn.FnCall(kind, x, wg, wu, sg, su, y, M, K, N, eps, dt)
+
+
+def _create(lib, calls):
+    arr = (fn.FnCall * max(1, len(calls)))(*calls)
+    h = ctypes.c_void_p(0x1234)
+    st = lib.fn_step_create(arr, len(calls), ctypes.byref(h))
+    return st, h
+
+
+def test_fn_call_layout_matches_header():
+    # kind, 6 pointers, 3 int64, float, enum: 4 + 4 (pad) + 48 + 24 + 4 + 4
+    assert ctypes.sizeof(fn.FnCall) == 88
+    assert fn.FnCall.x.offset == 8 and fn.FnCall.M.offset == 56 and fn.FnCall.eps.offset == 80
+
+
+def test_step_create_validates_every_call_first(lib):
+    # each bad call is rejected with its entry point's status, prefixed with
+    # its index, before any HIP call (none is possible without a GPU)
+    st, h = _create(lib, [_call(), _call(K=12)])
+    assert st == SHAPE and h.value is None
+    assert lib.fn_last_error().decode().startswith("call 1: K=12")
+    st, h = _create(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_SWIGLU)])
+    assert st == NULL and "call 0: W_up_packed" in lib.fn_last_error().decode()
+    st, _ = _create(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_FP8, sg=None)])
+    assert st == NULL and "scales" in lib.fn_last_error().decode()
+    st, _ = _create(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_SWIGLU_FP8, wu=0x21000, sg=0x30000, su=0x30002)])
+    assert st == ALIGN
+    st, _ = _create(lib, [_call(y=0x1000)])
+    assert st == ALIAS
+    st, _ = _create(lib, [_call(eps=-1.0)])
+    assert st == EPS
+    st, _ = _create(lib, [_call(kind=7)])
+    assert st == DTYPE and "call kind" in lib.fn_last_error().decode()
+    st, _ = _create(lib, [])
+    assert st == SHAPE and "n_calls" in lib.fn_last_error().decode()
+
+
+def test_step_null_arguments(lib):
+    assert lib.fn_step_create(None, 1, ctypes.byref(ctypes.c_void_p())) == NULL
+    arr = (fn.FnCall * 1)(_call())
+    assert lib.fn_step_create(arr, 1, None) == NULL
+    assert lib.fn_step_launch(None, None) == NULL
+    assert lib.fn_step_num_kernels(None) == -1
+    assert lib.fn_step_destroy(None) == OK
