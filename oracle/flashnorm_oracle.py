@@ -43,8 +43,9 @@ All arithmetic is float64.  Inputs are the stored (bf16 or fp32) values,
 up-cast exactly.  eps is taken as float64(float32(eps)), the exact value a
 GPU kernel receives as a float argument.
 
-The fp8-weight functions at the end (E4M3 codes with one scale per output
-column) follow the reading stated in their section.
+The fp8-weight functions (E4M3 codes with one scale per output column) and
+the fp8 output functions at the end (E4M3 codes with one scale per 16-column
+row block) follow the readings stated in their sections.
 
 Pins (see tests/test_oracle.py): hand-derived worked cases, brute force on
 tiny inputs, torch's float64 rms_norm followed by a float64 matmul, the fold
@@ -271,7 +272,66 @@ def norm_proj_swiglu_fp8(x, codes_gate, s_gate, codes_up, s_up, eps: float) -> n
     return silu(a) * b
 
 
+# ------------------------------------------ fp8 output with block scales --
+# The SwiGLU result can leave the kernel already quantised for the next
+# projection: [FlashInfer #4040] ("Fused SwiGLU 및 NVFP4 양자화 최적화 분석",
+# sections "들어가며" and "Fused Kernel 구현") quantises the silu * up values
+# in registers, one scale factor per vector of SF_VEC_SIZE consecutive
+# values, instead of writing them and quantising in a second kernel.  The
+# page's format is NVFP4; the reading taken here keeps the method and uses
+# the fp8 format of the weight path:
+#
+# * format: OCP E4M3 as above;
+# * blocks: 16 consecutive output columns of one row (the vector length of
+#   the page's NVFP4 scale factors); the last block of a row is shorter when
+#   N % 16 != 0;
+# * per block, from the fp32 values v: amax = max |v|, r = fp32(448 / amax),
+#   s = fp32(amax / 448) (r = s = 1 for an all-zero block) and
+#   codes = RNE_e4m3(fp32(v * r)); the value a consumer reads back is
+#   s * decode(code).  The same steps as the per-column weight scales, with
+#   the block in place of the column.
+
+Q8_BLOCK = 16
+
+
+def quantize_e4m3_row_blocks(v, block: int = Q8_BLOCK):
+    """Row-block E4M3 quantisation of v [M, N] (taken as fp32 values).
+    Returns (codes uint8 [M, N], s float32 [M, ceil(N / block)])."""
+    v32 = np.asarray(v, dtype=np.float32)
+    M, N = v32.shape
+    nb = -(-N // block)
+    padded = np.zeros((M, nb * block), dtype=np.float32)   # zero padding leaves every amax unchanged
+    padded[:, :N] = v32
+    cols = padded.reshape(M * nb, block).T                  # one block per column
+    codes, s, _ = quantize_e4m3_columns(cols)
+    return np.ascontiguousarray(codes.T.reshape(M, nb * block)[:, :N]), s.reshape(M, nb)
+
+
+def dequantize_row_blocks(codes, s, block: int = Q8_BLOCK) -> np.ndarray:
+    """s[m, n // block] * decode(codes[m, n]) in float64."""
+    codes = np.asarray(codes)
+    cols = np.arange(codes.shape[1]) // block
+    return e4m3_decode(codes) * _f64(s)[:, cols]
+
+
+def norm_proj_swiglu_q8(x, g, W_gate, W_up, eps: float):
+    """The SwiGLU output quantised in row blocks: (codes, s, v), v the
+    float64 SwiGLU output it quantises (through fp32)."""
+    v = norm_proj_swiglu(x, g, W_gate, W_up, eps)
+    codes, s = quantize_e4m3_row_blocks(v)
+    return codes, s, v
+
+
+def norm_proj_swiglu_fp8_q8(x, codes_gate, s_gate, codes_up, s_up, eps: float):
+    """E4M3 weights in, row-block E4M3 out: (codes, s, v)."""
+    v = norm_proj_swiglu_fp8(x, codes_gate, s_gate, codes_up, s_up, eps)
+    codes, s = quantize_e4m3_row_blocks(v)
+    return codes, s, v
+
+
 __all__ = ["rms", "rmsnorm", "norm_proj", "silu", "norm_proj_swiglu", "fold_exact",
            "round_to_bf16", "round_to_f32", "round_to", "fold_weights", "norm_proj_folded",
            "norm_proj_swiglu_folded", "eps_as_received", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
-           "quantize_e4m3_columns", "fold_weights_fp8", "norm_proj_fp8", "norm_proj_swiglu_fp8"]
+           "quantize_e4m3_columns", "fold_weights_fp8", "norm_proj_fp8", "norm_proj_swiglu_fp8",
+           "Q8_BLOCK", "quantize_e4m3_row_blocks", "dequantize_row_blocks", "norm_proj_swiglu_q8",
+           "norm_proj_swiglu_fp8_q8"]

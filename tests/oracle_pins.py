@@ -361,3 +361,76 @@ def check_norm_proj_fp8(o, seed=21):
 
 
 ALL_CHECKS += [check_e4m3_codes, check_e4m3_quantize, check_norm_proj_fp8]
+
+
+# --------------------------------------------------------------------------
+# fp8 output: E4M3 codes with one scale per 16-column row block
+# --------------------------------------------------------------------------
+def check_e4m3_row_blocks(o, seed=22):
+    """Row-block quantisation: a hand-evaluated case (ties, a subnormal, a
+    ragged last block, an all-zero row), codes equal to torch's
+    float8_e4m3fn conversion of the scaled fp32 values (scales computed here
+    block by block in plain loops), the rounding error bound of the values
+    read back, and independence of blocks and rows."""
+    import torch
+    gold = load_golden()["e4m3"]["quantize_row_blocks"]
+    codes, s = o.quantize_e4m3_row_blocks(np.array(gold["v"]))
+    assert codes.tolist() == gold["codes"], codes
+    assert s.tolist() == gold["s"], s
+    assert o.Q8_BLOCK == 16
+    rng = np.random.default_rng(seed)
+    M, N, B = 5, 37, 16
+    v = (rng.standard_normal((M, N)) * np.exp(rng.uniform(-6, 3, (M, 1)))).astype(np.float32)
+    v[2, 16:32] = 0.0                                   # an all-zero block inside a row
+    codes, s = o.quantize_e4m3_row_blocks(v)
+    assert codes.shape == (M, N) and s.shape == (M, 3) and codes.dtype == np.uint8
+    for m in range(M):
+        for b in range(3):
+            blk = v[m, b * B:(b + 1) * B]
+            amax = np.float32(max(abs(float(t)) for t in blk))
+            if amax == 0:
+                assert s[m, b] == 1.0 and np.all(codes[m, b * B:(b + 1) * B] == 0)
+                continue
+            r = np.float32(np.float32(448.0) / amax)
+            assert s[m, b] == np.float32(amax / np.float32(448.0)), (m, b)
+            scaled = (blk * r).astype(np.float32)
+            ref = torch.from_numpy(scaled.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(codes[m, b * B:(b + 1) * B], ref), (m, b)
+    back = o.dequantize_row_blocks(codes, s)
+    blk_s = np.repeat(s.astype(np.float64), B, axis=1)[:, :N]
+    _, e = np.frexp(np.abs(v.astype(np.float64) / blk_s))
+    bound = np.ldexp(1.0, np.maximum(e, -5) - 5) * blk_s * (1 + 1e-6)
+    assert np.all(np.abs(back - v) <= bound), "row-block rounding error bound"
+    w = v.copy()
+    w[0, 16:32] *= 1000.0                               # another block of row 0, and other rows untouched
+    w[4] = -w[4]
+    c2, s2 = o.quantize_e4m3_row_blocks(w)
+    assert np.array_equal(c2[0, :16], codes[0, :16]) and np.array_equal(c2[0, 32:], codes[0, 32:])
+    assert np.array_equal(c2[1:4], codes[1:4]) and np.array_equal(s2[1:4], s[1:4])
+    assert np.array_equal(o.dequantize_row_blocks(c2, s2)[4], -back[4]) and np.array_equal(s2[4], s[4]), "sign symmetry"
+
+
+def check_norm_proj_swiglu_q8(o, seed=23):
+    """The quantised SwiGLU output is the row-block quantisation of the
+    SwiGLU output (bf16 and fp8 weights), and reads back within the E4M3
+    bound of it."""
+    rng = np.random.default_rng(seed)
+    M, K, N = 3, 32, 20
+    x = rng.standard_normal((M, K))
+    g = rng.uniform(0.5, 1.5, K)
+    Wg, Wu = rng.standard_normal((K, N)) / 6, rng.standard_normal((K, N)) / 6
+    codes, s, v = o.norm_proj_swiglu_q8(x, g, Wg, Wu, 1e-6)
+    _close(v, o.norm_proj_swiglu(x, g, Wg, Wu, 1e-6), 0.0, "q8 value")
+    c2, s2 = o.quantize_e4m3_row_blocks(v)
+    assert np.array_equal(codes, c2) and np.array_equal(s, s2)
+    back = o.dequantize_row_blocks(codes, s)
+    assert np.all(np.abs(back - v) <= np.abs(v) / 16 + np.repeat(s, 16, axis=1)[:, :N] * 2.0 ** -9 + 1e-9)
+    cg, sg, _ = o.quantize_e4m3_columns(Wg.astype(np.float32))
+    cu, su, _ = o.quantize_e4m3_columns(Wu.astype(np.float32))
+    c8, s8, v8 = o.norm_proj_swiglu_fp8_q8(x, cg, sg, cu, su, 1e-6)
+    _close(v8, o.norm_proj_swiglu_fp8(x, cg, sg, cu, su, 1e-6), 0.0, "fp8 q8 value")
+    c3, s3 = o.quantize_e4m3_row_blocks(v8)
+    assert np.array_equal(c8, c3) and np.array_equal(s8, s3)
+
+
+ALL_CHECKS += [check_e4m3_row_blocks, check_norm_proj_swiglu_q8]

@@ -54,6 +54,11 @@ MUTANTS = {
     "fp8 scale inverted": ("norm_proj_fp8", lambda x, c, s, eps: (np.asarray(x, float) @ O.e4m3_decode(c))
                            / np.asarray(s, float)[None, :] / O.rms(x, eps)[:, None]),
     "fp8 scale per row": ("quantize_e4m3_columns", lambda W: _quantize_rows(W)),
+    "q8 blocks down the columns": ("quantize_e4m3_row_blocks", lambda v, block=16: _q8_columns(v, block)),
+    "q8 block of 32": ("quantize_e4m3_row_blocks", lambda v, block=16: _q8_ref(v, 32)),
+    "q8 blocks across rows": ("quantize_e4m3_row_blocks", lambda v, block=16: _q8_flat(v, block)),
+    "q8 scale inverted": ("dequantize_row_blocks", lambda c, s, block=16: _deq_ref(c, 1.0 / np.asarray(s, float),
+                                                                                 block)),
 }
 
 
@@ -87,6 +92,28 @@ def _quantize_rows(W):
     codes, s, r = _quantize_ref(Wt)
     n = np.asarray(W).shape[1]
     return codes.T.copy(), np.resize(s, n).astype(np.float32), np.resize(r, n).astype(np.float32)
+
+
+_q8_ref = O.quantize_e4m3_row_blocks
+_deq_ref = O.dequantize_row_blocks
+
+
+def _q8_columns(v, block):
+    """Blocks of 16 rows of one column instead of 16 columns of one row."""
+    c, s = _q8_ref(np.asarray(v, dtype=np.float32).T.copy(), block)
+    nb = -(-np.asarray(v).shape[1] // block)
+    return c.T.copy(), np.resize(s.T, (np.asarray(v).shape[0], nb)).astype(np.float32)
+
+
+def _q8_flat(v, block):
+    """Blocks of 16 consecutive values of the flattened matrix (rows not
+    padded: the last block of a row runs into the next row)."""
+    v32 = np.asarray(v, dtype=np.float32)
+    M, N = v32.shape
+    flat = v32.reshape(1, M * N)
+    c, s = _q8_ref(flat, block)
+    nb = -(-N // block)
+    return c.reshape(M, N), np.resize(s, (M, nb)).astype(np.float32)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
