@@ -43,6 +43,8 @@ def parse_args(argv=None):
     p.add_argument("--weights", default="native", choices=["native", "fp8"],
                    help="weight storage: the activations' dtype, or E4M3 codes with per-column scales "
                         "(bf16 decode workloads only)")
+    p.add_argument("--output", default="native", choices=["native", "q8"],
+                   help="q8: SwiGLU output as E4M3 codes + one scale per 16-column row block (ffn_decode)")
     p.add_argument("--no-chain", action="store_true", help="skip the unfused chain baselines")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
@@ -110,7 +112,8 @@ def pct(sorted_vals, q):
 # Sources each workload's dominant kernel is built from.
 KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": ("decode_x.hip", "fn_device.h"),
                   "qkv_decode_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_fp8": ("decode_x.hip", "fn_device.h"),
-                  "decode_step_fp8": ("decode_x.hip", "fn_device.h")}
+                  "decode_step_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_q8": ("decode_x.hip", "fn_device.h"),
+                  "ffn_decode_fp8_q8": ("decode_x.hip", "fn_device.h")}
 DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
 
 
@@ -142,8 +145,18 @@ def fp8_bytes(call):
     return call.mats * (call.K * call.N + 4 * call.N) + 2 * (call.M * call.K + call.M * call.N)
 
 
+def call_bytes(call, fp8, q8):
+    """Algorithmic bytes of one call: weights (bf16 W', or E4M3 codes and
+    column scales) once, x once, and the output once (bf16 y, or E4M3 codes
+    plus one fp32 scale per 16-column row block)."""
+    w = call.mats * (call.K * call.N + 4 * call.N) if fp8 else call.mats * call.K * call.N * (2 if call.dtype == "bf16" else 4)
+    e = 2 if call.dtype == "bf16" else 4
+    out = call.M * call.N + 4 * call.M * (-(-call.N // 16)) if q8 else e * call.M * call.N
+    return w + e * call.M * call.K + out
+
+
 # ------------------------------------------------------------ CPU oracle --
-def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False):
+def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False):
     """The float64 oracle as it stands, on the host cores, on a bounded sample
     of the same workload; scaled to the metric's unit."""
     import numpy as np
@@ -159,16 +172,20 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False):
         rows = max(1, int(2e10 // (call.K * call.N * call.mats)))
     x = inp.x[:rows]
     calls, t0 = 0, time.perf_counter()
-    q8 = None
+    w8 = None
     if fp8:
-        q8 = [oracle.fold_weights_fp8(inp.g, inp.W, call.dtype)]
+        w8 = [oracle.fold_weights_fp8(inp.g, inp.W, call.dtype)]
         if call.swiglu:
-            q8.append(oracle.fold_weights_fp8(inp.g, inp.W_up, call.dtype))
+            w8.append(oracle.fold_weights_fp8(inp.g, inp.W_up, call.dtype))
     while True:
-        if fp8 and call.swiglu:
-            oracle.norm_proj_swiglu_fp8(x, q8[0][0], q8[0][1], q8[1][0], q8[1][1], call.eps)
+        if q8 and fp8:
+            oracle.norm_proj_swiglu_fp8_q8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], call.eps)
+        elif q8:
+            oracle.norm_proj_swiglu_q8(x, inp.g, inp.W, inp.W_up, call.eps)
+        elif fp8 and call.swiglu:
+            oracle.norm_proj_swiglu_fp8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], call.eps)
         elif fp8:
-            oracle.norm_proj_fp8(x, q8[0][0], q8[0][1], call.eps)
+            oracle.norm_proj_fp8(x, w8[0][0], w8[0][1], call.eps)
         elif call.swiglu:
             oracle.norm_proj_swiglu(x, inp.g, inp.W, inp.W_up, call.eps)
         else:
@@ -181,11 +198,12 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False):
     if metric_unit == "TFLOP/s":
         value = call.flops() / per_call / 1e12
     elif metric_unit == "GB/s":
-        value = (fp8_bytes(call) if fp8 else call.algorithmic_bytes()) / per_call / 1e9
+        value = call_bytes(call, fp8, q8) / per_call / 1e9
     else:
         value = per_call * 1e6
     sample = (f"{calls} oracle call(s) on x[{rows},{call.K}] (of M={call.M}) x W[{call.K},{call.N}]"
-              f"{' x2 (gate, up)' if call.swiglu else ''}{' (E4M3 codes)' if fp8 else ''}, float64, {el:.1f} s;"
+              f"{' x2 (gate, up)' if call.swiglu else ''}{' (E4M3 codes)' if fp8 else ''}"
+              f"{', E4M3 row-block output' if q8 else ''}, float64, {el:.1f} s;"
               f" scaled by M/{rows}")
     return {"value": round(value, 4), "unit": metric_unit, "cores": cores, "kind": "oracle",
             "sample": sample, "seconds_per_call": per_call}
@@ -229,6 +247,13 @@ def run_single(args, torch, fn, workloads):
     pus = ([Pu] + [clone(Pu) for _ in range(rot - 1)]) if call.swiglu else None
     y = torch.empty((call.M, call.N), dtype=x.dtype, device="cuda")
     eps = call.eps
+    q8 = args.output == "q8"
+    if q8:
+        # SwiGLU quantised in the epilogue: E4M3 codes + row-block scales
+        qout = (torch.empty((call.M, call.N), dtype=torch.uint8, device="cuda"),
+                torch.empty((call.M, -(-call.N // 16)), dtype=torch.float32, device="cuda"))
+        proj_q8 = fn.norm_proj_swiglu_fp8_q8 if fp8 else fn.norm_proj_swiglu_q8
+        proj_sw = lambda x_, a_, b_, e_, out=None: proj_q8(x_, a_, b_, e_, out=qout)  # noqa: E731
 
     if call.swiglu:
         def fused(i):
@@ -261,8 +286,10 @@ def run_single(args, torch, fn, workloads):
         bgs = [Bg] + [fn.PackedWeights(Bg.data.clone(), Bg.K, Bg.N, Bg.dtype) for _ in range(brot - 1)]
         bus = ([Bu] + [fn.PackedWeights(Bu.data.clone(), Bu.K, Bu.N, Bu.dtype) for _ in range(brot - 1)]
                if call.swiglu else None)
+        bsw = ((lambda x_, a_, b_, e_, out=None: fn.norm_proj_swiglu_q8(x_, a_, b_, e_, out=qout)) if q8
+               else fn.norm_proj_swiglu)
         result["bf16_ms"] = time_region(
-            torch, lambda i: (fn.norm_proj_swiglu(x, bgs[i % brot], bus[i % brot], eps, out=y) if call.swiglu
+            torch, lambda i: (bsw(x, bgs[i % brot], bus[i % brot], eps, out=y) if call.swiglu
                               else fn.norm_proj(x, bgs[i % brot], eps, out=y)), args.steps, args.warmup)
         del bgs, bus
 
@@ -273,17 +300,30 @@ def run_single(args, torch, fn, workloads):
         xhat = torch.empty_like(x)
         N = call.N
 
+        def quantize(v):
+            # the chain's own quantisation step: row-block amax, scale, E4M3
+            nb = -(-N // 16)
+            vb = torch.nn.functional.pad(v.float(), (0, nb * 16 - N)).view(call.M, nb, 16)
+            amax = vb.abs().amax(-1, keepdim=True)
+            r = torch.where(amax > 0, 448.0 / amax, torch.ones_like(amax))
+            qout[0].copy_((vb * r).to(torch.float8_e4m3fn).view(torch.uint8).view(call.M, nb * 16)[:, :N])
+            qout[1].copy_(torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).view(call.M, nb))
+
         def chain_own(i):
             fn.rmsnorm(x, g, eps, out=xhat)
             h = torch.matmul(xhat, ws[i % rot])
             if call.swiglu:
                 fn.silu_mul(h, out=y)
+                if q8:
+                    quantize(y)
 
         def chain_torch(i):
             xn = torch.nn.functional.rms_norm(x, (call.K,), g, eps)
             h = torch.matmul(xn, ws[i % rot])
             if call.swiglu:
                 torch.mul(torch.nn.functional.silu(h[:, :N]), h[:, N:], out=y)
+                if q8:
+                    quantize(y)
 
         result["chain_own_ms"] = time_region(torch, chain_own, args.steps, args.warmup)
         result["chain_torch_ms"] = time_region(torch, chain_torch, args.steps, args.warmup)
@@ -391,7 +431,11 @@ def main(argv=None):
     if fp8 and args.workload in ("tiny", "prefill_qkv"):
         print(f"bench.py: --weights fp8 applies to the bf16 decode workloads, not {args.workload}", file=sys.stderr)
         return 2
-    suffix = "_fp8" if fp8 else ""
+    q8 = args.output == "q8"
+    if q8 and args.workload != "ffn_decode":
+        print(f"bench.py: --output q8 applies to the SwiGLU workload ffn_decode, not {args.workload}", file=sys.stderr)
+        return 2
+    suffix = ("_fp8" if fp8 else "") + ("_q8" if q8 else "")
 
     if args.workload == "decode_step":
         calls, r = run_decode_step(args, torch, fn, workloads)
@@ -410,9 +454,10 @@ def main(argv=None):
         per_unit = {"algorithmic_bytes_per_step": bytes_step, "flops_per_step": flops_step}
     else:
         call, inp, r = run_single(args, torch, fn, workloads)
-        bytes_call = fp8_bytes(call) if fp8 else call.algorithmic_bytes()
+        bytes_call = call_bytes(call, fp8, q8)
         flops_call = call.flops()
-        kernel = (fn.kernel_name_fp8(call.M, call.K, call.N, call.swiglu) if fp8 else
+        kernel = (fn.kernel_name_q8(call.M, call.K, call.N, fp8) if q8 else
+                  fn.kernel_name_fp8(call.M, call.K, call.N, call.swiglu) if fp8 else
                   fn.kernel_name(call.M, call.K, call.N, call.swiglu,
                                  torch.bfloat16 if call.dtype == "bf16" else torch.float32))
         config = {"workload": call.name, "M": call.M, "K": call.K, "N": call.N, "mats": call.mats,
@@ -441,6 +486,8 @@ def main(argv=None):
                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": counter_traffic(args.workload + suffix)}
         if fp8:
             config["weights"] = "fp8 E4M3 codes + one fp32 scale per output column"
+        if q8:
+            config["output"] = "fp8 E4M3 codes + one fp32 scale per 16-column row block"
 
     out = {
         "metric": METRIC,
@@ -484,7 +531,8 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         if cpu_inp is None:
             cpu_inp = workloads.make_inputs(cpu_call)
-        cb = cpu_baseline(cpu_call, cpu_inp, args.cpu_seconds, unit if unit != "us/call" else "us/call", fp8=fp8)
+        cb = cpu_baseline(cpu_call, cpu_inp, args.cpu_seconds, unit if unit != "us/call" else "us/call", fp8=fp8,
+                          q8=q8)
         if args.workload == "decode_step":
             # one head call sampled; scale to the whole step by algorithmic bytes
             per_call = cb.pop("seconds_per_call")

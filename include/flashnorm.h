@@ -203,6 +203,43 @@ const char* fn_kernel_name_fp8(int64_t M, int64_t K, int64_t N, int swiglu);
 const char* fn_kernel_name(int64_t M, int64_t K, int64_t N, int swiglu, fn_dtype dt);
 
 /* ---------------------------------------------------------------------------
+ * SwiGLU with fp8 output (E4M3 codes, one scale per 16-column row block)
+ *
+ * The SwiGLU result quantised where it is computed, so the next projection
+ * (the down projection) reads one byte per value and nothing else is
+ * written ([FlashInfer #4040] "Fused SwiGLU 및 NVFP4 양자화 최적화 분석",
+ * sections "들어가며" and "Fused Kernel 구현": the activation quantised in
+ * registers, one scale factor per vector of consecutive values).  Reading
+ * taken here (the page's format is NVFP4): OCP E4M3 codes as in the fp8
+ * weight section, blocks of 16 consecutive columns of one row (the last
+ * block of a row is shorter when N % 16 != 0); per block, from the fp32
+ * values v = silu(a) * b of the fused call,
+ *   amax = max |v|,  r = 448 / amax,  s = amax / 448   (one correctly
+ *   rounded fp32 division each; r = s = 1 for an all-zero block),
+ *   code = RNE_E4M3(v * r)   (one fp32 multiply; ties to even, saturating),
+ * and a consumer reads back s * decode(code).  A NaN in a block makes its
+ * scale and all its codes NaN (0x7F).
+ * out_codes:  [M,N] row-major bytes, fully overwritten (no alignment needed).
+ * out_scales: [M, ceil(N/16)] row-major fp32, 4-byte aligned, fully
+ *             overwritten.
+ * x is bf16.  Instances: the LDS-shared-x decode kernel up to 64 rows (any
+ * M with fp8 weights), the prefill kernel above 64 rows (bf16 weights).
+ * ------------------------------------------------------------------------- */
+
+/* bf16 packed weights (fn_fold_weights with FN_BF16). */
+fn_status fn_norm_proj_swiglu_q8(const void* x, const void* W_gate_packed, const void* W_up_packed, void* out_codes,
+                                 float* out_scales, int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream);
+
+/* fp8 weights (fn_fold_weights_fp8): fp8 in, fp8 out. */
+fn_status fn_norm_proj_swiglu_fp8_q8(const void* x, const void* W8_gate, const float* s_gate, const void* W8_up,
+                                     const float* s_up, void* out_codes, float* out_scales, int64_t M, int64_t K,
+                                     int64_t N, float eps, hipStream_t stream);
+
+/* Kernel instance the two calls above would launch (fp8_weights selects
+ * the second); "invalid" for bad shapes. */
+const char* fn_kernel_name_q8(int64_t M, int64_t K, int64_t N, int fp8_weights);
+
+/* ---------------------------------------------------------------------------
  * Recorded steps: a sequence of fused calls replayed with one launch
  *
  * A decode step starts the norm + projection once per layer, dozens of
@@ -224,13 +261,15 @@ typedef enum {
   FN_CALL_NORM_PROJ = 0,            /* fn_norm_proj: w_gate = W_packed */
   FN_CALL_NORM_PROJ_SWIGLU = 1,     /* fn_norm_proj_swiglu: w_gate, w_up */
   FN_CALL_NORM_PROJ_FP8 = 2,        /* fn_norm_proj_fp8: w_gate = W8_packed, s_gate = scales */
-  FN_CALL_NORM_PROJ_SWIGLU_FP8 = 3  /* fn_norm_proj_swiglu_fp8: w_gate, s_gate, w_up, s_up */
+  FN_CALL_NORM_PROJ_SWIGLU_FP8 = 3, /* fn_norm_proj_swiglu_fp8: w_gate, s_gate, w_up, s_up */
+  FN_CALL_NORM_PROJ_SWIGLU_Q8 = 4,  /* fn_norm_proj_swiglu_q8: y = out_codes, y_scales = out_scales */
+  FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8 = 5 /* fn_norm_proj_swiglu_fp8_q8: as kind 3, outputs as kind 4 */
 } fn_call_kind;
 
 /* One call of a step: the arguments of the entry point `kind` names.
  * Fields a kind does not use are ignored (w_up for single projections,
- * s_gate / s_up for bf16 and fp32 weights, dt for the fp8 kinds, which take
- * bf16 activations). */
+ * s_gate / s_up for bf16 and fp32 weights, y_scales except for the fp8
+ * output kinds, dt for kinds 2..5, which take bf16 activations). */
 typedef struct {
   fn_call_kind kind;
   const void* x;
@@ -242,6 +281,7 @@ typedef struct {
   int64_t M, K, N;
   float eps;
   fn_dtype dt;
+  float* y_scales;
 } fn_call;
 
 typedef struct fn_step_s* fn_step;   /* opaque handle */

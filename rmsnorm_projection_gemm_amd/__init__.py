@@ -71,6 +71,9 @@ def load():
         "fn_norm_proj_fp8": (i32, [vp, vp, vp, vp, i64, i64, i64, f32, vp]),
         "fn_norm_proj_swiglu_fp8": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp]),
         "fn_kernel_name_fp8": (ctypes.c_char_p, [i64, i64, i64, i32]),
+        "fn_norm_proj_swiglu_q8": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, f32, vp]),
+        "fn_norm_proj_swiglu_fp8_q8": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp]),
+        "fn_kernel_name_q8": (ctypes.c_char_p, [i64, i64, i64, i32]),
         "fn_step_create": (i32, [vp, i64, ctypes.POINTER(vp)]),
         "fn_step_launch": (i32, [vp, vp]),
         "fn_step_num_kernels": (i64, [vp]),
@@ -300,8 +303,63 @@ def kernel_name_fp8(M: int, K: int, N: int, swiglu: bool) -> str:
     return load().fn_kernel_name_fp8(M, K, N, int(swiglu)).decode()
 
 
+# ------------------------------------------- SwiGLU with fp8 output (q8) --
+Q8_BLOCK = 16
+
+
+def _q8_out(out, M, N, x):
+    """(codes uint8 [M, N], scales float32 [M, ceil(N/16)]) on x's device."""
+    torch = _torch()
+    nb = -(-N // Q8_BLOCK)
+    if out is None:
+        return (torch.empty((M, N), dtype=torch.uint8, device=x.device),
+                torch.empty((M, nb), dtype=torch.float32, device=x.device))
+    codes, scales = out
+    _need_cuda("codes", codes)
+    _need_cuda("scales", scales)
+    if tuple(codes.shape) != (M, N) or codes.dtype != torch.uint8:
+        raise ValueError(f"codes must be [{M}, {N}] uint8")
+    if tuple(scales.shape) != (M, nb) or scales.dtype != torch.float32:
+        raise ValueError(f"scales must be [{M}, {nb}] float32")
+    return codes, scales
+
+
+def norm_proj_swiglu_q8(x, Wg: PackedWeights, Wu: PackedWeights, eps: float = 1e-6, out=None):
+    """silu(a) * b quantised to E4M3 with one scale per 16-column row block:
+    returns (codes, scales); the values are scales[m, n // 16] * decode(codes[m, n])."""
+    torch = _torch()
+    _check_x(x, Wg)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("fp8 output takes bf16 activations and weights")
+    if (Wu.K, Wu.N, Wu.dtype) != (Wg.K, Wg.N, Wg.dtype):
+        raise ValueError("gate and up weights must have the same K, N and dtype")
+    M, N = x.shape[0], Wg.N
+    codes, scales = _q8_out(out, M, N, x)
+    _check(load().fn_norm_proj_swiglu_q8(x.data_ptr(), Wg.data.data_ptr(), Wu.data.data_ptr(), codes.data_ptr(),
+                                         scales.data_ptr(), M, Wg.K, N, eps, _stream(x)))
+    return codes, scales
+
+
+def norm_proj_swiglu_fp8_q8(x, Pg: PackedFp8, Pu: PackedFp8, eps: float = 1e-6, out=None):
+    """E4M3 weights in, E4M3 row-block output out: (codes, scales)."""
+    _check_x_fp8(x, Pg)
+    if (Pu.K, Pu.N) != (Pg.K, Pg.N):
+        raise ValueError("gate and up weights must have the same K and N")
+    M, N = x.shape[0], Pg.N
+    codes, scales = _q8_out(out, M, N, x)
+    _check(load().fn_norm_proj_swiglu_fp8_q8(x.data_ptr(), Pg.data.data_ptr(), Pg.scales.data_ptr(),
+                                             Pu.data.data_ptr(), Pu.scales.data_ptr(), codes.data_ptr(),
+                                             scales.data_ptr(), M, Pg.K, N, eps, _stream(x)))
+    return codes, scales
+
+
+def kernel_name_q8(M: int, K: int, N: int, fp8_weights: bool) -> str:
+    return load().fn_kernel_name_q8(M, K, N, int(fp8_weights)).decode()
+
+
 # ------------------------------------------------------- recorded steps --
 FN_CALL_NORM_PROJ, FN_CALL_NORM_PROJ_SWIGLU, FN_CALL_NORM_PROJ_FP8, FN_CALL_NORM_PROJ_SWIGLU_FP8 = 0, 1, 2, 3
+FN_CALL_NORM_PROJ_SWIGLU_Q8, FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8 = 4, 5
 
 
 class FnCall(ctypes.Structure):
@@ -309,7 +367,7 @@ class FnCall(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("x", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
                 ("w_up", ctypes.c_void_p), ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
-                ("eps", ctypes.c_float), ("dt", ctypes.c_int)]
+                ("eps", ctypes.c_float), ("dt", ctypes.c_int), ("y_scales", ctypes.c_void_p)]
 
 
 class Step:
@@ -323,10 +381,11 @@ class Step:
         self._keep = []
         self._handle = None
 
-    def _add(self, kind, x, wg, wu, sg, su, out, M, K, N, eps, dt, keep):
+    def _add(self, kind, x, wg, wu, sg, su, out, M, K, N, eps, dt, keep, out_scales=None):
         if self._handle is not None:
             raise RuntimeError("the step is already recorded")
-        self._calls.append(FnCall(kind, x.data_ptr(), wg, wu, sg, su, out.data_ptr(), M, K, N, eps, dt))
+        self._calls.append(FnCall(kind, x.data_ptr(), wg, wu, sg, su, out.data_ptr(), M, K, N, eps, dt,
+                                  None if out_scales is None else out_scales.data_ptr()))
         self._keep.extend(keep)
 
     def norm_proj(self, x, Wp: PackedWeights, out, eps: float = 1e-6):
@@ -357,6 +416,23 @@ class Step:
         self._add(FN_CALL_NORM_PROJ_SWIGLU_FP8, x, Pg.data.data_ptr(), Pu.data.data_ptr(), Pg.scales.data_ptr(),
                   Pu.scales.data_ptr(), out, x.shape[0], Pg.K, Pg.N, eps, FN_BF16,
                   (x, Pg.data, Pg.scales, Pu.data, Pu.scales, out))
+
+    def norm_proj_swiglu_q8(self, x, Wg: PackedWeights, Wu: PackedWeights, codes, scales, eps: float = 1e-6):
+        _check_x(x, Wg)
+        if (Wu.K, Wu.N, Wu.dtype) != (Wg.K, Wg.N, Wg.dtype):
+            raise ValueError("gate and up weights must have the same K, N and dtype")
+        _q8_out((codes, scales), x.shape[0], Wg.N, x)
+        self._add(FN_CALL_NORM_PROJ_SWIGLU_Q8, x, Wg.data.data_ptr(), Wu.data.data_ptr(), None, None, codes,
+                  x.shape[0], Wg.K, Wg.N, eps, FN_BF16, (x, Wg.data, Wu.data, codes, scales), scales)
+
+    def norm_proj_swiglu_fp8_q8(self, x, Pg: PackedFp8, Pu: PackedFp8, codes, scales, eps: float = 1e-6):
+        _check_x_fp8(x, Pg)
+        if (Pu.K, Pu.N) != (Pg.K, Pg.N):
+            raise ValueError("gate and up weights must have the same K and N")
+        _q8_out((codes, scales), x.shape[0], Pg.N, x)
+        self._add(FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8, x, Pg.data.data_ptr(), Pu.data.data_ptr(), Pg.scales.data_ptr(),
+                  Pu.scales.data_ptr(), codes, x.shape[0], Pg.K, Pg.N, eps, FN_BF16,
+                  (x, Pg.data, Pg.scales, Pu.data, Pu.scales, codes, scales), scales)
 
     def record(self):
         """Validate and record the calls (fn_step_create)."""
@@ -392,4 +468,6 @@ __all__ = ["load", "fold_weights", "norm_proj", "norm_proj_swiglu", "rmsnorm", "
            "packed_weight_bytes", "kernel_name", "PackedWeights", "FlashNormError", "header_functions",
            "LIB_PATH", "FN_F32", "FN_BF16", "PackedFp8", "packed_fp8_bytes", "fold_weights_fp8",
            "norm_proj_fp8", "norm_proj_swiglu_fp8", "kernel_name_fp8", "Step", "FnCall", "FN_CALL_NORM_PROJ",
-           "FN_CALL_NORM_PROJ_SWIGLU", "FN_CALL_NORM_PROJ_FP8", "FN_CALL_NORM_PROJ_SWIGLU_FP8"]
+           "FN_CALL_NORM_PROJ_SWIGLU", "FN_CALL_NORM_PROJ_FP8", "FN_CALL_NORM_PROJ_SWIGLU_FP8",
+           "FN_CALL_NORM_PROJ_SWIGLU_Q8", "FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8", "Q8_BLOCK", "norm_proj_swiglu_q8",
+           "norm_proj_swiglu_fp8_q8", "kernel_name_q8"]

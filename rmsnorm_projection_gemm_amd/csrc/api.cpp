@@ -131,6 +131,47 @@ fn_status fp8_common(const void* x, const void* wg, const float* sg, const void*
                     plan.name);
 }
 
+// SwiGLU with fp8 output: bf16 activations, bf16 packed weights (f8 false)
+// or E4M3 codes with column scales (f8 true); codes [M,N] and row-block
+// scales [M, ceil(N/16)] out.
+fn_status q8_common(const void* x, const void* wg, const float* sg, const void* wu, const float* su, void* codes,
+                    float* scales, int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream, bool f8,
+                    bool check_only = false) {
+  g_last_error[0] = '\0';
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(M, N));
+  FN_TRY(check_eps(eps));
+  if (M == 0 || N == 0) return FN_OK;
+  if (x == nullptr) return fail(FN_ERR_NULL, "x is NULL");
+  if (wg == nullptr || wu == nullptr) return fail(FN_ERR_NULL, "gate or up weights are NULL");
+  if (f8 && (sg == nullptr || su == nullptr)) return fail(FN_ERR_NULL, "s_gate or s_up is NULL");
+  if (codes == nullptr || scales == nullptr) return fail(FN_ERR_NULL, "out_codes or out_scales is NULL");
+  if (!aligned(x, 16)) return fail(FN_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(wg, 16) || !aligned(wu, 16)) return fail(FN_ERR_ALIGN, "packed weights must be 16-byte aligned");
+  if (f8 && (!aligned(sg, 4) || !aligned(su, 4))) return fail(FN_ERR_ALIGN, "scales must be 4-byte aligned");
+  if (!aligned(scales, 4)) return fail(FN_ERR_ALIGN, "out_scales must be 4-byte aligned");
+  const int64_t xb = M * K * 2, cb = M * N, qb = M * ((N + 15) / 16) * 4;
+  const int64_t wb = f8 ? packed_fp8_bytes(K, N) : packed_bytes(K, N, FN_BF16), sb = f8 ? N * 4 : 0;
+  for (const void* out : {static_cast<const void*>(codes), static_cast<const void*>(scales)}) {
+    const int64_t ob = out == codes ? cb : qb;
+    if (overlap(out, ob, x, xb) || overlap(out, ob, wg, wb) || overlap(out, ob, wu, wb) ||
+        (f8 && (overlap(out, ob, sg, sb) || overlap(out, ob, su, sb))))
+      return fail(FN_ERR_ALIAS, "an output overlaps an input");
+  }
+  if (overlap(codes, cb, scales, qb)) return fail(FN_ERR_ALIAS, "out_codes overlaps out_scales");
+  if (check_only) return FN_OK;
+  uint8_t* q = static_cast<uint8_t*>(codes);
+  if (!f8 && M > 64) {
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true);
+    return hip_status(fn::launch_prefill(fn::DType::BF16, plan, x, wg, wu, nullptr, (int)M, (int)K, (int)N, eps,
+                                         stream, q, scales),
+                      plan.name);
+  }
+  const fn::FusedPlan plan = fn::plan_decode_q8(f8, M, N);
+  return hip_status(fn::launch_decode_q8(f8, plan, x, wg, sg, wu, su, q, scales, (int)M, (int)K, (int)N, eps, stream),
+                    plan.name);
+}
+
 // One recorded call: validate (check_only) or enqueue it on `stream`.
 fn_status run_call(const fn_call& c, hipStream_t stream, bool check_only) {
   switch (c.kind) {
@@ -144,6 +185,12 @@ fn_status run_call(const fn_call& c, hipStream_t stream, bool check_only) {
     case FN_CALL_NORM_PROJ_SWIGLU_FP8:
       return fp8_common(c.x, c.w_gate, c.s_gate, c.w_up, c.s_up, c.y, c.M, c.K, c.N, c.eps, stream, true,
                         check_only);
+    case FN_CALL_NORM_PROJ_SWIGLU_Q8:
+      return q8_common(c.x, c.w_gate, nullptr, c.w_up, nullptr, c.y, c.y_scales, c.M, c.K, c.N, c.eps, stream,
+                       false, check_only);
+    case FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8:
+      return q8_common(c.x, c.w_gate, c.s_gate, c.w_up, c.s_up, c.y, c.y_scales, c.M, c.K, c.N, c.eps, stream,
+                       true, check_only);
   }
   return fail(FN_ERR_DTYPE, "unknown call kind %d", (int)c.kind);
 }
@@ -287,6 +334,24 @@ fn_status fn_norm_proj_swiglu_fp8(const void* x, const void* W8_gate, const floa
                                   const float* s_up, void* out, int64_t M, int64_t K, int64_t N, float eps,
                                   hipStream_t stream) {
   return fp8_common(x, W8_gate, s_gate, W8_up, s_up, out, M, K, N, eps, stream, true);
+}
+
+fn_status fn_norm_proj_swiglu_q8(const void* x, const void* W_gate_packed, const void* W_up_packed, void* out_codes,
+                                 float* out_scales, int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream) {
+  return q8_common(x, W_gate_packed, nullptr, W_up_packed, nullptr, out_codes, out_scales, M, K, N, eps, stream,
+                   false);
+}
+
+fn_status fn_norm_proj_swiglu_fp8_q8(const void* x, const void* W8_gate, const float* s_gate, const void* W8_up,
+                                     const float* s_up, void* out_codes, float* out_scales, int64_t M, int64_t K,
+                                     int64_t N, float eps, hipStream_t stream) {
+  return q8_common(x, W8_gate, s_gate, W8_up, s_up, out_codes, out_scales, M, K, N, eps, stream, true);
+}
+
+const char* fn_kernel_name_q8(int64_t M, int64_t K, int64_t N, int fp8_weights) {
+  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
+  if (!fp8_weights && M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true).name;
+  return fn::plan_decode_q8(fp8_weights != 0, M, N).name;
 }
 
 fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out) {

@@ -55,6 +55,8 @@ struct DecodeXArgs {
   float eps;
   const float* sg;   // fp8 weights: column scales of wg (else unused)
   const float* su;   // fp8 weights: column scales of wu
+  uint8_t* q;        // fp8 output: E4M3 codes [M, N] (y unused)
+  float* qs;         // fp8 output: scales [M, nblocks], one per 16-column row block
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_x;
@@ -88,8 +90,9 @@ __device__ inline void decode_e4m3x16(u32x4 w, u32x4& lo, u32x4& hi) {
 
 // MF: 16-row blocks of x.  NC: 16-column blocks per wave (for SwiGLU each
 // with its gate and up stream).  NWV: waves, sharing the x fragments.  U:
-// k-blocks per stage.
-template <int MF, int NC, int NWV, bool SW, int U, bool F8>
+// k-blocks per stage.  F8: E4M3 weights.  Q8: E4M3 output with row-block
+// scales instead of a y in x's dtype.
+template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8>
 __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   constexpr int NS = 4;                    // LDS ring slots
   constexpr int D = NS - 1;                // stages in flight
@@ -102,6 +105,10 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   // Loads q >= XF (when NWV does not divide XF) fetch nothing and write
   // zeros into the slot's padding, so every wave issues the same count.
   constexpr int SLOT = XPW * NWV * kFragBytes;
+  // Epilogue through LDS (one lane per row, 16-byte stores): fp8 output
+  // always, bf16 output when each wave owns one column block.
+  constexpr bool STAGE = Q8 || (NC == 1 && NWV <= NS);
+  static_assert(!STAGE || (NC == 1 && NWV <= NS && 16 * MF * 16 * 4 <= SLOT), "staging fits a ring slot");
   static_assert(U % 2 == 0, "each x load moves two k-blocks of 8 rows");
   static_assert((D - 1) * LPW < 64, "vmcnt range");
   static_assert(NS * SLOT + NWV * XPW * 16 * 4 <= 160 * 1024, "LDS budget");
@@ -111,6 +118,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[SLOT];
   __shared__ float ssp[NWV][XPW][16];      // Gram diagonals
+  __shared__ __attribute__((aligned(16))) float inv_s[MF * 16];   // 1/RMS per row
   auto slot_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
     return s == 0 ? ring0 : (s == 1 ? ring1 : (s == 2 ? ring2 : ring3));
   };
@@ -123,6 +131,15 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   // bytes of one packed column block: a fragment per k-block (bf16) or per
   // pair of k-blocks (fp8)
   const int64_t kfrag = (int64_t)(F8 ? (a.kblocks + 1) / 2 : a.kblocks) * kFragBytes;
+
+  // fp8 weights: this lane's column scales, fetched now so the epilogue does
+  // not wait for them
+  float scol[NST];
+#pragma unroll
+  for (int c = 0; c < NST; ++c) {
+    const int col = (nb0 + c % NC) * 16 + lrow;
+    scol[c] = F8 && col < a.N ? (c < NC ? a.sg : a.su)[col] : 1.f;
+  }
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc_x(static_cast<const __bf16*>(a.x) + (size_t)m0 * a.K,
                                                 (int64_t)min(MF * 16, a.M - m0) * a.K * 2);
@@ -270,31 +287,96 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
       ssp[w][j][lrow] = e == 0 ? gram[j][0] : (e == 1 ? gram[j][1] : (e == 2 ? gram[j][2] : gram[j][3]));
   }
   __syncthreads();
+  // 1/RMS once per row: thread t sums row t's Gram diagonals (accumulator j
+  // of wave v holds fragment q = v + NWV*j, row block q % MF)
+  if (threadIdx.x < MF * 16) {
+    const int i = threadIdx.x / 16, rr = threadIdx.x % 16;
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < NWV; ++v)
+#pragma unroll
+      for (int j = 0; j < XPW; ++j)
+        if (v + NWV * j < XF && (v + NWV * j) % MF == i) ss += ssp[v][j][rr];
+    inv_s[threadIdx.x] = inv_rms(ss, (float)a.K, a.eps);
+  }
+  __syncthreads();
 
-  const float kf = (float)a.K;
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
+    const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&inv_s[16 * i + 4 * lgrp]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int rr = 4 * lgrp + e;
       const int row = m0 + 16 * i + rr;
-      // Gram accumulator j of wave v holds fragment q = v + NWV*j, row block q % MF
-      float ss = 0.f;
-#pragma unroll
-      for (int v = 0; v < NWV; ++v)
-#pragma unroll
-        for (int j = 0; j < XPW; ++j)
-          if (v + NWV * j < XF && (v + NWV * j) % MF == i) ss += ssp[v][j][rr];
-      const float inv = inv_rms(ss, kf, a.eps);
+      const float inv = inv4[e];
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const int col = (nb0 + j) * 16 + lrow;
-        if (row < a.M && col < a.N) {
-          // fp8 weights: the column scale joins 1/RMS
-          const float ig = F8 ? a.sg[col] * inv : inv;
-          const float iu = F8 && SW ? a.su[col] * inv : inv;
+        const bool col_ok = col < a.N;
+        // fp8 weights: the column scale joins 1/RMS
+        const float ig = F8 ? scol[j] * inv : inv;
+        const float iu = F8 && SW ? scol[NC + j] * inv : inv;
+        if constexpr (STAGE) {
+          // staged in this wave's (now idle) ring slot as [row][16 columns]
+          const float val = SW ? silu_times(acc[j][i][e] * ig, acc[NC + j][i][e] * iu) : acc[j][i][e] * ig;
+          reinterpret_cast<float*>(slot_ptr(w))[(16 * i + rr) * 16 + lrow] = val;
+        } else if (row < a.M && col_ok) {
           const float val = SW ? silu_times(acc[j][i][e] * ig, acc[NC + j][i][e] * iu) : acc[j][i][e] * ig;
           Store<__bf16>::one(static_cast<__bf16*>(a.y) + (size_t)row * a.N + col, val);
+        }
+      }
+    }
+  }
+  if constexpr (STAGE) {
+    // One lane per row: the lane reads its row's 16 values of the wave's
+    // column block back and stores them with 16-byte stores when the block
+    // is whole and aligned.  fp8 output: the block's largest magnitude (NaN
+    // propagates), r = 448/amax and s = amax/448 (correctly rounded; 1 for
+    // an all-zero block), codes RNE_E4M3(v * r).
+    // the values cross lanes through LDS: order this wave's writes before its reads
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const float* tile = reinterpret_cast<const float*>(slot_ptr(w));
+    const int nb = nb0;
+    const int row = m0 + lane;
+    if (lane < 16 * MF && row < a.M && nb < a.nblocks) {
+      const int ncols = min(16, a.N - 16 * nb);
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 t4 = *reinterpret_cast<const f32x4*>(tile + lane * 16 + 4 * k);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[4 * k + c] = t4[c];
+      }
+      if constexpr (Q8) {
+        float m = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) m = nan_max(m, c < ncols ? fabsf(v[c]) : 0.f);
+        const bool zero = m == 0.f;
+        const float r = zero ? 1.f : __fdiv_rn(448.f, m);
+        u32x4 packed = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 16; ++c) packed[c / 4] |= e4m3_rne(v[c] * r) << (8 * (c % 4));
+        uint8_t* dst = a.q + (size_t)row * a.N + 16 * nb;
+        if (ncols == 16 && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+          *reinterpret_cast<u32x4*>(dst) = packed;
+        } else {
+          for (int c = 0; c < ncols; ++c) dst[c] = (uint8_t)(packed[c / 4] >> (8 * (c % 4)));
+        }
+        a.qs[(size_t)row * a.nblocks + nb] = zero ? 1.f : __fdiv_rn(m, 448.f);
+      } else {
+        u32x4 p0, p1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          p0[c] = pack_bf16x2(v[2 * c], v[2 * c + 1]);
+          p1[c] = pack_bf16x2(v[8 + 2 * c], v[8 + 2 * c + 1]);
+        }
+        __bf16* dst = static_cast<__bf16*>(a.y) + (size_t)row * a.N + 16 * nb;
+        if (ncols == 16 && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+          reinterpret_cast<u32x4*>(dst)[0] = p0;
+          reinterpret_cast<u32x4*>(dst)[1] = p1;
+        } else {
+          for (int c = 0; c < ncols; ++c) Store<__bf16>::one(dst + c, v[c]);
         }
       }
     }
@@ -304,27 +386,29 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 struct DecodeXInstance {
   const void* fn;
   int mf, nc, nwv, u;
-  bool sw, f8;
+  bool sw, f8, q8;
   const char* name;
 };
 
-#define FN_DECODE_X(MF, NC, NWV, SW, U, NAME)                                                            \
+#define FN_DECODE_XI(MF, NC, NWV, SW, U, F8, Q8, NAME)                                                     \
   DecodeXInstance {                                                                                     \
-    reinterpret_cast<const void*>(&decode_x_kernel<MF, NC, NWV, SW, U, false>), MF, NC, NWV, U, SW, false, NAME \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, NC, NWV, SW, U, F8, Q8>), MF, NC, NWV, U, SW, F8, Q8, NAME \
   }
-#define FN_DECODE_X8(MF, NC, NWV, SW, U, NAME)                                                         \
-  DecodeXInstance {                                                                                   \
-    reinterpret_cast<const void*>(&decode_x_kernel<MF, NC, NWV, SW, U, true>), MF, NC, NWV, U, SW, true, NAME \
-  }
+#define FN_DECODE_X(MF, NC, NWV, SW, U, NAME) FN_DECODE_XI(MF, NC, NWV, SW, U, false, false, NAME)
+#define FN_DECODE_X8(MF, NC, NWV, SW, U, NAME) FN_DECODE_XI(MF, NC, NWV, SW, U, true, false, NAME)
 
 // Rows tile over grid.y in blocks of 16*MF; sg and su are the fp8 column
-// scales (null for bf16 weights).
+// scales (null for bf16 weights); q and qs the fp8 output (codes, row-block
+// scales) of the Q8 instances.
 inline hipError_t launch_decode_x_instance(const DecodeXInstance& d, const void* x, const void* wg, const void* wu,
                                            void* y, int M, int K, int N, float eps, hipStream_t stream,
-                                           const float* sg = nullptr, const float* su = nullptr) {
+                                           const float* sg = nullptr, const float* su = nullptr,
+                                           uint8_t* q = nullptr, float* qs = nullptr) {
   DecodeXArgs a;
   a.sg = sg;
   a.su = su;
+  a.q = q;
+  a.qs = qs;
   a.x = x;
   a.wg = wg;
   a.wu = wu;
@@ -369,6 +453,16 @@ static const DecodeXInstance kDecodeF8[] = {
     FN_DECODE_X8(4, 1, 4, true, 2, "decode_swiglu_fp8_m64_xlds_w4_u2"),
 };
 
+// SwiGLU with fp8 output: the instances above with the row-block epilogue.
+static const DecodeXInstance kDecodeQ8[] = {
+    FN_DECODE_XI(1, 1, 3, true, 2, false, true, "decode_swiglu_bf16_q8_m16_xlds_w3_u2"),
+    FN_DECODE_XI(2, 1, 3, true, 2, false, true, "decode_swiglu_bf16_q8_m32_xlds_w3_u2"),
+    FN_DECODE_XI(4, 1, 3, true, 2, false, true, "decode_swiglu_bf16_q8_m64_xlds_w3_u2"),
+    FN_DECODE_XI(1, 1, 3, true, 4, true, true, "decode_swiglu_fp8_q8_m16_xlds_w3_u4"),
+    FN_DECODE_XI(2, 1, 3, true, 4, true, true, "decode_swiglu_fp8_q8_m32_xlds_w3_u4"),
+    FN_DECODE_XI(4, 1, 4, true, 2, true, true, "decode_swiglu_fp8_q8_m64_xlds_w4_u2"),
+};
+
 template <size_t L>
 static const DecodeXInstance* find_instance(const DecodeXInstance (&t)[L], int mf, bool sw) {
   for (const DecodeXInstance& d : t)
@@ -407,6 +501,26 @@ hipError_t launch_decode_x(DType dt, const FusedPlan& p, const void* x, const vo
 FusedPlan plan_fp8(int64_t M, int64_t K, int64_t N, bool swiglu) {
   (void)K;
   return plan_of(find_instance(kDecodeF8, M <= 16 ? 1 : (M <= 32 ? 2 : 4), swiglu), 3, M, N);
+}
+
+// SwiGLU with fp8 output, rows up to 64 (bf16 weights; larger M goes to the
+// prefill kernel) or any M (fp8 weights).
+static const DecodeXInstance* find_q8(bool f8, int mf) {
+  for (const DecodeXInstance& d : kDecodeQ8)
+    if (d.f8 == f8 && d.mf == mf) return &d;
+  return nullptr;
+}
+
+FusedPlan plan_decode_q8(bool f8_weights, int64_t M, int64_t N) {
+  return plan_of(find_q8(f8_weights, M <= 16 ? 1 : (M <= 32 ? 2 : 4)), 4, M, N);
+}
+
+hipError_t launch_decode_q8(bool f8_weights, const FusedPlan& p, const void* x, const void* wg, const float* sg,
+                            const void* wu, const float* su, uint8_t* q, float* qs, int M, int K, int N, float eps,
+                            hipStream_t stream) {
+  const DecodeXInstance* d = find_q8(f8_weights, p.mf);
+  if (d == nullptr || (!f8_weights && M > 16 * d->mf)) return hipErrorInvalidValue;
+  return launch_decode_x_instance(*d, x, wg, wu, nullptr, M, K, N, eps, stream, sg, su, q, qs);
 }
 
 hipError_t launch_fp8(const FusedPlan& p, const void* x, const void* wg, const float* sg, const void* wu,

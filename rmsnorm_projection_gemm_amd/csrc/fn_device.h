@@ -99,11 +99,73 @@ template <> __device__ inline f32x4 mfma_chunk<float>(u32x4 a, u32x4 b, f32x4 ac
   return acc;
 }
 
-__device__ inline float silu_times(float a, float b) { return a / (1.0f + expf(-a)) * b; }
+// silu(a) * b = a / (1 + e^-a) * b, with the hardware exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32: about 1 ulp each) instead of the libm-accurate
+// expf and a correctly rounded division -- a few fp32 ulps, far below the
+// bf16 (or E4M3) rounding that follows, for a fraction of the instructions.
+// Large negative a: e^-a overflows to inf, rcp(inf) = 0, result -0 or 0.
+__device__ inline float silu_times(float a, float b) {
+  const float e = __builtin_amdgcn_exp2f(a * -1.44269504088896341f);
+  return a * __builtin_amdgcn_rcpf(1.0f + e) * b;
+}
 
 // 1 / sqrt(sum_sq / K + eps) in fp32: the deferred per-row scale.
 __device__ inline float inv_rms(float sumsq, float k, float eps) {
   return 1.0f / sqrtf(sumsq / k + eps);
+}
+
+// ---- OCP fp8 E4M3 ----------------------------------------------------------
+// Round-to-nearest-even E4M3 code of v (bias 7, 3 mantissa bits, subnormals
+// on the 2^-9 grid, largest finite 448, NaN 0x7F).  Magnitudes that round
+// past 448 saturate to it.
+// Branch-free: in the normal range the fp32 mantissa is rounded to 3 bits
+// (add 2^19 - 1 plus the lowest kept bit, ties to even; a carry moves into
+// the exponent) and the exponent rebiased from 127 to 7; below 2^-6 the
+// value is counted in units of 2^-9 (exact scaling, rint ties to even).
+__device__ inline uint32_t e4m3_rne(float v) {
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t abits = bits & 0x7fffffffu;
+  const float a = __uint_as_float(abits);
+  const uint32_t rounded = abits + 0x7FFFFu + ((abits >> 20) & 1u);
+  const uint32_t normal = (rounded >> 20) - (120u << 3);      // (exponent - 127 + 7) << 3 | 3 mantissa bits
+  const uint32_t sub = (uint32_t)rintf(a * 512.0f);          // 0..8; 8 is the smallest normal's code
+  uint32_t code = a < 0.015625f ? sub : normal;
+  code = code < 0x7Eu ? code : 0x7Eu;                        // saturate at 448
+  return (a != a) ? 0x7Fu : (sign | code);
+}
+
+// Lane permutation inside each 16-lane row of the wave (DPP, no LDS).
+template <int CTRL>
+__device__ inline float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// max that propagates NaN from either side
+__device__ inline float nan_max(float m, float t) { return (m > t || m != m) ? m : t; }
+// Maximum over the 16 lanes of a DPP row: lane ^ 1, lane ^ 2 (quad
+// permutes), then the mirror within 8 lanes and within 16 lanes.
+__device__ inline float row16_max(float m) {
+  m = nan_max(m, dpp_move<0xB1>(m));    // quad_perm [1,0,3,2]
+  m = nan_max(m, dpp_move<0x4E>(m));    // quad_perm [2,3,0,1]
+  m = nan_max(m, dpp_move<0x141>(m));   // row_half_mirror
+  m = nan_max(m, dpp_move<0x140>(m));   // row_mirror
+  return m;
+}
+
+// fp8 output with one scale per 16-column row block.  In a 16x16
+// accumulator tile lane l holds column l%16 of row 4*(l/16)+e, so the 16
+// lanes sharing l/16 -- one DPP row -- hold one row's block: its largest
+// magnitude is a reduction over that row (NaN propagates).  Then
+// r = 448/amax and s = amax/448, both correctly rounded (r = s = 1 for an
+// all-zero block), and code = RNE_E4M3(v * r).  Every lane of the wave must
+// call this (cross-lane reduction); col_ok and row_ok mask what is stored,
+// blk_ok says the block exists (its scale is stored by the block's lane 0).
+__device__ inline void store_q8(float v, bool col_ok, bool row_ok, bool blk_ok, uint8_t* code, float* scale) {
+  const float m = row16_max(col_ok ? fabsf(v) : 0.f);
+  const bool zero = m == 0.f;
+  const float r = zero ? 1.f : __fdiv_rn(448.f, m);
+  if (row_ok && col_ok) *code = (uint8_t)e4m3_rne(v * r);
+  if (row_ok && blk_ok && (threadIdx.x & 15) == 0) *scale = zero ? 1.f : __fdiv_rn(m, 448.f);
 }
 
 }  // namespace fn

@@ -14,7 +14,8 @@ inline int k_per_block(DType t) { return t == DType::F32 ? 16 : 32; }   // KB of
 // Kernel instance chosen for one fused call.
 struct FusedPlan {
   int kind;           // 0 = decode (<= 16 rows, or fp32), 1 = prefill (tiled), 2 = decode with x in LDS,
-                      // 3 = fp8 weights (x in LDS, rows tiled over grid.y)
+                      // 3 = fp8 weights (x in LDS, rows tiled over grid.y),
+                      // 4 = SwiGLU with fp8 output (x in LDS), 5 = the same on the prefill kernel
   int mf;             // 16-row fragments per workgroup (decode)
   int nf;             // 16-column fragments per workgroup (decode)
   int waves;          // waves per workgroup
@@ -34,10 +35,11 @@ hipError_t launch_decode_x(DType dt, const FusedPlan& plan, const void* x, const
                            const void* w_up, void* y, int M, int K, int N, float eps,
                            hipStream_t stream);
 
-FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu);
+// q8: SwiGLU with fp8 output (codes q, row-block scales qs; y unused).
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8 = false);
 hipError_t launch_prefill(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
                           const void* w_up, void* y, int M, int K, int N, float eps,
-                          hipStream_t stream);
+                          hipStream_t stream, uint8_t* q = nullptr, float* qs = nullptr);
 
 hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
                        int K, int N, hipStream_t stream);
@@ -49,6 +51,14 @@ FusedPlan plan_fp8(int64_t M, int64_t K, int64_t N, bool swiglu);
 hipError_t launch_fp8(const FusedPlan& plan, const void* x, const void* wg, const float* sg,
                       const void* wu, const float* su, void* y, int M, int K, int N, float eps,
                       hipStream_t stream);
+
+// SwiGLU with fp8 output (E4M3 codes, one scale per 16-column row block):
+// the LDS-shared-x decode kernel (bf16 weights up to 64 rows, fp8 weights
+// any M).
+FusedPlan plan_decode_q8(bool f8_weights, int64_t M, int64_t N);
+hipError_t launch_decode_q8(bool f8_weights, const FusedPlan& plan, const void* x, const void* wg,
+                            const float* sg, const void* wu, const float* su, uint8_t* q, float* qs,
+                            int M, int K, int N, float eps, hipStream_t stream);
 
 hipError_t launch_fused(DType dt, const FusedPlan& plan, const void* x,
                         const void* w_gate, const void* w_up, void* y,

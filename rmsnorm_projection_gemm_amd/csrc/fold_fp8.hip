@@ -17,29 +17,6 @@
 
 namespace fn {
 
-// Round-to-nearest-even E4M3 code of v (OCP: bias 7, 3 mantissa bits,
-// subnormals on the 2^-9 grid, largest finite 448, NaN 0x7F).  Magnitudes
-// that round past 448 saturate to it.
-__device__ inline uint32_t e4m3_rne(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (!(a == a)) return 0x7Fu;
-  if (a < 0.015625f) {                         // below 2^-6: multiples of 2^-9
-    const float q = rintf(a * 512.0f);         // exact scaling, then ties to even
-    return sign | (uint32_t)q;                 // 0..8; 8 is the smallest normal's code
-  }
-  int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;   // a = 2^e * 1.f
-  if (e > 8) return sign | 0x7Eu;
-  float q = rintf(ldexpf(a, 3 - e));           // 8..16 quanta of 2^(e-3)
-  if (q >= 16.0f) {
-    q = 8.0f;
-    ++e;
-  }
-  const int field = e + 7;
-  if (field > 15 || (field == 15 && q > 14.0f)) return sign | 0x7Eu;
-  return sign | ((uint32_t)field << 3) | (uint32_t)(q - 8.0f);
-}
-
 // Stored folded weight as an fp32 value (zero outside the matrix).
 template <typename T>
 __device__ inline float folded_value(const T* g, const T* W, int k, int n, int K, int N) {

@@ -40,6 +40,8 @@ struct PrefillArgs {
   int kblocks;       // ceil(K / 32)
   int nblocks;       // ceil(N / 16)
   float eps;
+  uint8_t* q;        // fp8 output: E4M3 codes [M, N] (y unused)
+  float* qs;         // fp8 output: scales [M, nblocks], one per 16-column row block
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -59,7 +61,7 @@ __device__ inline void wait_vmcnt() {
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int FM, int FN, int WM, int WN, bool SW, int NS, bool GRAM>
+template <int FM, int FN, int WM, int WN, bool SW, int NS, bool GRAM, bool Q8>
 __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = SW ? 2 : 1;
@@ -268,7 +270,18 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
       const int rl = (wm * FM + i) * 16 + 4 * lgrp + r;   // row within the tile
       const int row = m0 + rl;
       const float inv = inv_rms(ssbuf[rl], kf, a.eps);
-      if (row < a.M) {
+      if constexpr (Q8) {
+        // fp8 output: every lane takes part in each block maximum
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int nb = nb0 + wn * FN + j;
+          const int col = nb * 16 + lrow;
+          const float v = SW ? silu_times(acc[0][i][j][r] * inv, acc[NMAT - 1][i][j][r] * inv)
+                             : acc[0][i][j][r] * inv;
+          store_q8(v, col < a.N, row < a.M, nb < a.nblocks, a.q + (size_t)row * a.N + col,
+                   a.qs + (size_t)row * a.nblocks + nb);
+        }
+      } else if (row < a.M) {
         __bf16* yrow = static_cast<__bf16*>(a.y) + (size_t)row * a.N;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -291,22 +304,25 @@ struct PrefillInstance {
   const char* name;
 };
 
-#define FN_PREFILL(FM, FN_, WM, WN, SW, NS, GRAM, NAME) \
-  PrefillInstance{reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, NS, GRAM>), FM, FN_, WM, WN, NS, SW, NAME}
+#define FN_PREFILL(FM, FN_, WM, WN, SW, NS, GRAM, Q8, NAME)                                                      \
+  PrefillInstance {                                                                                               \
+    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, NS, GRAM, Q8>), FM, FN_, WM, WN, NS, SW, NAME \
+  }
 
 static const PrefillInstance kPrefill[] = {
-    FN_PREFILL(4, 8, 4, 2, false, 4, true, "prefill_bf16_256x256_w4x2_s4"),
-    FN_PREFILL(4, 4, 4, 2, true, 4, true, "prefill_swiglu_bf16_256x128_w4x2_s4"),
+    FN_PREFILL(4, 8, 4, 2, false, 4, true, false, "prefill_bf16_256x256_w4x2_s4"),
+    FN_PREFILL(4, 4, 4, 2, true, 4, true, false, "prefill_swiglu_bf16_256x128_w4x2_s4"),
+    FN_PREFILL(4, 4, 4, 2, true, 4, true, true, "prefill_swiglu_bf16_q8_256x128_w4x2_s4"),
 };
 
-static const PrefillInstance& pick(bool sw) { return kPrefill[sw ? 1 : 0]; }
+static const PrefillInstance& pick(bool sw, bool q8 = false) { return kPrefill[q8 ? 2 : (sw ? 1 : 0)]; }
 
-FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8) {
   (void)dt;
   (void)K;
-  const PrefillInstance& d = pick(swiglu);
+  const PrefillInstance& d = pick(swiglu, q8);
   FusedPlan p{};
-  p.kind = 1;
+  p.kind = q8 ? 5 : 1;
   p.mf = d.fm * d.wm;
   p.nf = d.fn_ * d.wn;
   p.waves = d.wm * d.wn;
@@ -317,10 +333,12 @@ FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
 }
 
 hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
-                          int M, int K, int N, float eps, hipStream_t stream) {
-  if (dt != DType::BF16) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr);
+                          int M, int K, int N, float eps, hipStream_t stream, uint8_t* q, float* qs) {
+  if (dt != DType::BF16 || (q != nullptr && wu == nullptr)) return hipErrorInvalidValue;
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr);
   PrefillArgs a;
+  a.q = q;
+  a.qs = qs;
   a.x = x;
   a.wg = wg;
   a.wu = wu;

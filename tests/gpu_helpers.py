@@ -82,3 +82,48 @@ def pack_fp8_host(codes: np.ndarray) -> np.ndarray:
     # k = ((kp*2 + h)*4 + grp)*8 + j, n = nb*16 + c -> [nb, kp, grp, c, h, j]
     p = pad.reshape(kp, 2, 4, 8, nbl, 16).transpose(4, 0, 2, 5, 1, 3)
     return np.ascontiguousarray(p).reshape(-1)
+
+
+def assert_q8_close(codes, scales, v_ref, what: str, margin: float = 0.02, v_atol: float = 1e-5,
+                    s_rtol: float = 1e-4, max_flip_frac: float = 1e-3):
+    """fp8 row-block output (codes [M,N] uint8, scales [M,nb] fp32, from the
+    GPU) against the oracle's quantisation of the float64 reference v_ref.
+    Scales agree to s_rtol (the block maximum of the GPU's fp32 values);
+    codes agree exactly except where the reference's scaled value lies
+    within `margin` quanta, or within v_atol * (block maximum) before
+    scaling (the absolute error of an fp32 dot product over K terms), of a
+    rounding midpoint: there the GPU may take the neighbouring code.  At most
+    max_flip_frac of the codes may do so."""
+    import oracle
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.float64)
+    ref_codes, ref_s = oracle.quantize_e4m3_row_blocks(v_ref)
+    ref_s = ref_s.astype(np.float64)
+    assert codes.shape == ref_codes.shape and scales.shape == ref_s.shape, f"{what}: shapes"
+    nan_rows = np.isnan(ref_s)
+    assert np.array_equal(np.isnan(scales), nan_rows), f"{what}: NaN scales differ"
+    ok = ~nan_rows
+    assert np.all(np.abs(scales[ok] - ref_s[ok]) <= s_rtol * ref_s[ok]), \
+        f"{what}: scales differ by {np.max(np.abs(scales[ok] - ref_s[ok]) / ref_s[ok]):.3e} relative"
+    diff = codes != ref_codes
+    if not diff.any():
+        return 0
+    m_idx, n_idx = np.nonzero(diff)
+    blk = n_idx // 16
+    r = np.float32(448.0) / np.maximum(ref_s[m_idx, blk] * 448.0, 1e-300)
+    u = np.abs(np.asarray(v_ref, dtype=np.float32)[m_idx, n_idx].astype(np.float64) * r)
+    _, e = np.frexp(np.maximum(u, 1e-300))
+    quantum = np.ldexp(1.0, np.maximum(e, -5) - 4)
+    frac = u / quantum - np.floor(u / quantum)
+    near = np.abs(frac - 0.5) * quantum <= margin * quantum + v_atol * 448.0
+    dg = oracle.e4m3_decode(codes[m_idx, n_idx])
+    dr = oracle.e4m3_decode(ref_codes[m_idx, n_idx])
+    neighbour = ((codes[m_idx, n_idx] & 0x80) == (ref_codes[m_idx, n_idx] & 0x80)) & \
+        (np.abs(codes[m_idx, n_idx].astype(int) - ref_codes[m_idx, n_idx].astype(int)) == 1)
+    both_zero = (dg == 0) & (dr == 0)
+    bad = ~(both_zero | (near & neighbour))
+    assert not bad.any(), (f"{what}: {bad.sum()} codes differ away from a rounding midpoint, first at "
+                           f"{(m_idx[bad][0], n_idx[bad][0])}: {codes[m_idx[bad][0], n_idx[bad][0]]:#x} vs "
+                           f"{ref_codes[m_idx[bad][0], n_idx[bad][0]]:#x}")
+    assert diff.sum() <= max(2, max_flip_frac * diff.size), f"{what}: {diff.sum()} codes at midpoints"
+    return int(diff.sum())

@@ -201,8 +201,8 @@ def test_fp8_swiglu_and_fold_reject(lib):
 
 
 def _call(kind=fn.FN_CALL_NORM_PROJ, x=0x1000, wg=0x20000, wu=None, sg=None, su=None, y=0x40000, M=4, K=16, N=16,
-          eps=1e-6, dt=BF16):
-    return fn.FnCall(kind, x, wg, wu, sg, su, y, M, K, N, eps, dt)
+          eps=1e-6, dt=BF16, ys=None):
+    return fn.FnCall(kind, x, wg, wu, sg, su, y, M, K, N, eps, dt, ys)
 
 
 def _create(lib, calls):
@@ -213,9 +213,10 @@ def _create(lib, calls):
 
 
 def test_fn_call_layout_matches_header():
-    # kind, 6 pointers, 3 int64, float, enum: 4 + 4 (pad) + 48 + 24 + 4 + 4
-    assert ctypes.sizeof(fn.FnCall) == 88
+    # kind, 6 pointers, 3 int64, float, enum, pointer: 4 + 4 (pad) + 48 + 24 + 4 + 4 + 8
+    assert ctypes.sizeof(fn.FnCall) == 96
     assert fn.FnCall.x.offset == 8 and fn.FnCall.M.offset == 56 and fn.FnCall.eps.offset == 80
+    assert fn.FnCall.y_scales.offset == 88
 
 
 def test_step_create_validates_every_call_first(lib):
@@ -234,6 +235,11 @@ def test_step_create_validates_every_call_first(lib):
     assert st == ALIAS
     st, _ = _create(lib, [_call(eps=-1.0)])
     assert st == EPS
+    st, _ = _create(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_SWIGLU_Q8, wu=0x30000)])
+    assert st == NULL and "out_scales" in lib.fn_last_error().decode()
+    st, _ = _create(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8, wu=0x30000, sg=0x50000, su=0x51000,
+                                ys=0x40008)])
+    assert st == ALIAS and "out_codes overlaps out_scales" in lib.fn_last_error().decode()
     st, _ = _create(lib, [_call(kind=7)])
     assert st == DTYPE and "call kind" in lib.fn_last_error().decode()
     st, _ = _create(lib, [])
@@ -247,3 +253,43 @@ def test_step_null_arguments(lib):
     assert lib.fn_step_launch(None, None) == NULL
     assert lib.fn_step_num_kernels(None) == -1
     assert lib.fn_step_destroy(None) == OK
+
+
+def _q8(lib, x=0x1000, wg=0x20000, wu=0x30000, c=0x40000, s=0x50000, M=4, K=16, N=16, eps=1e-6):
+    return lib.fn_norm_proj_swiglu_q8(x, wg, wu, c, s, M, K, N, eps, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(x=None), NULL, "x is NULL"),
+    (dict(wu=None), NULL, "gate or up"),
+    (dict(c=None), NULL, "out_codes"),
+    (dict(s=None), NULL, "out_scales"),
+    (dict(K=12), SHAPE, "multiple of 8"),
+    (dict(x=0x1008), ALIGN, "x must be"),
+    (dict(wg=0x20008), ALIGN, "packed weights"),
+    (dict(s=0x50002), ALIGN, "out_scales"),
+    (dict(eps=float("nan")), EPS, "eps"),
+    (dict(c=0x1000), ALIAS, "overlaps"),
+    (dict(s=0x30000), ALIAS, "overlaps"),
+    (dict(s=0x40000), ALIAS, "out_codes overlaps out_scales"),
+])
+def test_swiglu_q8_rejects(lib, kwargs, status, needle):
+    assert _q8(lib, **kwargs) == status
+    assert needle in lib.fn_last_error().decode()
+
+
+def test_swiglu_q8_codes_need_no_alignment_and_empty_is_ok(lib):
+    # odd code addresses pass validation (byte stores); empty calls read nothing
+    assert _q8(lib, x=None, wg=None, wu=None, c=None, s=None, M=0) == OK
+    f = lib.fn_norm_proj_swiglu_fp8_q8
+    assert f(0x1000, 0x20000, None, 0x30000, 0x31000, 0x40001, 0x50000, 4, 16, 16, 1e-6, None) == NULL
+    assert "s_gate" in lib.fn_last_error().decode()
+    assert f(0x1000, 0x20000, 0x21000, 0x30000, 0x31002, 0x40001, 0x50000, 4, 16, 16, 1e-6, None) == ALIGN
+
+
+def test_q8_kernel_names(lib):
+    assert lib.fn_kernel_name_q8(16, 4096, 11008, 0).decode() == "decode_swiglu_bf16_q8_m16_xlds_w3_u2"
+    assert lib.fn_kernel_name_q8(64, 4096, 11008, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
+    assert lib.fn_kernel_name_q8(65, 4096, 11008, 0).decode().startswith("prefill_swiglu_bf16_q8")
+    assert lib.fn_kernel_name_q8(4096, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_q8_m64")
+    assert lib.fn_kernel_name_q8(0, 4096, 16, 0) == b"invalid"
