@@ -180,28 +180,55 @@ __global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
   // Partials meet in LDS.  Accumulator element r of lane l is row
   // 4*(l/16) + r, column l%16 of its 16x16 tile; the Gram diagonal (row ==
   // column) therefore sits in lanes whose l%16 / 4 == l/16, element l%4.
-  __shared__ float red_acc[WK][WN][NMAT][MF][NF][4][kWave];
+  // Without a k-split (WK == 1) the accumulators stay in registers and the
+  // diagonal lanes turn their sums of squares into 1/RMS right away, one
+  // per row.
+  constexpr bool ONE = WK == 1;
+  const float kf = (float)a.K;
+  __shared__ float red_acc[ONE ? 1 : WK][WN][NMAT][MF][NF][4][kWave];
   __shared__ float red_ss[WK][WN][MF][16];
+  if constexpr (!ONE) {
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf)
+      for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
-      for (int nf = 0; nf < NF; ++nf)
+        for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red_acc[wk][wn][m][mf][nf][r][lane] = acc[m][mf][nf][r];
+          for (int r = 0; r < 4; ++r) red_acc[wk][wn][m][mf][nf][r][lane] = acc[m][mf][nf][r];
+  }
   if ((lrow >> 2) == lgrp) {
     const int r = lrow & 3;
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) {
       const f32x4 gv = gram[mf];
-      red_ss[wk][wn][mf][lrow] = r == 0 ? gv[0] : (r == 1 ? gv[1] : (r == 2 ? gv[2] : gv[3]));
+      const float g = r == 0 ? gv[0] : (r == 1 ? gv[1] : (r == 2 ? gv[2] : gv[3]));
+      red_ss[wk][wn][mf][lrow] = ONE ? inv_rms(g, kf, a.eps) : g;
     }
   }
   __syncthreads();
 
+  if constexpr (ONE) {
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        const int col = (nb0 + nf) * 16 + lrow;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * lgrp + r;
+          const int row = m0 + 16 * mf + i;
+          if (row < a.M && col < a.N) {
+            const float inv = red_ss[0][wn][mf][i];
+            const float p0 = acc[0][mf][nf][r];
+            const float v = SW ? silu_times(p0 * inv, acc[NMAT - 1][mf][nf][r] * inv) : p0 * inv;
+            Store<T>::one(static_cast<T*>(a.y) + (size_t)row * a.N + col, v);
+          }
+        }
+      }
+    return;
+  }
   // Epilogue: the WK waves of column group wn finish its tiles wk, wk + WK, ...
-  const float kf = (float)a.K;
   for (int t = wk; t < MF * NF; t += WK) {
     const int mf = t / NF, nf = t % NF;
     const int col = (nb0 + nf) * 16 + lrow;

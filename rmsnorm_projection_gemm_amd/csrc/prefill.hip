@@ -5,27 +5,32 @@
 // 16*FN*WN columns per weight matrix) with WM x WN waves, each owning a
 // 16*FM x 16*FN sub-tile whose fp32 accumulators stay in registers for the
 // whole k loop.  The instances use 256x256 tiles (256x128 per matrix for
-// SwiGLU) with eight waves of 64x128, two waves per SIMD, and a 3-slot ring:
-// measured on MI355X this beats four waves of 128x128 by ~40%, the second
-// wave hiding the barrier and LDS latency of the first.  Operands stream through an NS-stage LDS ring, one 32-wide
-// k-block per stage, filled by direct global-to-LDS buffer loads (no
-// register staging).  Every operand lands in LDS already in MFMA fragment
-// order -- W' because the packed layout is fragment-major, x because each
-// lane of the loading wave fetches exactly the 16 bytes its MFMA lane will
-// own -- so each fragment read is one conflict-free ds_read_b128 at lane*16.
-// Loads past the matrix edges (rows >= M, columns past the packed width,
-// k >= K) use out-of-range buffer offsets, which read as zero.
+// SwiGLU) with eight waves of 64x128, two waves per SIMD: measured on MI355X
+// this beats four waves of 128x128 by ~40%, the second wave hiding the
+// barrier and LDS latency of the first.
+//
+// Operands stream through LDS rings filled by direct global-to-LDS buffer
+// loads (no register staging): W' one 32-wide k-block per slot (4 slots),
+// x a pair of k-blocks per slot (2 slots).  W' lands in MFMA fragment order
+// because the packed layout is fragment-major.  x arrives as whole 128-byte
+// lines -- each load brings 8 rows x 64 k values -- because a direct-to-LDS
+// load whose lanes fetch 16 rows x 64 bytes (half lines) measured 37.5 GB/s
+// per CU from L2-resident data against 88-90 GB/s for whole lines; row r's
+// 16-byte chunks are stored permuted by r/2 so the quarter-wave operand
+// reads (ds_read_b128) hit distinct bank groups.  Loads past the matrix
+// edges (rows >= M, columns past the packed width, k >= K) use out-of-range
+// buffer offsets, which read as zero.
 //
 // The per-row sum of squares comes from the x fragments already in
 // registers: each of the WN waves that share a row block takes a 1/WN share
-// of its row fragments, either on the VALU (convert and FMA) or, in the
-// instances, as the diagonal of an x x^T MFMA (GRAM), which measured faster
-// than the VALU form once the MFMA pipe is the bottleneck only 1/16 of the
-// time it spends on the projection.  The shares meet in LDS before the
+// of its row fragments as the diagonal of an x x^T MFMA (measured faster
+// than convert-and-FMA on the VALU).  The shares meet in LDS before the
 // epilogue applies 1/RMS (and SiLU * up) to the accumulators and stores
 // ([FlashNorm digest] proposals 1-2; [FlashInfer #5521] "Design" items 1-2,
 // tiles kept resident across the k loop and the SwiGLU applied to the
 // accumulators in registers).
+#include <type_traits>
+
 #include "fn_device.h"
 #include "fn_launch.h"
 
@@ -61,30 +66,33 @@ __device__ inline void wait_vmcnt() {
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int FM, int FN, int WM, int WN, bool SW, int NS, bool GRAM, bool Q8>
+template <int FM, int FN, int WM, int WN, bool SW, bool Q8>
 __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = SW ? 2 : 1;
   constexpr int BMF = FM * WM;                   // 16-row fragments per tile
   constexpr int BNF = FN * WN;                   // 16-column fragments per tile and matrix
-  constexpr int SFR = BMF + NMAT * BNF;          // fragments per stage (one k-block)
-  constexpr int LPW = SFR / NW;                  // loads per wave per stage
-  constexpr int ALPW = BMF / NW;                 // of which x fragments
+  constexpr int WFR = NMAT * BNF;                // W' fragments per k-block
+  constexpr int WPW = WFR / NW;                  // W' loads per wave per k-block
+  constexpr int XFR = 2 * BMF;                   // x loads per pair of k-blocks (8 rows x 128 B each)
+  constexpr int XPW = XFR / NW;                  // x loads per wave per pair
   constexpr int SSF = FM / WN;                   // row fragments whose squares this wave sums
-  static_assert(SFR % NW == 0 && BMF % NW == 0 && FM % WN == 0, "tile shape");
-  static_assert(NS >= 2 && NS <= 4 && (NS - 2) * LPW < 64, "stage count");
+  static_assert(WFR % NW == 0 && XFR % NW == 0 && FM % WN == 0, "tile shape");
+  constexpr int WSLOT = WFR * kFragBytes;
+  constexpr int XSLOT = XFR * kFragBytes;
+  static_assert(4 * WSLOT + 2 * XSLOT + BMF * 64 <= 160 * 1024, "LDS budget");
 
-  // One LDS array per ring slot: the compiler can then tell a read of slot s
-  // from the direct-to-LDS loads still filling the other slots, instead of
-  // waiting for all of them before every read.
-  constexpr int SLOT = SFR * kFragBytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring0[SLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring1[SLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[NS > 2 ? SLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring3[NS > 3 ? SLOT : 16];
-  __shared__ float ssbuf[BMF * 16];
-  // slot s is a literal at every call site, so this folds to one array
-  auto slot_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* { return s == 0 ? ring0 : (s == 1 ? ring1 : (s == 2 ? ring2 : ring3)); };
+  __shared__ __attribute__((aligned(1024))) uint8_t wring0[WSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t wring1[WSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t wring2[WSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t wring3[WSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t xring0[XSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t xring1[XSLOT];
+  __shared__ __attribute__((aligned(16))) float ssbuf[BMF * 16];   // sums of squares, then 1/RMS
+  auto wslot = [&](int s) __attribute__((always_inline)) -> uint8_t* {
+    return s == 0 ? wring0 : (s == 1 ? wring1 : (s == 2 ? wring2 : wring3));
+  };
+  auto xslot = [&](int s) __attribute__((always_inline)) -> uint8_t* { return s == 0 ? xring0 : xring1; };
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -92,42 +100,53 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int m0 = blockIdx.y * BMF * 16;
   const int nb0 = blockIdx.x * BNF;
-  const int64_t kfrag = (int64_t)a.kblocks * kFragBytes;   // bytes of one packed column block
+  const int64_t kfrag = (int64_t)a.kblocks * kFragBytes;
 
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(static_cast<const __bf16*>(a.x) + (size_t)m0 * a.K, (int64_t)min(BMF * 16, a.M - m0) * a.K * 2);
-  // (two named descriptors: an array of this opaque type would make the
-  // host compilation pass drop the kernel's launch stub)
   const int64_t wbytes = (int64_t)min(BNF, a.nblocks - nb0) * kfrag;
   const __amdgpu_buffer_rsrc_t wr0 = make_rsrc(static_cast<const uint8_t*>(a.wg) + nb0 * kfrag, wbytes);
   const __amdgpu_buffer_rsrc_t wr1 = make_rsrc(static_cast<const uint8_t*>(SW ? a.wu : a.wg) + nb0 * kfrag, wbytes);
 
-  // Fragments this wave loads each stage: f = wave + NW * i.  The first ALPW
-  // are x fragments (row block f), the rest W' fragments.
-  uint32_t xoff[ALPW];    // byte offset of this lane's x chunk at k-block 0
+  // x load q = wave + NW*j of a pair: rows 8*(q%2) .. +7 of row block q/2,
+  // both k-blocks; lane l brings row lr = 8*(q%2) + l/8 of the block, chunk
+  // (l%8) ^ (lr/2) of its eight 16-byte chunks (k within the pair).
+  uint32_t xoff[XPW];
+  int xk[XPW];
 #pragma unroll
-  for (int i = 0; i < ALPW; ++i) {
-    const int row = 16 * (wave + NW * i) + lrow;
-    xoff[i] = (uint32_t)(row * a.K + lgrp * 8) * 2u;
+  for (int j = 0; j < XPW; ++j) {
+    const int q = wave + NW * j;
+    const int lr = 8 * (q & 1) + (lane >> 3);
+    const int c = (lane & 7) ^ (lr >> 1);
+    xk[j] = (c >> 2) * 32 + (c & 3) * 8;
+    xoff[j] = (uint32_t)((16 * (q >> 1) + lr) * a.K + xk[j]) * 2u;
   }
-  auto issue = [&](uint8_t* base, int kb) __attribute__((always_inline)) {
-    // all-ones while in range, else zero: out-of-range offsets read as zero
-    const uint32_t xin = (uint32_t)((kb * 32 + lgrp * 8 - a.K) >> 31);
+  auto issue_x = [&](uint8_t* base, int p) __attribute__((always_inline)) {
+    const int k0 = p * 64;
+#pragma unroll
+    for (int j = 0; j < XPW; ++j) {
+      const uint32_t in = (uint32_t)((k0 + xk[j] - a.K) >> 31);   // all ones while k < K
+      const uint32_t off = ((xoff[j] + (uint32_t)k0 * 2u) & in) | (kOutOfRange & ~in);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(base + (wave + NW * j) * kFragBytes), 16, off, 0, 0,
+                                               0);
+    }
+  };
+  auto issue_w = [&](uint8_t* base, int kb) __attribute__((always_inline)) {
     const uint32_t win = (uint32_t)((kb - a.kblocks) >> 31);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
+    for (int i = 0; i < WPW; ++i) {
       const int f = wave + NW * i;
-      lds_ptr dst = (lds_ptr)(base + f * kFragBytes);
-      if (i < ALPW) {
-        const uint32_t off = ((xoff[i] + (uint32_t)kb * 64u) & xin) | (kOutOfRange & ~xin);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
-      } else {
-        const int g = f - BMF;
-        const int m = g / BNF, ni = g % BNF;
-        const uint32_t off = ((uint32_t)((ni * a.kblocks + kb) * kFragBytes + lane * 16) & win) | (kOutOfRange & ~win);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(m == 0 ? wr0 : wr1, dst, 16, off, 0, 0, 0);
-      }
+      const int m = f / BNF, ni = f % BNF;
+      const uint32_t off = ((uint32_t)((ni * a.kblocks + kb) * kFragBytes + lane * 16) & win) | (kOutOfRange & ~win);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(m == 0 ? wr0 : wr1, (lds_ptr)(base + f * kFragBytes), 16, off, 0, 0,
+                                               0);
     }
+  };
+  // LDS offset of this lane's x operand (row lrow, k-group lgrp) for k-block
+  // u of the pair and row block rb
+  auto x_at = [&](int u, int rb) __attribute__((always_inline)) -> int {
+    const int c = (u * 4 + lgrp) ^ (lrow >> 1);
+    return (2 * rb + (lrow >> 3)) * kFragBytes + (lrow & 7) * 128 + c * 16;
   };
 
   f32x4 acc[NMAT][FM][FN];
@@ -137,33 +156,21 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ss[SSF];
   f32x4 gram[SSF];
 #pragma unroll
-  for (int i = 0; i < SSF; ++i) {
-    ss[i] = 0.f;
-    gram[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int i = 0; i < SSF; ++i) gram[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Register plan: x fragments of two consecutive k-blocks (two sets), one
-  // set of W' fragments.  The MFMAs of k-block t run column by column, so the
-  // first half of the W' fragments is free by mid-step: there, after the
-  // barrier for k-block t+1, go the reads of t+1's x fragments and first W'
-  // half plus the refill of the slot t came from; t+1's second W' half is read
-  // once t's second half has been issued.  LDS latency and the barrier thus
-  // hide behind matrix work instead of stalling it.
   constexpr int NB = NMAT * FN;            // W' fragments per wave and k-block
   u32x4 av[2][FM], bv[NB];
-  auto read_a = [&](int r, const uint8_t* base) __attribute__((always_inline)) {
+  auto read_a = [&](int r, const uint8_t* base, int u) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      av[r][i] = *reinterpret_cast<const u32x4*>(base + (wm * FM + i) * kFragBytes + lane * 16);
+    for (int i = 0; i < FM; ++i) av[r][i] = *reinterpret_cast<const u32x4*>(base + x_at(u, wm * FM + i));
   };
   auto read_b = [&](int j0, int j1, const uint8_t* base) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
       const int m = j / FN, jj = j % FN;
-      bv[j] = *reinterpret_cast<const u32x4*>(base + (BMF + m * BNF + wn * FN + jj) * kFragBytes + lane * 16);
+      bv[j] = *reinterpret_cast<const u32x4*>(base + (m * BNF + wn * FN + jj) * kFragBytes + lane * 16);
     }
   };
   auto mfma_cols = [&](int r, int j0, int j1) __attribute__((always_inline)) {
@@ -175,103 +182,96 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   auto squares = [&](int r) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      if (i / SSF == wn) {
-        if (GRAM) gram[i % SSF] = mfma_chunk<__bf16>(av[r][i], av[r][i], gram[i % SSF]);
-        else ss[i % SSF] += sumsq16<__bf16>(av[r][i]);
-      }
+      if (i / SSF == wn) gram[i % SSF] = mfma_chunk<__bf16>(av[r][i], av[r][i], gram[i % SSF]);
   };
-  // k-block t (in slot s, x operands in register set r).  Memory instructions
-  // are spread between the MFMAs (scheduling groups) instead of issued in
-  // bursts.  The body has no branches, so the compiler can tell the slot being
-  // read from the slots still being filled and adds no wait of its own.
-  auto step = [&](int s, int r, int t) __attribute__((always_inline)) {
-    const uint8_t* cur = slot_ptr(s);
-    const uint8_t* next = slot_ptr((s + 1) % NS);
-    // first half: W' columns 0..NB/2 of t, while t's other W' half is read
+  // k-block t = t0 + T4 (T4 = t % 4, a compile-time constant): W' slot T4,
+  // x pair slot (T4 / 2), x registers T4 % 2; k-block t+1's operands come
+  // from W' slot (T4+1) % 4 and x pair slot ((T4+1) % 4) / 2, half (T4+1) % 2.
+  auto step = [&](auto T4c, int t) __attribute__((always_inline)) {
+    constexpr int T4 = decltype(T4c)::value;
+    constexpr int r = T4 % 2;
+    constexpr bool odd = (T4 % 2) == 1;
+    const uint8_t* wcur = wslot(T4);
+    const uint8_t* wnext = wslot((T4 + 1) % 4);
+    const uint8_t* xnext = xslot(((T4 + 1) % 4) / 2);
     __builtin_amdgcn_sched_barrier(0);
     mfma_cols(r, 0, NB / 2);
-    read_b(NB / 2, NB, cur);
+    read_b(NB / 2, NB, wcur);
 #pragma unroll
     for (int g = 0; g < NB / 2; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);       // FM MFMAs
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Every read of slot s has returned before the barrier; k-block t+1 has
-    // landed for this wave once at most the NS-2 younger ones are in flight,
-    // and the barrier extends both to every wave.
+    // k-block t+1's x pair and W' have landed for this wave once at most the
+    // loads issued after the newer of the two are in flight; the barrier
+    // extends that to every wave and retires every read of slot t.
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-    wait_vmcnt<(NS - 2) * LPW>();
+    if constexpr (odd) wait_vmcnt<2 * WPW>();
+    else wait_vmcnt<2 * WPW + XPW>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // second half: t's other W' columns and squares, while t+1's x fragments
-    // and first W' half are read and slot s is refilled with k-block t+NS
-    read_a(r ^ 1, next);
-    read_b(0, NB / 2, next);
+    read_a(r ^ 1, xnext, (T4 + 1) % 2);
+    read_b(0, NB / 2, wnext);
     mfma_cols(r, NB / 2, NB);
     squares(r);
-    issue(slot_ptr(s), t + NS);
+    if constexpr (odd) issue_x(xslot(T4 / 2), (t + 3) / 2);
+    issue_w(wslot(T4), t + 4);
 #pragma unroll
     for (int g = 0; g < FM + NB / 2; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
     }
 #pragma unroll
-    for (int g = 0; g < LPW; ++g) {
+    for (int g = 0; g < WPW + (odd ? XPW : 0); ++g) {
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);        // one global-to-LDS load
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        // two MFMAs
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  static_assert(NS == 4, "the unrolled schedule below assumes four ring slots");
-  issue(ring0, 0);
-  issue(ring1, 1);
-  issue(ring2, 2);
-  issue(ring3, 3);
-  wait_vmcnt<(NS - 1) * LPW>();
+  // prologue in the steady state's issue order (steps -4 .. -1)
+  issue_w(wring0, 0);
+  issue_x(xring0, 0);
+  issue_w(wring1, 1);
+  issue_w(wring2, 2);
+  issue_x(xring1, 1);
+  issue_w(wring3, 3);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<3 * WPW + XPW>();           // W' k-block 0 and x pair 0
   __builtin_amdgcn_s_barrier();
-  read_a(0, ring0);
-  read_b(0, NB / 2, ring0);
-  // k-blocks past the last one are zero-filled, so rounding the trip count up
-  // to whole rounds of the ring adds only zero products.
+  read_a(0, xring0, 0);
+  read_b(0, NB / 2, wring0);
   for (int t = 0; t < a.kblocks; t += 4) {
-    step(0, 0, t);
-    step(1, 1, t + 1);
-    step(2, 0, t + 2);
-    step(3, 1, t + 3);
+    step(std::integral_constant<int, 0>{}, t);
+    step(std::integral_constant<int, 1>{}, t + 1);
+    step(std::integral_constant<int, 2>{}, t + 2);
+    step(std::integral_constant<int, 3>{}, t + 3);
   }
   wait_vmcnt<0>();   // retire the zero-filled loads issued past the last k-block
 
-  // Sums of squares.  VALU form: lanes l, l^16, l^32, l^48 hold parts of
-  // row l%16.  Gram form: the diagonal of x x^T, element l%4 of the lanes
-  // whose (l%16)/4 == l/16.
 #pragma unroll
   for (int i = 0; i < SSF; ++i) {
-    if (GRAM) {
-      if ((lrow >> 2) == lgrp) {
-        const int r = lrow & 3;
-        const f32x4 gv = gram[i];
-        ssbuf[(wm * FM + wn * SSF + i) * 16 + lrow] = r == 0 ? gv[0] : (r == 1 ? gv[1] : (r == 2 ? gv[2] : gv[3]));
-      }
-    } else {
-      ss[i] += __shfl_xor(ss[i], 16);
-      ss[i] += __shfl_xor(ss[i], 32);
-      if (lgrp == 0) ssbuf[(wm * FM + wn * SSF + i) * 16 + lrow] = ss[i];
+    if ((lrow >> 2) == lgrp) {
+      const int e = lrow & 3;
+      const f32x4 gv = gram[i];
+      ssbuf[(wm * FM + wn * SSF + i) * 16 + lrow] = e == 0 ? gv[0] : (e == 1 ? gv[1] : (e == 2 ? gv[2] : gv[3]));
     }
   }
   __syncthreads();
+  // 1/RMS once per row of the tile, in place
+  if (threadIdx.x < BMF * 16) ssbuf[threadIdx.x] = inv_rms(ssbuf[threadIdx.x], (float)a.K, a.eps);
+  __syncthreads();
 
-  const float kf = (float)a.K;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&ssbuf[(wm * FM + i) * 16 + 4 * lgrp]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rl = (wm * FM + i) * 16 + 4 * lgrp + r;   // row within the tile
       const int row = m0 + rl;
-      const float inv = inv_rms(ssbuf[rl], kf, a.eps);
+      const float inv = inv4[r];
       if constexpr (Q8) {
-        // fp8 output: every lane takes part in each block maximum
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int nb = nb0 + wn * FN + j;
@@ -304,15 +304,15 @@ struct PrefillInstance {
   const char* name;
 };
 
-#define FN_PREFILL(FM, FN_, WM, WN, SW, NS, GRAM, Q8, NAME)                                                      \
-  PrefillInstance {                                                                                               \
-    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, NS, GRAM, Q8>), FM, FN_, WM, WN, NS, SW, NAME \
+#define FN_PREFILL(FM, FN_, WM, WN, SW, Q8, NAME)                                                           \
+  PrefillInstance {                                                                                          \
+    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, Q8>), FM, FN_, WM, WN, 4, SW, NAME \
   }
 
 static const PrefillInstance kPrefill[] = {
-    FN_PREFILL(4, 8, 4, 2, false, 4, true, false, "prefill_bf16_256x256_w4x2_s4"),
-    FN_PREFILL(4, 4, 4, 2, true, 4, true, false, "prefill_swiglu_bf16_256x128_w4x2_s4"),
-    FN_PREFILL(4, 4, 4, 2, true, 4, true, true, "prefill_swiglu_bf16_q8_256x128_w4x2_s4"),
+    FN_PREFILL(4, 8, 4, 2, false, false, "prefill_bf16_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, "prefill_swiglu_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, "prefill_swiglu_bf16_q8_256x128_w4x2_xl"),
 };
 
 static const PrefillInstance& pick(bool sw, bool q8 = false) { return kPrefill[q8 ? 2 : (sw ? 1 : 0)]; }
