@@ -44,8 +44,9 @@ up-cast exactly.  eps is taken as float64(float32(eps)), the exact value a
 GPU kernel receives as a float argument.
 
 The fp8-weight functions (E4M3 codes with one scale per output column) and
-the fp8 output functions at the end (E4M3 codes with one scale per 16-column
-row block) follow the readings stated in their sections.
+the fp8 output functions (E4M3 codes with one scale per 16-column row
+block) and the AdaLN functions at the end follow the readings stated in
+their sections.
 
 Pins (see tests/test_oracle.py): hand-derived worked cases, brute force on
 tiny inputs, torch's float64 rms_norm followed by a float64 matmul, the fold
@@ -329,9 +330,61 @@ def norm_proj_swiglu_fp8_q8(x, codes_gate, s_gate, codes_up, s_up, eps: float):
     return codes, s, v
 
 
+# ------------------------------------------------------ AdaLN prologue --
+# [FlashInfer #5521] ("MiniMax-H3 Fused FC1 + SwiGLU", sections "Segmented
+# Chain" and "Fused Kernel on SM120"): the diffusion model's FC1 step runs
+# RMSNorm + AdaLN, then the projection, then silu_and_mul, and the fused
+# call takes raw x, the norm weight, an AdaLN scale, an AdaLN shift and a
+# per-input index into them.  The page never writes the modulation.  The
+# reading taken here is the usual adaptive-norm modulation after the norm,
+# with the scale and shift rows of two tables [T, K] picked per row of x by
+# idx[m]:
+#
+#     h[m,k] = xhat[m,k] * (1 + scale[idx[m], k]) + shift[idx[m], k],
+#     xhat = RMSNorm_g(x),   y = h @ W,   or   out = silu(h @ W_gate) * (h @ W_up).
+#
+# The modulation is chosen at run time, so it cannot be folded into W'; the
+# gain still can.  In real arithmetic
+#     h @ W = ((x * (1 + scale_i)) @ W') / r + shift_i @ W,   W' = diag(g) W,
+# the second term a per-index bias row that depends only on the tables and
+# the unfolded W (computed once per table).
+
+
+def adaln_modulate(x, g, scale, shift, idx, eps: float) -> np.ndarray:
+    """h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx], row by row."""
+    i = np.asarray(idx, dtype=np.int64)
+    return rmsnorm(x, g, eps) * (1.0 + _f64(scale)[i]) + _f64(shift)[i]
+
+
+def adaln_norm_proj(x, g, scale, shift, idx, W, eps: float) -> np.ndarray:
+    """y = h @ W with h the AdaLN-modulated normalised x."""
+    return adaln_modulate(x, g, scale, shift, idx, eps) @ _f64(W)
+
+
+def adaln_norm_proj_swiglu(x, g, scale, shift, idx, W_gate, W_up, eps: float) -> np.ndarray:
+    """out = silu(h @ W_gate) * (h @ W_up)."""
+    h = adaln_modulate(x, g, scale, shift, idx, eps)
+    return silu(h @ _f64(W_gate)) * (h @ _f64(W_up))
+
+
+def adaln_shift_bias(shift, W) -> np.ndarray:
+    """Per-index bias rows shift @ W (unfolded W), [T, N]."""
+    return _f64(shift) @ _f64(W)
+
+
+def adaln_norm_proj_folded(x, W_folded, scale, bias, idx, eps: float) -> np.ndarray:
+    """Folded and deferred form: ((x * (1 + scale[idx])) @ W') / r + bias[idx];
+    equal to adaln_norm_proj in real arithmetic (pinned, not used by the
+    comparisons)."""
+    x = _f64(x)
+    i = np.asarray(idx, dtype=np.int64)
+    return ((x * (1.0 + _f64(scale)[i])) @ _f64(W_folded)) / rms(x, eps)[:, None] + _f64(bias)[i]
+
+
 __all__ = ["rms", "rmsnorm", "norm_proj", "silu", "norm_proj_swiglu", "fold_exact",
            "round_to_bf16", "round_to_f32", "round_to", "fold_weights", "norm_proj_folded",
            "norm_proj_swiglu_folded", "eps_as_received", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
            "quantize_e4m3_columns", "fold_weights_fp8", "norm_proj_fp8", "norm_proj_swiglu_fp8",
            "Q8_BLOCK", "quantize_e4m3_row_blocks", "dequantize_row_blocks", "norm_proj_swiglu_q8",
-           "norm_proj_swiglu_fp8_q8"]
+           "norm_proj_swiglu_fp8_q8", "adaln_modulate", "adaln_norm_proj", "adaln_norm_proj_swiglu",
+           "adaln_shift_bias", "adaln_norm_proj_folded"]

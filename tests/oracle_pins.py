@@ -434,3 +434,65 @@ def check_norm_proj_swiglu_q8(o, seed=23):
 
 
 ALL_CHECKS += [check_e4m3_row_blocks, check_norm_proj_swiglu_q8]
+
+
+# --------------------------------------------------------------------------
+# AdaLN prologue
+# --------------------------------------------------------------------------
+def check_adaln(o, seed=24):
+    """AdaLN after the norm: the hand-derived case, the reductions to the
+    plain path (zero tables; a constant scale), the folded/deferred identity
+    with the per-index bias rows, row permutation together with idx, table
+    row duplication, and brute force."""
+    gold = load_golden()["adaln"]
+    h = o.adaln_modulate(gold["x"], gold["g"], gold["scale"], gold["shift"], gold["idx"], 0.0)
+    assert np.array_equal(h, np.array(gold["h"])), h
+    y = o.adaln_norm_proj(gold["x"], gold["g"], gold["scale"], gold["shift"], gold["idx"], gold["W"], 0.0)
+    assert np.array_equal(y[:, 0], np.array(gold["y"])), y
+    out = o.adaln_norm_proj_swiglu(gold["x"], gold["g"], gold["scale"], gold["shift"], gold["idx"], gold["W"],
+                                   gold["W_up"], 0.0)
+    want = [a / (1 + math.exp(-a)) * b for a, b in zip(gold["a"], gold["b"])]
+    _close(out[:, 0], np.array(want), 1e-15, "adaln swiglu hand case")
+
+    rng = np.random.default_rng(seed)
+    M, K, N, T = 7, 24, 10, 3
+    x = rng.standard_normal((M, K))
+    g = rng.uniform(0.5, 1.5, K)
+    W = rng.standard_normal((K, N)) / 5
+    Wu = rng.standard_normal((K, N)) / 5
+    sc = rng.standard_normal((T, K)) * 0.3
+    sh = rng.standard_normal((T, K)) * 0.3
+    idx = rng.integers(0, T, M)
+    zeros = np.zeros((T, K))
+    assert np.array_equal(o.adaln_norm_proj(x, g, zeros, zeros, idx, W, 1e-6), o.norm_proj(x, g, W, 1e-6)), \
+        "zero tables give the plain path"
+    assert np.array_equal(o.adaln_norm_proj_swiglu(x, g, zeros, zeros, idx, W, Wu, 1e-6),
+                          o.norm_proj_swiglu(x, g, W, Wu, 1e-6))
+    const = np.full((T, K), 0.25)
+    _close(o.adaln_norm_proj(x, g, const, zeros, idx, W, 1e-6), 1.25 * o.norm_proj(x, g, W, 1e-6), 1e-13,
+           "constant scale")
+    Wf = g[:, None] * W
+    bias = o.adaln_shift_bias(sh, W)
+    _close(o.adaln_norm_proj_folded(x, Wf, sc, bias, idx, 1e-6), o.adaln_norm_proj(x, g, sc, sh, idx, W, 1e-6),
+           1e-12, "folded/deferred AdaLN identity")
+    perm = rng.permutation(M)
+    _close(o.adaln_norm_proj(x[perm], g, sc, sh, idx[perm], W, 1e-6),
+           o.adaln_norm_proj(x, g, sc, sh, idx, W, 1e-6)[perm], 1e-14, "row permutation with idx")
+    sc2, sh2 = np.vstack([sc, sc[1:2]]), np.vstack([sh, sh[1:2]])
+    idx2 = np.where(idx == 1, T, idx)
+    _close(o.adaln_norm_proj(x, g, sc2, sh2, idx2, W, 1e-6), o.adaln_norm_proj(x, g, sc, sh, idx, W, 1e-6), 1e-14,
+           "duplicated table row")
+    # brute force
+    xs, gs, Ws = x[:2, :5], g[:5], W[:5, :3]
+    got = o.adaln_norm_proj(xs, gs, sc[:, :5], sh[:, :5], idx[:2], Ws, 0.5)
+    for m in range(2):
+        r = math.sqrt(sum(float(v) ** 2 for v in xs[m]) / 5 + float(np.float32(0.5)))
+        for n in range(3):
+            acc = 0.0
+            for k in range(5):
+                hk = float(xs[m, k]) / r * float(gs[k]) * (1 + float(sc[idx[m], k])) + float(sh[idx[m], k])
+                acc += hk * float(Ws[k, n])
+            assert abs(got[m, n] - acc) <= 1e-12 * (abs(acc) + 1), (m, n)
+
+
+ALL_CHECKS += [check_adaln]

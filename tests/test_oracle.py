@@ -57,6 +57,15 @@ MUTANTS = {
     "q8 blocks down the columns": ("quantize_e4m3_row_blocks", lambda v, block=16: _q8_columns(v, block)),
     "q8 block of 32": ("quantize_e4m3_row_blocks", lambda v, block=16: _q8_ref(v, 32)),
     "q8 blocks across rows": ("quantize_e4m3_row_blocks", lambda v, block=16: _q8_flat(v, block)),
+    "adaln modulation before the norm": ("adaln_modulate", lambda x, g, sc, sh, idx, eps: O.rmsnorm(
+        np.asarray(x, float) * (1 + np.asarray(sc, float)[np.asarray(idx)]), g, eps) + np.asarray(sh, float)[np.asarray(idx)]),
+    "adaln scale without the one": ("adaln_modulate", lambda x, g, sc, sh, idx, eps: O.rmsnorm(x, g, eps)
+                                    * np.asarray(sc, float)[np.asarray(idx)] + np.asarray(sh, float)[np.asarray(idx)]),
+    "adaln shift inside the scale": ("adaln_modulate", lambda x, g, sc, sh, idx, eps: (O.rmsnorm(x, g, eps)
+                                     + np.asarray(sh, float)[np.asarray(idx)]) * (1 + np.asarray(sc, float)[np.asarray(idx)])),
+    "adaln index ignored": ("adaln_modulate", lambda x, g, sc, sh, idx, eps: O.rmsnorm(x, g, eps)
+                            * (1 + np.asarray(sc, float)[0]) + np.asarray(sh, float)[0]),
+    "adaln bias on the folded weights": ("adaln_shift_bias", lambda sh, W: np.asarray(sh, float) @ np.asarray(W, float) * 1.5),
     "q8 scale inverted": ("dequantize_row_blocks", lambda c, s, block=16: _deq_ref(c, 1.0 / np.asarray(s, float),
                                                                                  block)),
 }
