@@ -45,6 +45,8 @@ def parse_args(argv=None):
                         "(bf16 decode workloads only)")
     p.add_argument("--output", default="native", choices=["native", "q8"],
                    help="q8: SwiGLU output as E4M3 codes + one scale per 16-column row block (ffn_decode)")
+    p.add_argument("--prologue", default="none", choices=["none", "adaln"],
+                   help="adaln: AdaLN modulation after the norm (scale/shift tables of ADALN_T rows, per-row index)")
     p.add_argument("--no-chain", action="store_true", help="skip the unfused chain baselines")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
@@ -113,7 +115,8 @@ def pct(sorted_vals, q):
 KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": ("decode_x.hip", "fn_device.h"),
                   "qkv_decode_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_fp8": ("decode_x.hip", "fn_device.h"),
                   "decode_step_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_q8": ("decode_x.hip", "fn_device.h"),
-                  "ffn_decode_fp8_q8": ("decode_x.hip", "fn_device.h")}
+                  "ffn_decode_fp8_q8": ("decode_x.hip", "fn_device.h"), "qkv_decode_adaln": ("decode_x.hip", "fn_device.h"),
+                  "ffn_decode_adaln": ("decode_x.hip", "fn_device.h")}
 DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
 
 
@@ -145,6 +148,15 @@ def fp8_bytes(call):
     return call.mats * (call.K * call.N + 4 * call.N) + 2 * (call.M * call.K + call.M * call.N)
 
 
+ADALN_T = 4
+
+
+def adaln_extra_bytes(call):
+    """AdaLN inputs read once: the scale table [T, K] bf16, the row indices
+    [M] int32 and the bias rows [T, N] fp32 per weight matrix."""
+    return 2 * ADALN_T * call.K + 4 * call.M + 4 * ADALN_T * call.N * call.mats
+
+
 def call_bytes(call, fp8, q8):
     """Algorithmic bytes of one call: weights (bf16 W', or E4M3 codes and
     column scales) once, x once, and the output once (bf16 y, or E4M3 codes
@@ -156,7 +168,7 @@ def call_bytes(call, fp8, q8):
 
 
 # ------------------------------------------------------------ CPU oracle --
-def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False):
+def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False, adaln=False):
     """The float64 oracle as it stands, on the host cores, on a bounded sample
     of the same workload; scaled to the metric's unit."""
     import numpy as np
@@ -177,8 +189,16 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False):
         w8 = [oracle.fold_weights_fp8(inp.g, inp.W, call.dtype)]
         if call.swiglu:
             w8.append(oracle.fold_weights_fp8(inp.g, inp.W_up, call.dtype))
+    if adaln:
+        import workloads
+        sc, sh, idx = workloads.adaln_tables(ADALN_T, call.K, call.M, seed=call.seed + 100)
+        idx = idx[:rows]
     while True:
-        if q8 and fp8:
+        if adaln and call.swiglu:
+            oracle.adaln_norm_proj_swiglu(x, inp.g, sc, sh, idx, inp.W, inp.W_up, call.eps)
+        elif adaln:
+            oracle.adaln_norm_proj(x, inp.g, sc, sh, idx, inp.W, call.eps)
+        elif q8 and fp8:
             oracle.norm_proj_swiglu_fp8_q8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], call.eps)
         elif q8:
             oracle.norm_proj_swiglu_q8(x, inp.g, inp.W, inp.W_up, call.eps)
@@ -198,12 +218,12 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False):
     if metric_unit == "TFLOP/s":
         value = call.flops() / per_call / 1e12
     elif metric_unit == "GB/s":
-        value = call_bytes(call, fp8, q8) / per_call / 1e9
+        value = (call_bytes(call, fp8, q8) + (adaln_extra_bytes(call) if adaln else 0)) / per_call / 1e9
     else:
         value = per_call * 1e6
     sample = (f"{calls} oracle call(s) on x[{rows},{call.K}] (of M={call.M}) x W[{call.K},{call.N}]"
               f"{' x2 (gate, up)' if call.swiglu else ''}{' (E4M3 codes)' if fp8 else ''}"
-              f"{', E4M3 row-block output' if q8 else ''}, float64, {el:.1f} s;"
+              f"{', E4M3 row-block output' if q8 else ''}{', AdaLN prologue' if adaln else ''}, float64, {el:.1f} s;"
               f" scaled by M/{rows}")
     return {"value": round(value, 4), "unit": metric_unit, "cores": cores, "kind": "oracle",
             "sample": sample, "seconds_per_call": per_call}
@@ -247,6 +267,16 @@ def run_single(args, torch, fn, workloads):
     pus = ([Pu] + [clone(Pu) for _ in range(rot - 1)]) if call.swiglu else None
     y = torch.empty((call.M, call.N), dtype=x.dtype, device="cuda")
     eps = call.eps
+    adaln = args.prologue == "adaln"
+    if adaln:
+        sc_np, sh_np, idx_np = workloads.adaln_tables(ADALN_T, call.K, call.M, seed=call.seed + 100)
+        sc_t, sh_t = to_dev(torch, sc_np, "bf16"), to_dev(torch, sh_np, "bf16")
+        idx_t = torch.from_numpy(idx_np).cuda()
+        bg_t = fn.adaln_shift_bias(sh_t, Wg)
+        bu_t = fn.adaln_shift_bias(sh_t, Wu) if call.swiglu else None
+        proj = lambda x_, P_, e_, out=None: fn.norm_proj_adaln(x_, sc_t, idx_t, P_, bg_t, e_, out=out)  # noqa: E731
+        proj_sw = lambda x_, a_, b_, e_, out=None: fn.norm_proj_swiglu_adaln(  # noqa: E731
+            x_, sc_t, idx_t, a_, bg_t, b_, bu_t, e_, out=out)
     q8 = args.output == "q8"
     if q8:
         # SwiGLU quantised in the epilogue: E4M3 codes + row-block scales
@@ -311,7 +341,7 @@ def run_single(args, torch, fn, workloads):
 
         def chain_own(i):
             fn.rmsnorm(x, g, eps, out=xhat)
-            h = torch.matmul(xhat, ws[i % rot])
+            h = torch.matmul(xhat * (1 + sc_t[idx_t]) + sh_t[idx_t] if adaln else xhat, ws[i % rot])
             if call.swiglu:
                 fn.silu_mul(h, out=y)
                 if q8:
@@ -319,6 +349,8 @@ def run_single(args, torch, fn, workloads):
 
         def chain_torch(i):
             xn = torch.nn.functional.rms_norm(x, (call.K,), g, eps)
+            if adaln:
+                xn = xn * (1 + sc_t[idx_t]) + sh_t[idx_t]
             h = torch.matmul(xn, ws[i % rot])
             if call.swiglu:
                 torch.mul(torch.nn.functional.silu(h[:, :N]), h[:, N:], out=y)
@@ -435,7 +467,12 @@ def main(argv=None):
     if q8 and args.workload != "ffn_decode":
         print(f"bench.py: --output q8 applies to the SwiGLU workload ffn_decode, not {args.workload}", file=sys.stderr)
         return 2
-    suffix = ("_fp8" if fp8 else "") + ("_q8" if q8 else "")
+    adaln = args.prologue == "adaln"
+    if adaln and (fp8 or q8 or args.workload not in ("qkv_decode", "ffn_decode")):
+        print("bench.py: --prologue adaln applies to qkv_decode and ffn_decode with bf16 weights and output",
+              file=sys.stderr)
+        return 2
+    suffix = ("_fp8" if fp8 else "") + ("_q8" if q8 else "") + ("_adaln" if adaln else "")
 
     if args.workload == "decode_step":
         calls, r = run_decode_step(args, torch, fn, workloads)
@@ -454,9 +491,10 @@ def main(argv=None):
         per_unit = {"algorithmic_bytes_per_step": bytes_step, "flops_per_step": flops_step}
     else:
         call, inp, r = run_single(args, torch, fn, workloads)
-        bytes_call = call_bytes(call, fp8, q8)
+        bytes_call = call_bytes(call, fp8, q8) + (adaln_extra_bytes(call) if adaln else 0)
         flops_call = call.flops()
-        kernel = (fn.kernel_name_q8(call.M, call.K, call.N, fp8) if q8 else
+        kernel = (fn.kernel_name_adaln(call.M, call.K, call.N, call.swiglu) if adaln else
+                  fn.kernel_name_q8(call.M, call.K, call.N, fp8) if q8 else
                   fn.kernel_name_fp8(call.M, call.K, call.N, call.swiglu) if fp8 else
                   fn.kernel_name(call.M, call.K, call.N, call.swiglu,
                                  torch.bfloat16 if call.dtype == "bf16" else torch.float32))
@@ -488,6 +526,9 @@ def main(argv=None):
             config["weights"] = "fp8 E4M3 codes + one fp32 scale per output column"
         if q8:
             config["output"] = "fp8 E4M3 codes + one fp32 scale per 16-column row block"
+        if adaln:
+            config["prologue"] = (f"AdaLN: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx], tables of {ADALN_T} rows, "
+                                  "per-row index")
 
     out = {
         "metric": METRIC,
@@ -532,7 +573,7 @@ def main(argv=None):
         if cpu_inp is None:
             cpu_inp = workloads.make_inputs(cpu_call)
         cb = cpu_baseline(cpu_call, cpu_inp, args.cpu_seconds, unit if unit != "us/call" else "us/call", fp8=fp8,
-                          q8=q8)
+                          q8=q8, adaln=adaln)
         if args.workload == "decode_step":
             # one head call sampled; scale to the whole step by algorithmic bytes
             per_call = cb.pop("seconds_per_call")

@@ -240,6 +240,46 @@ fn_status fn_norm_proj_swiglu_fp8_q8(const void* x, const void* W8_gate, const f
 const char* fn_kernel_name_q8(int64_t M, int64_t K, int64_t N, int fp8_weights);
 
 /* ---------------------------------------------------------------------------
+ * AdaLN prologue (adaptive-norm modulation after the RMSNorm)
+ *
+ * The diffusion FC1 of [FlashInfer #5521] ("MiniMax-H3 Fused FC1 + SwiGLU",
+ * sections "Segmented Chain" and "Fused Kernel on SM120") runs RMSNorm +
+ * AdaLN before the projection, and its fused call takes raw x, the norm
+ * weight, an AdaLN scale and shift and a per-input index into them.  The
+ * page does not write the modulation; the reading taken here:
+ *   h[m][k] = RMSNorm_g(x)[m][k] * (1 + scale[idx[m]][k]) + shift[idx[m]][k]
+ *   y = h * W,  or  out = silu(h * W_gate) * (h * W_up).
+ * The modulation is picked at run time, so only the gain folds into W'
+ * (fn_fold_weights as usual); the shift reaches the output as bias rows
+ * bias[t] = shift[t] * W (fn_adaln_shift_bias, offline, unfolded W), and
+ *   y[m] = ((x[m] * (1 + scale[idx[m]])) * W') / RMS(x[m]) + bias[idx[m]],
+ * with RMS(x) of the unmodulated x.  Arithmetic: the modulated operand
+ * x + x * scale is formed in fp32 and rounded once (RNE) to bf16 for the
+ * matrix cores; sums in fp32; bf16 output rounded once.  bf16 only.
+ * scale: [T,K] bf16, 16-byte aligned.  idx: [M] int32, 4-byte aligned; an
+ * index outside [0, T) gives that row scale 0 and shift 0.  bias: [T,N]
+ * fp32, 4-byte aligned.  T >= 1 and T*K*2 < 2^31.
+ * ------------------------------------------------------------------------- */
+
+/* bias[t][n] = sum_k shift[t][k] * W[k][n] in fp32 (k in order).  shift:
+ * [T,K], W: [K,N] row-major (unfolded), both in dt; bias: [T,N] fp32,
+ * overwritten.  Offline, once per table and weight matrix.  T*N < 2^31. */
+fn_status fn_adaln_shift_bias(const void* shift, const void* W, float* bias, int64_t T, int64_t K, int64_t N,
+                              fn_dtype dt, hipStream_t stream);
+
+/* Fused RMSNorm + AdaLN + projection, one launch (bf16). */
+fn_status fn_norm_proj_adaln(const void* x, const void* scale, const int* idx, const void* W_packed, const float* bias,
+                             void* y, int64_t M, int64_t K, int64_t N, int64_t T, float eps, hipStream_t stream);
+
+/* Fused RMSNorm + AdaLN + gate/up projections + SwiGLU, one launch (bf16). */
+fn_status fn_norm_proj_swiglu_adaln(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+                                    const float* bias_gate, const void* W_up_packed, const float* bias_up, void* out,
+                                    int64_t M, int64_t K, int64_t N, int64_t T, float eps, hipStream_t stream);
+
+/* Kernel instance of the two AdaLN calls; "invalid" for bad shapes. */
+const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int swiglu);
+
+/* ---------------------------------------------------------------------------
  * Recorded steps: a sequence of fused calls replayed with one launch
  *
  * A decode step starts the norm + projection once per layer, dozens of

@@ -74,6 +74,10 @@ def load():
         "fn_norm_proj_swiglu_q8": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, f32, vp]),
         "fn_norm_proj_swiglu_fp8_q8": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp]),
         "fn_kernel_name_q8": (ctypes.c_char_p, [i64, i64, i64, i32]),
+        "fn_adaln_shift_bias": (i32, [vp, vp, vp, i64, i64, i64, i32, vp]),
+        "fn_norm_proj_adaln": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
+        "fn_norm_proj_swiglu_adaln": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
+        "fn_kernel_name_adaln": (ctypes.c_char_p, [i64, i64, i64, i32]),
         "fn_step_create": (i32, [vp, i64, ctypes.POINTER(vp)]),
         "fn_step_launch": (i32, [vp, vp]),
         "fn_step_num_kernels": (i64, [vp]),
@@ -357,6 +361,65 @@ def kernel_name_q8(M: int, K: int, N: int, fp8_weights: bool) -> str:
     return load().fn_kernel_name_q8(M, K, N, int(fp8_weights)).decode()
 
 
+# ------------------------------------------------------- AdaLN prologue --
+def adaln_shift_bias(shift, W, out=None):
+    """bias[t] = shift[t] @ W (unfolded W, fp32 sums): [T, N] float32."""
+    torch = _torch()
+    _need_cuda("shift", shift)
+    _need_cuda("W", W)
+    if shift.dim() != 2 or W.dim() != 2 or shift.shape[1] != W.shape[0] or shift.dtype != W.dtype:
+        raise ValueError(f"shift must be [T, {W.shape[0]}] of W's dtype, got {tuple(shift.shape)} {shift.dtype}")
+    T, K = shift.shape
+    N = W.shape[1]
+    bias = torch.empty((T, N), dtype=torch.float32, device=W.device) if out is None else out
+    _check(load().fn_adaln_shift_bias(shift.data_ptr(), W.data_ptr(), bias.data_ptr(), T, K, N, _dt(W.dtype),
+                                      _stream(W)))
+    return bias
+
+
+def _check_adaln(x, scale, idx, Wp: PackedWeights, bias):
+    torch = _torch()
+    _check_x(x, Wp)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("AdaLN calls take bf16 activations and weights")
+    for name, t in (("scale", scale), ("idx", idx), ("bias", bias)):
+        _need_cuda(name, t)
+    if scale.dim() != 2 or scale.shape[1] != Wp.K or scale.dtype != torch.bfloat16:
+        raise ValueError(f"scale must be [T, {Wp.K}] bf16")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (x.shape[0],):
+        raise ValueError(f"idx must be [{x.shape[0]}] int32")
+    if tuple(bias.shape) != (scale.shape[0], Wp.N) or bias.dtype != torch.float32:
+        raise ValueError(f"bias must be [{scale.shape[0]}, {Wp.N}] float32")
+
+
+def norm_proj_adaln(x, scale, idx, Wp: PackedWeights, bias, eps: float = 1e-6, out=None):
+    """y = (RMSNorm_g(x) * (1 + scale[idx]) + shift[idx]) @ W, one launch
+    (g folded into Wp, bias = adaln_shift_bias(shift, W))."""
+    _check_adaln(x, scale, idx, Wp, bias)
+    M, N = x.shape[0], Wp.N
+    y = _out(out, M, N, x)
+    _check(load().fn_norm_proj_adaln(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Wp.data.data_ptr(),
+                                     bias.data_ptr(), y.data_ptr(), M, Wp.K, N, scale.shape[0], eps, _stream(x)))
+    return y
+
+
+def norm_proj_swiglu_adaln(x, scale, idx, Wg: PackedWeights, bias_g, Wu: PackedWeights, bias_u, eps: float = 1e-6,
+                           out=None):
+    """out = silu(h @ W_gate) * (h @ W_up) with h the AdaLN-modulated norm, one launch."""
+    _check_adaln(x, scale, idx, Wg, bias_g)
+    _check_adaln(x, scale, idx, Wu, bias_u)
+    M, N = x.shape[0], Wg.N
+    y = _out(out, M, N, x)
+    _check(load().fn_norm_proj_swiglu_adaln(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Wg.data.data_ptr(),
+                                            bias_g.data_ptr(), Wu.data.data_ptr(), bias_u.data_ptr(), y.data_ptr(),
+                                            M, Wg.K, N, scale.shape[0], eps, _stream(x)))
+    return y
+
+
+def kernel_name_adaln(M: int, K: int, N: int, swiglu: bool) -> str:
+    return load().fn_kernel_name_adaln(M, K, N, int(swiglu)).decode()
+
+
 # ------------------------------------------------------- recorded steps --
 FN_CALL_NORM_PROJ, FN_CALL_NORM_PROJ_SWIGLU, FN_CALL_NORM_PROJ_FP8, FN_CALL_NORM_PROJ_SWIGLU_FP8 = 0, 1, 2, 3
 FN_CALL_NORM_PROJ_SWIGLU_Q8, FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8 = 4, 5
@@ -470,4 +533,5 @@ __all__ = ["load", "fold_weights", "norm_proj", "norm_proj_swiglu", "rmsnorm", "
            "norm_proj_fp8", "norm_proj_swiglu_fp8", "kernel_name_fp8", "Step", "FnCall", "FN_CALL_NORM_PROJ",
            "FN_CALL_NORM_PROJ_SWIGLU", "FN_CALL_NORM_PROJ_FP8", "FN_CALL_NORM_PROJ_SWIGLU_FP8",
            "FN_CALL_NORM_PROJ_SWIGLU_Q8", "FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8", "Q8_BLOCK", "norm_proj_swiglu_q8",
-           "norm_proj_swiglu_fp8_q8", "kernel_name_q8"]
+           "norm_proj_swiglu_fp8_q8", "kernel_name_q8", "adaln_shift_bias", "norm_proj_adaln",
+           "norm_proj_swiglu_adaln", "kernel_name_adaln"]

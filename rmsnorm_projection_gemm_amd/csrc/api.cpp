@@ -172,6 +172,39 @@ fn_status q8_common(const void* x, const void* wg, const float* sg, const void* 
                     plan.name);
 }
 
+// AdaLN prologue (bf16): x [M,K], scale [T,K], idx [M], packed W' (gate and
+// up for SwiGLU), bias rows [T,N] fp32, y [M,N].
+fn_status adaln_common(const void* x, const void* scale, const int* idx, const void* wg, const float* bg,
+                       const void* wu, const float* bu, void* y, int64_t M, int64_t K, int64_t N, int64_t T,
+                       float eps, hipStream_t stream, bool swiglu, bool check_only = false) {
+  g_last_error[0] = '\0';
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(M, N));
+  FN_TRY(check_eps(eps));
+  if (T < 1 || T > INT32_MAX || T * K * 2 > INT32_MAX)
+    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*2 < 2^31", (long long)T);
+  if (M == 0 || N == 0) return FN_OK;
+  if (x == nullptr || scale == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, scale or idx is NULL");
+  if (wg == nullptr || bg == nullptr) return fail(FN_ERR_NULL, "W_packed or bias is NULL");
+  if (swiglu && (wu == nullptr || bu == nullptr)) return fail(FN_ERR_NULL, "W_up_packed or bias_up is NULL");
+  if (y == nullptr) return fail(FN_ERR_NULL, "y is NULL");
+  if (!aligned(x, 16) || !aligned(scale, 16)) return fail(FN_ERR_ALIGN, "x and scale must be 16-byte aligned");
+  if (!aligned(wg, 16) || (swiglu && !aligned(wu, 16)))
+    return fail(FN_ERR_ALIGN, "packed weights must be 16-byte aligned");
+  if (!aligned(idx, 4) || !aligned(bg, 4) || (swiglu && !aligned(bu, 4)))
+    return fail(FN_ERR_ALIGN, "idx and bias must be 4-byte aligned");
+  if (!aligned(y, 16)) return fail(FN_ERR_ALIGN, "output must be 16-byte aligned");
+  const int64_t yb = M * N * 2, wb = packed_bytes(K, N, FN_BF16), bb = T * N * 4;
+  if (overlap(y, yb, x, M * K * 2) || overlap(y, yb, scale, T * K * 2) || overlap(y, yb, idx, M * 4) ||
+      overlap(y, yb, wg, wb) || overlap(y, yb, bg, bb) || (swiglu && (overlap(y, yb, wu, wb) || overlap(y, yb, bu, bb))))
+    return fail(FN_ERR_ALIAS, "output overlaps an input");
+  if (check_only) return FN_OK;
+  const fn::FusedPlan plan = fn::plan_adaln(M, N, swiglu);
+  const fn::AdalnArgs ad{scale, idx, bg, swiglu ? bu : nullptr, (int)T};
+  return hip_status(fn::launch_adaln(plan, x, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, eps, ad, stream),
+                    plan.name);
+}
+
 // One recorded call: validate (check_only) or enqueue it on `stream`.
 fn_status run_call(const fn_call& c, hipStream_t stream, bool check_only) {
   switch (c.kind) {
@@ -352,6 +385,41 @@ const char* fn_kernel_name_q8(int64_t M, int64_t K, int64_t N, int fp8_weights) 
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
   if (!fp8_weights && M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true).name;
   return fn::plan_decode_q8(fp8_weights != 0, M, N).name;
+}
+
+fn_status fn_adaln_shift_bias(const void* shift, const void* W, float* bias, int64_t T, int64_t K, int64_t N,
+                              fn_dtype dt, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!dtype_ok(dt)) return fail(FN_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(0, N));
+  if (T < 0 || T > INT32_MAX || T * K * esize(dt) > INT32_MAX || T * N > INT32_MAX)
+    return fail(FN_ERR_SHAPE, "T=%lld out of range (T*K*e and T*N must stay below 2^31)", (long long)T);
+  if (T == 0 || N == 0) return FN_OK;
+  if (shift == nullptr || W == nullptr || bias == nullptr) return fail(FN_ERR_NULL, "shift, W or bias is NULL");
+  const int64_t e = esize(dt);
+  if (!aligned(shift, (uintptr_t)e) || !aligned(W, (uintptr_t)e) || !aligned(bias, 4))
+    return fail(FN_ERR_ALIGN, "shift and W need their element alignment, bias 4 bytes");
+  if (overlap(bias, T * N * 4, shift, T * K * e) || overlap(bias, T * N * 4, W, K * N * e))
+    return fail(FN_ERR_ALIAS, "bias overlaps shift or W");
+  return hip_status(fn::launch_adaln_bias(to_dt(dt), shift, W, bias, (int)T, (int)K, (int)N, stream), "adaln_bias");
+}
+
+fn_status fn_norm_proj_adaln(const void* x, const void* scale, const int* idx, const void* W_packed, const float* bias,
+                             void* y, int64_t M, int64_t K, int64_t N, int64_t T, float eps, hipStream_t stream) {
+  return adaln_common(x, scale, idx, W_packed, bias, nullptr, nullptr, y, M, K, N, T, eps, stream, false);
+}
+
+fn_status fn_norm_proj_swiglu_adaln(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+                                    const float* bias_gate, const void* W_up_packed, const float* bias_up, void* out,
+                                    int64_t M, int64_t K, int64_t N, int64_t T, float eps, hipStream_t stream) {
+  return adaln_common(x, scale, idx, W_gate_packed, bias_gate, W_up_packed, bias_up, out, M, K, N, T, eps, stream,
+                      true);
+}
+
+const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int swiglu) {
+  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
+  return fn::plan_adaln(M, N, swiglu != 0).name;
 }
 
 fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out) {

@@ -57,7 +57,24 @@ struct DecodeXArgs {
   const float* su;   // fp8 weights: column scales of wu
   uint8_t* q;        // fp8 output: E4M3 codes [M, N] (y unused)
   float* qs;         // fp8 output: scales [M, nblocks], one per 16-column row block
+  const void* sc;    // AdaLN: scale table [T, K] (bf16)
+  const int* idx;    // AdaLN: table row of each x row [M]
+  const float* bg;   // AdaLN: bias rows shift @ W [T, N] (gate for SwiGLU)
+  const float* bu;   // AdaLN: bias rows of W_up
+  int T;             // AdaLN: table rows
 };
+
+// x * (1 + s) for the 8 bf16 values of a 16-byte chunk: fp32 x + x*s (one
+// rounding), then RNE to bf16 -- the AdaLN-modulated MFMA operand.
+__device__ inline u32x4 modulate8(u32x4 x, u32x4 s) {
+  u32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float x0 = bf16_lo(x[c]), x1 = bf16_hi(x[c]);
+    r[c] = pack_bf16x2(fmaf(x0, bf16_lo(s[c]), x0), fmaf(x1, bf16_hi(s[c]), x1));
+  }
+  return r;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_x;
 
@@ -91,8 +108,10 @@ __device__ inline void decode_e4m3x16(u32x4 w, u32x4& lo, u32x4& hi) {
 // MF: 16-row blocks of x.  NC: 16-column blocks per wave (for SwiGLU each
 // with its gate and up stream).  NWV: waves, sharing the x fragments.  U:
 // k-blocks per stage.  F8: E4M3 weights.  Q8: E4M3 output with row-block
-// scales instead of a y in x's dtype.
-template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8>
+// scales instead of a y in x's dtype.  AD: AdaLN -- each row's scale-table
+// row is staged beside x, the MFMA operand is x * (1 + scale) while the sum
+// of squares stays on x, and the epilogue adds the row's bias row.
+template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false>
 __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   constexpr int NS = 4;                    // LDS ring slots
   constexpr int D = NS - 1;                // stages in flight
@@ -101,14 +120,18 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   constexpr int XF = U * MF;               // x loads (1 KiB each) per stage
   constexpr int XPW = (XF + NWV - 1) / NWV;   // x loads each wave issues per stage
   constexpr int WLD = F8 ? U / 2 : U;      // weight loads per stream per stage (fp8: one per k-block pair)
-  constexpr int LPW = WLD * NST + XPW;     // vector-memory ops per wave per stage
+  constexpr int LPW = WLD * NST + (AD ? 2 : 1) * XPW;   // vector-memory ops per wave per stage
   // Loads q >= XF (when NWV does not divide XF) fetch nothing and write
   // zeros into the slot's padding, so every wave issues the same count.
-  constexpr int SLOT = XPW * NWV * kFragBytes;
+  constexpr int XSL = XPW * NWV * kFragBytes;   // x part of a slot
+  constexpr int SLOT = AD ? 2 * XSL : XSL;       // AdaLN: the scale rows follow
+  static_assert(!AD || (NC == 1 && !F8 && !Q8), "AdaLN: bf16 weights and output, one column block per wave");
+  constexpr bool AD_INPLACE = AD && MF > 1;    // modulate once per workgroup, in LDS
   // Epilogue through LDS (one lane per row, 16-byte stores): fp8 output
   // always, bf16 output when each wave owns one column block.
   constexpr bool STAGE = Q8 || (NC == 1 && NWV <= NS);
   static_assert(!STAGE || (NC == 1 && NWV <= NS && 16 * MF * 16 * 4 <= SLOT), "staging fits a ring slot");
+  static_assert(!AD || STAGE, "the AdaLN bias is added in the staged epilogue");
   static_assert(U % 2 == 0, "each x load moves two k-blocks of 8 rows");
   static_assert((D - 1) * LPW < 64, "vmcnt range");
   static_assert(NS * SLOT + NWV * XPW * 16 * 4 <= 160 * 1024, "LDS budget");
@@ -143,6 +166,28 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc_x(static_cast<const __bf16*>(a.x) + (size_t)m0 * a.K,
                                                 (int64_t)min(MF * 16, a.M - m0) * a.K * 2);
+  // AdaLN: this lane's bias values (its rows, its column), fetched now
+  float bias[MF][4][NMAT];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) bias[i][e][m] = 0.f;
+  if constexpr (AD) {
+    const int col = nb0 * 16 + lrow;
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + 16 * i + 4 * lgrp + e;
+        const int t = row < a.M ? a.idx[row] : -1;
+        if ((unsigned)t < (unsigned)a.T && col < a.N) {
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) bias[i][e][m] = (m ? a.bu : a.bg)[(size_t)t * a.N + col];
+        }
+      }
+  }
   // weight stream c = m * NC + j: matrix m, column block nb0 + j (reads zero past N)
   __amdgpu_buffer_rsrc_t wr[NST];
 #pragma unroll
@@ -163,6 +208,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   // row block i) whose Gram block wave q % NWV accumulates.
   uint32_t xoff[XPW];
   int xk[XPW];
+  uint32_t soff[XPW], sok[XPW];   // AdaLN: the same chunk of the row's scale-table row
 #pragma unroll
   for (int i = 0; i < XPW; ++i) {
     const int q = w + NWV * i;
@@ -171,7 +217,14 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     const int row = 16 * ((q >> 1) % MF) + lr;
     xk[i] = q < XF ? (2 * (q / (2 * MF)) + (c >> 2)) * 32 + (c & 3) * 8 : 1 << 30;   // past XF: never in range
     xoff[i] = (uint32_t)(row * a.K + (q < XF ? xk[i] : 0)) * 2u;
+    if constexpr (AD) {
+      const int t = (q < XF && m0 + row < a.M) ? a.idx[m0 + row] : -1;
+      sok[i] = (unsigned)t < (unsigned)a.T ? 0xffffffffu : 0u;   // out-of-range index: scale 0
+      soff[i] = sok[i] ? (uint32_t)(t * a.K + xk[i]) * 2u : 0u;
+    }
   }
+  __amdgpu_buffer_rsrc_t sr = xr;
+  if constexpr (AD) sr = make_rsrc_x(a.sc, (int64_t)a.T * a.K * 2);
   // LDS offset of this lane's MFMA operand (row lrow, chunk lgrp) for
   // k-block u, row block i of a stage
   auto x_at = [&](int u, int i) __attribute__((always_inline)) -> int {
@@ -194,6 +247,15 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
       const uint32_t off = ((xoff[i] + (uint32_t)k0 * 2u) & in) | (kOutOfRangeX & ~in);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_x)(base + (w + NWV * i) * kFragBytes), 16, off, 0, 0,
                                                0);
+    }
+    if constexpr (AD) {
+#pragma unroll
+      for (int i = 0; i < XPW; ++i) {
+        const uint32_t in = sok[i] & live & (uint32_t)((k0 + xk[i] - a.K) >> 31);
+        const uint32_t off = ((soff[i] + (uint32_t)k0 * 2u) & in) | (kOutOfRangeX & ~in);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_x)(base + XSL + (w + NWV * i) * kFragBytes), 16, off,
+                                                 0, 0, 0);
+      }
     }
   };
   u32x4 wv[NS][WLD][NST];
@@ -225,17 +287,42 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     // and retires every wave's reads of the slot refilled below.
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt_x<(D - 1) * LPW>();
+    uint8_t* base = slot_ptr(s);
+    if constexpr (AD_INPLACE) {
+      // AdaLN, several row blocks: each wave modulates the chunks it loaded
+      // itself (its loads have landed), x * (1 + scale) over the scale rows
+      // in place, so each chunk is modulated once per workgroup rather than
+      // once per wave; the barrier then publishes them.  x stays raw for the
+      // sums of squares.
+#pragma unroll
+      for (int j = 0; j < XPW; ++j) {
+        if (w + NWV * j < XF) {
+          const int o = (w + NWV * j) * kFragBytes + lane * 16;
+          u32x4* sp = reinterpret_cast<u32x4*>(base + XSL + o);
+          *sp = modulate8(*reinterpret_cast<const u32x4*>(base + o), *sp);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* base = slot_ptr(s);
     u32x4 xv[U][MF];
     u32x4 xg[XPW];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < MF; ++i) xv[u][i] = *reinterpret_cast<const u32x4*>(base + x_at(u, i));
+      for (int i = 0; i < MF; ++i) xv[u][i] = *reinterpret_cast<const u32x4*>(base + (AD_INPLACE ? XSL : 0) + x_at(u, i));
 #pragma unroll
     for (int j = 0; j < XPW; ++j) xg[j] = *reinterpret_cast<const u32x4*>(base + frag_at(w + NWV * j));
+    // AdaLN, one row block: the few operand chunks are modulated in
+    // registers, after the next stage's loads are issued
+    u32x4 sv[AD && !AD_INPLACE ? U : 1][AD && !AD_INPLACE ? MF : 1];
+    if constexpr (AD && !AD_INPLACE) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < MF; ++i) sv[u][i] = *reinterpret_cast<const u32x4*>(base + XSL + x_at(u, i));
+    }
     __builtin_amdgcn_sched_barrier(0);
     issue_w((s + D) % NS, st + D);
     issue_x(slot_ptr((s + D) % NS), st + D);
@@ -256,9 +343,12 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < MF; ++i)
+      for (int i = 0; i < MF; ++i) {
+        u32x4 xa = xv[u][i];
+        if constexpr (AD && !AD_INPLACE) xa = modulate8(xa, sv[u][AD && !AD_INPLACE ? i : 0]);
 #pragma unroll
-        for (int c = 0; c < NST; ++c) acc[c][i] = mfma_chunk<__bf16>(xv[u][i], bw[u][c], acc[c][i]);
+        for (int c = 0; c < NST; ++c) acc[c][i] = mfma_chunk<__bf16>(xa, bw[u][c], acc[c][i]);
+      }
 #pragma unroll
     for (int j = 0; j < XPW; ++j) gram[j] = mfma_chunk<__bf16>(xg[j], xg[j], gram[j]);
   };
@@ -318,7 +408,10 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
         const float iu = F8 && SW ? scol[NC + j] * inv : inv;
         if constexpr (STAGE) {
           // staged in this wave's (now idle) ring slot as [row][16 columns]
-          const float val = SW ? silu_times(acc[j][i][e] * ig, acc[NC + j][i][e] * iu) : acc[j][i][e] * ig;
+          const float ga = AD ? fmaf(acc[j][i][e], ig, bias[i][e][0]) : acc[j][i][e] * ig;
+          const float val = SW ? silu_times(ga, AD ? fmaf(acc[NC + j][i][e], iu, bias[i][e][NMAT - 1])
+                                                   : acc[NC + j][i][e] * iu)
+                               : ga;
           reinterpret_cast<float*>(slot_ptr(w))[(16 * i + rr) * 16 + lrow] = val;
         } else if (row < a.M && col_ok) {
           const float val = SW ? silu_times(acc[j][i][e] * ig, acc[NC + j][i][e] * iu) : acc[j][i][e] * ig;
@@ -394,6 +487,11 @@ struct DecodeXInstance {
   DecodeXInstance {                                                                                     \
     reinterpret_cast<const void*>(&decode_x_kernel<MF, NC, NWV, SW, U, F8, Q8>), MF, NC, NWV, U, SW, F8, Q8, NAME \
   }
+#define FN_DECODE_XA(MF, NWV, SW, U, NAME)                                                                      \
+  DecodeXInstance {                                                                                            \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, SW, U, false, false, true>), MF, 1, NWV, U, SW, false, \
+        false, NAME                                                                                            \
+  }
 #define FN_DECODE_X(MF, NC, NWV, SW, U, NAME) FN_DECODE_XI(MF, NC, NWV, SW, U, false, false, NAME)
 #define FN_DECODE_X8(MF, NC, NWV, SW, U, NAME) FN_DECODE_XI(MF, NC, NWV, SW, U, true, false, NAME)
 
@@ -403,12 +501,18 @@ struct DecodeXInstance {
 inline hipError_t launch_decode_x_instance(const DecodeXInstance& d, const void* x, const void* wg, const void* wu,
                                            void* y, int M, int K, int N, float eps, hipStream_t stream,
                                            const float* sg = nullptr, const float* su = nullptr,
-                                           uint8_t* q = nullptr, float* qs = nullptr) {
+                                           uint8_t* q = nullptr, float* qs = nullptr,
+                                           const AdalnArgs* ad = nullptr) {
   DecodeXArgs a;
   a.sg = sg;
   a.su = su;
   a.q = q;
   a.qs = qs;
+  a.sc = ad ? ad->scale : nullptr;
+  a.idx = ad ? ad->idx : nullptr;
+  a.bg = ad ? ad->bias_g : nullptr;
+  a.bu = ad ? ad->bias_u : nullptr;
+  a.T = ad ? ad->T : 0;
   a.x = x;
   a.wg = wg;
   a.wu = wu;
@@ -501,6 +605,27 @@ hipError_t launch_decode_x(DType dt, const FusedPlan& p, const void* x, const vo
 FusedPlan plan_fp8(int64_t M, int64_t K, int64_t N, bool swiglu) {
   (void)K;
   return plan_of(find_instance(kDecodeF8, M <= 16 ? 1 : (M <= 32 ? 2 : 4), swiglu), 3, M, N);
+}
+
+// AdaLN prologue (bf16): rows up to 64 per workgroup, more tile over grid.y.
+static const DecodeXInstance kDecodeAd[] = {
+    FN_DECODE_XA(1, 3, false, 2, "decode_adaln_bf16_m16_xlds_w3_u2"),
+    FN_DECODE_XA(2, 3, false, 2, "decode_adaln_bf16_m32_xlds_w3_u2"),
+    FN_DECODE_XA(4, 3, false, 2, "decode_adaln_bf16_m64_xlds_w3_u2"),
+    FN_DECODE_XA(1, 3, true, 2, "decode_swiglu_adaln_bf16_m16_xlds_w3_u2"),
+    FN_DECODE_XA(2, 3, true, 2, "decode_swiglu_adaln_bf16_m32_xlds_w3_u2"),
+    FN_DECODE_XA(4, 3, true, 2, "decode_swiglu_adaln_bf16_m64_xlds_w3_u2"),
+};
+
+FusedPlan plan_adaln(int64_t M, int64_t N, bool swiglu) {
+  return plan_of(find_instance(kDecodeAd, M <= 16 ? 1 : (M <= 32 ? 2 : 4), swiglu), 6, M, N);
+}
+
+hipError_t launch_adaln(const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y, int M, int K,
+                        int N, float eps, const AdalnArgs& ad, hipStream_t stream) {
+  const DecodeXInstance* d = find_instance(kDecodeAd, p.mf, wu != nullptr);
+  if (d == nullptr) return hipErrorInvalidValue;
+  return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream, nullptr, nullptr, nullptr, nullptr, &ad);
 }
 
 // SwiGLU with fp8 output, rows up to 64 (bf16 weights; larger M goes to the

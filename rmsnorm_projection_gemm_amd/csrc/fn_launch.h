@@ -15,7 +15,8 @@ inline int k_per_block(DType t) { return t == DType::F32 ? 16 : 32; }   // KB of
 struct FusedPlan {
   int kind;           // 0 = decode (<= 16 rows, or fp32), 1 = prefill (tiled), 2 = decode with x in LDS,
                       // 3 = fp8 weights (x in LDS, rows tiled over grid.y),
-                      // 4 = SwiGLU with fp8 output (x in LDS), 5 = the same on the prefill kernel
+                      // 4 = SwiGLU with fp8 output (x in LDS), 5 = the same on the prefill kernel,
+                      // 6 = AdaLN prologue (x and scale rows in LDS)
   int mf;             // 16-row fragments per workgroup (decode)
   int nf;             // 16-column fragments per workgroup (decode)
   int waves;          // waves per workgroup
@@ -59,6 +60,22 @@ FusedPlan plan_decode_q8(bool f8_weights, int64_t M, int64_t N);
 hipError_t launch_decode_q8(bool f8_weights, const FusedPlan& plan, const void* x, const void* wg,
                             const float* sg, const void* wu, const float* su, uint8_t* q, float* qs,
                             int M, int K, int N, float eps, hipStream_t stream);
+
+// AdaLN prologue: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx] before
+// the projection; the gain is folded into W', the shift enters as bias rows
+// shift @ W ([T, N], fp32).
+struct AdalnArgs {
+  const void* scale;     // [T, K] bf16
+  const int* idx;        // [M] table row of each x row
+  const float* bias_g;   // [T, N]
+  const float* bias_u;   // [T, N], SwiGLU only
+  int T;
+};
+FusedPlan plan_adaln(int64_t M, int64_t N, bool swiglu);
+hipError_t launch_adaln(const FusedPlan& plan, const void* x, const void* wg, const void* wu, void* y, int M,
+                        int K, int N, float eps, const AdalnArgs& ad, hipStream_t stream);
+hipError_t launch_adaln_bias(DType dt, const void* shift, const void* W, float* bias, int T, int K, int N,
+                             hipStream_t stream);
 
 hipError_t launch_fused(DType dt, const FusedPlan& plan, const void* x,
                         const void* w_gate, const void* w_up, void* y,

@@ -293,3 +293,46 @@ def test_q8_kernel_names(lib):
     assert lib.fn_kernel_name_q8(65, 4096, 11008, 0).decode().startswith("prefill_swiglu_bf16_q8")
     assert lib.fn_kernel_name_q8(4096, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_q8_m64")
     assert lib.fn_kernel_name_q8(0, 4096, 16, 0) == b"invalid"
+
+
+def _ad(lib, x=0x1000, sc=0x10000, idx=0x18000, w=0x20000, b=0x30000, y=0x40000, M=4, K=16, N=16, T=2, eps=1e-6):
+    return lib.fn_norm_proj_adaln(x, sc, idx, w, b, y, M, K, N, T, eps, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(x=None), NULL, "x, scale or idx"),
+    (dict(sc=None), NULL, "x, scale or idx"),
+    (dict(idx=None), NULL, "x, scale or idx"),
+    (dict(w=None), NULL, "W_packed or bias"),
+    (dict(b=None), NULL, "W_packed or bias"),
+    (dict(y=None), NULL, "y is NULL"),
+    (dict(T=0), SHAPE, "T=0"),
+    (dict(T=1 << 27, K=16), SHAPE, "T="),
+    (dict(K=12), SHAPE, "multiple of 8"),
+    (dict(sc=0x10008), ALIGN, "scale"),
+    (dict(idx=0x18002), ALIGN, "idx and bias"),
+    (dict(b=0x30002), ALIGN, "idx and bias"),
+    (dict(eps=-1.0), EPS, "eps"),
+    (dict(y=0x18000), ALIAS, "overlaps"),
+    (dict(y=0x30000), ALIAS, "overlaps"),
+])
+def test_norm_proj_adaln_rejects(lib, kwargs, status, needle):
+    assert _ad(lib, **kwargs) == status
+    assert needle in lib.fn_last_error().decode()
+
+
+def test_adaln_swiglu_bias_and_names(lib):
+    sw = lib.fn_norm_proj_swiglu_adaln
+    assert sw(0x1000, 0x10000, 0x18000, 0x20000, 0x30000, None, 0x31000, 0x40000, 4, 16, 16, 2, 1e-6, None) == NULL
+    assert sw(0x1000, 0x10000, 0x18000, 0x20000, 0x30000, 0x21000, None, 0x40000, 4, 16, 16, 2, 1e-6, None) == NULL
+    assert sw(None, None, None, None, None, None, None, None, 0, 16, 16, 2, 1e-6, None) == OK
+    f = lib.fn_adaln_shift_bias
+    assert f(0x1000, 0x2000, None, 2, 16, 16, BF16, None) == NULL
+    assert f(0x1001, 0x2000, 0x3000, 2, 16, 16, BF16, None) == ALIGN
+    assert f(0x1000, 0x2000, 0x1000, 2, 16, 16, BF16, None) == ALIAS
+    assert f(0x1000, 0x2000, 0x3000, 2, 16, 16, 7, None) == DTYPE
+    assert f(None, None, None, 0, 16, 16, BF16, None) == OK
+    assert lib.fn_kernel_name_adaln(16, 4096, 11008, 1).decode() == "decode_swiglu_adaln_bf16_m16_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln(64, 4096, 11008, 0).decode() == "decode_adaln_bf16_m64_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln(1000, 4096, 11008, 0).decode() == "decode_adaln_bf16_m64_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln(0, 4096, 16, 0) == b"invalid"

@@ -180,6 +180,17 @@ def make_inputs_device(call: Call, device="cuda"):
     return x.to(tdt), g.to(tdt), W, W_up
 
 
+def adaln_tables(T: int, K: int, M: int, seed: int, dtype: str = "bf16"):
+    """AdaLN inputs of the same family: scale and shift tables [T, K] drawn
+    N(0, 0.3^2) and rounded to the storage dtype, and a table row per x row
+    (uniform in [0, T)).  Returns (scale, shift, idx int32)."""
+    rng = np.random.default_rng(seed)
+    scale = _to_storage(rng.standard_normal((T, K), dtype=np.float32) * np.float32(0.3), dtype)
+    shift = _to_storage(rng.standard_normal((T, K), dtype=np.float32) * np.float32(0.3), dtype)
+    idx = rng.integers(0, T, M).astype(np.int32)
+    return scale, shift, idx
+
+
 def sample_indices(n: int, count: int, seed: int) -> np.ndarray:
     """Seeded sorted subset of range(n), always including the first and last index."""
     if count >= n:
@@ -191,4 +202,4 @@ def sample_indices(n: int, count: int, seed: int) -> np.ndarray:
 
 __all__ = ["Call", "Inputs", "EPS", "TINY", "QKV_DECODE", "FFN_DECODE", "PREFILL_QKV",
            "WORKLOADS", "decode_step_calls", "make_inputs", "make_inputs_device", "random_inputs", "make_x",
-           "sample_indices", "DECODE_STEP_LAYERS", "DECODE_STEP_M"]
+           "sample_indices", "DECODE_STEP_LAYERS", "DECODE_STEP_M", "adaln_tables"]
