@@ -47,7 +47,8 @@ def parse_args(argv=None):
                    help="q8: SwiGLU output as E4M3 codes + one scale per 16-column row block (ffn_decode)")
     p.add_argument("--prologue", default="none", choices=["none", "adaln"],
                    help="adaln: AdaLN modulation after the norm (scale/shift tables of ADALN_T rows, per-row index)")
-    p.add_argument("--no-chain", action="store_true", help="skip the unfused chain baselines")
+    p.add_argument("--no-chain", action="store_true",
+                   help="skip the comparison runs (unfused chains; bf16 weights beside fp8)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     p.add_argument("--hot", action="store_true", help="time a single weight buffer only (no rotation)")
@@ -307,7 +308,7 @@ def run_single(args, torch, fn, workloads):
         result["graph_ms"] = time_region(torch, lambda _: step.launch(), args.steps, args.warmup) / TINY_STEP_CALLS
         torch.cuda.synchronize()
         step.close()
-    if fp8:
+    if fp8 and not args.no_chain:
         # the same call with bf16 folded weights, same rotation rule, for comparison
         del pgs, pus
         Bg = fn.fold_weights(g, Wg)
