@@ -111,9 +111,9 @@ __device__ inline void decode_e4m3x16(u32x4 w, u32x4& lo, u32x4& hi) {
 // scales instead of a y in x's dtype.  AD: AdaLN -- each row's scale-table
 // row is staged beside x, the MFMA operand is x * (1 + scale) while the sum
 // of squares stays on x, and the epilogue adds the row's bias row.
-template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false>
+template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false, int NS = 4>
 __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
-  constexpr int NS = 4;                    // LDS ring slots
+  static_assert(NS >= 3 && NS <= 6, "LDS ring slots");
   constexpr int D = NS - 1;                // stages in flight
   constexpr int NMAT = SW ? 2 : 1;
   constexpr int NST = NMAT * NC;           // weight streams per wave
@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   constexpr int WLD = F8 ? U / 2 : U;      // weight loads per stream per stage (fp8: one per k-block pair)
   constexpr int LPW = WLD * NST + (AD ? 2 : 1) * XPW;   // vector-memory ops per wave per stage
   // Loads q >= XF (when NWV does not divide XF) fetch nothing and write
-  // zeros into the slot's padding, so every wave issues the same count.
+  // zeros into the slot's padding, so every wave issues the same count
+  // (measured: skipping them instead is no faster).
   constexpr int XSL = XPW * NWV * kFragBytes;   // x part of a slot
   constexpr int SLOT = AD ? 2 * XSL : XSL;       // AdaLN: the scale rows follow
   static_assert(!AD || (NC == 1 && !F8 && !Q8), "AdaLN: bf16 weights and output, one column block per wave");
@@ -139,11 +140,13 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[SLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring3[SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[NS > 3 ? SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring4[NS > 4 ? SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring5[NS > 5 ? SLOT : 16];
   __shared__ float ssp[NWV][XPW][16];      // Gram diagonals
   __shared__ __attribute__((aligned(16))) float inv_s[MF * 16];   // 1/RMS per row
   auto slot_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
-    return s == 0 ? ring0 : (s == 1 ? ring1 : (s == 2 ? ring2 : ring3));
+    return s == 0 ? ring0 : (s == 1 ? ring1 : (s == 2 ? ring2 : (s == 3 ? ring3 : (s == 4 ? ring4 : ring5))));
   };
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -361,10 +364,8 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   }
   // whole rounds of the ring; stages past the last read as zero
   for (int st = 0; st < a.stages; st += NS) {
-    step(0, st);
-    step(1, st + 1);
-    step(2, st + 2);
-    step(3, st + 3);
+#pragma unroll
+    for (int r = 0; r < NS; ++r) step(r, st + r);
   }
   wait_vmcnt_x<0>();
 
@@ -539,7 +540,9 @@ inline hipError_t launch_decode_x_instance(const DecodeXInstance& d, const void*
 // workgroups) measured 10-15% slower, two waves slower still; wider waves,
 // deeper stages and k-splits inside the workgroup did not help.
 static const DecodeXInstance kDecodeX[] = {
-    FN_DECODE_X(2, 1, 3, false, 2, "decode_bf16_m32_xlds_w3_u2"),
+    // 32-row projection: a 5-slot ring (four stages in flight) measured 7% faster
+    DecodeXInstance{reinterpret_cast<const void*>(&decode_x_kernel<2, 1, 3, false, 2, false, false, false, 5>), 2, 1, 3,
+                    2, false, false, false, "decode_bf16_m32_xlds_w3_u2_s5"},
     FN_DECODE_X(4, 1, 3, false, 2, "decode_bf16_m64_xlds_w3_u2"),
     FN_DECODE_X(2, 1, 3, true, 2, "decode_swiglu_bf16_m32_xlds_w3_u2"),
     FN_DECODE_X(4, 1, 3, true, 2, "decode_swiglu_bf16_m64_xlds_w3_u2"),
