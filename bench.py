@@ -117,7 +117,7 @@ KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": (
                   "qkv_decode_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_fp8": ("decode_x.hip", "fn_device.h"),
                   "decode_step_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_q8": ("decode_x.hip", "fn_device.h"),
                   "ffn_decode_fp8_q8": ("decode_x.hip", "fn_device.h"), "qkv_decode_adaln": ("decode_x.hip", "fn_device.h"),
-                  "ffn_decode_adaln": ("decode_x.hip", "fn_device.h")}
+                  "ffn_decode_adaln": ("decode_x.hip", "fn_device.h"), "prefill_qkv_adaln": ("prefill.hip", "fn_device.h")}
 DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
 
 
@@ -469,9 +469,9 @@ def main(argv=None):
         print(f"bench.py: --output q8 applies to the SwiGLU workload ffn_decode, not {args.workload}", file=sys.stderr)
         return 2
     adaln = args.prologue == "adaln"
-    if adaln and (fp8 or q8 or args.workload not in ("qkv_decode", "ffn_decode")):
-        print("bench.py: --prologue adaln applies to qkv_decode and ffn_decode with bf16 weights and output",
-              file=sys.stderr)
+    if adaln and (fp8 or q8 or args.workload not in ("qkv_decode", "ffn_decode", "prefill_qkv")):
+        print("bench.py: --prologue adaln applies to qkv_decode, ffn_decode and prefill_qkv with bf16 weights and "
+              "output", file=sys.stderr)
         return 2
     suffix = ("_fp8" if fp8 else "") + ("_q8" if q8 else "") + ("_adaln" if adaln else "")
 
@@ -494,7 +494,7 @@ def main(argv=None):
         call, inp, r = run_single(args, torch, fn, workloads)
         bytes_call = call_bytes(call, fp8, q8) + (adaln_extra_bytes(call) if adaln else 0)
         flops_call = call.flops()
-        kernel = (fn.kernel_name_adaln(call.M, call.K, call.N, call.swiglu) if adaln else
+        kernel = (fn.kernel_name_adaln(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln else
                   fn.kernel_name_q8(call.M, call.K, call.N, fp8) if q8 else
                   fn.kernel_name_fp8(call.M, call.K, call.N, call.swiglu) if fp8 else
                   fn.kernel_name(call.M, call.K, call.N, call.swiglu,

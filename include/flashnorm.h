@@ -256,6 +256,9 @@ const char* fn_kernel_name_q8(int64_t M, int64_t K, int64_t N, int fp8_weights);
  * with RMS(x) of the unmodulated x.  Arithmetic: the modulated operand
  * x + x * scale is formed in fp32 and rounded once (RNE) to bf16 for the
  * matrix cores; sums in fp32; bf16 output rounded once.  bf16 only.
+ * Instances: the LDS-shared-x decode kernel up to 64 rows; above, the
+ * prefill kernel when T <= 63 (the whole table slice is staged), else the
+ * decode kernel tiled over rows (each 64-row tile streams W' again).
  * scale: [T,K] bf16, 16-byte aligned.  idx: [M] int32, 4-byte aligned; an
  * index outside [0, T) gives that row scale 0 and shift 0.  bias: [T,N]
  * fp32, 4-byte aligned.  T >= 1 and T*K*2 < 2^31.
@@ -276,8 +279,10 @@ fn_status fn_norm_proj_swiglu_adaln(const void* x, const void* scale, const int*
                                     const float* bias_gate, const void* W_up_packed, const float* bias_up, void* out,
                                     int64_t M, int64_t K, int64_t N, int64_t T, float eps, hipStream_t stream);
 
-/* Kernel instance of the two AdaLN calls; "invalid" for bad shapes. */
-const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int swiglu);
+/* Kernel instance of the two AdaLN calls (the prefill kernel above 64 rows
+ * when T <= 63, else the decode kernel tiled over rows); "invalid" for bad
+ * shapes. */
+const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu);
 
 /* ---------------------------------------------------------------------------
  * Recorded steps: a sequence of fused calls replayed with one launch

@@ -77,7 +77,7 @@ def load():
         "fn_adaln_shift_bias": (i32, [vp, vp, vp, i64, i64, i64, i32, vp]),
         "fn_norm_proj_adaln": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
         "fn_norm_proj_swiglu_adaln": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
-        "fn_kernel_name_adaln": (ctypes.c_char_p, [i64, i64, i64, i32]),
+        "fn_kernel_name_adaln": (ctypes.c_char_p, [i64, i64, i64, i64, i32]),
         "fn_step_create": (i32, [vp, i64, ctypes.POINTER(vp)]),
         "fn_step_launch": (i32, [vp, vp]),
         "fn_step_num_kernels": (i64, [vp]),
@@ -416,8 +416,8 @@ def norm_proj_swiglu_adaln(x, scale, idx, Wg: PackedWeights, bias_g, Wu: PackedW
     return y
 
 
-def kernel_name_adaln(M: int, K: int, N: int, swiglu: bool) -> str:
-    return load().fn_kernel_name_adaln(M, K, N, int(swiglu)).decode()
+def kernel_name_adaln(M: int, K: int, N: int, T: int, swiglu: bool) -> str:
+    return load().fn_kernel_name_adaln(M, K, N, T, int(swiglu)).decode()
 
 
 # ------------------------------------------------------- recorded steps --

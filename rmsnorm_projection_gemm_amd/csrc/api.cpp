@@ -199,8 +199,14 @@ fn_status adaln_common(const void* x, const void* scale, const int* idx, const v
       overlap(y, yb, wg, wb) || overlap(y, yb, bg, bb) || (swiglu && (overlap(y, yb, wu, wb) || overlap(y, yb, bu, bb))))
     return fail(FN_ERR_ALIAS, "output overlaps an input");
   if (check_only) return FN_OK;
-  const fn::FusedPlan plan = fn::plan_adaln(M, N, swiglu);
   const fn::AdalnArgs ad{scale, idx, bg, swiglu ? bu : nullptr, (int)T};
+  if (M > 64 && fn::prefill_adaln_fits(T)) {
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, true);
+    return hip_status(fn::launch_prefill(fn::DType::BF16, plan, x, wg, swiglu ? wu : nullptr, y, (int)M, (int)K,
+                                         (int)N, eps, stream, nullptr, nullptr, &ad),
+                      plan.name);
+  }
+  const fn::FusedPlan plan = fn::plan_adaln(M, N, swiglu);
   return hip_status(fn::launch_adaln(plan, x, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, eps, ad, stream),
                     plan.name);
 }
@@ -417,8 +423,9 @@ fn_status fn_norm_proj_swiglu_adaln(const void* x, const void* scale, const int*
                       true);
 }
 
-const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int swiglu) {
-  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
+const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
+  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
+  if (M > 64 && fn::prefill_adaln_fits(T)) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, true).name;
   return fn::plan_adaln(M, N, swiglu != 0).name;
 }
 

@@ -64,17 +64,6 @@ struct DecodeXArgs {
   int T;             // AdaLN: table rows
 };
 
-// x * (1 + s) for the 8 bf16 values of a 16-byte chunk: fp32 x + x*s (one
-// rounding), then RNE to bf16 -- the AdaLN-modulated MFMA operand.
-__device__ inline u32x4 modulate8(u32x4 x, u32x4 s) {
-  u32x4 r;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float x0 = bf16_lo(x[c]), x1 = bf16_hi(x[c]);
-    r[c] = pack_bf16x2(fmaf(x0, bf16_lo(s[c]), x0), fmaf(x1, bf16_hi(s[c]), x1));
-  }
-  return r;
-}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_x;
 

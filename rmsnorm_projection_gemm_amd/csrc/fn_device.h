@@ -104,6 +104,18 @@ template <> __device__ inline f32x4 mfma_chunk<float>(u32x4 a, u32x4 b, f32x4 ac
 // expf and a correctly rounded division -- a few fp32 ulps, far below the
 // bf16 (or E4M3) rounding that follows, for a fraction of the instructions.
 // Large negative a: e^-a overflows to inf, rcp(inf) = 0, result -0 or 0.
+// x * (1 + s) for the 8 bf16 values of a 16-byte chunk: fp32 x + x*s (one
+// rounding), then RNE to bf16 -- the AdaLN-modulated MFMA operand.
+__device__ inline u32x4 modulate8(u32x4 x, u32x4 s) {
+  u32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float x0 = bf16_lo(x[c]), x1 = bf16_hi(x[c]);
+    r[c] = pack_bf16x2(fmaf(x0, bf16_lo(s[c]), x0), fmaf(x1, bf16_hi(s[c]), x1));
+  }
+  return r;
+}
+
 __device__ inline float silu_times(float a, float b) {
   const float e = __builtin_amdgcn_exp2f(a * -1.44269504088896341f);
   return a * __builtin_amdgcn_rcpf(1.0f + e) * b;

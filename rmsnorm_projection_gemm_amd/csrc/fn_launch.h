@@ -16,7 +16,7 @@ struct FusedPlan {
   int kind;           // 0 = decode (<= 16 rows, or fp32), 1 = prefill (tiled), 2 = decode with x in LDS,
                       // 3 = fp8 weights (x in LDS, rows tiled over grid.y),
                       // 4 = SwiGLU with fp8 output (x in LDS), 5 = the same on the prefill kernel,
-                      // 6 = AdaLN prologue (x and scale rows in LDS)
+                      // 6 = AdaLN prologue (x and scale rows in LDS), 7 = AdaLN on the prefill kernel
   int mf;             // 16-row fragments per workgroup (decode)
   int nf;             // 16-column fragments per workgroup (decode)
   int waves;          // waves per workgroup
@@ -36,11 +36,25 @@ hipError_t launch_decode_x(DType dt, const FusedPlan& plan, const void* x, const
                            const void* w_up, void* y, int M, int K, int N, float eps,
                            hipStream_t stream);
 
+// AdaLN prologue: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx] before
+// the projection; the gain is folded into W', the shift enters as bias rows
+// shift @ W ([T, N], fp32).
+struct AdalnArgs {
+  const void* scale;     // [T, K] bf16
+  const int* idx;        // [M] table row of each x row
+  const float* bias_g;   // [T, N]
+  const float* bias_u;   // [T, N], SwiGLU only
+  int T;
+};
+
 // q8: SwiGLU with fp8 output (codes q, row-block scales qs; y unused).
-FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8 = false);
+// ad: AdaLN prologue (tables of at most 63 rows, prefill_adaln_fits).
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8 = false, bool ad = false);
 hipError_t launch_prefill(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
                           const void* w_up, void* y, int M, int K, int N, float eps,
-                          hipStream_t stream, uint8_t* q = nullptr, float* qs = nullptr);
+                          hipStream_t stream, uint8_t* q = nullptr, float* qs = nullptr,
+                          const AdalnArgs* ad = nullptr);
+bool prefill_adaln_fits(int64_t T);
 
 hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
                        int K, int N, hipStream_t stream);
@@ -61,16 +75,6 @@ hipError_t launch_decode_q8(bool f8_weights, const FusedPlan& plan, const void* 
                             const float* sg, const void* wu, const float* su, uint8_t* q, float* qs,
                             int M, int K, int N, float eps, hipStream_t stream);
 
-// AdaLN prologue: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx] before
-// the projection; the gain is folded into W', the shift enters as bias rows
-// shift @ W ([T, N], fp32).
-struct AdalnArgs {
-  const void* scale;     // [T, K] bf16
-  const int* idx;        // [M] table row of each x row
-  const float* bias_g;   // [T, N]
-  const float* bias_u;   // [T, N], SwiGLU only
-  int T;
-};
 FusedPlan plan_adaln(int64_t M, int64_t N, bool swiglu);
 hipError_t launch_adaln(const FusedPlan& plan, const void* x, const void* wg, const void* wu, void* y, int M,
                         int K, int N, float eps, const AdalnArgs& ad, hipStream_t stream);

@@ -47,6 +47,11 @@ struct PrefillArgs {
   float eps;
   uint8_t* q;        // fp8 output: E4M3 codes [M, N] (y unused)
   float* qs;         // fp8 output: scales [M, nblocks], one per 16-column row block
+  const void* sc;    // AdaLN: scale table [T, K] (bf16), T < 8 * waves
+  const int* idx;    // AdaLN: table row of each x row [M]
+  const float* bg;   // AdaLN: bias rows [T, N] (gate for SwiGLU)
+  const float* bu;   // AdaLN: bias rows of W_up
+  int T;
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -66,7 +71,14 @@ __device__ inline void wait_vmcnt() {
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int FM, int FN, int WM, int WN, bool SW, bool Q8>
+// AD: AdaLN.  The whole scale table's slice of each x pair is staged (one
+// load per wave: table rows 8*wave .. +7, so T < 8 * waves), one pair ahead
+// of the x pair it serves, so that a barrier has published every wave's part
+// of it before it is read.  Each wave modulates the x chunks it loaded itself
+// in place, x + x * scale[idx] rounded to bf16, before the pair's barrier,
+// and takes the sums of squares of the raw values on the way (the Gram
+// blocks would see modulated x); the epilogue adds the row's bias rows.
+template <int FM, int FN, int WM, int WN, bool SW, bool Q8, bool AD = false>
 __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = SW ? 2 : 1;
@@ -80,7 +92,14 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   static_assert(WFR % NW == 0 && XFR % NW == 0 && FM % WN == 0, "tile shape");
   constexpr int WSLOT = WFR * kFragBytes;
   constexpr int XSLOT = XFR * kFragBytes;
-  static_assert(4 * WSLOT + 2 * XSLOT + BMF * 64 <= 160 * 1024, "LDS budget");
+  constexpr int TSLOT = AD ? NW * kFragBytes : 16;   // AdaLN table slice of a pair: 8 rows per wave
+  constexpr int LXP = XPW + (AD ? 1 : 0);             // loads per wave per pair (x, table)
+  static_assert(4 * WSLOT + 2 * XSLOT + 2 * TSLOT + BMF * 64 <= 160 * 1024, "LDS budget");
+  static_assert(!AD || !Q8, "AdaLN with bf16 output");
+  // AdaLN needs a few registers more: one register set for the x operands
+  // (row fragment i of k-block t+1 is read as soon as row i of t is
+  // consumed) keeps it within 256 without spills
+  constexpr bool A1 = AD;
 
   __shared__ __attribute__((aligned(1024))) uint8_t wring0[WSLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t wring1[WSLOT];
@@ -88,11 +107,14 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   __shared__ __attribute__((aligned(1024))) uint8_t wring3[WSLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t xring0[XSLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t xring1[XSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t tring0[TSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t tring1[TSLOT];
   __shared__ __attribute__((aligned(16))) float ssbuf[BMF * 16];   // sums of squares, then 1/RMS
   auto wslot = [&](int s) __attribute__((always_inline)) -> uint8_t* {
     return s == 0 ? wring0 : (s == 1 ? wring1 : (s == 2 ? wring2 : wring3));
   };
   auto xslot = [&](int s) __attribute__((always_inline)) -> uint8_t* { return s == 0 ? xring0 : xring1; };
+  auto tslot = [&](int s) __attribute__((always_inline)) -> uint8_t* { return s == 0 ? tring0 : tring1; };
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -121,6 +143,51 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     xk[j] = (c >> 2) * 32 + (c & 3) * 8;
     xoff[j] = (uint32_t)((16 * (q >> 1) + lr) * a.K + xk[j]) * 2u;
   }
+  // AdaLN: the table row of each x row this lane loads, and its chunk's
+  // place in the staged table slice (row t at t*128, chunk c at c*16)
+  int toff[AD ? XPW : 1];
+  float ssx[AD ? XPW : 1];
+  __amdgpu_buffer_rsrc_t tr = xr;
+  uint32_t tload = kOutOfRange;
+  if constexpr (AD) {
+#pragma unroll
+    for (int j = 0; j < XPW; ++j) {
+      const int q = wave + NW * j;
+      const int lr = 8 * (q & 1) + (lane >> 3);
+      const int row = m0 + 16 * (q >> 1) + lr;
+      const int t = row < a.M ? a.idx[row] : -1;
+      // an index outside the table reads the last staged row, always zero
+      // (T < 8 * waves)
+      toff[j] = ((unsigned)t < (unsigned)a.T ? t : 8 * NW - 1) * 128 + ((lane & 7) ^ (lr >> 1)) * 16;
+      ssx[j] = 0.f;
+    }
+    tr = make_rsrc(a.sc, (int64_t)a.T * a.K * 2);
+    const int trow = 8 * wave + (lane >> 3);
+    tload = trow < a.T ? (uint32_t)(trow * a.K + (lane & 7) * 8) * 2u : kOutOfRange;
+  }
+  auto issue_t = [&](uint8_t* base, int p) __attribute__((always_inline)) {
+    const uint32_t in = (uint32_t)((p * 64 + (lane & 7) * 8 - a.K) >> 31) & (tload == kOutOfRange ? 0u : ~0u);
+    const uint32_t off = ((tload + (uint32_t)p * 128u) & in) | (kOutOfRange & ~in);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, (lds_ptr)(base + wave * kFragBytes), 16, off, 0, 0, 0);
+  };
+  // modulate this wave's own chunks of a landed pair in place; sums of
+  // squares of the raw values
+  auto modulate_pair = [&](uint8_t* xb, const uint8_t* tb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < XPW; ++j) {
+      u32x4* xp = reinterpret_cast<u32x4*>(xb + (wave + NW * j) * kFragBytes + lane * 16);
+      const u32x4 xv = *xp;
+      float s2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float x0 = bf16_lo(xv[c]), x1 = bf16_hi(xv[c]);
+        s2 = fmaf(x0, x0, s2);
+        s2 = fmaf(x1, x1, s2);
+      }
+      ssx[j] += s2;
+      *xp = modulate8(xv, *reinterpret_cast<const u32x4*>(tb + toff[j]));
+    }
+  };
   auto issue_x = [&](uint8_t* base, int p) __attribute__((always_inline)) {
     const int k0 = p * 64;
 #pragma unroll
@@ -161,7 +228,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   for (int i = 0; i < SSF; ++i) gram[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int NB = NMAT * FN;            // W' fragments per wave and k-block
-  u32x4 av[2][FM], bv[NB];
+  u32x4 av[A1 ? 1 : 2][FM], bv[NB];
   auto read_a = [&](int r, const uint8_t* base, int u) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) av[r][i] = *reinterpret_cast<const u32x4*>(base + x_at(u, wm * FM + i));
@@ -189,7 +256,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   // from W' slot (T4+1) % 4 and x pair slot ((T4+1) % 4) / 2, half (T4+1) % 2.
   auto step = [&](auto T4c, int t) __attribute__((always_inline)) {
     constexpr int T4 = decltype(T4c)::value;
-    constexpr int r = T4 % 2;
+    constexpr int r = A1 ? 0 : T4 % 2;
     constexpr bool odd = (T4 % 2) == 1;
     const uint8_t* wcur = wslot(T4);
     const uint8_t* wnext = wslot((T4 + 1) % 4);
@@ -207,38 +274,87 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     // loads issued after the newer of the two are in flight; the barrier
     // extends that to every wave and retires every read of slot t.
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-    if constexpr (odd) wait_vmcnt<2 * WPW>();
-    else wait_vmcnt<2 * WPW + XPW>();
+    if constexpr (odd) wait_vmcnt<2 * WPW + (AD ? 1 : 0)>();
+    else wait_vmcnt<2 * WPW + LXP>();
+    if constexpr (AD && odd) {
+      // k-block t+1 opens the next pair: modulate this wave's part of it
+      modulate_pair(xslot(((T4 + 1) % 4) / 2), tslot(((T4 + 1) % 4) / 2));
+      __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_a(r ^ 1, xnext, (T4 + 1) % 2);
-    read_b(0, NB / 2, wnext);
-    mfma_cols(r, NB / 2, NB);
-    squares(r);
-    if constexpr (odd) issue_x(xslot(T4 / 2), (t + 3) / 2);
-    issue_w(wslot(T4), t + 4);
+    if constexpr (A1) {
+      // rows outer: once row i of t is consumed, row i of t+1 replaces it
 #pragma unroll
-    for (int g = 0; g < FM + NB / 2; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = NB / 2; j < NB; ++j)
+          acc[j / FN][i][j % FN] = mfma_chunk<__bf16>(av[0][i], bv[j], acc[j / FN][i][j % FN]);
+        if constexpr (!AD) {
+          if (i / SSF == wn) gram[i % SSF] = mfma_chunk<__bf16>(av[0][i], av[0][i], gram[i % SSF]);
+        }
+        av[0][i] = *reinterpret_cast<const u32x4*>(xnext + x_at((T4 + 1) % 2, wm * FM + i));
+      }
+      read_b(0, NB / 2, wnext);
+    } else {
+      read_a(r ^ 1, xnext, (T4 + 1) % 2);
+      read_b(0, NB / 2, wnext);
+      mfma_cols(r, NB / 2, NB);
+      if constexpr (!AD) squares(r);
+    }
+    if constexpr (odd) issue_x(xslot(T4 / 2), (t + 3) / 2);
+    if constexpr (odd && AD) issue_t(tslot(T4 == 1 ? 1 : 0), (t + 5) / 2);   // one pair ahead
+    issue_w(wslot(T4), t + 4);
+    if constexpr (A1) {
+#pragma unroll
+      for (int g = 0; g < FM; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NB / 2, 0);   // row g's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // row g's next fragment
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < FM + NB / 2; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+      }
     }
 #pragma unroll
-    for (int g = 0; g < WPW + (odd ? XPW : 0); ++g) {
+    for (int g = 0; g < WPW + (odd ? LXP : 0); ++g) {
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);        // one global-to-LDS load
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        // two MFMAs
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue in the steady state's issue order (steps -4 .. -1)
-  issue_w(wring0, 0);
-  issue_x(xring0, 0);
-  issue_w(wring1, 1);
-  issue_w(wring2, 2);
-  issue_x(xring1, 1);
-  issue_w(wring3, 3);
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<3 * WPW + XPW>();           // W' k-block 0 and x pair 0
+  if constexpr (AD) {
+    // table slices 0 and 1 first; pair 0 is modulated once table 0 has
+    // landed for every wave, before table 2 reuses its slot
+    issue_t(tring0, 0);
+    issue_w(wring0, 0);
+    issue_x(xring0, 0);
+    issue_t(tring1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<1>();
+    __builtin_amdgcn_s_barrier();
+    modulate_pair(xring0, tring0);
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    issue_w(wring1, 1);
+    issue_w(wring2, 2);
+    issue_x(xring1, 1);
+    issue_t(tring0, 2);
+    issue_w(wring3, 3);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    // prologue in the steady state's issue order (steps -4 .. -1)
+    issue_w(wring0, 0);
+    issue_x(xring0, 0);
+    issue_w(wring1, 1);
+    issue_w(wring2, 2);
+    issue_x(xring1, 1);
+    issue_w(wring3, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<3 * WPW + XPW>();           // W' k-block 0 and x pair 0
+  }
   __builtin_amdgcn_s_barrier();
   read_a(0, xring0, 0);
   read_b(0, NB / 2, wring0);
@@ -250,8 +366,21 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   }
   wait_vmcnt<0>();   // retire the zero-filled loads issued past the last k-block
 
+  if constexpr (AD) {
+    // the 8 lanes l/8 == r of each own load hold row r's 8 chunks: reduce
+    // over lane bits 0..2
 #pragma unroll
-  for (int i = 0; i < SSF; ++i) {
+    for (int j = 0; j < XPW; ++j) {
+      float v = ssx[j];
+      v += dpp_move<0xB1>(v);     // lane ^ 1
+      v += dpp_move<0x4E>(v);     // lane ^ 2
+      v += dpp_move<0x141>(v);    // mirror within 8 lanes
+      const int q = wave + NW * j;
+      if ((lane & 7) == 0) ssbuf[16 * (q >> 1) + 8 * (q & 1) + (lane >> 3)] = v;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < (AD ? 0 : SSF); ++i) {
     if ((lrow >> 2) == lgrp) {
       const int e = lrow & 3;
       const f32x4 gv = gram[i];
@@ -283,12 +412,19 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
         }
       } else if (row < a.M) {
         __bf16* yrow = static_cast<__bf16*>(a.y) + (size_t)row * a.N;
+        // AdaLN: the row's bias rows (an index outside the table adds nothing)
+        const int trow = AD ? a.idx[row] : -1;
+        const bool tv = AD && (unsigned)trow < (unsigned)a.T;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = (nb0 + wn * FN + j) * 16 + lrow;
           if (col < a.N) {
-            const float v = SW ? silu_times(acc[0][i][j][r] * inv, acc[NMAT - 1][i][j][r] * inv)
-                               : acc[0][i][j][r] * inv;
+            float ga = acc[0][i][j][r] * inv, ua = acc[NMAT - 1][i][j][r] * inv;
+            if (tv) {
+              ga += a.bg[(size_t)trow * a.N + col];
+              if (SW) ua += a.bu[(size_t)trow * a.N + col];
+            }
+            const float v = SW ? silu_times(ga, ua) : ga;
             Store<__bf16>::one(yrow + col, v);
           }
         }
@@ -304,25 +440,34 @@ struct PrefillInstance {
   const char* name;
 };
 
-#define FN_PREFILL(FM, FN_, WM, WN, SW, Q8, NAME)                                                           \
-  PrefillInstance {                                                                                          \
-    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, Q8>), FM, FN_, WM, WN, 4, SW, NAME \
+#define FN_PREFILL(FM, FN_, WM, WN, SW, Q8, AD, NAME)                                                           \
+  PrefillInstance {                                                                                              \
+    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, Q8, AD>), FM, FN_, WM, WN, 4, SW, NAME \
   }
 
 static const PrefillInstance kPrefill[] = {
-    FN_PREFILL(4, 8, 4, 2, false, false, "prefill_bf16_256x256_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, false, "prefill_swiglu_bf16_256x128_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, true, "prefill_swiglu_bf16_q8_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, false, "prefill_bf16_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, false, "prefill_swiglu_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, false, "prefill_swiglu_bf16_q8_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, true, "prefill_adaln_bf16_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, true, "prefill_swiglu_adaln_bf16_256x128_w4x2_xl"),
 };
 
-static const PrefillInstance& pick(bool sw, bool q8 = false) { return kPrefill[q8 ? 2 : (sw ? 1 : 0)]; }
+static const PrefillInstance& pick(bool sw, bool q8 = false, bool ad = false) {
+  return kPrefill[ad ? (sw ? 4 : 3) : (q8 ? 2 : (sw ? 1 : 0))];
+}
 
-FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8) {
+// Largest AdaLN table the prefill kernel stages whole (8 rows per wave, the
+// last staged row kept zero for indices outside the table).
+constexpr int kPrefillAdalnMaxT = 8 * 8 - 1;
+bool prefill_adaln_fits(int64_t T) { return T >= 1 && T <= kPrefillAdalnMaxT; }
+
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8, bool ad) {
   (void)dt;
   (void)K;
-  const PrefillInstance& d = pick(swiglu, q8);
+  const PrefillInstance& d = pick(swiglu, q8, ad);
   FusedPlan p{};
-  p.kind = q8 ? 5 : 1;
+  p.kind = ad ? 7 : (q8 ? 5 : 1);
   p.mf = d.fm * d.wm;
   p.nf = d.fn_ * d.wn;
   p.waves = d.wm * d.wn;
@@ -333,10 +478,17 @@ FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, b
 }
 
 hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
-                          int M, int K, int N, float eps, hipStream_t stream, uint8_t* q, float* qs) {
-  if (dt != DType::BF16 || (q != nullptr && wu == nullptr)) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr);
+                          int M, int K, int N, float eps, hipStream_t stream, uint8_t* q, float* qs,
+                          const AdalnArgs* ad) {
+  if (dt != DType::BF16 || (q != nullptr && wu == nullptr) || (ad != nullptr && (q != nullptr || !prefill_adaln_fits(ad->T))))
+    return hipErrorInvalidValue;
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, ad != nullptr);
   PrefillArgs a;
+  a.sc = ad ? ad->scale : nullptr;
+  a.idx = ad ? ad->idx : nullptr;
+  a.bg = ad ? ad->bias_g : nullptr;
+  a.bu = ad ? ad->bias_u : nullptr;
+  a.T = ad ? ad->T : 0;
   a.q = q;
   a.qs = qs;
   a.x = x;

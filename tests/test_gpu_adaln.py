@@ -91,15 +91,17 @@ def _run(fn, M, K, N, T, swiglu, seed, bad_idx=False):
 @pytest.mark.parametrize("swiglu", [False, True])
 @pytest.mark.parametrize("M,K,N,T", [(1, 8, 16, 1), (3, 40, 37, 2), (9, 4104, 530, 3), (16, 1032, 270, 5),
                                      (17, 256, 48, 2), (40, 1032, 270, 4), (64, 264, 1100, 3), (65, 256, 160, 2),
-                                     (130, 520, 33, 3)])
+                                     (130, 520, 33, 3), (300, 1032, 530, 5), (520, 4104, 270, 63),
+                                     (257, 264, 1100, 64)])
 def test_adaln_parity(gpu_lib, swiglu, M, K, N, T):
     y, ref, bound = _run(gpu_lib, M, K, N, T, swiglu, seed=M * 3 + K + N + T)
     _check(y, ref, bound, f"{'swiglu' if swiglu else 'proj'} adaln {M}x{K}x{N} T={T}")
 
 
+@pytest.mark.parametrize("M", [20, 300])
 @pytest.mark.parametrize("swiglu", [False, True])
-def test_adaln_out_of_range_index(gpu_lib, swiglu):
-    y, ref, bound = _run(gpu_lib, 20, 264, 100, 3, swiglu, seed=5, bad_idx=True)
+def test_adaln_out_of_range_index(gpu_lib, swiglu, M):
+    y, ref, bound = _run(gpu_lib, M, 264, 100, 3, swiglu, seed=5, bad_idx=True)
     _check(y, ref, bound, f"{'swiglu' if swiglu else 'proj'} adaln with indices outside the table")
 
 
@@ -128,3 +130,34 @@ def test_adaln_zero_tables_match_the_plain_path(gpu_lib):
     want = fn.norm_proj_swiglu(x, Pg, Pu, 1e-6)
     assert fn.kernel_name(M, K, N, True, torch.bfloat16).endswith("m64_xlds_w3_u2")
     assert torch.equal(y.view(torch.int16), want.view(torch.int16))
+
+
+def test_adaln_kernel_choice(gpu_lib):
+    """Up to 64 rows the decode kernel; above, the prefill kernel while the
+    table fits its staging (T <= 63), else the decode kernel tiled over rows."""
+    fn = gpu_lib
+    assert fn.kernel_name_adaln(64, 4096, 11008, 4, True).startswith("decode_swiglu_adaln")
+    assert fn.kernel_name_adaln(65, 4096, 11008, 63, True).startswith("prefill_swiglu_adaln")
+    assert fn.kernel_name_adaln(4096, 4096, 11008, 64, False).startswith("decode_adaln")
+
+
+def test_adaln_prefill_sampled_rows(gpu_lib):
+    """4096 rows x 4096 -> 2 x 2048 through the prefill kernel; the oracle on a
+    seeded sample of rows."""
+    import torch
+    fn = gpu_lib
+    M, K, N, T = 4096, 4096, 2048, 16
+    inp = W.random_inputs(M, K, N, "bf16", seed=41, swiglu=True)
+    scale, shift, idx = W.adaln_tables(T, K, M, seed=42)
+    x, g = to_dev(inp.x, "bf16"), to_dev(inp.g, "bf16")
+    sc, sh = to_dev(scale, "bf16"), to_dev(shift, "bf16")
+    Wg, Wu = to_dev(inp.W, "bf16"), to_dev(inp.W_up, "bf16")
+    y = fn.norm_proj_swiglu_adaln(x, sc, _idx_dev(idx), fn.fold_weights(g, Wg), fn.adaln_shift_bias(sh, Wg),
+                                  fn.fold_weights(g, Wu), fn.adaln_shift_bias(sh, Wu), 1e-6)
+    torch.cuda.synchronize()
+    rows = W.sample_indices(M, 40, seed=7)
+    sub = W.random_inputs(1, K, N, "bf16", seed=41, swiglu=True)
+    sub.x, sub.g, sub.W, sub.W_up = inp.x[rows], inp.g, inp.W, inp.W_up
+    ref = oracle.adaln_norm_proj_swiglu(sub.x, sub.g, scale, shift, idx[rows], sub.W, sub.W_up, 1e-6)
+    bound = _bound(sub, scale, shift, idx[rows], True, ref)
+    _check(to_f64(y)[rows], ref, bound, "swiglu adaln prefill rows")
