@@ -132,17 +132,15 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
 
   // x load q = wave + NW*j of a pair: rows 8*(q%2) .. +7 of row block q/2,
   // both k-blocks; lane l brings row lr = 8*(q%2) + l/8 of the block, chunk
-  // (l%8) ^ (lr/2) of its eight 16-byte chunks (k within the pair).
-  uint32_t xoff[XPW];
-  int xk[XPW];
-#pragma unroll
-  for (int j = 0; j < XPW; ++j) {
-    const int q = wave + NW * j;
-    const int lr = 8 * (q & 1) + (lane >> 3);
-    const int c = (lane & 7) ^ (lr >> 1);
-    xk[j] = (c >> 2) * 32 + (c & 3) * 8;
-    xoff[j] = (uint32_t)((16 * (q >> 1) + lr) * a.K + xk[j]) * 2u;
-  }
+  // (l%8) ^ (lr/2) of its eight 16-byte chunks (k within the pair).  NW is
+  // even, so q%2 (hence lr and the chunk) is the same for every j and load j
+  // sits 8*NW*j rows below load 0: one lane offset plus a uniform stride.
+  static_assert(NW % 2 == 0, "x load rows");
+  const int x_lr = 8 * (wave & 1) + (lane >> 3);
+  const int x_c = (lane & 7) ^ (x_lr >> 1);
+  const int xk = (x_c >> 2) * 32 + (x_c & 3) * 8;
+  const uint32_t xoff0 = (uint32_t)((16 * (wave >> 1) + x_lr) * a.K + xk) * 2u;
+  const uint32_t xstride = (uint32_t)(16 * NW) * (uint32_t)a.K;   // bytes between loads j and j+1
   // AdaLN: the table row of each x row this lane loads, and its chunk's
   // place in the staged table slice (row t at t*128, chunk c at c*16)
   int toff[AD ? XPW : 1];
@@ -152,13 +150,11 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   if constexpr (AD) {
 #pragma unroll
     for (int j = 0; j < XPW; ++j) {
-      const int q = wave + NW * j;
-      const int lr = 8 * (q & 1) + (lane >> 3);
-      const int row = m0 + 16 * (q >> 1) + lr;
+      const int row = m0 + 16 * ((wave >> 1) + (NW / 2) * j) + x_lr;
       const int t = row < a.M ? a.idx[row] : -1;
       // an index outside the table reads the last staged row, always zero
       // (T < 8 * waves)
-      toff[j] = ((unsigned)t < (unsigned)a.T ? t : 8 * NW - 1) * 128 + ((lane & 7) ^ (lr >> 1)) * 16;
+      toff[j] = ((unsigned)t < (unsigned)a.T ? t : 8 * NW - 1) * 128 + x_c * 16;
       ssx[j] = 0.f;
     }
     tr = make_rsrc(a.sc, (int64_t)a.T * a.K * 2);
@@ -190,10 +186,16 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   };
   auto issue_x = [&](uint8_t* base, int p) __attribute__((always_inline)) {
     const int k0 = p * 64;
+    const uint32_t in = (uint32_t)((k0 + xk - a.K) >> 31);   // all ones while k < K
+    // opaque to the optimiser: otherwise the XPW loop-invariant sums
+    // xoff0 + j * xstride are hoisted out of the k loop into registers that
+    // the AdaLN instances cannot spare (a spilled offset's reload waits for
+    // every DMA load in flight)
+    uint32_t xb = xoff0 + (uint32_t)k0 * 2u;
+    asm volatile("" : "+v"(xb));
 #pragma unroll
     for (int j = 0; j < XPW; ++j) {
-      const uint32_t in = (uint32_t)((k0 + xk[j] - a.K) >> 31);   // all ones while k < K
-      const uint32_t off = ((xoff[j] + (uint32_t)k0 * 2u) & in) | (kOutOfRange & ~in);
+      const uint32_t off = ((xb + xstride * (uint32_t)j) & in) | (kOutOfRange & ~in);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(base + (wave + NW * j) * kFragBytes), 16, off, 0, 0,
                                                0);
     }
