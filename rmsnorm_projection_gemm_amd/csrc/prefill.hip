@@ -330,7 +330,8 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
 
   if constexpr (AD) {
     // table slices 0 and 1 first; pair 0 is modulated once table 0 has
-    // landed for every wave, before table 2 reuses its slot
+    // landed for every wave, and table 2 reuses its slot only after a
+    // barrier behind every wave's modulation
     issue_t(tring0, 0);
     issue_w(wring0, 0);
     issue_x(xring0, 0);
@@ -340,6 +341,8 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     __builtin_amdgcn_s_barrier();
     modulate_pair(xring0, tring0);
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    // every wave has read table slice 0 before any wave's slice 2 replaces it
+    __builtin_amdgcn_s_barrier();
     issue_w(wring1, 1);
     issue_w(wring2, 2);
     issue_x(xring1, 1);

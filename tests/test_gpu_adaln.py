@@ -141,23 +141,32 @@ def test_adaln_kernel_choice(gpu_lib):
     assert fn.kernel_name_adaln(4096, 4096, 11008, 64, False).startswith("decode_adaln")
 
 
-def test_adaln_prefill_sampled_rows(gpu_lib):
-    """4096 rows x 4096 -> 2 x 2048 through the prefill kernel; the oracle on a
-    seeded sample of rows."""
+@pytest.mark.parametrize("N,T,swiglu,rows", [(2048, 16, True, 96), (12288, 8, False, 128)])
+def test_adaln_prefill_sampled_rows(gpu_lib, N, T, swiglu, rows):
+    """4096 rows x 4096 through the prefill kernel (SwiGLU 2 x 2048 columns
+    with 16 table rows; the 12288-column QKV projection with 8); the oracle
+    on a seeded sample of rows."""
     import torch
     fn = gpu_lib
-    M, K, N, T = 4096, 4096, 2048, 16
-    inp = W.random_inputs(M, K, N, "bf16", seed=41, swiglu=True)
+    M, K = 4096, 4096
+    inp = W.random_inputs(M, K, N, "bf16", seed=41, swiglu=swiglu)
     scale, shift, idx = W.adaln_tables(T, K, M, seed=42)
     x, g = to_dev(inp.x, "bf16"), to_dev(inp.g, "bf16")
     sc, sh = to_dev(scale, "bf16"), to_dev(shift, "bf16")
-    Wg, Wu = to_dev(inp.W, "bf16"), to_dev(inp.W_up, "bf16")
-    y = fn.norm_proj_swiglu_adaln(x, sc, _idx_dev(idx), fn.fold_weights(g, Wg), fn.adaln_shift_bias(sh, Wg),
-                                  fn.fold_weights(g, Wu), fn.adaln_shift_bias(sh, Wu), 1e-6)
+    Wg = to_dev(inp.W, "bf16")
+    if swiglu:
+        Wu = to_dev(inp.W_up, "bf16")
+        y = fn.norm_proj_swiglu_adaln(x, sc, _idx_dev(idx), fn.fold_weights(g, Wg), fn.adaln_shift_bias(sh, Wg),
+                                      fn.fold_weights(g, Wu), fn.adaln_shift_bias(sh, Wu), 1e-6)
+    else:
+        y = fn.norm_proj_adaln(x, sc, _idx_dev(idx), fn.fold_weights(g, Wg), fn.adaln_shift_bias(sh, Wg), 1e-6)
     torch.cuda.synchronize()
-    rows = W.sample_indices(M, 40, seed=7)
-    sub = W.random_inputs(1, K, N, "bf16", seed=41, swiglu=True)
-    sub.x, sub.g, sub.W, sub.W_up = inp.x[rows], inp.g, inp.W, inp.W_up
-    ref = oracle.adaln_norm_proj_swiglu(sub.x, sub.g, scale, shift, idx[rows], sub.W, sub.W_up, 1e-6)
-    bound = _bound(sub, scale, shift, idx[rows], True, ref)
-    _check(to_f64(y)[rows], ref, bound, "swiglu adaln prefill rows")
+    pick = W.sample_indices(M, rows, seed=7)
+    sub = W.random_inputs(1, K, N, "bf16", seed=41, swiglu=swiglu)
+    sub.x, sub.g, sub.W, sub.W_up = inp.x[pick], inp.g, inp.W, inp.W_up
+    if swiglu:
+        ref = oracle.adaln_norm_proj_swiglu(sub.x, sub.g, scale, shift, idx[pick], sub.W, sub.W_up, 1e-6)
+    else:
+        ref = oracle.adaln_norm_proj(sub.x, sub.g, scale, shift, idx[pick], sub.W, 1e-6)
+    bound = _bound(sub, scale, shift, idx[pick], swiglu, ref)
+    _check(to_f64(y)[pick], ref, bound, f"{'swiglu' if swiglu else 'proj'} adaln prefill rows")
