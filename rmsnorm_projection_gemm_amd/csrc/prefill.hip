@@ -9,6 +9,18 @@
 // this beats four waves of 128x128 by ~40%, the second wave hiding the
 // barrier and LDS latency of the first.
 //
+// Schedule (without AdaLN): ping-pong.  Waves 0-3 (one per SIMD) and waves
+// 4-7 alternate between a compute slot -- the k-block's MFMAs, operands
+// already in registers -- and a memory slot -- LDS reads of the wave's next
+// k-block into registers, its share of the global-to-LDS loads, the waits --
+// with a barrier between slots, so each SIMD's matrix pipe is fed by one
+// wave while the other wave's memory work runs beside it (measured 2-3%
+// faster than interleaving loads and MFMAs in every wave; without the
+// global loads the same loop runs at the MFMA-only time, so the L2-to-CU
+// delivery of the operands, about 32 KiB per k-block per CU, is what bounds
+// it).  The AdaLN instances keep an interleaved schedule in every wave: their
+// x pair is modulated in LDS by the waves that loaded it before a barrier.
+//
 // Operands stream through LDS rings filled by direct global-to-LDS buffer
 // loads (no register staging): W' one 32-wide k-block per slot (4 slots),
 // x a pair of k-blocks per slot (2 slots).  W' lands in MFMA fragment order
@@ -96,10 +108,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   constexpr int LXP = XPW + (AD ? 1 : 0);             // loads per wave per pair (x, table)
   static_assert(4 * WSLOT + 2 * XSLOT + 2 * TSLOT + BMF * 64 <= 160 * 1024, "LDS budget");
   static_assert(!AD || !Q8, "AdaLN with bf16 output");
-  // AdaLN needs a few registers more: one register set for the x operands
-  // (row fragment i of k-block t+1 is read as soon as row i of t is
-  // consumed) keeps it within 256 without spills
-  constexpr bool A1 = AD;
+  static_assert(AD || NW == 8, "ping-pong: two groups of one wave per SIMD");
 
   __shared__ __attribute__((aligned(1024))) uint8_t wring0[WSLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t wring1[WSLOT];
@@ -230,10 +239,10 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   for (int i = 0; i < SSF; ++i) gram[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int NB = NMAT * FN;            // W' fragments per wave and k-block
-  u32x4 av[A1 ? 1 : 2][FM], bv[NB];
-  auto read_a = [&](int r, const uint8_t* base, int u) __attribute__((always_inline)) {
+  u32x4 av[FM], bv[NB];                    // one k-block's operands
+  auto read_a = [&](const uint8_t* base, int u) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) av[r][i] = *reinterpret_cast<const u32x4*>(base + x_at(u, wm * FM + i));
+    for (int i = 0; i < FM; ++i) av[i] = *reinterpret_cast<const u32x4*>(base + x_at(u, wm * FM + i));
   };
   auto read_b = [&](int j0, int j1, const uint8_t* base) __attribute__((always_inline)) {
 #pragma unroll
@@ -242,93 +251,166 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
       bv[j] = *reinterpret_cast<const u32x4*>(base + (m * BNF + wn * FN + jj) * kFragBytes + lane * 16);
     }
   };
-  auto mfma_cols = [&](int r, int j0, int j1) __attribute__((always_inline)) {
+  auto mfma_cols = [&](int j0, int j1) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = j0; j < j1; ++j)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) acc[j / FN][i][j % FN] = mfma_chunk<__bf16>(av[r][i], bv[j], acc[j / FN][i][j % FN]);
+      for (int i = 0; i < FM; ++i) acc[j / FN][i][j % FN] = mfma_chunk<__bf16>(av[i], bv[j], acc[j / FN][i][j % FN]);
   };
-  auto squares = [&](int r) __attribute__((always_inline)) {
+  auto squares = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      if (i / SSF == wn) gram[i % SSF] = mfma_chunk<__bf16>(av[r][i], av[r][i], gram[i % SSF]);
+      if (i / SSF == wn) gram[i % SSF] = mfma_chunk<__bf16>(av[i], av[i], gram[i % SSF]);
   };
-  // k-block t = t0 + T4 (T4 = t % 4, a compile-time constant): W' slot T4,
-  // x pair slot (T4 / 2), x registers T4 % 2; k-block t+1's operands come
-  // from W' slot (T4+1) % 4 and x pair slot ((T4+1) % 4) / 2, half (T4+1) % 2.
-  auto step = [&](auto T4c, int t) __attribute__((always_inline)) {
-    constexpr int T4 = decltype(T4c)::value;
-    constexpr int r = A1 ? 0 : T4 % 2;
-    constexpr bool odd = (T4 % 2) == 1;
-    const uint8_t* wcur = wslot(T4);
-    const uint8_t* wnext = wslot((T4 + 1) % 4);
-    const uint8_t* xnext = xslot(((T4 + 1) % 4) / 2);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_cols(r, 0, NB / 2);
-    read_b(NB / 2, NB, wcur);
-#pragma unroll
-    for (int g = 0; g < NB / 2; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);       // FM MFMAs
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // k-block t+1's x pair and W' have landed for this wave once at most the
-    // loads issued after the newer of the two are in flight; the barrier
-    // extends that to every wave and retires every read of slot t.
+  auto lgkm0 = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-    if constexpr (odd) wait_vmcnt<2 * WPW + (AD ? 1 : 0)>();
-    else wait_vmcnt<2 * WPW + LXP>();
-    if constexpr (AD && odd) {
-      // k-block t+1 opens the next pair: modulate this wave's part of it
-      modulate_pair(xslot(((T4 + 1) % 4) / 2), tslot(((T4 + 1) % 4) / 2));
-      __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+  };
+
+  if constexpr (!AD) {
+    // Ping-pong.  k-block s: group A (waves 0-3) reads it in slot 2s-1 and
+    // computes it in slot 2s; group B (waves 4-7) reads it in slot 2s and
+    // computes it in slot 2s+1.  A memory slot also issues the wave's share
+    // of the loads of a later k-block: group A W'(s+4) in slot 2s+1, group
+    // B W'(s+3) in slot 2s -- each into the ring slot whose last reader
+    // (group B) passed a barrier before -- and the x pair of k-blocks 2p,
+    // 2p+1 in slots 4p-5 (A) and 4p-4 (B), after group B's last read of
+    // pair p-2.  Unrolled by four k-blocks (W' slot s % 4, x slot s/2 % 2).
+    auto compute = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_cols(0, NB);
+      squares();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // k-block q = s+1 is first read in slot 2s+1: every wave's loads of it
+    // (W'(q), and x pair q/2 when q is even) must have landed by the barrier
+    // that ends slot 2s.  In both groups' issue orders at most 2 WPW loads
+    // follow them when q is even, 2 WPW + XPW when q is odd.
+    auto ready = [&](auto T4c) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T4c)::value;
+      if constexpr (T4 % 2 == 1) wait_vmcnt<2 * WPW>();
+      else wait_vmcnt<2 * WPW + XPW>();
+    };
+    auto stepA = [&](auto T4c, int s) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T4c)::value;
+      compute();
+      ready(T4c);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(xslot(((T4 + 1) % 4) / 2), (T4 + 1) % 2);
+      read_b(0, NB, wslot((T4 + 1) % 4));
+      if constexpr (T4 % 2 == 1) issue_x(xslot(((T4 + 3) / 2) % 2), (s + 3) / 2);
+      issue_w(wslot(T4), s + 4);
+      lgkm0();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+    };
+    auto stepB = [&](auto T4c, int s) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T4c)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(xslot(T4 / 2), T4 % 2);
+      read_b(0, NB, wslot(T4));
+      if constexpr (T4 % 2 == 0) issue_x(xslot(((T4 + 2) / 2) % 2), (s + 2) / 2);
+      issue_w(wslot((T4 + 3) % 4), s + 3);
+      lgkm0();
+      ready(T4c);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      compute();
+      __builtin_amdgcn_s_barrier();
+    };
+    // prologues: each group's loads of the slots before 0 in its own issue
+    // order; then k-block 0 and x pair 0 have landed everywhere
+    if (wave & 4) {
+      issue_w(wring0, 0);
+      issue_x(xring0, 0);
+      issue_w(wring1, 1);
+      issue_w(wring2, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<2 * WPW>();
+      __builtin_amdgcn_s_barrier();
+      for (int s = 0; s < a.kblocks; s += 4) {
+        stepB(std::integral_constant<int, 0>{}, s);
+        stepB(std::integral_constant<int, 1>{}, s + 1);
+        stepB(std::integral_constant<int, 2>{}, s + 2);
+        stepB(std::integral_constant<int, 3>{}, s + 3);
+      }
+    } else {
+      issue_w(wring0, 0);
+      issue_x(xring0, 0);
+      issue_w(wring1, 1);
+      issue_w(wring2, 2);
+      issue_x(xring1, 1);
+      issue_w(wring3, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<3 * WPW + XPW>();
+      __builtin_amdgcn_s_barrier();
+      read_a(xring0, 0);
+      read_b(0, NB, wring0);
+      for (int s = 0; s < a.kblocks; s += 4) {
+        stepA(std::integral_constant<int, 0>{}, s);
+        stepA(std::integral_constant<int, 1>{}, s + 1);
+        stepA(std::integral_constant<int, 2>{}, s + 2);
+        stepA(std::integral_constant<int, 3>{}, s + 3);
+      }
     }
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (A1) {
-      // rows outer: once row i of t is consumed, row i of t+1 replaces it
+  } else {
+    // AdaLN: every wave interleaves.  k-block t = t0 + T4 (T4 = t % 4, a
+    // compile-time constant): W' slot T4, x pair slot T4 / 2; k-block t+1's
+    // operands come from W' slot (T4+1) % 4 and x pair slot ((T4+1) % 4) / 2,
+    // half (T4+1) % 2.  One register set for the x operands: row fragment i
+    // of k-block t+1 is read as soon as row i of t is consumed (this keeps
+    // the instance within 256 registers without spills).
+    auto step = [&](auto T4c, int t) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T4c)::value;
+      constexpr bool odd = (T4 % 2) == 1;
+      const uint8_t* wcur = wslot(T4);
+      const uint8_t* wnext = wslot((T4 + 1) % 4);
+      const uint8_t* xnext = xslot(((T4 + 1) % 4) / 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_cols(0, NB / 2);
+      read_b(NB / 2, NB, wcur);
+#pragma unroll
+      for (int g = 0; g < NB / 2; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);       // FM MFMAs
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // k-block t+1's x pair and W' have landed for this wave once at most
+      // the loads issued after the newer of the two are in flight; the
+      // barrier extends that to every wave and retires every read of slot t.
+      lgkm0();
+      if constexpr (odd) wait_vmcnt<2 * WPW + 1>();
+      else wait_vmcnt<2 * WPW + LXP>();
+      if constexpr (odd) {
+        // k-block t+1 opens the next pair: modulate this wave's part of it
+        modulate_pair(xslot(((T4 + 1) % 4) / 2), tslot(((T4 + 1) % 4) / 2));
+        lgkm0();
+      }
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = NB / 2; j < NB; ++j)
-          acc[j / FN][i][j % FN] = mfma_chunk<__bf16>(av[0][i], bv[j], acc[j / FN][i][j % FN]);
-        if constexpr (!AD) {
-          if (i / SSF == wn) gram[i % SSF] = mfma_chunk<__bf16>(av[0][i], av[0][i], gram[i % SSF]);
-        }
-        av[0][i] = *reinterpret_cast<const u32x4*>(xnext + x_at((T4 + 1) % 2, wm * FM + i));
+          acc[j / FN][i][j % FN] = mfma_chunk<__bf16>(av[i], bv[j], acc[j / FN][i][j % FN]);
+        av[i] = *reinterpret_cast<const u32x4*>(xnext + x_at((T4 + 1) % 2, wm * FM + i));
       }
       read_b(0, NB / 2, wnext);
-    } else {
-      read_a(r ^ 1, xnext, (T4 + 1) % 2);
-      read_b(0, NB / 2, wnext);
-      mfma_cols(r, NB / 2, NB);
-      if constexpr (!AD) squares(r);
-    }
-    if constexpr (odd) issue_x(xslot(T4 / 2), (t + 3) / 2);
-    if constexpr (odd && AD) issue_t(tslot(T4 == 1 ? 1 : 0), (t + 5) / 2);   // one pair ahead
-    issue_w(wslot(T4), t + 4);
-    if constexpr (A1) {
+      if constexpr (odd) issue_x(xslot(T4 / 2), (t + 3) / 2);
+      if constexpr (odd) issue_t(tslot(T4 == 1 ? 1 : 0), (t + 5) / 2);   // one pair ahead
+      issue_w(wslot(T4), t + 4);
 #pragma unroll
       for (int g = 0; g < FM; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, NB / 2, 0);   // row g's MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // row g's next fragment
       }
-    } else {
 #pragma unroll
-      for (int g = 0; g < FM + NB / 2; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+      for (int g = 0; g < WPW + (odd ? LXP : 0); ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);        // one global-to-LDS load
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        // two MFMAs
       }
-    }
-#pragma unroll
-    for (int g = 0; g < WPW + (odd ? LXP : 0); ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);        // one global-to-LDS load
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        // two MFMAs
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  if constexpr (AD) {
+      __builtin_amdgcn_sched_barrier(0);
+    };
     // table slices 0 and 1 first; pair 0 is modulated once table 0 has
     // landed for every wave, and table 2 reuses its slot only after a
     // barrier behind every wave's modulation
@@ -340,7 +422,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     wait_vmcnt<1>();
     __builtin_amdgcn_s_barrier();
     modulate_pair(xring0, tring0);
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    lgkm0();
     // every wave has read table slice 0 before any wave's slice 2 replaces it
     __builtin_amdgcn_s_barrier();
     issue_w(wring1, 1);
@@ -349,25 +431,15 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     issue_t(tring0, 2);
     issue_w(wring3, 3);
     __builtin_amdgcn_sched_barrier(0);
-  } else {
-    // prologue in the steady state's issue order (steps -4 .. -1)
-    issue_w(wring0, 0);
-    issue_x(xring0, 0);
-    issue_w(wring1, 1);
-    issue_w(wring2, 2);
-    issue_x(xring1, 1);
-    issue_w(wring3, 3);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<3 * WPW + XPW>();           // W' k-block 0 and x pair 0
-  }
-  __builtin_amdgcn_s_barrier();
-  read_a(0, xring0, 0);
-  read_b(0, NB / 2, wring0);
-  for (int t = 0; t < a.kblocks; t += 4) {
-    step(std::integral_constant<int, 0>{}, t);
-    step(std::integral_constant<int, 1>{}, t + 1);
-    step(std::integral_constant<int, 2>{}, t + 2);
-    step(std::integral_constant<int, 3>{}, t + 3);
+    __builtin_amdgcn_s_barrier();
+    read_a(xring0, 0);
+    read_b(0, NB / 2, wring0);
+    for (int t = 0; t < a.kblocks; t += 4) {
+      step(std::integral_constant<int, 0>{}, t);
+      step(std::integral_constant<int, 1>{}, t + 1);
+      step(std::integral_constant<int, 2>{}, t + 2);
+      step(std::integral_constant<int, 3>{}, t + 3);
+    }
   }
   wait_vmcnt<0>();   // retire the zero-filled loads issued past the last k-block
 
