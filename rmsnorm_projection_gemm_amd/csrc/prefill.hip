@@ -472,6 +472,29 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&ssbuf[(wm * FM + i) * 16 + 4 * lgrp]);
+    // AdaLN: the bias values of this row fragment's outputs, all fetched
+    // before its first store (the loads then overlap instead of each waiting
+    // behind the previous store); where the index is outside the table or
+    // the output outside the matrix a valid element is read and dropped, so
+    // an index outside the table adds nothing
+    float bias[NMAT][4][FN];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + (wm * FM + i) * 16 + 4 * lgrp + r;
+      const int trow = AD && row < a.M ? a.idx[row] : -1;
+      const bool tv = AD && (unsigned)trow < (unsigned)a.T;
+      const size_t tb = (size_t)(tv ? trow : 0) * a.N;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = min((nb0 + wn * FN + j) * 16 + lrow, a.N - 1);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          float b = 0.f;
+          if constexpr (AD) b = (m == 0 ? a.bg : a.bu)[tb + col];
+          bias[m][r][j] = tv ? b : 0.f;
+        }
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rl = (wm * FM + i) * 16 + 4 * lgrp + r;   // row within the tile
@@ -489,18 +512,12 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
         }
       } else if (row < a.M) {
         __bf16* yrow = static_cast<__bf16*>(a.y) + (size_t)row * a.N;
-        // AdaLN: the row's bias rows (an index outside the table adds nothing)
-        const int trow = AD ? a.idx[row] : -1;
-        const bool tv = AD && (unsigned)trow < (unsigned)a.T;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = (nb0 + wn * FN + j) * 16 + lrow;
           if (col < a.N) {
-            float ga = acc[0][i][j][r] * inv, ua = acc[NMAT - 1][i][j][r] * inv;
-            if (tv) {
-              ga += a.bg[(size_t)trow * a.N + col];
-              if (SW) ua += a.bu[(size_t)trow * a.N + col];
-            }
+            const float ga = acc[0][i][j][r] * inv + bias[0][r][j];
+            const float ua = acc[NMAT - 1][i][j][r] * inv + bias[NMAT - 1][r][j];
             const float v = SW ? silu_times(ga, ua) : ga;
             Store<__bf16>::one(yrow + col, v);
           }
