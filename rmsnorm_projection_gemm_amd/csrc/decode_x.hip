@@ -529,10 +529,12 @@ inline hipError_t launch_decode_x_instance(const DecodeXInstance& d, const void*
 // workgroups) measured 10-15% slower, two waves slower still; wider waves,
 // deeper stages and k-splits inside the workgroup did not help.
 static const DecodeXInstance kDecodeX[] = {
-    // 32-row projection: a 5-slot ring (four stages in flight) measured 7% faster
+    // plain projections: a 5-slot ring (four stages in flight) measured 7%
+    // (32 rows) and 2% (64 rows) faster; the SwiGLU rungs are fastest with 4
     DecodeXInstance{reinterpret_cast<const void*>(&decode_x_kernel<2, 1, 3, false, 2, false, false, false, 5>), 2, 1, 3,
                     2, false, false, false, "decode_bf16_m32_xlds_w3_u2_s5"},
-    FN_DECODE_X(4, 1, 3, false, 2, "decode_bf16_m64_xlds_w3_u2"),
+    DecodeXInstance{reinterpret_cast<const void*>(&decode_x_kernel<4, 1, 3, false, 2, false, false, false, 5>), 4, 1, 3,
+                    2, false, false, false, "decode_bf16_m64_xlds_w3_u2_s5"},
     FN_DECODE_X(2, 1, 3, true, 2, "decode_swiglu_bf16_m32_xlds_w3_u2"),
     FN_DECODE_X(4, 1, 3, true, 2, "decode_swiglu_bf16_m64_xlds_w3_u2"),
 };
