@@ -6,8 +6,8 @@
 // 16*FM x 16*FN sub-tile whose fp32 accumulators stay in registers for the
 // whole k loop.  The instances use 256x256 tiles (256x128 per matrix for
 // SwiGLU) with eight waves of 64x128, two waves per SIMD: measured on MI355X
-// this beats four waves of 128x128 by ~40%, the second wave hiding the
-// barrier and LDS latency of the first.
+// four waves of 128x128 (one per SIMD) ran 1.8x slower, nothing covering one
+// wave's barrier and memory latency.
 //
 // Schedule (without AdaLN): ping-pong.  Waves 0-3 (one per SIMD) and waves
 // 4-7 alternate between a compute slot -- the k-block's MFMAs, operands
@@ -27,7 +27,7 @@
 // because the packed layout is fragment-major.  x arrives as whole 128-byte
 // lines -- each load brings 8 rows x 64 k values -- because a direct-to-LDS
 // load whose lanes fetch 16 rows x 64 bytes (half lines) measured 37.5 GB/s
-// per CU from L2-resident data against 88-90 GB/s for whole lines; row r's
+// per CU from L2-resident data against 74-90 GB/s for whole lines; row r's
 // 16-byte chunks are stored permuted by r/2 so the quarter-wave operand
 // reads (ds_read_b128) hit distinct bank groups.  Loads past the matrix
 // edges (rows >= M, columns past the packed width, k >= K) use out-of-range
