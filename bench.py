@@ -20,6 +20,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -121,12 +122,20 @@ KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": (
 DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed, so that
+    editing a comment does not mark counters taken on the same code stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(workload):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rmsnorm_projection_gemm_amd", "csrc")
     for f in KERNEL_SOURCES.get(workload, DEFAULT_KERNEL_SOURCES):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
