@@ -206,7 +206,7 @@ fn_status adaln_common(const void* x, const void* scale, const int* idx, const v
                                          (int)N, eps, stream, nullptr, nullptr, &ad),
                       plan.name);
   }
-  const fn::FusedPlan plan = fn::plan_adaln(M, N, swiglu);
+  const fn::FusedPlan plan = fn::plan_adaln(M, N, T, swiglu);
   return hip_status(fn::launch_adaln(plan, x, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, eps, ad, stream),
                     plan.name);
 }
@@ -426,7 +426,7 @@ fn_status fn_norm_proj_swiglu_adaln(const void* x, const void* scale, const int*
 const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
   if (M > 64 && fn::prefill_adaln_fits(T)) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, true).name;
-  return fn::plan_adaln(M, N, swiglu != 0).name;
+  return fn::plan_adaln(M, N, T, swiglu != 0).name;
 }
 
 fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out) {

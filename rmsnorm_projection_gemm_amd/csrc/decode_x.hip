@@ -97,10 +97,12 @@ __device__ inline void decode_e4m3x16(u32x4 w, u32x4& lo, u32x4& hi) {
 // MF: 16-row blocks of x.  NC: 16-column blocks per wave (for SwiGLU each
 // with its gate and up stream).  NWV: waves, sharing the x fragments.  U:
 // k-blocks per stage.  F8: E4M3 weights.  Q8: E4M3 output with row-block
-// scales instead of a y in x's dtype.  AD: AdaLN -- each row's scale-table
-// row is staged beside x, the MFMA operand is x * (1 + scale) while the sum
-// of squares stays on x, and the epilogue adds the row's bias row.
-template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false, int NS = 4>
+// scales instead of a y in x's dtype.  AD: AdaLN -- the MFMA operand is
+// x * (1 + scale[idx]) while the sum of squares stays on x, and the epilogue
+// adds the row's bias row.  TSL (AdaLN tables of fewer than 8 * NWV rows):
+// each stage stages the table's slice (all T rows, the stage's 64 k values,
+// eight rows per wave) instead of one scale row per x row.
+template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false, int NS = 4, bool TSL = false>
 __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   static_assert(NS >= 3 && NS <= 6, "LDS ring slots");
   constexpr int D = NS - 1;                // stages in flight
@@ -109,22 +111,35 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   constexpr int XF = U * MF;               // x loads (1 KiB each) per stage
   constexpr int XPW = (XF + NWV - 1) / NWV;   // x loads each wave issues per stage
   constexpr int WLD = F8 ? U / 2 : U;      // weight loads per stream per stage (fp8: one per k-block pair)
-  constexpr int LPW = WLD * NST + (AD ? 2 : 1) * XPW;   // vector-memory ops per wave per stage
+  // vector-memory ops per wave per stage (AdaLN: the scale rows of its x
+  // loads, or one load of the table slice)
+  constexpr int LPW = WLD * NST + XPW + (AD ? (TSL ? 1 : XPW) : 0);
+  static_assert(!TSL || (AD && U == 2), "table slices: AdaLN, 64 k values per stage");
   // Loads q >= XF (when NWV does not divide XF) fetch nothing and write
   // zeros into the slot's padding, so every wave issues the same count
   // (measured: skipping them instead is no faster).
   constexpr int XSL = XPW * NWV * kFragBytes;   // x part of a slot
-  constexpr int SLOT = AD ? 2 * XSL : XSL;       // AdaLN: the scale rows follow
+  constexpr int TSLOT = TSL ? NWV * kFragBytes : 0;   // table slice: rows 8w .. 8w+7 from wave w
+  // AdaLN: per ring slot also the scale rows, modulated in place (or, TSL,
+  // the modulated x) and the table slice, each in an LDS array of its own:
+  // the compiler then sees that the operand reads of a slot cannot alias the
+  // global-to-LDS loads still landing in other slots (one shared array made
+  // it drain every load in flight before them)
+  constexpr int SLOT = XSL;
+  constexpr int MSLOT = AD ? XSL : 16;
   static_assert(!AD || (NC == 1 && !F8 && !Q8), "AdaLN: bf16 weights and output, one column block per wave");
-  constexpr bool AD_INPLACE = AD && MF > 1;    // modulate once per workgroup, in LDS
+  // modulate once per workgroup, in LDS, before the stage barrier: several
+  // row blocks, or a table slice (read only before the barrier that lets
+  // the slot's next slice be loaded)
+  constexpr bool AD_INPLACE = AD && (MF > 1 || TSL);
   // Epilogue through LDS (one lane per row, 16-byte stores): fp8 output
   // always, bf16 output when each wave owns one column block.
   constexpr bool STAGE = Q8 || (NC == 1 && NWV <= NS);
   static_assert(!STAGE || (NC == 1 && NWV <= NS && 16 * MF * 16 * 4 <= SLOT), "staging fits a ring slot");
   static_assert(!AD || STAGE, "the AdaLN bias is added in the staged epilogue");
   static_assert(U % 2 == 0, "each x load moves two k-blocks of 8 rows");
-  static_assert((D - 1) * LPW < 64, "vmcnt range");
-  static_assert(NS * SLOT + NWV * XPW * 16 * 4 <= 160 * 1024, "LDS budget");
+  static_assert(D * LPW < 64, "vmcnt range");
+  static_assert(NS * (SLOT + (AD ? MSLOT + TSLOT : 0)) + NWV * XPW * 16 * 4 <= 160 * 1024, "LDS budget");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[SLOT];
@@ -132,10 +147,28 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[NS > 3 ? SLOT : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t ring4[NS > 4 ? SLOT : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t ring5[NS > 5 ? SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t mring0[MSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t mring1[MSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t mring2[MSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t mring3[NS > 3 ? MSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t mring4[NS > 4 ? MSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t mring5[NS > 5 ? MSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t tring0[TSL ? TSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t tring1[TSL ? TSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t tring2[TSL ? TSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t tring3[TSL && NS > 3 ? TSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t tring4[TSL && NS > 4 ? TSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t tring5[TSL && NS > 5 ? TSLOT : 16];
   __shared__ float ssp[NWV][XPW][16];      // Gram diagonals
   __shared__ __attribute__((aligned(16))) float inv_s[MF * 16];   // 1/RMS per row
   auto slot_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
     return s == 0 ? ring0 : (s == 1 ? ring1 : (s == 2 ? ring2 : (s == 3 ? ring3 : (s == 4 ? ring4 : ring5))));
+  };
+  auto mod_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
+    return s == 0 ? mring0 : (s == 1 ? mring1 : (s == 2 ? mring2 : (s == 3 ? mring3 : (s == 4 ? mring4 : mring5))));
+  };
+  auto tab_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
+    return s == 0 ? tring0 : (s == 1 ? tring1 : (s == 2 ? tring2 : (s == 3 ? tring3 : (s == 4 ? tring4 : tring5))));
   };
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -212,8 +245,17 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     if constexpr (AD) {
       const int t = (q < XF && m0 + row < a.M) ? a.idx[m0 + row] : -1;
       sok[i] = (unsigned)t < (unsigned)a.T ? 0xffffffffu : 0u;   // out-of-range index: scale 0
-      soff[i] = sok[i] ? (uint32_t)(t * a.K + xk[i]) * 2u : 0u;
+      if constexpr (TSL)   // the chunk's place in the staged slice; the last row stays zero
+        soff[i] = (uint32_t)((sok[i] ? t : 8 * NWV - 1) * 128 + c * 16);
+      else
+        soff[i] = sok[i] ? (uint32_t)(t * a.K + xk[i]) * 2u : 0u;
     }
+  }
+  // TSL: this wave's one table load of each stage (rows 8w .. 8w+7)
+  uint32_t tload = kOutOfRangeX;
+  if constexpr (TSL) {
+    const int trow = 8 * w + (lane >> 3);
+    if (trow < a.T) tload = (uint32_t)(trow * a.K + (lane & 7) * 8) * 2u;
   }
   __amdgpu_buffer_rsrc_t sr = xr;
   if constexpr (AD) sr = make_rsrc_x(a.sc, (int64_t)a.T * a.K * 2);
@@ -230,7 +272,8 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   };
   // Issue stage st into slot base; stages past the last, and k past K, read
   // as zero without touching memory.
-  auto issue_x = [&](uint8_t* base, int st) __attribute__((always_inline)) {
+  auto issue_x = [&](int slot, int st) __attribute__((always_inline)) {
+    uint8_t* base = slot_ptr(slot);
     const uint32_t live = (uint32_t)((st - a.stages) >> 31);
     const int k0 = st * U * 32;
 #pragma unroll
@@ -240,14 +283,23 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_x)(base + (w + NWV * i) * kFragBytes), 16, off, 0, 0,
                                                0);
     }
-    if constexpr (AD) {
+    if constexpr (AD && !TSL) {
 #pragma unroll
       for (int i = 0; i < XPW; ++i) {
         const uint32_t in = sok[i] & live & (uint32_t)((k0 + xk[i] - a.K) >> 31);
         const uint32_t off = ((soff[i] + (uint32_t)k0 * 2u) & in) | (kOutOfRangeX & ~in);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_x)(base + XSL + (w + NWV * i) * kFragBytes), 16, off,
-                                                 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_x)(mod_ptr(slot) + (w + NWV * i) * kFragBytes), 16,
+                                                 off, 0, 0, 0);
       }
+    }
+  };
+  // TSL: the table slice of stage st (rows past T and k past K read zero)
+  auto issue_t = [&](int slot, int st) __attribute__((always_inline)) {
+    if constexpr (TSL) {
+      const uint32_t in = (uint32_t)((st - a.stages) >> 31) & (tload == kOutOfRangeX ? 0u : ~0u) &
+                          (uint32_t)((st * 64 + (lane & 7) * 8 - a.K) >> 31);
+      const uint32_t off = ((tload + (uint32_t)st * 128u) & in) | (kOutOfRangeX & ~in);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_x)(tab_ptr(slot) + w * kFragBytes), 16, off, 0, 0, 0);
     }
   };
   u32x4 wv[NS][WLD][NST];
@@ -272,30 +324,37 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 #pragma unroll
   for (int j = 0; j < XPW; ++j) gram[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Stage st lives in ring slot s and W' buffer s.
+  // AdaLN, in LDS: this wave modulates the x chunks it loaded itself (its
+  // loads have landed), x * (1 + scale) into the slot's second x area, so
+  // each chunk is modulated once per workgroup; x stays raw for the sums of
+  // squares.  The scale comes from the chunk's scale row or (TSL) from the
+  // staged table slice.
+  auto modulate_own = [&](int slot) __attribute__((always_inline)) {
+    const uint8_t* base = slot_ptr(slot);
+    uint8_t* mb = mod_ptr(slot);
+#pragma unroll
+    for (int j = 0; j < XPW; ++j) {
+      if (w + NWV * j < XF) {
+        const int o = (w + NWV * j) * kFragBytes + lane * 16;
+        u32x4* sp = reinterpret_cast<u32x4*>(mb + o);
+        const u32x4 sc = *reinterpret_cast<const u32x4*>(TSL ? tab_ptr(slot) + soff[j] : mb + o);
+        *sp = modulate8(*reinterpret_cast<const u32x4*>(base + o), sc);
+      }
+    }
+  };
+  // Stage st lives in ring slot s and W' buffer s.  TSL: stage st+1 is
+  // modulated during step st, after its barrier (so off the path to the
+  // next one): the wait below then also covers this wave's loads of stage
+  // st+1, and the next barrier publishes the modulated chunks.
   auto step = [&](int s, int st) __attribute__((always_inline)) {
     // Own loads of stage st are done once at most the D-1 younger stages
     // are in flight; the barrier extends that to the x loads of every wave
     // and retires every wave's reads of the slot refilled below.
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt_x<(D - 1) * LPW>();
+    wait_vmcnt_x<(TSL ? D - 2 : D - 1) * LPW>();
     uint8_t* base = slot_ptr(s);
-    if constexpr (AD_INPLACE) {
-      // AdaLN, several row blocks: each wave modulates the chunks it loaded
-      // itself (its loads have landed), x * (1 + scale) over the scale rows
-      // in place, so each chunk is modulated once per workgroup rather than
-      // once per wave; the barrier then publishes them.  x stays raw for the
-      // sums of squares.
-#pragma unroll
-      for (int j = 0; j < XPW; ++j) {
-        if (w + NWV * j < XF) {
-          const int o = (w + NWV * j) * kFragBytes + lane * 16;
-          u32x4* sp = reinterpret_cast<u32x4*>(base + XSL + o);
-          *sp = modulate8(*reinterpret_cast<const u32x4*>(base + o), *sp);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-    }
+    if constexpr (AD_INPLACE && !TSL) modulate_own(s);
+    if constexpr (AD_INPLACE) __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     u32x4 xv[U][MF];
@@ -303,7 +362,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < MF; ++i) xv[u][i] = *reinterpret_cast<const u32x4*>(base + (AD_INPLACE ? XSL : 0) + x_at(u, i));
+      for (int i = 0; i < MF; ++i) xv[u][i] = *reinterpret_cast<const u32x4*>((AD_INPLACE ? mod_ptr(s) : base) + x_at(u, i));
 #pragma unroll
     for (int j = 0; j < XPW; ++j) xg[j] = *reinterpret_cast<const u32x4*>(base + frag_at(w + NWV * j));
     // AdaLN, one row block: the few operand chunks are modulated in
@@ -313,12 +372,17 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int i = 0; i < MF; ++i) sv[u][i] = *reinterpret_cast<const u32x4*>(base + XSL + x_at(u, i));
+        for (int i = 0; i < MF; ++i) sv[u][i] = *reinterpret_cast<const u32x4*>(mod_ptr(s) + x_at(u, i));
     }
     __builtin_amdgcn_sched_barrier(0);
     issue_w((s + D) % NS, st + D);
-    issue_x(slot_ptr((s + D) % NS), st + D);
+    issue_x((s + D) % NS, st + D);
+    issue_t(s, st + NS);   // this slot's slice was last read before the previous barrier
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (TSL) {
+      modulate_own((s + 1) % NS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // B operands: the bf16 fragments as loaded, or the two halves of each
     // fp8 fragment decoded exactly to bf16 (every E4M3 value is a bf16 value)
     u32x4 bw[U][NST];
@@ -345,11 +409,23 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     for (int j = 0; j < XPW; ++j) gram[j] = mfma_chunk<__bf16>(xg[j], xg[j], gram[j]);
   };
 
+  // the loop's load order: W', x, then (TSL) the slice of the stage after;
+  // a stage's slice is published by the barrier before the one that
+  // modulates it -- stage 0's by the barrier below
+  issue_t(0, 0);
 #pragma unroll
   for (int p = 0; p < D; ++p) {
     issue_w(p, p);
-    issue_x(slot_ptr(p), p);
-    __builtin_amdgcn_sched_barrier(0);   // keep the loop's load order: W', then x
+    issue_x(p, p);
+    issue_t(p + 1, p + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (TSL) {
+    // stage 0's loads and slice (and slice 1) have landed; once every
+    // wave's have, modulate stage 0
+    wait_vmcnt_x<(D - 1) * LPW>();
+    __builtin_amdgcn_s_barrier();
+    modulate_own(0);
   }
   // whole rounds of the ring; stages past the last read as zero
   for (int st = 0; st < a.stages; st += NS) {
@@ -602,22 +678,49 @@ FusedPlan plan_fp8(int64_t M, int64_t K, int64_t N, bool swiglu) {
 }
 
 // AdaLN prologue (bf16): rows up to 64 per workgroup, more tile over grid.y.
+// Measured on MI355X: 32 and 64 rows with tables of fewer than 24 rows
+// (three waves x 8 rows) stage the table's slice of each stage and modulate
+// a stage ahead (five ring slots keep three stages in flight); larger tables
+// one scale row per x row.  16 rows: one scale row per x row and the
+// operands modulated in registers, with five ring slots, was fastest.
+#define FN_DECODE_XT(MF, NWV, SW, U, NAME)                                                                       \
+  DecodeXInstance {                                                                                             \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, SW, U, false, false, true, 5, true>), MF, 1, NWV, U, \
+        SW, false, false, NAME                                                                                  \
+  }
+constexpr int kAdTableSliceRows = 8 * 3 - 1;   // the last staged row stays zero (indices outside the table)
+static const DecodeXInstance kDecodeAdT[] = {
+    FN_DECODE_XT(2, 3, false, 2, "decode_adaln_bf16_m32_xlds_w3_u2_tab"),
+    FN_DECODE_XT(4, 3, false, 2, "decode_adaln_bf16_m64_xlds_w3_u2_tab"),
+    FN_DECODE_XT(2, 3, true, 2, "decode_swiglu_adaln_bf16_m32_xlds_w3_u2_tab"),
+    FN_DECODE_XT(4, 3, true, 2, "decode_swiglu_adaln_bf16_m64_xlds_w3_u2_tab"),
+};
+#define FN_DECODE_XA5(NWV, SW, U, NAME)                                                                         \
+  DecodeXInstance {                                                                                            \
+    reinterpret_cast<const void*>(&decode_x_kernel<1, 1, NWV, SW, U, false, false, true, 5>), 1, 1, NWV, U, SW, \
+        false, false, NAME                                                                                     \
+  }
 static const DecodeXInstance kDecodeAd[] = {
-    FN_DECODE_XA(1, 3, false, 2, "decode_adaln_bf16_m16_xlds_w3_u2"),
+    FN_DECODE_XA5(3, false, 2, "decode_adaln_bf16_m16_xlds_w3_u2_s5"),
     FN_DECODE_XA(2, 3, false, 2, "decode_adaln_bf16_m32_xlds_w3_u2"),
     FN_DECODE_XA(4, 3, false, 2, "decode_adaln_bf16_m64_xlds_w3_u2"),
-    FN_DECODE_XA(1, 3, true, 2, "decode_swiglu_adaln_bf16_m16_xlds_w3_u2"),
+    FN_DECODE_XA5(3, true, 2, "decode_swiglu_adaln_bf16_m16_xlds_w3_u2_s5"),
     FN_DECODE_XA(2, 3, true, 2, "decode_swiglu_adaln_bf16_m32_xlds_w3_u2"),
     FN_DECODE_XA(4, 3, true, 2, "decode_swiglu_adaln_bf16_m64_xlds_w3_u2"),
 };
 
-FusedPlan plan_adaln(int64_t M, int64_t N, bool swiglu) {
-  return plan_of(find_instance(kDecodeAd, M <= 16 ? 1 : (M <= 32 ? 2 : 4), swiglu), 6, M, N);
+static bool adaln_table_slice(int mf, int64_t T) { return mf > 1 && T <= kAdTableSliceRows; }
+
+FusedPlan plan_adaln(int64_t M, int64_t N, int64_t T, bool swiglu) {
+  const int mf = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  return plan_of(adaln_table_slice(mf, T) ? find_instance(kDecodeAdT, mf, swiglu) : find_instance(kDecodeAd, mf, swiglu),
+                 6, M, N);
 }
 
 hipError_t launch_adaln(const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y, int M, int K,
                         int N, float eps, const AdalnArgs& ad, hipStream_t stream) {
-  const DecodeXInstance* d = find_instance(kDecodeAd, p.mf, wu != nullptr);
+  const DecodeXInstance* d = adaln_table_slice(p.mf, ad.T) ? find_instance(kDecodeAdT, p.mf, wu != nullptr)
+                                                             : find_instance(kDecodeAd, p.mf, wu != nullptr);
   if (d == nullptr) return hipErrorInvalidValue;
   return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream, nullptr, nullptr, nullptr, nullptr, &ad);
 }

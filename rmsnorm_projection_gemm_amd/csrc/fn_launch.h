@@ -75,7 +75,7 @@ hipError_t launch_decode_q8(bool f8_weights, const FusedPlan& plan, const void* 
                             const float* sg, const void* wu, const float* su, uint8_t* q, float* qs,
                             int M, int K, int N, float eps, hipStream_t stream);
 
-FusedPlan plan_adaln(int64_t M, int64_t N, bool swiglu);
+FusedPlan plan_adaln(int64_t M, int64_t N, int64_t T, bool swiglu);
 hipError_t launch_adaln(const FusedPlan& plan, const void* x, const void* wg, const void* wu, void* y, int M,
                         int K, int N, float eps, const AdalnArgs& ad, hipStream_t stream);
 hipError_t launch_adaln_bias(DType dt, const void* shift, const void* W, float* bias, int T, int K, int N,

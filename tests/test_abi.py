@@ -332,8 +332,11 @@ def test_adaln_swiglu_bias_and_names(lib):
     assert f(0x1000, 0x2000, 0x1000, 2, 16, 16, BF16, None) == ALIAS
     assert f(0x1000, 0x2000, 0x3000, 2, 16, 16, 7, None) == DTYPE
     assert f(None, None, None, 0, 16, 16, BF16, None) == OK
-    assert lib.fn_kernel_name_adaln(16, 4096, 11008, 4, 1).decode() == "decode_swiglu_adaln_bf16_m16_xlds_w3_u2"
-    assert lib.fn_kernel_name_adaln(64, 4096, 11008, 4, 0).decode() == "decode_adaln_bf16_m64_xlds_w3_u2"
+    # 32-64 rows and up to 23 table rows: the decode kernel stages the table's slice per stage; more table
+    # rows, or 16 rows, one scale row per x row
+    assert lib.fn_kernel_name_adaln(16, 4096, 11008, 4, 1).decode() == "decode_swiglu_adaln_bf16_m16_xlds_w3_u2_s5"
+    assert lib.fn_kernel_name_adaln(64, 4096, 11008, 23, 0).decode() == "decode_adaln_bf16_m64_xlds_w3_u2_tab"
+    assert lib.fn_kernel_name_adaln(64, 4096, 11008, 24, 0).decode() == "decode_adaln_bf16_m64_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln(1000, 4096, 11008, 63, 0).decode() == "prefill_adaln_bf16_256x256_w4x2_xl"
     assert lib.fn_kernel_name_adaln(1000, 4096, 11008, 64, 1).decode() == "decode_swiglu_adaln_bf16_m64_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln(0, 4096, 16, 4, 0) == b"invalid"

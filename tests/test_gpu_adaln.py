@@ -92,7 +92,9 @@ def _run(fn, M, K, N, T, swiglu, seed, bad_idx=False):
 @pytest.mark.parametrize("M,K,N,T", [(1, 8, 16, 1), (3, 40, 37, 2), (9, 4104, 530, 3), (16, 1032, 270, 5),
                                      (17, 256, 48, 2), (40, 1032, 270, 4), (64, 264, 1100, 3), (65, 256, 160, 2),
                                      (130, 520, 33, 3), (300, 1032, 530, 5), (520, 4104, 270, 63),
-                                     (257, 264, 1100, 64)])
+                                     (257, 264, 1100, 64),
+                                     # decode with the largest staged table slice, and tables past it
+                                     (33, 1032, 270, 23), (16, 264, 100, 24), (40, 1032, 270, 30), (64, 4104, 530, 40)])
 def test_adaln_parity(gpu_lib, swiglu, M, K, N, T):
     y, ref, bound = _run(gpu_lib, M, K, N, T, swiglu, seed=M * 3 + K + N + T)
     _check(y, ref, bound, f"{'swiglu' if swiglu else 'proj'} adaln {M}x{K}x{N} T={T}")
@@ -137,6 +139,8 @@ def test_adaln_kernel_choice(gpu_lib):
     table fits its staging (T <= 63), else the decode kernel tiled over rows."""
     fn = gpu_lib
     assert fn.kernel_name_adaln(64, 4096, 11008, 4, True).startswith("decode_swiglu_adaln")
+    assert fn.kernel_name_adaln(64, 4096, 11008, 23, True).endswith("_tab")
+    assert not fn.kernel_name_adaln(64, 4096, 11008, 24, True).endswith("_tab")
     assert fn.kernel_name_adaln(65, 4096, 11008, 63, True).startswith("prefill_swiglu_adaln")
     assert fn.kernel_name_adaln(4096, 4096, 11008, 64, False).startswith("decode_adaln")
 

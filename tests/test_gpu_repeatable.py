@@ -90,7 +90,8 @@ def test_q8_output_repeatable(gpu_lib, M):
     _repeat(lambda: fn.norm_proj_swiglu_q8(x, Pg, Pu, 1e-6), lambda r: list(r))
 
 
-@pytest.mark.parametrize("M,N,T,swiglu", [(16, 12288, 4, False), (64, 11008, 4, True), (4096, 12288, 8, False),
+@pytest.mark.parametrize("M,N,T,swiglu", [(16, 12288, 4, False), (64, 11008, 4, True), (64, 11008, 30, True),
+                                          (4096, 12288, 8, False),
                                           (4096, 11008, 16, True), (4096, 4096, 63, False), (4096, 4096, 64, True)])
 def test_adaln_repeatable(gpu_lib, M, N, T, swiglu):
     import torch
