@@ -51,6 +51,8 @@ def parse_args(argv=None):
     p.add_argument("--no-chain", action="store_true",
                    help="skip the comparison runs (unfused chains; bf16 weights beside fp8)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    p.add_argument("--no-measured-peak", dest="measured_peak", action="store_false",
+                   help="skip measuring the attainable peak (roofline.measured_peak, frac_measured)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     p.add_argument("--hot", action="store_true", help="time a single weight buffer only (no rotation)")
     p.add_argument("--clock-warmup-s", type=float, default=0.5,
@@ -439,6 +441,38 @@ def run_decode_step(args, torch, fn, workloads):
     return calls, result
 
 
+def measured_peak(torch, fn, bound):
+    """What this GPU sustains, measured with the library's probes right after
+    the timed region: a streaming read of 1 GiB (beyond the 256 MB
+    Infinity Cache) for HBM, an MFMA-only loop (v_mfma_f32_16x16x32_bf16,
+    register operands) for bf16 matrix work.  Median of five rounds of ten
+    back-to-back calls."""
+    times = []
+    if bound == "hbm":
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        buf.fill_(3)
+        fn.probe_hbm_read(buf)
+        work = float(buf.numel())
+        call = lambda: fn.probe_hbm_read(buf)   # noqa: E731
+        scale, unit = 1e9, "GB/s"
+    else:
+        iters, wgs = 2048, 2048
+        fn.probe_mfma_bf16(iters, wgs)
+        work = float(wgs * iters * fn.PROBE_MFMA_FLOPS_PER_WG_ITER)
+        call = lambda: fn.probe_mfma_bf16(iters, wgs)   # noqa: E731
+        scale, unit = 1e12, "TFLOP/s"
+    torch.cuda.synchronize()
+    for _ in range(5):   # five rounds of ten back-to-back calls
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3 / 10)
+    return round(work / pct(sorted(times), 0.5) / scale, 1), unit
+
+
 def calibrate_copy(torch):
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -540,6 +574,13 @@ def main(argv=None):
             config["prologue"] = (f"AdaLN: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx], tables of {ADALN_T} rows, "
                                   "per-row index")
 
+    if args.measured_peak and roof["bound"] in ("hbm", "mfma") and unit != "us/call":
+        peak, peak_unit = measured_peak(torch, fn, roof["bound"])
+        if peak_unit == roof["unit"]:
+            roof["measured_peak"] = peak
+            roof["frac_measured"] = round(roof["achieved"] / peak, 4)
+            roof["measured_peak_probe"] = ("fn_probe_hbm_read over 1 GiB" if roof["bound"] == "hbm"
+                                           else "fn_probe_mfma_bf16 (MFMA-only loop)")
     out = {
         "metric": METRIC,
         "value": round(value, 4),

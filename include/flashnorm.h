@@ -133,6 +133,29 @@ fn_status fn_rmsnorm(const void* x, const void* g, void* xhat,
 fn_status fn_silu_mul(const void* h, void* out, int64_t M, int64_t N,
                       fn_dtype dt, hipStream_t stream);
 
+/* Measurement probes, not part of the method: the attainable peaks that
+ * roofline fractions are also reported against (a fraction of the vendor
+ * peak and a fraction of what this GPU sustains).
+ *
+ * fn_probe_hbm_read: `workgroups` workgroups of 256 threads stream all of
+ * [src, src + bytes) once with 16-byte loads and write one 32-bit XOR of
+ * what they read to sink[w] (sink: workgroups x 4 bytes, caller-owned
+ * device memory).  bytes must be a multiple of 16 and src 16-byte aligned;
+ * 1 <= workgroups <= 65536.  Bytes read per call = bytes.
+ *
+ * fn_probe_mfma_bf16: `workgroups` workgroups of four waves; every wave runs
+ * iters x 8 v_mfma_f32_16x16x32_bf16 on register operands (eight
+ * independent accumulator chains) and each workgroup writes one float to
+ * sink[w] (workgroups x 4 bytes).  FLOPs per call = workgroups * iters *
+ * 524288.  1 <= iters <= 2^20, 1 <= workgroups <= 65536.
+ *
+ * Both enqueue one launch on `stream`; errors: FN_ERR_NULL, FN_ERR_ALIGN,
+ * FN_ERR_SHAPE (sizes out of range), FN_ERR_HIP. */
+fn_status fn_probe_hbm_read(const void* src, int64_t bytes, void* sink,
+                            int64_t workgroups, hipStream_t stream);
+fn_status fn_probe_mfma_bf16(void* sink, int64_t iters, int64_t workgroups,
+                             hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * fp8 weights (E4M3, one scale per output column)
  *

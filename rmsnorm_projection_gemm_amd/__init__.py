@@ -64,6 +64,8 @@ def load():
         "fn_norm_proj": (i32, [vp, vp, vp, i64, i64, i64, f32, i32, vp]),
         "fn_norm_proj_swiglu": (i32, [vp, vp, vp, vp, i64, i64, i64, f32, i32, vp]),
         "fn_rmsnorm": (i32, [vp, vp, vp, i64, i64, f32, i32, vp]),
+        "fn_probe_hbm_read": (i32, [vp, i64, vp, i64, vp]),
+        "fn_probe_mfma_bf16": (i32, [vp, i64, i64, vp]),
         "fn_silu_mul": (i32, [vp, vp, i64, i64, i32, vp]),
         "fn_kernel_name": (ctypes.c_char_p, [i64, i64, i64, i32, i32]),
         "fn_packed_fp8_bytes": (ctypes.c_size_t, [i64, i64]),
@@ -211,6 +213,31 @@ def rmsnorm(x, g, eps: float = 1e-6, out=None):
     y = _out(out, M, K, x)
     _check(load().fn_rmsnorm(x.data_ptr(), g.data_ptr(), y.data_ptr(), M, K, eps, _dt(x.dtype), _stream(x)))
     return y
+
+
+PROBE_MFMA_FLOPS_PER_WG_ITER = 524288   # 4 waves x 8 MFMAs x 16*16*32*2
+
+
+def probe_hbm_read(src, workgroups: int = 2048):
+    """Measurement probe: stream all of `src` (a contiguous device tensor whose
+    size is a multiple of 16 bytes) once; returns the sink tensor."""
+    _need_cuda("src", src)
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    import torch
+    sink = torch.empty((workgroups,), dtype=torch.int32, device=src.device)
+    nbytes = src.numel() * src.element_size()
+    _check(load().fn_probe_hbm_read(src.data_ptr(), nbytes, sink.data_ptr(), workgroups, _stream(src)))
+    return sink
+
+
+def probe_mfma_bf16(iters: int, workgroups: int = 2048, device="cuda"):
+    """Measurement probe: an MFMA-only loop of workgroups * iters * 524288
+    bf16 FLOPs on the current stream; returns the sink tensor."""
+    import torch
+    sink = torch.empty((workgroups,), dtype=torch.float32, device=device)
+    _check(load().fn_probe_mfma_bf16(sink.data_ptr(), iters, workgroups, _stream(sink)))
+    return sink
 
 
 def silu_mul(h, out=None):

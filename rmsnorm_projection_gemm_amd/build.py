@@ -22,11 +22,12 @@ ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in any kernel.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source extras.  The decode kernels keep their few accumulators in
-# VGPRs (the AGPR form made the compiler shuffle accumulators every
-# iteration); the prefill kernel needs the AGPR file for its 256.
+# Per-source extras.  The decode kernels and the MFMA probe keep their few
+# accumulators in VGPRs (the AGPR form made the compiler shuffle
+# accumulators every iteration); the prefill kernel needs the AGPR file for
+# its 256.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-FILE_FLAGS = {"decode.hip": _VGPR_FORM, "decode_x.hip": _VGPR_FORM}
+FILE_FLAGS = {"decode.hip": _VGPR_FORM, "decode_x.hip": _VGPR_FORM, "probe.hip": _VGPR_FORM}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
                 "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
 

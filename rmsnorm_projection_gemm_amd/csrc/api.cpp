@@ -337,6 +337,24 @@ fn_status fn_silu_mul(const void* h, void* out, int64_t M, int64_t N, fn_dtype d
   return hip_status(fn::launch_silu_mul(to_dt(dt), h, out, (int)M, (int)N, stream), "silu_mul");
 }
 
+fn_status fn_probe_hbm_read(const void* src, int64_t bytes, void* sink, int64_t workgroups, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (bytes < 16 || bytes % 16 != 0) return fail(FN_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (workgroups < 1 || workgroups > 65536) return fail(FN_ERR_SHAPE, "workgroups must be in [1, 65536]");
+  if (src == nullptr || sink == nullptr) return fail(FN_ERR_NULL, "src and sink must be non-NULL");
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(FN_ERR_ALIGN, "src must be 16-byte and sink 4-byte aligned");
+  return hip_status(fn::launch_probe_read(src, bytes, sink, (int)workgroups, stream), "probe_read");
+}
+
+fn_status fn_probe_mfma_bf16(void* sink, int64_t iters, int64_t workgroups, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (iters < 1 || iters > (1 << 20)) return fail(FN_ERR_SHAPE, "iters must be in [1, 2^20]");
+  if (workgroups < 1 || workgroups > 65536) return fail(FN_ERR_SHAPE, "workgroups must be in [1, 65536]");
+  if (sink == nullptr) return fail(FN_ERR_NULL, "sink must be non-NULL");
+  if (!aligned(sink, 4)) return fail(FN_ERR_ALIGN, "sink must be 4-byte aligned");
+  return hip_status(fn::launch_probe_mfma(sink, (int)iters, (int)workgroups, stream), "probe_mfma");
+}
+
 size_t fn_packed_fp8_bytes(int64_t K, int64_t N) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || N < 0 || N > kMaxN) return 0;
   return (size_t)packed_fp8_bytes(K, N);

@@ -78,6 +78,10 @@ hipError_t launch_decode_q8(bool f8_weights, const FusedPlan& plan, const void* 
 FusedPlan plan_adaln(int64_t M, int64_t N, int64_t T, bool swiglu);
 hipError_t launch_adaln(const FusedPlan& plan, const void* x, const void* wg, const void* wu, void* y, int M,
                         int K, int N, float eps, const AdalnArgs& ad, hipStream_t stream);
+// Measurement probes (a streaming read, an MFMA-only loop).
+hipError_t launch_probe_read(const void* src, int64_t bytes, void* sink, int workgroups, hipStream_t stream);
+hipError_t launch_probe_mfma(void* sink, int iters, int workgroups, hipStream_t stream);
+
 hipError_t launch_adaln_bias(DType dt, const void* shift, const void* W, float* bias, int T, int K, int N,
                              hipStream_t stream);
 

@@ -128,6 +128,23 @@ def test_chain_helpers_reject(lib):
     assert lib.fn_silu_mul(None, None, 0, 8, BF16, None) == OK
 
 
+def test_probes_reject(lib):
+    """The measurement probes validate before any HIP call."""
+    f = lib.fn_probe_hbm_read
+    assert f(None, 1024, 0x1000, 8, None) == NULL
+    assert f(0x1000, 1000, 0x1000, 8, None) == SHAPE        # not a multiple of 16
+    assert f(0x1000, 0, 0x1000, 8, None) == SHAPE
+    assert f(0x1000, 1024, 0x1000, 0, None) == SHAPE
+    assert f(0x1000, 1024, 0x1000, 65537, None) == SHAPE
+    assert f(0x1008, 1024, 0x1000, 8, None) == ALIGN
+    g = lib.fn_probe_mfma_bf16
+    assert g(None, 16, 8, None) == NULL
+    assert g(0x1000, 0, 8, None) == SHAPE
+    assert g(0x1000, (1 << 20) + 1, 8, None) == SHAPE
+    assert g(0x1000, 16, 0, None) == SHAPE
+    assert g(0x1002, 16, 8, None) == ALIGN
+
+
 def test_status_strings(lib):
     for s in range(8):
         assert lib.fn_status_string(s)
