@@ -598,6 +598,9 @@ def main(argv=None):
         "roofline": roof,
         "us_per_step": round(r["ms"] * 1e3, 3),
         "us_p10_p50_p90": [round(pct(r["each"], q) * 1e3, 3) for q in (0.1, 0.5, 0.9)],
+        # the same throughput priced at the median of the individually timed calls
+        "value_at_p50": (None if unit == "us/call" else
+                         round(value * r["ms"] / pct(r["each"], 0.5), 4)),
         "hot_us_per_step": None if r["hot_ms"] is None else round(r["hot_ms"] * 1e3, 3),
         "kernel": kernel,
         **per_unit,
