@@ -120,7 +120,7 @@ KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": (
                   "qkv_decode_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_fp8": ("decode_x.hip", "fn_device.h"),
                   "decode_step_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_q8": ("decode_x.hip", "fn_device.h"),
                   "ffn_decode_fp8_q8": ("decode_x.hip", "fn_device.h"), "qkv_decode_adaln": ("decode_x.hip", "fn_device.h"),
-                  "ffn_decode_adaln": ("decode_x.hip", "fn_device.h"), "prefill_qkv_adaln": ("prefill.hip", "fn_device.h")}
+                  "ffn_decode_adaln": ("decode_x.hip", "fn_device.h"), "prefill_qkv_adaln": ("prefill.hip", "adaln.hip", "fn_device.h")}
 DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
 
 
@@ -286,9 +286,13 @@ def run_single(args, torch, fn, workloads):
         idx_t = torch.from_numpy(idx_np).cuda()
         bg_t = fn.adaln_shift_bias(sh_t, Wg)
         bu_t = fn.adaln_shift_bias(sh_t, Wu) if call.swiglu else None
-        proj = lambda x_, P_, e_, out=None: fn.norm_proj_adaln(x_, sc_t, idx_t, P_, bg_t, e_, out=out)  # noqa: E731
-        proj_sw = lambda x_, a_, b_, e_, out=None: fn.norm_proj_swiglu_adaln(  # noqa: E731
-            x_, sc_t, idx_t, a_, bg_t, b_, bu_t, e_, out=out)
+        # the two-launch form above 64 rows (pre-pass into a workspace allocated here, once)
+        nws = fn.adaln_workspace_bytes(call.M, call.K)
+        ws_t = torch.empty((nws,), dtype=torch.uint8, device="cuda") if nws else None
+        proj = lambda x_, P_, e_, out=None: fn.norm_proj_adaln_ws(  # noqa: E731
+            x_, sc_t, idx_t, P_, bg_t, e_, out=out, workspace=ws_t)
+        proj_sw = lambda x_, a_, b_, e_, out=None: fn.norm_proj_swiglu_adaln_ws(  # noqa: E731
+            x_, sc_t, idx_t, a_, bg_t, b_, bu_t, e_, out=out, workspace=ws_t)
     q8 = args.output == "q8"
     if q8:
         # SwiGLU quantised in the epilogue: E4M3 codes + row-block scales
@@ -537,7 +541,7 @@ def main(argv=None):
         call, inp, r = run_single(args, torch, fn, workloads)
         bytes_call = call_bytes(call, fp8, q8) + (adaln_extra_bytes(call) if adaln else 0)
         flops_call = call.flops()
-        kernel = (fn.kernel_name_adaln(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln else
+        kernel = (fn.kernel_name_adaln_ws(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln else
                   fn.kernel_name_q8(call.M, call.K, call.N, fp8) if q8 else
                   fn.kernel_name_fp8(call.M, call.K, call.N, call.swiglu) if fp8 else
                   fn.kernel_name(call.M, call.K, call.N, call.swiglu,
@@ -553,7 +557,7 @@ def main(argv=None):
             unit = "TFLOP/s"
             value = flops_call / (r["ms"] * 1e-3) / 1e12
             roof = {"bound": "mfma", "achieved": round(value, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(value / BF16_PEAK_TFLOPS, 4), "traffic": counter_traffic(args.workload)}
+                    "frac": round(value / BF16_PEAK_TFLOPS, 4), "traffic": counter_traffic(args.workload + suffix)}
         elif args.workload == "tiny":
             unit = "us/call"
             value = r["ms"] * 1e3
@@ -572,7 +576,8 @@ def main(argv=None):
             config["output"] = "fp8 E4M3 codes + one fp32 scale per 16-column row block"
         if adaln:
             config["prologue"] = (f"AdaLN: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx], tables of {ADALN_T} rows, "
-                                  "per-row index")
+                                  "per-row index" + (", two launches (adaln_modulate pre-pass, then the kernel named)"
+                                                     if fn.adaln_workspace_bytes(call.M, call.K) else ", one launch"))
 
     if args.measured_peak and roof["bound"] in ("hbm", "mfma") and unit != "us/call":
         peak, peak_unit = measured_peak(torch, fn, roof["bound"])

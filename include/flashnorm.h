@@ -69,7 +69,8 @@ typedef enum fn_status {
   FN_ERR_DTYPE = 4,  /* dt is not a member of fn_dtype                     */
   FN_ERR_EPS = 5,    /* eps is negative, NaN or infinite                   */
   FN_ERR_ALIAS = 6,  /* an output buffer overlaps an input buffer          */
-  FN_ERR_HIP = 7     /* the HIP runtime rejected a launch                  */
+  FN_ERR_HIP = 7,    /* the HIP runtime rejected a launch                  */
+  FN_ERR_WORKSPACE = 8 /* a caller workspace is NULL, misaligned or short */
 } fn_status;
 
 typedef enum fn_dtype {
@@ -306,6 +307,51 @@ fn_status fn_norm_proj_swiglu_adaln(const void* x, const void* scale, const int*
  * when T <= 63, else the decode kernel tiled over rows); "invalid" for bad
  * shapes. */
 const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu);
+
+/* Two-launch form of the two AdaLN calls above, for many rows.  A pre-pass
+ * (fn_adaln_modulate below) writes the modulated operand and 1/RMS of each
+ * raw row into a caller workspace; the prefill kernel then projects that
+ * operand and applies the deferred 1/RMS and the bias rows in its epilogue.
+ * The one-launch kernels modulate x once per output tile (every workgroup
+ * along N repeats it); here it is done once per row, and any T is served.
+ * The page's own AdaLN FC1 kernel runs as two launches as well
+ * ([FlashInfer #5521] "Fused Kernel on SM120").  Same arithmetic and
+ * arguments as fn_norm_proj_adaln / fn_norm_proj_swiglu_adaln, plus:
+ * workspace: device memory of at least fn_adaln_workspace_bytes(M, K)
+ *   bytes, 256-byte aligned, overlapping no other argument.  The call writes
+ *   it and reads it back in stream order; its contents afterwards are
+ *   unspecified, and calls in flight at the same time need separate
+ *   workspaces.  For M <= 64 the call is the one-launch call (the
+ *   workspace is not touched and may be NULL, with workspace_bytes 0).
+ * Errors as the one-launch calls, plus FN_ERR_WORKSPACE (M > 64 and the
+ * workspace NULL, misaligned or smaller than needed) and FN_ERR_ALIAS (the
+ * workspace overlaps an argument). */
+fn_status fn_norm_proj_adaln_ws(const void* x, const void* scale, const int* idx, const void* W_packed,
+                                const float* bias, void* y, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
+                                void* workspace, int64_t workspace_bytes, hipStream_t stream);
+fn_status fn_norm_proj_swiglu_adaln_ws(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+                                       const float* bias_gate, const void* W_up_packed, const float* bias_up,
+                                       void* out, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
+                                       void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes the two calls above need: the operand (M*K bf16) and one
+ * fp32 per row, each rounded up to 256 bytes; 0 when M <= 64 (one launch)
+ * or when M or K is outside the limits. */
+int64_t fn_adaln_workspace_bytes(int64_t M, int64_t K);
+
+/* Projection kernel instance of the two-launch calls (their one-launch
+ * kernel for M <= 64); "invalid" for bad shapes. */
+const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu);
+
+/* The pre-pass alone: for each row m, with s = scale[idx[m]] (all zero when
+ * idx[m] is outside [0, T)),
+ *   u[m][k] = bf16_rne(fp32(x[m][k] + x[m][k] * s[k]))   (one fp32 rounding)
+ *   rs[m]   = 1 / sqrt(sum_k x[m][k]^2 / K + eps)         (fp32, raw x)
+ * -- the operand the one-launch AdaLN kernels form in LDS, and the deferred
+ * scale.  x, scale: as above; u: [M,K] bf16, 16-byte aligned; rs: [M] fp32,
+ * 4-byte aligned; neither may overlap an input or the other. */
+fn_status fn_adaln_modulate(const void* x, const void* scale, const int* idx, void* u, float* rs, int64_t M,
+                            int64_t K, int64_t T, float eps, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Recorded steps: a sequence of fused calls replayed with one launch

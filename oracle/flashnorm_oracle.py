@@ -381,10 +381,26 @@ def adaln_norm_proj_folded(x, W_folded, scale, bias, idx, eps: float) -> np.ndar
     return ((x * (1.0 + _f64(scale)[i])) @ _f64(W_folded)) / rms(x, eps)[:, None] + _f64(bias)[i]
 
 
+def adaln_operand(x, scale, idx) -> np.ndarray:
+    """The modulated matrix-core operand of the AdaLN path, as the kernels
+    form it: x + x * scale[idx[m]] rounded once to float32, then to bf16 with
+    ties to even (the reading stated with the AdaLN section above: the
+    fp32 -> bf16 step rounds to nearest even, [FlashInfer #4040]); an index
+    outside [0, T) takes scale 0.  For bf16 x and scale the float64 sum is
+    exact.  This fixes bits, so it is compared bit for bit; the projection
+    oracles above stay in float64."""
+    x = _f64(x)
+    sc = _f64(scale)
+    i = np.asarray(idx, dtype=np.int64)
+    ok = (i >= 0) & (i < sc.shape[0])
+    s = np.where(ok[:, None], sc[np.where(ok, i, 0)], 0.0)
+    return round_to_bf16(round_to_f32(x + x * s))
+
+
 __all__ = ["rms", "rmsnorm", "norm_proj", "silu", "norm_proj_swiglu", "fold_exact",
            "round_to_bf16", "round_to_f32", "round_to", "fold_weights", "norm_proj_folded",
            "norm_proj_swiglu_folded", "eps_as_received", "E4M3_MAX", "e4m3_decode", "e4m3_encode",
            "quantize_e4m3_columns", "fold_weights_fp8", "norm_proj_fp8", "norm_proj_swiglu_fp8",
            "Q8_BLOCK", "quantize_e4m3_row_blocks", "dequantize_row_blocks", "norm_proj_swiglu_q8",
            "norm_proj_swiglu_fp8_q8", "adaln_modulate", "adaln_norm_proj", "adaln_norm_proj_swiglu",
-           "adaln_shift_bias", "adaln_norm_proj_folded"]
+           "adaln_shift_bias", "adaln_norm_proj_folded", "adaln_operand"]

@@ -30,7 +30,7 @@ FN_F32 = 0
 FN_BF16 = 1
 
 STATUS = {0: "FN_OK", 1: "FN_ERR_NULL", 2: "FN_ERR_SHAPE", 3: "FN_ERR_ALIGN", 4: "FN_ERR_DTYPE",
-          5: "FN_ERR_EPS", 6: "FN_ERR_ALIAS", 7: "FN_ERR_HIP"}
+          5: "FN_ERR_EPS", 6: "FN_ERR_ALIAS", 7: "FN_ERR_HIP", 8: "FN_ERR_WORKSPACE"}
 
 _lib = None
 
@@ -80,6 +80,12 @@ def load():
         "fn_norm_proj_adaln": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
         "fn_norm_proj_swiglu_adaln": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
         "fn_kernel_name_adaln": (ctypes.c_char_p, [i64, i64, i64, i64, i32]),
+        "fn_norm_proj_adaln_ws": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp, i64, vp]),
+        "fn_norm_proj_swiglu_adaln_ws": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp, i64,
+                                               vp]),
+        "fn_adaln_workspace_bytes": (i64, [i64, i64]),
+        "fn_kernel_name_adaln_ws": (ctypes.c_char_p, [i64, i64, i64, i64, i32]),
+        "fn_adaln_modulate": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, f32, vp]),
         "fn_step_create": (i32, [vp, i64, ctypes.POINTER(vp)]),
         "fn_step_launch": (i32, [vp, vp]),
         "fn_step_num_kernels": (i64, [vp]),
@@ -447,6 +453,77 @@ def kernel_name_adaln(M: int, K: int, N: int, T: int, swiglu: bool) -> str:
     return load().fn_kernel_name_adaln(M, K, N, T, int(swiglu)).decode()
 
 
+def adaln_workspace_bytes(M: int, K: int) -> int:
+    """Workspace bytes of the two-launch AdaLN calls (0: one launch)."""
+    return int(load().fn_adaln_workspace_bytes(M, K))
+
+
+def _workspace(workspace, M: int, K: int, like):
+    """(pointer, bytes) of the caller's workspace, or of a new one from
+    torch's caching allocator when none is given and the call needs it."""
+    need = adaln_workspace_bytes(M, K)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = _torch().empty((need,), dtype=_torch().uint8, device=like.device)
+    _need_cuda("workspace", workspace)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def norm_proj_adaln_ws(x, scale, idx, Wp: PackedWeights, bias, eps: float = 1e-6, out=None, workspace=None):
+    """norm_proj_adaln in two launches above 64 rows: the AdaLN pre-pass
+    into a workspace (allocated here when not given), then the prefill
+    kernel on the modulated operand."""
+    _check_adaln(x, scale, idx, Wp, bias)
+    M, N = x.shape[0], Wp.N
+    y = _out(out, M, N, x)
+    ws, nbytes = _workspace(workspace, M, Wp.K, x)
+    _check(load().fn_norm_proj_adaln_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Wp.data.data_ptr(),
+                                        bias.data_ptr(), y.data_ptr(), M, Wp.K, N, scale.shape[0], eps,
+                                        None if ws is None else ws.data_ptr(), nbytes, _stream(x)))
+    return y
+
+
+def norm_proj_swiglu_adaln_ws(x, scale, idx, Wg: PackedWeights, bias_g, Wu: PackedWeights, bias_u,
+                              eps: float = 1e-6, out=None, workspace=None):
+    """norm_proj_swiglu_adaln in two launches above 64 rows (see
+    norm_proj_adaln_ws)."""
+    _check_adaln(x, scale, idx, Wg, bias_g)
+    _check_adaln(x, scale, idx, Wu, bias_u)
+    M, N = x.shape[0], Wg.N
+    y = _out(out, M, N, x)
+    ws, nbytes = _workspace(workspace, M, Wg.K, x)
+    _check(load().fn_norm_proj_swiglu_adaln_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Wg.data.data_ptr(),
+                                               bias_g.data_ptr(), Wu.data.data_ptr(), bias_u.data_ptr(),
+                                               y.data_ptr(), M, Wg.K, N, scale.shape[0], eps,
+                                               None if ws is None else ws.data_ptr(), nbytes, _stream(x)))
+    return y
+
+
+def kernel_name_adaln_ws(M: int, K: int, N: int, T: int, swiglu: bool) -> str:
+    return load().fn_kernel_name_adaln_ws(M, K, N, T, int(swiglu)).decode()
+
+
+def adaln_modulate(x, scale, idx, eps: float = 1e-6, u=None, rs=None):
+    """The AdaLN pre-pass alone: (u, rs) with u = bf16(x + x * scale[idx])
+    [M, K] and rs = 1/RMS(x) [M] float32."""
+    torch = _torch()
+    for name, t in (("x", x), ("scale", scale), ("idx", idx)):
+        _need_cuda(name, t)
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] bf16 tensor")
+    M, K = x.shape
+    if scale.dim() != 2 or scale.shape[1] != K or scale.dtype != torch.bfloat16 or not scale.is_contiguous():
+        raise ValueError(f"scale must be a contiguous [T, {K}] bf16 tensor")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (M,):
+        raise ValueError(f"idx must be [{M}] int32")
+    u = torch.empty((M, K), dtype=torch.bfloat16, device=x.device) if u is None else u
+    rs = torch.empty((M,), dtype=torch.float32, device=x.device) if rs is None else rs
+    _check(load().fn_adaln_modulate(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), u.data_ptr(), rs.data_ptr(), M, K,
+                                    scale.shape[0], eps, _stream(x)))
+    return u, rs
+
+
 # ------------------------------------------------------- recorded steps --
 FN_CALL_NORM_PROJ, FN_CALL_NORM_PROJ_SWIGLU, FN_CALL_NORM_PROJ_FP8, FN_CALL_NORM_PROJ_SWIGLU_FP8 = 0, 1, 2, 3
 FN_CALL_NORM_PROJ_SWIGLU_Q8, FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8 = 4, 5
@@ -561,4 +638,5 @@ __all__ = ["load", "fold_weights", "norm_proj", "norm_proj_swiglu", "rmsnorm", "
            "FN_CALL_NORM_PROJ_SWIGLU", "FN_CALL_NORM_PROJ_FP8", "FN_CALL_NORM_PROJ_SWIGLU_FP8",
            "FN_CALL_NORM_PROJ_SWIGLU_Q8", "FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8", "Q8_BLOCK", "norm_proj_swiglu_q8",
            "norm_proj_swiglu_fp8_q8", "kernel_name_q8", "adaln_shift_bias", "norm_proj_adaln",
-           "norm_proj_swiglu_adaln", "kernel_name_adaln"]
+           "norm_proj_swiglu_adaln", "kernel_name_adaln", "adaln_workspace_bytes", "norm_proj_adaln_ws",
+           "norm_proj_swiglu_adaln_ws", "kernel_name_adaln_ws", "adaln_modulate"]

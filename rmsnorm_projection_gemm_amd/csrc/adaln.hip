@@ -21,6 +21,61 @@ __global__ __launch_bounds__(256) void adaln_bias_kernel(const T* __restrict__ s
   bias[id] = acc;
 }
 
+// Pre-pass of the two-launch AdaLN form, one wave per row of x: the
+// modulated operand u = x + x * scale[idx] (fp32, one rounding, then RNE to
+// bf16 -- modulate8, the same operand the one-launch kernels form; scale 0
+// for an index outside [0, T)) and 1/RMS of the raw row in fp32.  The
+// projection then runs once on u and applies the deferred 1/RMS from rs, so
+// the modulation is done once per row instead of once per output tile
+// ([FlashInfer #5521] "Fused Kernel on SM120": the page's own AdaLN FC1 also
+// runs as two launches).  Four 16-byte chunks per lane are loaded before any
+// is used, so each wave keeps 4 KiB of reads in flight.
+__global__ __launch_bounds__(256) void adaln_modulate_kernel(const u32x4* __restrict__ x,
+                                                             const u32x4* __restrict__ scale,
+                                                             const int* __restrict__ idx, int T,
+                                                             u32x4* __restrict__ u, float* __restrict__ rs, int M,
+                                                             int K8, float k, float eps) {
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  if (row >= M) return;   // whole waves only; no workgroup barrier follows
+  const int t = idx[row];
+  const bool tv = (unsigned)t < (unsigned)T;
+  const u32x4* xr = x + (size_t)row * K8;
+  const u32x4* sr = scale + (size_t)(tv ? t : 0) * K8;
+  u32x4* ur = u + (size_t)row * K8;
+  constexpr int B = 4;
+  float ss = 0.f;
+  for (int c0 = lane; c0 < K8; c0 += B * kWave) {
+    u32x4 xv[B], sv[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int c = c0 + b * kWave;
+      xv[b] = c < K8 ? xr[c] : u32x4{0u, 0u, 0u, 0u};
+      sv[b] = (tv && c < K8) ? sr[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int c = c0 + b * kWave;
+      ss += sumsq16<__bf16>(xv[b]);
+      if (c < K8) ur[c] = modulate8(xv[b], sv[b]);
+    }
+  }
+  for (int off = kWave / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if (lane == 0) rs[row] = inv_rms(ss, k, eps);
+}
+
+hipError_t launch_adaln_modulate(const void* x, const void* scale, const int* idx, int T, void* u, float* rs, int M,
+                                 int K, float eps, hipStream_t stream) {
+  const u32x4* xp = static_cast<const u32x4*>(x);
+  const u32x4* sp = static_cast<const u32x4*>(scale);
+  u32x4* up = static_cast<u32x4*>(u);
+  int K8 = K / 8;
+  float k = (float)K;
+  void* args[] = {&xp, &sp, &idx, &T, &up, &rs, &M, &K8, &k, &eps};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&adaln_modulate_kernel), dim3((unsigned)ceil_div(M, 4)),
+                         dim3(256), args, 0, stream);
+}
+
 hipError_t launch_adaln_bias(DType dt, const void* shift, const void* W, float* bias, int T, int K, int N,
                              hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div((int64_t)T * N, 256)), block(256);

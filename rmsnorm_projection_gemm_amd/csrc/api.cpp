@@ -211,6 +211,42 @@ fn_status adaln_common(const void* x, const void* scale, const int* idx, const v
                     plan.name);
 }
 
+constexpr int64_t kAdalnOneLaunchRows = 64;   // up to here the _ws calls run the one-launch kernel
+
+int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// Two-launch AdaLN workspace: the modulated operand u [M,K] bf16, then
+// 1/RMS per row [M] fp32, each at a 256-byte boundary.
+int64_t adaln_ws_need(int64_t M, int64_t K) { return align256(M * K * 2) + align256(M * 4); }
+
+fn_status adaln_ws_common(const void* x, const void* scale, const int* idx, const void* wg, const float* bg,
+                          const void* wu, const float* bu, void* y, int64_t M, int64_t K, int64_t N, int64_t T,
+                          float eps, void* ws, int64_t ws_bytes, hipStream_t stream, bool swiglu) {
+  FN_TRY(adaln_common(x, scale, idx, wg, bg, wu, bu, y, M, K, N, T, eps, stream, swiglu, true));
+  if (M == 0 || N == 0) return FN_OK;
+  if (M <= kAdalnOneLaunchRows)
+    return adaln_common(x, scale, idx, wg, bg, wu, bu, y, M, K, N, T, eps, stream, swiglu);
+  const int64_t need = adaln_ws_need(M, K);
+  if (ws == nullptr) return fail(FN_ERR_WORKSPACE, "workspace is NULL (the call needs %lld bytes)", (long long)need);
+  if (!aligned(ws, 256)) return fail(FN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(FN_ERR_WORKSPACE, "workspace_bytes=%lld, the call needs %lld", (long long)ws_bytes, (long long)need);
+  const int64_t wb = packed_bytes(K, N, FN_BF16), bb = T * N * 4;
+  if (overlap(ws, need, x, M * K * 2) || overlap(ws, need, scale, T * K * 2) || overlap(ws, need, idx, M * 4) ||
+      overlap(ws, need, wg, wb) || overlap(ws, need, bg, bb) || overlap(ws, need, y, M * N * 2) ||
+      (swiglu && (overlap(ws, need, wu, wb) || overlap(ws, need, bu, bb))))
+    return fail(FN_ERR_ALIAS, "workspace overlaps an argument");
+  void* u = ws;
+  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(M * K * 2));
+  FN_TRY(hip_status(fn::launch_adaln_modulate(x, scale, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
+                    "adaln_modulate"));
+  const fn::AdalnArgs ad{nullptr, idx, bg, swiglu ? bu : nullptr, (int)T};
+  const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, false, true);
+  return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, ad,
+                                              stream),
+                    plan.name);
+}
+
 // One recorded call: validate (check_only) or enqueue it on `stream`.
 fn_status run_call(const fn_call& c, hipStream_t stream, bool check_only) {
   switch (c.kind) {
@@ -447,6 +483,55 @@ const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int
   return fn::plan_adaln(M, N, T, swiglu != 0).name;
 }
 
+int64_t fn_adaln_workspace_bytes(int64_t M, int64_t K) {
+  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 0 || M > kMaxM || M <= kAdalnOneLaunchRows) return 0;
+  return adaln_ws_need(M, K);
+}
+
+fn_status fn_norm_proj_adaln_ws(const void* x, const void* scale, const int* idx, const void* W_packed,
+                                const float* bias, void* y, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
+                                void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return adaln_ws_common(x, scale, idx, W_packed, bias, nullptr, nullptr, y, M, K, N, T, eps, workspace,
+                         workspace_bytes, stream, false);
+}
+
+fn_status fn_norm_proj_swiglu_adaln_ws(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+                                       const float* bias_gate, const void* W_up_packed, const float* bias_up,
+                                       void* out, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
+                                       void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return adaln_ws_common(x, scale, idx, W_gate_packed, bias_gate, W_up_packed, bias_up, out, M, K, N, T, eps,
+                         workspace, workspace_bytes, stream, true);
+}
+
+const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
+  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
+  if (M > kAdalnOneLaunchRows) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true).name;
+  return fn_kernel_name_adaln(M, K, N, T, swiglu);
+}
+
+fn_status fn_adaln_modulate(const void* x, const void* scale, const int* idx, void* u, float* rs, int64_t M,
+                            int64_t K, int64_t T, float eps, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(M, 0));
+  FN_TRY(check_eps(eps));
+  if (T < 1 || T > INT32_MAX || T * K * 2 > INT32_MAX)
+    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*2 < 2^31", (long long)T);
+  if (M == 0) return FN_OK;
+  if (x == nullptr || scale == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, scale or idx is NULL");
+  if (u == nullptr || rs == nullptr) return fail(FN_ERR_NULL, "u or rs is NULL");
+  if (!aligned(x, 16) || !aligned(scale, 16) || !aligned(u, 16))
+    return fail(FN_ERR_ALIGN, "x, scale and u must be 16-byte aligned");
+  if (!aligned(idx, 4) || !aligned(rs, 4)) return fail(FN_ERR_ALIGN, "idx and rs must be 4-byte aligned");
+  const int64_t xb = M * K * 2;
+  if (overlap(u, xb, x, xb) || overlap(u, xb, scale, T * K * 2) || overlap(u, xb, idx, M * 4) ||
+      overlap(rs, M * 4, x, xb) || overlap(rs, M * 4, scale, T * K * 2) || overlap(rs, M * 4, idx, M * 4) ||
+      overlap(u, xb, rs, M * 4))
+    return fail(FN_ERR_ALIAS, "output overlaps an input");
+  return hip_status(fn::launch_adaln_modulate(x, scale, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
+                    "adaln_modulate");
+}
+
 fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out) {
   g_last_error[0] = '\0';
   if (out == nullptr) return fail(FN_ERR_NULL, "out is NULL");
@@ -533,6 +618,7 @@ const char* fn_status_string(fn_status s) {
     case FN_ERR_EPS: return "eps must be finite and non-negative";
     case FN_ERR_ALIAS: return "output overlaps an input";
     case FN_ERR_HIP: return "HIP launch failed";
+    case FN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
   }
   return "unknown status";
 }

@@ -16,7 +16,8 @@ struct FusedPlan {
   int kind;           // 0 = decode (<= 16 rows, or fp32), 1 = prefill (tiled), 2 = decode with x in LDS,
                       // 3 = fp8 weights (x in LDS, rows tiled over grid.y),
                       // 4 = SwiGLU with fp8 output (x in LDS), 5 = the same on the prefill kernel,
-                      // 6 = AdaLN prologue (x and scale rows in LDS), 7 = AdaLN on the prefill kernel
+                      // 6 = AdaLN prologue (x and scale rows in LDS), 7 = AdaLN on the prefill kernel,
+                      // 8 = prefill on an operand modulated by the AdaLN pre-pass
   int mf;             // 16-row fragments per workgroup (decode)
   int nf;             // 16-column fragments per workgroup (decode)
   int waves;          // waves per workgroup
@@ -49,12 +50,23 @@ struct AdalnArgs {
 
 // q8: SwiGLU with fp8 output (codes q, row-block scales qs; y unused).
 // ad: AdaLN prologue (tables of at most 63 rows, prefill_adaln_fits).
-FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8 = false, bool ad = false);
+// ex: the prefill kernel on an operand the AdaLN pre-pass modulated (1/RMS
+// per row from the pre-pass, bias rows in the epilogue).
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8 = false, bool ad = false,
+                       bool ex = false);
 hipError_t launch_prefill(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
                           const void* w_up, void* y, int M, int K, int N, float eps,
                           hipStream_t stream, uint8_t* q = nullptr, float* qs = nullptr,
                           const AdalnArgs* ad = nullptr);
 bool prefill_adaln_fits(int64_t T);
+// Two-launch AdaLN: the pre-pass writes u = bf16(x + x * scale[idx]) [M,K]
+// and rs = 1/RMS(x) [M]; the prefill kernel then runs on u (plan from
+// plan_prefill(..., ex = true); ad.scale unused).
+hipError_t launch_adaln_modulate(const void* x, const void* scale, const int* idx, int T, void* u, float* rs, int M,
+                                 int K, float eps, hipStream_t stream);
+hipError_t launch_prefill_premod(const FusedPlan& plan, const void* u, const float* rs, const void* wg,
+                                 const void* wu, void* y, int M, int K, int N, const AdalnArgs& ad,
+                                 hipStream_t stream);
 
 hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
                        int K, int N, hipStream_t stream);

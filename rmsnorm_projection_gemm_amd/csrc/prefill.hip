@@ -64,6 +64,7 @@ struct PrefillArgs {
   const float* bg;   // AdaLN: bias rows [T, N] (gate for SwiGLU)
   const float* bu;   // AdaLN: bias rows of W_up
   int T;
+  const float* rs;   // EX: 1/RMS of each row [M], from the AdaLN pre-pass
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -90,7 +91,12 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // in place, x + x * scale[idx] rounded to bf16, before the pair's barrier,
 // and takes the sums of squares of the raw values on the way (the Gram
 // blocks would see modulated x); the epilogue adds the row's bias rows.
-template <int FM, int FN, int WM, int WN, bool SW, bool Q8, bool AD = false>
+//
+// EX: the projection half of the two-launch AdaLN form.  x is the operand
+// the pre-pass already modulated, 1/RMS of each raw row comes from a.rs (no
+// Gram blocks), and the epilogue adds the row's bias rows; the loop is the
+// ping-pong one of the plain instances.
+template <int FM, int FN, int WM, int WN, bool SW, bool Q8, bool AD = false, bool EX = false>
 __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = SW ? 2 : 1;
@@ -109,6 +115,8 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   static_assert(4 * WSLOT + 2 * XSLOT + 2 * TSLOT + BMF * 64 <= 160 * 1024, "LDS budget");
   static_assert(!AD || !Q8, "AdaLN with bf16 output");
   static_assert(AD || NW == 8, "ping-pong: two groups of one wave per SIMD");
+  static_assert(!EX || (!AD && !Q8), "pre-modulated operand: ping-pong loop, bf16 output");
+  constexpr bool BIAS = AD || EX;
 
   __shared__ __attribute__((aligned(1024))) uint8_t wring0[WSLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t wring1[WSLOT];
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     auto compute = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
       mfma_cols(0, NB);
-      squares();
+      if constexpr (!EX) squares();
       __builtin_amdgcn_sched_barrier(0);
     };
     // k-block q = s+1 is first read in slot 2s+1: every wave's loads of it
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     }
   }
 #pragma unroll
-  for (int i = 0; i < (AD ? 0 : SSF); ++i) {
+  for (int i = 0; i < (AD || EX ? 0 : SSF); ++i) {
     if ((lrow >> 2) == lgrp) {
       const int e = lrow & 3;
       const f32x4 gv = gram[i];
@@ -465,8 +473,15 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     }
   }
   __syncthreads();
-  // 1/RMS once per row of the tile, in place
-  if (threadIdx.x < BMF * 16) ssbuf[threadIdx.x] = inv_rms(ssbuf[threadIdx.x], (float)a.K, a.eps);
+  // 1/RMS once per row of the tile, in place (EX: the pre-pass's)
+  if (threadIdx.x < BMF * 16) {
+    if constexpr (EX) {
+      const int row = m0 + (int)threadIdx.x;
+      ssbuf[threadIdx.x] = row < a.M ? a.rs[row] : 0.f;
+    } else {
+      ssbuf[threadIdx.x] = inv_rms(ssbuf[threadIdx.x], (float)a.K, a.eps);
+    }
+  }
   __syncthreads();
 
 #pragma unroll
@@ -481,8 +496,8 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = m0 + (wm * FM + i) * 16 + 4 * lgrp + r;
-      const int trow = AD && row < a.M ? a.idx[row] : -1;
-      const bool tv = AD && (unsigned)trow < (unsigned)a.T;
+      const int trow = BIAS && row < a.M ? a.idx[row] : -1;
+      const bool tv = BIAS && (unsigned)trow < (unsigned)a.T;
       const size_t tb = (size_t)(tv ? trow : 0) * a.N;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -490,7 +505,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
           float b = 0.f;
-          if constexpr (AD) b = (m == 0 ? a.bg : a.bu)[tb + col];
+          if constexpr (BIAS) b = (m == 0 ? a.bg : a.bu)[tb + col];
           bias[m][r][j] = tv ? b : 0.f;
         }
       }
@@ -534,21 +549,23 @@ struct PrefillInstance {
   const char* name;
 };
 
-#define FN_PREFILL(FM, FN_, WM, WN, SW, Q8, AD, NAME)                                                           \
-  PrefillInstance {                                                                                              \
-    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, Q8, AD>), FM, FN_, WM, WN, 4, SW, NAME \
+#define FN_PREFILL(FM, FN_, WM, WN, SW, Q8, AD, EX, NAME)                                                          \
+  PrefillInstance {                                                                                                 \
+    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, Q8, AD, EX>), FM, FN_, WM, WN, 4, SW, NAME \
   }
 
 static const PrefillInstance kPrefill[] = {
-    FN_PREFILL(4, 8, 4, 2, false, false, false, "prefill_bf16_256x256_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, false, false, "prefill_swiglu_bf16_256x128_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, true, false, "prefill_swiglu_bf16_q8_256x128_w4x2_xl"),
-    FN_PREFILL(4, 8, 4, 2, false, false, true, "prefill_adaln_bf16_256x256_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, false, true, "prefill_swiglu_adaln_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, false, false, "prefill_bf16_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, false, false, "prefill_swiglu_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, false, false, "prefill_swiglu_bf16_q8_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, true, false, "prefill_adaln_bf16_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, true, false, "prefill_swiglu_adaln_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, false, true, "prefill_premod_bf16_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, false, true, "prefill_swiglu_premod_bf16_256x128_w4x2_xl"),
 };
 
-static const PrefillInstance& pick(bool sw, bool q8 = false, bool ad = false) {
-  return kPrefill[ad ? (sw ? 4 : 3) : (q8 ? 2 : (sw ? 1 : 0))];
+static const PrefillInstance& pick(bool sw, bool q8 = false, bool ad = false, bool ex = false) {
+  return kPrefill[ex ? (sw ? 6 : 5) : (ad ? (sw ? 4 : 3) : (q8 ? 2 : (sw ? 1 : 0)))];
 }
 
 // Largest AdaLN table the prefill kernel stages whole (8 rows per wave, the
@@ -556,12 +573,12 @@ static const PrefillInstance& pick(bool sw, bool q8 = false, bool ad = false) {
 constexpr int kPrefillAdalnMaxT = 8 * 8 - 1;
 bool prefill_adaln_fits(int64_t T) { return T >= 1 && T <= kPrefillAdalnMaxT; }
 
-FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8, bool ad) {
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8, bool ad, bool ex) {
   (void)dt;
   (void)K;
-  const PrefillInstance& d = pick(swiglu, q8, ad);
+  const PrefillInstance& d = pick(swiglu, q8, ad, ex);
   FusedPlan p{};
-  p.kind = ad ? 7 : (q8 ? 5 : 1);
+  p.kind = ex ? 8 : (ad ? 7 : (q8 ? 5 : 1));
   p.mf = d.fm * d.wm;
   p.nf = d.fn_ * d.wn;
   p.waves = d.wm * d.wn;
@@ -583,6 +600,7 @@ hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const voi
   a.bg = ad ? ad->bias_g : nullptr;
   a.bu = ad ? ad->bias_u : nullptr;
   a.T = ad ? ad->T : 0;
+  a.rs = nullptr;
   a.q = q;
   a.qs = qs;
   a.x = x;
@@ -597,6 +615,28 @@ hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const voi
   a.eps = eps;
   void* args[] = {&a};
   (void)p;
+  return hipLaunchKernel(d.fn, p.grid, p.block, args, 0, stream);
+}
+
+hipError_t launch_prefill_premod(const FusedPlan& p, const void* u, const float* rs, const void* wg, const void* wu,
+                                 void* y, int M, int K, int N, const AdalnArgs& ad, hipStream_t stream) {
+  const PrefillInstance& d = pick(wu != nullptr, false, false, true);
+  PrefillArgs a{};
+  a.x = u;
+  a.wg = wg;
+  a.wu = wu;
+  a.y = y;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.kblocks = (int)ceil_div(K, 32);
+  a.nblocks = (int)ceil_div(N, 16);
+  a.idx = ad.idx;
+  a.bg = ad.bias_g;
+  a.bu = ad.bias_u;
+  a.T = ad.T;
+  a.rs = rs;
+  void* args[] = {&a};
   return hipLaunchKernel(d.fn, p.grid, p.block, args, 0, stream);
 }
 

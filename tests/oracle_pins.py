@@ -496,3 +496,34 @@ def check_adaln(o, seed=24):
 
 
 ALL_CHECKS += [check_adaln]
+
+
+def check_adaln_operand(o, seed=25):
+    """The AdaLN operand: hand-derived roundings (ties to even both ways, a
+    rounding up and down off the midpoint, exact zero and doubling, indices
+    outside the table), and on random bf16 values the reductions that fix
+    it without rounding: scale 0 gives x, scale -1 gives 0, scale 1 gives 2x,
+    and a per-row table lookup equals the row-by-row computation."""
+    for c in load_golden()["adaln_operand"]["cases"]:
+        got = o.adaln_operand(np.array([[c["x"]]]), np.array([[c["s"]]]), np.array([c["idx"]]))
+        assert got.shape == (1, 1) and got[0, 0] == c["u"], (c, got)
+    rng = np.random.default_rng(seed)
+    M, K, T = 6, 40, 3
+    x = o.round_to_bf16(rng.standard_normal((M, K)))
+    sc = o.round_to_bf16(rng.standard_normal((T, K)) * 0.3)
+    idx = rng.integers(0, T, M)
+    assert np.array_equal(o.adaln_operand(x, np.zeros((T, K)), idx), x)
+    assert np.array_equal(o.adaln_operand(x, -np.ones((T, K)), idx), np.zeros((M, K)))
+    assert np.array_equal(o.adaln_operand(x, np.ones((T, K)), idx), 2 * x)
+    got = o.adaln_operand(x, sc, idx)
+    for m in range(M):
+        row = o.adaln_operand(x[m:m + 1], sc[idx[m]:idx[m] + 1], np.array([0]))
+        assert np.array_equal(got[m], row[0]), m
+    # every result is a bf16 value within half a bf16 step of the exact product
+    exact = x * (1 + sc[idx])
+    step = np.ldexp(1.0, np.frexp(exact)[1] - 8)
+    assert np.all(np.abs(got - exact) <= step / 2 + 1e-300)
+    assert np.array_equal(o.round_to_bf16(got), got)
+
+
+ALL_CHECKS += [check_adaln_operand]

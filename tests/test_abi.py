@@ -357,3 +357,64 @@ def test_adaln_swiglu_bias_and_names(lib):
     assert lib.fn_kernel_name_adaln(1000, 4096, 11008, 63, 0).decode() == "prefill_adaln_bf16_256x256_w4x2_xl"
     assert lib.fn_kernel_name_adaln(1000, 4096, 11008, 64, 1).decode() == "decode_swiglu_adaln_bf16_m64_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln(0, 4096, 16, 4, 0) == b"invalid"
+
+
+WORKSPACE = 8
+
+
+def _adw(lib, x=0x1000, sc=0x10000, idx=0x18000, w=0x20000, b=0x30000, y=0x40000, M=100, K=16, N=16, T=2, eps=1e-6,
+         ws=0x100000, wsb=1 << 20):
+    return lib.fn_norm_proj_adaln_ws(x, sc, idx, w, b, y, M, K, N, T, eps, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(ws=None), WORKSPACE, "workspace is NULL"),
+    (dict(ws=0x100080), WORKSPACE, "256-byte"),
+    (dict(wsb=2048), WORKSPACE, "workspace_bytes=2048"),
+    (dict(ws=0x40000), ALIAS, "workspace overlaps"),
+    (dict(ws=0x1000 - 256), ALIAS, "workspace overlaps"),
+    # the one-launch checks come first
+    (dict(x=None, ws=None), NULL, "x, scale or idx"),
+    (dict(K=12), SHAPE, "multiple of 8"),
+    (dict(T=0), SHAPE, "T=0"),
+    (dict(eps=float("nan")), EPS, "eps"),
+    (dict(y=0x30000), ALIAS, "output overlaps"),
+])
+def test_norm_proj_adaln_ws_rejects(lib, kwargs, status, needle):
+    assert _adw(lib, **kwargs) == status
+    assert needle in lib.fn_last_error().decode()
+    assert lib.fn_status_string(WORKSPACE) == b"workspace missing, misaligned or too small"
+
+
+def test_adaln_ws_sizes_and_names(lib):
+    # operand M*K bf16, then one fp32 per row, each rounded up to 256 bytes; none up to 64 rows
+    assert lib.fn_adaln_workspace_bytes(64, 4096) == 0
+    assert lib.fn_adaln_workspace_bytes(65, 8) == 1280 + 512
+    assert lib.fn_adaln_workspace_bytes(4096, 4096) == 4096 * 4096 * 2 + 4096 * 4
+    assert lib.fn_adaln_workspace_bytes(100, 12) == 0 and lib.fn_adaln_workspace_bytes(-1, 16) == 0
+    assert lib.fn_kernel_name_adaln_ws(4096, 4096, 12288, 4, 0).decode() == "prefill_premod_bf16_256x256_w4x2_xl"
+    assert lib.fn_kernel_name_adaln_ws(65, 4096, 11008, 500, 1).decode() == "prefill_swiglu_premod_bf16_256x128_w4x2_xl"
+    assert lib.fn_kernel_name_adaln_ws(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_adaln_bf16_m64_xlds_w3_u2_tab"
+    assert lib.fn_kernel_name_adaln_ws(0, 4096, 16, 4, 0) == b"invalid"
+    sw = lib.fn_norm_proj_swiglu_adaln_ws
+    # SwiGLU: missing up operands, a short workspace, and the empty call (nothing read)
+    assert sw(0x1000, 0x10000, 0x18000, 0x20000, 0x30000, None, 0x31000, 0x40000, 100, 16, 16, 2, 1e-6, 0x100000,
+              1 << 20, None) == NULL
+    assert sw(0x1000, 0x10000, 0x18000, 0x20000, 0x30000, 0x21000, 0x31000, 0x40000, 100, 16, 16, 2, 1e-6, 0x100000,
+              16, None) == WORKSPACE
+    assert sw(None, None, None, None, None, None, None, None, 0, 16, 16, 2, 1e-6, None, 0, None) == OK
+
+
+def test_adaln_modulate_rejects(lib):
+    f = lib.fn_adaln_modulate
+    assert f(None, 0x10000, 0x18000, 0x20000, 0x30000, 4, 16, 2, 1e-6, None) == NULL
+    assert f(0x1000, 0x10000, 0x18000, None, 0x30000, 4, 16, 2, 1e-6, None) == NULL
+    assert "u or rs" in lib.fn_last_error().decode()
+    assert f(0x1000, 0x10000, 0x18000, 0x20008, 0x30000, 4, 16, 2, 1e-6, None) == ALIGN
+    assert f(0x1000, 0x10000, 0x18000, 0x20000, 0x30002, 4, 16, 2, 1e-6, None) == ALIGN
+    assert f(0x1000, 0x10000, 0x18000, 0x1000, 0x30000, 4, 16, 2, 1e-6, None) == ALIAS
+    assert f(0x1000, 0x10000, 0x18000, 0x20000, 0x20010, 4, 16, 2, 1e-6, None) == ALIAS
+    assert f(0x1000, 0x10000, 0x18000, 0x20000, 0x30000, 4, 12, 2, 1e-6, None) == SHAPE
+    assert f(0x1000, 0x10000, 0x18000, 0x20000, 0x30000, 4, 16, 0, 1e-6, None) == SHAPE
+    assert f(0x1000, 0x10000, 0x18000, 0x20000, 0x30000, 4, 16, 2, -1.0, None) == EPS
+    assert f(None, None, None, None, None, 0, 16, 2, 1e-6, None) == OK

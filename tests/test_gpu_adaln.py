@@ -174,3 +174,130 @@ def test_adaln_prefill_sampled_rows(gpu_lib, N, T, swiglu, rows):
         ref = oracle.adaln_norm_proj(sub.x, sub.g, scale, shift, idx[pick], sub.W, 1e-6)
     bound = _bound(sub, scale, shift, idx[pick], swiglu, ref)
     _check(to_f64(y)[pick], ref, bound, f"{'swiglu' if swiglu else 'proj'} adaln prefill rows")
+
+
+# ---------------------------------------------------------------------------
+# Two-launch form: the pre-pass (fn_adaln_modulate) into a caller workspace,
+# then the prefill kernel on the modulated operand
+# ---------------------------------------------------------------------------
+def _bf16_bits(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("M,K,T", [(1, 8, 1), (5, 264, 3), (70, 1032, 5), (301, 4104, 100), (4096, 4096, 4)])
+def test_adaln_modulate_matches_oracle(gpu_lib, M, K, T):
+    """The pre-pass operand bit for bit (a rounding decides every bit: the
+    oracle takes it in the same two steps, fp32 then bf16), and 1/RMS of the
+    raw rows within the fp32 bound of its sum."""
+    from tests.gpu_helpers import storage_bits
+    fn = gpu_lib
+    seed = M + K + T
+    inp = W.random_inputs(M, K, 16, "bf16", seed=seed)
+    scale, _, idx = W.adaln_tables(T, K, M, seed=seed + 1)
+    if M >= 3:
+        idx[0], idx[-1] = -1, T           # outside the table: scale 0
+    u, rs = fn.adaln_modulate(to_dev(inp.x, "bf16"), to_dev(scale, "bf16"), _idx_dev(idx), 1e-6)
+    want = oracle.adaln_operand(inp.x, scale, idx)
+    got = _bf16_bits(u)
+    bad = got != storage_bits(want, "bf16")
+    assert not bad.any(), f"{bad.sum()} operand values differ, first at {np.argwhere(bad)[:3].tolist()}"
+    ref = 1.0 / oracle.rms(inp.x, 1e-6)
+    # each lane sums K/64 squares in order, then six pairwise steps; sqrt and division add a few ulps
+    rel = (K / 64 + 16) * 2.0 ** -24 + 4 * 2.0 ** -24
+    err = np.abs(to_f64(rs) - ref) / ref
+    assert np.all(err <= rel), f"1/RMS off by {err.max():.2e} > {rel:.2e}"
+
+
+def _run_ws(fn, M, K, N, T, swiglu, seed, bad_idx=False, workspace=None):
+    inp = W.random_inputs(M, K, N, "bf16", seed=seed, swiglu=swiglu)
+    scale, shift, idx = W.adaln_tables(T, K, M, seed=seed + 1)
+    if bad_idx and M >= 3:
+        idx[0], idx[-1] = -1, T
+    x, g = to_dev(inp.x, "bf16"), to_dev(inp.g, "bf16")
+    sc, sh = to_dev(scale, "bf16"), to_dev(shift, "bf16")
+    idx_d = _idx_dev(idx)
+    Wg = to_dev(inp.W, "bf16")
+    Pg, bg = fn.fold_weights(g, Wg), fn.adaln_shift_bias(sh, Wg)
+    scale0 = np.vstack([scale, np.zeros((1, K), np.float32)])
+    shift0 = np.vstack([shift, np.zeros((1, K), np.float32)])
+    idx0 = np.where((idx < 0) | (idx >= T), T, idx)
+    if swiglu:
+        Wu = to_dev(inp.W_up, "bf16")
+        Pu, bu = fn.fold_weights(g, Wu), fn.adaln_shift_bias(sh, Wu)
+        y = fn.norm_proj_swiglu_adaln_ws(x, sc, idx_d, Pg, bg, Pu, bu, inp.call.eps, workspace=workspace)
+        ref = oracle.adaln_norm_proj_swiglu(inp.x, inp.g, scale0, shift0, idx0, inp.W, inp.W_up, inp.call.eps)
+    else:
+        y = fn.norm_proj_adaln_ws(x, sc, idx_d, Pg, bg, inp.call.eps, workspace=workspace)
+        ref = oracle.adaln_norm_proj(inp.x, inp.g, scale0, shift0, idx0, inp.W, inp.call.eps)
+    return to_f64(y), ref, _bound(inp, scale0, shift0, idx0, swiglu, ref)
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("M,K,N,T", [(65, 256, 160, 2), (130, 520, 33, 3), (300, 1032, 530, 5), (257, 264, 1100, 64),
+                                     (520, 4104, 270, 63), (200, 1032, 300, 500), (777, 264, 48, 1)])
+def test_adaln_ws_parity(gpu_lib, swiglu, M, K, N, T):
+    """Ragged row, column and k tails through both kernels, any table size."""
+    y, ref, bound = _run_ws(gpu_lib, M, K, N, T, swiglu, seed=M * 5 + K + N + T, bad_idx=True)
+    _check(y, ref, bound, f"{'swiglu' if swiglu else 'proj'} adaln two-launch {M}x{K}x{N} T={T}")
+
+
+def test_adaln_ws_workspace_reuse(gpu_lib):
+    """One workspace for two calls in a row, the second with fewer rows
+    (its contents from the first call are overwritten, not trusted)."""
+    import torch
+    fn = gpu_lib
+    ws = torch.empty((fn.adaln_workspace_bytes(300, 1032),), dtype=torch.uint8, device="cuda")
+    for M in (300, 97):
+        y, ref, bound = _run_ws(fn, M, 1032, 270, 7, True, seed=M, workspace=ws)
+        _check(y, ref, bound, f"swiglu adaln two-launch, shared workspace, M={M}")
+
+
+def test_adaln_ws_up_to_64_rows_is_the_one_launch_call(gpu_lib):
+    """Up to 64 rows the two-launch entry runs the one-launch kernel: the
+    same bits, with no workspace."""
+    import torch
+    fn = gpu_lib
+    M, K, N, T = 64, 1032, 530, 5
+    inp = W.random_inputs(M, K, N, "bf16", seed=8, swiglu=True)
+    scale, shift, idx = W.adaln_tables(T, K, M, seed=9)
+    x, g = to_dev(inp.x, "bf16"), to_dev(inp.g, "bf16")
+    sc, sh = to_dev(scale, "bf16"), to_dev(shift, "bf16")
+    Wg, Wu = to_dev(inp.W, "bf16"), to_dev(inp.W_up, "bf16")
+    Pg, Pu = fn.fold_weights(g, Wg), fn.fold_weights(g, Wu)
+    bg, bu = fn.adaln_shift_bias(sh, Wg), fn.adaln_shift_bias(sh, Wu)
+    assert fn.adaln_workspace_bytes(M, K) == 0
+    a = fn.norm_proj_swiglu_adaln_ws(x, sc, _idx_dev(idx), Pg, bg, Pu, bu, 1e-6)
+    b = fn.norm_proj_swiglu_adaln(x, sc, _idx_dev(idx), Pg, bg, Pu, bu, 1e-6)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("N,T,swiglu,rows", [(11008, 16, True, 64), (12288, 4, False, 96)])
+def test_adaln_ws_prefill_sampled_rows(gpu_lib, N, T, swiglu, rows):
+    """The full prefill shapes through the two-launch form (FFN 4096 x 4096
+    -> 2 x 11008 with 16 table rows; QKV 4096 x 4096 -> 12288 with 4), the
+    oracle on a seeded sample of rows."""
+    import torch
+    fn = gpu_lib
+    M, K = 4096, 4096
+    inp = W.random_inputs(M, K, N, "bf16", seed=43, swiglu=swiglu)
+    scale, shift, idx = W.adaln_tables(T, K, M, seed=44)
+    x, g = to_dev(inp.x, "bf16"), to_dev(inp.g, "bf16")
+    sc, sh = to_dev(scale, "bf16"), to_dev(shift, "bf16")
+    Wg = to_dev(inp.W, "bf16")
+    if swiglu:
+        Wu = to_dev(inp.W_up, "bf16")
+        y = fn.norm_proj_swiglu_adaln_ws(x, sc, _idx_dev(idx), fn.fold_weights(g, Wg), fn.adaln_shift_bias(sh, Wg),
+                                         fn.fold_weights(g, Wu), fn.adaln_shift_bias(sh, Wu), 1e-6)
+    else:
+        y = fn.norm_proj_adaln_ws(x, sc, _idx_dev(idx), fn.fold_weights(g, Wg), fn.adaln_shift_bias(sh, Wg), 1e-6)
+    torch.cuda.synchronize()
+    pick = W.sample_indices(M, rows, seed=8)
+    sub = W.random_inputs(1, K, N, "bf16", seed=43, swiglu=swiglu)
+    sub.x, sub.g, sub.W, sub.W_up = inp.x[pick], inp.g, inp.W, inp.W_up
+    if swiglu:
+        ref = oracle.adaln_norm_proj_swiglu(sub.x, sub.g, scale, shift, idx[pick], sub.W, sub.W_up, 1e-6)
+    else:
+        ref = oracle.adaln_norm_proj(sub.x, sub.g, scale, shift, idx[pick], sub.W, 1e-6)
+    bound = _bound(sub, scale, shift, idx[pick], swiglu, ref)
+    _check(to_f64(y)[pick], ref, bound, f"{'swiglu' if swiglu else 'proj'} adaln two-launch prefill rows")

@@ -66,12 +66,34 @@ MUTANTS = {
     "adaln index ignored": ("adaln_modulate", lambda x, g, sc, sh, idx, eps: O.rmsnorm(x, g, eps)
                             * (1 + np.asarray(sc, float)[0]) + np.asarray(sh, float)[0]),
     "adaln bias on the folded weights": ("adaln_shift_bias", lambda sh, W: np.asarray(sh, float) @ np.asarray(W, float) * 1.5),
+    "adaln operand without the one": ("adaln_operand", lambda x, sc, idx: O.round_to_bf16(
+        np.asarray(x, float) * np.asarray(sc, float)[np.clip(np.asarray(idx), 0, np.asarray(sc).shape[0] - 1)])),
+    "adaln operand ties away": ("adaln_operand", lambda x, sc, idx: _operand_with(x, sc, idx, lambda v: np.floor(v + 0.5))),
+    "adaln operand truncated": ("adaln_operand", lambda x, sc, idx: _operand_with(x, sc, idx, np.trunc)),
+    "adaln operand index clamped": ("adaln_operand", lambda x, sc, idx: _operand_ref(
+        x, sc, np.clip(np.asarray(idx), 0, np.asarray(sc).shape[0] - 1))),
     "q8 scale inverted": ("dequantize_row_blocks", lambda c, s, block=16: _deq_ref(c, 1.0 / np.asarray(s, float),
                                                                                  block)),
 }
 
 
 _encode_ref = O.e4m3_encode
+_operand_ref = O.adaln_operand
+
+
+def _operand_with(x, sc, idx, rnd):
+    """The AdaLN operand with another rounding of the positive magnitude to
+    the bf16 grid (8 significant bits)."""
+    x = np.asarray(x, float)
+    sc = np.asarray(sc, float)
+    i = np.asarray(idx)
+    ok = (i >= 0) & (i < sc.shape[0])
+    v = x + x * np.where(ok[:, None], sc[np.where(ok, i, 0)], 0.0)
+    mag = np.abs(v)
+    with np.errstate(all="ignore"):
+        _, e = np.frexp(mag)
+        q = np.ldexp(rnd(np.ldexp(mag, 8 - e)), e - 8)
+    return np.copysign(q, v)
 _decode_ref = O.e4m3_decode
 _quantize_ref = O.quantize_e4m3_columns
 
