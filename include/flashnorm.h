@@ -308,10 +308,12 @@ fn_status fn_norm_proj_swiglu_adaln(const void* x, const void* scale, const int*
  * shapes. */
 const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu);
 
-/* Two-launch form of the two AdaLN calls above, for many rows.  A pre-pass
- * (fn_adaln_modulate below) writes the modulated operand and 1/RMS of each
- * raw row into a caller workspace; the prefill kernel then projects that
- * operand and applies the deferred 1/RMS and the bias rows in its epilogue.
+/* Two-launch form of the two AdaLN calls above, for more than 16 rows.  A
+ * pre-pass (fn_adaln_modulate below) writes the modulated operand and 1/RMS
+ * of each raw row into a caller workspace; the plain projection kernel of the
+ * row count (the LDS-shared-x decode kernel up to 64 rows, the prefill kernel
+ * above) then projects that operand and applies the deferred 1/RMS and the
+ * bias rows in its epilogue.
  * The one-launch kernels modulate x once per output tile (every workgroup
  * along N repeats it); here it is done once per row, and any T is served.
  * The page's own AdaLN FC1 kernel runs as two launches as well
@@ -321,9 +323,9 @@ const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int
  *   bytes, 256-byte aligned, overlapping no other argument.  The call writes
  *   it and reads it back in stream order; its contents afterwards are
  *   unspecified, and calls in flight at the same time need separate
- *   workspaces.  For M <= 64 the call is the one-launch call (the
+ *   workspaces.  For M <= 16 the call is the one-launch call (the
  *   workspace is not touched and may be NULL, with workspace_bytes 0).
- * Errors as the one-launch calls, plus FN_ERR_WORKSPACE (M > 64 and the
+ * Errors as the one-launch calls, plus FN_ERR_WORKSPACE (M > 16 and the
  * workspace NULL, misaligned or smaller than needed) and FN_ERR_ALIAS (the
  * workspace overlaps an argument). */
 fn_status fn_norm_proj_adaln_ws(const void* x, const void* scale, const int* idx, const void* W_packed,
@@ -335,12 +337,12 @@ fn_status fn_norm_proj_swiglu_adaln_ws(const void* x, const void* scale, const i
                                        void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes the two calls above need: the operand (M*K bf16) and one
- * fp32 per row, each rounded up to 256 bytes; 0 when M <= 64 (one launch)
+ * fp32 per row, each rounded up to 256 bytes; 0 when M <= 16 (one launch)
  * or when M or K is outside the limits. */
 int64_t fn_adaln_workspace_bytes(int64_t M, int64_t K);
 
 /* Projection kernel instance of the two-launch calls (their one-launch
- * kernel for M <= 64); "invalid" for bad shapes. */
+ * kernel for M <= 16); "invalid" for bad shapes. */
 const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu);
 
 /* The pre-pass alone: for each row m, with s = scale[idx[m]] (all zero when

@@ -28,8 +28,9 @@ __global__ __launch_bounds__(256) void adaln_bias_kernel(const T* __restrict__ s
 // projection then runs once on u and applies the deferred 1/RMS from rs, so
 // the modulation is done once per row instead of once per output tile
 // ([FlashInfer #5521] "Fused Kernel on SM120": the page's own AdaLN FC1 also
-// runs as two launches).  Four 16-byte chunks per lane are loaded before any
-// is used, so each wave keeps 4 KiB of reads in flight.
+// runs as two launches).  Eight 16-byte chunks per lane are loaded before
+// any is used (a 4096-wide row in one round trip), so each wave keeps 8 KiB
+// of reads in flight.
 __global__ __launch_bounds__(256) void adaln_modulate_kernel(const u32x4* __restrict__ x,
                                                              const u32x4* __restrict__ scale,
                                                              const int* __restrict__ idx, int T,
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(256) void adaln_modulate_kernel(const u32x4* __rest
   const u32x4* xr = x + (size_t)row * K8;
   const u32x4* sr = scale + (size_t)(tv ? t : 0) * K8;
   u32x4* ur = u + (size_t)row * K8;
-  constexpr int B = 4;
+  constexpr int B = 8;
   float ss = 0.f;
   for (int c0 = lane; c0 < K8; c0 += B * kWave) {
     u32x4 xv[B], sv[B];

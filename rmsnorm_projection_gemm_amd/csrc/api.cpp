@@ -211,7 +211,7 @@ fn_status adaln_common(const void* x, const void* scale, const int* idx, const v
                     plan.name);
 }
 
-constexpr int64_t kAdalnOneLaunchRows = 64;   // up to here the _ws calls run the one-launch kernel
+constexpr int64_t kAdalnOneLaunchRows = 16;   // up to here the _ws calls run the one-launch kernel
 
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
@@ -241,6 +241,12 @@ fn_status adaln_ws_common(const void* x, const void* scale, const int* idx, cons
   FN_TRY(hip_status(fn::launch_adaln_modulate(x, scale, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
                     "adaln_modulate"));
   const fn::AdalnArgs ad{nullptr, idx, bg, swiglu ? bu : nullptr, (int)T};
+  if (M <= 64) {
+    const fn::FusedPlan plan = fn::plan_decode_premod(M, N, swiglu);
+    return hip_status(fn::launch_decode_premod(plan, u, rs, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, ad,
+                                               stream),
+                      plan.name);
+  }
   const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, false, true);
   return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, ad,
                                               stream),
@@ -505,7 +511,8 @@ fn_status fn_norm_proj_swiglu_adaln_ws(const void* x, const void* scale, const i
 
 const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
-  if (M > kAdalnOneLaunchRows) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true).name;
+  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true).name;
+  if (M > kAdalnOneLaunchRows) return fn::plan_decode_premod(M, N, swiglu != 0).name;
   return fn_kernel_name_adaln(M, K, N, T, swiglu);
 }
 

@@ -62,6 +62,7 @@ struct DecodeXArgs {
   const float* bg;   // AdaLN: bias rows shift @ W [T, N] (gate for SwiGLU)
   const float* bu;   // AdaLN: bias rows of W_up
   int T;             // AdaLN: table rows
+  const float* rs;   // EX: 1/RMS of each row [M], from the AdaLN pre-pass
 };
 
 
@@ -101,8 +102,12 @@ __device__ inline void decode_e4m3x16(u32x4 w, u32x4& lo, u32x4& hi) {
 // x * (1 + scale[idx]) while the sum of squares stays on x, and the epilogue
 // adds the row's bias row.  TSL (AdaLN tables of fewer than 8 * NWV rows):
 // each stage stages the table's slice (all T rows, the stage's 64 k values,
-// eight rows per wave) instead of one scale row per x row.
-template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false, int NS = 4, bool TSL = false>
+// eight rows per wave) instead of one scale row per x row.  EX: the
+// projection half of the two-launch AdaLN form -- x is the operand the
+// pre-pass already modulated, 1/RMS of each raw row comes from a.rs (no Gram
+// blocks) and the epilogue adds the row's bias row.
+template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false, int NS = 4, bool TSL = false,
+          bool EX = false>
 __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   static_assert(NS >= 3 && NS <= 6, "LDS ring slots");
   constexpr int D = NS - 1;                // stages in flight
@@ -136,7 +141,9 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   // always, bf16 output when each wave owns one column block.
   constexpr bool STAGE = Q8 || (NC == 1 && NWV <= NS);
   static_assert(!STAGE || (NC == 1 && NWV <= NS && 16 * MF * 16 * 4 <= SLOT), "staging fits a ring slot");
-  static_assert(!AD || STAGE, "the AdaLN bias is added in the staged epilogue");
+  static_assert(!EX || (!AD && NC == 1 && !F8 && !Q8), "pre-modulated operand: bf16, one column block per wave");
+  constexpr bool BIAS = AD || EX;
+  static_assert(!BIAS || STAGE, "the AdaLN bias is added in the staged epilogue");
   static_assert(U % 2 == 0, "each x load moves two k-blocks of 8 rows");
   static_assert(D * LPW < 64, "vmcnt range");
   static_assert(NS * (SLOT + (AD ? MSLOT + TSLOT : 0)) + NWV * XPW * 16 * 4 <= 160 * 1024, "LDS budget");
@@ -199,7 +206,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) bias[i][e][m] = 0.f;
-  if constexpr (AD) {
+  if constexpr (BIAS) {
     const int col = nb0 * 16 + lrow;
 #pragma unroll
     for (int i = 0; i < MF; ++i)
@@ -363,8 +370,10 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < MF; ++i) xv[u][i] = *reinterpret_cast<const u32x4*>((AD_INPLACE ? mod_ptr(s) : base) + x_at(u, i));
+    if constexpr (!EX) {
 #pragma unroll
-    for (int j = 0; j < XPW; ++j) xg[j] = *reinterpret_cast<const u32x4*>(base + frag_at(w + NWV * j));
+      for (int j = 0; j < XPW; ++j) xg[j] = *reinterpret_cast<const u32x4*>(base + frag_at(w + NWV * j));
+    }
     // AdaLN, one row block: the few operand chunks are modulated in
     // registers, after the next stage's loads are issued
     u32x4 sv[AD && !AD_INPLACE ? U : 1][AD && !AD_INPLACE ? MF : 1];
@@ -405,8 +414,10 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 #pragma unroll
         for (int c = 0; c < NST; ++c) acc[c][i] = mfma_chunk<__bf16>(xa, bw[u][c], acc[c][i]);
       }
+    if constexpr (!EX) {
 #pragma unroll
-    for (int j = 0; j < XPW; ++j) gram[j] = mfma_chunk<__bf16>(xg[j], xg[j], gram[j]);
+      for (int j = 0; j < XPW; ++j) gram[j] = mfma_chunk<__bf16>(xg[j], xg[j], gram[j]);
+    }
   };
 
   // the loop's load order: W', x, then (TSL) the slice of the stage after;
@@ -436,7 +447,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 
   // Accumulator element e of lane l is row 4*(l/16) + e, column l%16 of its
   // 16x16 tile, so the Gram diagonal sits in lanes with (l%16)/4 == l/16.
-  if ((lrow >> 2) == lgrp) {
+  if (!EX && (lrow >> 2) == lgrp) {
     const int e = lrow & 3;
 #pragma unroll
     for (int j = 0; j < XPW; ++j)
@@ -446,14 +457,19 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   // 1/RMS once per row: thread t sums row t's Gram diagonals (accumulator j
   // of wave v holds fragment q = v + NWV*j, row block q % MF)
   if (threadIdx.x < MF * 16) {
-    const int i = threadIdx.x / 16, rr = threadIdx.x % 16;
-    float ss = 0.f;
+    if constexpr (EX) {
+      const int row = m0 + (int)threadIdx.x;
+      inv_s[threadIdx.x] = row < a.M ? a.rs[row] : 0.f;
+    } else {
+      const int i = threadIdx.x / 16, rr = threadIdx.x % 16;
+      float ss = 0.f;
 #pragma unroll
-    for (int v = 0; v < NWV; ++v)
+      for (int v = 0; v < NWV; ++v)
 #pragma unroll
-      for (int j = 0; j < XPW; ++j)
-        if (v + NWV * j < XF && (v + NWV * j) % MF == i) ss += ssp[v][j][rr];
-    inv_s[threadIdx.x] = inv_rms(ss, (float)a.K, a.eps);
+        for (int j = 0; j < XPW; ++j)
+          if (v + NWV * j < XF && (v + NWV * j) % MF == i) ss += ssp[v][j][rr];
+      inv_s[threadIdx.x] = inv_rms(ss, (float)a.K, a.eps);
+    }
   }
   __syncthreads();
 
@@ -474,8 +490,8 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
         const float iu = F8 && SW ? scol[NC + j] * inv : inv;
         if constexpr (STAGE) {
           // staged in this wave's (now idle) ring slot as [row][16 columns]
-          const float ga = AD ? fmaf(acc[j][i][e], ig, bias[i][e][0]) : acc[j][i][e] * ig;
-          const float val = SW ? silu_times(ga, AD ? fmaf(acc[NC + j][i][e], iu, bias[i][e][NMAT - 1])
+          const float ga = BIAS ? fmaf(acc[j][i][e], ig, bias[i][e][0]) : acc[j][i][e] * ig;
+          const float val = SW ? silu_times(ga, BIAS ? fmaf(acc[NC + j][i][e], iu, bias[i][e][NMAT - 1])
                                                    : acc[NC + j][i][e] * iu)
                                : ga;
           reinterpret_cast<float*>(slot_ptr(w))[(16 * i + rr) * 16 + lrow] = val;
@@ -568,8 +584,9 @@ inline hipError_t launch_decode_x_instance(const DecodeXInstance& d, const void*
                                            void* y, int M, int K, int N, float eps, hipStream_t stream,
                                            const float* sg = nullptr, const float* su = nullptr,
                                            uint8_t* q = nullptr, float* qs = nullptr,
-                                           const AdalnArgs* ad = nullptr) {
+                                           const AdalnArgs* ad = nullptr, const float* rs = nullptr) {
   DecodeXArgs a;
+  a.rs = rs;
   a.sg = sg;
   a.su = su;
   a.q = q;
@@ -723,6 +740,32 @@ hipError_t launch_adaln(const FusedPlan& p, const void* x, const void* wg, const
                                                              : find_instance(kDecodeAd, p.mf, wu != nullptr);
   if (d == nullptr) return hipErrorInvalidValue;
   return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream, nullptr, nullptr, nullptr, nullptr, &ad);
+}
+
+// Two-launch AdaLN, 17..64 rows: the plain 32- and 64-row rungs on the
+// operand the pre-pass modulated, 1/RMS from the pre-pass, bias rows added in
+// the epilogue (no Gram blocks).
+#define FN_DECODE_XE(MF, SW, NS, NAME)                                                                          \
+  DecodeXInstance {                                                                                            \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, 3, SW, 2, false, false, false, NS, false, true>), MF, 1, \
+        3, 2, SW, false, false, NAME                                                                           \
+  }
+static const DecodeXInstance kDecodeEx[] = {
+    FN_DECODE_XE(2, false, 5, "decode_premod_bf16_m32_xlds_w3_u2_s5"),
+    FN_DECODE_XE(4, false, 5, "decode_premod_bf16_m64_xlds_w3_u2_s5"),
+    FN_DECODE_XE(2, true, 4, "decode_swiglu_premod_bf16_m32_xlds_w3_u2"),
+    FN_DECODE_XE(4, true, 4, "decode_swiglu_premod_bf16_m64_xlds_w3_u2"),
+};
+
+FusedPlan plan_decode_premod(int64_t M, int64_t N, bool swiglu) {
+  return plan_of(find_instance(kDecodeEx, M <= 32 ? 2 : 4, swiglu), 9, M, N);
+}
+
+hipError_t launch_decode_premod(const FusedPlan& p, const void* u, const float* rs, const void* wg, const void* wu,
+                                void* y, int M, int K, int N, const AdalnArgs& ad, hipStream_t stream) {
+  const DecodeXInstance* d = find_instance(kDecodeEx, p.mf, wu != nullptr);
+  if (d == nullptr || M > 16 * d->mf) return hipErrorInvalidValue;
+  return launch_decode_x_instance(*d, u, wg, wu, y, M, K, N, 0.f, stream, nullptr, nullptr, nullptr, nullptr, &ad, rs);
 }
 
 // SwiGLU with fp8 output, rows up to 64 (bf16 weights; larger M goes to the

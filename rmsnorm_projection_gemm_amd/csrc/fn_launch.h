@@ -17,7 +17,8 @@ struct FusedPlan {
                       // 3 = fp8 weights (x in LDS, rows tiled over grid.y),
                       // 4 = SwiGLU with fp8 output (x in LDS), 5 = the same on the prefill kernel,
                       // 6 = AdaLN prologue (x and scale rows in LDS), 7 = AdaLN on the prefill kernel,
-                      // 8 = prefill on an operand modulated by the AdaLN pre-pass
+                      // 8 = prefill on an operand modulated by the AdaLN pre-pass,
+                      // 9 = the same on the LDS-shared-x decode kernel (17..64 rows)
   int mf;             // 16-row fragments per workgroup (decode)
   int nf;             // 16-column fragments per workgroup (decode)
   int waves;          // waves per workgroup
@@ -67,6 +68,10 @@ hipError_t launch_adaln_modulate(const void* x, const void* scale, const int* id
 hipError_t launch_prefill_premod(const FusedPlan& plan, const void* u, const float* rs, const void* wg,
                                  const void* wu, void* y, int M, int K, int N, const AdalnArgs& ad,
                                  hipStream_t stream);
+FusedPlan plan_decode_premod(int64_t M, int64_t N, bool swiglu);   // 17..64 rows
+hipError_t launch_decode_premod(const FusedPlan& plan, const void* u, const float* rs, const void* wg,
+                                const void* wu, void* y, int M, int K, int N, const AdalnArgs& ad,
+                                hipStream_t stream);
 
 hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
                        int K, int N, hipStream_t stream);

@@ -362,7 +362,7 @@ def test_adaln_swiglu_bias_and_names(lib):
 WORKSPACE = 8
 
 
-def _adw(lib, x=0x1000, sc=0x10000, idx=0x18000, w=0x20000, b=0x30000, y=0x40000, M=100, K=16, N=16, T=2, eps=1e-6,
+def _adw(lib, x=0x1000, sc=0x10000, idx=0x18000, w=0x20000, b=0x30000, y=0x40000, M=40, K=16, N=16, T=2, eps=1e-6,
          ws=0x100000, wsb=1 << 20):
     return lib.fn_norm_proj_adaln_ws(x, sc, idx, w, b, y, M, K, N, T, eps, ws, wsb, None)
 
@@ -370,7 +370,7 @@ def _adw(lib, x=0x1000, sc=0x10000, idx=0x18000, w=0x20000, b=0x30000, y=0x40000
 @pytest.mark.parametrize("kwargs,status,needle", [
     (dict(ws=None), WORKSPACE, "workspace is NULL"),
     (dict(ws=0x100080), WORKSPACE, "256-byte"),
-    (dict(wsb=2048), WORKSPACE, "workspace_bytes=2048"),
+    (dict(wsb=1024), WORKSPACE, "workspace_bytes=1024"),
     (dict(ws=0x40000), ALIAS, "workspace overlaps"),
     (dict(ws=0x1000 - 256), ALIAS, "workspace overlaps"),
     # the one-launch checks come first
@@ -387,14 +387,17 @@ def test_norm_proj_adaln_ws_rejects(lib, kwargs, status, needle):
 
 
 def test_adaln_ws_sizes_and_names(lib):
-    # operand M*K bf16, then one fp32 per row, each rounded up to 256 bytes; none up to 64 rows
-    assert lib.fn_adaln_workspace_bytes(64, 4096) == 0
+    # operand M*K bf16, then one fp32 per row, each rounded up to 256 bytes; none up to 16 rows
+    assert lib.fn_adaln_workspace_bytes(16, 4096) == 0
+    assert lib.fn_adaln_workspace_bytes(17, 8) == 512 + 256
     assert lib.fn_adaln_workspace_bytes(65, 8) == 1280 + 512
     assert lib.fn_adaln_workspace_bytes(4096, 4096) == 4096 * 4096 * 2 + 4096 * 4
     assert lib.fn_adaln_workspace_bytes(100, 12) == 0 and lib.fn_adaln_workspace_bytes(-1, 16) == 0
     assert lib.fn_kernel_name_adaln_ws(4096, 4096, 12288, 4, 0).decode() == "prefill_premod_bf16_256x256_w4x2_xl"
     assert lib.fn_kernel_name_adaln_ws(65, 4096, 11008, 500, 1).decode() == "prefill_swiglu_premod_bf16_256x128_w4x2_xl"
-    assert lib.fn_kernel_name_adaln_ws(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_adaln_bf16_m64_xlds_w3_u2_tab"
+    assert lib.fn_kernel_name_adaln_ws(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_premod_bf16_m64_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln_ws(17, 4096, 12288, 500, 0).decode() == "decode_premod_bf16_m32_xlds_w3_u2_s5"
+    assert lib.fn_kernel_name_adaln_ws(16, 4096, 12288, 4, 0).decode() == "decode_adaln_bf16_m16_xlds_w3_u2_s5"
     assert lib.fn_kernel_name_adaln_ws(0, 4096, 16, 4, 0) == b"invalid"
     sw = lib.fn_norm_proj_swiglu_adaln_ws
     # SwiGLU: missing up operands, a short workspace, and the empty call (nothing read)

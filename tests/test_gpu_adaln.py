@@ -234,10 +234,15 @@ def _run_ws(fn, M, K, N, T, swiglu, seed, bad_idx=False, workspace=None):
 
 
 @pytest.mark.parametrize("swiglu", [False, True])
-@pytest.mark.parametrize("M,K,N,T", [(65, 256, 160, 2), (130, 520, 33, 3), (300, 1032, 530, 5), (257, 264, 1100, 64),
-                                     (520, 4104, 270, 63), (200, 1032, 300, 500), (777, 264, 48, 1)])
+@pytest.mark.parametrize("M,K,N,T", [
+    # 17..64 rows: the decode kernel on the pre-modulated operand
+    (17, 1032, 270, 23), (33, 4104, 530, 100), (40, 1032, 270, 4), (64, 264, 1100, 3), (64, 4096, 11008, 4),
+    # above: the prefill kernel
+    (65, 256, 160, 2), (130, 520, 33, 3), (300, 1032, 530, 5), (257, 264, 1100, 64),
+    (520, 4104, 270, 63), (200, 1032, 300, 500), (777, 264, 48, 1)])
 def test_adaln_ws_parity(gpu_lib, swiglu, M, K, N, T):
-    """Ragged row, column and k tails through both kernels, any table size."""
+    """Ragged row, column and k tails through the pre-pass and both
+    projection kernels, any table size."""
     y, ref, bound = _run_ws(gpu_lib, M, K, N, T, swiglu, seed=M * 5 + K + N + T, bad_idx=True)
     _check(y, ref, bound, f"{'swiglu' if swiglu else 'proj'} adaln two-launch {M}x{K}x{N} T={T}")
 
@@ -253,12 +258,12 @@ def test_adaln_ws_workspace_reuse(gpu_lib):
         _check(y, ref, bound, f"swiglu adaln two-launch, shared workspace, M={M}")
 
 
-def test_adaln_ws_up_to_64_rows_is_the_one_launch_call(gpu_lib):
-    """Up to 64 rows the two-launch entry runs the one-launch kernel: the
+def test_adaln_ws_up_to_16_rows_is_the_one_launch_call(gpu_lib):
+    """Up to 16 rows the two-launch entry runs the one-launch kernel: the
     same bits, with no workspace."""
     import torch
     fn = gpu_lib
-    M, K, N, T = 64, 1032, 530, 5
+    M, K, N, T = 16, 1032, 530, 5
     inp = W.random_inputs(M, K, N, "bf16", seed=8, swiglu=True)
     scale, shift, idx = W.adaln_tables(T, K, M, seed=9)
     x, g = to_dev(inp.x, "bf16"), to_dev(inp.g, "bf16")

@@ -112,7 +112,8 @@ def test_adaln_repeatable(gpu_lib, M, N, T, swiglu):
     _repeat(call, lambda y: [y])
 
 
-@pytest.mark.parametrize("M,N,T,swiglu", [(4096, 12288, 4, False), (4096, 11008, 100, True), (1000, 4096, 7, False)])
+@pytest.mark.parametrize("M,N,T,swiglu", [(4096, 12288, 4, False), (4096, 11008, 100, True), (1000, 4096, 7, False),
+                                          (64, 11008, 4, True), (32, 12288, 30, False)])
 def test_adaln_two_launch_repeatable(gpu_lib, M, N, T, swiglu):
     import torch
     fn = gpu_lib
