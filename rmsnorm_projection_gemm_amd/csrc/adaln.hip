@@ -1,4 +1,7 @@
-// AdaLN bias rows, offline: bias[t][n] = sum_k shift[t][k] * W[k][n] with the
+// AdaLN helpers: the bias rows (offline) and the modulation pre-pass of the
+// two-launch calls.
+//
+// Bias rows: bias[t][n] = sum_k shift[t][k] * W[k][n] with the
 // unfolded W, accumulated in fp32 in k order.  With the gain folded into W'
 // and the modulation h = xhat * (1 + scale) + shift, the shift reaches the
 // output as this row of biases ([FlashInfer #5521] "Fused Kernel on SM120":
