@@ -345,6 +345,38 @@ int64_t fn_adaln_workspace_bytes(int64_t M, int64_t K);
  * kernel for M <= 16); "invalid" for bad shapes. */
 const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu);
 
+/* AdaLN with fp8 weights (fn_fold_weights_fp8: E4M3 codes, one scale per
+ * output column), in two launches for every M: the pre-pass above, then the
+ * fp8-weight decode kernel of the row count on the modulated operand, with
+ *   y[m] = s * (u[m] * q) / RMS(x[m]) + bias[idx[m]]
+ * (rows past 64 tile over the grid, each 64-row tile streaming the codes
+ * again, as in fn_norm_proj_fp8).  The pages' AdaLN FC1 kernel is an fp8
+ * kernel with pre-processed weights and scales ([FlashInfer #5521] "Fused
+ * Kernel on SM120").  bias rows come from fn_adaln_shift_bias on the
+ * unfolded bf16 W.  Arguments as fn_norm_proj_fp8 / fn_norm_proj_swiglu_fp8
+ * plus scale, idx, bias and T as in the AdaLN calls above; workspace: at
+ * least fn_adaln_fp8_workspace_bytes(M, K) bytes, 256-byte aligned,
+ * overlapping no other argument (always needed).  Errors as the calls
+ * above. */
+fn_status fn_norm_proj_adaln_fp8_ws(const void* x, const void* scale, const int* idx, const void* W8_packed,
+                                    const float* scales, const float* bias, void* y, int64_t M, int64_t K, int64_t N,
+                                    int64_t T, float eps, void* workspace, int64_t workspace_bytes,
+                                    hipStream_t stream);
+fn_status fn_norm_proj_swiglu_adaln_fp8_ws(const void* x, const void* scale, const int* idx, const void* W8_gate,
+                                           const float* s_gate, const float* bias_gate, const void* W8_up,
+                                           const float* s_up, const float* bias_up, void* out, int64_t M, int64_t K,
+                                           int64_t N, int64_t T, float eps, void* workspace, int64_t workspace_bytes,
+                                           hipStream_t stream);
+
+/* Workspace bytes of the two fp8 calls above (the same layout as
+ * fn_adaln_workspace_bytes, needed for every M >= 1); 0 for M < 1 or M, K
+ * outside the limits. */
+int64_t fn_adaln_fp8_workspace_bytes(int64_t M, int64_t K);
+
+/* Projection kernel instance of the fp8 AdaLN calls; "invalid" for bad
+ * shapes. */
+const char* fn_kernel_name_adaln_fp8(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu);
+
 /* The pre-pass alone: for each row m, with s = scale[idx[m]] (all zero when
  * idx[m] is outside [0, T)),
  *   u[m][k] = bf16_rne(fp32(x[m][k] + x[m][k] * s[k]))   (one fp32 rounding)

@@ -381,6 +381,26 @@ def adaln_norm_proj_folded(x, W_folded, scale, bias, idx, eps: float) -> np.ndar
     return ((x * (1.0 + _f64(scale)[i])) @ _f64(W_folded)) / rms(x, eps)[:, None] + _f64(bias)[i]
 
 
+def adaln_norm_proj_fp8(x, codes, s, scale, bias, idx, eps: float) -> np.ndarray:
+    """AdaLN with E4M3 weights (the page's AdaLN FC1 kernel takes
+    pre-processed fp8 weights with their scales, [FlashInfer #5521] "Fused
+    Kernel on SM120"): ((x * (1 + scale[idx])) @ (s[n] * q)) / r + bias[idx]
+    -- the folded/deferred AdaLN form with the quantised weights in place of
+    W'; bias = shift @ W from the unfolded weights."""
+    x = _f64(x)
+    i = np.asarray(idx, dtype=np.int64)
+    Wq = e4m3_decode(codes) * _f64(s)[None, :]
+    return ((x * (1.0 + _f64(scale)[i])) @ Wq) / rms(x, eps)[:, None] + _f64(bias)[i]
+
+
+def adaln_norm_proj_swiglu_fp8(x, codes_gate, s_gate, codes_up, s_up, scale, bias_gate, bias_up, idx,
+                               eps: float) -> np.ndarray:
+    """SwiGLU variant: a, b as in adaln_norm_proj_fp8, out = silu(a) * b."""
+    a = adaln_norm_proj_fp8(x, codes_gate, s_gate, scale, bias_gate, idx, eps)
+    b = adaln_norm_proj_fp8(x, codes_up, s_up, scale, bias_up, idx, eps)
+    return silu(a) * b
+
+
 def adaln_operand(x, scale, idx) -> np.ndarray:
     """The modulated matrix-core operand of the AdaLN path, as the kernels
     form it: x + x * scale[idx[m]] rounded once to float32, then to bf16 with
@@ -403,4 +423,5 @@ __all__ = ["rms", "rmsnorm", "norm_proj", "silu", "norm_proj_swiglu", "fold_exac
            "quantize_e4m3_columns", "fold_weights_fp8", "norm_proj_fp8", "norm_proj_swiglu_fp8",
            "Q8_BLOCK", "quantize_e4m3_row_blocks", "dequantize_row_blocks", "norm_proj_swiglu_q8",
            "norm_proj_swiglu_fp8_q8", "adaln_modulate", "adaln_norm_proj", "adaln_norm_proj_swiglu",
-           "adaln_shift_bias", "adaln_norm_proj_folded", "adaln_operand"]
+           "adaln_shift_bias", "adaln_norm_proj_folded", "adaln_operand", "adaln_norm_proj_fp8",
+           "adaln_norm_proj_swiglu_fp8"]

@@ -86,6 +86,11 @@ def load():
         "fn_adaln_workspace_bytes": (i64, [i64, i64]),
         "fn_kernel_name_adaln_ws": (ctypes.c_char_p, [i64, i64, i64, i64, i32]),
         "fn_adaln_modulate": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, f32, vp]),
+        "fn_norm_proj_adaln_fp8_ws": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp, i64, vp]),
+        "fn_norm_proj_swiglu_adaln_fp8_ws": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32,
+                                                   vp, i64, vp]),
+        "fn_adaln_fp8_workspace_bytes": (i64, [i64, i64]),
+        "fn_kernel_name_adaln_fp8": (ctypes.c_char_p, [i64, i64, i64, i64, i32]),
         "fn_step_create": (i32, [vp, i64, ctypes.POINTER(vp)]),
         "fn_step_launch": (i32, [vp, vp]),
         "fn_step_num_kernels": (i64, [vp]),
@@ -504,6 +509,68 @@ def kernel_name_adaln_ws(M: int, K: int, N: int, T: int, swiglu: bool) -> str:
     return load().fn_kernel_name_adaln_ws(M, K, N, T, int(swiglu)).decode()
 
 
+def adaln_fp8_workspace_bytes(M: int, K: int) -> int:
+    """Workspace bytes of the fp8-weight AdaLN calls (needed for every M)."""
+    return int(load().fn_adaln_fp8_workspace_bytes(M, K))
+
+
+def _check_adaln_fp8(x, scale, idx, P: PackedFp8, bias):
+    torch = _torch()
+    _check_x_fp8(x, P)
+    for name, t in (("scale", scale), ("idx", idx), ("bias", bias)):
+        _need_cuda(name, t)
+    if scale.dim() != 2 or scale.shape[1] != P.K or scale.dtype != torch.bfloat16:
+        raise ValueError(f"scale must be [T, {P.K}] bf16")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (x.shape[0],):
+        raise ValueError(f"idx must be [{x.shape[0]}] int32")
+    if tuple(bias.shape) != (scale.shape[0], P.N) or bias.dtype != torch.float32:
+        raise ValueError(f"bias must be [{scale.shape[0]}, {P.N}] float32")
+
+
+def _workspace_fp8(workspace, M: int, K: int, like):
+    if workspace is None:
+        n = adaln_fp8_workspace_bytes(M, K)
+        if n == 0:
+            return None, 0
+        workspace = _torch().empty((n,), dtype=_torch().uint8, device=like.device)
+    _need_cuda("workspace", workspace)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def norm_proj_adaln_fp8_ws(x, scale, idx, P: PackedFp8, bias, eps: float = 1e-6, out=None, workspace=None):
+    """AdaLN with E4M3 weights, two launches (the pre-pass into a workspace,
+    allocated here when not given, then the fp8 kernel)."""
+    _check_adaln_fp8(x, scale, idx, P, bias)
+    M, N = x.shape[0], P.N
+    y = _out(out, M, N, x)
+    ws, nbytes = _workspace_fp8(workspace, M, P.K, x)
+    _check(load().fn_norm_proj_adaln_fp8_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), P.data.data_ptr(),
+                                            P.scales.data_ptr(), bias.data_ptr(), y.data_ptr(), M, P.K, N,
+                                            scale.shape[0], eps, None if ws is None else ws.data_ptr(), nbytes,
+                                            _stream(x)))
+    return y
+
+
+def norm_proj_swiglu_adaln_fp8_ws(x, scale, idx, Pg: PackedFp8, bias_g, Pu: PackedFp8, bias_u, eps: float = 1e-6,
+                                  out=None, workspace=None):
+    """SwiGLU AdaLN with E4M3 gate/up weights, two launches."""
+    _check_adaln_fp8(x, scale, idx, Pg, bias_g)
+    _check_adaln_fp8(x, scale, idx, Pu, bias_u)
+    M, N = x.shape[0], Pg.N
+    y = _out(out, M, N, x)
+    ws, nbytes = _workspace_fp8(workspace, M, Pg.K, x)
+    _check(load().fn_norm_proj_swiglu_adaln_fp8_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Pg.data.data_ptr(),
+                                                   Pg.scales.data_ptr(), bias_g.data_ptr(), Pu.data.data_ptr(),
+                                                   Pu.scales.data_ptr(), bias_u.data_ptr(), y.data_ptr(), M, Pg.K, N,
+                                                   scale.shape[0], eps, None if ws is None else ws.data_ptr(),
+                                                   nbytes, _stream(x)))
+    return y
+
+
+def kernel_name_adaln_fp8(M: int, K: int, N: int, T: int, swiglu: bool) -> str:
+    return load().fn_kernel_name_adaln_fp8(M, K, N, T, int(swiglu)).decode()
+
+
 def adaln_modulate(x, scale, idx, eps: float = 1e-6, u=None, rs=None):
     """The AdaLN pre-pass alone: (u, rs) with u = bf16(x + x * scale[idx])
     [M, K] and rs = 1/RMS(x) [M] float32."""
@@ -639,4 +706,5 @@ __all__ = ["load", "fold_weights", "norm_proj", "norm_proj_swiglu", "rmsnorm", "
            "FN_CALL_NORM_PROJ_SWIGLU_Q8", "FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8", "Q8_BLOCK", "norm_proj_swiglu_q8",
            "norm_proj_swiglu_fp8_q8", "kernel_name_q8", "adaln_shift_bias", "norm_proj_adaln",
            "norm_proj_swiglu_adaln", "kernel_name_adaln", "adaln_workspace_bytes", "norm_proj_adaln_ws",
-           "norm_proj_swiglu_adaln_ws", "kernel_name_adaln_ws", "adaln_modulate"]
+           "norm_proj_swiglu_adaln_ws", "kernel_name_adaln_ws", "adaln_modulate", "adaln_fp8_workspace_bytes",
+           "norm_proj_adaln_fp8_ws", "norm_proj_swiglu_adaln_fp8_ws", "kernel_name_adaln_fp8"]

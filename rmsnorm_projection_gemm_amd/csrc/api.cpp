@@ -243,13 +243,63 @@ fn_status adaln_ws_common(const void* x, const void* scale, const int* idx, cons
   const fn::AdalnArgs ad{nullptr, idx, bg, swiglu ? bu : nullptr, (int)T};
   if (M <= 64) {
     const fn::FusedPlan plan = fn::plan_decode_premod(M, N, swiglu);
-    return hip_status(fn::launch_decode_premod(plan, u, rs, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, ad,
-                                               stream),
+    return hip_status(fn::launch_decode_premod(plan, u, rs, wg, nullptr, swiglu ? wu : nullptr, nullptr, y, (int)M,
+                                               (int)K, (int)N, ad, stream),
                       plan.name);
   }
   const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, false, true);
   return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, ad,
                                               stream),
+                    plan.name);
+}
+
+// Two-launch AdaLN with fp8 weights (E4M3 codes + column scales), every M:
+// the pre-pass, then the fp8 decode kernel on the modulated operand.
+fn_status adaln_fp8_ws_common(const void* x, const void* scale, const int* idx, const void* wg, const float* sg,
+                              const float* bg, const void* wu, const float* su, const float* bu, void* y, int64_t M,
+                              int64_t K, int64_t N, int64_t T, float eps, void* ws, int64_t ws_bytes,
+                              hipStream_t stream, bool swiglu) {
+  g_last_error[0] = '\0';
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(M, N));
+  FN_TRY(check_eps(eps));
+  if (T < 1 || T > INT32_MAX || T * K * 2 > INT32_MAX)
+    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*2 < 2^31", (long long)T);
+  if (M == 0 || N == 0) return FN_OK;
+  if (x == nullptr || scale == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, scale or idx is NULL");
+  if (wg == nullptr || sg == nullptr || bg == nullptr)
+    return fail(FN_ERR_NULL, swiglu ? "W8_gate, s_gate or bias_gate is NULL" : "W8_packed, scales or bias is NULL");
+  if (swiglu && (wu == nullptr || su == nullptr || bu == nullptr))
+    return fail(FN_ERR_NULL, "W8_up, s_up or bias_up is NULL");
+  if (y == nullptr) return fail(FN_ERR_NULL, swiglu ? "out is NULL" : "y is NULL");
+  if (!aligned(x, 16) || !aligned(scale, 16)) return fail(FN_ERR_ALIGN, "x and scale must be 16-byte aligned");
+  if (!aligned(wg, 16) || (swiglu && !aligned(wu, 16)))
+    return fail(FN_ERR_ALIGN, "packed fp8 weights must be 16-byte aligned");
+  if (!aligned(idx, 4) || !aligned(sg, 4) || !aligned(bg, 4) || (swiglu && (!aligned(su, 4) || !aligned(bu, 4))))
+    return fail(FN_ERR_ALIGN, "idx, scales and bias must be 4-byte aligned");
+  if (!aligned(y, 16)) return fail(FN_ERR_ALIGN, "output must be 16-byte aligned");
+  const int64_t yb = M * N * 2, wb = packed_fp8_bytes(K, N), sb = N * 4, bb = T * N * 4;
+  const void* ins[] = {x, scale, idx, wg, sg, bg, swiglu ? wu : nullptr, swiglu ? su : nullptr,
+                       swiglu ? bu : nullptr};
+  const int64_t inb[] = {M * K * 2, T * K * 2, M * 4, wb, sb, bb, wb, sb, bb};
+  for (int i = 0; i < 9; ++i)
+    if (overlap(y, yb, ins[i], inb[i])) return fail(FN_ERR_ALIAS, "output overlaps an input");
+  const int64_t need = adaln_ws_need(M, K);
+  if (ws == nullptr) return fail(FN_ERR_WORKSPACE, "workspace is NULL (the call needs %lld bytes)", (long long)need);
+  if (!aligned(ws, 256)) return fail(FN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(FN_ERR_WORKSPACE, "workspace_bytes=%lld, the call needs %lld", (long long)ws_bytes, (long long)need);
+  for (int i = 0; i < 9; ++i)
+    if (overlap(ws, need, ins[i], inb[i])) return fail(FN_ERR_ALIAS, "workspace overlaps an argument");
+  if (overlap(ws, need, y, yb)) return fail(FN_ERR_ALIAS, "workspace overlaps an argument");
+  void* u = ws;
+  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(M * K * 2));
+  FN_TRY(hip_status(fn::launch_adaln_modulate(x, scale, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
+                    "adaln_modulate"));
+  const fn::AdalnArgs ad{nullptr, idx, bg, swiglu ? bu : nullptr, (int)T};
+  const fn::FusedPlan plan = fn::plan_decode_premod(M, N, swiglu, true);
+  return hip_status(fn::launch_decode_premod(plan, u, rs, wg, sg, swiglu ? wu : nullptr, swiglu ? su : nullptr, y,
+                                             (int)M, (int)K, (int)N, ad, stream),
                     plan.name);
 }
 
@@ -514,6 +564,33 @@ const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, 
   if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true).name;
   if (M > kAdalnOneLaunchRows) return fn::plan_decode_premod(M, N, swiglu != 0).name;
   return fn_kernel_name_adaln(M, K, N, T, swiglu);
+}
+
+int64_t fn_adaln_fp8_workspace_bytes(int64_t M, int64_t K) {
+  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM) return 0;
+  return adaln_ws_need(M, K);
+}
+
+fn_status fn_norm_proj_adaln_fp8_ws(const void* x, const void* scale, const int* idx, const void* W8_packed,
+                                    const float* scales, const float* bias, void* y, int64_t M, int64_t K, int64_t N,
+                                    int64_t T, float eps, void* workspace, int64_t workspace_bytes,
+                                    hipStream_t stream) {
+  return adaln_fp8_ws_common(x, scale, idx, W8_packed, scales, bias, nullptr, nullptr, nullptr, y, M, K, N, T, eps,
+                             workspace, workspace_bytes, stream, false);
+}
+
+fn_status fn_norm_proj_swiglu_adaln_fp8_ws(const void* x, const void* scale, const int* idx, const void* W8_gate,
+                                           const float* s_gate, const float* bias_gate, const void* W8_up,
+                                           const float* s_up, const float* bias_up, void* out, int64_t M, int64_t K,
+                                           int64_t N, int64_t T, float eps, void* workspace, int64_t workspace_bytes,
+                                           hipStream_t stream) {
+  return adaln_fp8_ws_common(x, scale, idx, W8_gate, s_gate, bias_gate, W8_up, s_up, bias_up, out, M, K, N, T, eps,
+                             workspace, workspace_bytes, stream, true);
+}
+
+const char* fn_kernel_name_adaln_fp8(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
+  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
+  return fn::plan_decode_premod(M, N, swiglu != 0, true).name;
 }
 
 fn_status fn_adaln_modulate(const void* x, const void* scale, const int* idx, void* u, float* rs, int64_t M,

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   // always, bf16 output when each wave owns one column block.
   constexpr bool STAGE = Q8 || (NC == 1 && NWV <= NS);
   static_assert(!STAGE || (NC == 1 && NWV <= NS && 16 * MF * 16 * 4 <= SLOT), "staging fits a ring slot");
-  static_assert(!EX || (!AD && NC == 1 && !F8 && !Q8), "pre-modulated operand: bf16, one column block per wave");
+  static_assert(!EX || (!AD && NC == 1 && !Q8), "pre-modulated operand: one column block per wave, bf16 output");
   constexpr bool BIAS = AD || EX;
   static_assert(!BIAS || STAGE, "the AdaLN bias is added in the staged epilogue");
   static_assert(U % 2 == 0, "each x load moves two k-blocks of 8 rows");
@@ -757,15 +757,35 @@ static const DecodeXInstance kDecodeEx[] = {
     FN_DECODE_XE(4, true, 4, "decode_swiglu_premod_bf16_m64_xlds_w3_u2"),
 };
 
-FusedPlan plan_decode_premod(int64_t M, int64_t N, bool swiglu) {
+// fp8 weights: the fp8 rungs above on the pre-modulated operand (every M;
+// past 64 rows the 64-row tiles repeat over grid.y).
+#define FN_DECODE_X8E(MF, NWV, SW, U, NAME)                                                                      \
+  DecodeXInstance {                                                                                             \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, SW, U, true, false, false, 4, false, true>), MF, 1, \
+        NWV, U, SW, true, false, NAME                                                                           \
+  }
+static const DecodeXInstance kDecodeF8Ex[] = {
+    FN_DECODE_X8E(1, 3, false, 8, "decode_fp8_premod_m16_xlds_w3_u8"),
+    FN_DECODE_X8E(2, 3, false, 4, "decode_fp8_premod_m32_xlds_w3_u4"),
+    FN_DECODE_X8E(4, 3, false, 2, "decode_fp8_premod_m64_xlds_w3_u2"),
+    FN_DECODE_X8E(1, 3, true, 4, "decode_swiglu_fp8_premod_m16_xlds_w3_u4"),
+    FN_DECODE_X8E(2, 3, true, 4, "decode_swiglu_fp8_premod_m32_xlds_w3_u4"),
+    FN_DECODE_X8E(4, 4, true, 2, "decode_swiglu_fp8_premod_m64_xlds_w4_u2"),
+};
+
+FusedPlan plan_decode_premod(int64_t M, int64_t N, bool swiglu, bool f8) {
+  if (f8) return plan_of(find_instance(kDecodeF8Ex, M <= 16 ? 1 : (M <= 32 ? 2 : 4), swiglu), 9, M, N);
   return plan_of(find_instance(kDecodeEx, M <= 32 ? 2 : 4, swiglu), 9, M, N);
 }
 
-hipError_t launch_decode_premod(const FusedPlan& p, const void* u, const float* rs, const void* wg, const void* wu,
-                                void* y, int M, int K, int N, const AdalnArgs& ad, hipStream_t stream) {
-  const DecodeXInstance* d = find_instance(kDecodeEx, p.mf, wu != nullptr);
-  if (d == nullptr || M > 16 * d->mf) return hipErrorInvalidValue;
-  return launch_decode_x_instance(*d, u, wg, wu, y, M, K, N, 0.f, stream, nullptr, nullptr, nullptr, nullptr, &ad, rs);
+hipError_t launch_decode_premod(const FusedPlan& p, const void* u, const float* rs, const void* wg, const float* sg,
+                                const void* wu, const float* su, void* y, int M, int K, int N, const AdalnArgs& ad,
+                                hipStream_t stream) {
+  const bool f8 = sg != nullptr;
+  const DecodeXInstance* d =
+      f8 ? find_instance(kDecodeF8Ex, p.mf, wu != nullptr) : find_instance(kDecodeEx, p.mf, wu != nullptr);
+  if (d == nullptr || (!f8 && M > 16 * d->mf)) return hipErrorInvalidValue;
+  return launch_decode_x_instance(*d, u, wg, wu, y, M, K, N, 0.f, stream, sg, su, nullptr, nullptr, &ad, rs);
 }
 
 // SwiGLU with fp8 output, rows up to 64 (bf16 weights; larger M goes to the

@@ -68,10 +68,11 @@ hipError_t launch_adaln_modulate(const void* x, const void* scale, const int* id
 hipError_t launch_prefill_premod(const FusedPlan& plan, const void* u, const float* rs, const void* wg,
                                  const void* wu, void* y, int M, int K, int N, const AdalnArgs& ad,
                                  hipStream_t stream);
-FusedPlan plan_decode_premod(int64_t M, int64_t N, bool swiglu);   // 17..64 rows
+// bf16 weights: 17..64 rows; fp8 weights (column scales sg, su): every M.
+FusedPlan plan_decode_premod(int64_t M, int64_t N, bool swiglu, bool f8 = false);
 hipError_t launch_decode_premod(const FusedPlan& plan, const void* u, const float* rs, const void* wg,
-                                const void* wu, void* y, int M, int K, int N, const AdalnArgs& ad,
-                                hipStream_t stream);
+                                const float* sg, const void* wu, const float* su, void* y, int M, int K, int N,
+                                const AdalnArgs& ad, hipStream_t stream);
 
 hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
                        int K, int N, hipStream_t stream);

@@ -527,3 +527,49 @@ def check_adaln_operand(o, seed=25):
 
 
 ALL_CHECKS += [check_adaln_operand]
+
+
+def check_adaln_fp8(o, seed=26):
+    """AdaLN with E4M3 weights: with weights whose scaled values are exact
+    E4M3 values it is the folded/deferred AdaLN form exactly (itself pinned
+    to the unfolded definition above); zero tables and zero bias give the
+    plain fp8 path; brute force on a tiny case."""
+    rng = np.random.default_rng(seed)
+    K, N, M, T = 48, 24, 6, 3
+    pool = o.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    pick = rng.choice(pool, size=(K, N)) * rng.choice([-1.0, 1.0], size=(K, N))
+    pick[0, :] = 448.0
+    Wf = (pick * np.ldexp(1.0, -6)).astype(np.float32)
+    codes, s, _ = o.quantize_e4m3_columns(Wf)
+    codes_u, s_u, _ = o.quantize_e4m3_columns(Wf[::-1].copy())
+    x = rng.standard_normal((M, K))
+    sc = rng.standard_normal((T, K)) * 0.3
+    bias = rng.standard_normal((T, N))
+    bias_u = rng.standard_normal((T, N))
+    idx = rng.integers(0, T, M)
+    _close(o.adaln_norm_proj_fp8(x, codes, s, sc, bias, idx, 1e-6),
+           o.adaln_norm_proj_folded(x, Wf.astype(np.float64), sc, bias, idx, 1e-6), 1e-12,
+           "fp8 AdaLN exact weights vs folded AdaLN")
+    a = o.adaln_norm_proj_folded(x, Wf.astype(np.float64), sc, bias, idx, 1e-6)
+    b = o.adaln_norm_proj_folded(x, Wf[::-1].astype(np.float64), sc, bias_u, idx, 1e-6)
+    _close(o.adaln_norm_proj_swiglu_fp8(x, codes, s, codes_u, s_u, sc, bias, bias_u, idx, 1e-6),
+           a / (1 + np.exp(-a)) * b, 1e-12, "fp8 AdaLN SwiGLU exact weights")
+    zt, zb = np.zeros((T, K)), np.zeros((T, N))
+    assert np.array_equal(o.adaln_norm_proj_fp8(x, codes, s, zt, zb, idx, 1e-6), o.norm_proj_fp8(x, codes, s, 1e-6))
+    # brute force, arbitrary weights
+    Wr = rng.standard_normal((5, 3)).astype(np.float32)
+    c2, s2, _ = o.quantize_e4m3_columns(Wr)
+    xs, scs, bs, ids = x[:2, :5], sc[:, :5], bias[:, :3], np.array([2, 0])
+    got = o.adaln_norm_proj_fp8(xs, c2, s2, scs, bs, ids, 0.25)
+    for m in range(2):
+        rr = math.sqrt(sum(float(v) ** 2 for v in xs[m]) / 5 + float(np.float32(0.25)))
+        for n in range(3):
+            acc = 0.0
+            for k in range(5):
+                w = float(o.e4m3_decode(np.array([c2[k, n]]))[0]) * float(s2[n])
+                acc += float(xs[m, k]) * (1 + float(scs[ids[m], k])) * w
+            want = acc / rr + float(bs[ids[m], n])
+            assert abs(got[m, n] - want) <= 1e-12 * (abs(want) + 1), (m, n, got[m, n], want)
+
+
+ALL_CHECKS += [check_adaln_fp8]

@@ -421,3 +421,42 @@ def test_adaln_modulate_rejects(lib):
     assert f(0x1000, 0x10000, 0x18000, 0x20000, 0x30000, 4, 16, 0, 1e-6, None) == SHAPE
     assert f(0x1000, 0x10000, 0x18000, 0x20000, 0x30000, 4, 16, 2, -1.0, None) == EPS
     assert f(None, None, None, None, None, 0, 16, 2, 1e-6, None) == OK
+
+
+def _adf(lib, x=0x1000, sc=0x10000, idx=0x18000, w=0x20000, s=0x28000, b=0x30000, y=0x40000, M=4, K=16, N=16, T=2,
+         eps=1e-6, ws=0x100000, wsb=512):
+    return lib.fn_norm_proj_adaln_fp8_ws(x, sc, idx, w, s, b, y, M, K, N, T, eps, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(ws=None), WORKSPACE, "workspace is NULL"),
+    (dict(ws=0x100010), WORKSPACE, "256-byte"),
+    (dict(wsb=256), WORKSPACE, "workspace_bytes=256"),
+    (dict(ws=0x28000 - 256), ALIAS, "workspace overlaps"),
+    (dict(s=None), NULL, "W8_packed, scales or bias"),
+    (dict(b=None), NULL, "W8_packed, scales or bias"),
+    (dict(x=None), NULL, "x, scale or idx"),
+    (dict(s=0x28002), ALIGN, "idx, scales and bias"),
+    (dict(w=0x20008), ALIGN, "packed fp8 weights"),
+    (dict(K=12), SHAPE, "multiple of 8"),
+    (dict(T=0), SHAPE, "T=0"),
+    (dict(y=0x28000), ALIAS, "output overlaps"),
+])
+def test_norm_proj_adaln_fp8_ws_rejects(lib, kwargs, status, needle):
+    assert _adf(lib, **kwargs) == status
+    assert needle in lib.fn_last_error().decode()
+
+
+def test_adaln_fp8_sizes_and_names(lib):
+    # needed for every M: the operand and 1/RMS, each rounded up to 256 bytes
+    assert lib.fn_adaln_fp8_workspace_bytes(4, 16) == 256 + 256
+    assert lib.fn_adaln_fp8_workspace_bytes(0, 16) == 0
+    assert lib.fn_kernel_name_adaln_fp8(16, 4096, 12288, 4, 0).decode() == "decode_fp8_premod_m16_xlds_w3_u8"
+    assert lib.fn_kernel_name_adaln_fp8(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_premod_m64_xlds_w4_u2"
+    assert lib.fn_kernel_name_adaln_fp8(4096, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_premod_m64_xlds_w4_u2"
+    assert lib.fn_kernel_name_adaln_fp8(0, 4096, 16, 4, 0) == b"invalid"
+    sw = lib.fn_norm_proj_swiglu_adaln_fp8_ws
+    assert sw(0x1000, 0x10000, 0x18000, 0x20000, 0x28000, 0x30000, 0x21000, None, 0x31000, 0x40000, 4, 16, 16, 2,
+              1e-6, 0x100000, 512, None) == NULL
+    assert "W8_up, s_up or bias_up" in lib.fn_last_error().decode()
+    assert sw(None, None, None, None, None, None, None, None, None, None, 0, 16, 16, 2, 1e-6, None, 0, None) == OK

@@ -132,3 +132,24 @@ def test_adaln_two_launch_repeatable(gpu_lib, M, N, T, swiglu):
     else:
         call = lambda: fn.norm_proj_adaln_ws(x, sc, idx, Pg, bg, 1e-6, workspace=ws)                  # noqa: E731
     _repeat(call, lambda y: [y])
+
+
+@pytest.mark.parametrize("M,N,swiglu", [(64, 11008, True), (16, 12288, False), (300, 4096, True)])
+def test_adaln_fp8_repeatable(gpu_lib, M, N, swiglu):
+    import torch
+    fn = gpu_lib
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(70 + M)
+    K, T = 4096, 4
+    x = _rand((M, K), gen)
+    _, Wg, Wu, Pg, Pu = _weights(fn, K, N, swiglu, gen, fp8=True)
+    sc, sh = _rand((T, K), gen, 0.3), _rand((T, K), gen, 0.3)
+    idx = torch.randint(0, T, (M,), generator=gen, device="cuda", dtype=torch.int32)
+    ws = torch.empty((fn.adaln_fp8_workspace_bytes(M, K),), dtype=torch.uint8, device="cuda")
+    bg = fn.adaln_shift_bias(sh, Wg)
+    if swiglu:
+        bu = fn.adaln_shift_bias(sh, Wu)
+        call = lambda: fn.norm_proj_swiglu_adaln_fp8_ws(x, sc, idx, Pg, bg, Pu, bu, 1e-6, workspace=ws)   # noqa: E731
+    else:
+        call = lambda: fn.norm_proj_adaln_fp8_ws(x, sc, idx, Pg, bg, 1e-6, workspace=ws)                  # noqa: E731
+    _repeat(call, lambda y: [y])

@@ -72,6 +72,12 @@ MUTANTS = {
     "adaln operand truncated": ("adaln_operand", lambda x, sc, idx: _operand_with(x, sc, idx, np.trunc)),
     "adaln operand index clamped": ("adaln_operand", lambda x, sc, idx: _operand_ref(
         x, sc, np.clip(np.asarray(idx), 0, np.asarray(sc).shape[0] - 1))),
+    "adaln fp8 column scale dropped": ("adaln_norm_proj_fp8", lambda x, c, s, sc, b, idx, eps: _adaln_fp8_ref(
+        x, c, np.ones_like(np.asarray(s, float)), sc, b, idx, eps)),
+    "adaln fp8 bias dropped": ("adaln_norm_proj_fp8", lambda x, c, s, sc, b, idx, eps: _adaln_fp8_ref(
+        x, c, s, sc, np.zeros_like(np.asarray(b, float)), idx, eps)),
+    "adaln fp8 modulation dropped": ("adaln_norm_proj_fp8", lambda x, c, s, sc, b, idx, eps: _adaln_fp8_ref(
+        x, c, s, np.zeros_like(np.asarray(sc, float)), b, idx, eps)),
     "q8 scale inverted": ("dequantize_row_blocks", lambda c, s, block=16: _deq_ref(c, 1.0 / np.asarray(s, float),
                                                                                  block)),
 }
@@ -79,6 +85,7 @@ MUTANTS = {
 
 _encode_ref = O.e4m3_encode
 _operand_ref = O.adaln_operand
+_adaln_fp8_ref = O.adaln_norm_proj_fp8
 
 
 def _operand_with(x, sc, idx, rnd):
