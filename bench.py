@@ -120,7 +120,9 @@ KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": (
                   "qkv_decode_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_fp8": ("decode_x.hip", "fn_device.h"),
                   "decode_step_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_q8": ("decode_x.hip", "fn_device.h"),
                   "ffn_decode_fp8_q8": ("decode_x.hip", "fn_device.h"), "qkv_decode_adaln": ("decode_x.hip", "fn_device.h"),
-                  "ffn_decode_adaln": ("decode_x.hip", "fn_device.h"), "prefill_qkv_adaln": ("prefill.hip", "adaln.hip", "fn_device.h")}
+                  "qkv_decode_fp8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
+                  "ffn_decode_fp8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
+                  "ffn_decode_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"), "prefill_qkv_adaln": ("prefill.hip", "adaln.hip", "fn_device.h")}
 DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
 
 
@@ -205,8 +207,15 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False, adaln=Fa
         import workloads
         sc, sh, idx = workloads.adaln_tables(ADALN_T, call.K, call.M, seed=call.seed + 100)
         idx = idx[:rows]
+        if fp8:
+            bias8 = [oracle.adaln_shift_bias(sh, inp.W)] + ([oracle.adaln_shift_bias(sh, inp.W_up)] if call.swiglu else [])
     while True:
-        if adaln and call.swiglu:
+        if adaln and fp8 and call.swiglu:
+            oracle.adaln_norm_proj_swiglu_fp8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], sc, bias8[0], bias8[1], idx,
+                                              call.eps)
+        elif adaln and fp8:
+            oracle.adaln_norm_proj_fp8(x, w8[0][0], w8[0][1], sc, bias8[0], idx, call.eps)
+        elif adaln and call.swiglu:
             oracle.adaln_norm_proj_swiglu(x, inp.g, sc, sh, idx, inp.W, inp.W_up, call.eps)
         elif adaln:
             oracle.adaln_norm_proj(x, inp.g, sc, sh, idx, inp.W, call.eps)
@@ -286,12 +295,13 @@ def run_single(args, torch, fn, workloads):
         idx_t = torch.from_numpy(idx_np).cuda()
         bg_t = fn.adaln_shift_bias(sh_t, Wg)
         bu_t = fn.adaln_shift_bias(sh_t, Wu) if call.swiglu else None
-        # the two-launch form above 64 rows (pre-pass into a workspace allocated here, once)
-        nws = fn.adaln_workspace_bytes(call.M, call.K)
+        # the two-launch form above 16 rows, and with fp8 weights (pre-pass into a workspace allocated here, once)
+        nws = fn.adaln_fp8_workspace_bytes(call.M, call.K) if fp8 else fn.adaln_workspace_bytes(call.M, call.K)
         ws_t = torch.empty((nws,), dtype=torch.uint8, device="cuda") if nws else None
-        proj = lambda x_, P_, e_, out=None: fn.norm_proj_adaln_ws(  # noqa: E731
-            x_, sc_t, idx_t, P_, bg_t, e_, out=out, workspace=ws_t)
-        proj_sw = lambda x_, a_, b_, e_, out=None: fn.norm_proj_swiglu_adaln_ws(  # noqa: E731
+        f1, f2 = ((fn.norm_proj_adaln_fp8_ws, fn.norm_proj_swiglu_adaln_fp8_ws) if fp8 else
+                  (fn.norm_proj_adaln_ws, fn.norm_proj_swiglu_adaln_ws))
+        proj = lambda x_, P_, e_, out=None: f1(x_, sc_t, idx_t, P_, bg_t, e_, out=out, workspace=ws_t)  # noqa: E731
+        proj_sw = lambda x_, a_, b_, e_, out=None: f2(  # noqa: E731
             x_, sc_t, idx_t, a_, bg_t, b_, bu_t, e_, out=out, workspace=ws_t)
     q8 = args.output == "q8"
     if q8:
@@ -516,9 +526,9 @@ def main(argv=None):
         print(f"bench.py: --output q8 applies to the SwiGLU workload ffn_decode, not {args.workload}", file=sys.stderr)
         return 2
     adaln = args.prologue == "adaln"
-    if adaln and (fp8 or q8 or args.workload not in ("qkv_decode", "ffn_decode", "prefill_qkv")):
-        print("bench.py: --prologue adaln applies to qkv_decode, ffn_decode and prefill_qkv with bf16 weights and "
-              "output", file=sys.stderr)
+    if adaln and (q8 or args.workload not in ("qkv_decode", "ffn_decode", "prefill_qkv")):
+        print("bench.py: --prologue adaln applies to qkv_decode, ffn_decode and prefill_qkv with bf16 output",
+              file=sys.stderr)
         return 2
     suffix = ("_fp8" if fp8 else "") + ("_q8" if q8 else "") + ("_adaln" if adaln else "")
 
@@ -541,7 +551,8 @@ def main(argv=None):
         call, inp, r = run_single(args, torch, fn, workloads)
         bytes_call = call_bytes(call, fp8, q8) + (adaln_extra_bytes(call) if adaln else 0)
         flops_call = call.flops()
-        kernel = (fn.kernel_name_adaln_ws(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln else
+        kernel = (fn.kernel_name_adaln_fp8(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln and fp8 else
+                  fn.kernel_name_adaln_ws(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln else
                   fn.kernel_name_q8(call.M, call.K, call.N, fp8) if q8 else
                   fn.kernel_name_fp8(call.M, call.K, call.N, call.swiglu) if fp8 else
                   fn.kernel_name(call.M, call.K, call.N, call.swiglu,
@@ -577,7 +588,8 @@ def main(argv=None):
         if adaln:
             config["prologue"] = (f"AdaLN: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx], tables of {ADALN_T} rows, "
                                   "per-row index" + (", two launches (adaln_modulate pre-pass, then the kernel named)"
-                                                     if fn.adaln_workspace_bytes(call.M, call.K) else ", one launch"))
+                                                     if fp8 or fn.adaln_workspace_bytes(call.M, call.K) else
+                                                     ", one launch"))
 
     if args.measured_peak and roof["bound"] in ("hbm", "mfma") and unit != "us/call":
         peak, peak_unit = measured_peak(torch, fn, roof["bound"])
