@@ -296,7 +296,7 @@ def run_single(args, torch, fn, workloads):
         bg_t = fn.adaln_shift_bias(sh_t, Wg)
         bu_t = fn.adaln_shift_bias(sh_t, Wu) if call.swiglu else None
         # the two-launch form above 16 rows, and with fp8 weights (pre-pass into a workspace allocated here, once)
-        nws = fn.adaln_fp8_workspace_bytes(call.M, call.K) if fp8 else fn.adaln_workspace_bytes(call.M, call.K)
+        nws = fn.adaln_prepass_bytes(call.M, call.K) if fp8 else fn.adaln_workspace_bytes(call.M, call.K)
         ws_t = torch.empty((nws,), dtype=torch.uint8, device="cuda") if nws else None
         f1, f2 = ((fn.norm_proj_adaln_fp8_ws, fn.norm_proj_swiglu_adaln_fp8_ws) if fp8 else
                   (fn.norm_proj_adaln_ws, fn.norm_proj_swiglu_adaln_ws))

@@ -355,7 +355,7 @@ const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, 
  * Kernel on SM120").  bias rows come from fn_adaln_shift_bias on the
  * unfolded bf16 W.  Arguments as fn_norm_proj_fp8 / fn_norm_proj_swiglu_fp8
  * plus scale, idx, bias and T as in the AdaLN calls above; workspace: at
- * least fn_adaln_fp8_workspace_bytes(M, K) bytes, 256-byte aligned,
+ * least fn_adaln_prepass_bytes(M, K) bytes, 256-byte aligned,
  * overlapping no other argument (always needed).  Errors as the calls
  * above. */
 fn_status fn_norm_proj_adaln_fp8_ws(const void* x, const void* scale, const int* idx, const void* W8_packed,
@@ -368,14 +368,45 @@ fn_status fn_norm_proj_swiglu_adaln_fp8_ws(const void* x, const void* scale, con
                                            int64_t N, int64_t T, float eps, void* workspace, int64_t workspace_bytes,
                                            hipStream_t stream);
 
-/* Workspace bytes of the two fp8 calls above (the same layout as
- * fn_adaln_workspace_bytes, needed for every M >= 1); 0 for M < 1 or M, K
+/* Workspace bytes of the AdaLN calls that always run the pre-pass (the two
+ * fp8-weight calls above and the two fp8-output calls below): the operand
+ * (M*K bf16) and 1/RMS (M fp32), each rounded up to 256 bytes -- the layout
+ * of fn_adaln_workspace_bytes, for every M >= 1; 0 for M < 1 or M, K
  * outside the limits. */
-int64_t fn_adaln_fp8_workspace_bytes(int64_t M, int64_t K);
+int64_t fn_adaln_prepass_bytes(int64_t M, int64_t K);
 
 /* Projection kernel instance of the fp8 AdaLN calls; "invalid" for bad
  * shapes. */
 const char* fn_kernel_name_adaln_fp8(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu);
+
+/* AdaLN + gate/up projections + SwiGLU with fp8 row-block output (E4M3
+ * codes, one fp32 scale per 16-column row block, as fn_norm_proj_swiglu_q8),
+ * in two launches for every M: the pre-pass, then the q8 kernel of the row
+ * count on the modulated operand (bf16 weights: the LDS-shared-x decode
+ * kernel up to 64 rows, the prefill kernel above; fp8 weights: the fp8
+ * decode kernel).  The AdaLN FC1 block of [FlashInfer #5521] ("Segmented
+ * Chain": norm + AdaLN, FC1, SwiGLU, quantisation for the next projection)
+ * with the output format of [FlashInfer #4040] as read for
+ * fn_norm_proj_swiglu_q8.  The block values are
+ *   v = silu(a) * b,  a = (u * W'_gate) / RMS(x) + bias_gate[idx],  b likewise,
+ * u the pre-pass operand; arguments and errors as the calls above plus
+ * out_codes [M,N] (uint8) and out_scales [M, ceil(N/16)] (fp32, 4-byte
+ * aligned); workspace: fn_adaln_prepass_bytes(M, K) bytes. */
+fn_status fn_norm_proj_swiglu_adaln_q8_ws(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+                                          const float* bias_gate, const void* W_up_packed, const float* bias_up,
+                                          void* out_codes, float* out_scales, int64_t M, int64_t K, int64_t N,
+                                          int64_t T, float eps, void* workspace, int64_t workspace_bytes,
+                                          hipStream_t stream);
+fn_status fn_norm_proj_swiglu_adaln_fp8_q8_ws(const void* x, const void* scale, const int* idx, const void* W8_gate,
+                                              const float* s_gate, const float* bias_gate, const void* W8_up,
+                                              const float* s_up, const float* bias_up, void* out_codes,
+                                              float* out_scales, int64_t M, int64_t K, int64_t N, int64_t T,
+                                              float eps, void* workspace, int64_t workspace_bytes,
+                                              hipStream_t stream);
+
+/* Kernel instance of the two fp8-output AdaLN calls; "invalid" for bad
+ * shapes. */
+const char* fn_kernel_name_adaln_q8(int64_t M, int64_t K, int64_t N, int64_t T, int fp8_weights);
 
 /* The pre-pass alone: for each row m, with s = scale[idx[m]] (all zero when
  * idx[m] is outside [0, T)),

@@ -401,6 +401,40 @@ def adaln_norm_proj_swiglu_fp8(x, codes_gate, s_gate, codes_up, s_up, scale, bia
     return silu(a) * b
 
 
+def _rows_or_zero(table, idx) -> np.ndarray:
+    """table[idx[m]] per row, all zero where idx[m] is outside the table."""
+    t = _f64(table)
+    i = np.asarray(idx, dtype=np.int64)
+    ok = (i >= 0) & (i < t.shape[0])
+    return np.where(ok[:, None], t[np.where(ok, i, 0)], 0.0)
+
+
+def adaln_norm_proj_swiglu_q8(x, scale, idx, Wg_folded, Wu_folded, bias_gate, bias_up, eps: float):
+    """AdaLN FC1 with fp8 row-block output ([FlashInfer #5521] "Segmented
+    Chain": norm + AdaLN, FC1, SwiGLU, quantisation for the next projection;
+    the format as read for norm_proj_swiglu_q8).  The codes are decisions,
+    so the values quantised are formed on the operand the kernels use,
+    u = adaln_operand(x, scale, idx) (the reading stated there):
+        a = (u @ W'_gate) / r + bias_gate[idx],  b likewise,  v = silu(a) * b,
+    then quantize_e4m3_row_blocks(v).  An index outside the table takes
+    scale 0 and bias 0.  Returns (codes, s, v)."""
+    u = adaln_operand(x, scale, idx)
+    r = rms(x, eps)[:, None]
+    a = (u @ _f64(Wg_folded)) / r + _rows_or_zero(bias_gate, idx)
+    b = (u @ _f64(Wu_folded)) / r + _rows_or_zero(bias_up, idx)
+    v = silu(a) * b
+    codes, s = quantize_e4m3_row_blocks(v)
+    return codes, s, v
+
+
+def adaln_norm_proj_swiglu_fp8_q8(x, scale, idx, codes_gate, s_gate, codes_up, s_up, bias_gate, bias_up,
+                                  eps: float):
+    """The same with E4M3 weights: W' = s[n] * q."""
+    Wg = e4m3_decode(codes_gate) * _f64(s_gate)[None, :]
+    Wu = e4m3_decode(codes_up) * _f64(s_up)[None, :]
+    return adaln_norm_proj_swiglu_q8(x, scale, idx, Wg, Wu, bias_gate, bias_up, eps)
+
+
 def adaln_operand(x, scale, idx) -> np.ndarray:
     """The modulated matrix-core operand of the AdaLN path, as the kernels
     form it: x + x * scale[idx[m]] rounded once to float32, then to bf16 with
@@ -424,4 +458,4 @@ __all__ = ["rms", "rmsnorm", "norm_proj", "silu", "norm_proj_swiglu", "fold_exac
            "Q8_BLOCK", "quantize_e4m3_row_blocks", "dequantize_row_blocks", "norm_proj_swiglu_q8",
            "norm_proj_swiglu_fp8_q8", "adaln_modulate", "adaln_norm_proj", "adaln_norm_proj_swiglu",
            "adaln_shift_bias", "adaln_norm_proj_folded", "adaln_operand", "adaln_norm_proj_fp8",
-           "adaln_norm_proj_swiglu_fp8"]
+           "adaln_norm_proj_swiglu_fp8", "adaln_norm_proj_swiglu_q8", "adaln_norm_proj_swiglu_fp8_q8"]

@@ -89,8 +89,13 @@ def load():
         "fn_norm_proj_adaln_fp8_ws": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp, i64, vp]),
         "fn_norm_proj_swiglu_adaln_fp8_ws": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32,
                                                    vp, i64, vp]),
-        "fn_adaln_fp8_workspace_bytes": (i64, [i64, i64]),
+        "fn_adaln_prepass_bytes": (i64, [i64, i64]),
         "fn_kernel_name_adaln_fp8": (ctypes.c_char_p, [i64, i64, i64, i64, i32]),
+        "fn_norm_proj_swiglu_adaln_q8_ws": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp,
+                                                  i64, vp]),
+        "fn_norm_proj_swiglu_adaln_fp8_q8_ws": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                      f32, vp, i64, vp]),
+        "fn_kernel_name_adaln_q8": (ctypes.c_char_p, [i64, i64, i64, i64, i32]),
         "fn_step_create": (i32, [vp, i64, ctypes.POINTER(vp)]),
         "fn_step_launch": (i32, [vp, vp]),
         "fn_step_num_kernels": (i64, [vp]),
@@ -509,9 +514,9 @@ def kernel_name_adaln_ws(M: int, K: int, N: int, T: int, swiglu: bool) -> str:
     return load().fn_kernel_name_adaln_ws(M, K, N, T, int(swiglu)).decode()
 
 
-def adaln_fp8_workspace_bytes(M: int, K: int) -> int:
+def adaln_prepass_bytes(M: int, K: int) -> int:
     """Workspace bytes of the fp8-weight AdaLN calls (needed for every M)."""
-    return int(load().fn_adaln_fp8_workspace_bytes(M, K))
+    return int(load().fn_adaln_prepass_bytes(M, K))
 
 
 def _check_adaln_fp8(x, scale, idx, P: PackedFp8, bias):
@@ -529,7 +534,7 @@ def _check_adaln_fp8(x, scale, idx, P: PackedFp8, bias):
 
 def _workspace_fp8(workspace, M: int, K: int, like):
     if workspace is None:
-        n = adaln_fp8_workspace_bytes(M, K)
+        n = adaln_prepass_bytes(M, K)
         if n == 0:
             return None, 0
         workspace = _torch().empty((n,), dtype=_torch().uint8, device=like.device)
@@ -569,6 +574,42 @@ def norm_proj_swiglu_adaln_fp8_ws(x, scale, idx, Pg: PackedFp8, bias_g, Pu: Pack
 
 def kernel_name_adaln_fp8(M: int, K: int, N: int, T: int, swiglu: bool) -> str:
     return load().fn_kernel_name_adaln_fp8(M, K, N, T, int(swiglu)).decode()
+
+
+def norm_proj_swiglu_adaln_q8_ws(x, scale, idx, Wg: PackedWeights, bias_g, Wu: PackedWeights, bias_u,
+                                 eps: float = 1e-6, out=None, workspace=None):
+    """AdaLN FC1 + SwiGLU with E4M3 row-block output, two launches:
+    (codes, scales)."""
+    _check_adaln(x, scale, idx, Wg, bias_g)
+    _check_adaln(x, scale, idx, Wu, bias_u)
+    M, N = x.shape[0], Wg.N
+    codes, scales = _q8_out(out, M, N, x)
+    ws, nbytes = _workspace_fp8(workspace, M, Wg.K, x)
+    _check(load().fn_norm_proj_swiglu_adaln_q8_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Wg.data.data_ptr(),
+                                                  bias_g.data_ptr(), Wu.data.data_ptr(), bias_u.data_ptr(),
+                                                  codes.data_ptr(), scales.data_ptr(), M, Wg.K, N, scale.shape[0], eps,
+                                                  None if ws is None else ws.data_ptr(), nbytes, _stream(x)))
+    return codes, scales
+
+
+def norm_proj_swiglu_adaln_fp8_q8_ws(x, scale, idx, Pg: PackedFp8, bias_g, Pu: PackedFp8, bias_u,
+                                     eps: float = 1e-6, out=None, workspace=None):
+    """The same with E4M3 gate/up weights: (codes, scales)."""
+    _check_adaln_fp8(x, scale, idx, Pg, bias_g)
+    _check_adaln_fp8(x, scale, idx, Pu, bias_u)
+    M, N = x.shape[0], Pg.N
+    codes, scales = _q8_out(out, M, N, x)
+    ws, nbytes = _workspace_fp8(workspace, M, Pg.K, x)
+    _check(load().fn_norm_proj_swiglu_adaln_fp8_q8_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(),
+                                                      Pg.data.data_ptr(), Pg.scales.data_ptr(), bias_g.data_ptr(),
+                                                      Pu.data.data_ptr(), Pu.scales.data_ptr(), bias_u.data_ptr(),
+                                                      codes.data_ptr(), scales.data_ptr(), M, Pg.K, N, scale.shape[0],
+                                                      eps, None if ws is None else ws.data_ptr(), nbytes, _stream(x)))
+    return codes, scales
+
+
+def kernel_name_adaln_q8(M: int, K: int, N: int, T: int, fp8_weights: bool) -> str:
+    return load().fn_kernel_name_adaln_q8(M, K, N, T, int(fp8_weights)).decode()
 
 
 def adaln_modulate(x, scale, idx, eps: float = 1e-6, u=None, rs=None):
@@ -706,5 +747,6 @@ __all__ = ["load", "fold_weights", "norm_proj", "norm_proj_swiglu", "rmsnorm", "
            "FN_CALL_NORM_PROJ_SWIGLU_Q8", "FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8", "Q8_BLOCK", "norm_proj_swiglu_q8",
            "norm_proj_swiglu_fp8_q8", "kernel_name_q8", "adaln_shift_bias", "norm_proj_adaln",
            "norm_proj_swiglu_adaln", "kernel_name_adaln", "adaln_workspace_bytes", "norm_proj_adaln_ws",
-           "norm_proj_swiglu_adaln_ws", "kernel_name_adaln_ws", "adaln_modulate", "adaln_fp8_workspace_bytes",
-           "norm_proj_adaln_fp8_ws", "norm_proj_swiglu_adaln_fp8_ws", "kernel_name_adaln_fp8"]
+           "norm_proj_swiglu_adaln_ws", "kernel_name_adaln_ws", "adaln_modulate", "adaln_prepass_bytes",
+           "norm_proj_adaln_fp8_ws", "norm_proj_swiglu_adaln_fp8_ws", "kernel_name_adaln_fp8",
+           "norm_proj_swiglu_adaln_q8_ws", "norm_proj_swiglu_adaln_fp8_q8_ws", "kernel_name_adaln_q8"]

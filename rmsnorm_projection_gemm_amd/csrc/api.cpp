@@ -303,6 +303,64 @@ fn_status adaln_fp8_ws_common(const void* x, const void* scale, const int* idx, 
                     plan.name);
 }
 
+// Two-launch AdaLN + SwiGLU with fp8 row-block output, every M: bf16 weights
+// (f8 false) or E4M3 codes with column scales (f8 true).
+fn_status adaln_q8_ws_common(const void* x, const void* scale, const int* idx, const void* wg, const float* sg,
+                             const float* bg, const void* wu, const float* su, const float* bu, void* codes,
+                             float* qscales, int64_t M, int64_t K, int64_t N, int64_t T, float eps, void* ws,
+                             int64_t ws_bytes, hipStream_t stream, bool f8) {
+  g_last_error[0] = '\0';
+  FN_TRY(check_k(K));
+  FN_TRY(check_mn(M, N));
+  FN_TRY(check_eps(eps));
+  if (T < 1 || T > INT32_MAX || T * K * 2 > INT32_MAX)
+    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*2 < 2^31", (long long)T);
+  if (M == 0 || N == 0) return FN_OK;
+  if (x == nullptr || scale == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, scale or idx is NULL");
+  if (wg == nullptr || wu == nullptr || bg == nullptr || bu == nullptr)
+    return fail(FN_ERR_NULL, "gate or up weights or bias rows are NULL");
+  if (f8 && (sg == nullptr || su == nullptr)) return fail(FN_ERR_NULL, "s_gate or s_up is NULL");
+  if (codes == nullptr || qscales == nullptr) return fail(FN_ERR_NULL, "out_codes or out_scales is NULL");
+  if (!aligned(x, 16) || !aligned(scale, 16)) return fail(FN_ERR_ALIGN, "x and scale must be 16-byte aligned");
+  if (!aligned(wg, 16) || !aligned(wu, 16)) return fail(FN_ERR_ALIGN, "packed weights must be 16-byte aligned");
+  if (!aligned(idx, 4) || !aligned(bg, 4) || !aligned(bu, 4) || (f8 && (!aligned(sg, 4) || !aligned(su, 4))))
+    return fail(FN_ERR_ALIGN, "idx, scales and bias must be 4-byte aligned");
+  if (!aligned(qscales, 4)) return fail(FN_ERR_ALIGN, "out_scales must be 4-byte aligned");
+  const int64_t wb = f8 ? packed_fp8_bytes(K, N) : packed_bytes(K, N, FN_BF16), sb = f8 ? N * 4 : 0, bb = T * N * 4;
+  const void* ins[] = {x, scale, idx, wg, wu, bg, bu, f8 ? sg : nullptr, f8 ? su : nullptr};
+  const int64_t inb[] = {M * K * 2, T * K * 2, M * 4, wb, wb, bb, bb, sb, sb};
+  const int64_t cb = M * N, qb = M * ((N + 15) / 16) * 4;
+  for (int i = 0; i < 9; ++i)
+    if (overlap(codes, cb, ins[i], inb[i]) || overlap(qscales, qb, ins[i], inb[i]))
+      return fail(FN_ERR_ALIAS, "an output overlaps an input");
+  if (overlap(codes, cb, qscales, qb)) return fail(FN_ERR_ALIAS, "out_codes overlaps out_scales");
+  const int64_t need = adaln_ws_need(M, K);
+  if (ws == nullptr) return fail(FN_ERR_WORKSPACE, "workspace is NULL (the call needs %lld bytes)", (long long)need);
+  if (!aligned(ws, 256)) return fail(FN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(FN_ERR_WORKSPACE, "workspace_bytes=%lld, the call needs %lld", (long long)ws_bytes, (long long)need);
+  for (int i = 0; i < 9; ++i)
+    if (overlap(ws, need, ins[i], inb[i])) return fail(FN_ERR_ALIAS, "workspace overlaps an argument");
+  if (overlap(ws, need, codes, cb) || overlap(ws, need, qscales, qb))
+    return fail(FN_ERR_ALIAS, "workspace overlaps an argument");
+  void* u = ws;
+  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(M * K * 2));
+  FN_TRY(hip_status(fn::launch_adaln_modulate(x, scale, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
+                    "adaln_modulate"));
+  const fn::AdalnArgs ad{nullptr, idx, bg, bu, (int)T};
+  uint8_t* q = static_cast<uint8_t*>(codes);
+  if (!f8 && M > 64) {
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, true);
+    return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, wu, nullptr, (int)M, (int)K, (int)N, ad, stream, q,
+                                                qscales),
+                      plan.name);
+  }
+  const fn::FusedPlan plan = fn::plan_decode_q8_premod(f8, M, N);
+  return hip_status(fn::launch_decode_q8_premod(f8, plan, u, rs, wg, f8 ? sg : nullptr, wu, f8 ? su : nullptr, q,
+                                                qscales, (int)M, (int)K, (int)N, ad, stream),
+                    plan.name);
+}
+
 // One recorded call: validate (check_only) or enqueue it on `stream`.
 fn_status run_call(const fn_call& c, hipStream_t stream, bool check_only) {
   switch (c.kind) {
@@ -566,7 +624,7 @@ const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, 
   return fn_kernel_name_adaln(M, K, N, T, swiglu);
 }
 
-int64_t fn_adaln_fp8_workspace_bytes(int64_t M, int64_t K) {
+int64_t fn_adaln_prepass_bytes(int64_t M, int64_t K) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM) return 0;
   return adaln_ws_need(M, K);
 }
@@ -591,6 +649,31 @@ fn_status fn_norm_proj_swiglu_adaln_fp8_ws(const void* x, const void* scale, con
 const char* fn_kernel_name_adaln_fp8(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
   return fn::plan_decode_premod(M, N, swiglu != 0, true).name;
+}
+
+fn_status fn_norm_proj_swiglu_adaln_q8_ws(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+                                          const float* bias_gate, const void* W_up_packed, const float* bias_up,
+                                          void* out_codes, float* out_scales, int64_t M, int64_t K, int64_t N,
+                                          int64_t T, float eps, void* workspace, int64_t workspace_bytes,
+                                          hipStream_t stream) {
+  return adaln_q8_ws_common(x, scale, idx, W_gate_packed, nullptr, bias_gate, W_up_packed, nullptr, bias_up, out_codes,
+                            out_scales, M, K, N, T, eps, workspace, workspace_bytes, stream, false);
+}
+
+fn_status fn_norm_proj_swiglu_adaln_fp8_q8_ws(const void* x, const void* scale, const int* idx, const void* W8_gate,
+                                              const float* s_gate, const float* bias_gate, const void* W8_up,
+                                              const float* s_up, const float* bias_up, void* out_codes,
+                                              float* out_scales, int64_t M, int64_t K, int64_t N, int64_t T,
+                                              float eps, void* workspace, int64_t workspace_bytes,
+                                              hipStream_t stream) {
+  return adaln_q8_ws_common(x, scale, idx, W8_gate, s_gate, bias_gate, W8_up, s_up, bias_up, out_codes, out_scales, M,
+                            K, N, T, eps, workspace, workspace_bytes, stream, true);
+}
+
+const char* fn_kernel_name_adaln_q8(int64_t M, int64_t K, int64_t N, int64_t T, int fp8_weights) {
+  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
+  if (!fp8_weights && M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, true).name;
+  return fn::plan_decode_q8_premod(fp8_weights != 0, M, N).name;
 }
 
 fn_status fn_adaln_modulate(const void* x, const void* scale, const int* idx, void* u, float* rs, int64_t M,

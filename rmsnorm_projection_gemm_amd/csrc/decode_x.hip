@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   // always, bf16 output when each wave owns one column block.
   constexpr bool STAGE = Q8 || (NC == 1 && NWV <= NS);
   static_assert(!STAGE || (NC == 1 && NWV <= NS && 16 * MF * 16 * 4 <= SLOT), "staging fits a ring slot");
-  static_assert(!EX || (!AD && NC == 1 && !Q8), "pre-modulated operand: one column block per wave, bf16 output");
+  static_assert(!EX || (!AD && NC == 1), "pre-modulated operand: one column block per wave");
   constexpr bool BIAS = AD || EX;
   static_assert(!BIAS || STAGE, "the AdaLN bias is added in the staged epilogue");
   static_assert(U % 2 == 0, "each x load moves two k-blocks of 8 rows");
@@ -772,6 +772,40 @@ static const DecodeXInstance kDecodeF8Ex[] = {
     FN_DECODE_X8E(2, 3, true, 4, "decode_swiglu_fp8_premod_m32_xlds_w3_u4"),
     FN_DECODE_X8E(4, 4, true, 2, "decode_swiglu_fp8_premod_m64_xlds_w4_u2"),
 };
+
+// SwiGLU with fp8 output on the pre-modulated operand: the q8 rungs above
+// (bf16 weights up to 64 rows; fp8 weights every M).
+#define FN_DECODE_XQE(MF, NWV, U, F8, NAME)                                                                     \
+  DecodeXInstance {                                                                                            \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, true, U, F8, true, false, 4, false, true>), MF, 1, \
+        NWV, U, true, F8, true, NAME                                                                           \
+  }
+static const DecodeXInstance kDecodeQ8Ex[] = {
+    FN_DECODE_XQE(1, 3, 2, false, "decode_swiglu_bf16_q8_premod_m16_xlds_w3_u2"),
+    FN_DECODE_XQE(2, 3, 2, false, "decode_swiglu_bf16_q8_premod_m32_xlds_w3_u2"),
+    FN_DECODE_XQE(4, 3, 2, false, "decode_swiglu_bf16_q8_premod_m64_xlds_w3_u2"),
+    FN_DECODE_XQE(1, 3, 4, true, "decode_swiglu_fp8_q8_premod_m16_xlds_w3_u4"),
+    FN_DECODE_XQE(2, 3, 4, true, "decode_swiglu_fp8_q8_premod_m32_xlds_w3_u4"),
+    FN_DECODE_XQE(4, 4, 2, true, "decode_swiglu_fp8_q8_premod_m64_xlds_w4_u2"),
+};
+
+static const DecodeXInstance* find_q8_premod(bool f8, int mf) {
+  for (const DecodeXInstance& d : kDecodeQ8Ex)
+    if (d.f8 == f8 && d.mf == mf) return &d;
+  return nullptr;
+}
+
+FusedPlan plan_decode_q8_premod(bool f8_weights, int64_t M, int64_t N) {
+  return plan_of(find_q8_premod(f8_weights, M <= 16 ? 1 : (M <= 32 ? 2 : 4)), 10, M, N);
+}
+
+hipError_t launch_decode_q8_premod(bool f8_weights, const FusedPlan& p, const void* u, const float* rs,
+                                   const void* wg, const float* sg, const void* wu, const float* su, uint8_t* q,
+                                   float* qs, int M, int K, int N, const AdalnArgs& ad, hipStream_t stream) {
+  const DecodeXInstance* d = find_q8_premod(f8_weights, p.mf);
+  if (d == nullptr || (!f8_weights && M > 16 * d->mf)) return hipErrorInvalidValue;
+  return launch_decode_x_instance(*d, u, wg, wu, nullptr, M, K, N, 0.f, stream, sg, su, q, qs, &ad, rs);
+}
 
 FusedPlan plan_decode_premod(int64_t M, int64_t N, bool swiglu, bool f8) {
   if (f8) return plan_of(find_instance(kDecodeF8Ex, M <= 16 ? 1 : (M <= 32 ? 2 : 4), swiglu), 9, M, N);

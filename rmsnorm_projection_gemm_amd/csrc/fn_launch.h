@@ -18,7 +18,7 @@ struct FusedPlan {
                       // 4 = SwiGLU with fp8 output (x in LDS), 5 = the same on the prefill kernel,
                       // 6 = AdaLN prologue (x and scale rows in LDS), 7 = AdaLN on the prefill kernel,
                       // 8 = prefill on an operand modulated by the AdaLN pre-pass,
-                      // 9 = the same on the LDS-shared-x decode kernel (17..64 rows)
+                      // 9 = the same on the LDS-shared-x decode kernel, 10 = the same with fp8 output
   int mf;             // 16-row fragments per workgroup (decode)
   int nf;             // 16-column fragments per workgroup (decode)
   int waves;          // waves per workgroup
@@ -65,9 +65,16 @@ bool prefill_adaln_fits(int64_t T);
 // plan_prefill(..., ex = true); ad.scale unused).
 hipError_t launch_adaln_modulate(const void* x, const void* scale, const int* idx, int T, void* u, float* rs, int M,
                                  int K, float eps, hipStream_t stream);
+// q, qs: SwiGLU with fp8 row-block output (y unused).
 hipError_t launch_prefill_premod(const FusedPlan& plan, const void* u, const float* rs, const void* wg,
                                  const void* wu, void* y, int M, int K, int N, const AdalnArgs& ad,
-                                 hipStream_t stream);
+                                 hipStream_t stream, uint8_t* q = nullptr, float* qs = nullptr);
+// SwiGLU with fp8 output on the pre-modulated operand (bf16 weights up to 64
+// rows, fp8 weights every M).
+FusedPlan plan_decode_q8_premod(bool f8_weights, int64_t M, int64_t N);
+hipError_t launch_decode_q8_premod(bool f8_weights, const FusedPlan& plan, const void* u, const float* rs,
+                                   const void* wg, const float* sg, const void* wu, const float* su, uint8_t* q,
+                                   float* qs, int M, int K, int N, const AdalnArgs& ad, hipStream_t stream);
 // bf16 weights: 17..64 rows; fp8 weights (column scales sg, su): every M.
 FusedPlan plan_decode_premod(int64_t M, int64_t N, bool swiglu, bool f8 = false);
 hipError_t launch_decode_premod(const FusedPlan& plan, const void* u, const float* rs, const void* wg,

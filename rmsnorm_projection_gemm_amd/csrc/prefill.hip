@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   static_assert(4 * WSLOT + 2 * XSLOT + 2 * TSLOT + BMF * 64 <= 160 * 1024, "LDS budget");
   static_assert(!AD || !Q8, "AdaLN with bf16 output");
   static_assert(AD || NW == 8, "ping-pong: two groups of one wave per SIMD");
-  static_assert(!EX || (!AD && !Q8), "pre-modulated operand: ping-pong loop, bf16 output");
+  static_assert(!EX || !AD, "pre-modulated operand: ping-pong loop");
   constexpr bool BIAS = AD || EX;
 
   __shared__ __attribute__((aligned(1024))) uint8_t wring0[WSLOT];
@@ -520,8 +520,9 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
         for (int j = 0; j < FN; ++j) {
           const int nb = nb0 + wn * FN + j;
           const int col = nb * 16 + lrow;
-          const float v = SW ? silu_times(acc[0][i][j][r] * inv, acc[NMAT - 1][i][j][r] * inv)
-                             : acc[0][i][j][r] * inv;
+          const float ga = BIAS ? fmaf(acc[0][i][j][r], inv, bias[0][r][j]) : acc[0][i][j][r] * inv;
+          const float ua = BIAS ? fmaf(acc[NMAT - 1][i][j][r], inv, bias[NMAT - 1][r][j]) : acc[NMAT - 1][i][j][r] * inv;
+          const float v = SW ? silu_times(ga, ua) : ga;
           store_q8(v, col < a.N, row < a.M, nb < a.nblocks, a.q + (size_t)row * a.N + col,
                    a.qs + (size_t)row * a.nblocks + nb);
         }
@@ -562,10 +563,11 @@ static const PrefillInstance kPrefill[] = {
     FN_PREFILL(4, 4, 4, 2, true, false, true, false, "prefill_swiglu_adaln_bf16_256x128_w4x2_xl"),
     FN_PREFILL(4, 8, 4, 2, false, false, false, true, "prefill_premod_bf16_256x256_w4x2_xl"),
     FN_PREFILL(4, 4, 4, 2, true, false, false, true, "prefill_swiglu_premod_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, false, true, "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"),
 };
 
 static const PrefillInstance& pick(bool sw, bool q8 = false, bool ad = false, bool ex = false) {
-  return kPrefill[ex ? (sw ? 6 : 5) : (ad ? (sw ? 4 : 3) : (q8 ? 2 : (sw ? 1 : 0)))];
+  return kPrefill[ex ? (q8 ? 7 : (sw ? 6 : 5)) : (ad ? (sw ? 4 : 3) : (q8 ? 2 : (sw ? 1 : 0)))];
 }
 
 // Largest AdaLN table the prefill kernel stages whole (8 rows per wave, the
@@ -578,7 +580,7 @@ FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, b
   (void)K;
   const PrefillInstance& d = pick(swiglu, q8, ad, ex);
   FusedPlan p{};
-  p.kind = ex ? 8 : (ad ? 7 : (q8 ? 5 : 1));
+  p.kind = ex ? (q8 ? 10 : 8) : (ad ? 7 : (q8 ? 5 : 1));
   p.mf = d.fm * d.wm;
   p.nf = d.fn_ * d.wn;
   p.waves = d.wm * d.wn;
@@ -619,9 +621,13 @@ hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const voi
 }
 
 hipError_t launch_prefill_premod(const FusedPlan& p, const void* u, const float* rs, const void* wg, const void* wu,
-                                 void* y, int M, int K, int N, const AdalnArgs& ad, hipStream_t stream) {
-  const PrefillInstance& d = pick(wu != nullptr, false, false, true);
+                                 void* y, int M, int K, int N, const AdalnArgs& ad, hipStream_t stream, uint8_t* q,
+                                 float* qs) {
+  if (q != nullptr && wu == nullptr) return hipErrorInvalidValue;
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, true);
   PrefillArgs a{};
+  a.q = q;
+  a.qs = qs;
   a.x = u;
   a.wg = wg;
   a.wu = wu;

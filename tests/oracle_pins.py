@@ -573,3 +573,50 @@ def check_adaln_fp8(o, seed=26):
 
 
 ALL_CHECKS += [check_adaln_fp8]
+
+
+def check_adaln_q8(o, seed=27):
+    """AdaLN with fp8 row-block output: with scales whose modulated operand
+    is exact in bf16 (scale in {0, 1, -1/2}) the block values are the
+    SwiGLU of the folded AdaLN form exactly, and the codes are
+    quantize_e4m3_row_blocks of them; zero tables and bias give the plain q8
+    path on the folded weights; an index outside the table takes scale 0
+    and bias 0; the fp8-weight form with E4M3-exact weights equals the
+    bf16-weight form."""
+    rng = np.random.default_rng(seed)
+    M, K, N, T = 5, 32, 40, 3
+    x = o.round_to_bf16(rng.standard_normal((M, K)))
+    Wg = o.round_to_bf16(rng.standard_normal((K, N)) / 4)
+    Wu = o.round_to_bf16(rng.standard_normal((K, N)) / 4)
+    sc = rng.choice([0.0, 1.0, -0.5], size=(T, K))
+    bg, bu = rng.standard_normal((T, N)), rng.standard_normal((T, N))
+    idx = rng.integers(0, T, M)
+    c, s, v = o.adaln_norm_proj_swiglu_q8(x, sc, idx, Wg, Wu, bg, bu, 1e-6)
+    a = o.adaln_norm_proj_folded(x, Wg, sc, bg, idx, 1e-6)
+    b = o.adaln_norm_proj_folded(x, Wu, sc, bu, idx, 1e-6)
+    _close(v, a / (1 + np.exp(-a)) * b, 1e-12, "AdaLN q8 values on an exact operand")
+    c2, s2 = o.quantize_e4m3_row_blocks(v)
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+    zt, zb = np.zeros((T, K)), np.zeros((T, N))
+    cz, sz, vz = o.adaln_norm_proj_swiglu_q8(x, zt, idx, Wg, Wu, zb, zb, 1e-6)
+    assert np.array_equal(vz, o.norm_proj_swiglu_folded(x, Wg, Wu, 1e-6))
+    bad = idx.copy()
+    bad[0], bad[-1] = -1, T
+    _, _, vb = o.adaln_norm_proj_swiglu_q8(x, sc, bad, Wg, Wu, bg, bu, 1e-6)
+    _, _, v0 = o.adaln_norm_proj_swiglu_q8(x[[0, M - 1]], zt, idx[[0, M - 1]], Wg, Wu, zb, zb, 1e-6)
+    assert np.array_equal(vb[[0, M - 1]], v0)
+    assert np.array_equal(vb[1:M - 1], v[1:M - 1])
+    # fp8 weights whose values are exact E4M3 values (column maxima 448 * 2^-6, so s = 2^-6)
+    pool = o.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    pick = rng.choice(pool, size=(K, N)) * rng.choice([-1.0, 1.0], size=(K, N))
+    pick[0, :] = 448.0
+    W8 = pick * np.ldexp(1.0, -6)
+    cg, sg, _ = o.quantize_e4m3_columns(W8.astype(np.float32))
+    cu, su, _ = o.quantize_e4m3_columns(W8[::-1].astype(np.float32).copy())
+    got = o.adaln_norm_proj_swiglu_fp8_q8(x, sc, idx, cg, sg, cu, su, bg, bu, 1e-6)
+    want = o.adaln_norm_proj_swiglu_q8(x, sc, idx, W8, W8[::-1], bg, bu, 1e-6)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    _close(got[2], want[2], 1e-13, "fp8-weight AdaLN q8 values")
+
+
+ALL_CHECKS += [check_adaln_q8]

@@ -449,8 +449,8 @@ def test_norm_proj_adaln_fp8_ws_rejects(lib, kwargs, status, needle):
 
 def test_adaln_fp8_sizes_and_names(lib):
     # needed for every M: the operand and 1/RMS, each rounded up to 256 bytes
-    assert lib.fn_adaln_fp8_workspace_bytes(4, 16) == 256 + 256
-    assert lib.fn_adaln_fp8_workspace_bytes(0, 16) == 0
+    assert lib.fn_adaln_prepass_bytes(4, 16) == 256 + 256
+    assert lib.fn_adaln_prepass_bytes(0, 16) == 0
     assert lib.fn_kernel_name_adaln_fp8(16, 4096, 12288, 4, 0).decode() == "decode_fp8_premod_m16_xlds_w3_u8"
     assert lib.fn_kernel_name_adaln_fp8(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_premod_m64_xlds_w4_u2"
     assert lib.fn_kernel_name_adaln_fp8(4096, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_premod_m64_xlds_w4_u2"
@@ -460,3 +460,45 @@ def test_adaln_fp8_sizes_and_names(lib):
               1e-6, 0x100000, 512, None) == NULL
     assert "W8_up, s_up or bias_up" in lib.fn_last_error().decode()
     assert sw(None, None, None, None, None, None, None, None, None, None, 0, 16, 16, 2, 1e-6, None, 0, None) == OK
+
+
+def _adq(lib, x=0x1000, sc=0x10000, idx=0x18000, wg=0x20000, bg=0x30000, wu=0x24000, bu=0x34000, c=0x40000,
+         s=0x48000, M=4, K=16, N=16, T=2, eps=1e-6, ws=0x100000, wsb=512):
+    return lib.fn_norm_proj_swiglu_adaln_q8_ws(x, sc, idx, wg, bg, wu, bu, c, s, M, K, N, T, eps, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(ws=None), WORKSPACE, "workspace is NULL"),
+    (dict(wsb=128), WORKSPACE, "workspace_bytes=128"),
+    (dict(ws=0x48000 - 256), ALIAS, "workspace overlaps"),
+    (dict(wu=None), NULL, "gate or up weights or bias rows"),
+    (dict(bu=None), NULL, "gate or up weights or bias rows"),
+    (dict(c=None), NULL, "out_codes or out_scales"),
+    (dict(s=0x48002), ALIGN, "out_scales"),
+    (dict(bg=0x30002), ALIGN, "idx, scales and bias"),
+    (dict(c=0x34000), ALIAS, "an output overlaps"),
+    (dict(s=0x40008), ALIAS, "out_codes overlaps out_scales"),
+    (dict(T=0), SHAPE, "T=0"),
+])
+def test_norm_proj_swiglu_adaln_q8_ws_rejects(lib, kwargs, status, needle):
+    assert _adq(lib, **kwargs) == status
+    assert needle in lib.fn_last_error().decode()
+
+
+def test_adaln_q8_names_and_fp8(lib):
+    assert lib.fn_kernel_name_adaln_q8(16, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m16_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln_q8(64, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m64_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln_q8(65, 4096, 11008, 4, 0).decode() == "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"
+    assert lib.fn_kernel_name_adaln_q8(4096, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_q8_premod_m64_xlds_w4_u2"
+    assert lib.fn_kernel_name_adaln_q8(0, 4096, 16, 4, 0) == b"invalid"
+    f = lib.fn_norm_proj_swiglu_adaln_fp8_q8_ws
+    args = [0x1000, 0x10000, 0x18000, 0x20000, 0x22000, 0x30000, 0x24000, 0x26000, 0x34000, 0x40000, 0x48000,
+            4, 16, 16, 2, 1e-6, 0x100000, 512, None]
+    bad = list(args)
+    bad[4] = None
+    assert f(*bad) == NULL and "s_gate or s_up" in lib.fn_last_error().decode()
+    bad = list(args)
+    bad[16] = None
+    assert f(*bad) == WORKSPACE
+    assert f(None, None, None, None, None, None, None, None, None, None, None, 0, 16, 16, 2, 1e-6, None, 0,
+             None) == OK

@@ -145,7 +145,7 @@ def test_adaln_fp8_repeatable(gpu_lib, M, N, swiglu):
     _, Wg, Wu, Pg, Pu = _weights(fn, K, N, swiglu, gen, fp8=True)
     sc, sh = _rand((T, K), gen, 0.3), _rand((T, K), gen, 0.3)
     idx = torch.randint(0, T, (M,), generator=gen, device="cuda", dtype=torch.int32)
-    ws = torch.empty((fn.adaln_fp8_workspace_bytes(M, K),), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((fn.adaln_prepass_bytes(M, K),), dtype=torch.uint8, device="cuda")
     bg = fn.adaln_shift_bias(sh, Wg)
     if swiglu:
         bu = fn.adaln_shift_bias(sh, Wu)
@@ -153,3 +153,20 @@ def test_adaln_fp8_repeatable(gpu_lib, M, N, swiglu):
     else:
         call = lambda: fn.norm_proj_adaln_fp8_ws(x, sc, idx, Pg, bg, 1e-6, workspace=ws)                  # noqa: E731
     _repeat(call, lambda y: [y])
+
+
+@pytest.mark.parametrize("M,f8", [(64, False), (4096, False), (64, True)])
+def test_adaln_q8_repeatable(gpu_lib, M, f8):
+    import torch
+    fn = gpu_lib
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(80 + M)
+    K, N, T = 4096, 11008, 4
+    x = _rand((M, K), gen)
+    _, Wg, Wu, Pg, Pu = _weights(fn, K, N, True, gen, fp8=f8)
+    sc, sh = _rand((T, K), gen, 0.3), _rand((T, K), gen, 0.3)
+    idx = torch.randint(0, T, (M,), generator=gen, device="cuda", dtype=torch.int32)
+    ws = torch.empty((fn.adaln_prepass_bytes(M, K),), dtype=torch.uint8, device="cuda")
+    bg, bu = fn.adaln_shift_bias(sh, Wg), fn.adaln_shift_bias(sh, Wu)
+    f = fn.norm_proj_swiglu_adaln_fp8_q8_ws if f8 else fn.norm_proj_swiglu_adaln_q8_ws
+    _repeat(lambda: f(x, sc, idx, Pg, bg, Pu, bu, 1e-6, workspace=ws), lambda r: list(r))

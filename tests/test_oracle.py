@@ -78,6 +78,10 @@ MUTANTS = {
         x, c, s, sc, np.zeros_like(np.asarray(b, float)), idx, eps)),
     "adaln fp8 modulation dropped": ("adaln_norm_proj_fp8", lambda x, c, s, sc, b, idx, eps: _adaln_fp8_ref(
         x, c, s, np.zeros_like(np.asarray(sc, float)), b, idx, eps)),
+    "adaln q8 on the unrounded operand": ("adaln_operand", lambda x, sc, idx: np.asarray(x, float) * (
+        1 + O._rows_or_zero(sc, idx))),
+    "adaln q8 bias on the wrong rows": ("_rows_or_zero", lambda t, idx: np.asarray(t, float)[
+        (np.asarray(idx) + 1) % np.asarray(t).shape[0]]),
     "q8 scale inverted": ("dequantize_row_blocks", lambda c, s, block=16: _deq_ref(c, 1.0 / np.asarray(s, float),
                                                                                  block)),
 }
