@@ -122,6 +122,8 @@ KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": (
                   "ffn_decode_fp8_q8": ("decode_x.hip", "fn_device.h"), "qkv_decode_adaln": ("decode_x.hip", "fn_device.h"),
                   "qkv_decode_fp8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
                   "ffn_decode_fp8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
+                  "ffn_decode_q8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
+                  "ffn_decode_fp8_q8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
                   "ffn_decode_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"), "prefill_qkv_adaln": ("prefill.hip", "adaln.hip", "fn_device.h")}
 DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
 
@@ -209,8 +211,16 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False, adaln=Fa
         idx = idx[:rows]
         if fp8:
             bias8 = [oracle.adaln_shift_bias(sh, inp.W)] + ([oracle.adaln_shift_bias(sh, inp.W_up)] if call.swiglu else [])
+    if adaln and q8:
+        rbg, rbu = oracle.adaln_shift_bias(sh, inp.W), oracle.adaln_shift_bias(sh, inp.W_up)
+        if not fp8:
+            Wgf, Wuf = oracle.fold_weights(inp.g, inp.W, call.dtype), oracle.fold_weights(inp.g, inp.W_up, call.dtype)
     while True:
-        if adaln and fp8 and call.swiglu:
+        if adaln and q8 and fp8:
+            oracle.adaln_norm_proj_swiglu_fp8_q8(x, sc, idx, w8[0][0], w8[0][1], w8[1][0], w8[1][1], rbg, rbu, call.eps)
+        elif adaln and q8:
+            oracle.adaln_norm_proj_swiglu_q8(x, sc, idx, Wgf, Wuf, rbg, rbu, call.eps)
+        elif adaln and fp8 and call.swiglu:
             oracle.adaln_norm_proj_swiglu_fp8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], sc, bias8[0], bias8[1], idx,
                                               call.eps)
         elif adaln and fp8:
@@ -296,7 +306,8 @@ def run_single(args, torch, fn, workloads):
         bg_t = fn.adaln_shift_bias(sh_t, Wg)
         bu_t = fn.adaln_shift_bias(sh_t, Wu) if call.swiglu else None
         # the two-launch form above 16 rows, and with fp8 weights (pre-pass into a workspace allocated here, once)
-        nws = fn.adaln_prepass_bytes(call.M, call.K) if fp8 else fn.adaln_workspace_bytes(call.M, call.K)
+        nws = (fn.adaln_prepass_bytes(call.M, call.K) if fp8 or args.output == "q8" else
+               fn.adaln_workspace_bytes(call.M, call.K))
         ws_t = torch.empty((nws,), dtype=torch.uint8, device="cuda") if nws else None
         f1, f2 = ((fn.norm_proj_adaln_fp8_ws, fn.norm_proj_swiglu_adaln_fp8_ws) if fp8 else
                   (fn.norm_proj_adaln_ws, fn.norm_proj_swiglu_adaln_ws))
@@ -308,8 +319,13 @@ def run_single(args, torch, fn, workloads):
         # SwiGLU quantised in the epilogue: E4M3 codes + row-block scales
         qout = (torch.empty((call.M, call.N), dtype=torch.uint8, device="cuda"),
                 torch.empty((call.M, -(-call.N // 16)), dtype=torch.float32, device="cuda"))
-        proj_q8 = fn.norm_proj_swiglu_fp8_q8 if fp8 else fn.norm_proj_swiglu_q8
-        proj_sw = lambda x_, a_, b_, e_, out=None: proj_q8(x_, a_, b_, e_, out=qout)  # noqa: E731
+        if adaln:
+            fq = fn.norm_proj_swiglu_adaln_fp8_q8_ws if fp8 else fn.norm_proj_swiglu_adaln_q8_ws
+            proj_sw = lambda x_, a_, b_, e_, out=None: fq(  # noqa: E731
+                x_, sc_t, idx_t, a_, bg_t, b_, bu_t, e_, out=qout, workspace=ws_t)
+        else:
+            proj_q8 = fn.norm_proj_swiglu_fp8_q8 if fp8 else fn.norm_proj_swiglu_q8
+            proj_sw = lambda x_, a_, b_, e_, out=None: proj_q8(x_, a_, b_, e_, out=qout)  # noqa: E731
 
     if call.swiglu:
         def fused(i):
@@ -526,9 +542,8 @@ def main(argv=None):
         print(f"bench.py: --output q8 applies to the SwiGLU workload ffn_decode, not {args.workload}", file=sys.stderr)
         return 2
     adaln = args.prologue == "adaln"
-    if adaln and (q8 or args.workload not in ("qkv_decode", "ffn_decode", "prefill_qkv")):
-        print("bench.py: --prologue adaln applies to qkv_decode, ffn_decode and prefill_qkv with bf16 output",
-              file=sys.stderr)
+    if adaln and args.workload not in ("qkv_decode", "ffn_decode", "prefill_qkv"):
+        print("bench.py: --prologue adaln applies to qkv_decode, ffn_decode and prefill_qkv", file=sys.stderr)
         return 2
     suffix = ("_fp8" if fp8 else "") + ("_q8" if q8 else "") + ("_adaln" if adaln else "")
 
@@ -551,7 +566,8 @@ def main(argv=None):
         call, inp, r = run_single(args, torch, fn, workloads)
         bytes_call = call_bytes(call, fp8, q8) + (adaln_extra_bytes(call) if adaln else 0)
         flops_call = call.flops()
-        kernel = (fn.kernel_name_adaln_fp8(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln and fp8 else
+        kernel = (fn.kernel_name_adaln_q8(call.M, call.K, call.N, ADALN_T, fp8) if adaln and q8 else
+                  fn.kernel_name_adaln_fp8(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln and fp8 else
                   fn.kernel_name_adaln_ws(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln else
                   fn.kernel_name_q8(call.M, call.K, call.N, fp8) if q8 else
                   fn.kernel_name_fp8(call.M, call.K, call.N, call.swiglu) if fp8 else
@@ -588,7 +604,7 @@ def main(argv=None):
         if adaln:
             config["prologue"] = (f"AdaLN: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx], tables of {ADALN_T} rows, "
                                   "per-row index" + (", two launches (adaln_modulate pre-pass, then the kernel named)"
-                                                     if fp8 or fn.adaln_workspace_bytes(call.M, call.K) else
+                                                     if fp8 or q8 or fn.adaln_workspace_bytes(call.M, call.K) else
                                                      ", one launch"))
 
     if args.measured_peak and roof["bound"] in ("hbm", "mfma") and unit != "us/call":
