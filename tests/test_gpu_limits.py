@@ -1,0 +1,99 @@
+"""GPU parity at the size limits the C ABI accepts, with the other
+dimensions kept small: K at its maximum (2^20, the longest k loops and the
+largest in-buffer offsets of every kernel family), very wide N (4097
+column blocks) and many rows (65539: thousands of row tiles and pre-pass
+workgroups), each against the float64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.gpu_helpers import assert_close, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+K_MAX = 1 << 20
+
+
+def _plain(fn, M, K, N, dtype, swiglu, seed):
+    inp = W.random_inputs(M, K, N, dtype, seed=seed, swiglu=swiglu)
+    x, g = to_dev(inp.x, dtype), to_dev(inp.g, dtype)
+    Pg = fn.fold_weights(g, to_dev(inp.W, dtype))
+    if swiglu:
+        Pu = fn.fold_weights(g, to_dev(inp.W_up, dtype))
+        y = fn.norm_proj_swiglu(x, Pg, Pu, inp.call.eps)
+        ref = oracle.norm_proj_swiglu(inp.x, inp.g, inp.W, inp.W_up, inp.call.eps)
+    else:
+        y = fn.norm_proj(x, Pg, inp.call.eps)
+        ref = oracle.norm_proj(inp.x, inp.g, inp.W, inp.call.eps)
+    return to_f64(y), ref
+
+
+def _fp8(fn, M, K, N, swiglu, seed):
+    inp = W.random_inputs(M, K, N, "bf16", seed=seed, swiglu=swiglu)
+    x, g = to_dev(inp.x, "bf16"), to_dev(inp.g, "bf16")
+    Pg = fn.fold_weights_fp8(g, to_dev(inp.W, "bf16"))
+    cg, sg = oracle.fold_weights_fp8(inp.g, inp.W, "bf16")
+    if swiglu:
+        Pu = fn.fold_weights_fp8(g, to_dev(inp.W_up, "bf16"))
+        cu, su = oracle.fold_weights_fp8(inp.g, inp.W_up, "bf16")
+        y = fn.norm_proj_swiglu_fp8(x, Pg, Pu, inp.call.eps)
+        ref = oracle.norm_proj_swiglu_fp8(inp.x, cg, sg, cu, su, inp.call.eps)
+    else:
+        y = fn.norm_proj_fp8(x, Pg, inp.call.eps)
+        ref = oracle.norm_proj_fp8(inp.x, cg, sg, inp.call.eps)
+    return to_f64(y), ref
+
+
+@pytest.mark.parametrize("M,swiglu,dtype", [(1, False, "bf16"), (16, True, "bf16"), (33, False, "bf16"),
+                                            (64, True, "bf16"), (65, False, "bf16"), (4, False, "f32")])
+def test_max_k(gpu_lib, M, swiglu, dtype):
+    y, ref = _plain(gpu_lib, M, K_MAX, 24, dtype, swiglu, seed=M + 1)
+    if dtype == "bf16":
+        assert_close(y, ref, dtype, f"K=2^20 M={M} {dtype} swiglu={swiglu}")
+        return
+    # The fp32 rule (1e-5 relative) is stated for the 256-wide fp32 workload;
+    # independent fp32 rounding errors of a K-term sum grow as sqrt(K), so at
+    # K = 2^20 the same rule scales by sqrt(K / 256) = 64.
+    tol = 1e-5 * np.sqrt(K_MAX / 256)
+    err = np.max(np.abs(y - ref) / (np.abs(ref) + 1.0))
+    assert np.all(np.isfinite(y)) and err <= tol, f"fp32 K=2^20: {err:.3e} > {tol:.1e}"
+
+
+@pytest.mark.parametrize("M,swiglu", [(16, False), (64, True)])
+def test_max_k_fp8(gpu_lib, M, swiglu):
+    y, ref = _fp8(gpu_lib, M, K_MAX, 24, swiglu, seed=M + 2)
+    assert_close(y, ref, "bf16", f"fp8 K=2^20 M={M} swiglu={swiglu}")
+
+
+@pytest.mark.parametrize("M,swiglu", [(16, False), (64, True), (300, False)])
+def test_wide_n(gpu_lib, M, swiglu):
+    y, ref = _plain(gpu_lib, M, 72, 65552, "bf16", swiglu, seed=M + 3)
+    assert_close(y, ref, "bf16", f"N=65552 M={M} swiglu={swiglu}")
+
+
+@pytest.mark.parametrize("kind", ["bf16", "bf16_swiglu", "fp8"])
+def test_many_rows(gpu_lib, kind):
+    M = 65539
+    if kind == "fp8":
+        y, ref = _fp8(gpu_lib, M, 64, 48, False, seed=5)
+    else:
+        y, ref = _plain(gpu_lib, M, 64, 48, "bf16", kind.endswith("swiglu"), seed=6)
+    assert_close(y, ref, "bf16", f"M={M} {kind}")
+
+
+@pytest.mark.parametrize("M,K,N,T", [(65, K_MAX, 24, 3), (40, K_MAX, 24, 2), (65539, 64, 48, 5)])
+def test_adaln_two_launch_limits(gpu_lib, M, K, N, T):
+    """The AdaLN pre-pass and the projection on the modulated operand at the
+    longest rows (K = 2^20: 2048 chunks per lane) and the most rows."""
+    fn = gpu_lib
+    inp = W.random_inputs(M, K, N, "bf16", seed=M + K + T)
+    scale, shift, idx = W.adaln_tables(T, K, M, seed=7)
+    x, g = to_dev(inp.x, "bf16"), to_dev(inp.g, "bf16")
+    sc, sh = to_dev(scale, "bf16"), to_dev(shift, "bf16")
+    Wg = to_dev(inp.W, "bf16")
+    import torch
+    y = fn.norm_proj_adaln_ws(x, sc, torch.from_numpy(idx.astype(np.int32)).cuda(), fn.fold_weights(g, Wg),
+                              fn.adaln_shift_bias(sh, Wg), inp.call.eps)
+    ref = oracle.adaln_norm_proj(inp.x, inp.g, scale, shift, idx, inp.W, inp.call.eps)
+    assert_close(to_f64(y), ref, "bf16", f"adaln two-launch M={M} K={K}")
