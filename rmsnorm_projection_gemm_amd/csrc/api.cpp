@@ -125,6 +125,12 @@ fn_status fp8_common(const void* x, const void* wg, const float* sg, const void*
       (swiglu && (overlap(y, yb, wu, wb) || overlap(y, yb, su, sb))))
     return fail(FN_ERR_ALIAS, "output overlaps an input");
   if (check_only) return FN_OK;
+  if (M > 64) {
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, false, false, true);
+    return hip_status(fn::launch_prefill_fp8(plan, x, wg, sg, swiglu ? wu : nullptr, swiglu ? su : nullptr, y, (int)M,
+                                             (int)K, (int)N, eps, stream),
+                      plan.name);
+  }
   const fn::FusedPlan plan = fn::plan_fp8(M, K, N, swiglu);
   return hip_status(fn::launch_fp8(plan, x, wg, sg, swiglu ? wu : nullptr, swiglu ? su : nullptr, y, (int)M, (int)K,
                                    (int)N, eps, stream),
@@ -161,8 +167,12 @@ fn_status q8_common(const void* x, const void* wg, const float* sg, const void* 
   if (overlap(codes, cb, scales, qb)) return fail(FN_ERR_ALIAS, "out_codes overlaps out_scales");
   if (check_only) return FN_OK;
   uint8_t* q = static_cast<uint8_t*>(codes);
-  if (!f8 && M > 64) {
-    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true);
+  if (M > 64) {
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, false, f8);
+    if (f8)
+      return hip_status(fn::launch_prefill_fp8(plan, x, wg, sg, wu, su, nullptr, (int)M, (int)K, (int)N, eps, stream, q,
+                                               scales),
+                        plan.name);
     return hip_status(fn::launch_prefill(fn::DType::BF16, plan, x, wg, wu, nullptr, (int)M, (int)K, (int)N, eps,
                                          stream, q, scales),
                       plan.name);
@@ -297,6 +307,12 @@ fn_status adaln_fp8_ws_common(const void* x, const void* scale, const int* idx, 
   FN_TRY(hip_status(fn::launch_adaln_modulate(x, scale, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
                     "adaln_modulate"));
   const fn::AdalnArgs ad{nullptr, idx, bg, swiglu ? bu : nullptr, (int)T};
+  if (M > 64) {
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, false, true, true);
+    return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, ad,
+                                                stream, nullptr, nullptr, sg, swiglu ? su : nullptr),
+                      plan.name);
+  }
   const fn::FusedPlan plan = fn::plan_decode_premod(M, N, swiglu, true);
   return hip_status(fn::launch_decode_premod(plan, u, rs, wg, sg, swiglu ? wu : nullptr, swiglu ? su : nullptr, y,
                                              (int)M, (int)K, (int)N, ad, stream),
@@ -349,10 +365,10 @@ fn_status adaln_q8_ws_common(const void* x, const void* scale, const int* idx, c
                     "adaln_modulate"));
   const fn::AdalnArgs ad{nullptr, idx, bg, bu, (int)T};
   uint8_t* q = static_cast<uint8_t*>(codes);
-  if (!f8 && M > 64) {
-    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, true);
+  if (M > 64) {
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, true, f8);
     return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, wu, nullptr, (int)M, (int)K, (int)N, ad, stream, q,
-                                                qscales),
+                                                qscales, f8 ? sg : nullptr, f8 ? su : nullptr),
                       plan.name);
   }
   const fn::FusedPlan plan = fn::plan_decode_q8_premod(f8, M, N);
@@ -557,7 +573,7 @@ fn_status fn_norm_proj_swiglu_fp8_q8(const void* x, const void* W8_gate, const f
 
 const char* fn_kernel_name_q8(int64_t M, int64_t K, int64_t N, int fp8_weights) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
-  if (!fp8_weights && M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true).name;
+  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, false, fp8_weights != 0).name;
   return fn::plan_decode_q8(fp8_weights != 0, M, N).name;
 }
 
@@ -648,6 +664,7 @@ fn_status fn_norm_proj_swiglu_adaln_fp8_ws(const void* x, const void* scale, con
 
 const char* fn_kernel_name_adaln_fp8(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
+  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true, true).name;
   return fn::plan_decode_premod(M, N, swiglu != 0, true).name;
 }
 
@@ -672,7 +689,7 @@ fn_status fn_norm_proj_swiglu_adaln_fp8_q8_ws(const void* x, const void* scale, 
 
 const char* fn_kernel_name_adaln_q8(int64_t M, int64_t K, int64_t N, int64_t T, int fp8_weights) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
-  if (!fp8_weights && M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, true).name;
+  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, true, fp8_weights != 0).name;
   return fn::plan_decode_q8_premod(fp8_weights != 0, M, N).name;
 }
 
@@ -766,6 +783,7 @@ fn_status fn_step_destroy(fn_step step) {
 
 const char* fn_kernel_name_fp8(int64_t M, int64_t K, int64_t N, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
+  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, false, true).name;
   return fn::plan_fp8(M, K, N, swiglu != 0).name;
 }
 

@@ -18,7 +18,8 @@ struct FusedPlan {
                       // 4 = SwiGLU with fp8 output (x in LDS), 5 = the same on the prefill kernel,
                       // 6 = AdaLN prologue (x and scale rows in LDS), 7 = AdaLN on the prefill kernel,
                       // 8 = prefill on an operand modulated by the AdaLN pre-pass,
-                      // 9 = the same on the LDS-shared-x decode kernel, 10 = the same with fp8 output
+                      // 9 = the same on the LDS-shared-x decode kernel, 10 = the same with fp8 output,
+                      // 11 = the prefill kernel with fp8 weights
   int mf;             // 16-row fragments per workgroup (decode)
   int nf;             // 16-column fragments per workgroup (decode)
   int waves;          // waves per workgroup
@@ -53,8 +54,13 @@ struct AdalnArgs {
 // ad: AdaLN prologue (tables of at most 63 rows, prefill_adaln_fits).
 // ex: the prefill kernel on an operand the AdaLN pre-pass modulated (1/RMS
 // per row from the pre-pass, bias rows in the epilogue).
+// f8: fp8 (E4M3) weights with column scales (launch_prefill_fp8, or
+// launch_prefill_premod with scales).
 FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8 = false, bool ad = false,
-                       bool ex = false);
+                       bool ex = false, bool f8 = false);
+hipError_t launch_prefill_fp8(const FusedPlan& plan, const void* x, const void* wg, const float* sg, const void* wu,
+                              const float* su, void* y, int M, int K, int N, float eps, hipStream_t stream,
+                              uint8_t* q = nullptr, float* qs = nullptr);
 hipError_t launch_prefill(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
                           const void* w_up, void* y, int M, int K, int N, float eps,
                           hipStream_t stream, uint8_t* q = nullptr, float* qs = nullptr,
@@ -65,10 +71,11 @@ bool prefill_adaln_fits(int64_t T);
 // plan_prefill(..., ex = true); ad.scale unused).
 hipError_t launch_adaln_modulate(const void* x, const void* scale, const int* idx, int T, void* u, float* rs, int M,
                                  int K, float eps, hipStream_t stream);
-// q, qs: SwiGLU with fp8 row-block output (y unused).
+// q, qs: SwiGLU with fp8 row-block output (y unused); sg, su: fp8 weights.
 hipError_t launch_prefill_premod(const FusedPlan& plan, const void* u, const float* rs, const void* wg,
                                  const void* wu, void* y, int M, int K, int N, const AdalnArgs& ad,
-                                 hipStream_t stream, uint8_t* q = nullptr, float* qs = nullptr);
+                                 hipStream_t stream, uint8_t* q = nullptr, float* qs = nullptr,
+                                 const float* sg = nullptr, const float* su = nullptr);
 // SwiGLU with fp8 output on the pre-modulated operand (bf16 weights up to 64
 // rows, fp8 weights every M).
 FusedPlan plan_decode_q8_premod(bool f8_weights, int64_t M, int64_t N);

@@ -65,6 +65,8 @@ struct PrefillArgs {
   const float* bu;   // AdaLN: bias rows of W_up
   int T;
   const float* rs;   // EX: 1/RMS of each row [M], from the AdaLN pre-pass
+  const float* sg;   // F8: column scales of wg [N]
+  const float* su;   // F8: column scales of wu [N]
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -96,7 +98,16 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // the pre-pass already modulated, 1/RMS of each raw row comes from a.rs (no
 // Gram blocks), and the epilogue adds the row's bias rows; the loop is the
 // ping-pong one of the plain instances.
-template <int FM, int FN, int WM, int WN, bool SW, bool Q8, bool AD = false, bool EX = false>
+//
+// F8: fp8 (E4M3) weights with one scale per output column, packed in 1 KiB
+// fragments of 16 columns x 64 k (a pair of k-blocks, the lane's 16 bytes
+// holding its 8 codes of each).  W' then travels with x: both rings hold
+// pairs, filled together, and each B operand is the lane's 8 codes of the
+// k-block (ds_read_b64) decoded to bf16 in the memory slot
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1 is exact).  Per k-block a CU
+// moves 24 KiB of operands instead of 32 and its waves read 64 KiB of LDS
+// instead of 96; the column scale joins 1/RMS in the epilogue.
+template <int FM, int FN, int WM, int WN, bool SW, bool Q8, bool AD = false, bool EX = false, bool F8 = false>
 __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = SW ? 2 : 1;
@@ -116,6 +127,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   static_assert(!AD || !Q8, "AdaLN with bf16 output");
   static_assert(AD || NW == 8, "ping-pong: two groups of one wave per SIMD");
   static_assert(!EX || !AD, "pre-modulated operand: ping-pong loop");
+  static_assert(!F8 || !AD, "fp8 weights: ping-pong loop");
   constexpr bool BIAS = AD || EX;
 
   __shared__ __attribute__((aligned(1024))) uint8_t wring0[WSLOT];
@@ -139,7 +151,10 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int m0 = blockIdx.y * BMF * 16;
   const int nb0 = blockIdx.x * BNF;
-  const int64_t kfrag = (int64_t)a.kblocks * kFragBytes;
+  // bytes of one packed column block: a fragment per k-block (bf16) or per
+  // pair of k-blocks (fp8)
+  const int kpairs = (a.kblocks + 1) / 2;
+  const int64_t kfrag = (int64_t)(F8 ? kpairs : a.kblocks) * kFragBytes;
 
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(static_cast<const __bf16*>(a.x) + (size_t)m0 * a.K, (int64_t)min(BMF * 16, a.M - m0) * a.K * 2);
@@ -228,6 +243,19 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
                                                0);
     }
   };
+  // F8: the W' fragments of pair p (16 columns x 64 k each) into a pair slot
+  constexpr int WP8 = WPW;   // fragments per wave per pair (the bf16 count per k-block)
+  auto issue_w8 = [&](uint8_t* base, int p) __attribute__((always_inline)) {
+    const uint32_t win = (uint32_t)((p - kpairs) >> 31);
+#pragma unroll
+    for (int i = 0; i < WP8; ++i) {
+      const int f = wave + NW * i;
+      const int m = f / BNF, ni = f % BNF;
+      const uint32_t off = ((uint32_t)((ni * kpairs + p) * kFragBytes + lane * 16) & win) | (kOutOfRange & ~win);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(m == 0 ? wr0 : wr1, (lds_ptr)(base + f * kFragBytes), 16, off, 0, 0,
+                                               0);
+    }
+  };
   // LDS offset of this lane's x operand (row lrow, k-group lgrp) for k-block
   // u of the pair and row block rb
   auto x_at = [&](int u, int rb) __attribute__((always_inline)) -> int {
@@ -259,6 +287,30 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
       bv[j] = *reinterpret_cast<const u32x4*>(base + (m * BNF + wn * FN + jj) * kFragBytes + lane * 16);
     }
   };
+  // F8: this lane's 8 codes of k-block u of the pair for each B fragment,
+  // then (after lgkmcnt(0)) decoded exactly to the bf16 operands
+  uint32_t braw[F8 ? NB : 1][2];
+  auto read_b8 = [&](const uint8_t* base, int u) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int m = j / FN, jj = j % FN;
+      const uint2 w = *reinterpret_cast<const uint2*>(base + (m * BNF + wn * FN + jj) * kFragBytes + lane * 16 + u * 8);
+      braw[F8 ? j : 0][0] = w.x;
+      braw[F8 ? j : 0][1] = w.y;
+    }
+  };
+  auto decode_b8 = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bv[j][2 * h] = __builtin_bit_cast(uint32_t,
+                                          __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(braw[F8 ? j : 0][h], 1.0f, false));
+        bv[j][2 * h + 1] = __builtin_bit_cast(uint32_t,
+                                              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(braw[F8 ? j : 0][h], 1.0f, true));
+      }
+    }
+  };
   auto mfma_cols = [&](int j0, int j1) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = j0; j < j1; ++j)
@@ -274,7 +326,85 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
   };
 
-  if constexpr (!AD) {
+  if constexpr (F8) {
+    // Ping-pong with pairs: the same slots as below, but W' rides with x --
+    // pair p (k-blocks 2p, 2p+1) of both is loaded in slots 4p-5 (group A)
+    // and 4p-4 (group B) into pair slot p % 2, after group B's last read of
+    // pair p-2.  When the next k-block q opens a pair, that pair's loads are
+    // the newest this wave has issued, so all must have landed (vmcnt 0);
+    // when q is the second half, its pair landed before the previous slot.
+    auto compute = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_cols(0, NB);
+      if constexpr (!EX) squares();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto ready = [&](auto T4c) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T4c)::value;
+      if constexpr (T4 % 2 == 1) wait_vmcnt<0>();
+      else wait_vmcnt<XPW + WP8>();
+    };
+    auto issue_pair = [&](int slot, int p) __attribute__((always_inline)) {
+      issue_x(xslot(slot), p);
+      issue_w8(wslot(slot), p);
+    };
+    auto stepA = [&](auto T4c, int s) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T4c)::value;
+      compute();
+      ready(T4c);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(xslot(((T4 + 1) % 4) / 2), (T4 + 1) % 2);
+      read_b8(wslot(((T4 + 1) % 4) / 2), (T4 + 1) % 2);
+      if constexpr (T4 % 2 == 1) issue_pair(((T4 + 3) / 2) % 2, (s + 3) / 2);
+      lgkm0();
+      decode_b8();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+    };
+    auto stepB = [&](auto T4c, int s) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T4c)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(xslot(T4 / 2), T4 % 2);
+      read_b8(wslot(T4 / 2), T4 % 2);
+      if constexpr (T4 % 2 == 0) issue_pair(((T4 + 2) / 2) % 2, (s + 2) / 2);
+      lgkm0();
+      decode_b8();
+      ready(T4c);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      compute();
+      __builtin_amdgcn_s_barrier();
+    };
+    if (wave & 4) {
+      issue_pair(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      for (int s = 0; s < a.kblocks; s += 4) {
+        stepB(std::integral_constant<int, 0>{}, s);
+        stepB(std::integral_constant<int, 1>{}, s + 1);
+        stepB(std::integral_constant<int, 2>{}, s + 2);
+        stepB(std::integral_constant<int, 3>{}, s + 3);
+      }
+    } else {
+      issue_pair(0, 0);
+      issue_pair(1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<XPW + WP8>();
+      __builtin_amdgcn_s_barrier();
+      read_a(xring0, 0);
+      read_b8(wring0, 0);
+      lgkm0();
+      decode_b8();
+      for (int s = 0; s < a.kblocks; s += 4) {
+        stepA(std::integral_constant<int, 0>{}, s);
+        stepA(std::integral_constant<int, 1>{}, s + 1);
+        stepA(std::integral_constant<int, 2>{}, s + 2);
+        stepA(std::integral_constant<int, 3>{}, s + 3);
+      }
+    }
+  } else if constexpr (!AD) {
     // Ping-pong.  k-block s: group A (waves 0-3) reads it in slot 2s-1 and
     // computes it in slot 2s; group B (waves 4-7) reads it in slot 2s and
     // computes it in slot 2s+1.  A memory slot also issues the wave's share
@@ -484,6 +614,15 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   }
   __syncthreads();
 
+  // F8: this lane's column scales (its columns, both matrices)
+  float csc[NMAT][FN];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = min((nb0 + wn * FN + j) * 16 + lrow, a.N - 1);
+      csc[m][j] = F8 ? (m == 0 ? a.sg : a.su)[col] : 1.f;
+    }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&ssbuf[(wm * FM + i) * 16 + 4 * lgrp]);
@@ -520,8 +659,9 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
         for (int j = 0; j < FN; ++j) {
           const int nb = nb0 + wn * FN + j;
           const int col = nb * 16 + lrow;
-          const float ga = BIAS ? fmaf(acc[0][i][j][r], inv, bias[0][r][j]) : acc[0][i][j][r] * inv;
-          const float ua = BIAS ? fmaf(acc[NMAT - 1][i][j][r], inv, bias[NMAT - 1][r][j]) : acc[NMAT - 1][i][j][r] * inv;
+          const float i0 = F8 ? inv * csc[0][j] : inv, i1 = F8 ? inv * csc[NMAT - 1][j] : inv;
+          const float ga = BIAS ? fmaf(acc[0][i][j][r], i0, bias[0][r][j]) : acc[0][i][j][r] * i0;
+          const float ua = BIAS ? fmaf(acc[NMAT - 1][i][j][r], i1, bias[NMAT - 1][r][j]) : acc[NMAT - 1][i][j][r] * i1;
           const float v = SW ? silu_times(ga, ua) : ga;
           store_q8(v, col < a.N, row < a.M, nb < a.nblocks, a.q + (size_t)row * a.N + col,
                    a.qs + (size_t)row * a.nblocks + nb);
@@ -532,8 +672,9 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
         for (int j = 0; j < FN; ++j) {
           const int col = (nb0 + wn * FN + j) * 16 + lrow;
           if (col < a.N) {
-            const float ga = acc[0][i][j][r] * inv + bias[0][r][j];
-            const float ua = acc[NMAT - 1][i][j][r] * inv + bias[NMAT - 1][r][j];
+            const float i0 = F8 ? inv * csc[0][j] : inv, i1 = F8 ? inv * csc[NMAT - 1][j] : inv;
+            const float ga = acc[0][i][j][r] * i0 + bias[0][r][j];
+            const float ua = acc[NMAT - 1][i][j][r] * i1 + bias[NMAT - 1][r][j];
             const float v = SW ? silu_times(ga, ua) : ga;
             Store<__bf16>::one(yrow + col, v);
           }
@@ -546,28 +687,40 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
 struct PrefillInstance {
   const void* fn;
   int fm, fn_, wm, wn, ns;
-  bool sw;
+  bool sw, q8, ad, ex, f8;
   const char* name;
 };
 
-#define FN_PREFILL(FM, FN_, WM, WN, SW, Q8, AD, EX, NAME)                                                          \
-  PrefillInstance {                                                                                                 \
-    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, Q8, AD, EX>), FM, FN_, WM, WN, 4, SW, NAME \
+#define FN_PREFILL(FM, FN_, WM, WN, SW, Q8, AD, EX, F8, NAME)                                                 \
+  PrefillInstance {                                                                                          \
+    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, Q8, AD, EX, F8>), FM, FN_, WM, WN, 4, SW, \
+        Q8, AD, EX, F8, NAME                                                                                 \
   }
 
 static const PrefillInstance kPrefill[] = {
-    FN_PREFILL(4, 8, 4, 2, false, false, false, false, "prefill_bf16_256x256_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, false, false, false, "prefill_swiglu_bf16_256x128_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, true, false, false, "prefill_swiglu_bf16_q8_256x128_w4x2_xl"),
-    FN_PREFILL(4, 8, 4, 2, false, false, true, false, "prefill_adaln_bf16_256x256_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, false, true, false, "prefill_swiglu_adaln_bf16_256x128_w4x2_xl"),
-    FN_PREFILL(4, 8, 4, 2, false, false, false, true, "prefill_premod_bf16_256x256_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, false, false, true, "prefill_swiglu_premod_bf16_256x128_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, true, false, true, "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, false, false, false, "prefill_bf16_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, false, false, false, "prefill_swiglu_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, false, false, false, "prefill_swiglu_bf16_q8_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, true, false, false, "prefill_adaln_bf16_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, true, false, false, "prefill_swiglu_adaln_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, false, true, false, "prefill_premod_bf16_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, false, true, false, "prefill_swiglu_premod_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, false, true, false, "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"),
+    // fp8 (E4M3) weights with column scales
+    FN_PREFILL(4, 8, 4, 2, false, false, false, false, true, "prefill_fp8_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, false, false, true, "prefill_swiglu_fp8_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, false, false, true, "prefill_swiglu_fp8_q8_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, false, true, true, "prefill_fp8_premod_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, false, true, true, "prefill_swiglu_fp8_premod_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, false, true, true, "prefill_swiglu_fp8_q8_premod_256x128_w4x2_xl"),
 };
 
-static const PrefillInstance& pick(bool sw, bool q8 = false, bool ad = false, bool ex = false) {
-  return kPrefill[ex ? (q8 ? 7 : (sw ? 6 : 5)) : (ad ? (sw ? 4 : 3) : (q8 ? 2 : (sw ? 1 : 0)))];
+// The instance with exactly these flags (q8 implies SwiGLU); the plain
+// projection when none matches.
+static const PrefillInstance& pick(bool sw, bool q8 = false, bool ad = false, bool ex = false, bool f8 = false) {
+  for (const PrefillInstance& d : kPrefill)
+    if (d.sw == (sw || q8) && d.q8 == q8 && d.ad == ad && d.ex == ex && d.f8 == f8) return d;
+  return kPrefill[0];
 }
 
 // Largest AdaLN table the prefill kernel stages whole (8 rows per wave, the
@@ -575,12 +728,12 @@ static const PrefillInstance& pick(bool sw, bool q8 = false, bool ad = false, bo
 constexpr int kPrefillAdalnMaxT = 8 * 8 - 1;
 bool prefill_adaln_fits(int64_t T) { return T >= 1 && T <= kPrefillAdalnMaxT; }
 
-FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8, bool ad, bool ex) {
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8, bool ad, bool ex, bool f8) {
   (void)dt;
   (void)K;
-  const PrefillInstance& d = pick(swiglu, q8, ad, ex);
+  const PrefillInstance& d = pick(swiglu, q8, ad, ex, f8);
   FusedPlan p{};
-  p.kind = ex ? (q8 ? 10 : 8) : (ad ? 7 : (q8 ? 5 : 1));
+  p.kind = f8 ? 11 : (ex ? (q8 ? 10 : 8) : (ad ? 7 : (q8 ? 5 : 1)));
   p.mf = d.fm * d.wm;
   p.nf = d.fn_ * d.wn;
   p.waves = d.wm * d.wn;
@@ -605,6 +758,8 @@ hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const voi
   a.rs = nullptr;
   a.q = q;
   a.qs = qs;
+  a.sg = nullptr;
+  a.su = nullptr;
   a.x = x;
   a.wg = wg;
   a.wu = wu;
@@ -620,12 +775,40 @@ hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const voi
   return hipLaunchKernel(d.fn, p.grid, p.block, args, 0, stream);
 }
 
+hipError_t launch_prefill_fp8(const FusedPlan& p, const void* x, const void* wg, const float* sg, const void* wu,
+                              const float* su, void* y, int M, int K, int N, float eps, hipStream_t stream, uint8_t* q,
+                              float* qs) {
+  if ((q != nullptr && wu == nullptr) || sg == nullptr || (wu != nullptr && su == nullptr)) return hipErrorInvalidValue;
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, false, true);
+  PrefillArgs a{};
+  a.x = x;
+  a.wg = wg;
+  a.wu = wu;
+  a.y = y;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.kblocks = (int)ceil_div(K, 32);
+  a.nblocks = (int)ceil_div(N, 16);
+  a.eps = eps;
+  a.q = q;
+  a.qs = qs;
+  a.sg = sg;
+  a.su = su;
+  void* args[] = {&a};
+  return hipLaunchKernel(d.fn, p.grid, p.block, args, 0, stream);
+}
+
 hipError_t launch_prefill_premod(const FusedPlan& p, const void* u, const float* rs, const void* wg, const void* wu,
                                  void* y, int M, int K, int N, const AdalnArgs& ad, hipStream_t stream, uint8_t* q,
-                                 float* qs) {
+                                 float* qs, const float* sg, const float* su) {
   if (q != nullptr && wu == nullptr) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, true);
+  const bool f8 = sg != nullptr;
+  if (f8 && wu != nullptr && su == nullptr) return hipErrorInvalidValue;
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, true, f8);
   PrefillArgs a{};
+  a.sg = sg;
+  a.su = su;
   a.q = q;
   a.qs = qs;
   a.x = u;

@@ -174,7 +174,9 @@ def test_fp8_kernel_names(lib):
     assert lib.fn_kernel_name_fp8(16, 4096, 12288, 0).decode().startswith("decode_fp8_m16")
     assert lib.fn_kernel_name_fp8(17, 4096, 12288, 0).decode().startswith("decode_fp8_m32")
     assert lib.fn_kernel_name_fp8(64, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_m64")
-    assert lib.fn_kernel_name_fp8(4096, 4096, 12288, 1).decode().startswith("decode_swiglu_fp8_m64")
+    # above 64 rows the prefill kernel with fp8 weights
+    assert lib.fn_kernel_name_fp8(65, 4096, 12288, 0).decode() == "prefill_fp8_256x256_w4x2_xl"
+    assert lib.fn_kernel_name_fp8(4096, 4096, 12288, 1).decode() == "prefill_swiglu_fp8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_fp8(0, 4096, 16, 0) == b"invalid"
 
 
@@ -308,7 +310,8 @@ def test_q8_kernel_names(lib):
     assert lib.fn_kernel_name_q8(16, 4096, 11008, 0).decode() == "decode_swiglu_bf16_q8_m16_xlds_w3_u2"
     assert lib.fn_kernel_name_q8(64, 4096, 11008, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
     assert lib.fn_kernel_name_q8(65, 4096, 11008, 0).decode().startswith("prefill_swiglu_bf16_q8")
-    assert lib.fn_kernel_name_q8(4096, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_q8_m64")
+    assert lib.fn_kernel_name_q8(64, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_q8_m64")
+    assert lib.fn_kernel_name_q8(4096, 4096, 11008, 1).decode() == "prefill_swiglu_fp8_q8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_q8(0, 4096, 16, 0) == b"invalid"
 
 
@@ -453,7 +456,8 @@ def test_adaln_fp8_sizes_and_names(lib):
     assert lib.fn_adaln_prepass_bytes(0, 16) == 0
     assert lib.fn_kernel_name_adaln_fp8(16, 4096, 12288, 4, 0).decode() == "decode_fp8_premod_m16_xlds_w3_u8"
     assert lib.fn_kernel_name_adaln_fp8(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_premod_m64_xlds_w4_u2"
-    assert lib.fn_kernel_name_adaln_fp8(4096, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_premod_m64_xlds_w4_u2"
+    assert lib.fn_kernel_name_adaln_fp8(4096, 4096, 11008, 4, 1).decode() == "prefill_swiglu_fp8_premod_256x128_w4x2_xl"
+    assert lib.fn_kernel_name_adaln_fp8(65, 4096, 12288, 4, 0).decode() == "prefill_fp8_premod_256x256_w4x2_xl"
     assert lib.fn_kernel_name_adaln_fp8(0, 4096, 16, 4, 0) == b"invalid"
     sw = lib.fn_norm_proj_swiglu_adaln_fp8_ws
     assert sw(0x1000, 0x10000, 0x18000, 0x20000, 0x28000, 0x30000, 0x21000, None, 0x31000, 0x40000, 4, 16, 16, 2,
@@ -489,7 +493,8 @@ def test_adaln_q8_names_and_fp8(lib):
     assert lib.fn_kernel_name_adaln_q8(16, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m16_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln_q8(64, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m64_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln_q8(65, 4096, 11008, 4, 0).decode() == "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"
-    assert lib.fn_kernel_name_adaln_q8(4096, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_q8_premod_m64_xlds_w4_u2"
+    assert lib.fn_kernel_name_adaln_q8(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_q8_premod_m64_xlds_w4_u2"
+    assert lib.fn_kernel_name_adaln_q8(4096, 4096, 11008, 4, 1).decode() == "prefill_swiglu_fp8_q8_premod_256x128_w4x2_xl"
     assert lib.fn_kernel_name_adaln_q8(0, 4096, 16, 4, 0) == b"invalid"
     f = lib.fn_norm_proj_swiglu_adaln_fp8_q8_ws
     args = [0x1000, 0x10000, 0x18000, 0x20000, 0x22000, 0x30000, 0x24000, 0x26000, 0x34000, 0x40000, 0x48000,

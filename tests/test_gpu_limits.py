@@ -60,7 +60,7 @@ def test_max_k(gpu_lib, M, swiglu, dtype):
     assert np.all(np.isfinite(y)) and err <= tol, f"fp32 K=2^20: {err:.3e} > {tol:.1e}"
 
 
-@pytest.mark.parametrize("M,swiglu", [(16, False), (64, True)])
+@pytest.mark.parametrize("M,swiglu", [(16, False), (64, True), (65, False), (130, True)])
 def test_max_k_fp8(gpu_lib, M, swiglu):
     y, ref = _fp8(gpu_lib, M, K_MAX, 24, swiglu, seed=M + 2)
     assert_close(y, ref, "bf16", f"fp8 K=2^20 M={M} swiglu={swiglu}")

@@ -170,3 +170,14 @@ def test_adaln_q8_repeatable(gpu_lib, M, f8):
     bg, bu = fn.adaln_shift_bias(sh, Wg), fn.adaln_shift_bias(sh, Wu)
     f = fn.norm_proj_swiglu_adaln_fp8_q8_ws if f8 else fn.norm_proj_swiglu_adaln_q8_ws
     _repeat(lambda: f(x, sc, idx, Pg, bg, Pu, bu, 1e-6, workspace=ws), lambda r: list(r))
+
+
+def test_fp8_prefill_qkv_repeatable(gpu_lib):
+    import torch
+    fn = gpu_lib
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(92)
+    M, K, N = 4096, 4096, 12288
+    x = _rand((M, K), gen)
+    _, _, _, Pg, _ = _weights(fn, K, N, False, gen, fp8=True)
+    _repeat(lambda: fn.norm_proj_fp8(x, Pg, 1e-6), lambda y: [y])
