@@ -124,7 +124,9 @@ KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": (
                   "ffn_decode_fp8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
                   "ffn_decode_q8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
                   "ffn_decode_fp8_q8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
-                  "ffn_decode_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"), "prefill_qkv_adaln": ("prefill.hip", "adaln.hip", "fn_device.h")}
+                  "ffn_decode_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"), "prefill_qkv_adaln": ("prefill.hip", "adaln.hip", "fn_device.h"),
+                  "prefill_qkv_fp8": ("prefill.hip", "fn_device.h"),
+                  "prefill_qkv_fp8_adaln": ("prefill.hip", "adaln.hip", "fn_device.h")}
 DEFAULT_KERNEL_SOURCES = ("decode.hip", "fn_device.h")
 
 
@@ -534,8 +536,8 @@ def main(argv=None):
         calibrate_copy(torch)
         return 0
     fp8 = args.weights == "fp8"
-    if fp8 and args.workload in ("tiny", "prefill_qkv"):
-        print(f"bench.py: --weights fp8 applies to the bf16 decode workloads, not {args.workload}", file=sys.stderr)
+    if fp8 and args.workload == "tiny":
+        print(f"bench.py: --weights fp8 applies to the bf16 workloads, not {args.workload}", file=sys.stderr)
         return 2
     q8 = args.output == "q8"
     if q8 and args.workload != "ffn_decode":

@@ -205,7 +205,10 @@ fn_status fn_fold_weights_fp8(const void* g, const void* W, void* W8_packed, flo
 /* Fused RMSNorm + projection with fp8 weights, one launch:
  *   y[m][n] = round_bf16( s[n] * (sum_k x[m][k] * q[k][n]) / sqrt(sum_k x[m][k]^2 / K + eps) )
  * x: [M,K] bf16; W8_packed, scales: from fn_fold_weights_fp8 for this K, N;
- * y: [M,N] bf16, fully overwritten.  scales must be 4-byte aligned. */
+ * y: [M,N] bf16, fully overwritten.  scales must be 4-byte aligned.
+ * Instances: the LDS-shared-x decode kernel up to 64 rows, the prefill
+ * kernel with fp8 weights above (the codes decoded exactly to bf16 operands
+ * inside the k loop). */
 fn_status fn_norm_proj_fp8(const void* x, const void* W8_packed, const float* scales, void* y,
                            int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream);
 
@@ -246,8 +249,8 @@ const char* fn_kernel_name(int64_t M, int64_t K, int64_t N, int swiglu, fn_dtype
  * out_codes:  [M,N] row-major bytes, fully overwritten (no alignment needed).
  * out_scales: [M, ceil(N/16)] row-major fp32, 4-byte aligned, fully
  *             overwritten.
- * x is bf16.  Instances: the LDS-shared-x decode kernel up to 64 rows (any
- * M with fp8 weights), the prefill kernel above 64 rows (bf16 weights).
+ * x is bf16.  Instances: the LDS-shared-x decode kernel up to 64 rows, the
+ * prefill kernel above (bf16 or fp8 weights).
  * ------------------------------------------------------------------------- */
 
 /* bf16 packed weights (fn_fold_weights with FN_BF16). */
@@ -347,11 +350,11 @@ const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, 
 
 /* AdaLN with fp8 weights (fn_fold_weights_fp8: E4M3 codes, one scale per
  * output column), in two launches for every M: the pre-pass above, then the
- * fp8-weight decode kernel of the row count on the modulated operand, with
- *   y[m] = s * (u[m] * q) / RMS(x[m]) + bias[idx[m]]
- * (rows past 64 tile over the grid, each 64-row tile streaming the codes
- * again, as in fn_norm_proj_fp8).  The pages' AdaLN FC1 kernel is an fp8
- * kernel with pre-processed weights and scales ([FlashInfer #5521] "Fused
+ * fp8-weight kernel of the row count on the modulated operand (decode up to
+ * 64 rows, prefill above), with
+ *   y[m] = s * (u[m] * q) / RMS(x[m]) + bias[idx[m]].
+ * The pages' AdaLN FC1 kernel is an fp8 kernel with pre-processed weights
+ * and scales ([FlashInfer #5521] "Fused
  * Kernel on SM120").  bias rows come from fn_adaln_shift_bias on the
  * unfolded bf16 W.  Arguments as fn_norm_proj_fp8 / fn_norm_proj_swiglu_fp8
  * plus scale, idx, bias and T as in the AdaLN calls above; workspace: at
@@ -382,9 +385,8 @@ const char* fn_kernel_name_adaln_fp8(int64_t M, int64_t K, int64_t N, int64_t T,
 /* AdaLN + gate/up projections + SwiGLU with fp8 row-block output (E4M3
  * codes, one fp32 scale per 16-column row block, as fn_norm_proj_swiglu_q8),
  * in two launches for every M: the pre-pass, then the q8 kernel of the row
- * count on the modulated operand (bf16 weights: the LDS-shared-x decode
- * kernel up to 64 rows, the prefill kernel above; fp8 weights: the fp8
- * decode kernel).  The AdaLN FC1 block of [FlashInfer #5521] ("Segmented
+ * count on the modulated operand (the LDS-shared-x decode kernel up to 64
+ * rows, the prefill kernel above, with bf16 or fp8 weights).  The AdaLN FC1 block of [FlashInfer #5521] ("Segmented
  * Chain": norm + AdaLN, FC1, SwiGLU, quantisation for the next projection)
  * with the output format of [FlashInfer #4040] as read for
  * fn_norm_proj_swiglu_q8.  The block values are
