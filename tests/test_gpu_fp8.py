@@ -136,7 +136,8 @@ def test_fp8_prefill_sampled_rows(gpu_lib, N, swiglu, rows):
     assert_close(to_f64(y)[pick], ref, "bf16", f"fp8 prefill {M}x{K}x{N} swiglu={swiglu}")
 
 
-@pytest.mark.parametrize("M,K,N", [(65, 64, 16), (97, 8, 1), (256, 200, 300), (257, 4104, 33), (1000, 1032, 1100)])
+@pytest.mark.parametrize("M,K,N", [(65, 64, 16), (97, 8, 1), (256, 200, 300), (257, 4104, 33), (1000, 1032, 1100),
+                                   (2048, 264, 768)])
 def test_fp8_prefill_ragged(gpu_lib, M, K, N):
     """Ragged rows, columns and k (a half pair at the end) through the fp8
     prefill instances, projection and SwiGLU."""

@@ -260,3 +260,22 @@ def test_python_binding_rejects_bad_arguments(gpu_lib):
     with pytest.raises(gpu_lib.FlashNormError):
         gpu_lib.norm_proj(torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda"), Wp, eps=-1.0)
     assert tdtype("bf16") == torch.bfloat16
+
+
+@pytest.mark.parametrize("M,K,N,swiglu", [(2048, 264, 768, False), (1792, 136, 1024, True), (512, 72, 1024, False),
+                                          (4096, 40, 500, True)])
+def test_prefill_tile_order(gpu_lib, M, K, N, swiglu):
+    """Tile counts that divide by 8 take the XCD-grouped tile order (groups of
+    6 row tiles, here with a partial last group): every output against the
+    oracle, so a tile computed twice or not at all would show.  The oracle
+    takes the folded bf16 weights the kernel reads (the fold's rounding is
+    not what this checks; the unfolded comparison is the other tests')."""
+    inp = W.random_inputs(M, K, N, "bf16", seed=M + K + N, swiglu=swiglu)
+    y = fused(gpu_lib, inp)
+    assert np.all(np.isfinite(y))
+    Wg = oracle.fold_weights(inp.g, inp.W, "bf16")
+    if swiglu:
+        ref = oracle.norm_proj_swiglu_folded(inp.x, Wg, oracle.fold_weights(inp.g, inp.W_up, "bf16"), inp.call.eps)
+    else:
+        ref = oracle.norm_proj_folded(inp.x, Wg, inp.call.eps)
+    assert_close(y, ref, "bf16", f"prefill tile order {M}x{K}x{N} swiglu={swiglu}")
