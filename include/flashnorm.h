@@ -326,7 +326,8 @@ const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int
  *   bytes, 256-byte aligned, overlapping no other argument.  The call writes
  *   it and reads it back in stream order; its contents afterwards are
  *   unspecified, and calls in flight at the same time need separate
- *   workspaces.  For M <= 16 the call is the one-launch call (the
+ *   workspaces.  With the workspace given the calls allocate nothing, so a
+ *   caller may capture them into a HIP graph.  For M <= 16 the call is the one-launch call (the
  *   workspace is not touched and may be NULL, with workspace_bytes 0).
  * Errors as the one-launch calls, plus FN_ERR_WORKSPACE (M > 16 and the
  * workspace NULL, misaligned or smaller than needed) and FN_ERR_ALIAS (the
