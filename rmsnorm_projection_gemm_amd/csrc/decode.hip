@@ -268,13 +268,21 @@ struct DecodeInstance {
   }
 
 // Tile choices measured on MI355X (cold weights, >= 1 GiB rotation): at one
-// row block a single wave per workgroup streaming the whole k range with
-// two 4-k-block stages in flight beats splitting k across waves.  bf16 with
-// more than 16 rows goes to the kernel that shares x through LDS
-// (decode_x.hip); fp32 keeps all three rungs here.
+// row block and full projection widths a single wave per workgroup
+// streaming the whole k range with two 4-k-block stages in flight beats
+// splitting k across waves.  Narrow projections -- one GPU's column share
+// under tensor parallelism -- have too few column blocks to give every CU a
+// wave, and there the k range is split over 4 waves (2 for SwiGLU up to 512
+// blocks): measured 12.0 -> 8.1 us for 1536 QKV columns and 21.3 -> 10.9 us
+// for 2 x 1376 gate/up columns at 16 rows.  bf16 with more than 16 rows goes
+// to the kernel that shares x through LDS (decode_x.hip); fp32 keeps all
+// three rungs here.
 static const DecodeInstance kDecode[] = {
     FN_DECODE(__bf16, DType::BF16, 1, 1, false, 1, 1, 4, "decode_bf16_m16_n16_k1_u4"),
     FN_DECODE(__bf16, DType::BF16, 1, 1, true, 1, 1, 2, "decode_swiglu_bf16_m16_n16_k1_u2"),
+    FN_DECODE(__bf16, DType::BF16, 1, 1, false, 1, 4, 4, "decode_bf16_m16_n16_k4_u4"),
+    FN_DECODE(__bf16, DType::BF16, 1, 1, true, 1, 2, 2, "decode_swiglu_bf16_m16_n16_k2_u2"),
+    FN_DECODE(__bf16, DType::BF16, 1, 1, true, 1, 4, 2, "decode_swiglu_bf16_m16_n16_k4_u2"),
     FN_DECODE(float, DType::F32, 1, 1, false, 1, 4, 2, "decode_f32_m16_n16_k4_u2"),
     FN_DECODE(float, DType::F32, 2, 1, false, 1, 4, 2, "decode_f32_m32_n16_k4_u2"),
     FN_DECODE(float, DType::F32, 4, 1, false, 1, 4, 2, "decode_f32_m64_n16_k4_u2"),
@@ -283,10 +291,21 @@ static const DecodeInstance kDecode[] = {
     FN_DECODE(float, DType::F32, 4, 1, true, 1, 4, 2, "decode_swiglu_f32_m64_n16_k4_u2"),
 };
 
-static const DecodeInstance* find_decode(DType dt, int mf, bool sw) {
+// wk 0: the first instance of (dt, mf, sw) in the table (its default).
+static const DecodeInstance* find_decode(DType dt, int mf, bool sw, int wk = 0) {
   for (const DecodeInstance& d : kDecode)
-    if (d.dt == dt && d.mf == mf && d.sw == sw) return &d;
+    if (d.dt == dt && d.mf == mf && d.sw == sw && (wk == 0 || d.wk == wk)) return &d;
   return nullptr;
+}
+
+// k-split for bf16 at one row block: 4 waves when there are at most 256
+// workgroups of one wave (fewer than the CUs), 2 for SwiGLU up to 512.
+static int decode_k_split(DType dt, int64_t M, int64_t N, bool swiglu) {
+  if (dt != DType::BF16) return 0;
+  const int64_t wgs = ceil_div(N, 16) * ceil_div(M, 16);
+  if (wgs <= 256) return 4;
+  if (swiglu && wgs <= 512) return 2;
+  return 1;
 }
 
 // M-ladder: the smallest row capacity in {16, 32, 64} that holds M (the
@@ -295,8 +314,9 @@ static const DecodeInstance* find_decode(DType dt, int mf, bool sw) {
 FusedPlan plan_decode(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
   (void)K;
   const int mf = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  const DecodeInstance* d = find_decode(dt, mf, swiglu);
-  if (d == nullptr) d = find_decode(dt, 1, swiglu);   // bf16 above 16 rows: tiled over grid.y
+  const DecodeInstance* d = find_decode(dt, mf, swiglu, decode_k_split(dt, M, N, swiglu));
+  if (d == nullptr) d = find_decode(dt, 1, swiglu, decode_k_split(dt, M, N, swiglu));   // bf16 above 16 rows: tiled
+  if (d == nullptr) d = find_decode(dt, 1, swiglu);
   FusedPlan p{};
   p.kind = 0;
   p.mf = d->mf;
@@ -311,7 +331,7 @@ FusedPlan plan_decode(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
 
 hipError_t launch_decode(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
                          int M, int K, int N, float eps, hipStream_t stream) {
-  const DecodeInstance* d = find_decode(dt, p.mf, wu != nullptr);
+  const DecodeInstance* d = find_decode(dt, p.mf, wu != nullptr, p.waves);   // one column group: waves = k-split
   if (d == nullptr) return hipErrorInvalidValue;
   DecodeArgs a;
   a.x = x;

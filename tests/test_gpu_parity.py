@@ -178,7 +178,8 @@ def test_row_permutation_bit_exact(gpu_lib):
 
 def test_column_concatenation_bit_exact(gpu_lib):
     """Columns are independent: splitting W' by columns splits y, bit for bit
-    (the split sits at 1536 columns, a multiple of every workgroup width)."""
+    (the split sits at 1536 columns, a multiple of every workgroup width, and
+    all three widths take the same k-split: at most 256 column blocks)."""
     inp = W.random_inputs(8, 256, 1632, "bf16", seed=14)
     full = _fold_and_run(gpu_lib, inp.x, inp.g, inp.W, "bf16", 1e-6)
     left = _fold_and_run(gpu_lib, inp.x, inp.g, np.ascontiguousarray(inp.W[:, :1536]), "bf16", 1e-6)
