@@ -735,6 +735,7 @@ static const PrefillInstance kPrefill[] = {
     FN_PREFILL(4, 4, 4, 2, true, true, false, true, false, "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"),
     // fp8 (E4M3) weights with column scales
     FN_PREFILL(4, 8, 4, 2, false, false, false, false, true, "prefill_fp8_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, false, false, false, false, true, "prefill_fp8_256x128_w4x2_xl"),   // narrow
     FN_PREFILL(4, 4, 4, 2, true, false, false, false, true, "prefill_swiglu_fp8_256x128_w4x2_xl"),
     FN_PREFILL(4, 4, 4, 2, true, true, false, false, true, "prefill_swiglu_fp8_q8_256x128_w4x2_xl"),
     FN_PREFILL(4, 8, 4, 2, false, false, false, true, true, "prefill_fp8_premod_256x256_w4x2_xl"),
@@ -762,7 +763,7 @@ bool prefill_adaln_fits(int64_t T) { return T >= 1 && T <= kPrefillAdalnMaxT; }
 FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8, bool ad, bool ex, bool f8) {
   (void)dt;
   (void)K;
-  const bool plain = !swiglu && !q8 && !ad && !ex && !f8;
+  const bool plain = !swiglu && !q8 && !ad && !ex;
   const bool narrow = plain && ceil_div(N, 256) * ceil_div(M, 256) < 128;
   const PrefillInstance& d = pick(swiglu, q8, ad, ex, f8, narrow ? 8 : 0);
   FusedPlan p{};
@@ -812,7 +813,7 @@ hipError_t launch_prefill_fp8(const FusedPlan& p, const void* x, const void* wg,
                               const float* su, void* y, int M, int K, int N, float eps, hipStream_t stream, uint8_t* q,
                               float* qs) {
   if ((q != nullptr && wu == nullptr) || sg == nullptr || (wu != nullptr && su == nullptr)) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, false, true);
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, false, true, p.nf);
   PrefillArgs a{};
   a.x = x;
   a.wg = wg;
