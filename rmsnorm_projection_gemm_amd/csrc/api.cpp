@@ -424,8 +424,8 @@ namespace fn {
 // over rows.
 FusedPlan plan_fused(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
   if (dt == DType::BF16 && M > 64) return plan_prefill(dt, M, K, N, swiglu);
-  // narrow SwiGLU pairs at 33-64 rows: the register-x kernel with a k-split
-  if (dt == DType::BF16 && swiglu && M > 32 && (N + 15) / 16 <= 256) return plan_decode(dt, M, K, N, swiglu);
+  // narrow SwiGLU pairs at 17-64 rows: the register-x kernel with a k-split
+  if (dt == DType::BF16 && swiglu && M > 16 && (N + 15) / 16 <= 256) return plan_decode(dt, M, K, N, swiglu);
   if (dt == DType::BF16 && M > 16) return plan_decode_x(dt, M, K, N, swiglu);
   return plan_decode(dt, M, K, N, swiglu);
 }

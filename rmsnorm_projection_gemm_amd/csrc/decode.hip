@@ -283,9 +283,11 @@ static const DecodeInstance kDecode[] = {
     FN_DECODE(__bf16, DType::BF16, 1, 1, false, 1, 4, 4, "decode_bf16_m16_n16_k4_u4"),
     FN_DECODE(__bf16, DType::BF16, 1, 1, true, 1, 2, 2, "decode_swiglu_bf16_m16_n16_k2_u2"),
     FN_DECODE(__bf16, DType::BF16, 1, 1, true, 1, 4, 2, "decode_swiglu_bf16_m16_n16_k4_u2"),
-    // narrow gate/up pairs at 33-64 rows (the LDS-shared-x kernel would run a
-    // workgroup per three column blocks, 29 for 1376 columns): 64 rows in
-    // registers, k over 4 waves -- 26.4 -> 22.7 us at 2 x 1376 columns
+    // narrow gate/up pairs at 17-64 rows (the LDS-shared-x kernel would run a
+    // workgroup per three column blocks, 29 for 1376 columns): the rows in
+    // registers, k over 4 waves -- at 2 x 1376 columns 21.9 -> 15.0 us for 32
+    // rows, 26.4 -> 22.7 us for 64
+    FN_DECODE(__bf16, DType::BF16, 2, 1, true, 1, 4, 2, "decode_swiglu_bf16_m32_n16_k4_u2"),
     FN_DECODE(__bf16, DType::BF16, 4, 1, true, 1, 4, 2, "decode_swiglu_bf16_m64_n16_k4_u2"),
     FN_DECODE(float, DType::F32, 1, 1, false, 1, 4, 2, "decode_f32_m16_n16_k4_u2"),
     FN_DECODE(float, DType::F32, 2, 1, false, 1, 4, 2, "decode_f32_m32_n16_k4_u2"),

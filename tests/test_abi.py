@@ -175,7 +175,9 @@ def test_fp8_kernel_names(lib):
     assert lib.fn_kernel_name_fp8(17, 4096, 12288, 0).decode().startswith("decode_fp8_m32")
     assert lib.fn_kernel_name_fp8(64, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_m64")
     # above 64 rows the prefill kernel with fp8 weights
-    assert lib.fn_kernel_name_fp8(65, 4096, 12288, 0).decode() == "prefill_fp8_256x256_w4x2_xl"
+    assert lib.fn_kernel_name_fp8(4096, 4096, 12288, 0).decode() == "prefill_fp8_256x256_w4x2_xl"
+    # fewer than 128 tiles of 256 x 256: 256 x 128 tiles
+    assert lib.fn_kernel_name_fp8(65, 4096, 12288, 0).decode() == "prefill_fp8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_fp8(4096, 4096, 12288, 1).decode() == "prefill_swiglu_fp8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_fp8(0, 4096, 16, 0) == b"invalid"
 
