@@ -343,15 +343,25 @@ def norm_proj_swiglu_fp8_q8(x, codes_gate, s_gate, codes_up, s_up, eps: float):
 #     h[m,k] = xhat[m,k] * (1 + scale[idx[m], k]) + shift[idx[m], k],
 #     xhat = RMSNorm_g(x),   y = h @ W,   or   out = silu(h @ W_gate) * (h @ W_up).
 #
-# The modulation is chosen at run time, so it cannot be folded into W'; the
-# gain still can.  In real arithmetic
-#     h @ W = ((x * (1 + scale_i)) @ W') / r + shift_i @ W,   W' = diag(g) W,
-# the second term a per-index bias row that depends only on the tables and
-# the unfolded W (computed once per table).
+# The modulation is chosen at run time, so it cannot be folded into the
+# weights.  The gain can still be folded offline -- here into the
+# modulation table instead of W: in real arithmetic
+#
+#     h @ W = ((x * mod[idx]) @ W) / r + bias[idx],
+#     mod[t,k] = g[k] * (1 + scale[t,k]),   bias[t,:] = shift[t,:] @ W,
+#
+# with W the plain (unfolded) weights.  A matrix-core operand x * mod must be
+# rounded to bf16 anyway; folding g into W as well would round every
+# product term twice (once in W', once in the operand), so the AdaLN path
+# keeps W exact and carries the gain in the table (an fp32 table, one
+# rounding of the float64 product).  An index outside [0, T) selects no
+# table row: that row's h is taken as 0 (mod row 0, bias row 0), so its
+# output is 0.
 
 
 def adaln_modulate(x, g, scale, shift, idx, eps: float) -> np.ndarray:
-    """h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx], row by row."""
+    """h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx], row by row
+    (idx within [0, T))."""
     i = np.asarray(idx, dtype=np.int64)
     return rmsnorm(x, g, eps) * (1.0 + _f64(scale)[i]) + _f64(shift)[i]
 
@@ -367,38 +377,17 @@ def adaln_norm_proj_swiglu(x, g, scale, shift, idx, W_gate, W_up, eps: float) ->
     return silu(h @ _f64(W_gate)) * (h @ _f64(W_up))
 
 
+def adaln_fold_table(g, scale) -> np.ndarray:
+    """The gain folded into the modulation table, as stored: mod[t,k] =
+    g[k] * (1 + scale[t,k]), the sum and the product taken in float64 and
+    the result rounded once to float32.  Returned as float64 holding the
+    float32 values."""
+    return round_to_f32(_f64(g)[None, :] * (1.0 + _f64(scale)))
+
+
 def adaln_shift_bias(shift, W) -> np.ndarray:
     """Per-index bias rows shift @ W (unfolded W), [T, N]."""
     return _f64(shift) @ _f64(W)
-
-
-def adaln_norm_proj_folded(x, W_folded, scale, bias, idx, eps: float) -> np.ndarray:
-    """Folded and deferred form: ((x * (1 + scale[idx])) @ W') / r + bias[idx];
-    equal to adaln_norm_proj in real arithmetic (pinned, not used by the
-    comparisons)."""
-    x = _f64(x)
-    i = np.asarray(idx, dtype=np.int64)
-    return ((x * (1.0 + _f64(scale)[i])) @ _f64(W_folded)) / rms(x, eps)[:, None] + _f64(bias)[i]
-
-
-def adaln_norm_proj_fp8(x, codes, s, scale, bias, idx, eps: float) -> np.ndarray:
-    """AdaLN with E4M3 weights (the page's AdaLN FC1 kernel takes
-    pre-processed fp8 weights with their scales, [FlashInfer #5521] "Fused
-    Kernel on SM120"): ((x * (1 + scale[idx])) @ (s[n] * q)) / r + bias[idx]
-    -- the folded/deferred AdaLN form with the quantised weights in place of
-    W'; bias = shift @ W from the unfolded weights."""
-    x = _f64(x)
-    i = np.asarray(idx, dtype=np.int64)
-    Wq = e4m3_decode(codes) * _f64(s)[None, :]
-    return ((x * (1.0 + _f64(scale)[i])) @ Wq) / rms(x, eps)[:, None] + _f64(bias)[i]
-
-
-def adaln_norm_proj_swiglu_fp8(x, codes_gate, s_gate, codes_up, s_up, scale, bias_gate, bias_up, idx,
-                               eps: float) -> np.ndarray:
-    """SwiGLU variant: a, b as in adaln_norm_proj_fp8, out = silu(a) * b."""
-    a = adaln_norm_proj_fp8(x, codes_gate, s_gate, scale, bias_gate, idx, eps)
-    b = adaln_norm_proj_fp8(x, codes_up, s_up, scale, bias_up, idx, eps)
-    return silu(a) * b
 
 
 def _rows_or_zero(table, idx) -> np.ndarray:
@@ -409,46 +398,68 @@ def _rows_or_zero(table, idx) -> np.ndarray:
     return np.where(ok[:, None], t[np.where(ok, i, 0)], 0.0)
 
 
-def adaln_norm_proj_swiglu_q8(x, scale, idx, Wg_folded, Wu_folded, bias_gate, bias_up, eps: float):
+def adaln_norm_proj_fold(x, W, mod, bias, idx, eps: float) -> np.ndarray:
+    """Folded and deferred form: ((x * mod[idx]) @ W) / r + bias[idx], the
+    rows of an index outside the table zero.  With mod = g * (1 + scale)
+    unrounded it equals adaln_norm_proj in real arithmetic (pinned); with
+    the stored (float32) table it is what the kernels compute up to the
+    rounding of their bf16 operand and their fp32 sums."""
+    x = _f64(x)
+    return ((x * _rows_or_zero(mod, idx)) @ _f64(W)) / rms(x, eps)[:, None] + _rows_or_zero(bias, idx)
+
+
+def adaln_norm_proj_swiglu_fold(x, W_gate, W_up, mod, bias_gate, bias_up, idx, eps: float) -> np.ndarray:
+    """SwiGLU on the folded and deferred form: a, b as in
+    adaln_norm_proj_fold, out = silu(a) * b."""
+    a = adaln_norm_proj_fold(x, W_gate, mod, bias_gate, idx, eps)
+    b = adaln_norm_proj_fold(x, W_up, mod, bias_up, idx, eps)
+    return silu(a) * b
+
+
+def adaln_norm_proj_fp8(x, codes, s, mod, bias, idx, eps: float) -> np.ndarray:
+    """AdaLN with E4M3 weights (the page's AdaLN FC1 kernel takes
+    pre-processed fp8 weights with their scales, [FlashInfer #5521] "Fused
+    Kernel on SM120"): the folded/deferred form with the quantised plain
+    weights s[n] * q in place of W; bias = shift @ W from the bf16 weights."""
+    return adaln_norm_proj_fold(x, e4m3_decode(codes) * _f64(s)[None, :], mod, bias, idx, eps)
+
+
+def adaln_norm_proj_swiglu_fp8(x, codes_gate, s_gate, codes_up, s_up, mod, bias_gate, bias_up, idx,
+                               eps: float) -> np.ndarray:
+    """SwiGLU variant: a, b as in adaln_norm_proj_fp8, out = silu(a) * b."""
+    a = adaln_norm_proj_fp8(x, codes_gate, s_gate, mod, bias_gate, idx, eps)
+    b = adaln_norm_proj_fp8(x, codes_up, s_up, mod, bias_up, idx, eps)
+    return silu(a) * b
+
+
+def adaln_norm_proj_swiglu_q8(x, g, scale, shift, idx, W_gate, W_up, eps: float):
     """AdaLN FC1 with fp8 row-block output ([FlashInfer #5521] "Segmented
     Chain": norm + AdaLN, FC1, SwiGLU, quantisation for the next projection;
-    the format as read for norm_proj_swiglu_q8).  The codes are decisions,
-    so the values quantised are formed on the operand the kernels use,
-    u = adaln_operand(x, scale, idx) (the reading stated there):
-        a = (u @ W'_gate) / r + bias_gate[idx],  b likewise,  v = silu(a) * b,
-    then quantize_e4m3_row_blocks(v).  An index outside the table takes
-    scale 0 and bias 0.  Returns (codes, s, v)."""
-    u = adaln_operand(x, scale, idx)
-    r = rms(x, eps)[:, None]
-    a = (u @ _f64(Wg_folded)) / r + _rows_or_zero(bias_gate, idx)
-    b = (u @ _f64(Wu_folded)) / r + _rows_or_zero(bias_up, idx)
-    v = silu(a) * b
+    the format as read for norm_proj_swiglu_q8): the row-block quantisation
+    of the SwiGLU output of the definition.  Returns (codes, s, v)."""
+    v = adaln_norm_proj_swiglu(x, g, scale, shift, idx, W_gate, W_up, eps)
     codes, s = quantize_e4m3_row_blocks(v)
     return codes, s, v
 
 
-def adaln_norm_proj_swiglu_fp8_q8(x, scale, idx, codes_gate, s_gate, codes_up, s_up, bias_gate, bias_up,
+def adaln_norm_proj_swiglu_fp8_q8(x, codes_gate, s_gate, codes_up, s_up, mod, bias_gate, bias_up, idx,
                                   eps: float):
-    """The same with E4M3 weights: W' = s[n] * q."""
-    Wg = e4m3_decode(codes_gate) * _f64(s_gate)[None, :]
-    Wu = e4m3_decode(codes_up) * _f64(s_up)[None, :]
-    return adaln_norm_proj_swiglu_q8(x, scale, idx, Wg, Wu, bias_gate, bias_up, eps)
+    """The same with E4M3 weights: the row-block quantisation of
+    adaln_norm_proj_swiglu_fp8.  Returns (codes, s, v)."""
+    v = adaln_norm_proj_swiglu_fp8(x, codes_gate, s_gate, codes_up, s_up, mod, bias_gate, bias_up, idx, eps)
+    codes, s = quantize_e4m3_row_blocks(v)
+    return codes, s, v
 
 
-def adaln_operand(x, scale, idx) -> np.ndarray:
-    """The modulated matrix-core operand of the AdaLN path, as the kernels
-    form it: x + x * scale[idx[m]] rounded once to float32, then to bf16 with
-    ties to even (the reading stated with the AdaLN section above: the
-    fp32 -> bf16 step rounds to nearest even, [FlashInfer #4040]); an index
-    outside [0, T) takes scale 0.  For bf16 x and scale the float64 sum is
-    exact.  This fixes bits, so it is compared bit for bit; the projection
-    oracles above stay in float64."""
-    x = _f64(x)
-    sc = _f64(scale)
-    i = np.asarray(idx, dtype=np.int64)
-    ok = (i >= 0) & (i < sc.shape[0])
-    s = np.where(ok[:, None], sc[np.where(ok, i, 0)], 0.0)
-    return round_to_bf16(round_to_f32(x + x * s))
+def adaln_operand(x, mod, idx) -> np.ndarray:
+    """The modulated matrix-core operand of the AdaLN path: x * mod[idx[m]]
+    (float64-exact for bf16 x and a float32 table) rounded to float32, then
+    to bf16 with ties to even ([FlashInfer #4040]: the fp32 -> bf16 step
+    rounds to nearest even); a row whose index is outside [0, T) is 0.  This
+    is the specification of the library's modulation pre-pass, which
+    exports the operand, so it fixes bits; the projection oracles above do
+    not use it."""
+    return round_to_bf16(round_to_f32(_f64(x) * _rows_or_zero(mod, idx)))
 
 
 __all__ = ["rms", "rmsnorm", "norm_proj", "silu", "norm_proj_swiglu", "fold_exact",
@@ -457,5 +468,6 @@ __all__ = ["rms", "rmsnorm", "norm_proj", "silu", "norm_proj_swiglu", "fold_exac
            "quantize_e4m3_columns", "fold_weights_fp8", "norm_proj_fp8", "norm_proj_swiglu_fp8",
            "Q8_BLOCK", "quantize_e4m3_row_blocks", "dequantize_row_blocks", "norm_proj_swiglu_q8",
            "norm_proj_swiglu_fp8_q8", "adaln_modulate", "adaln_norm_proj", "adaln_norm_proj_swiglu",
-           "adaln_shift_bias", "adaln_norm_proj_folded", "adaln_operand", "adaln_norm_proj_fp8",
-           "adaln_norm_proj_swiglu_fp8", "adaln_norm_proj_swiglu_q8", "adaln_norm_proj_swiglu_fp8_q8"]
+           "adaln_fold_table", "adaln_shift_bias", "adaln_norm_proj_fold", "adaln_norm_proj_swiglu_fold",
+           "adaln_operand", "adaln_norm_proj_fp8", "adaln_norm_proj_swiglu_fp8", "adaln_norm_proj_swiglu_q8",
+           "adaln_norm_proj_swiglu_fp8_q8"]

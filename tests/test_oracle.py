@@ -66,22 +66,45 @@ MUTANTS = {
     "adaln index ignored": ("adaln_modulate", lambda x, g, sc, sh, idx, eps: O.rmsnorm(x, g, eps)
                             * (1 + np.asarray(sc, float)[0]) + np.asarray(sh, float)[0]),
     "adaln bias on the folded weights": ("adaln_shift_bias", lambda sh, W: np.asarray(sh, float) @ np.asarray(W, float) * 1.5),
-    "adaln operand without the one": ("adaln_operand", lambda x, sc, idx: O.round_to_bf16(
-        np.asarray(x, float) * np.asarray(sc, float)[np.clip(np.asarray(idx), 0, np.asarray(sc).shape[0] - 1)])),
-    "adaln operand ties away": ("adaln_operand", lambda x, sc, idx: _operand_with(x, sc, idx, lambda v: np.floor(v + 0.5))),
-    "adaln operand truncated": ("adaln_operand", lambda x, sc, idx: _operand_with(x, sc, idx, np.trunc)),
-    "adaln operand index clamped": ("adaln_operand", lambda x, sc, idx: _operand_ref(
-        x, sc, np.clip(np.asarray(idx), 0, np.asarray(sc).shape[0] - 1))),
-    "adaln fp8 column scale dropped": ("adaln_norm_proj_fp8", lambda x, c, s, sc, b, idx, eps: _adaln_fp8_ref(
-        x, c, np.ones_like(np.asarray(s, float)), sc, b, idx, eps)),
-    "adaln fp8 bias dropped": ("adaln_norm_proj_fp8", lambda x, c, s, sc, b, idx, eps: _adaln_fp8_ref(
-        x, c, s, sc, np.zeros_like(np.asarray(b, float)), idx, eps)),
-    "adaln fp8 modulation dropped": ("adaln_norm_proj_fp8", lambda x, c, s, sc, b, idx, eps: _adaln_fp8_ref(
-        x, c, s, np.zeros_like(np.asarray(sc, float)), b, idx, eps)),
-    "adaln q8 on the unrounded operand": ("adaln_operand", lambda x, sc, idx: np.asarray(x, float) * (
-        1 + O._rows_or_zero(sc, idx))),
-    "adaln q8 bias on the wrong rows": ("_rows_or_zero", lambda t, idx: np.asarray(t, float)[
+    "adaln table without the one": ("adaln_fold_table", lambda g, sc: O.round_to_f32(
+        np.asarray(g, float)[None, :] * np.asarray(sc, float))),
+    "adaln table gain dropped": ("adaln_fold_table", lambda g, sc: O.round_to_f32(1.0 + np.asarray(sc, float))),
+    "adaln table in float32 steps": ("adaln_fold_table", lambda g, sc: O.round_to_f32(
+        O.round_to_f32(1.0 + np.asarray(sc, float)) * np.asarray(g, float)[None, :])),
+    "adaln table stored in bf16": ("adaln_fold_table", lambda g, sc: O.round_to_bf16(
+        np.asarray(g, float)[None, :] * (1.0 + np.asarray(sc, float)))),
+    "adaln fold bias dropped": ("adaln_norm_proj_fold", lambda x, W, mod, b, idx, eps: _fold_ref(
+        x, W, mod, np.zeros_like(np.asarray(b, float)), idx, eps)),
+    "adaln fold deferred multiply": ("adaln_norm_proj_fold", lambda x, W, mod, b, idx, eps: (
+        (np.asarray(x, float) * O._rows_or_zero(mod, idx)) @ np.asarray(W, float)) * O.rms(x, eps)[:, None]
+        + O._rows_or_zero(b, idx)),
+    "adaln fold index clamped": ("adaln_norm_proj_fold", lambda x, W, mod, b, idx, eps: _fold_ref(
+        x, W, mod, b, np.clip(np.asarray(idx), 0, np.asarray(mod).shape[0] - 1), eps)),
+    "adaln operand without the table": ("adaln_operand", lambda x, mod, idx: O.round_to_bf16(np.asarray(x, float))),
+    "adaln operand ties away": ("adaln_operand", lambda x, mod, idx: _operand_with(x, mod, idx, lambda v: np.floor(v + 0.5))),
+    "adaln operand truncated": ("adaln_operand", lambda x, mod, idx: _operand_with(x, mod, idx, np.trunc)),
+    "adaln operand rounded once": ("adaln_operand", lambda x, mod, idx: O.round_to_bf16(
+        np.asarray(x, float) * O._rows_or_zero(mod, idx))),
+    "adaln operand unrounded": ("adaln_operand", lambda x, mod, idx: np.asarray(x, float) * O._rows_or_zero(mod, idx)),
+    "adaln operand index clamped": ("adaln_operand", lambda x, mod, idx: _operand_ref(
+        x, mod, np.clip(np.asarray(idx), 0, np.asarray(mod).shape[0] - 1))),
+    "adaln fp8 column scale dropped": ("adaln_norm_proj_fp8", lambda x, c, s, mod, b, idx, eps: _adaln_fp8_ref(
+        x, c, np.ones_like(np.asarray(s, float)), mod, b, idx, eps)),
+    "adaln fp8 bias dropped": ("adaln_norm_proj_fp8", lambda x, c, s, mod, b, idx, eps: _adaln_fp8_ref(
+        x, c, s, mod, np.zeros_like(np.asarray(b, float)), idx, eps)),
+    "adaln fp8 modulation dropped": ("adaln_norm_proj_fp8", lambda x, c, s, mod, b, idx, eps: _adaln_fp8_ref(
+        x, c, s, np.ones_like(np.asarray(mod, float)), b, idx, eps)),
+    "adaln q8 on the bf16 operand": ("adaln_norm_proj_swiglu_q8", lambda x, g, sc, sh, idx, Wg, Wu, eps: _q8_on_operand(
+        x, g, sc, sh, idx, Wg, Wu, eps)),
+    "adaln fp8 q8 without the bias": ("adaln_norm_proj_swiglu_fp8_q8", lambda x, cg, sg, cu, su, mod, bg, bu, idx, eps:
+                                      _adaln_fp8_q8_ref(x, cg, sg, cu, su, mod, 0 * np.asarray(bg, float),
+                                                        0 * np.asarray(bu, float), idx, eps)),
+    "adaln bias on the wrong rows": ("_rows_or_zero", lambda t, idx: np.asarray(t, float)[
         (np.asarray(idx) + 1) % np.asarray(t).shape[0]]),
+    "fp8 fold quantises the unfolded W": ("fold_weights_fp8", lambda g, W, dtype: O.quantize_e4m3_columns(
+        O.round_to(W, dtype))[:2]),
+    "fp8 fold without storage rounding": ("fold_weights_fp8", lambda g, W, dtype: O.quantize_e4m3_columns(
+        O.fold_exact(g, W))[:2]),
     "q8 scale inverted": ("dequantize_row_blocks", lambda c, s, block=16: _deq_ref(c, 1.0 / np.asarray(s, float),
                                                                                  block)),
 }
@@ -90,21 +113,32 @@ MUTANTS = {
 _encode_ref = O.e4m3_encode
 _operand_ref = O.adaln_operand
 _adaln_fp8_ref = O.adaln_norm_proj_fp8
+_fold_ref = O.adaln_norm_proj_fold
+_adaln_fp8_q8_ref = O.adaln_norm_proj_swiglu_fp8_q8
 
 
-def _operand_with(x, sc, idx, rnd):
+def _operand_with(x, mod, idx, rnd):
     """The AdaLN operand with another rounding of the positive magnitude to
     the bf16 grid (8 significant bits)."""
-    x = np.asarray(x, float)
-    sc = np.asarray(sc, float)
-    i = np.asarray(idx)
-    ok = (i >= 0) & (i < sc.shape[0])
-    v = x + x * np.where(ok[:, None], sc[np.where(ok, i, 0)], 0.0)
+    v = O.round_to_f32(np.asarray(x, float) * O._rows_or_zero(mod, idx))
     mag = np.abs(v)
     with np.errstate(all="ignore"):
         _, e = np.frexp(mag)
         q = np.ldexp(rnd(np.ldexp(mag, 8 - e)), e - 8)
     return np.copysign(q, v)
+
+
+def _q8_on_operand(x, g, sc, sh, idx, Wg, Wu, eps):
+    """The AdaLN q8 values formed on a bf16-rounded modulated operand
+    (the arithmetic of a kernel, not the definition)."""
+    mod = O.adaln_fold_table(g, sc)
+    u = O.adaln_operand(x, mod, idx)
+    r = O.rms(x, eps)[:, None]
+    a = (u @ np.asarray(Wg, float)) / r + (np.asarray(sh, float) @ np.asarray(Wg, float))[np.asarray(idx)]
+    b = (u @ np.asarray(Wu, float)) / r + (np.asarray(sh, float) @ np.asarray(Wu, float))[np.asarray(idx)]
+    v = O.silu(a) * b
+    c, s = O.quantize_e4m3_row_blocks(v)
+    return c, s, v
 _decode_ref = O.e4m3_decode
 _quantize_ref = O.quantize_e4m3_columns
 
