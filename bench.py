@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of fused RMSNorm + projection (libflashnorm) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--configs LIST|none]
 
 A step is one pass of the hot path over one batch: one fused call for the
 single-call workloads, or the 65 calls of the 32-layer decode step.  Inputs
@@ -10,8 +10,17 @@ workloads rotate distinct copies of the folded weights (>= 1 GiB in total)
 so the 256 MB Infinity Cache cannot serve repeated calls ("cold", the
 headline); the single-buffer ("hot") figure is reported beside it.
 
-Prints ONE JSON line.  Default workload: the QKV decode projection,
-x[16,4096] bf16 -> W'[4096,12288].
+Timing: after a clock warm-up and W untimed steps, K steps run back to back
+in blocks, an event pair around each block (no event per call); the mean
+over the region gives ms_per_step and roofline.achieved, the median block
+gives `value` (with p10/p90 of the blocks beside it).
+
+Prints ONE JSON line: the headline workload (default: the QKV decode
+projection, x[16,4096] bf16 -> W'[4096,12288]) at the top level, and under
+"configs" every other workload of the metric measured in the same process
+(tiny fp32 decode, FFN SwiGLU decode, prefill QKV, the 32-layer decode step,
+and the two decode shapes with fp8 weights), each with its own rate,
+roofline fraction, unfused-chain speed-ups and CPU-oracle baseline.
 """
 from __future__ import annotations
 
@@ -54,12 +63,25 @@ def parse_args(argv=None):
     p.add_argument("--no-measured-peak", dest="measured_peak", action="store_false",
                    help="skip measuring the attainable peak (roofline.measured_peak, frac_measured)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
+    p.add_argument("--configs", default=",".join(DEFAULT_CONFIGS),
+                   help="other workloads to measure in the same run, comma-separated names from "
+                        f"{', '.join(CONFIG_CHOICES)}, or 'none'")
     p.add_argument("--hot", action="store_true", help="time a single weight buffer only (no rotation)")
     p.add_argument("--clock-warmup-s", type=float, default=0.5,
                    help="untimed seconds of steps before warmup (clock ramp-up); 0 under a profiler")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run 1 GiB device-to-device copies (counter calibration) and exit")
     return p.parse_args(argv)
+
+
+# Workloads measured beside the headline (name: workload, weights).
+CONFIG_CHOICES = {"tiny": ("tiny", "native"), "qkv_decode": ("qkv_decode", "native"),
+                  "ffn_decode": ("ffn_decode", "native"), "prefill_qkv": ("prefill_qkv", "native"),
+                  "decode_step": ("decode_step", "native"), "qkv_decode_fp8": ("qkv_decode", "fp8"),
+                  "ffn_decode_fp8": ("ffn_decode", "fp8")}
+DEFAULT_CONFIGS = ("tiny", "ffn_decode", "prefill_qkv", "decode_step", "qkv_decode_fp8", "ffn_decode_fp8")
+# steps and warmup of a config run: the headline's, capped where one step is long
+CONFIG_STEP_CAP = {"prefill_qkv": (50, 5), "decode_step": (20, 3)}
 
 
 # ----------------------------------------------------------------- timing --
@@ -80,34 +102,32 @@ def clock_warmup(torch, launch):
         torch.cuda.synchronize()
 
 
-def time_region(torch, launch, steps, warmup):
-    """Average ms per step over `steps` back-to-back steps (events on the
-    current stream, which is the stream every launch uses), after a clock
-    warm-up and `warmup` untimed steps."""
+def time_blocks(torch, launch, steps, warmup):
+    """(mean ms per step over the region, sorted per-block ms per step):
+    after a clock warm-up and `warmup` untimed steps, `steps` back-to-back
+    steps in up to 20 blocks with an event recorded between blocks (events
+    on the current stream, which is the stream every launch uses), bracketed
+    by device synchronisations."""
     clock_warmup(torch, launch)
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        launch(i)
-    e1.record()
+    nb = max(1, min(20, steps))
+    bounds = [steps * b // nb for b in range(nb + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    evs[0].record()
+    for b in range(nb):
+        for i in range(bounds[b], bounds[b + 1]):
+            launch(i)
+        evs[b + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    blocks = sorted(evs[b].elapsed_time(evs[b + 1]) / (bounds[b + 1] - bounds[b]) for b in range(nb))
+    return evs[0].elapsed_time(evs[nb]) / steps, blocks
 
 
-def time_each(torch, launch, count):
-    """Per-step durations (ms) with an event pair around every step."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(count)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        a.record()
-        launch(i)
-        b.record()
-    torch.cuda.synchronize()
-    return sorted(a.elapsed_time(b) for a, b in evs)
+def time_region(torch, launch, steps, warmup):
+    """Mean ms per step over the region (time_blocks)."""
+    return time_blocks(torch, launch, steps, warmup)[0]
 
 
 def pct(sorted_vals, q):
@@ -170,9 +190,9 @@ ADALN_T = 4
 
 
 def adaln_extra_bytes(call):
-    """AdaLN inputs read once: the scale table [T, K] bf16, the row indices
-    [M] int32 and the bias rows [T, N] fp32 per weight matrix."""
-    return 2 * ADALN_T * call.K + 4 * call.M + 4 * ADALN_T * call.N * call.mats
+    """AdaLN inputs read once: the modulation table [T, K] fp32, the row
+    indices [M] int32 and the bias rows [T, N] fp32 per weight matrix."""
+    return 4 * ADALN_T * call.K + 4 * call.M + 4 * ADALN_T * call.N * call.mats
 
 
 def call_bytes(call, fp8, q8):
@@ -186,9 +206,29 @@ def call_bytes(call, fp8, q8):
 
 
 # ------------------------------------------------------------ CPU oracle --
-def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False, adaln=False):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False, adaln=False, one_thread_s=0.0):
     """The float64 oracle as it stands, on the host cores, on a bounded sample
-    of the same workload; scaled to the metric's unit."""
+    of the same workload; scaled to the metric's unit.  one_thread_s > 0: the
+    same sample again with the BLAS pool limited to one thread."""
+    if one_thread_s > 0:
+        out = cpu_baseline(call, inp, budget_s, metric_unit, fp8, q8, adaln)
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = cpu_baseline(call, inp, one_thread_s, metric_unit, fp8, q8, adaln)
+        out["one_thread"] = {"value": one["value"], "unit": one["unit"], "cores": one["cores"],
+                             "sample": one["sample"]}
+        return out
     import numpy as np
     import oracle
     try:
@@ -204,29 +244,28 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False, adaln=Fa
     calls, t0 = 0, time.perf_counter()
     w8 = None
     if fp8:
-        w8 = [oracle.fold_weights_fp8(inp.g, inp.W, call.dtype)]
+        # the AdaLN calls quantise the plain W (the gain goes into the table)
+        gq = np.ones(call.K) if adaln else inp.g
+        w8 = [oracle.fold_weights_fp8(gq, inp.W, call.dtype)]
         if call.swiglu:
-            w8.append(oracle.fold_weights_fp8(inp.g, inp.W_up, call.dtype))
+            w8.append(oracle.fold_weights_fp8(gq, inp.W_up, call.dtype))
     if adaln:
         import workloads
         sc, sh, idx = workloads.adaln_tables(ADALN_T, call.K, call.M, seed=call.seed + 100)
         idx = idx[:rows]
-        if fp8:
-            bias8 = [oracle.adaln_shift_bias(sh, inp.W)] + ([oracle.adaln_shift_bias(sh, inp.W_up)] if call.swiglu else [])
-    if adaln and q8:
-        rbg, rbu = oracle.adaln_shift_bias(sh, inp.W), oracle.adaln_shift_bias(sh, inp.W_up)
-        if not fp8:
-            Wgf, Wuf = oracle.fold_weights(inp.g, inp.W, call.dtype), oracle.fold_weights(inp.g, inp.W_up, call.dtype)
+        mod = oracle.adaln_fold_table(inp.g, sc)
+        bias8 = [oracle.adaln_shift_bias(sh, inp.W)] + ([oracle.adaln_shift_bias(sh, inp.W_up)] if call.swiglu else [])
     while True:
         if adaln and q8 and fp8:
-            oracle.adaln_norm_proj_swiglu_fp8_q8(x, sc, idx, w8[0][0], w8[0][1], w8[1][0], w8[1][1], rbg, rbu, call.eps)
+            oracle.adaln_norm_proj_swiglu_fp8_q8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], mod, bias8[0], bias8[1],
+                                                 idx, call.eps)
         elif adaln and q8:
-            oracle.adaln_norm_proj_swiglu_q8(x, sc, idx, Wgf, Wuf, rbg, rbu, call.eps)
+            oracle.adaln_norm_proj_swiglu_q8(x, inp.g, sc, sh, idx, inp.W, inp.W_up, call.eps)
         elif adaln and fp8 and call.swiglu:
-            oracle.adaln_norm_proj_swiglu_fp8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], sc, bias8[0], bias8[1], idx,
+            oracle.adaln_norm_proj_swiglu_fp8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], mod, bias8[0], bias8[1], idx,
                                               call.eps)
         elif adaln and fp8:
-            oracle.adaln_norm_proj_fp8(x, w8[0][0], w8[0][1], sc, bias8[0], idx, call.eps)
+            oracle.adaln_norm_proj_fp8(x, w8[0][0], w8[0][1], mod, bias8[0], idx, call.eps)
         elif adaln and call.swiglu:
             oracle.adaln_norm_proj_swiglu(x, inp.g, sc, sh, idx, inp.W, inp.W_up, call.eps)
         elif adaln:
@@ -259,7 +298,7 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False, adaln=Fa
               f"{', E4M3 row-block output' if q8 else ''}{', AdaLN prologue' if adaln else ''}, float64, {el:.1f} s;"
               f" scaled by M/{rows}")
     return {"value": round(value, 4), "unit": metric_unit, "cores": cores, "kind": "oracle",
-            "sample": sample, "seconds_per_call": per_call}
+            "sample": sample, "seconds_per_call": per_call, "cpu_model": cpu_model(), "nproc": os.cpu_count()}
 
 
 # ---------------------------------------------------------- single calls --
@@ -279,17 +318,19 @@ def run_single(args, torch, fn, workloads):
     Wg = to_dev(torch, inp.W, call.dtype)
     Wu = to_dev(torch, inp.W_up, call.dtype) if call.swiglu else None
     fp8 = args.weights == "fp8"
+    adaln = args.prologue == "adaln"
+    gw = None if adaln else g      # AdaLN: the gain folds into the modulation table, the weights stay plain
     if fp8:
-        Pg = fn.fold_weights_fp8(g, Wg)
-        Pu = fn.fold_weights_fp8(g, Wu) if call.swiglu else None
+        Pg = fn.fold_weights_fp8(gw, Wg)
+        Pu = fn.fold_weights_fp8(gw, Wu) if call.swiglu else None
         wbytes = (Pg.data.numel() + Pg.scales.numel() * 4) * call.mats
 
         def clone(P):
             return fn.PackedFp8(P.data.clone(), P.scales.clone(), P.K, P.N)
         proj, proj_sw = fn.norm_proj_fp8, fn.norm_proj_swiglu_fp8
     else:
-        Pg = fn.fold_weights(g, Wg)
-        Pu = fn.fold_weights(g, Wu) if call.swiglu else None
+        Pg = fn.fold_weights(gw, Wg)
+        Pu = fn.fold_weights(gw, Wu) if call.swiglu else None
         wbytes = Pg.data.numel() * call.mats
 
         def clone(P):
@@ -300,10 +341,10 @@ def run_single(args, torch, fn, workloads):
     pus = ([Pu] + [clone(Pu) for _ in range(rot - 1)]) if call.swiglu else None
     y = torch.empty((call.M, call.N), dtype=x.dtype, device="cuda")
     eps = call.eps
-    adaln = args.prologue == "adaln"
     if adaln:
         sc_np, sh_np, idx_np = workloads.adaln_tables(ADALN_T, call.K, call.M, seed=call.seed + 100)
         sc_t, sh_t = to_dev(torch, sc_np, "bf16"), to_dev(torch, sh_np, "bf16")
+        mod_t = fn.adaln_fold_table(g, sc_t)
         idx_t = torch.from_numpy(idx_np).cuda()
         bg_t = fn.adaln_shift_bias(sh_t, Wg)
         bu_t = fn.adaln_shift_bias(sh_t, Wu) if call.swiglu else None
@@ -313,9 +354,9 @@ def run_single(args, torch, fn, workloads):
         ws_t = torch.empty((nws,), dtype=torch.uint8, device="cuda") if nws else None
         f1, f2 = ((fn.norm_proj_adaln_fp8_ws, fn.norm_proj_swiglu_adaln_fp8_ws) if fp8 else
                   (fn.norm_proj_adaln_ws, fn.norm_proj_swiglu_adaln_ws))
-        proj = lambda x_, P_, e_, out=None: f1(x_, sc_t, idx_t, P_, bg_t, e_, out=out, workspace=ws_t)  # noqa: E731
+        proj = lambda x_, P_, e_, out=None: f1(x_, mod_t, idx_t, P_, bg_t, e_, out=out, workspace=ws_t)  # noqa: E731
         proj_sw = lambda x_, a_, b_, e_, out=None: f2(  # noqa: E731
-            x_, sc_t, idx_t, a_, bg_t, b_, bu_t, e_, out=out, workspace=ws_t)
+            x_, mod_t, idx_t, a_, bg_t, b_, bu_t, e_, out=out, workspace=ws_t)
     q8 = args.output == "q8"
     if q8:
         # SwiGLU quantised in the epilogue: E4M3 codes + row-block scales
@@ -324,7 +365,7 @@ def run_single(args, torch, fn, workloads):
         if adaln:
             fq = fn.norm_proj_swiglu_adaln_fp8_q8_ws if fp8 else fn.norm_proj_swiglu_adaln_q8_ws
             proj_sw = lambda x_, a_, b_, e_, out=None: fq(  # noqa: E731
-                x_, sc_t, idx_t, a_, bg_t, b_, bu_t, e_, out=qout, workspace=ws_t)
+                x_, mod_t, idx_t, a_, bg_t, b_, bu_t, e_, out=qout, workspace=ws_t)
         else:
             proj_q8 = fn.norm_proj_swiglu_fp8_q8 if fp8 else fn.norm_proj_swiglu_q8
             proj_sw = lambda x_, a_, b_, e_, out=None: proj_q8(x_, a_, b_, e_, out=qout)  # noqa: E731
@@ -336,11 +377,10 @@ def run_single(args, torch, fn, workloads):
         def fused(i):
             proj(x, pgs[i % rot], eps, out=y)
 
-    ms = time_region(torch, fused, args.steps, args.warmup)
-    each = time_each(torch, fused, min(args.steps, 200))
+    ms, blocks = time_blocks(torch, fused, args.steps, args.warmup)
     hot_ms = time_region(torch, lambda i: (proj_sw(x, Pg, Pu, eps, out=y) if call.swiglu
                                            else proj(x, Pg, eps, out=y)), args.steps, args.warmup)
-    result = {"ms": ms, "each": each, "hot_ms": hot_ms, "rot": rot, "wbytes": wbytes}
+    result = {"ms": ms, "blocks": blocks, "hot_ms": hot_ms, "rot": rot, "wbytes": wbytes}
     if args.workload == "tiny":
         # launch-bound: the same call recorded TINY_STEP_CALLS times into one
         # step, replayed with one graph launch; reported per call
@@ -434,8 +474,7 @@ def run_decode_step(args, torch, fn, workloads):
             else:
                 proj(it["x"], it["Pg"], c.eps, out=it["y"])
 
-    ms = time_region(torch, fused, args.steps, args.warmup)
-    each = time_each(torch, fused, min(args.steps, 20))
+    ms, blocks = time_blocks(torch, fused, args.steps, args.warmup)
     # the same 65 calls recorded once into a HIP graph, replayed with one launch
     step = fn.Step()
     for it in items:
@@ -448,7 +487,7 @@ def run_decode_step(args, torch, fn, workloads):
     graph_ms = time_region(torch, lambda _: step.launch(), args.steps, args.warmup)
     torch.cuda.synchronize()
     step.close()
-    result = {"ms": ms, "each": each, "hot_ms": None, "rot": 1, "graph_ms": graph_ms,
+    result = {"ms": ms, "blocks": blocks, "hot_ms": None, "rot": 1, "graph_ms": graph_ms,
               "wbytes": sum((it["Pg"].data.numel() + (it["Pg"].scales.numel() * 4 if fp8 else 0)) * it["call"].mats
                             for it in items)}
     if not args.no_chain:
@@ -517,6 +556,127 @@ def calibrate_copy(torch):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
 
 
+def measure(args, torch, fn, workloads):
+    """Run one workload as args describes; returns the measurement fields
+    (the headline line's, or a config's)."""
+    fp8 = args.weights == "fp8"
+    q8 = args.output == "q8"
+    adaln = args.prologue == "adaln"
+    suffix = ("_fp8" if fp8 else "") + ("_q8" if q8 else "") + ("_adaln" if adaln else "")
+    if args.workload == "decode_step":
+        calls, r = run_decode_step(args, torch, fn, workloads)
+        bytes_step = sum((fp8_bytes(c) if fp8 else c.algorithmic_bytes()) for c in calls)
+        flops_step = sum(c.flops() for c in calls)
+        name = "32-layer decode step, M=8: 32 x (norm+QKV 4096->12288, norm+gate/up SwiGLU 4096->2x11008) + norm+head 4096->32000"
+        config = {"workload": name, "calls_per_step": len(calls), "M": 8, "K": 4096,
+                  "weights_bytes": r["wbytes"], "cache": "cold (9.3 GB of distinct weights per step)"}
+        kernel = fn.kernel_name_fp8(8, 4096, 12288, False) if fp8 else fn.kernel_name(8, 4096, 12288, False, torch.bfloat16)
+        cpu_call, cpu_inp = calls[-1], None
+        unit = "GB/s"
+        work = bytes_step
+        roof = {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": counter_traffic("decode_step" + suffix)}
+        dtype = "bf16"
+        per_unit = {"algorithmic_bytes_per_step": bytes_step, "flops_per_step": flops_step}
+    else:
+        call, inp, r = run_single(args, torch, fn, workloads)
+        bytes_call = call_bytes(call, fp8, q8) + (adaln_extra_bytes(call) if adaln else 0)
+        flops_call = call.flops()
+        kernel = (fn.kernel_name_adaln_q8(call.M, call.K, call.N, ADALN_T, fp8) if adaln and q8 else
+                  fn.kernel_name_adaln_fp8(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln and fp8 else
+                  fn.kernel_name_adaln_ws(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln else
+                  fn.kernel_name_q8(call.M, call.K, call.N, fp8) if q8 else
+                  fn.kernel_name_fp8(call.M, call.K, call.N, call.swiglu) if fp8 else
+                  fn.kernel_name(call.M, call.K, call.N, call.swiglu,
+                                 torch.bfloat16 if call.dtype == "bf16" else torch.float32))
+        config = {"workload": call.name, "M": call.M, "K": call.K, "N": call.N, "mats": call.mats,
+                  "eps": call.eps, "kernel": kernel,
+                  "cache": (f"cold ({r['rot']} rotated W' copies, {r['rot'] * r['wbytes'] / 2**30:.2f} GiB)"
+                            if r["rot"] > 1 else "hot (one weight buffer)")}
+        cpu_call, cpu_inp = call, inp
+        dtype = call.dtype
+        per_unit = {"algorithmic_bytes_per_call": bytes_call, "flops_per_call": flops_call}
+        if args.workload == "prefill_qkv":
+            unit, work = "TFLOP/s", flops_call
+            roof = {"bound": "mfma", "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "traffic": counter_traffic(args.workload + suffix)}
+        elif args.workload == "tiny":
+            unit, work = "us/call", bytes_call
+            roof = {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": counter_traffic(args.workload),
+                    "note": "launch-latency bound; the fraction is not meaningful here"}
+        else:
+            unit, work = "GB/s", bytes_call
+            roof = {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "traffic": counter_traffic(args.workload + suffix)}
+        if fp8:
+            config["weights"] = "fp8 E4M3 codes + one fp32 scale per output column"
+        if q8:
+            config["output"] = "fp8 E4M3 codes + one fp32 scale per 16-column row block"
+        if adaln:
+            config["prologue"] = (f"AdaLN: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx], tables of {ADALN_T} rows, "
+                                  "per-row index, the gain folded into the fp32 modulation table"
+                                  + (", two launches (adaln_modulate pre-pass, then the kernel named)"
+                                     if fp8 or q8 or fn.adaln_workspace_bytes(call.M, call.K) else ", one launch"))
+    # achieved: work per step / the region's mean step time (the kernel's
+    # average launch duration for the single-kernel workloads); value: the
+    # same work priced at the median block
+    scale = 1e12 if roof["unit"] == "TFLOP/s" else 1e9
+    med = pct(r["blocks"], 0.5)
+    achieved = work / (r["ms"] * 1e-3) / scale
+    roof["achieved"] = round(achieved, 6 if unit == "us/call" else 2)
+    roof["frac"] = round(achieved / roof["peak"], 6 if unit == "us/call" else 4)
+    roof = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "note") if k in roof}
+    value = med * 1e3 if unit == "us/call" else work / (med * 1e-3) / scale
+    if args.measured_peak and roof["bound"] in ("hbm", "mfma") and unit != "us/call":
+        peak, peak_unit = measured_peak(torch, fn, roof["bound"])
+        if peak_unit == roof["unit"]:
+            roof["measured_peak"] = peak
+            roof["frac_measured"] = round(roof["achieved"] / peak, 4)
+            roof["measured_peak_probe"] = ("fn_probe_hbm_read over 1 GiB" if roof["bound"] == "hbm"
+                                           else "fn_probe_mfma_bf16 (MFMA-only loop)")
+    out = {
+        "value": round(value, 4), "unit": unit, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 6), "dtype": dtype, "config": config, "roofline": roof,
+        "us_per_step": round(r["ms"] * 1e3, 3),
+        "us_median_p10_p90": [round(pct(r["blocks"], q) * 1e3, 3) for q in (0.5, 0.1, 0.9)],
+        "timing": f"{len(r['blocks'])} blocks of back-to-back steps, an event pair per block; "
+                  "value at the median block, ms_per_step and roofline.achieved the region mean",
+        "hot_us_per_step": None if r["hot_ms"] is None else round(r["hot_ms"] * 1e3, 3),
+        "kernel": kernel,
+        **per_unit,
+    }
+    if "graph_ms" in r:
+        out["recorded_step"] = {"us_per_step" if args.workload == "decode_step" else "us_per_call":
+                                round(r["graph_ms"] * 1e3, 3),
+                                "speedup_vs_eager": round(r["ms"] / r["graph_ms"], 3),
+                                "note": ("the same calls recorded once (fn_step_create), one graph launch per step"
+                                         if args.workload == "decode_step" else
+                                         f"{TINY_STEP_CALLS} calls recorded into one step (fn_step_create), "
+                                         "one graph launch, time per call")}
+    if "bf16_ms" in r:
+        out["bf16_weights_us"] = round(r["bf16_ms"] * 1e3, 3)
+        out["speedup_vs_bf16_weights"] = round(r["bf16_ms"] / r["ms"], 3)
+    if "chain_own_ms" in r:
+        out["chain"] = {
+            "own_rmsnorm_then_hipblaslt_us": round(r["chain_own_ms"] * 1e3, 3),
+            "torch_rms_norm_then_matmul_us": round(r["chain_torch_ms"] * 1e3, 3),
+            "fused_speedup_vs_own_chain": round(r["chain_own_ms"] / r["ms"], 3),
+            "fused_speedup_vs_torch_chain": round(r["chain_torch_ms"] / r["ms"], 3),
+        }
+    if not args.no_cpu_baseline:
+        if cpu_inp is None:
+            cpu_inp = workloads.make_inputs(cpu_call)
+        cb = cpu_baseline(cpu_call, cpu_inp, args.cpu_seconds, unit if unit != "us/call" else "us/call", fp8=fp8,
+                          q8=q8, adaln=adaln, one_thread_s=getattr(args, "one_thread_s", 0.0))
+        per_call = cb.pop("seconds_per_call")
+        if args.workload == "decode_step":
+            # one head call sampled; scale to the whole step by algorithmic bytes
+            step_s = per_call * bytes_step / (fp8_bytes(cpu_call) if fp8 else cpu_call.algorithmic_bytes())
+            cb["value"] = round(bytes_step / step_s / 1e9, 4)
+            cb["sample"] += "; scaled to the 65-call step by algorithmic bytes"
+        out["cpu_baseline"] = cb
+    return out
+
+
 def main(argv=None):
     args = parse_args(argv)
     global CLOCK_WARMUP_S
@@ -547,131 +707,55 @@ def main(argv=None):
     if adaln and args.workload not in ("qkv_decode", "ffn_decode", "prefill_qkv"):
         print("bench.py: --prologue adaln applies to qkv_decode, ffn_decode and prefill_qkv", file=sys.stderr)
         return 2
-    suffix = ("_fp8" if fp8 else "") + ("_q8" if q8 else "") + ("_adaln" if adaln else "")
+    configs = [] if args.configs.strip() in ("", "none") else [c.strip() for c in args.configs.split(",")]
+    bad = [c for c in configs if c not in CONFIG_CHOICES]
+    if bad:
+        print(f"bench.py: unknown config(s) {bad}; choose from {', '.join(CONFIG_CHOICES)}", file=sys.stderr)
+        return 2
 
-    if args.workload == "decode_step":
-        calls, r = run_decode_step(args, torch, fn, workloads)
-        bytes_step = sum((fp8_bytes(c) if fp8 else c.algorithmic_bytes()) for c in calls)
-        flops_step = sum(c.flops() for c in calls)
-        name = "32-layer decode step, M=8: 32 x (norm+QKV 4096->12288, norm+gate/up SwiGLU 4096->2x11008) + norm+head 4096->32000"
-        config = {"workload": name, "calls_per_step": len(calls), "M": 8, "K": 4096,
-                  "weights_bytes": r["wbytes"], "cache": "cold (9.3 GB of distinct weights per step)"}
-        kernel = fn.kernel_name_fp8(8, 4096, 12288, False) if fp8 else fn.kernel_name(8, 4096, 12288, False, torch.bfloat16)
-        cpu_call, cpu_inp = calls[-1], None
-        unit = "GB/s"
-        value = bytes_step / (r["ms"] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(value / HBM_PEAK_GBS, 4), "traffic": counter_traffic("decode_step" + suffix)}
-        dtype = "bf16"
-        per_unit = {"algorithmic_bytes_per_step": bytes_step, "flops_per_step": flops_step}
-    else:
-        call, inp, r = run_single(args, torch, fn, workloads)
-        bytes_call = call_bytes(call, fp8, q8) + (adaln_extra_bytes(call) if adaln else 0)
-        flops_call = call.flops()
-        kernel = (fn.kernel_name_adaln_q8(call.M, call.K, call.N, ADALN_T, fp8) if adaln and q8 else
-                  fn.kernel_name_adaln_fp8(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln and fp8 else
-                  fn.kernel_name_adaln_ws(call.M, call.K, call.N, ADALN_T, call.swiglu) if adaln else
-                  fn.kernel_name_q8(call.M, call.K, call.N, fp8) if q8 else
-                  fn.kernel_name_fp8(call.M, call.K, call.N, call.swiglu) if fp8 else
-                  fn.kernel_name(call.M, call.K, call.N, call.swiglu,
-                                 torch.bfloat16 if call.dtype == "bf16" else torch.float32))
-        config = {"workload": call.name, "M": call.M, "K": call.K, "N": call.N, "mats": call.mats,
-                  "eps": call.eps, "kernel": kernel,
-                  "cache": (f"cold ({r['rot']} rotated W' copies, {r['rot'] * r['wbytes'] / 2**30:.2f} GiB)"
-                            if r["rot"] > 1 else "hot (one weight buffer)")}
-        cpu_call, cpu_inp = call, inp
-        dtype = call.dtype
-        per_unit = {"algorithmic_bytes_per_call": bytes_call, "flops_per_call": flops_call}
-        if args.workload == "prefill_qkv":
-            unit = "TFLOP/s"
-            value = flops_call / (r["ms"] * 1e-3) / 1e12
-            roof = {"bound": "mfma", "achieved": round(value, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(value / BF16_PEAK_TFLOPS, 4), "traffic": counter_traffic(args.workload + suffix)}
-        elif args.workload == "tiny":
-            unit = "us/call"
-            value = r["ms"] * 1e3
-            gbs = bytes_call / (r["ms"] * 1e-3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": counter_traffic(args.workload),
-                    "note": "launch-latency bound; the fraction is not meaningful here"}
-        else:
-            unit = "GB/s"
-            value = bytes_call / (r["ms"] * 1e-3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(value / HBM_PEAK_GBS, 4), "traffic": counter_traffic(args.workload + suffix)}
-        if fp8:
-            config["weights"] = "fp8 E4M3 codes + one fp32 scale per output column"
-        if q8:
-            config["output"] = "fp8 E4M3 codes + one fp32 scale per 16-column row block"
-        if adaln:
-            config["prologue"] = (f"AdaLN: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx], tables of {ADALN_T} rows, "
-                                  "per-row index" + (", two launches (adaln_modulate pre-pass, then the kernel named)"
-                                                     if fp8 or q8 or fn.adaln_workspace_bytes(call.M, call.K) else
-                                                     ", one launch"))
+    # the headline: the workload named, with a one-thread CPU oracle figure
+    head_args = argparse.Namespace(**vars(args))
+    head_args.one_thread_s = min(5.0, args.cpu_seconds)
+    head = measure(head_args, torch, fn, workloads)
+    torch.cuda.empty_cache()
+    sub = {}
+    for name in configs:
+        wl, weights = CONFIG_CHOICES[name]
+        if (wl, weights) == (args.workload, args.weights) and not q8 and not adaln:
+            continue    # the headline itself
+        cargs = argparse.Namespace(**vars(args))
+        cargs.workload, cargs.weights, cargs.output, cargs.prologue, cargs.hot = wl, weights, "native", "none", False
+        cargs.steps, cargs.warmup = CONFIG_STEP_CAP.get(wl, (args.steps, args.warmup))
+        cargs.steps, cargs.warmup = min(cargs.steps, args.steps), min(cargs.warmup, args.warmup)
+        cargs.measured_peak = False
+        if weights == "fp8":
+            cargs.no_chain, cargs.no_cpu_baseline = True, True    # timing only; bf16 beside it in its own config
+        sub[name] = measure(cargs, torch, fn, workloads)
+        torch.cuda.empty_cache()
 
-    if args.measured_peak and roof["bound"] in ("hbm", "mfma") and unit != "us/call":
-        peak, peak_unit = measured_peak(torch, fn, roof["bound"])
-        if peak_unit == roof["unit"]:
-            roof["measured_peak"] = peak
-            roof["frac_measured"] = round(roof["achieved"] / peak, 4)
-            roof["measured_peak_probe"] = ("fn_probe_hbm_read over 1 GiB" if roof["bound"] == "hbm"
-                                           else "fn_probe_mfma_bf16 (MFMA-only loop)")
     out = {
         "metric": METRIC,
-        "value": round(value, 4),
-        "unit": unit,
+        "value": head["value"],
+        "unit": head["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["ms"], 6),
-        "higher_is_better": unit != "us/call",
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": head["unit"] != "us/call",
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": head["dtype"],
         "data": "synthetic (seeded; random-init weights of the named shapes)",
-        "config": config,
-        "roofline": roof,
-        "us_per_step": round(r["ms"] * 1e3, 3),
-        "us_p10_p50_p90": [round(pct(r["each"], q) * 1e3, 3) for q in (0.1, 0.5, 0.9)],
-        # the same throughput priced at the median of the individually timed calls
-        "value_at_p50": (None if unit == "us/call" else
-                         round(value * r["ms"] / pct(r["each"], 0.5), 4)),
-        "hot_us_per_step": None if r["hot_ms"] is None else round(r["hot_ms"] * 1e3, 3),
-        "kernel": kernel,
-        **per_unit,
+        "config": head["config"],
+        "roofline": head["roofline"],
     }
-    if "graph_ms" in r:
-        out["recorded_step"] = {"us_per_step" if args.workload == "decode_step" else "us_per_call":
-                                round(r["graph_ms"] * 1e3, 3),
-                                "speedup_vs_eager": round(r["ms"] / r["graph_ms"], 3),
-                                "note": ("the same calls recorded once (fn_step_create), one graph launch per step"
-                                         if args.workload == "decode_step" else
-                                         f"{TINY_STEP_CALLS} calls recorded into one step (fn_step_create), "
-                                         "one graph launch, time per call")}
-    if "bf16_ms" in r:
-        out["bf16_weights_us"] = round(r["bf16_ms"] * 1e3, 3)
-        out["speedup_vs_bf16_weights"] = round(r["bf16_ms"] / r["ms"], 3)
-    if "chain_own_ms" in r:
-        out["chain"] = {
-            "own_rmsnorm_then_hipblaslt_us": round(r["chain_own_ms"] * 1e3, 3),
-            "torch_rms_norm_then_matmul_us": round(r["chain_torch_ms"] * 1e3, 3),
-            "fused_speedup_vs_own_chain": round(r["chain_own_ms"] / r["ms"], 3),
-            "fused_speedup_vs_torch_chain": round(r["chain_torch_ms"] / r["ms"], 3),
-        }
-    if not args.no_cpu_baseline:
-        if cpu_inp is None:
-            cpu_inp = workloads.make_inputs(cpu_call)
-        cb = cpu_baseline(cpu_call, cpu_inp, args.cpu_seconds, unit if unit != "us/call" else "us/call", fp8=fp8,
-                          q8=q8, adaln=adaln)
-        if args.workload == "decode_step":
-            # one head call sampled; scale to the whole step by algorithmic bytes
-            per_call = cb.pop("seconds_per_call")
-            step_s = per_call * bytes_step / (fp8_bytes(cpu_call) if fp8 else cpu_call.algorithmic_bytes())
-            cb["value"] = round(bytes_step / step_s / 1e9, 4)
-            cb["sample"] += "; scaled to the 65-call step by algorithmic bytes"
-        else:
-            cb.pop("seconds_per_call")
-        out["cpu_baseline"] = cb
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
+    for k, v in head.items():
+        if k not in out and k not in ("config", "roofline", "cpu_baseline", "dtype"):
+            out[k] = v
+    if sub:
+        out["configs"] = sub
     print(json.dumps(out), flush=True)
     return 0
 

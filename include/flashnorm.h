@@ -276,20 +276,33 @@ const char* fn_kernel_name_q8(int64_t M, int64_t K, int64_t N, int fp8_weights);
  * page does not write the modulation; the reading taken here:
  *   h[m][k] = RMSNorm_g(x)[m][k] * (1 + scale[idx[m]][k]) + shift[idx[m]][k]
  *   y = h * W,  or  out = silu(h * W_gate) * (h * W_up).
- * The modulation is picked at run time, so only the gain folds into W'
- * (fn_fold_weights as usual); the shift reaches the output as bias rows
- * bias[t] = shift[t] * W (fn_adaln_shift_bias, offline, unfolded W), and
- *   y[m] = ((x[m] * (1 + scale[idx[m]])) * W') / RMS(x[m]) + bias[idx[m]],
- * with RMS(x) of the unmodulated x.  Arithmetic: the modulated operand
- * x + x * scale is formed in fp32 and rounded once (RNE) to bf16 for the
- * matrix cores; sums in fp32; bf16 output rounded once.  bf16 only.
- * Instances: the LDS-shared-x decode kernel up to 64 rows; above, the
- * prefill kernel when T <= 63 (the whole table slice is staged), else the
- * decode kernel tiled over rows (each 64-row tile streams W' again).
- * scale: [T,K] bf16, 16-byte aligned.  idx: [M] int32, 4-byte aligned; an
- * index outside [0, T) gives that row scale 0 and shift 0.  bias: [T,N]
- * fp32, 4-byte aligned.  T >= 1 and T*K*2 < 2^31.
+ * The modulation is picked at run time, so it cannot be folded into the
+ * weights.  The gain still folds offline ([FlashNorm digest] proposal 1),
+ * here into the modulation table rather than into W: the matrix-core
+ * operand x * (1 + scale) has to be rounded to bf16 anyway, and a rounded
+ * W' as well would round every product term twice.  So the AdaLN calls take
+ *   mod[t][k] = g[k] * (1 + scale[t][k])   (fn_adaln_fold_table, fp32)
+ *   the plain weights W, packed by fn_fold_weights with g = NULL (or
+ *     quantised by fn_fold_weights_fp8 with g = NULL),
+ *   bias[t] = shift[t] * W                  (fn_adaln_shift_bias, fp32)
+ * and compute, with RMS(x) of the unmodulated x,
+ *   y[m] = ((x[m] * mod[idx[m]]) * W) / RMS(x[m]) + bias[idx[m]].
+ * Arithmetic: the operand x * mod is formed in fp32 and rounded once (RNE)
+ * to bf16 for the matrix cores (the one rounding a bf16 W' has in the plain
+ * path); sums in fp32; bf16 output rounded once.  bf16 only.
+ * mod: [T,K] fp32, 16-byte aligned.  idx: [M] int32, 4-byte aligned; an
+ * index outside [0, T) selects no table row: that row's h is 0 (its output
+ * is 0).  bias: [T,N] fp32, 4-byte aligned.  T >= 1 and T*K*4 < 2^31.
  * ------------------------------------------------------------------------- */
+
+/* mod[t][k] = fp32(g[k] * (1 + scale[t][k])), the sum and product taken in
+ * fp64 and rounded once.  g: [K], scale: [T,K] row-major, both in dt with
+ * their element alignment; mod: [T,K] fp32, 4-byte aligned (the AdaLN calls
+ * need 16), overwritten, overlapping neither input.  Offline, once per
+ * table.  Errors: FN_ERR_DTYPE, FN_ERR_SHAPE (K % 8, T*K*4 >= 2^31),
+ * FN_ERR_NULL, FN_ERR_ALIGN, FN_ERR_ALIAS, FN_ERR_HIP. */
+fn_status fn_adaln_fold_table(const void* g, const void* scale, float* mod, int64_t T, int64_t K, fn_dtype dt,
+                              hipStream_t stream);
 
 /* bias[t][n] = sum_k shift[t][k] * W[k][n] in fp32 (k in order).  shift:
  * [T,K], W: [K,N] row-major (unfolded), both in dt; bias: [T,N] fp32,
@@ -297,29 +310,32 @@ const char* fn_kernel_name_q8(int64_t M, int64_t K, int64_t N, int fp8_weights);
 fn_status fn_adaln_shift_bias(const void* shift, const void* W, float* bias, int64_t T, int64_t K, int64_t N,
                               fn_dtype dt, hipStream_t stream);
 
-/* Fused RMSNorm + AdaLN + projection, one launch (bf16). */
-fn_status fn_norm_proj_adaln(const void* x, const void* scale, const int* idx, const void* W_packed, const float* bias,
+/* Fused RMSNorm + AdaLN + projection, one launch (bf16), for M <= 16: the
+ * LDS-shared-x decode kernel with one modulation-table row per x row loaded
+ * beside x and the operand modulated in registers.  More rows return
+ * FN_ERR_SHAPE: the two-launch calls below serve them, faster than one
+ * launch would (the modulation is done once per row instead of once per
+ * output tile). */
+fn_status fn_norm_proj_adaln(const void* x, const float* mod, const int* idx, const void* W_packed, const float* bias,
                              void* y, int64_t M, int64_t K, int64_t N, int64_t T, float eps, hipStream_t stream);
 
-/* Fused RMSNorm + AdaLN + gate/up projections + SwiGLU, one launch (bf16). */
-fn_status fn_norm_proj_swiglu_adaln(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+/* Fused RMSNorm + AdaLN + gate/up projections + SwiGLU, one launch (bf16),
+ * M <= 16 as above. */
+fn_status fn_norm_proj_swiglu_adaln(const void* x, const float* mod, const int* idx, const void* W_gate_packed,
                                     const float* bias_gate, const void* W_up_packed, const float* bias_up, void* out,
                                     int64_t M, int64_t K, int64_t N, int64_t T, float eps, hipStream_t stream);
 
-/* Kernel instance of the two AdaLN calls (the prefill kernel above 64 rows
- * when T <= 63, else the decode kernel tiled over rows); "invalid" for bad
- * shapes. */
+/* Kernel instance of the two one-launch AdaLN calls; "invalid" for bad
+ * shapes and for M > 16. */
 const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu);
 
-/* Two-launch form of the two AdaLN calls above, for more than 16 rows.  A
- * pre-pass (fn_adaln_modulate below) writes the modulated operand and 1/RMS
- * of each raw row into a caller workspace; the plain projection kernel of the
- * row count (the LDS-shared-x decode kernel up to 64 rows, the prefill kernel
+/* Two-launch form of the two AdaLN calls above, any M.  A pre-pass
+ * (fn_adaln_modulate below) writes the modulated operand and 1/RMS of each
+ * raw row into a caller workspace; the plain projection kernel of the row
+ * count (the LDS-shared-x decode kernel up to 64 rows, the prefill kernel
  * above) then projects that operand and applies the deferred 1/RMS and the
- * bias rows in its epilogue.
- * The one-launch kernels modulate x once per output tile (every workgroup
- * along N repeats it); here it is done once per row, and any T is served.
- * The page's own AdaLN FC1 kernel runs as two launches as well
+ * bias rows in its epilogue.  The modulation is done once per row, and any
+ * T is served.  The page's own AdaLN FC1 kernel runs as two launches as well
  * ([FlashInfer #5521] "Fused Kernel on SM120").  Same arithmetic and
  * arguments as fn_norm_proj_adaln / fn_norm_proj_swiglu_adaln, plus:
  * workspace: device memory of at least fn_adaln_workspace_bytes(M, K)
@@ -327,56 +343,62 @@ const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int
  *   it and reads it back in stream order; its contents afterwards are
  *   unspecified, and calls in flight at the same time need separate
  *   workspaces.  With the workspace given the calls allocate nothing, so a
- *   caller may capture them into a HIP graph.  For M <= 16 the call is the one-launch call (the
- *   workspace is not touched and may be NULL, with workspace_bytes 0).
- * Errors as the one-launch calls, plus FN_ERR_WORKSPACE (M > 16 and the
- * workspace NULL, misaligned or smaller than needed) and FN_ERR_ALIAS (the
- * workspace overlaps an argument). */
-fn_status fn_norm_proj_adaln_ws(const void* x, const void* scale, const int* idx, const void* W_packed,
+ *   caller may capture them into a HIP graph.  For M <= 16 the call is the
+ *   one-launch call (the workspace is not touched and may be NULL, with
+ *   workspace_bytes 0).
+ * Errors as the one-launch calls (without their row limit), plus
+ * FN_ERR_WORKSPACE (M > 16 and the workspace NULL, misaligned or smaller
+ * than needed) and FN_ERR_ALIAS (the workspace overlaps an argument). */
+fn_status fn_norm_proj_adaln_ws(const void* x, const float* mod, const int* idx, const void* W_packed,
                                 const float* bias, void* y, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
                                 void* workspace, int64_t workspace_bytes, hipStream_t stream);
-fn_status fn_norm_proj_swiglu_adaln_ws(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+fn_status fn_norm_proj_swiglu_adaln_ws(const void* x, const float* mod, const int* idx, const void* W_gate_packed,
                                        const float* bias_gate, const void* W_up_packed, const float* bias_up,
                                        void* out, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
                                        void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes the two calls above need: the operand (M*K bf16) and one
- * fp32 per row, each rounded up to 256 bytes; 0 when M <= 16 (one launch)
- * or when M or K is outside the limits. */
+/* Workspace bytes the two calls above need: the operand and one fp32 per
+ * row, each rounded up to 256 bytes; 0 when M <= 16 (one launch) or when M
+ * or K is outside the limits.  The SwiGLU call multiplies the operand split
+ * in two bf16 parts (the rounded product and its remainder, 2*M*K bf16) with
+ * the same weights, so that its two products are those of the unrounded
+ * operand: the SiLU times up of two once-rounded products has no margin
+ * left against the bf16 tolerance at prefill sizes, the projection (M*K
+ * bf16, one rounding per term) has.  The size returned is the split one,
+ * enough for either call. */
 int64_t fn_adaln_workspace_bytes(int64_t M, int64_t K);
 
 /* Projection kernel instance of the two-launch calls (their one-launch
  * kernel for M <= 16); "invalid" for bad shapes. */
 const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu);
 
-/* AdaLN with fp8 weights (fn_fold_weights_fp8: E4M3 codes, one scale per
- * output column), in two launches for every M: the pre-pass above, then the
- * fp8-weight kernel of the row count on the modulated operand (decode up to
- * 64 rows, prefill above), with
+/* AdaLN with fp8 weights (fn_fold_weights_fp8 of the plain W, g = NULL:
+ * E4M3 codes, one scale per output column), in two launches for every M:
+ * the pre-pass above, then the fp8-weight kernel of the row count on the
+ * modulated operand (decode up to 64 rows, prefill above), with
  *   y[m] = s * (u[m] * q) / RMS(x[m]) + bias[idx[m]].
  * The pages' AdaLN FC1 kernel is an fp8 kernel with pre-processed weights
- * and scales ([FlashInfer #5521] "Fused
- * Kernel on SM120").  bias rows come from fn_adaln_shift_bias on the
- * unfolded bf16 W.  Arguments as fn_norm_proj_fp8 / fn_norm_proj_swiglu_fp8
- * plus scale, idx, bias and T as in the AdaLN calls above; workspace: at
- * least fn_adaln_prepass_bytes(M, K) bytes, 256-byte aligned,
- * overlapping no other argument (always needed).  Errors as the calls
- * above. */
-fn_status fn_norm_proj_adaln_fp8_ws(const void* x, const void* scale, const int* idx, const void* W8_packed,
+ * and scales ([FlashInfer #5521] "Fused Kernel on SM120").  bias rows come
+ * from fn_adaln_shift_bias on the bf16 W.  Arguments as fn_norm_proj_fp8 /
+ * fn_norm_proj_swiglu_fp8 plus mod, idx, bias and T as in the AdaLN calls
+ * above; workspace: at least fn_adaln_prepass_bytes(M, K) bytes, 256-byte
+ * aligned, overlapping no other argument (always needed).  Errors as the
+ * calls above. */
+fn_status fn_norm_proj_adaln_fp8_ws(const void* x, const float* mod, const int* idx, const void* W8_packed,
                                     const float* scales, const float* bias, void* y, int64_t M, int64_t K, int64_t N,
                                     int64_t T, float eps, void* workspace, int64_t workspace_bytes,
                                     hipStream_t stream);
-fn_status fn_norm_proj_swiglu_adaln_fp8_ws(const void* x, const void* scale, const int* idx, const void* W8_gate,
+fn_status fn_norm_proj_swiglu_adaln_fp8_ws(const void* x, const float* mod, const int* idx, const void* W8_gate,
                                            const float* s_gate, const float* bias_gate, const void* W8_up,
                                            const float* s_up, const float* bias_up, void* out, int64_t M, int64_t K,
                                            int64_t N, int64_t T, float eps, void* workspace, int64_t workspace_bytes,
                                            hipStream_t stream);
 
 /* Workspace bytes of the AdaLN calls that always run the pre-pass (the two
- * fp8-weight calls above and the two fp8-output calls below): the operand
- * (M*K bf16) and 1/RMS (M fp32), each rounded up to 256 bytes -- the layout
- * of fn_adaln_workspace_bytes, for every M >= 1; 0 for M < 1 or M, K
- * outside the limits. */
+ * fp8-weight calls above, the SwiGLU one on the split operand, and the two
+ * fp8-output calls below, on the operand rounded once): the size of
+ * fn_adaln_workspace_bytes for every M >= 1; 0 for M < 1 or M, K outside
+ * the limits. */
 int64_t fn_adaln_prepass_bytes(int64_t M, int64_t K);
 
 /* Projection kernel instance of the fp8 AdaLN calls; "invalid" for bad
@@ -387,20 +409,21 @@ const char* fn_kernel_name_adaln_fp8(int64_t M, int64_t K, int64_t N, int64_t T,
  * codes, one fp32 scale per 16-column row block, as fn_norm_proj_swiglu_q8),
  * in two launches for every M: the pre-pass, then the q8 kernel of the row
  * count on the modulated operand (the LDS-shared-x decode kernel up to 64
- * rows, the prefill kernel above, with bf16 or fp8 weights).  The AdaLN FC1 block of [FlashInfer #5521] ("Segmented
- * Chain": norm + AdaLN, FC1, SwiGLU, quantisation for the next projection)
- * with the output format of [FlashInfer #4040] as read for
- * fn_norm_proj_swiglu_q8.  The block values are
- *   v = silu(a) * b,  a = (u * W'_gate) / RMS(x) + bias_gate[idx],  b likewise,
+ * rows, the prefill kernel above, with bf16 or fp8 weights).  The AdaLN FC1
+ * block of [FlashInfer #5521] ("Segmented Chain": norm + AdaLN, FC1, SwiGLU,
+ * quantisation for the next projection) with the output format of
+ * [FlashInfer #4040] as read for fn_norm_proj_swiglu_q8.  The block values
+ * are
+ *   v = silu(a) * b,  a = (u * W_gate) / RMS(x) + bias_gate[idx],  b likewise,
  * u the pre-pass operand; arguments and errors as the calls above plus
  * out_codes [M,N] (uint8) and out_scales [M, ceil(N/16)] (fp32, 4-byte
  * aligned); workspace: fn_adaln_prepass_bytes(M, K) bytes. */
-fn_status fn_norm_proj_swiglu_adaln_q8_ws(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+fn_status fn_norm_proj_swiglu_adaln_q8_ws(const void* x, const float* mod, const int* idx, const void* W_gate_packed,
                                           const float* bias_gate, const void* W_up_packed, const float* bias_up,
                                           void* out_codes, float* out_scales, int64_t M, int64_t K, int64_t N,
                                           int64_t T, float eps, void* workspace, int64_t workspace_bytes,
                                           hipStream_t stream);
-fn_status fn_norm_proj_swiglu_adaln_fp8_q8_ws(const void* x, const void* scale, const int* idx, const void* W8_gate,
+fn_status fn_norm_proj_swiglu_adaln_fp8_q8_ws(const void* x, const float* mod, const int* idx, const void* W8_gate,
                                               const float* s_gate, const float* bias_gate, const void* W8_up,
                                               const float* s_up, const float* bias_up, void* out_codes,
                                               float* out_scales, int64_t M, int64_t K, int64_t N, int64_t T,
@@ -411,14 +434,14 @@ fn_status fn_norm_proj_swiglu_adaln_fp8_q8_ws(const void* x, const void* scale, 
  * shapes. */
 const char* fn_kernel_name_adaln_q8(int64_t M, int64_t K, int64_t N, int64_t T, int fp8_weights);
 
-/* The pre-pass alone: for each row m, with s = scale[idx[m]] (all zero when
+/* The pre-pass alone: for each row m, with mo = mod[idx[m]] (all zero when
  * idx[m] is outside [0, T)),
- *   u[m][k] = bf16_rne(fp32(x[m][k] + x[m][k] * s[k]))   (one fp32 rounding)
+ *   u[m][k] = bf16_rne(fp32(x[m][k] * mo[k]))
  *   rs[m]   = 1 / sqrt(sum_k x[m][k]^2 / K + eps)         (fp32, raw x)
- * -- the operand the one-launch AdaLN kernels form in LDS, and the deferred
- * scale.  x, scale: as above; u: [M,K] bf16, 16-byte aligned; rs: [M] fp32,
- * 4-byte aligned; neither may overlap an input or the other. */
-fn_status fn_adaln_modulate(const void* x, const void* scale, const int* idx, void* u, float* rs, int64_t M,
+ * -- the operand the one-launch AdaLN kernel forms in registers, and the
+ * deferred scale.  x, mod: as above; u: [M,K] bf16, 16-byte aligned; rs: [M]
+ * fp32, 4-byte aligned; neither may overlap an input or the other. */
+fn_status fn_adaln_modulate(const void* x, const float* mod, const int* idx, void* u, float* rs, int64_t M,
                             int64_t K, int64_t T, float eps, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------

@@ -77,6 +77,7 @@ def load():
         "fn_norm_proj_swiglu_fp8_q8": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp]),
         "fn_kernel_name_q8": (ctypes.c_char_p, [i64, i64, i64, i32]),
         "fn_adaln_shift_bias": (i32, [vp, vp, vp, i64, i64, i64, i32, vp]),
+        "fn_adaln_fold_table": (i32, [vp, vp, vp, i64, i64, i32, vp]),
         "fn_norm_proj_adaln": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
         "fn_norm_proj_swiglu_adaln": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
         "fn_kernel_name_adaln": (ctypes.c_char_p, [i64, i64, i64, i64, i32]),
@@ -420,42 +421,64 @@ def adaln_shift_bias(shift, W, out=None):
     return bias
 
 
-def _check_adaln(x, scale, idx, Wp: PackedWeights, bias):
+def adaln_fold_table(g, scale, out=None):
+    """mod[t] = g * (1 + scale[t]) in float32 (float64 arithmetic, one
+    rounding): the gain folded into the AdaLN modulation table, [T, K]."""
+    torch = _torch()
+    _need_cuda("g", g)
+    _need_cuda("scale", scale)
+    if scale.dim() != 2 or g.dim() != 1 or scale.shape[1] != g.shape[0] or scale.dtype != g.dtype:
+        raise ValueError(f"scale must be [T, {g.shape[0]}] of g's dtype, got {tuple(scale.shape)} {scale.dtype}")
+    T, K = scale.shape
+    mod = torch.empty((T, K), dtype=torch.float32, device=g.device) if out is None else out
+    _check(load().fn_adaln_fold_table(g.data_ptr(), scale.data_ptr(), mod.data_ptr(), T, K, _dt(g.dtype), _stream(g)))
+    return mod
+
+
+def _check_mod(mod, K):
+    torch = _torch()
+    _need_cuda("mod", mod)
+    if mod.dim() != 2 or mod.shape[1] != K or mod.dtype != torch.float32 or not mod.is_contiguous():
+        raise ValueError(f"mod must be a contiguous [T, {K}] float32 tensor (adaln_fold_table)")
+
+
+def _check_adaln(x, mod, idx, Wp: PackedWeights, bias):
     torch = _torch()
     _check_x(x, Wp)
     if x.dtype != torch.bfloat16:
         raise ValueError("AdaLN calls take bf16 activations and weights")
-    for name, t in (("scale", scale), ("idx", idx), ("bias", bias)):
+    for name, t in (("idx", idx), ("bias", bias)):
         _need_cuda(name, t)
-    if scale.dim() != 2 or scale.shape[1] != Wp.K or scale.dtype != torch.bfloat16:
-        raise ValueError(f"scale must be [T, {Wp.K}] bf16")
+    _check_mod(mod, Wp.K)
     if idx.dtype != torch.int32 or tuple(idx.shape) != (x.shape[0],):
         raise ValueError(f"idx must be [{x.shape[0]}] int32")
-    if tuple(bias.shape) != (scale.shape[0], Wp.N) or bias.dtype != torch.float32:
-        raise ValueError(f"bias must be [{scale.shape[0]}, {Wp.N}] float32")
+    if tuple(bias.shape) != (mod.shape[0], Wp.N) or bias.dtype != torch.float32:
+        raise ValueError(f"bias must be [{mod.shape[0]}, {Wp.N}] float32")
 
 
-def norm_proj_adaln(x, scale, idx, Wp: PackedWeights, bias, eps: float = 1e-6, out=None):
-    """y = (RMSNorm_g(x) * (1 + scale[idx]) + shift[idx]) @ W, one launch
-    (g folded into Wp, bias = adaln_shift_bias(shift, W))."""
-    _check_adaln(x, scale, idx, Wp, bias)
+def norm_proj_adaln(x, mod, idx, Wp: PackedWeights, bias, eps: float = 1e-6, out=None):
+    """y = (RMSNorm_g(x) * (1 + scale[idx]) + shift[idx]) @ W, one launch, up
+    to 16 rows (mod = adaln_fold_table(g, scale), Wp = fold_weights(None, W),
+    bias = adaln_shift_bias(shift, W))."""
+    _check_adaln(x, mod, idx, Wp, bias)
     M, N = x.shape[0], Wp.N
     y = _out(out, M, N, x)
-    _check(load().fn_norm_proj_adaln(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Wp.data.data_ptr(),
-                                     bias.data_ptr(), y.data_ptr(), M, Wp.K, N, scale.shape[0], eps, _stream(x)))
+    _check(load().fn_norm_proj_adaln(x.data_ptr(), mod.data_ptr(), idx.data_ptr(), Wp.data.data_ptr(),
+                                     bias.data_ptr(), y.data_ptr(), M, Wp.K, N, mod.shape[0], eps, _stream(x)))
     return y
 
 
-def norm_proj_swiglu_adaln(x, scale, idx, Wg: PackedWeights, bias_g, Wu: PackedWeights, bias_u, eps: float = 1e-6,
+def norm_proj_swiglu_adaln(x, mod, idx, Wg: PackedWeights, bias_g, Wu: PackedWeights, bias_u, eps: float = 1e-6,
                            out=None):
-    """out = silu(h @ W_gate) * (h @ W_up) with h the AdaLN-modulated norm, one launch."""
-    _check_adaln(x, scale, idx, Wg, bias_g)
-    _check_adaln(x, scale, idx, Wu, bias_u)
+    """out = silu(h @ W_gate) * (h @ W_up) with h the AdaLN-modulated norm, one
+    launch, up to 16 rows."""
+    _check_adaln(x, mod, idx, Wg, bias_g)
+    _check_adaln(x, mod, idx, Wu, bias_u)
     M, N = x.shape[0], Wg.N
     y = _out(out, M, N, x)
-    _check(load().fn_norm_proj_swiglu_adaln(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Wg.data.data_ptr(),
+    _check(load().fn_norm_proj_swiglu_adaln(x.data_ptr(), mod.data_ptr(), idx.data_ptr(), Wg.data.data_ptr(),
                                             bias_g.data_ptr(), Wu.data.data_ptr(), bias_u.data_ptr(), y.data_ptr(),
-                                            M, Wg.K, N, scale.shape[0], eps, _stream(x)))
+                                            M, Wg.K, N, mod.shape[0], eps, _stream(x)))
     return y
 
 
@@ -480,32 +503,31 @@ def _workspace(workspace, M: int, K: int, like):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def norm_proj_adaln_ws(x, scale, idx, Wp: PackedWeights, bias, eps: float = 1e-6, out=None, workspace=None):
-    """norm_proj_adaln in two launches above 64 rows: the AdaLN pre-pass
-    into a workspace (allocated here when not given), then the prefill
-    kernel on the modulated operand."""
-    _check_adaln(x, scale, idx, Wp, bias)
+def norm_proj_adaln_ws(x, mod, idx, Wp: PackedWeights, bias, eps: float = 1e-6, out=None, workspace=None):
+    """norm_proj_adaln for any M: above 16 rows in two launches, the AdaLN
+    pre-pass into a workspace (allocated here when not given), then the
+    projection kernel of the row count on the modulated operand."""
+    _check_adaln(x, mod, idx, Wp, bias)
     M, N = x.shape[0], Wp.N
     y = _out(out, M, N, x)
     ws, nbytes = _workspace(workspace, M, Wp.K, x)
-    _check(load().fn_norm_proj_adaln_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Wp.data.data_ptr(),
-                                        bias.data_ptr(), y.data_ptr(), M, Wp.K, N, scale.shape[0], eps,
+    _check(load().fn_norm_proj_adaln_ws(x.data_ptr(), mod.data_ptr(), idx.data_ptr(), Wp.data.data_ptr(),
+                                        bias.data_ptr(), y.data_ptr(), M, Wp.K, N, mod.shape[0], eps,
                                         None if ws is None else ws.data_ptr(), nbytes, _stream(x)))
     return y
 
 
-def norm_proj_swiglu_adaln_ws(x, scale, idx, Wg: PackedWeights, bias_g, Wu: PackedWeights, bias_u,
+def norm_proj_swiglu_adaln_ws(x, mod, idx, Wg: PackedWeights, bias_g, Wu: PackedWeights, bias_u,
                               eps: float = 1e-6, out=None, workspace=None):
-    """norm_proj_swiglu_adaln in two launches above 64 rows (see
-    norm_proj_adaln_ws)."""
-    _check_adaln(x, scale, idx, Wg, bias_g)
-    _check_adaln(x, scale, idx, Wu, bias_u)
+    """norm_proj_swiglu_adaln for any M (see norm_proj_adaln_ws)."""
+    _check_adaln(x, mod, idx, Wg, bias_g)
+    _check_adaln(x, mod, idx, Wu, bias_u)
     M, N = x.shape[0], Wg.N
     y = _out(out, M, N, x)
     ws, nbytes = _workspace(workspace, M, Wg.K, x)
-    _check(load().fn_norm_proj_swiglu_adaln_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Wg.data.data_ptr(),
+    _check(load().fn_norm_proj_swiglu_adaln_ws(x.data_ptr(), mod.data_ptr(), idx.data_ptr(), Wg.data.data_ptr(),
                                                bias_g.data_ptr(), Wu.data.data_ptr(), bias_u.data_ptr(),
-                                               y.data_ptr(), M, Wg.K, N, scale.shape[0], eps,
+                                               y.data_ptr(), M, Wg.K, N, mod.shape[0], eps,
                                                None if ws is None else ws.data_ptr(), nbytes, _stream(x)))
     return y
 
@@ -519,17 +541,16 @@ def adaln_prepass_bytes(M: int, K: int) -> int:
     return int(load().fn_adaln_prepass_bytes(M, K))
 
 
-def _check_adaln_fp8(x, scale, idx, P: PackedFp8, bias):
+def _check_adaln_fp8(x, mod, idx, P: PackedFp8, bias):
     torch = _torch()
     _check_x_fp8(x, P)
-    for name, t in (("scale", scale), ("idx", idx), ("bias", bias)):
+    for name, t in (("idx", idx), ("bias", bias)):
         _need_cuda(name, t)
-    if scale.dim() != 2 or scale.shape[1] != P.K or scale.dtype != torch.bfloat16:
-        raise ValueError(f"scale must be [T, {P.K}] bf16")
+    _check_mod(mod, P.K)
     if idx.dtype != torch.int32 or tuple(idx.shape) != (x.shape[0],):
         raise ValueError(f"idx must be [{x.shape[0]}] int32")
-    if tuple(bias.shape) != (scale.shape[0], P.N) or bias.dtype != torch.float32:
-        raise ValueError(f"bias must be [{scale.shape[0]}, {P.N}] float32")
+    if tuple(bias.shape) != (mod.shape[0], P.N) or bias.dtype != torch.float32:
+        raise ValueError(f"bias must be [{mod.shape[0]}, {P.N}] float32")
 
 
 def _workspace_fp8(workspace, M: int, K: int, like):
@@ -542,32 +563,32 @@ def _workspace_fp8(workspace, M: int, K: int, like):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def norm_proj_adaln_fp8_ws(x, scale, idx, P: PackedFp8, bias, eps: float = 1e-6, out=None, workspace=None):
+def norm_proj_adaln_fp8_ws(x, mod, idx, P: PackedFp8, bias, eps: float = 1e-6, out=None, workspace=None):
     """AdaLN with E4M3 weights, two launches (the pre-pass into a workspace,
     allocated here when not given, then the fp8 kernel)."""
-    _check_adaln_fp8(x, scale, idx, P, bias)
+    _check_adaln_fp8(x, mod, idx, P, bias)
     M, N = x.shape[0], P.N
     y = _out(out, M, N, x)
     ws, nbytes = _workspace_fp8(workspace, M, P.K, x)
-    _check(load().fn_norm_proj_adaln_fp8_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), P.data.data_ptr(),
+    _check(load().fn_norm_proj_adaln_fp8_ws(x.data_ptr(), mod.data_ptr(), idx.data_ptr(), P.data.data_ptr(),
                                             P.scales.data_ptr(), bias.data_ptr(), y.data_ptr(), M, P.K, N,
-                                            scale.shape[0], eps, None if ws is None else ws.data_ptr(), nbytes,
+                                            mod.shape[0], eps, None if ws is None else ws.data_ptr(), nbytes,
                                             _stream(x)))
     return y
 
 
-def norm_proj_swiglu_adaln_fp8_ws(x, scale, idx, Pg: PackedFp8, bias_g, Pu: PackedFp8, bias_u, eps: float = 1e-6,
+def norm_proj_swiglu_adaln_fp8_ws(x, mod, idx, Pg: PackedFp8, bias_g, Pu: PackedFp8, bias_u, eps: float = 1e-6,
                                   out=None, workspace=None):
     """SwiGLU AdaLN with E4M3 gate/up weights, two launches."""
-    _check_adaln_fp8(x, scale, idx, Pg, bias_g)
-    _check_adaln_fp8(x, scale, idx, Pu, bias_u)
+    _check_adaln_fp8(x, mod, idx, Pg, bias_g)
+    _check_adaln_fp8(x, mod, idx, Pu, bias_u)
     M, N = x.shape[0], Pg.N
     y = _out(out, M, N, x)
     ws, nbytes = _workspace_fp8(workspace, M, Pg.K, x)
-    _check(load().fn_norm_proj_swiglu_adaln_fp8_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Pg.data.data_ptr(),
+    _check(load().fn_norm_proj_swiglu_adaln_fp8_ws(x.data_ptr(), mod.data_ptr(), idx.data_ptr(), Pg.data.data_ptr(),
                                                    Pg.scales.data_ptr(), bias_g.data_ptr(), Pu.data.data_ptr(),
                                                    Pu.scales.data_ptr(), bias_u.data_ptr(), y.data_ptr(), M, Pg.K, N,
-                                                   scale.shape[0], eps, None if ws is None else ws.data_ptr(),
+                                                   mod.shape[0], eps, None if ws is None else ws.data_ptr(),
                                                    nbytes, _stream(x)))
     return y
 
@@ -576,34 +597,34 @@ def kernel_name_adaln_fp8(M: int, K: int, N: int, T: int, swiglu: bool) -> str:
     return load().fn_kernel_name_adaln_fp8(M, K, N, T, int(swiglu)).decode()
 
 
-def norm_proj_swiglu_adaln_q8_ws(x, scale, idx, Wg: PackedWeights, bias_g, Wu: PackedWeights, bias_u,
+def norm_proj_swiglu_adaln_q8_ws(x, mod, idx, Wg: PackedWeights, bias_g, Wu: PackedWeights, bias_u,
                                  eps: float = 1e-6, out=None, workspace=None):
     """AdaLN FC1 + SwiGLU with E4M3 row-block output, two launches:
     (codes, scales)."""
-    _check_adaln(x, scale, idx, Wg, bias_g)
-    _check_adaln(x, scale, idx, Wu, bias_u)
+    _check_adaln(x, mod, idx, Wg, bias_g)
+    _check_adaln(x, mod, idx, Wu, bias_u)
     M, N = x.shape[0], Wg.N
     codes, scales = _q8_out(out, M, N, x)
     ws, nbytes = _workspace_fp8(workspace, M, Wg.K, x)
-    _check(load().fn_norm_proj_swiglu_adaln_q8_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), Wg.data.data_ptr(),
+    _check(load().fn_norm_proj_swiglu_adaln_q8_ws(x.data_ptr(), mod.data_ptr(), idx.data_ptr(), Wg.data.data_ptr(),
                                                   bias_g.data_ptr(), Wu.data.data_ptr(), bias_u.data_ptr(),
-                                                  codes.data_ptr(), scales.data_ptr(), M, Wg.K, N, scale.shape[0], eps,
+                                                  codes.data_ptr(), scales.data_ptr(), M, Wg.K, N, mod.shape[0], eps,
                                                   None if ws is None else ws.data_ptr(), nbytes, _stream(x)))
     return codes, scales
 
 
-def norm_proj_swiglu_adaln_fp8_q8_ws(x, scale, idx, Pg: PackedFp8, bias_g, Pu: PackedFp8, bias_u,
+def norm_proj_swiglu_adaln_fp8_q8_ws(x, mod, idx, Pg: PackedFp8, bias_g, Pu: PackedFp8, bias_u,
                                      eps: float = 1e-6, out=None, workspace=None):
     """The same with E4M3 gate/up weights: (codes, scales)."""
-    _check_adaln_fp8(x, scale, idx, Pg, bias_g)
-    _check_adaln_fp8(x, scale, idx, Pu, bias_u)
+    _check_adaln_fp8(x, mod, idx, Pg, bias_g)
+    _check_adaln_fp8(x, mod, idx, Pu, bias_u)
     M, N = x.shape[0], Pg.N
     codes, scales = _q8_out(out, M, N, x)
     ws, nbytes = _workspace_fp8(workspace, M, Pg.K, x)
-    _check(load().fn_norm_proj_swiglu_adaln_fp8_q8_ws(x.data_ptr(), scale.data_ptr(), idx.data_ptr(),
+    _check(load().fn_norm_proj_swiglu_adaln_fp8_q8_ws(x.data_ptr(), mod.data_ptr(), idx.data_ptr(),
                                                       Pg.data.data_ptr(), Pg.scales.data_ptr(), bias_g.data_ptr(),
                                                       Pu.data.data_ptr(), Pu.scales.data_ptr(), bias_u.data_ptr(),
-                                                      codes.data_ptr(), scales.data_ptr(), M, Pg.K, N, scale.shape[0],
+                                                      codes.data_ptr(), scales.data_ptr(), M, Pg.K, N, mod.shape[0],
                                                       eps, None if ws is None else ws.data_ptr(), nbytes, _stream(x)))
     return codes, scales
 
@@ -612,23 +633,22 @@ def kernel_name_adaln_q8(M: int, K: int, N: int, T: int, fp8_weights: bool) -> s
     return load().fn_kernel_name_adaln_q8(M, K, N, T, int(fp8_weights)).decode()
 
 
-def adaln_modulate(x, scale, idx, eps: float = 1e-6, u=None, rs=None):
-    """The AdaLN pre-pass alone: (u, rs) with u = bf16(x + x * scale[idx])
+def adaln_modulate(x, mod, idx, eps: float = 1e-6, u=None, rs=None):
+    """The AdaLN pre-pass alone: (u, rs) with u = bf16(fp32(x * mod[idx]))
     [M, K] and rs = 1/RMS(x) [M] float32."""
     torch = _torch()
-    for name, t in (("x", x), ("scale", scale), ("idx", idx)):
+    for name, t in (("x", x), ("idx", idx)):
         _need_cuda(name, t)
     if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_contiguous():
         raise ValueError("x must be a contiguous [M, K] bf16 tensor")
     M, K = x.shape
-    if scale.dim() != 2 or scale.shape[1] != K or scale.dtype != torch.bfloat16 or not scale.is_contiguous():
-        raise ValueError(f"scale must be a contiguous [T, {K}] bf16 tensor")
+    _check_mod(mod, K)
     if idx.dtype != torch.int32 or tuple(idx.shape) != (M,):
         raise ValueError(f"idx must be [{M}] int32")
     u = torch.empty((M, K), dtype=torch.bfloat16, device=x.device) if u is None else u
     rs = torch.empty((M,), dtype=torch.float32, device=x.device) if rs is None else rs
-    _check(load().fn_adaln_modulate(x.data_ptr(), scale.data_ptr(), idx.data_ptr(), u.data_ptr(), rs.data_ptr(), M, K,
-                                    scale.shape[0], eps, _stream(x)))
+    _check(load().fn_adaln_modulate(x.data_ptr(), mod.data_ptr(), idx.data_ptr(), u.data_ptr(), rs.data_ptr(), M, K,
+                                    mod.shape[0], eps, _stream(x)))
     return u, rs
 
 
@@ -745,7 +765,7 @@ __all__ = ["load", "fold_weights", "norm_proj", "norm_proj_swiglu", "rmsnorm", "
            "norm_proj_fp8", "norm_proj_swiglu_fp8", "kernel_name_fp8", "Step", "FnCall", "FN_CALL_NORM_PROJ",
            "FN_CALL_NORM_PROJ_SWIGLU", "FN_CALL_NORM_PROJ_FP8", "FN_CALL_NORM_PROJ_SWIGLU_FP8",
            "FN_CALL_NORM_PROJ_SWIGLU_Q8", "FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8", "Q8_BLOCK", "norm_proj_swiglu_q8",
-           "norm_proj_swiglu_fp8_q8", "kernel_name_q8", "adaln_shift_bias", "norm_proj_adaln",
+           "norm_proj_swiglu_fp8_q8", "kernel_name_q8", "adaln_shift_bias", "adaln_fold_table", "norm_proj_adaln",
            "norm_proj_swiglu_adaln", "kernel_name_adaln", "adaln_workspace_bytes", "norm_proj_adaln_ws",
            "norm_proj_swiglu_adaln_ws", "kernel_name_adaln_ws", "adaln_modulate", "adaln_prepass_bytes",
            "norm_proj_adaln_fp8_ws", "norm_proj_swiglu_adaln_fp8_ws", "kernel_name_adaln_fp8",

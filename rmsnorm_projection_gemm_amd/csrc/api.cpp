@@ -126,7 +126,7 @@ fn_status fp8_common(const void* x, const void* wg, const float* sg, const void*
     return fail(FN_ERR_ALIAS, "output overlaps an input");
   if (check_only) return FN_OK;
   if (M > 64) {
-    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, false, false, true);
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, false, true);
     return hip_status(fn::launch_prefill_fp8(plan, x, wg, sg, swiglu ? wu : nullptr, swiglu ? su : nullptr, y, (int)M,
                                              (int)K, (int)N, eps, stream),
                       plan.name);
@@ -168,7 +168,7 @@ fn_status q8_common(const void* x, const void* wg, const float* sg, const void* 
   if (check_only) return FN_OK;
   uint8_t* q = static_cast<uint8_t*>(codes);
   if (M > 64) {
-    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, false, f8);
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, f8);
     if (f8)
       return hip_status(fn::launch_prefill_fp8(plan, x, wg, sg, wu, su, nullptr, (int)M, (int)K, (int)N, eps, stream, q,
                                                scales),
@@ -182,73 +182,79 @@ fn_status q8_common(const void* x, const void* wg, const float* sg, const void* 
                     plan.name);
 }
 
-// AdaLN prologue (bf16): x [M,K], scale [T,K], idx [M], packed W' (gate and
-// up for SwiGLU), bias rows [T,N] fp32, y [M,N].
-fn_status adaln_common(const void* x, const void* scale, const int* idx, const void* wg, const float* bg,
+constexpr int64_t kAdalnOneLaunchRows = 16;   // the one-launch AdaLN kernel's rows; the _ws calls run it up to here
+
+// AdaLN prologue (bf16): x [M,K], modulation table mod [T,K] fp32 (the gain
+// folded in), idx [M], packed plain W (gate and up for SwiGLU), bias rows
+// [T,N] fp32, y [M,N].  check_only validates the arguments every AdaLN call
+// shares; the one-launch call itself takes at most 16 rows.
+fn_status adaln_common(const void* x, const float* mod, const int* idx, const void* wg, const float* bg,
                        const void* wu, const float* bu, void* y, int64_t M, int64_t K, int64_t N, int64_t T,
                        float eps, hipStream_t stream, bool swiglu, bool check_only = false) {
   g_last_error[0] = '\0';
   FN_TRY(check_k(K));
   FN_TRY(check_mn(M, N));
   FN_TRY(check_eps(eps));
-  if (T < 1 || T > INT32_MAX || T * K * 2 > INT32_MAX)
-    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*2 < 2^31", (long long)T);
+  if (T < 1 || T > INT32_MAX || T * K * 4 > INT32_MAX)
+    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*4 < 2^31", (long long)T);
+  if (!check_only && M > kAdalnOneLaunchRows)
+    return fail(FN_ERR_SHAPE,
+                "M=%lld: the one-launch AdaLN calls take at most %lld rows; more rows run faster in two launches "
+                "(fn_norm_proj_adaln_ws / fn_norm_proj_swiglu_adaln_ws with a workspace)",
+                (long long)M, (long long)kAdalnOneLaunchRows);
   if (M == 0 || N == 0) return FN_OK;
-  if (x == nullptr || scale == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, scale or idx is NULL");
+  if (x == nullptr || mod == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, mod or idx is NULL");
   if (wg == nullptr || bg == nullptr) return fail(FN_ERR_NULL, "W_packed or bias is NULL");
   if (swiglu && (wu == nullptr || bu == nullptr)) return fail(FN_ERR_NULL, "W_up_packed or bias_up is NULL");
   if (y == nullptr) return fail(FN_ERR_NULL, "y is NULL");
-  if (!aligned(x, 16) || !aligned(scale, 16)) return fail(FN_ERR_ALIGN, "x and scale must be 16-byte aligned");
+  if (!aligned(x, 16) || !aligned(mod, 16)) return fail(FN_ERR_ALIGN, "x and mod must be 16-byte aligned");
   if (!aligned(wg, 16) || (swiglu && !aligned(wu, 16)))
     return fail(FN_ERR_ALIGN, "packed weights must be 16-byte aligned");
   if (!aligned(idx, 4) || !aligned(bg, 4) || (swiglu && !aligned(bu, 4)))
     return fail(FN_ERR_ALIGN, "idx and bias must be 4-byte aligned");
   if (!aligned(y, 16)) return fail(FN_ERR_ALIGN, "output must be 16-byte aligned");
   const int64_t yb = M * N * 2, wb = packed_bytes(K, N, FN_BF16), bb = T * N * 4;
-  if (overlap(y, yb, x, M * K * 2) || overlap(y, yb, scale, T * K * 2) || overlap(y, yb, idx, M * 4) ||
+  if (overlap(y, yb, x, M * K * 2) || overlap(y, yb, mod, T * K * 4) || overlap(y, yb, idx, M * 4) ||
       overlap(y, yb, wg, wb) || overlap(y, yb, bg, bb) || (swiglu && (overlap(y, yb, wu, wb) || overlap(y, yb, bu, bb))))
     return fail(FN_ERR_ALIAS, "output overlaps an input");
   if (check_only) return FN_OK;
-  const fn::AdalnArgs ad{scale, idx, bg, swiglu ? bu : nullptr, (int)T};
-  if (M > 64 && fn::prefill_adaln_fits(T)) {
-    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, true);
-    return hip_status(fn::launch_prefill(fn::DType::BF16, plan, x, wg, swiglu ? wu : nullptr, y, (int)M, (int)K,
-                                         (int)N, eps, stream, nullptr, nullptr, &ad),
-                      plan.name);
-  }
-  const fn::FusedPlan plan = fn::plan_adaln(M, N, T, swiglu);
+  const fn::AdalnArgs ad{mod, idx, bg, swiglu ? bu : nullptr, (int)T};
+  const fn::FusedPlan plan = fn::plan_adaln(M, N, swiglu);
   return hip_status(fn::launch_adaln(plan, x, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, eps, ad, stream),
                     plan.name);
 }
 
-constexpr int64_t kAdalnOneLaunchRows = 16;   // up to here the _ws calls run the one-launch kernel
-
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
-// Two-launch AdaLN workspace: the modulated operand u [M,K] bf16, then
-// 1/RMS per row [M] fp32, each at a 256-byte boundary.
-int64_t adaln_ws_need(int64_t M, int64_t K) { return align256(M * K * 2) + align256(M * 4); }
+// Two-launch AdaLN workspace: the modulated operand u [M,K] bf16 (split in
+// two parts for SwiGLU with bf16 output: [2M,K]), then 1/RMS per row [M]
+// fp32, each at a 256-byte boundary.  The exported sizes are those of the
+// split form, enough for every call.
+int64_t adaln_u_bytes(int64_t M, int64_t K, bool split) { return align256(M * K * 2 * (split ? 2 : 1)); }
+int64_t adaln_ws_need(int64_t M, int64_t K, bool split = true) {
+  return adaln_u_bytes(M, K, split) + align256(M * 4);
+}
 
-fn_status adaln_ws_common(const void* x, const void* scale, const int* idx, const void* wg, const float* bg,
+fn_status adaln_ws_common(const void* x, const float* mod, const int* idx, const void* wg, const float* bg,
                           const void* wu, const float* bu, void* y, int64_t M, int64_t K, int64_t N, int64_t T,
                           float eps, void* ws, int64_t ws_bytes, hipStream_t stream, bool swiglu) {
-  FN_TRY(adaln_common(x, scale, idx, wg, bg, wu, bu, y, M, K, N, T, eps, stream, swiglu, true));
+  FN_TRY(adaln_common(x, mod, idx, wg, bg, wu, bu, y, M, K, N, T, eps, stream, swiglu, true));
   if (M == 0 || N == 0) return FN_OK;
   if (M <= kAdalnOneLaunchRows)
-    return adaln_common(x, scale, idx, wg, bg, wu, bu, y, M, K, N, T, eps, stream, swiglu);
-  const int64_t need = adaln_ws_need(M, K);
+    return adaln_common(x, mod, idx, wg, bg, wu, bu, y, M, K, N, T, eps, stream, swiglu);
+  const int64_t need = adaln_ws_need(M, K, swiglu);
   if (ws == nullptr) return fail(FN_ERR_WORKSPACE, "workspace is NULL (the call needs %lld bytes)", (long long)need);
   if (!aligned(ws, 256)) return fail(FN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (ws_bytes < need)
     return fail(FN_ERR_WORKSPACE, "workspace_bytes=%lld, the call needs %lld", (long long)ws_bytes, (long long)need);
   const int64_t wb = packed_bytes(K, N, FN_BF16), bb = T * N * 4;
-  if (overlap(ws, need, x, M * K * 2) || overlap(ws, need, scale, T * K * 2) || overlap(ws, need, idx, M * 4) ||
+  if (overlap(ws, need, x, M * K * 2) || overlap(ws, need, mod, T * K * 4) || overlap(ws, need, idx, M * 4) ||
       overlap(ws, need, wg, wb) || overlap(ws, need, bg, bb) || overlap(ws, need, y, M * N * 2) ||
       (swiglu && (overlap(ws, need, wu, wb) || overlap(ws, need, bu, bb))))
     return fail(FN_ERR_ALIAS, "workspace overlaps an argument");
   void* u = ws;
-  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(M * K * 2));
-  FN_TRY(hip_status(fn::launch_adaln_modulate(x, scale, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
+  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + adaln_u_bytes(M, K, swiglu));
+  FN_TRY(hip_status(fn::launch_adaln_modulate(x, mod, idx, (int)T, u, rs, (int)M, (int)K, eps, stream, swiglu),
                     "adaln_modulate"));
   const fn::AdalnArgs ad{nullptr, idx, bg, swiglu ? bu : nullptr, (int)T};
   if (M <= 64) {
@@ -257,7 +263,7 @@ fn_status adaln_ws_common(const void* x, const void* scale, const int* idx, cons
                                                (int)K, (int)N, ad, stream),
                       plan.name);
   }
-  const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, false, true);
+  const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, true);
   return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, ad,
                                               stream),
                     plan.name);
@@ -265,7 +271,7 @@ fn_status adaln_ws_common(const void* x, const void* scale, const int* idx, cons
 
 // Two-launch AdaLN with fp8 weights (E4M3 codes + column scales), every M:
 // the pre-pass, then the fp8 decode kernel on the modulated operand.
-fn_status adaln_fp8_ws_common(const void* x, const void* scale, const int* idx, const void* wg, const float* sg,
+fn_status adaln_fp8_ws_common(const void* x, const float* mod, const int* idx, const void* wg, const float* sg,
                               const float* bg, const void* wu, const float* su, const float* bu, void* y, int64_t M,
                               int64_t K, int64_t N, int64_t T, float eps, void* ws, int64_t ws_bytes,
                               hipStream_t stream, bool swiglu) {
@@ -273,28 +279,28 @@ fn_status adaln_fp8_ws_common(const void* x, const void* scale, const int* idx, 
   FN_TRY(check_k(K));
   FN_TRY(check_mn(M, N));
   FN_TRY(check_eps(eps));
-  if (T < 1 || T > INT32_MAX || T * K * 2 > INT32_MAX)
-    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*2 < 2^31", (long long)T);
+  if (T < 1 || T > INT32_MAX || T * K * 4 > INT32_MAX)
+    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*4 < 2^31", (long long)T);
   if (M == 0 || N == 0) return FN_OK;
-  if (x == nullptr || scale == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, scale or idx is NULL");
+  if (x == nullptr || mod == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, mod or idx is NULL");
   if (wg == nullptr || sg == nullptr || bg == nullptr)
     return fail(FN_ERR_NULL, swiglu ? "W8_gate, s_gate or bias_gate is NULL" : "W8_packed, scales or bias is NULL");
   if (swiglu && (wu == nullptr || su == nullptr || bu == nullptr))
     return fail(FN_ERR_NULL, "W8_up, s_up or bias_up is NULL");
   if (y == nullptr) return fail(FN_ERR_NULL, swiglu ? "out is NULL" : "y is NULL");
-  if (!aligned(x, 16) || !aligned(scale, 16)) return fail(FN_ERR_ALIGN, "x and scale must be 16-byte aligned");
+  if (!aligned(x, 16) || !aligned(mod, 16)) return fail(FN_ERR_ALIGN, "x and mod must be 16-byte aligned");
   if (!aligned(wg, 16) || (swiglu && !aligned(wu, 16)))
     return fail(FN_ERR_ALIGN, "packed fp8 weights must be 16-byte aligned");
   if (!aligned(idx, 4) || !aligned(sg, 4) || !aligned(bg, 4) || (swiglu && (!aligned(su, 4) || !aligned(bu, 4))))
     return fail(FN_ERR_ALIGN, "idx, scales and bias must be 4-byte aligned");
   if (!aligned(y, 16)) return fail(FN_ERR_ALIGN, "output must be 16-byte aligned");
   const int64_t yb = M * N * 2, wb = packed_fp8_bytes(K, N), sb = N * 4, bb = T * N * 4;
-  const void* ins[] = {x, scale, idx, wg, sg, bg, swiglu ? wu : nullptr, swiglu ? su : nullptr,
+  const void* ins[] = {x, mod, idx, wg, sg, bg, swiglu ? wu : nullptr, swiglu ? su : nullptr,
                        swiglu ? bu : nullptr};
-  const int64_t inb[] = {M * K * 2, T * K * 2, M * 4, wb, sb, bb, wb, sb, bb};
+  const int64_t inb[] = {M * K * 2, T * K * 4, M * 4, wb, sb, bb, wb, sb, bb};
   for (int i = 0; i < 9; ++i)
     if (overlap(y, yb, ins[i], inb[i])) return fail(FN_ERR_ALIAS, "output overlaps an input");
-  const int64_t need = adaln_ws_need(M, K);
+  const int64_t need = adaln_ws_need(M, K, swiglu);
   if (ws == nullptr) return fail(FN_ERR_WORKSPACE, "workspace is NULL (the call needs %lld bytes)", (long long)need);
   if (!aligned(ws, 256)) return fail(FN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (ws_bytes < need)
@@ -303,12 +309,12 @@ fn_status adaln_fp8_ws_common(const void* x, const void* scale, const int* idx, 
     if (overlap(ws, need, ins[i], inb[i])) return fail(FN_ERR_ALIAS, "workspace overlaps an argument");
   if (overlap(ws, need, y, yb)) return fail(FN_ERR_ALIAS, "workspace overlaps an argument");
   void* u = ws;
-  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(M * K * 2));
-  FN_TRY(hip_status(fn::launch_adaln_modulate(x, scale, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
+  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + adaln_u_bytes(M, K, swiglu));
+  FN_TRY(hip_status(fn::launch_adaln_modulate(x, mod, idx, (int)T, u, rs, (int)M, (int)K, eps, stream, swiglu),
                     "adaln_modulate"));
   const fn::AdalnArgs ad{nullptr, idx, bg, swiglu ? bu : nullptr, (int)T};
   if (M > 64) {
-    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, false, true, true);
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, true, true);
     return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, ad,
                                                 stream, nullptr, nullptr, sg, swiglu ? su : nullptr),
                       plan.name);
@@ -321,7 +327,7 @@ fn_status adaln_fp8_ws_common(const void* x, const void* scale, const int* idx, 
 
 // Two-launch AdaLN + SwiGLU with fp8 row-block output, every M: bf16 weights
 // (f8 false) or E4M3 codes with column scales (f8 true).
-fn_status adaln_q8_ws_common(const void* x, const void* scale, const int* idx, const void* wg, const float* sg,
+fn_status adaln_q8_ws_common(const void* x, const float* mod, const int* idx, const void* wg, const float* sg,
                              const float* bg, const void* wu, const float* su, const float* bu, void* codes,
                              float* qscales, int64_t M, int64_t K, int64_t N, int64_t T, float eps, void* ws,
                              int64_t ws_bytes, hipStream_t stream, bool f8) {
@@ -329,28 +335,28 @@ fn_status adaln_q8_ws_common(const void* x, const void* scale, const int* idx, c
   FN_TRY(check_k(K));
   FN_TRY(check_mn(M, N));
   FN_TRY(check_eps(eps));
-  if (T < 1 || T > INT32_MAX || T * K * 2 > INT32_MAX)
-    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*2 < 2^31", (long long)T);
+  if (T < 1 || T > INT32_MAX || T * K * 4 > INT32_MAX)
+    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*4 < 2^31", (long long)T);
   if (M == 0 || N == 0) return FN_OK;
-  if (x == nullptr || scale == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, scale or idx is NULL");
+  if (x == nullptr || mod == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, mod or idx is NULL");
   if (wg == nullptr || wu == nullptr || bg == nullptr || bu == nullptr)
     return fail(FN_ERR_NULL, "gate or up weights or bias rows are NULL");
   if (f8 && (sg == nullptr || su == nullptr)) return fail(FN_ERR_NULL, "s_gate or s_up is NULL");
   if (codes == nullptr || qscales == nullptr) return fail(FN_ERR_NULL, "out_codes or out_scales is NULL");
-  if (!aligned(x, 16) || !aligned(scale, 16)) return fail(FN_ERR_ALIGN, "x and scale must be 16-byte aligned");
+  if (!aligned(x, 16) || !aligned(mod, 16)) return fail(FN_ERR_ALIGN, "x and mod must be 16-byte aligned");
   if (!aligned(wg, 16) || !aligned(wu, 16)) return fail(FN_ERR_ALIGN, "packed weights must be 16-byte aligned");
   if (!aligned(idx, 4) || !aligned(bg, 4) || !aligned(bu, 4) || (f8 && (!aligned(sg, 4) || !aligned(su, 4))))
     return fail(FN_ERR_ALIGN, "idx, scales and bias must be 4-byte aligned");
   if (!aligned(qscales, 4)) return fail(FN_ERR_ALIGN, "out_scales must be 4-byte aligned");
   const int64_t wb = f8 ? packed_fp8_bytes(K, N) : packed_bytes(K, N, FN_BF16), sb = f8 ? N * 4 : 0, bb = T * N * 4;
-  const void* ins[] = {x, scale, idx, wg, wu, bg, bu, f8 ? sg : nullptr, f8 ? su : nullptr};
-  const int64_t inb[] = {M * K * 2, T * K * 2, M * 4, wb, wb, bb, bb, sb, sb};
+  const void* ins[] = {x, mod, idx, wg, wu, bg, bu, f8 ? sg : nullptr, f8 ? su : nullptr};
+  const int64_t inb[] = {M * K * 2, T * K * 4, M * 4, wb, wb, bb, bb, sb, sb};
   const int64_t cb = M * N, qb = M * ((N + 15) / 16) * 4;
   for (int i = 0; i < 9; ++i)
     if (overlap(codes, cb, ins[i], inb[i]) || overlap(qscales, qb, ins[i], inb[i]))
       return fail(FN_ERR_ALIAS, "an output overlaps an input");
   if (overlap(codes, cb, qscales, qb)) return fail(FN_ERR_ALIAS, "out_codes overlaps out_scales");
-  const int64_t need = adaln_ws_need(M, K);
+  const int64_t need = adaln_ws_need(M, K, false);
   if (ws == nullptr) return fail(FN_ERR_WORKSPACE, "workspace is NULL (the call needs %lld bytes)", (long long)need);
   if (!aligned(ws, 256)) return fail(FN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (ws_bytes < need)
@@ -360,13 +366,13 @@ fn_status adaln_q8_ws_common(const void* x, const void* scale, const int* idx, c
   if (overlap(ws, need, codes, cb) || overlap(ws, need, qscales, qb))
     return fail(FN_ERR_ALIAS, "workspace overlaps an argument");
   void* u = ws;
-  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256(M * K * 2));
-  FN_TRY(hip_status(fn::launch_adaln_modulate(x, scale, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
+  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + adaln_u_bytes(M, K, false));
+  FN_TRY(hip_status(fn::launch_adaln_modulate(x, mod, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
                     "adaln_modulate"));
   const fn::AdalnArgs ad{nullptr, idx, bg, bu, (int)T};
   uint8_t* q = static_cast<uint8_t*>(codes);
   if (M > 64) {
-    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, true, f8);
+    const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, true, f8);
     return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, wu, nullptr, (int)M, (int)K, (int)N, ad, stream, q,
                                                 qscales, f8 ? sg : nullptr, f8 ? su : nullptr),
                       plan.name);
@@ -575,7 +581,7 @@ fn_status fn_norm_proj_swiglu_fp8_q8(const void* x, const void* W8_gate, const f
 
 const char* fn_kernel_name_q8(int64_t M, int64_t K, int64_t N, int fp8_weights) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
-  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, false, fp8_weights != 0).name;
+  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, fp8_weights != 0).name;
   return fn::plan_decode_q8(fp8_weights != 0, M, N).name;
 }
 
@@ -597,22 +603,39 @@ fn_status fn_adaln_shift_bias(const void* shift, const void* W, float* bias, int
   return hip_status(fn::launch_adaln_bias(to_dt(dt), shift, W, bias, (int)T, (int)K, (int)N, stream), "adaln_bias");
 }
 
-fn_status fn_norm_proj_adaln(const void* x, const void* scale, const int* idx, const void* W_packed, const float* bias,
-                             void* y, int64_t M, int64_t K, int64_t N, int64_t T, float eps, hipStream_t stream) {
-  return adaln_common(x, scale, idx, W_packed, bias, nullptr, nullptr, y, M, K, N, T, eps, stream, false);
+fn_status fn_adaln_fold_table(const void* g, const void* scale, float* mod, int64_t T, int64_t K, fn_dtype dt,
+                              hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (!dtype_ok(dt)) return fail(FN_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  FN_TRY(check_k(K));
+  if (T < 0 || T > INT32_MAX || T * K * 4 > INT32_MAX)
+    return fail(FN_ERR_SHAPE, "T=%lld out of range (T*K*4 must stay below 2^31)", (long long)T);
+  if (T == 0) return FN_OK;
+  if (g == nullptr || scale == nullptr || mod == nullptr) return fail(FN_ERR_NULL, "g, scale or mod is NULL");
+  const int64_t e = esize(dt);
+  if (!aligned(g, (uintptr_t)e) || !aligned(scale, (uintptr_t)e) || !aligned(mod, 4))
+    return fail(FN_ERR_ALIGN, "g and scale need their element alignment, mod 4 bytes");
+  if (overlap(mod, T * K * 4, g, K * e) || overlap(mod, T * K * 4, scale, T * K * e))
+    return fail(FN_ERR_ALIAS, "mod overlaps g or scale");
+  return hip_status(fn::launch_adaln_fold_table(to_dt(dt), g, scale, mod, (int)T, (int)K, stream), "adaln_fold_table");
 }
 
-fn_status fn_norm_proj_swiglu_adaln(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+fn_status fn_norm_proj_adaln(const void* x, const float* mod, const int* idx, const void* W_packed, const float* bias,
+                             void* y, int64_t M, int64_t K, int64_t N, int64_t T, float eps, hipStream_t stream) {
+  return adaln_common(x, mod, idx, W_packed, bias, nullptr, nullptr, y, M, K, N, T, eps, stream, false);
+}
+
+fn_status fn_norm_proj_swiglu_adaln(const void* x, const float* mod, const int* idx, const void* W_gate_packed,
                                     const float* bias_gate, const void* W_up_packed, const float* bias_up, void* out,
                                     int64_t M, int64_t K, int64_t N, int64_t T, float eps, hipStream_t stream) {
-  return adaln_common(x, scale, idx, W_gate_packed, bias_gate, W_up_packed, bias_up, out, M, K, N, T, eps, stream,
+  return adaln_common(x, mod, idx, W_gate_packed, bias_gate, W_up_packed, bias_up, out, M, K, N, T, eps, stream,
                       true);
 }
 
 const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
-  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
-  if (M > 64 && fn::prefill_adaln_fits(T)) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, true).name;
-  return fn::plan_adaln(M, N, T, swiglu != 0).name;
+  if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kAdalnOneLaunchRows || N < 1 || N > kMaxN || T < 1)
+    return "invalid";
+  return fn::plan_adaln(M, N, swiglu != 0).name;
 }
 
 int64_t fn_adaln_workspace_bytes(int64_t M, int64_t K) {
@@ -620,24 +643,24 @@ int64_t fn_adaln_workspace_bytes(int64_t M, int64_t K) {
   return adaln_ws_need(M, K);
 }
 
-fn_status fn_norm_proj_adaln_ws(const void* x, const void* scale, const int* idx, const void* W_packed,
+fn_status fn_norm_proj_adaln_ws(const void* x, const float* mod, const int* idx, const void* W_packed,
                                 const float* bias, void* y, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
                                 void* workspace, int64_t workspace_bytes, hipStream_t stream) {
-  return adaln_ws_common(x, scale, idx, W_packed, bias, nullptr, nullptr, y, M, K, N, T, eps, workspace,
+  return adaln_ws_common(x, mod, idx, W_packed, bias, nullptr, nullptr, y, M, K, N, T, eps, workspace,
                          workspace_bytes, stream, false);
 }
 
-fn_status fn_norm_proj_swiglu_adaln_ws(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+fn_status fn_norm_proj_swiglu_adaln_ws(const void* x, const float* mod, const int* idx, const void* W_gate_packed,
                                        const float* bias_gate, const void* W_up_packed, const float* bias_up,
                                        void* out, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
                                        void* workspace, int64_t workspace_bytes, hipStream_t stream) {
-  return adaln_ws_common(x, scale, idx, W_gate_packed, bias_gate, W_up_packed, bias_up, out, M, K, N, T, eps,
+  return adaln_ws_common(x, mod, idx, W_gate_packed, bias_gate, W_up_packed, bias_up, out, M, K, N, T, eps,
                          workspace, workspace_bytes, stream, true);
 }
 
 const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
-  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true).name;
+  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, true).name;
   if (M > kAdalnOneLaunchRows) return fn::plan_decode_premod(M, N, swiglu != 0).name;
   return fn_kernel_name_adaln(M, K, N, T, swiglu);
 }
@@ -647,74 +670,74 @@ int64_t fn_adaln_prepass_bytes(int64_t M, int64_t K) {
   return adaln_ws_need(M, K);
 }
 
-fn_status fn_norm_proj_adaln_fp8_ws(const void* x, const void* scale, const int* idx, const void* W8_packed,
+fn_status fn_norm_proj_adaln_fp8_ws(const void* x, const float* mod, const int* idx, const void* W8_packed,
                                     const float* scales, const float* bias, void* y, int64_t M, int64_t K, int64_t N,
                                     int64_t T, float eps, void* workspace, int64_t workspace_bytes,
                                     hipStream_t stream) {
-  return adaln_fp8_ws_common(x, scale, idx, W8_packed, scales, bias, nullptr, nullptr, nullptr, y, M, K, N, T, eps,
+  return adaln_fp8_ws_common(x, mod, idx, W8_packed, scales, bias, nullptr, nullptr, nullptr, y, M, K, N, T, eps,
                              workspace, workspace_bytes, stream, false);
 }
 
-fn_status fn_norm_proj_swiglu_adaln_fp8_ws(const void* x, const void* scale, const int* idx, const void* W8_gate,
+fn_status fn_norm_proj_swiglu_adaln_fp8_ws(const void* x, const float* mod, const int* idx, const void* W8_gate,
                                            const float* s_gate, const float* bias_gate, const void* W8_up,
                                            const float* s_up, const float* bias_up, void* out, int64_t M, int64_t K,
                                            int64_t N, int64_t T, float eps, void* workspace, int64_t workspace_bytes,
                                            hipStream_t stream) {
-  return adaln_fp8_ws_common(x, scale, idx, W8_gate, s_gate, bias_gate, W8_up, s_up, bias_up, out, M, K, N, T, eps,
+  return adaln_fp8_ws_common(x, mod, idx, W8_gate, s_gate, bias_gate, W8_up, s_up, bias_up, out, M, K, N, T, eps,
                              workspace, workspace_bytes, stream, true);
 }
 
 const char* fn_kernel_name_adaln_fp8(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
-  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true, true).name;
+  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, true, true).name;
   return fn::plan_decode_premod(M, N, swiglu != 0, true).name;
 }
 
-fn_status fn_norm_proj_swiglu_adaln_q8_ws(const void* x, const void* scale, const int* idx, const void* W_gate_packed,
+fn_status fn_norm_proj_swiglu_adaln_q8_ws(const void* x, const float* mod, const int* idx, const void* W_gate_packed,
                                           const float* bias_gate, const void* W_up_packed, const float* bias_up,
                                           void* out_codes, float* out_scales, int64_t M, int64_t K, int64_t N,
                                           int64_t T, float eps, void* workspace, int64_t workspace_bytes,
                                           hipStream_t stream) {
-  return adaln_q8_ws_common(x, scale, idx, W_gate_packed, nullptr, bias_gate, W_up_packed, nullptr, bias_up, out_codes,
+  return adaln_q8_ws_common(x, mod, idx, W_gate_packed, nullptr, bias_gate, W_up_packed, nullptr, bias_up, out_codes,
                             out_scales, M, K, N, T, eps, workspace, workspace_bytes, stream, false);
 }
 
-fn_status fn_norm_proj_swiglu_adaln_fp8_q8_ws(const void* x, const void* scale, const int* idx, const void* W8_gate,
+fn_status fn_norm_proj_swiglu_adaln_fp8_q8_ws(const void* x, const float* mod, const int* idx, const void* W8_gate,
                                               const float* s_gate, const float* bias_gate, const void* W8_up,
                                               const float* s_up, const float* bias_up, void* out_codes,
                                               float* out_scales, int64_t M, int64_t K, int64_t N, int64_t T,
                                               float eps, void* workspace, int64_t workspace_bytes,
                                               hipStream_t stream) {
-  return adaln_q8_ws_common(x, scale, idx, W8_gate, s_gate, bias_gate, W8_up, s_up, bias_up, out_codes, out_scales, M,
+  return adaln_q8_ws_common(x, mod, idx, W8_gate, s_gate, bias_gate, W8_up, s_up, bias_up, out_codes, out_scales, M,
                             K, N, T, eps, workspace, workspace_bytes, stream, true);
 }
 
 const char* fn_kernel_name_adaln_q8(int64_t M, int64_t K, int64_t N, int64_t T, int fp8_weights) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
-  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, true, fp8_weights != 0).name;
+  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, true, fp8_weights != 0).name;
   return fn::plan_decode_q8_premod(fp8_weights != 0, M, N).name;
 }
 
-fn_status fn_adaln_modulate(const void* x, const void* scale, const int* idx, void* u, float* rs, int64_t M,
+fn_status fn_adaln_modulate(const void* x, const float* mod, const int* idx, void* u, float* rs, int64_t M,
                             int64_t K, int64_t T, float eps, hipStream_t stream) {
   g_last_error[0] = '\0';
   FN_TRY(check_k(K));
   FN_TRY(check_mn(M, 0));
   FN_TRY(check_eps(eps));
-  if (T < 1 || T > INT32_MAX || T * K * 2 > INT32_MAX)
-    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*2 < 2^31", (long long)T);
+  if (T < 1 || T > INT32_MAX || T * K * 4 > INT32_MAX)
+    return fail(FN_ERR_SHAPE, "T=%lld must be >= 1 with T*K*4 < 2^31", (long long)T);
   if (M == 0) return FN_OK;
-  if (x == nullptr || scale == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, scale or idx is NULL");
+  if (x == nullptr || mod == nullptr || idx == nullptr) return fail(FN_ERR_NULL, "x, mod or idx is NULL");
   if (u == nullptr || rs == nullptr) return fail(FN_ERR_NULL, "u or rs is NULL");
-  if (!aligned(x, 16) || !aligned(scale, 16) || !aligned(u, 16))
-    return fail(FN_ERR_ALIGN, "x, scale and u must be 16-byte aligned");
+  if (!aligned(x, 16) || !aligned(mod, 16) || !aligned(u, 16))
+    return fail(FN_ERR_ALIGN, "x, mod and u must be 16-byte aligned");
   if (!aligned(idx, 4) || !aligned(rs, 4)) return fail(FN_ERR_ALIGN, "idx and rs must be 4-byte aligned");
   const int64_t xb = M * K * 2;
-  if (overlap(u, xb, x, xb) || overlap(u, xb, scale, T * K * 2) || overlap(u, xb, idx, M * 4) ||
-      overlap(rs, M * 4, x, xb) || overlap(rs, M * 4, scale, T * K * 2) || overlap(rs, M * 4, idx, M * 4) ||
+  if (overlap(u, xb, x, xb) || overlap(u, xb, mod, T * K * 4) || overlap(u, xb, idx, M * 4) ||
+      overlap(rs, M * 4, x, xb) || overlap(rs, M * 4, mod, T * K * 4) || overlap(rs, M * 4, idx, M * 4) ||
       overlap(u, xb, rs, M * 4))
     return fail(FN_ERR_ALIAS, "output overlaps an input");
-  return hip_status(fn::launch_adaln_modulate(x, scale, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
+  return hip_status(fn::launch_adaln_modulate(x, mod, idx, (int)T, u, rs, (int)M, (int)K, eps, stream),
                     "adaln_modulate");
 }
 
@@ -785,7 +808,7 @@ fn_status fn_step_destroy(fn_step step) {
 
 const char* fn_kernel_name_fp8(int64_t M, int64_t K, int64_t N, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
-  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, false, true).name;
+  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true).name;
   return fn::plan_fp8(M, K, N, swiglu != 0).name;
 }
 

@@ -29,6 +29,8 @@
 // of masked: their results are never stored, and rows do not mix in the
 // product (nor on the Gram diagonal), so the clamped lanes cannot disturb
 // valid outputs.  Only the ragged last k-block (K % KB != 0) is masked.
+#include <type_traits>
+
 #include "fn_device.h"
 #include "fn_launch.h"
 
@@ -87,6 +89,41 @@ __global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) acc[m][mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // fp32 operands: two-level sums.  The MFMAs accumulate a run of k-blocks
+  // into acc / gram, which are then added into the totals and cleared, so
+  // each fp32 sum has about sqrt(K) terms per level instead of K in one
+  // (the rounding error of a K-term fp32 sum grows with its length: a
+  // single level misses 1e-5 relative at K = 2^20).  bf16 keeps one level:
+  // its operands' own rounding dominates.
+  constexpr bool TWO = std::is_same<T, float>::value;
+  f32x4 tacc[TWO ? NMAT : 1][TWO ? MF : 1][TWO ? NF : 1];
+  f32x4 tgram[TWO ? MF : 1];
+#pragma unroll
+  for (int mf = 0; mf < (TWO ? MF : 1); ++mf) {
+    tgram[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < (TWO ? NMAT : 1); ++m)
+#pragma unroll
+      for (int nf = 0; nf < (TWO ? NF : 1); ++nf) tacc[m][mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto fold = [&]() {
+    if constexpr (TWO) {
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+        tgram[mf] += gram[mf];
+        gram[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) {
+            tacc[m][mf][nf] += acc[m][mf][nf];
+            acc[m][mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+    }
+  };
+  // k-blocks per first-level run: 64 (1024 k values of fp32)
+  constexpr int FOLD_ITERS = 32 / U > 0 ? 32 / U : 1;   // main-loop iterations of 2 U k-blocks
 
   // One stage = U k-blocks of operands in registers.
   struct Stage {
@@ -137,6 +174,7 @@ __global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
     if (kb + 2 * U <= hi) {
       Stage s0, s1;
       load(s0, kb);
+      int it = 0;
       for (; kb + 4 * U <= hi; kb += 2 * U) {
         load(s1, kb + U);
         __builtin_amdgcn_sched_barrier(0);
@@ -146,6 +184,12 @@ __global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         compute(s1);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (TWO) {
+          if (++it == FOLD_ITERS) {
+            fold();
+            it = 0;
+          }
+        }
       }
       load(s1, kb + U);
       __builtin_amdgcn_sched_barrier(0);
@@ -175,6 +219,18 @@ __global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) wv[m][nf] = __builtin_nontemporal_load(wp[m][nf] + (size_t)kb * kWave);
     step(xv, wv);
+  }
+  if constexpr (TWO) {
+    // the totals become the sums the epilogue reads
+    fold();
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) {
+      gram[mf] = tgram[mf];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) acc[m][mf][nf] = tacc[m][mf][nf];
+    }
   }
 
   // Partials meet in LDS.  Accumulator element r of lane l is row

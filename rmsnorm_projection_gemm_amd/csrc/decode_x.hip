@@ -57,7 +57,7 @@ struct DecodeXArgs {
   const float* su;   // fp8 weights: column scales of wu
   uint8_t* q;        // fp8 output: E4M3 codes [M, N] (y unused)
   float* qs;         // fp8 output: scales [M, nblocks], one per 16-column row block
-  const void* sc;    // AdaLN: scale table [T, K] (bf16)
+  const float* mod;  // AdaLN: modulation table g * (1 + scale) [T, K] (fp32)
   const int* idx;    // AdaLN: table row of each x row [M]
   const float* bg;   // AdaLN: bias rows shift @ W [T, N] (gate for SwiGLU)
   const float* bu;   // AdaLN: bias rows of W_up
@@ -98,16 +98,20 @@ __device__ inline void decode_e4m3x16(u32x4 w, u32x4& lo, u32x4& hi) {
 // MF: 16-row blocks of x.  NC: 16-column blocks per wave (for SwiGLU each
 // with its gate and up stream).  NWV: waves, sharing the x fragments.  U:
 // k-blocks per stage.  F8: E4M3 weights.  Q8: E4M3 output with row-block
-// scales instead of a y in x's dtype.  AD: AdaLN -- the MFMA operand is
-// x * (1 + scale[idx]) while the sum of squares stays on x, and the epilogue
-// adds the row's bias row.  TSL (AdaLN tables of fewer than 8 * NWV rows):
-// each stage stages the table's slice (all T rows, the stage's 64 k values,
-// eight rows per wave) instead of one scale row per x row.  EX: the
-// projection half of the two-launch AdaLN form -- x is the operand the
-// pre-pass already modulated, 1/RMS of each raw row comes from a.rs (no Gram
-// blocks) and the epilogue adds the row's bias row.
-template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false, int NS = 4, bool TSL = false,
-          bool EX = false>
+// scales instead of a y in x's dtype.  AD: AdaLN, one row block -- the
+// MFMA operand is x * mod[idx] (the modulation table row of each x row,
+// loaded beside x in x's layout, two 16-byte loads per x chunk since the
+// table is fp32) rounded to bf16 in registers, while the sum of squares
+// stays on x; the epilogue adds the row's bias row.  EX: the projection
+// half of the two-launch AdaLN form -- x is the operand the pre-pass already
+// modulated, 1/RMS of each raw row comes from a.rs (no Gram blocks) and the
+// epilogue adds the row's bias row.  LO: the operand in two bf16 parts,
+// each multiplied with the same weight fragment, so the product is that of
+// the unrounded operand (AD: split in registers, modulate8_split; EX: the
+// pre-pass's [2M, K] operand, row 2m the rounded part of x row m and row
+// 2m+1 the remainder, the remainder staged in LDS beside x).
+template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false, int NS = 4, bool EX = false,
+          bool LO = false>
 __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   static_assert(NS >= 3 && NS <= 6, "LDS ring slots");
   constexpr int D = NS - 1;                // stages in flight
@@ -116,27 +120,23 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   constexpr int XF = U * MF;               // x loads (1 KiB each) per stage
   constexpr int XPW = (XF + NWV - 1) / NWV;   // x loads each wave issues per stage
   constexpr int WLD = F8 ? U / 2 : U;      // weight loads per stream per stage (fp8: one per k-block pair)
-  // vector-memory ops per wave per stage (AdaLN: the scale rows of its x
-  // loads, or one load of the table slice)
-  constexpr int LPW = WLD * NST + XPW + (AD ? (TSL ? 1 : XPW) : 0);
-  static_assert(!TSL || (AD && U == 2), "table slices: AdaLN, 64 k values per stage");
+  // vector-memory ops per wave per stage (AdaLN: two loads of modulation
+  // values per x load; a split operand: one load of its remainder)
+  constexpr int LPW = WLD * NST + XPW + (AD ? 2 * XPW : 0) + (EX && LO ? XPW : 0);
+  static_assert(!LO || (AD && MF == 1) || (EX && !Q8), "split operand: AdaLN, bf16 output");
   // Loads q >= XF (when NWV does not divide XF) fetch nothing and write
   // zeros into the slot's padding, so every wave issues the same count
   // (measured: skipping them instead is no faster).
   constexpr int XSL = XPW * NWV * kFragBytes;   // x part of a slot
-  constexpr int TSLOT = TSL ? NWV * kFragBytes : 0;   // table slice: rows 8w .. 8w+7 from wave w
-  // AdaLN: per ring slot also the scale rows, modulated in place (or, TSL,
-  // the modulated x) and the table slice, each in an LDS array of its own:
-  // the compiler then sees that the operand reads of a slot cannot alias the
+  // AdaLN: per ring slot also the modulation values of its x chunks, the
+  // first and the second four of each chunk in LDS arrays of their own: the
+  // compiler then sees that the operand reads of a slot cannot alias the
   // global-to-LDS loads still landing in other slots (one shared array made
   // it drain every load in flight before them)
   constexpr int SLOT = XSL;
-  constexpr int MSLOT = AD ? XSL : 16;
-  static_assert(!AD || (NC == 1 && !F8 && !Q8), "AdaLN: bf16 weights and output, one column block per wave");
-  // modulate once per workgroup, in LDS, before the stage barrier: several
-  // row blocks, or a table slice (read only before the barrier that lets
-  // the slot's next slice be loaded)
-  constexpr bool AD_INPLACE = AD && (MF > 1 || TSL);
+  constexpr int MSLOT = AD || LO ? XSL : 16;   // EX && LO: the remainder part of x
+  static_assert(!AD || (MF == 1 && NC == 1 && !F8 && !Q8),
+                "AdaLN: one row block, bf16 weights and output, one column block per wave");
   // Epilogue through LDS (one lane per row, 16-byte stores): fp8 output
   // always, bf16 output when each wave owns one column block.
   constexpr bool STAGE = Q8 || (NC == 1 && NWV <= NS);
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   static_assert(!BIAS || STAGE, "the AdaLN bias is added in the staged epilogue");
   static_assert(U % 2 == 0, "each x load moves two k-blocks of 8 rows");
   static_assert(D * LPW < 64, "vmcnt range");
-  static_assert(NS * (SLOT + (AD ? MSLOT + TSLOT : 0)) + NWV * XPW * 16 * 4 <= 160 * 1024, "LDS budget");
+  static_assert(NS * (SLOT + (AD ? 2 * MSLOT : (LO ? MSLOT : 0))) + NWV * XPW * 16 * 4 <= 160 * 1024, "LDS budget");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[SLOT];
@@ -160,12 +160,12 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t mring3[NS > 3 ? MSLOT : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t mring4[NS > 4 ? MSLOT : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t mring5[NS > 5 ? MSLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t tring0[TSL ? TSLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t tring1[TSL ? TSLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t tring2[TSL ? TSLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t tring3[TSL && NS > 3 ? TSLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t tring4[TSL && NS > 4 ? TSLOT : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t tring5[TSL && NS > 5 ? TSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t hring0[MSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t hring1[MSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t hring2[MSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t hring3[NS > 3 ? MSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t hring4[NS > 4 ? MSLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t hring5[NS > 5 ? MSLOT : 16];
   __shared__ float ssp[NWV][XPW][16];      // Gram diagonals
   __shared__ __attribute__((aligned(16))) float inv_s[MF * 16];   // 1/RMS per row
   auto slot_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
@@ -174,8 +174,8 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   auto mod_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
     return s == 0 ? mring0 : (s == 1 ? mring1 : (s == 2 ? mring2 : (s == 3 ? mring3 : (s == 4 ? mring4 : mring5))));
   };
-  auto tab_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
-    return s == 0 ? tring0 : (s == 1 ? tring1 : (s == 2 ? tring2 : (s == 3 ? tring3 : (s == 4 ? tring4 : tring5))));
+  auto modh_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* {
+    return s == 0 ? hring0 : (s == 1 ? hring1 : (s == 2 ? hring2 : (s == 3 ? hring3 : (s == 4 ? hring4 : hring5))));
   };
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -196,8 +196,16 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     scol[c] = F8 && col < a.N ? (c < NC ? a.sg : a.su)[col] : 1.f;
   }
 
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc_x(static_cast<const __bf16*>(a.x) + (size_t)m0 * a.K,
-                                                (int64_t)min(MF * 16, a.M - m0) * a.K * 2);
+  // x rows of this workgroup; a split operand (EX && LO) has two rows per x
+  // row, the rounded part at even rows and the remainder at odd ones: rows
+  // past M then lie past both ranges
+  constexpr int XRS = EX && LO ? 2 : 1;   // operand rows per x row
+  const int nrows = min(MF * 16, a.M - m0);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc_x(static_cast<const __bf16*>(a.x) + (size_t)XRS * m0 * a.K,
+                                                (int64_t)(XRS * nrows - (XRS - 1)) * a.K * 2);
+  __amdgpu_buffer_rsrc_t xlr = xr;
+  if constexpr (EX && LO)
+    xlr = make_rsrc_x(static_cast<const __bf16*>(a.x) + ((size_t)2 * m0 + 1) * a.K, (int64_t)(2 * nrows - 1) * a.K * 2);
   // AdaLN: this lane's bias values (its rows, its column), fetched now
   float bias[MF][4][NMAT];
 #pragma unroll
@@ -240,7 +248,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   // row block i) whose Gram block wave q % NWV accumulates.
   uint32_t xoff[XPW];
   int xk[XPW];
-  uint32_t soff[XPW], sok[XPW];   // AdaLN: the same chunk of the row's scale-table row
+  uint32_t soff[XPW], sok[XPW];   // AdaLN: the same chunk of the row's modulation-table row (fp32)
 #pragma unroll
   for (int i = 0; i < XPW; ++i) {
     const int q = w + NWV * i;
@@ -248,24 +256,15 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     const int c = (lane & 7) ^ (lr >> 1);
     const int row = 16 * ((q >> 1) % MF) + lr;
     xk[i] = q < XF ? (2 * (q / (2 * MF)) + (c >> 2)) * 32 + (c & 3) * 8 : 1 << 30;   // past XF: never in range
-    xoff[i] = (uint32_t)(row * a.K + (q < XF ? xk[i] : 0)) * 2u;
+    xoff[i] = (uint32_t)(row * XRS * a.K + (q < XF ? xk[i] : 0)) * 2u;
     if constexpr (AD) {
       const int t = (q < XF && m0 + row < a.M) ? a.idx[m0 + row] : -1;
-      sok[i] = (unsigned)t < (unsigned)a.T ? 0xffffffffu : 0u;   // out-of-range index: scale 0
-      if constexpr (TSL)   // the chunk's place in the staged slice; the last row stays zero
-        soff[i] = (uint32_t)((sok[i] ? t : 8 * NWV - 1) * 128 + c * 16);
-      else
-        soff[i] = sok[i] ? (uint32_t)(t * a.K + xk[i]) * 2u : 0u;
+      sok[i] = (unsigned)t < (unsigned)a.T ? 0xffffffffu : 0u;   // out-of-range index: modulation 0
+      soff[i] = sok[i] ? (uint32_t)(t * a.K + xk[i]) * 4u : 0u;
     }
   }
-  // TSL: this wave's one table load of each stage (rows 8w .. 8w+7)
-  uint32_t tload = kOutOfRangeX;
-  if constexpr (TSL) {
-    const int trow = 8 * w + (lane >> 3);
-    if (trow < a.T) tload = (uint32_t)(trow * a.K + (lane & 7) * 8) * 2u;
-  }
   __amdgpu_buffer_rsrc_t sr = xr;
-  if constexpr (AD) sr = make_rsrc_x(a.sc, (int64_t)a.T * a.K * 2);
+  if constexpr (AD) sr = make_rsrc_x(a.mod, (int64_t)a.T * a.K * 4);
   // LDS offset of this lane's MFMA operand (row lrow, chunk lgrp) for
   // k-block u, row block i of a stage
   auto x_at = [&](int u, int i) __attribute__((always_inline)) -> int {
@@ -290,23 +289,29 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_x)(base + (w + NWV * i) * kFragBytes), 16, off, 0, 0,
                                                0);
     }
-    if constexpr (AD && !TSL) {
+    if constexpr (AD) {
+      // the chunk's 8 modulation values, 32 bytes: the first 16 into the
+      // slot's first array, the second 16 into its second
 #pragma unroll
       for (int i = 0; i < XPW; ++i) {
         const uint32_t in = sok[i] & live & (uint32_t)((k0 + xk[i] - a.K) >> 31);
-        const uint32_t off = ((soff[i] + (uint32_t)k0 * 2u) & in) | (kOutOfRangeX & ~in);
+        const uint32_t off = ((soff[i] + (uint32_t)k0 * 4u) & in) | (kOutOfRangeX & ~in);
+        const uint32_t offh = ((soff[i] + (uint32_t)k0 * 4u + 16u) & in) | (kOutOfRangeX & ~in);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_x)(mod_ptr(slot) + (w + NWV * i) * kFragBytes), 16,
                                                  off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_x)(modh_ptr(slot) + (w + NWV * i) * kFragBytes), 16,
+                                                 offh, 0, 0, 0);
       }
     }
-  };
-  // TSL: the table slice of stage st (rows past T and k past K read zero)
-  auto issue_t = [&](int slot, int st) __attribute__((always_inline)) {
-    if constexpr (TSL) {
-      const uint32_t in = (uint32_t)((st - a.stages) >> 31) & (tload == kOutOfRangeX ? 0u : ~0u) &
-                          (uint32_t)((st * 64 + (lane & 7) * 8 - a.K) >> 31);
-      const uint32_t off = ((tload + (uint32_t)st * 128u) & in) | (kOutOfRangeX & ~in);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_x)(tab_ptr(slot) + w * kFragBytes), 16, off, 0, 0, 0);
+    if constexpr (EX && LO) {
+      // the remainder rows, at the same offsets from their own base
+#pragma unroll
+      for (int i = 0; i < XPW; ++i) {
+        const uint32_t in = live & (uint32_t)((k0 + xk[i] - a.K) >> 31);
+        const uint32_t off = ((xoff[i] + (uint32_t)k0 * 2u) & in) | (kOutOfRangeX & ~in);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xlr, (lds_ptr_x)(mod_ptr(slot) + (w + NWV * i) * kFragBytes), 16, off,
+                                                 0, 0, 0);
+      }
     }
   };
   u32x4 wv[NS][WLD][NST];
@@ -331,37 +336,14 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 #pragma unroll
   for (int j = 0; j < XPW; ++j) gram[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // AdaLN, in LDS: this wave modulates the x chunks it loaded itself (its
-  // loads have landed), x * (1 + scale) into the slot's second x area, so
-  // each chunk is modulated once per workgroup; x stays raw for the sums of
-  // squares.  The scale comes from the chunk's scale row or (TSL) from the
-  // staged table slice.
-  auto modulate_own = [&](int slot) __attribute__((always_inline)) {
-    const uint8_t* base = slot_ptr(slot);
-    uint8_t* mb = mod_ptr(slot);
-#pragma unroll
-    for (int j = 0; j < XPW; ++j) {
-      if (w + NWV * j < XF) {
-        const int o = (w + NWV * j) * kFragBytes + lane * 16;
-        u32x4* sp = reinterpret_cast<u32x4*>(mb + o);
-        const u32x4 sc = *reinterpret_cast<const u32x4*>(TSL ? tab_ptr(slot) + soff[j] : mb + o);
-        *sp = modulate8(*reinterpret_cast<const u32x4*>(base + o), sc);
-      }
-    }
-  };
-  // Stage st lives in ring slot s and W' buffer s.  TSL: stage st+1 is
-  // modulated during step st, after its barrier (so off the path to the
-  // next one): the wait below then also covers this wave's loads of stage
-  // st+1, and the next barrier publishes the modulated chunks.
+  // Stage st lives in ring slot s and W' buffer s.
   auto step = [&](int s, int st) __attribute__((always_inline)) {
     // Own loads of stage st are done once at most the D-1 younger stages
     // are in flight; the barrier extends that to the x loads of every wave
     // and retires every wave's reads of the slot refilled below.
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt_x<(TSL ? D - 2 : D - 1) * LPW>();
+    wait_vmcnt_x<(D - 1) * LPW>();
     uint8_t* base = slot_ptr(s);
-    if constexpr (AD_INPLACE && !TSL) modulate_own(s);
-    if constexpr (AD_INPLACE) __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     u32x4 xv[U][MF];
@@ -369,29 +351,32 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < MF; ++i) xv[u][i] = *reinterpret_cast<const u32x4*>((AD_INPLACE ? mod_ptr(s) : base) + x_at(u, i));
+      for (int i = 0; i < MF; ++i) xv[u][i] = *reinterpret_cast<const u32x4*>(base + x_at(u, i));
     if constexpr (!EX) {
 #pragma unroll
       for (int j = 0; j < XPW; ++j) xg[j] = *reinterpret_cast<const u32x4*>(base + frag_at(w + NWV * j));
     }
-    // AdaLN, one row block: the few operand chunks are modulated in
-    // registers, after the next stage's loads are issued
-    u32x4 sv[AD && !AD_INPLACE ? U : 1][AD && !AD_INPLACE ? MF : 1];
-    if constexpr (AD && !AD_INPLACE) {
+    // AdaLN: the few operand chunks are modulated in registers, after the
+    // next stage's loads are issued
+    u32x4 svl[AD ? U : 1], svh[AD ? U : 1];
+    if constexpr (AD) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        svl[u] = *reinterpret_cast<const u32x4*>(mod_ptr(s) + x_at(u, 0));
+        svh[u] = *reinterpret_cast<const u32x4*>(modh_ptr(s) + x_at(u, 0));
+      }
+    }
+    u32x4 xl[EX && LO ? U : 1][EX && LO ? MF : 1];   // the operand's remainder part
+    if constexpr (EX && LO) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int i = 0; i < MF; ++i) sv[u][i] = *reinterpret_cast<const u32x4*>(mod_ptr(s) + x_at(u, i));
+        for (int i = 0; i < MF; ++i) xl[u][i] = *reinterpret_cast<const u32x4*>(mod_ptr(s) + x_at(u, i));
     }
     __builtin_amdgcn_sched_barrier(0);
     issue_w((s + D) % NS, st + D);
     issue_x((s + D) % NS, st + D);
-    issue_t(s, st + NS);   // this slot's slice was last read before the previous barrier
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (TSL) {
-      modulate_own((s + 1) % NS);
-      __builtin_amdgcn_sched_barrier(0);
-    }
     // B operands: the bf16 fragments as loaded, or the two halves of each
     // fp8 fragment decoded exactly to bf16 (every E4M3 value is a bf16 value)
     u32x4 bw[U][NST];
@@ -409,10 +394,15 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < MF; ++i) {
-        u32x4 xa = xv[u][i];
-        if constexpr (AD && !AD_INPLACE) xa = modulate8(xa, sv[u][AD && !AD_INPLACE ? i : 0]);
+        u32x4 xa = xv[u][i], xb = {0u, 0u, 0u, 0u};
+        if constexpr (AD && LO) modulate8_split(xa, svl[AD ? u : 0], svh[AD ? u : 0], xa, xb);
+        else if constexpr (AD) xa = modulate8(xa, svl[AD ? u : 0], svh[AD ? u : 0]);
+        if constexpr (EX && LO) xb = xl[EX && LO ? u : 0][EX && LO ? i : 0];
 #pragma unroll
-        for (int c = 0; c < NST; ++c) acc[c][i] = mfma_chunk<__bf16>(xa, bw[u][c], acc[c][i]);
+        for (int c = 0; c < NST; ++c) {
+          acc[c][i] = mfma_chunk<__bf16>(xa, bw[u][c], acc[c][i]);
+          if constexpr (LO) acc[c][i] = mfma_chunk<__bf16>(xb, bw[u][c], acc[c][i]);
+        }
       }
     if constexpr (!EX) {
 #pragma unroll
@@ -420,23 +410,12 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     }
   };
 
-  // the loop's load order: W', x, then (TSL) the slice of the stage after;
-  // a stage's slice is published by the barrier before the one that
-  // modulates it -- stage 0's by the barrier below
-  issue_t(0, 0);
+  // the loop's load order: W', then x (and its modulation values)
 #pragma unroll
   for (int p = 0; p < D; ++p) {
     issue_w(p, p);
     issue_x(p, p);
-    issue_t(p + 1, p + 1);
     __builtin_amdgcn_sched_barrier(0);
-  }
-  if constexpr (TSL) {
-    // stage 0's loads and slice (and slice 1) have landed; once every
-    // wave's have, modulate stage 0
-    wait_vmcnt_x<(D - 1) * LPW>();
-    __builtin_amdgcn_s_barrier();
-    modulate_own(0);
   }
   // whole rounds of the ring; stages past the last read as zero
   for (int st = 0; st < a.stages; st += NS) {
@@ -569,11 +548,6 @@ struct DecodeXInstance {
   DecodeXInstance {                                                                                     \
     reinterpret_cast<const void*>(&decode_x_kernel<MF, NC, NWV, SW, U, F8, Q8>), MF, NC, NWV, U, SW, F8, Q8, NAME \
   }
-#define FN_DECODE_XA(MF, NWV, SW, U, NAME)                                                                      \
-  DecodeXInstance {                                                                                            \
-    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, SW, U, false, false, true>), MF, 1, NWV, U, SW, false, \
-        false, NAME                                                                                            \
-  }
 #define FN_DECODE_X(MF, NC, NWV, SW, U, NAME) FN_DECODE_XI(MF, NC, NWV, SW, U, false, false, NAME)
 #define FN_DECODE_X8(MF, NC, NWV, SW, U, NAME) FN_DECODE_XI(MF, NC, NWV, SW, U, true, false, NAME)
 
@@ -591,7 +565,7 @@ inline hipError_t launch_decode_x_instance(const DecodeXInstance& d, const void*
   a.su = su;
   a.q = q;
   a.qs = qs;
-  a.sc = ad ? ad->scale : nullptr;
+  a.mod = ad ? ad->mod : nullptr;
   a.idx = ad ? ad->idx : nullptr;
   a.bg = ad ? ad->bias_g : nullptr;
   a.bu = ad ? ad->bias_u : nullptr;
@@ -612,7 +586,6 @@ inline hipError_t launch_decode_x_instance(const DecodeXInstance& d, const void*
                          dim3(kWave * d.nwv), args, 0, stream);
 }
 
-#ifndef FN_DECODE_X_NO_TABLE
 // Measured on MI355X (cold weights): three one-column-block waves per
 // workgroup, two-k-block stages.  A skinny kernel is bounded by each CU's
 // vector-memory request rate, so what counts is the bytes each CU moves and
@@ -694,90 +667,71 @@ FusedPlan plan_fp8(int64_t M, int64_t K, int64_t N, bool swiglu) {
   return plan_of(find_instance(kDecodeF8, M <= 16 ? 1 : (M <= 32 ? 2 : 4), swiglu), 3, M, N);
 }
 
-// AdaLN prologue (bf16): rows up to 64 per workgroup, more tile over grid.y.
-// Measured on MI355X: 32 and 64 rows with tables of fewer than 24 rows
-// (three waves x 8 rows) stage the table's slice of each stage and modulate
-// a stage ahead (five ring slots keep three stages in flight); larger tables
-// one scale row per x row.  16 rows: one scale row per x row and the
-// operands modulated in registers, with five ring slots, was fastest.
-#define FN_DECODE_XT(MF, NWV, SW, U, NAME)                                                                       \
-  DecodeXInstance {                                                                                             \
-    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, SW, U, false, false, true, 5, true>), MF, 1, NWV, U, \
-        SW, false, false, NAME                                                                                  \
-  }
-constexpr int kAdTableSliceRows = 8 * 3 - 1;   // the last staged row stays zero (indices outside the table)
-static const DecodeXInstance kDecodeAdT[] = {
-    FN_DECODE_XT(2, 3, false, 2, "decode_adaln_bf16_m32_xlds_w3_u2_tab"),
-    FN_DECODE_XT(4, 3, false, 2, "decode_adaln_bf16_m64_xlds_w3_u2_tab"),
-    FN_DECODE_XT(2, 3, true, 2, "decode_swiglu_adaln_bf16_m32_xlds_w3_u2_tab"),
-    FN_DECODE_XT(4, 3, true, 2, "decode_swiglu_adaln_bf16_m64_xlds_w3_u2_tab"),
-};
+// AdaLN prologue (bf16), one launch, up to 16 rows: one modulation-table row
+// per x row, the operands modulated in registers; five ring slots measured
+// fastest.  SwiGLU takes the operand split in two parts (two MFMAs per
+// weight fragment, idle matrix cores in this HBM-bound kernel): the SiLU
+// times up of two rounded products has no margin left against the
+// tolerance at large sizes, the single-rounding projection does.
 #define FN_DECODE_XA5(NWV, SW, U, NAME)                                                                         \
   DecodeXInstance {                                                                                            \
-    reinterpret_cast<const void*>(&decode_x_kernel<1, 1, NWV, SW, U, false, false, true, 5>), 1, 1, NWV, U, SW, \
-        false, false, NAME                                                                                     \
+    reinterpret_cast<const void*>(&decode_x_kernel<1, 1, NWV, SW, U, false, false, true, 5, false, SW>), 1, 1, NWV, \
+        U, SW, false, false, NAME                                                                              \
   }
 static const DecodeXInstance kDecodeAd[] = {
     FN_DECODE_XA5(3, false, 2, "decode_adaln_bf16_m16_xlds_w3_u2_s5"),
-    FN_DECODE_XA(2, 3, false, 2, "decode_adaln_bf16_m32_xlds_w3_u2"),
-    FN_DECODE_XA(4, 3, false, 2, "decode_adaln_bf16_m64_xlds_w3_u2"),
-    FN_DECODE_XA5(3, true, 2, "decode_swiglu_adaln_bf16_m16_xlds_w3_u2_s5"),
-    FN_DECODE_XA(2, 3, true, 2, "decode_swiglu_adaln_bf16_m32_xlds_w3_u2"),
-    FN_DECODE_XA(4, 3, true, 2, "decode_swiglu_adaln_bf16_m64_xlds_w3_u2"),
+    FN_DECODE_XA5(3, true, 2, "decode_swiglu_adaln_split_bf16_m16_xlds_w3_u2_s5"),
 };
 
-static bool adaln_table_slice(int mf, int64_t T) { return mf > 1 && T <= kAdTableSliceRows; }
-
-FusedPlan plan_adaln(int64_t M, int64_t N, int64_t T, bool swiglu) {
-  const int mf = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  return plan_of(adaln_table_slice(mf, T) ? find_instance(kDecodeAdT, mf, swiglu) : find_instance(kDecodeAd, mf, swiglu),
-                 6, M, N);
+FusedPlan plan_adaln(int64_t M, int64_t N, bool swiglu) {
+  return plan_of(find_instance(kDecodeAd, 1, swiglu), 6, M, N);
 }
 
 hipError_t launch_adaln(const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y, int M, int K,
                         int N, float eps, const AdalnArgs& ad, hipStream_t stream) {
-  const DecodeXInstance* d = adaln_table_slice(p.mf, ad.T) ? find_instance(kDecodeAdT, p.mf, wu != nullptr)
-                                                             : find_instance(kDecodeAd, p.mf, wu != nullptr);
-  if (d == nullptr) return hipErrorInvalidValue;
+  const DecodeXInstance* d = find_instance(kDecodeAd, p.mf, wu != nullptr);
+  if (d == nullptr || M > 16) return hipErrorInvalidValue;
   return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream, nullptr, nullptr, nullptr, nullptr, &ad);
 }
 
 // Two-launch AdaLN, 17..64 rows: the plain 32- and 64-row rungs on the
 // operand the pre-pass modulated, 1/RMS from the pre-pass, bias rows added in
 // the epilogue (no Gram blocks).
+// SwiGLU: the split operand (LO).
 #define FN_DECODE_XE(MF, SW, NS, NAME)                                                                          \
   DecodeXInstance {                                                                                            \
-    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, 3, SW, 2, false, false, false, NS, false, true>), MF, 1, \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, 3, SW, 2, false, false, false, NS, true, SW>), MF, 1, \
         3, 2, SW, false, false, NAME                                                                           \
   }
 static const DecodeXInstance kDecodeEx[] = {
     FN_DECODE_XE(2, false, 5, "decode_premod_bf16_m32_xlds_w3_u2_s5"),
     FN_DECODE_XE(4, false, 5, "decode_premod_bf16_m64_xlds_w3_u2_s5"),
-    FN_DECODE_XE(2, true, 4, "decode_swiglu_premod_bf16_m32_xlds_w3_u2"),
-    FN_DECODE_XE(4, true, 4, "decode_swiglu_premod_bf16_m64_xlds_w3_u2"),
+    FN_DECODE_XE(2, true, 4, "decode_swiglu_premod_split_bf16_m32_xlds_w3_u2"),
+    FN_DECODE_XE(4, true, 4, "decode_swiglu_premod_split_bf16_m64_xlds_w3_u2"),
 };
 
 // fp8 weights: the fp8 rungs above on the pre-modulated operand (every M;
-// past 64 rows the 64-row tiles repeat over grid.y).
+// past 64 rows the 64-row tiles repeat over grid.y); SwiGLU on the split
+// operand.
 #define FN_DECODE_X8E(MF, NWV, SW, U, NAME)                                                                      \
   DecodeXInstance {                                                                                             \
-    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, SW, U, true, false, false, 4, false, true>), MF, 1, \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, SW, U, true, false, false, 4, true, SW>), MF, 1, \
         NWV, U, SW, true, false, NAME                                                                           \
   }
 static const DecodeXInstance kDecodeF8Ex[] = {
     FN_DECODE_X8E(1, 3, false, 8, "decode_fp8_premod_m16_xlds_w3_u8"),
     FN_DECODE_X8E(2, 3, false, 4, "decode_fp8_premod_m32_xlds_w3_u4"),
     FN_DECODE_X8E(4, 3, false, 2, "decode_fp8_premod_m64_xlds_w3_u2"),
-    FN_DECODE_X8E(1, 3, true, 4, "decode_swiglu_fp8_premod_m16_xlds_w3_u4"),
-    FN_DECODE_X8E(2, 3, true, 4, "decode_swiglu_fp8_premod_m32_xlds_w3_u4"),
-    FN_DECODE_X8E(4, 4, true, 2, "decode_swiglu_fp8_premod_m64_xlds_w4_u2"),
+    FN_DECODE_X8E(1, 3, true, 4, "decode_swiglu_fp8_premod_split_m16_xlds_w3_u4"),
+    FN_DECODE_X8E(2, 3, true, 4, "decode_swiglu_fp8_premod_split_m32_xlds_w3_u4"),
+    FN_DECODE_X8E(4, 4, true, 2, "decode_swiglu_fp8_premod_split_m64_xlds_w4_u2"),
 };
 
 // SwiGLU with fp8 output on the pre-modulated operand: the q8 rungs above
 // (bf16 weights up to 64 rows; fp8 weights every M).
 #define FN_DECODE_XQE(MF, NWV, U, F8, NAME)                                                                     \
   DecodeXInstance {                                                                                            \
-    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, true, U, F8, true, false, 4, false, true>), MF, 1, \
+    reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, true, U, F8, true, false, 4, true>), MF, 1,     \
         NWV, U, true, F8, true, NAME                                                                           \
   }
 static const DecodeXInstance kDecodeQ8Ex[] = {
@@ -848,6 +802,4 @@ hipError_t launch_fp8(const FusedPlan& p, const void* x, const void* wg, const f
   if (d == nullptr) return hipErrorInvalidValue;
   return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream, sg, su);
 }
-#endif
-
 }  // namespace fn

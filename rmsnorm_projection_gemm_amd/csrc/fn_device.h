@@ -99,23 +99,41 @@ template <> __device__ inline f32x4 mfma_chunk<float>(u32x4 a, u32x4 b, f32x4 ac
   return acc;
 }
 
+// AdaLN-modulated MFMA operand: the 8 bf16 values of a 16-byte chunk times
+// their 8 fp32 modulation values (the first four in mlo, the second four in
+// mhi), each product rounded to fp32 and then RNE to bf16.
+__device__ inline u32x4 modulate8(u32x4 x, u32x4 mlo, u32x4 mhi) {
+  u32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 m = c < 2 ? mlo : mhi;   // values 2c and 2c+1
+    const int j = 2 * (c & 1);
+    r[c] = pack_bf16x2(bf16_lo(x[c]) * __uint_as_float(m[j]), bf16_hi(x[c]) * __uint_as_float(m[j + 1]));
+  }
+  return r;
+}
+
+// The same operand split exactly into two bf16 parts: p = fp32(x * m),
+// hi = RNE_bf16(p), lo = RNE_bf16(p - hi) (p - hi is exact in fp32), so
+// hi + lo carries p to about 16 significant bits and two MFMAs against the
+// same weights give the product of the unrounded operand.
+__device__ inline void modulate8_split(u32x4 x, u32x4 mlo, u32x4 mhi, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 m = c < 2 ? mlo : mhi;   // values 2c and 2c+1
+    const int j = 2 * (c & 1);
+    const float p0 = bf16_lo(x[c]) * __uint_as_float(m[j]), p1 = bf16_hi(x[c]) * __uint_as_float(m[j + 1]);
+    const uint32_t h = pack_bf16x2(p0, p1);
+    hi[c] = h;
+    lo[c] = pack_bf16x2(p0 - bf16_lo(h), p1 - bf16_hi(h));
+  }
+}
+
 // silu(a) * b = a / (1 + e^-a) * b, with the hardware exp2 and reciprocal
 // (v_exp_f32, v_rcp_f32: about 1 ulp each) instead of the libm-accurate
 // expf and a correctly rounded division -- a few fp32 ulps, far below the
 // bf16 (or E4M3) rounding that follows, for a fraction of the instructions.
 // Large negative a: e^-a overflows to inf, rcp(inf) = 0, result -0 or 0.
-// x * (1 + s) for the 8 bf16 values of a 16-byte chunk: fp32 x + x*s (one
-// rounding), then RNE to bf16 -- the AdaLN-modulated MFMA operand.
-__device__ inline u32x4 modulate8(u32x4 x, u32x4 s) {
-  u32x4 r;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float x0 = bf16_lo(x[c]), x1 = bf16_hi(x[c]);
-    r[c] = pack_bf16x2(fmaf(x0, bf16_lo(s[c]), x0), fmaf(x1, bf16_hi(s[c]), x1));
-  }
-  return r;
-}
-
 __device__ inline float silu_times(float a, float b) {
   const float e = __builtin_amdgcn_exp2f(a * -1.44269504088896341f);
   return a * __builtin_amdgcn_rcpf(1.0f + e) * b;

@@ -16,7 +16,7 @@ struct FusedPlan {
   int kind;           // 0 = decode (<= 16 rows, or fp32), 1 = prefill (tiled), 2 = decode with x in LDS,
                       // 3 = fp8 weights (x in LDS, rows tiled over grid.y),
                       // 4 = SwiGLU with fp8 output (x in LDS), 5 = the same on the prefill kernel,
-                      // 6 = AdaLN prologue (x and scale rows in LDS), 7 = AdaLN on the prefill kernel,
+                      // 6 = AdaLN prologue (x and modulation rows in LDS, up to 16 rows),
                       // 8 = prefill on an operand modulated by the AdaLN pre-pass,
                       // 9 = the same on the LDS-shared-x decode kernel, 10 = the same with fp8 output,
                       // 11 = the prefill kernel with fp8 weights
@@ -40,10 +40,11 @@ hipError_t launch_decode_x(DType dt, const FusedPlan& plan, const void* x, const
                            hipStream_t stream);
 
 // AdaLN prologue: h = RMSNorm_g(x) * (1 + scale[idx]) + shift[idx] before
-// the projection; the gain is folded into W', the shift enters as bias rows
-// shift @ W ([T, N], fp32).
+// the projection; the gain is folded into the modulation table
+// mod = g * (1 + scale) ([T, K], fp32), the weights are the plain W, and the
+// shift enters as bias rows shift @ W ([T, N], fp32).
 struct AdalnArgs {
-  const void* scale;     // [T, K] bf16
+  const float* mod;      // [T, K] fp32
   const int* idx;        // [M] table row of each x row
   const float* bias_g;   // [T, N]
   const float* bias_u;   // [T, N], SwiGLU only
@@ -51,26 +52,29 @@ struct AdalnArgs {
 };
 
 // q8: SwiGLU with fp8 output (codes q, row-block scales qs; y unused).
-// ad: AdaLN prologue (tables of at most 63 rows, prefill_adaln_fits).
 // ex: the prefill kernel on an operand the AdaLN pre-pass modulated (1/RMS
 // per row from the pre-pass, bias rows in the epilogue).
 // f8: fp8 (E4M3) weights with column scales (launch_prefill_fp8, or
 // launch_prefill_premod with scales).
-FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8 = false, bool ad = false,
-                       bool ex = false, bool f8 = false);
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8 = false, bool ex = false,
+                       bool f8 = false);
 hipError_t launch_prefill_fp8(const FusedPlan& plan, const void* x, const void* wg, const float* sg, const void* wu,
                               const float* su, void* y, int M, int K, int N, float eps, hipStream_t stream,
                               uint8_t* q = nullptr, float* qs = nullptr);
 hipError_t launch_prefill(DType dt, const FusedPlan& plan, const void* x, const void* w_gate,
                           const void* w_up, void* y, int M, int K, int N, float eps,
-                          hipStream_t stream, uint8_t* q = nullptr, float* qs = nullptr,
-                          const AdalnArgs* ad = nullptr);
-bool prefill_adaln_fits(int64_t T);
-// Two-launch AdaLN: the pre-pass writes u = bf16(x + x * scale[idx]) [M,K]
-// and rs = 1/RMS(x) [M]; the prefill kernel then runs on u (plan from
-// plan_prefill(..., ex = true); ad.scale unused).
-hipError_t launch_adaln_modulate(const void* x, const void* scale, const int* idx, int T, void* u, float* rs, int M,
-                                 int K, float eps, hipStream_t stream);
+                          hipStream_t stream, uint8_t* q = nullptr, float* qs = nullptr);
+// Two-launch AdaLN: the pre-pass writes u = bf16(fp32(x * mod[idx])) [M,K]
+// (a zero row for an index outside the table) and rs = 1/RMS(x) [M]; the
+// projection kernel then runs on u (plan from plan_prefill(..., ex = true)
+// or plan_decode_premod; ad.mod unused).
+// split: u is [2M, K], row 2m the bf16 operand (hi) and row 2m+1 its
+// rounding remainder (lo), for the SwiGLU projections.
+hipError_t launch_adaln_modulate(const void* x, const float* mod, const int* idx, int T, void* u, float* rs, int M,
+                                 int K, float eps, hipStream_t stream, bool split = false);
+// Offline: mod[t][k] = fp32(g[k] * (1 + scale[t][k])) computed in fp64.
+hipError_t launch_adaln_fold_table(DType dt, const void* g, const void* scale, float* mod, int T, int K,
+                                   hipStream_t stream);
 // q, qs: SwiGLU with fp8 row-block output (y unused); sg, su: fp8 weights.
 hipError_t launch_prefill_premod(const FusedPlan& plan, const void* u, const float* rs, const void* wg,
                                  const void* wu, void* y, int M, int K, int N, const AdalnArgs& ad,
@@ -107,7 +111,8 @@ hipError_t launch_decode_q8(bool f8_weights, const FusedPlan& plan, const void* 
                             const float* sg, const void* wu, const float* su, uint8_t* q, float* qs,
                             int M, int K, int N, float eps, hipStream_t stream);
 
-FusedPlan plan_adaln(int64_t M, int64_t N, int64_t T, bool swiglu);
+// One-launch AdaLN, up to 16 rows.
+FusedPlan plan_adaln(int64_t M, int64_t N, bool swiglu);
 hipError_t launch_adaln(const FusedPlan& plan, const void* x, const void* wg, const void* wu, void* y, int M,
                         int K, int N, float eps, const AdalnArgs& ad, hipStream_t stream);
 // Measurement probes (a streaming read, an MFMA-only loop).

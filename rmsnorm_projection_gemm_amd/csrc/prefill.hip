@@ -9,7 +9,7 @@
 // four waves of 128x128 (one per SIMD) ran 1.8x slower, nothing covering one
 // wave's barrier and memory latency.
 //
-// Schedule (without AdaLN): ping-pong.  Waves 0-3 (one per SIMD) and waves
+// Schedule: ping-pong.  Waves 0-3 (one per SIMD) and waves
 // 4-7 alternate between a compute slot -- the k-block's MFMAs, operands
 // already in registers -- and a memory slot -- LDS reads of the wave's next
 // k-block into registers, its share of the global-to-LDS loads, the waits --
@@ -18,8 +18,7 @@
 // faster than interleaving loads and MFMAs in every wave; without the
 // global loads the same loop runs at the MFMA-only time, so the L2-to-CU
 // delivery of the operands, about 32 KiB per k-block per CU, is what bounds
-// it).  The AdaLN instances keep an interleaved schedule in every wave: their
-// x pair is modulated in LDS by the waves that loaded it before a barrier.
+// it).
 //
 // Operands stream through LDS rings filled by direct global-to-LDS buffer
 // loads (no register staging): W' one 32-wide k-block per slot (4 slots),
@@ -59,11 +58,10 @@ struct PrefillArgs {
   float eps;
   uint8_t* q;        // fp8 output: E4M3 codes [M, N] (y unused)
   float* qs;         // fp8 output: scales [M, nblocks], one per 16-column row block
-  const void* sc;    // AdaLN: scale table [T, K] (bf16), T < 8 * waves
-  const int* idx;    // AdaLN: table row of each x row [M]
-  const float* bg;   // AdaLN: bias rows [T, N] (gate for SwiGLU)
-  const float* bu;   // AdaLN: bias rows of W_up
-  int T;
+  const int* idx;    // EX: AdaLN table row of each x row [M]
+  const float* bg;   // EX: AdaLN bias rows [T, N] (gate for SwiGLU)
+  const float* bu;   // EX: AdaLN bias rows of W_up
+  int T;             // EX: AdaLN table rows
   const float* rs;   // EX: 1/RMS of each row [M], from the AdaLN pre-pass
   const float* sg;   // F8: column scales of wg [N]
   const float* su;   // F8: column scales of wu [N]
@@ -86,18 +84,17 @@ __device__ inline void wait_vmcnt() {
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// AD: AdaLN.  The whole scale table's slice of each x pair is staged (one
-// load per wave: table rows 8*wave .. +7, so T < 8 * waves), one pair ahead
-// of the x pair it serves, so that a barrier has published every wave's part
-// of it before it is read.  Each wave modulates the x chunks it loaded itself
-// in place, x + x * scale[idx] rounded to bf16, before the pair's barrier,
-// and takes the sums of squares of the raw values on the way (the Gram
-// blocks would see modulated x); the epilogue adds the row's bias rows.
-//
 // EX: the projection half of the two-launch AdaLN form.  x is the operand
 // the pre-pass already modulated, 1/RMS of each raw row comes from a.rs (no
-// Gram blocks), and the epilogue adds the row's bias rows; the loop is the
-// ping-pong one of the plain instances.
+// Gram blocks), and the epilogue adds the row's bias rows (zero for an
+// index outside the table, whose operand row the pre-pass zeroed).
+//
+// PAIR (with EX, bf16 output): the operand arrives split in two bf16 parts,
+// row 2m the rounded operand of x row m and row 2m+1 its remainder, and the
+// kernel runs over the 2M operand rows (a.M = 2M).  A lane's accumulator
+// holds 4 consecutive rows, so each pair meets in registers and the
+// epilogue adds the two products before the scale, the bias and the
+// SwiGLU: the product of the unrounded operand at twice the matrix work.
 //
 // F8: fp8 (E4M3) weights with one scale per output column, packed in 1 KiB
 // fragments of 16 columns x 64 k (a pair of k-blocks, the lane's 16 bytes
@@ -107,7 +104,7 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // (v_cvt_scalef32_pk_bf16_fp8 with scale 1 is exact).  Per k-block a CU
 // moves 24 KiB of operands instead of 32 and its waves read 64 KiB of LDS
 // instead of 96; the column scale joins 1/RMS in the epilogue.
-template <int FM, int FN, int WM, int WN, bool SW, bool Q8, bool AD = false, bool EX = false, bool F8 = false>
+template <int FM, int FN, int WM, int WN, bool SW, bool Q8, bool EX = false, bool F8 = false, bool PAIR = false>
 __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = SW ? 2 : 1;
@@ -121,14 +118,10 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   static_assert(WFR % NW == 0 && XFR % NW == 0 && FM % WN == 0, "tile shape");
   constexpr int WSLOT = WFR * kFragBytes;
   constexpr int XSLOT = XFR * kFragBytes;
-  constexpr int TSLOT = AD ? NW * kFragBytes : 16;   // AdaLN table slice of a pair: 8 rows per wave
-  constexpr int LXP = XPW + (AD ? 1 : 0);             // loads per wave per pair (x, table)
-  static_assert(4 * WSLOT + 2 * XSLOT + 2 * TSLOT + BMF * 64 <= 160 * 1024, "LDS budget");
-  static_assert(!AD || !Q8, "AdaLN with bf16 output");
-  static_assert(AD || NW == 8, "ping-pong: two groups of one wave per SIMD");
-  static_assert(!EX || !AD, "pre-modulated operand: ping-pong loop");
-  static_assert(!F8 || !AD, "fp8 weights: ping-pong loop");
-  constexpr bool BIAS = AD || EX;
+  static_assert(4 * WSLOT + 2 * XSLOT + BMF * 64 <= 160 * 1024, "LDS budget");
+  static_assert(NW == 8, "ping-pong: two groups of one wave per SIMD");
+  static_assert(!PAIR || (EX && !Q8), "split operand: the two-launch AdaLN form, bf16 output");
+  constexpr bool BIAS = EX;
 
   __shared__ __attribute__((aligned(1024))) uint8_t wring0[WSLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t wring1[WSLOT];
@@ -136,14 +129,11 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   __shared__ __attribute__((aligned(1024))) uint8_t wring3[WSLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t xring0[XSLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t xring1[XSLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t tring0[TSLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t tring1[TSLOT];
   __shared__ __attribute__((aligned(16))) float ssbuf[BMF * 16];   // sums of squares, then 1/RMS
   auto wslot = [&](int s) __attribute__((always_inline)) -> uint8_t* {
     return s == 0 ? wring0 : (s == 1 ? wring1 : (s == 2 ? wring2 : wring3));
   };
   auto xslot = [&](int s) __attribute__((always_inline)) -> uint8_t* { return s == 0 ? xring0 : xring1; };
-  auto tslot = [&](int s) __attribute__((always_inline)) -> uint8_t* { return s == 0 ? tring0 : tring1; };
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -196,56 +186,12 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   const int xk = (x_c >> 2) * 32 + (x_c & 3) * 8;
   const uint32_t xoff0 = (uint32_t)((16 * (wave >> 1) + x_lr) * a.K + xk) * 2u;
   const uint32_t xstride = (uint32_t)(16 * NW) * (uint32_t)a.K;   // bytes between loads j and j+1
-  // AdaLN: the table row of each x row this lane loads, and its chunk's
-  // place in the staged table slice (row t at t*128, chunk c at c*16)
-  int toff[AD ? XPW : 1];
-  float ssx[AD ? XPW : 1];
-  __amdgpu_buffer_rsrc_t tr = xr;
-  uint32_t tload = kOutOfRange;
-  if constexpr (AD) {
-#pragma unroll
-    for (int j = 0; j < XPW; ++j) {
-      const int row = m0 + 16 * ((wave >> 1) + (NW / 2) * j) + x_lr;
-      const int t = row < a.M ? a.idx[row] : -1;
-      // an index outside the table reads the last staged row, always zero
-      // (T < 8 * waves)
-      toff[j] = ((unsigned)t < (unsigned)a.T ? t : 8 * NW - 1) * 128 + x_c * 16;
-      ssx[j] = 0.f;
-    }
-    tr = make_rsrc(a.sc, (int64_t)a.T * a.K * 2);
-    const int trow = 8 * wave + (lane >> 3);
-    tload = trow < a.T ? (uint32_t)(trow * a.K + (lane & 7) * 8) * 2u : kOutOfRange;
-  }
-  auto issue_t = [&](uint8_t* base, int p) __attribute__((always_inline)) {
-    const uint32_t in = (uint32_t)((p * 64 + (lane & 7) * 8 - a.K) >> 31) & (tload == kOutOfRange ? 0u : ~0u);
-    const uint32_t off = ((tload + (uint32_t)p * 128u) & in) | (kOutOfRange & ~in);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, (lds_ptr)(base + wave * kFragBytes), 16, off, 0, 0, 0);
-  };
-  // modulate this wave's own chunks of a landed pair in place; sums of
-  // squares of the raw values
-  auto modulate_pair = [&](uint8_t* xb, const uint8_t* tb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < XPW; ++j) {
-      u32x4* xp = reinterpret_cast<u32x4*>(xb + (wave + NW * j) * kFragBytes + lane * 16);
-      const u32x4 xv = *xp;
-      float s2 = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float x0 = bf16_lo(xv[c]), x1 = bf16_hi(xv[c]);
-        s2 = fmaf(x0, x0, s2);
-        s2 = fmaf(x1, x1, s2);
-      }
-      ssx[j] += s2;
-      *xp = modulate8(xv, *reinterpret_cast<const u32x4*>(tb + toff[j]));
-    }
-  };
   auto issue_x = [&](uint8_t* base, int p) __attribute__((always_inline)) {
     const int k0 = p * 64;
     const uint32_t in = (uint32_t)((k0 + xk - a.K) >> 31);   // all ones while k < K
     // opaque to the optimiser: otherwise the XPW loop-invariant sums
-    // xoff0 + j * xstride are hoisted out of the k loop into registers that
-    // the AdaLN instances cannot spare (a spilled offset's reload waits for
-    // every DMA load in flight)
+    // xoff0 + j * xstride are hoisted out of the k loop into registers (a
+    // spilled offset's reload would wait for every DMA load in flight)
     uint32_t xb = xoff0 + (uint32_t)k0 * 2u;
     asm volatile("" : "+v"(xb));
 #pragma unroll
@@ -427,7 +373,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
         stepA(std::integral_constant<int, 3>{}, s + 3);
       }
     }
-  } else if constexpr (!AD) {
+  } else {
     // Ping-pong.  k-block s: group A (waves 0-3) reads it in slot 2s-1 and
     // computes it in slot 2s; group B (waves 4-7) reads it in slot 2s and
     // computes it in slot 2s+1.  A memory slot also issues the wave's share
@@ -514,111 +460,11 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
         stepA(std::integral_constant<int, 3>{}, s + 3);
       }
     }
-  } else {
-    // AdaLN: every wave interleaves.  k-block t = t0 + T4 (T4 = t % 4, a
-    // compile-time constant): W' slot T4, x pair slot T4 / 2; k-block t+1's
-    // operands come from W' slot (T4+1) % 4 and x pair slot ((T4+1) % 4) / 2,
-    // half (T4+1) % 2.  One register set for the x operands: row fragment i
-    // of k-block t+1 is read as soon as row i of t is consumed (this keeps
-    // the instance within 256 registers without spills).
-    auto step = [&](auto T4c, int t) __attribute__((always_inline)) {
-      constexpr int T4 = decltype(T4c)::value;
-      constexpr bool odd = (T4 % 2) == 1;
-      const uint8_t* wcur = wslot(T4);
-      const uint8_t* wnext = wslot((T4 + 1) % 4);
-      const uint8_t* xnext = xslot(((T4 + 1) % 4) / 2);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_cols(0, NB / 2);
-      read_b(NB / 2, NB, wcur);
-#pragma unroll
-      for (int g = 0; g < NB / 2; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);       // FM MFMAs
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // k-block t+1's x pair and W' have landed for this wave once at most
-      // the loads issued after the newer of the two are in flight; the
-      // barrier extends that to every wave and retires every read of slot t.
-      lgkm0();
-      if constexpr (odd) wait_vmcnt<2 * WPW + 1>();
-      else wait_vmcnt<2 * WPW + LXP>();
-      if constexpr (odd) {
-        // k-block t+1 opens the next pair: modulate this wave's part of it
-        modulate_pair(xslot(((T4 + 1) % 4) / 2), tslot(((T4 + 1) % 4) / 2));
-        lgkm0();
-      }
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = NB / 2; j < NB; ++j)
-          acc[j / FN][i][j % FN] = mfma_chunk<__bf16>(av[i], bv[j], acc[j / FN][i][j % FN]);
-        av[i] = *reinterpret_cast<const u32x4*>(xnext + x_at((T4 + 1) % 2, wm * FM + i));
-      }
-      read_b(0, NB / 2, wnext);
-      if constexpr (odd) issue_x(xslot(T4 / 2), (t + 3) / 2);
-      if constexpr (odd) issue_t(tslot(T4 == 1 ? 1 : 0), (t + 5) / 2);   // one pair ahead
-      issue_w(wslot(T4), t + 4);
-#pragma unroll
-      for (int g = 0; g < FM; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, NB / 2, 0);   // row g's MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // row g's next fragment
-      }
-#pragma unroll
-      for (int g = 0; g < WPW + (odd ? LXP : 0); ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);        // one global-to-LDS load
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        // two MFMAs
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // table slices 0 and 1 first; pair 0 is modulated once table 0 has
-    // landed for every wave, and table 2 reuses its slot only after a
-    // barrier behind every wave's modulation
-    issue_t(tring0, 0);
-    issue_w(wring0, 0);
-    issue_x(xring0, 0);
-    issue_t(tring1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<1>();
-    __builtin_amdgcn_s_barrier();
-    modulate_pair(xring0, tring0);
-    lgkm0();
-    // every wave has read table slice 0 before any wave's slice 2 replaces it
-    __builtin_amdgcn_s_barrier();
-    issue_w(wring1, 1);
-    issue_w(wring2, 2);
-    issue_x(xring1, 1);
-    issue_t(tring0, 2);
-    issue_w(wring3, 3);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    read_a(xring0, 0);
-    read_b(0, NB / 2, wring0);
-    for (int t = 0; t < a.kblocks; t += 4) {
-      step(std::integral_constant<int, 0>{}, t);
-      step(std::integral_constant<int, 1>{}, t + 1);
-      step(std::integral_constant<int, 2>{}, t + 2);
-      step(std::integral_constant<int, 3>{}, t + 3);
-    }
   }
   wait_vmcnt<0>();   // retire the zero-filled loads issued past the last k-block
 
-  if constexpr (AD) {
-    // the 8 lanes l/8 == r of each own load hold row r's 8 chunks: reduce
-    // over lane bits 0..2
 #pragma unroll
-    for (int j = 0; j < XPW; ++j) {
-      float v = ssx[j];
-      v += dpp_move<0xB1>(v);     // lane ^ 1
-      v += dpp_move<0x4E>(v);     // lane ^ 2
-      v += dpp_move<0x141>(v);    // mirror within 8 lanes
-      const int q = wave + NW * j;
-      if ((lane & 7) == 0) ssbuf[16 * (q >> 1) + 8 * (q & 1) + (lane >> 3)] = v;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < (AD || EX ? 0 : SSF); ++i) {
+  for (int i = 0; i < (EX ? 0 : SSF); ++i) {
     if ((lrow >> 2) == lgrp) {
       const int e = lrow & 3;
       const f32x4 gv = gram[i];
@@ -630,7 +476,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   if (threadIdx.x < BMF * 16) {
     if constexpr (EX) {
       const int row = m0 + (int)threadIdx.x;
-      ssbuf[threadIdx.x] = row < a.M ? a.rs[row] : 0.f;
+      ssbuf[threadIdx.x] = row < a.M ? a.rs[PAIR ? row >> 1 : row] : 0.f;
     } else {
       ssbuf[threadIdx.x] = inv_rms(ssbuf[threadIdx.x], (float)a.K, a.eps);
     }
@@ -649,7 +495,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&ssbuf[(wm * FM + i) * 16 + 4 * lgrp]);
-    // AdaLN: the bias values of this row fragment's outputs, all fetched
+    // EX: the AdaLN bias values of this row fragment's outputs, all fetched
     // before its first store (the loads then overlap instead of each waiting
     // behind the previous store); where the index is outside the table or
     // the output outside the matrix a valid element is read and dropped, so
@@ -658,7 +504,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = m0 + (wm * FM + i) * 16 + 4 * lgrp + r;
-      const int trow = BIAS && row < a.M ? a.idx[row] : -1;
+      const int trow = BIAS && row < a.M ? a.idx[PAIR ? row >> 1 : row] : -1;
       const bool tv = BIAS && (unsigned)trow < (unsigned)a.T;
       const size_t tb = (size_t)(tv ? trow : 0) * a.N;
 #pragma unroll
@@ -673,10 +519,15 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
       }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 4; r += (PAIR ? 2 : 1)) {
       const int rl = (wm * FM + i) * 16 + 4 * lgrp + r;   // row within the tile
       const int row = m0 + rl;
       const float inv = inv4[r];
+      // PAIR: operand rows r and r+1 are one output row's two parts
+      auto prod = [&](int m, int j) __attribute__((always_inline)) -> float {
+        if constexpr (PAIR) return acc[m][i][j][r] + acc[m][i][j][r + 1];
+        else return acc[m][i][j][r];
+      };
       if constexpr (Q8) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -690,14 +541,14 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
                    a.qs + (size_t)row * a.nblocks + nb);
         }
       } else if (row < a.M) {
-        __bf16* yrow = static_cast<__bf16*>(a.y) + (size_t)row * a.N;
+        __bf16* yrow = static_cast<__bf16*>(a.y) + (size_t)(PAIR ? row >> 1 : row) * a.N;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = (nb0 + wn * FN + j) * 16 + lrow;
           if (col < a.N) {
             const float i0 = F8 ? inv * csc[0][j] : inv, i1 = F8 ? inv * csc[NMAT - 1][j] : inv;
-            const float ga = acc[0][i][j][r] * i0 + bias[0][r][j];
-            const float ua = acc[NMAT - 1][i][j][r] * i1 + bias[NMAT - 1][r][j];
+            const float ga = prod(0, j) * i0 + bias[0][r][j];
+            const float ua = prod(NMAT - 1, j) * i1 + bias[NMAT - 1][r][j];
             const float v = SW ? silu_times(ga, ua) : ga;
             Store<__bf16>::one(yrow + col, v);
           }
@@ -710,86 +561,77 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
 struct PrefillInstance {
   const void* fn;
   int fm, fn_, wm, wn, ns;
-  bool sw, q8, ad, ex, f8;
+  bool sw, q8, ex, f8, pair;
   const char* name;
 };
 
-#define FN_PREFILL(FM, FN_, WM, WN, SW, Q8, AD, EX, F8, NAME)                                                 \
+#define FN_PREFILL(FM, FN_, WM, WN, SW, Q8, EX, F8, NAME)                                                   \
   PrefillInstance {                                                                                          \
-    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, Q8, AD, EX, F8>), FM, FN_, WM, WN, 4, SW, \
-        Q8, AD, EX, F8, NAME                                                                                 \
+    reinterpret_cast<const void*>(&prefill_kernel<FM, FN_, WM, WN, SW, Q8, EX, F8>), FM, FN_, WM, WN, 4, SW, Q8, \
+        EX, F8, false, NAME                                                                                  \
+  }
+// the two-launch AdaLN SwiGLU on the split operand (bf16 output)
+#define FN_PREFILL_PAIR(F8, NAME)                                                                            \
+  PrefillInstance {                                                                                          \
+    reinterpret_cast<const void*>(&prefill_kernel<4, 4, 4, 2, true, false, true, F8, true>), 4, 4, 4, 2, 4, true, \
+        false, true, F8, true, NAME                                                                          \
   }
 
 static const PrefillInstance kPrefill[] = {
-    FN_PREFILL(4, 8, 4, 2, false, false, false, false, false, "prefill_bf16_256x256_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, false, false, "prefill_bf16_256x256_w4x2_xl"),
     // narrow projections (one GPU's column share under tensor parallelism):
     // fewer than 128 tiles of 256 x 256 leave most CUs idle; 256 x 128 tiles
     // double the count (1536 columns x 4096 rows: 81.3 -> 57.9 us, same bits)
-    FN_PREFILL(4, 4, 4, 2, false, false, false, false, false, "prefill_bf16_256x128_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, false, false, false, false, "prefill_swiglu_bf16_256x128_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, true, false, false, false, "prefill_swiglu_bf16_q8_256x128_w4x2_xl"),
-    FN_PREFILL(4, 8, 4, 2, false, false, true, false, false, "prefill_adaln_bf16_256x256_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, false, true, false, false, "prefill_swiglu_adaln_bf16_256x128_w4x2_xl"),
-    FN_PREFILL(4, 8, 4, 2, false, false, false, true, false, "prefill_premod_bf16_256x256_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, false, false, true, false, "prefill_swiglu_premod_bf16_256x128_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, true, false, true, false, "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, false, false, false, false, "prefill_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, false, false, false, "prefill_swiglu_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, false, false, "prefill_swiglu_bf16_q8_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, true, false, "prefill_premod_bf16_256x256_w4x2_xl"),
+    FN_PREFILL_PAIR(false, "prefill_swiglu_premod_split_bf16_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, true, false, "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"),
     // fp8 (E4M3) weights with column scales
-    FN_PREFILL(4, 8, 4, 2, false, false, false, false, true, "prefill_fp8_256x256_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, false, false, false, false, true, "prefill_fp8_256x128_w4x2_xl"),   // narrow
-    FN_PREFILL(4, 4, 4, 2, true, false, false, false, true, "prefill_swiglu_fp8_256x128_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, true, false, false, true, "prefill_swiglu_fp8_q8_256x128_w4x2_xl"),
-    FN_PREFILL(4, 8, 4, 2, false, false, false, true, true, "prefill_fp8_premod_256x256_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, false, false, true, true, "prefill_swiglu_fp8_premod_256x128_w4x2_xl"),
-    FN_PREFILL(4, 4, 4, 2, true, true, false, true, true, "prefill_swiglu_fp8_q8_premod_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, false, true, "prefill_fp8_256x256_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, false, false, false, true, "prefill_fp8_256x128_w4x2_xl"),   // narrow
+    FN_PREFILL(4, 4, 4, 2, true, false, false, true, "prefill_swiglu_fp8_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, false, true, "prefill_swiglu_fp8_q8_256x128_w4x2_xl"),
+    FN_PREFILL(4, 8, 4, 2, false, false, true, true, "prefill_fp8_premod_256x256_w4x2_xl"),
+    FN_PREFILL_PAIR(true, "prefill_swiglu_fp8_premod_split_256x128_w4x2_xl"),
+    FN_PREFILL(4, 4, 4, 2, true, true, true, true, "prefill_swiglu_fp8_q8_premod_256x128_w4x2_xl"),
 };
 
 // The first instance with exactly these flags (q8 implies SwiGLU) and, when
 // nf is given, 16-column fragments per tile; the plain projection when none
 // matches.
-static const PrefillInstance& pick(bool sw, bool q8 = false, bool ad = false, bool ex = false, bool f8 = false,
-                                   int nf = 0) {
+static const PrefillInstance& pick(bool sw, bool q8 = false, bool ex = false, bool f8 = false, int nf = 0) {
   for (const PrefillInstance& d : kPrefill)
-    if (d.sw == (sw || q8) && d.q8 == q8 && d.ad == ad && d.ex == ex && d.f8 == f8 &&
+    if (d.sw == (sw || q8) && d.q8 == q8 && d.ex == ex && d.f8 == f8 &&
         (nf == 0 || d.fn_ * d.wn == nf))
       return d;
   return kPrefill[0];
 }
 
-// Largest AdaLN table the prefill kernel stages whole (8 rows per wave, the
-// last staged row kept zero for indices outside the table).
-constexpr int kPrefillAdalnMaxT = 8 * 8 - 1;
-bool prefill_adaln_fits(int64_t T) { return T >= 1 && T <= kPrefillAdalnMaxT; }
-
-FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8, bool ad, bool ex, bool f8) {
+FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8, bool ex, bool f8) {
   (void)dt;
   (void)K;
-  const bool plain = !swiglu && !q8 && !ad && !ex;
+  const bool plain = !swiglu && !q8 && !ex;
   const bool narrow = plain && ceil_div(N, 256) * ceil_div(M, 256) < 128;
-  const PrefillInstance& d = pick(swiglu, q8, ad, ex, f8, narrow ? 8 : 0);
+  const PrefillInstance& d = pick(swiglu, q8, ex, f8, narrow ? 8 : 0);
   FusedPlan p{};
-  p.kind = f8 ? 11 : (ex ? (q8 ? 10 : 8) : (ad ? 7 : (q8 ? 5 : 1)));
+  p.kind = f8 ? 11 : (ex ? (q8 ? 10 : 8) : (q8 ? 5 : 1));
   p.mf = d.fm * d.wm;
   p.nf = d.fn_ * d.wn;
   p.waves = d.wm * d.wn;
-  p.grid = dim3((unsigned)ceil_div(ceil_div(N, 16), p.nf), (unsigned)ceil_div(M, 16 * p.mf), 1);
+  // a split operand has two rows per output row
+  p.grid = dim3((unsigned)ceil_div(ceil_div(N, 16), p.nf), (unsigned)ceil_div(d.pair ? 2 * M : M, 16 * p.mf), 1);
   p.block = dim3(kWave * p.waves, 1, 1);
   p.name = d.name;
   return p;
 }
 
 hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
-                          int M, int K, int N, float eps, hipStream_t stream, uint8_t* q, float* qs,
-                          const AdalnArgs* ad) {
-  if (dt != DType::BF16 || (q != nullptr && wu == nullptr) || (ad != nullptr && (q != nullptr || !prefill_adaln_fits(ad->T))))
-    return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, ad != nullptr, false, false, p.nf);
-  PrefillArgs a;
-  a.sc = ad ? ad->scale : nullptr;
-  a.idx = ad ? ad->idx : nullptr;
-  a.bg = ad ? ad->bias_g : nullptr;
-  a.bu = ad ? ad->bias_u : nullptr;
-  a.T = ad ? ad->T : 0;
-  a.rs = nullptr;
+                          int M, int K, int N, float eps, hipStream_t stream, uint8_t* q, float* qs) {
+  if (dt != DType::BF16 || (q != nullptr && wu == nullptr)) return hipErrorInvalidValue;
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, false, p.nf);
+  PrefillArgs a{};
   a.q = q;
   a.qs = qs;
   a.sg = nullptr;
@@ -813,7 +655,7 @@ hipError_t launch_prefill_fp8(const FusedPlan& p, const void* x, const void* wg,
                               const float* su, void* y, int M, int K, int N, float eps, hipStream_t stream, uint8_t* q,
                               float* qs) {
   if ((q != nullptr && wu == nullptr) || sg == nullptr || (wu != nullptr && su == nullptr)) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, false, true, p.nf);
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, true, p.nf);
   PrefillArgs a{};
   a.x = x;
   a.wg = wg;
@@ -839,7 +681,7 @@ hipError_t launch_prefill_premod(const FusedPlan& p, const void* u, const float*
   if (q != nullptr && wu == nullptr) return hipErrorInvalidValue;
   const bool f8 = sg != nullptr;
   if (f8 && wu != nullptr && su == nullptr) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, true, f8);
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, true, f8);
   PrefillArgs a{};
   a.sg = sg;
   a.su = su;
@@ -849,7 +691,7 @@ hipError_t launch_prefill_premod(const FusedPlan& p, const void* u, const float*
   a.wg = wg;
   a.wu = wu;
   a.y = y;
-  a.M = M;
+  a.M = d.pair ? 2 * M : M;   // operand rows
   a.K = K;
   a.N = N;
   a.kblocks = (int)ceil_div(K, 32);

@@ -322,16 +322,17 @@ def _ad(lib, x=0x1000, sc=0x10000, idx=0x18000, w=0x20000, b=0x30000, y=0x40000,
 
 
 @pytest.mark.parametrize("kwargs,status,needle", [
-    (dict(x=None), NULL, "x, scale or idx"),
-    (dict(sc=None), NULL, "x, scale or idx"),
-    (dict(idx=None), NULL, "x, scale or idx"),
+    (dict(x=None), NULL, "x, mod or idx"),
+    (dict(sc=None), NULL, "x, mod or idx"),
+    (dict(idx=None), NULL, "x, mod or idx"),
     (dict(w=None), NULL, "W_packed or bias"),
     (dict(b=None), NULL, "W_packed or bias"),
     (dict(y=None), NULL, "y is NULL"),
     (dict(T=0), SHAPE, "T=0"),
     (dict(T=1 << 27, K=16), SHAPE, "T="),
     (dict(K=12), SHAPE, "multiple of 8"),
-    (dict(sc=0x10008), ALIGN, "scale"),
+    (dict(sc=0x10008), ALIGN, "x and mod"),
+    (dict(M=17), SHAPE, "at most 16 rows"),
     (dict(idx=0x18002), ALIGN, "idx and bias"),
     (dict(b=0x30002), ALIGN, "idx and bias"),
     (dict(eps=-1.0), EPS, "eps"),
@@ -354,14 +355,23 @@ def test_adaln_swiglu_bias_and_names(lib):
     assert f(0x1000, 0x2000, 0x1000, 2, 16, 16, BF16, None) == ALIAS
     assert f(0x1000, 0x2000, 0x3000, 2, 16, 16, 7, None) == DTYPE
     assert f(None, None, None, 0, 16, 16, BF16, None) == OK
-    # 32-64 rows and up to 23 table rows: the decode kernel stages the table's slice per stage; more table
-    # rows, or 16 rows, one scale row per x row
-    assert lib.fn_kernel_name_adaln(16, 4096, 11008, 4, 1).decode() == "decode_swiglu_adaln_bf16_m16_xlds_w3_u2_s5"
-    assert lib.fn_kernel_name_adaln(64, 4096, 11008, 23, 0).decode() == "decode_adaln_bf16_m64_xlds_w3_u2_tab"
-    assert lib.fn_kernel_name_adaln(64, 4096, 11008, 24, 0).decode() == "decode_adaln_bf16_m64_xlds_w3_u2"
-    assert lib.fn_kernel_name_adaln(1000, 4096, 11008, 63, 0).decode() == "prefill_adaln_bf16_256x256_w4x2_xl"
-    assert lib.fn_kernel_name_adaln(1000, 4096, 11008, 64, 1).decode() == "decode_swiglu_adaln_bf16_m64_xlds_w3_u2"
+    # the one-launch kernel: up to 16 rows
+    assert lib.fn_kernel_name_adaln(16, 4096, 11008, 4, 1).decode() == "decode_swiglu_adaln_split_bf16_m16_xlds_w3_u2_s5"
+    assert lib.fn_kernel_name_adaln(1, 4096, 12288, 900, 0).decode() == "decode_adaln_bf16_m16_xlds_w3_u2_s5"
+    assert lib.fn_kernel_name_adaln(17, 4096, 11008, 4, 0) == b"invalid"
     assert lib.fn_kernel_name_adaln(0, 4096, 16, 4, 0) == b"invalid"
+
+
+def test_adaln_fold_table_rejects(lib):
+    f = lib.fn_adaln_fold_table
+    assert f(0x1000, 0x2000, None, 2, 16, BF16, None) == NULL
+    assert f(0x1001, 0x2000, 0x3000, 2, 16, BF16, None) == ALIGN
+    assert f(0x1000, 0x2000, 0x3002, 2, 16, BF16, None) == ALIGN
+    assert f(0x1000, 0x2000, 0x2010, 2, 16, BF16, None) == ALIAS
+    assert f(0x1000, 0x2000, 0x3000, 2, 16, 7, None) == DTYPE
+    assert f(0x1000, 0x2000, 0x3000, 2, 12, BF16, None) == SHAPE
+    assert f(0x1000, 0x2000, 0x3000, 1 << 27, 16, BF16, None) == SHAPE
+    assert f(None, None, None, 0, 16, BF16, None) == OK
 
 
 WORKSPACE = 8
@@ -379,7 +389,7 @@ def _adw(lib, x=0x1000, sc=0x10000, idx=0x18000, w=0x20000, b=0x30000, y=0x40000
     (dict(ws=0x40000), ALIAS, "workspace overlaps"),
     (dict(ws=0x1000 - 256), ALIAS, "workspace overlaps"),
     # the one-launch checks come first
-    (dict(x=None, ws=None), NULL, "x, scale or idx"),
+    (dict(x=None, ws=None), NULL, "x, mod or idx"),
     (dict(K=12), SHAPE, "multiple of 8"),
     (dict(T=0), SHAPE, "T=0"),
     (dict(eps=float("nan")), EPS, "eps"),
@@ -392,15 +402,17 @@ def test_norm_proj_adaln_ws_rejects(lib, kwargs, status, needle):
 
 
 def test_adaln_ws_sizes_and_names(lib):
-    # operand M*K bf16, then one fp32 per row, each rounded up to 256 bytes; none up to 16 rows
+    # the split operand 2*M*K bf16, then one fp32 per row, each rounded up to 256 bytes; none up to 16 rows
     assert lib.fn_adaln_workspace_bytes(16, 4096) == 0
-    assert lib.fn_adaln_workspace_bytes(17, 8) == 512 + 256
-    assert lib.fn_adaln_workspace_bytes(65, 8) == 1280 + 512
-    assert lib.fn_adaln_workspace_bytes(4096, 4096) == 4096 * 4096 * 2 + 4096 * 4
+    assert lib.fn_adaln_workspace_bytes(17, 8) == 768 + 256
+    assert lib.fn_adaln_workspace_bytes(65, 8) == 2304 + 512
+    assert lib.fn_adaln_workspace_bytes(4096, 4096) == 2 * 4096 * 4096 * 2 + 4096 * 4
     assert lib.fn_adaln_workspace_bytes(100, 12) == 0 and lib.fn_adaln_workspace_bytes(-1, 16) == 0
     assert lib.fn_kernel_name_adaln_ws(4096, 4096, 12288, 4, 0).decode() == "prefill_premod_bf16_256x256_w4x2_xl"
-    assert lib.fn_kernel_name_adaln_ws(65, 4096, 11008, 500, 1).decode() == "prefill_swiglu_premod_bf16_256x128_w4x2_xl"
-    assert lib.fn_kernel_name_adaln_ws(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_premod_bf16_m64_xlds_w3_u2"
+    assert (lib.fn_kernel_name_adaln_ws(65, 4096, 11008, 500, 1).decode() ==
+            "prefill_swiglu_premod_split_bf16_256x128_w4x2_xl")
+    assert lib.fn_kernel_name_adaln_ws(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_premod_split_bf16_m64_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln_ws(16, 4096, 11008, 4, 1).decode() == "decode_swiglu_adaln_split_bf16_m16_xlds_w3_u2_s5"
     assert lib.fn_kernel_name_adaln_ws(17, 4096, 12288, 500, 0).decode() == "decode_premod_bf16_m32_xlds_w3_u2_s5"
     assert lib.fn_kernel_name_adaln_ws(16, 4096, 12288, 4, 0).decode() == "decode_adaln_bf16_m16_xlds_w3_u2_s5"
     assert lib.fn_kernel_name_adaln_ws(0, 4096, 16, 4, 0) == b"invalid"
@@ -440,7 +452,7 @@ def _adf(lib, x=0x1000, sc=0x10000, idx=0x18000, w=0x20000, s=0x28000, b=0x30000
     (dict(ws=0x28000 - 256), ALIAS, "workspace overlaps"),
     (dict(s=None), NULL, "W8_packed, scales or bias"),
     (dict(b=None), NULL, "W8_packed, scales or bias"),
-    (dict(x=None), NULL, "x, scale or idx"),
+    (dict(x=None), NULL, "x, mod or idx"),
     (dict(s=0x28002), ALIGN, "idx, scales and bias"),
     (dict(w=0x20008), ALIGN, "packed fp8 weights"),
     (dict(K=12), SHAPE, "multiple of 8"),
@@ -453,12 +465,15 @@ def test_norm_proj_adaln_fp8_ws_rejects(lib, kwargs, status, needle):
 
 
 def test_adaln_fp8_sizes_and_names(lib):
-    # needed for every M: the operand and 1/RMS, each rounded up to 256 bytes
+    # needed for every M: the (split) operand and 1/RMS, each rounded up to 256 bytes
     assert lib.fn_adaln_prepass_bytes(4, 16) == 256 + 256
+    assert lib.fn_adaln_prepass_bytes(5, 16) == 512 + 256
     assert lib.fn_adaln_prepass_bytes(0, 16) == 0
     assert lib.fn_kernel_name_adaln_fp8(16, 4096, 12288, 4, 0).decode() == "decode_fp8_premod_m16_xlds_w3_u8"
-    assert lib.fn_kernel_name_adaln_fp8(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_premod_m64_xlds_w4_u2"
-    assert lib.fn_kernel_name_adaln_fp8(4096, 4096, 11008, 4, 1).decode() == "prefill_swiglu_fp8_premod_256x128_w4x2_xl"
+    assert (lib.fn_kernel_name_adaln_fp8(64, 4096, 11008, 4, 1).decode() ==
+            "decode_swiglu_fp8_premod_split_m64_xlds_w4_u2")
+    assert (lib.fn_kernel_name_adaln_fp8(4096, 4096, 11008, 4, 1).decode() ==
+            "prefill_swiglu_fp8_premod_split_256x128_w4x2_xl")
     assert lib.fn_kernel_name_adaln_fp8(65, 4096, 12288, 4, 0).decode() == "prefill_fp8_premod_256x256_w4x2_xl"
     assert lib.fn_kernel_name_adaln_fp8(0, 4096, 16, 4, 0) == b"invalid"
     sw = lib.fn_norm_proj_swiglu_adaln_fp8_ws

@@ -110,11 +110,11 @@ def test_fp8_binding_rejects(gpu_lib):
     assert tuple(y.shape) == (0, 32)
 
 
-@pytest.mark.parametrize("N,swiglu,rows", [(12288, False, 96), (11008, True, 64)])
-def test_fp8_prefill_sampled_rows(gpu_lib, N, swiglu, rows):
+@pytest.mark.parametrize("N,swiglu", [(12288, False), (11008, True)])
+def test_fp8_prefill_full(gpu_lib, N, swiglu):
     """4096 rows x 4096 through the prefill kernel with fp8 weights (the
-    QKV projection and the FFN gate/up pair); the oracle on a seeded sample
-    of rows with the same codes and scales."""
+    QKV projection and the FFN gate/up pair), every output against the
+    oracle with the same codes and scales."""
     import torch
     fn = gpu_lib
     M, K = 4096, 4096
@@ -123,17 +123,17 @@ def test_fp8_prefill_sampled_rows(gpu_lib, N, swiglu, rows):
     x, g = to_dev(inp.x, "bf16"), to_dev(inp.g, "bf16")
     Pg = fn.fold_weights_fp8(g, to_dev(inp.W, "bf16"))
     cg, sg = oracle.fold_weights_fp8(inp.g, inp.W, "bf16")
-    pick = W.sample_indices(M, rows, seed=9)
     if swiglu:
         Pu = fn.fold_weights_fp8(g, to_dev(inp.W_up, "bf16"))
         cu, su = oracle.fold_weights_fp8(inp.g, inp.W_up, "bf16")
         y = fn.norm_proj_swiglu_fp8(x, Pg, Pu, inp.call.eps)
-        ref = oracle.norm_proj_swiglu_fp8(inp.x[pick], cg, sg, cu, su, inp.call.eps)
+        ref = oracle.norm_proj_swiglu_fp8(inp.x, cg, sg, cu, su, inp.call.eps)
     else:
         y = fn.norm_proj_fp8(x, Pg, inp.call.eps)
-        ref = oracle.norm_proj_fp8(inp.x[pick], cg, sg, inp.call.eps)
+        ref = oracle.norm_proj_fp8(inp.x, cg, sg, inp.call.eps)
     torch.cuda.synchronize()
-    assert_close(to_f64(y)[pick], ref, "bf16", f"fp8 prefill {M}x{K}x{N} swiglu={swiglu}")
+    err = assert_close(to_f64(y), ref, "bf16", f"fp8 prefill {M}x{K}x{N} swiglu={swiglu}")
+    print(f"fp8 prefill {M}x{K}x{N} swiglu={swiglu}: max |err|/(|ref|+1) = {err:.2e}")
 
 
 @pytest.mark.parametrize("M,K,N", [(65, 64, 16), (97, 8, 1), (256, 200, 300), (257, 4104, 33), (1000, 1032, 1100),

@@ -55,9 +55,8 @@ def test_q8_ffn_decode_full(gpu_lib, weights):
     print(f"midpoint flips: {flips} of {codes.size}")
 
 
-def test_q8_prefill_sampled_rows(gpu_lib):
-    """4096 rows through the prefill kernel's fp8 epilogue; the oracle on a
-    seeded sample of rows (row independence)."""
+def test_q8_prefill_full(gpu_lib):
+    """4096 rows through the prefill kernel's fp8 epilogue, every output."""
     import torch
     M, K, N = 4096, 1024, 2048
     inp = W.random_inputs(M, K, N, "bf16", seed=77, swiglu=True)
@@ -67,11 +66,10 @@ def test_q8_prefill_sampled_rows(gpu_lib):
     assert gpu_lib.kernel_name_q8(M, K, N, False).startswith("prefill_swiglu_bf16_q8")
     c, s = gpu_lib.norm_proj_swiglu_q8(x, Pg, Pu, 1e-6)
     torch.cuda.synchronize()
-    rows = W.sample_indices(M, 48, seed=5)
     Wg = oracle.fold_weights(inp.g, inp.W, "bf16")
     Wu = oracle.fold_weights(inp.g, inp.W_up, "bf16")
-    v = oracle.norm_proj_swiglu_folded(inp.x[rows], Wg, Wu, 1e-6)
-    assert_q8_close(c.cpu().numpy()[rows], s.cpu().numpy()[rows], v, "q8 prefill rows")
+    v = oracle.norm_proj_swiglu_folded(inp.x, Wg, Wu, 1e-6)
+    assert_q8_close(c.cpu().numpy(), s.cpu().numpy(), v, "q8 prefill")
 
 
 def test_q8_nan_row_and_zero_blocks(gpu_lib):

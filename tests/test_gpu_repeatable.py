@@ -90,9 +90,7 @@ def test_q8_output_repeatable(gpu_lib, M):
     _repeat(lambda: fn.norm_proj_swiglu_q8(x, Pg, Pu, 1e-6), lambda r: list(r))
 
 
-@pytest.mark.parametrize("M,N,T,swiglu", [(16, 12288, 4, False), (64, 11008, 4, True), (64, 11008, 30, True),
-                                          (4096, 12288, 8, False),
-                                          (4096, 11008, 16, True), (4096, 4096, 63, False), (4096, 4096, 64, True)])
+@pytest.mark.parametrize("M,N,T,swiglu", [(16, 12288, 4, False), (16, 11008, 4, True), (8, 11008, 30, True)])
 def test_adaln_repeatable(gpu_lib, M, N, T, swiglu):
     import torch
     fn = gpu_lib
@@ -100,8 +98,8 @@ def test_adaln_repeatable(gpu_lib, M, N, T, swiglu):
     gen.manual_seed(20 + T)
     K = 4096
     x = _rand((M, K), gen)
-    _, Wg, Wu, Pg, Pu = _weights(fn, K, N, swiglu, gen)
-    sc, sh = _rand((T, K), gen, 0.3), _rand((T, K), gen, 0.3)
+    g, Wg, Wu, Pg, Pu = _weights(fn, K, N, swiglu, gen)
+    sc, sh = fn.adaln_fold_table(g, _rand((T, K), gen, 0.3)), _rand((T, K), gen, 0.3)
     idx = torch.randint(0, T, (M,), generator=gen, device="cuda", dtype=torch.int32)
     bg = fn.adaln_shift_bias(sh, Wg)
     if swiglu:
@@ -121,8 +119,8 @@ def test_adaln_two_launch_repeatable(gpu_lib, M, N, T, swiglu):
     gen.manual_seed(60 + T)
     K = 4096
     x = _rand((M, K), gen)
-    _, Wg, Wu, Pg, Pu = _weights(fn, K, N, swiglu, gen)
-    sc, sh = _rand((T, K), gen, 0.3), _rand((T, K), gen, 0.3)
+    g, Wg, Wu, Pg, Pu = _weights(fn, K, N, swiglu, gen)
+    sc, sh = fn.adaln_fold_table(g, _rand((T, K), gen, 0.3)), _rand((T, K), gen, 0.3)
     idx = torch.randint(0, T, (M,), generator=gen, device="cuda", dtype=torch.int32)
     ws = torch.empty((fn.adaln_workspace_bytes(M, K),), dtype=torch.uint8, device="cuda")
     bg = fn.adaln_shift_bias(sh, Wg)
@@ -142,8 +140,8 @@ def test_adaln_fp8_repeatable(gpu_lib, M, N, swiglu):
     gen.manual_seed(70 + M)
     K, T = 4096, 4
     x = _rand((M, K), gen)
-    _, Wg, Wu, Pg, Pu = _weights(fn, K, N, swiglu, gen, fp8=True)
-    sc, sh = _rand((T, K), gen, 0.3), _rand((T, K), gen, 0.3)
+    g, Wg, Wu, Pg, Pu = _weights(fn, K, N, swiglu, gen, fp8=True)
+    sc, sh = fn.adaln_fold_table(g, _rand((T, K), gen, 0.3)), _rand((T, K), gen, 0.3)
     idx = torch.randint(0, T, (M,), generator=gen, device="cuda", dtype=torch.int32)
     ws = torch.empty((fn.adaln_prepass_bytes(M, K),), dtype=torch.uint8, device="cuda")
     bg = fn.adaln_shift_bias(sh, Wg)
@@ -163,8 +161,8 @@ def test_adaln_q8_repeatable(gpu_lib, M, f8):
     gen.manual_seed(80 + M)
     K, N, T = 4096, 11008, 4
     x = _rand((M, K), gen)
-    _, Wg, Wu, Pg, Pu = _weights(fn, K, N, True, gen, fp8=f8)
-    sc, sh = _rand((T, K), gen, 0.3), _rand((T, K), gen, 0.3)
+    g, Wg, Wu, Pg, Pu = _weights(fn, K, N, True, gen, fp8=f8)
+    sc, sh = fn.adaln_fold_table(g, _rand((T, K), gen, 0.3)), _rand((T, K), gen, 0.3)
     idx = torch.randint(0, T, (M,), generator=gen, device="cuda", dtype=torch.int32)
     ws = torch.empty((fn.adaln_prepass_bytes(M, K),), dtype=torch.uint8, device="cuda")
     bg, bu = fn.adaln_shift_bias(sh, Wg), fn.adaln_shift_bias(sh, Wu)

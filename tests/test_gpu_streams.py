@@ -18,7 +18,7 @@ def _case(fn, M, K, N, T, seed):
     sc = (torch.randn((T, K), generator=gen, device="cuda") * 0.3).to(torch.bfloat16)
     sh = (torch.randn((T, K), generator=gen, device="cuda") * 0.3).to(torch.bfloat16)
     idx = torch.randint(0, T, (M,), generator=gen, device="cuda", dtype=torch.int32)
-    return x, sc, idx, fn.fold_weights(g, W), fn.adaln_shift_bias(sh, W)
+    return x, fn.adaln_fold_table(g, sc), idx, fn.fold_weights(None, W), fn.adaln_shift_bias(sh, W)
 
 
 def test_two_streams_separate_workspaces(gpu_lib):
