@@ -357,6 +357,25 @@ fn_status fn_norm_proj_swiglu_adaln_ws(const void* x, const float* mod, const in
                                        void* out, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
                                        void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
+/* fn_norm_proj_swiglu_adaln_ws without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the call's workspace is
+ * a device array of this library's own, fn_norm_proj_swiglu_adaln_static_max_bytes()
+ * bytes (64 MiB + 64 KiB) on each GPU the library runs on, held until the
+ * process ends; the call allocates and frees nothing.  Arguments, arithmetic
+ * and results are those of fn_norm_proj_swiglu_adaln_ws (bit for bit: the
+ * same kernels).  Calls whose workspace would exceed the array
+ * (fn_adaln_workspace_bytes(M, K) > the maximum, e.g. M * K > 2^24) return
+ * FN_ERR_SHAPE before any HIP call.  Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (on different streams,
+ * or from different threads) race and must not be issued; calls on
+ * different GPUs do not interact.  M <= 16 uses no scratch (one launch). */
+fn_status fn_norm_proj_swiglu_adaln_static(const void* x, const float* mod, const int* idx, const void* W_gate_packed,
+                                           const float* bias_gate, const void* W_up_packed, const float* bias_up,
+                                           void* out, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
+                                           hipStream_t stream);
+int64_t fn_norm_proj_swiglu_adaln_static_max_bytes(void);
+
 /* Workspace bytes the two calls above need: the operand and one fp32 per
  * row, each rounded up to 256 bytes; 0 when M <= 16 (one launch) or when M
  * or K is outside the limits.  The SwiGLU call multiplies the operand split

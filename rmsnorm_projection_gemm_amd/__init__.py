@@ -78,6 +78,8 @@ def load():
         "fn_kernel_name_q8": (ctypes.c_char_p, [i64, i64, i64, i32]),
         "fn_adaln_shift_bias": (i32, [vp, vp, vp, i64, i64, i64, i32, vp]),
         "fn_adaln_fold_table": (i32, [vp, vp, vp, i64, i64, i32, vp]),
+        "fn_norm_proj_swiglu_adaln_static": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
+        "fn_norm_proj_swiglu_adaln_static_max_bytes": (i64, []),
         "fn_norm_proj_adaln": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
         "fn_norm_proj_swiglu_adaln": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]),
         "fn_kernel_name_adaln": (ctypes.c_char_p, [i64, i64, i64, i64, i32]),
@@ -532,6 +534,26 @@ def norm_proj_swiglu_adaln_ws(x, mod, idx, Wg: PackedWeights, bias_g, Wu: Packed
     return y
 
 
+def norm_proj_swiglu_adaln_static(x, mod, idx, Wg: PackedWeights, bias_g, Wu: PackedWeights, bias_u,
+                                  eps: float = 1e-6, out=None):
+    """norm_proj_swiglu_adaln_ws with the library's own device scratch as the
+    workspace (the entry point allocates nothing; pass `out` to allocate
+    nothing here either).  Calls that overlap on one GPU race."""
+    _check_adaln(x, mod, idx, Wg, bias_g)
+    _check_adaln(x, mod, idx, Wu, bias_u)
+    M, N = x.shape[0], Wg.N
+    y = _out(out, M, N, x)
+    _check(load().fn_norm_proj_swiglu_adaln_static(x.data_ptr(), mod.data_ptr(), idx.data_ptr(), Wg.data.data_ptr(),
+                                                   bias_g.data_ptr(), Wu.data.data_ptr(), bias_u.data_ptr(),
+                                                   y.data_ptr(), M, Wg.K, N, mod.shape[0], eps, _stream(x)))
+    return y
+
+
+def adaln_static_max_bytes() -> int:
+    """Bytes of the device scratch norm_proj_swiglu_adaln_static uses."""
+    return int(load().fn_norm_proj_swiglu_adaln_static_max_bytes())
+
+
 def kernel_name_adaln_ws(M: int, K: int, N: int, T: int, swiglu: bool) -> str:
     return load().fn_kernel_name_adaln_ws(M, K, N, T, int(swiglu)).decode()
 
@@ -767,6 +789,6 @@ __all__ = ["load", "fold_weights", "norm_proj", "norm_proj_swiglu", "rmsnorm", "
            "FN_CALL_NORM_PROJ_SWIGLU_Q8", "FN_CALL_NORM_PROJ_SWIGLU_FP8_Q8", "Q8_BLOCK", "norm_proj_swiglu_q8",
            "norm_proj_swiglu_fp8_q8", "kernel_name_q8", "adaln_shift_bias", "adaln_fold_table", "norm_proj_adaln",
            "norm_proj_swiglu_adaln", "kernel_name_adaln", "adaln_workspace_bytes", "norm_proj_adaln_ws",
-           "norm_proj_swiglu_adaln_ws", "kernel_name_adaln_ws", "adaln_modulate", "adaln_prepass_bytes",
+           "norm_proj_swiglu_adaln_ws", "norm_proj_swiglu_adaln_static", "adaln_static_max_bytes", "kernel_name_adaln_ws", "adaln_modulate", "adaln_prepass_bytes",
            "norm_proj_adaln_fp8_ws", "norm_proj_swiglu_adaln_fp8_ws", "kernel_name_adaln_fp8",
            "norm_proj_swiglu_adaln_q8_ws", "norm_proj_swiglu_adaln_fp8_q8_ws", "kernel_name_adaln_q8"]

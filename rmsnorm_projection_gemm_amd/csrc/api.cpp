@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "fn_launch.h"
@@ -656,6 +657,62 @@ fn_status fn_norm_proj_swiglu_adaln_ws(const void* x, const float* mod, const in
                                        void* workspace, int64_t workspace_bytes, hipStream_t stream) {
   return adaln_ws_common(x, mod, idx, W_gate_packed, bias_gate, W_up_packed, bias_up, out, M, K, N, T, eps,
                          workspace, workspace_bytes, stream, true);
+}
+
+// ---------------------------------------------------------------------------
+// The same SwiGLU AdaLN call for callers that cannot allocate: its workspace
+// is this library's own device array.  In host code `scratch` names a
+// host-side stand-in, not the device memory: the device address of each
+// GPU's copy is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = (int64_t(64) << 20) + (int64_t(64) << 10);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up on its first use there.
+fn_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  FN_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FN_ERR_HIP, "device %d out of the supported range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    FN_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (p == nullptr) return fail(FN_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FN_OK;
+}
+}  // namespace
+
+int64_t fn_norm_proj_swiglu_adaln_static_max_bytes(void) { return kScratchBytes; }
+
+fn_status fn_norm_proj_swiglu_adaln_static(const void* x, const float* mod, const int* idx, const void* W_gate_packed,
+                                           const float* bias_gate, const void* W_up_packed, const float* bias_up,
+                                           void* out, int64_t M, int64_t K, int64_t N, int64_t T, float eps,
+                                           hipStream_t stream) {
+  g_last_error[0] = '\0';
+  // arguments first (no HIP call on a bad call), then the size limit
+  FN_TRY(adaln_common(x, mod, idx, W_gate_packed, bias_gate, W_up_packed, bias_up, out, M, K, N, T, eps, stream,
+                      true, true));
+  if (M == 0 || N == 0) return FN_OK;
+  if (M <= kAdalnOneLaunchRows)
+    return adaln_common(x, mod, idx, W_gate_packed, bias_gate, W_up_packed, bias_up, out, M, K, N, T, eps, stream,
+                        true);
+  const int64_t need = adaln_ws_need(M, K, true);
+  if (need > kScratchBytes)
+    return fail(FN_ERR_SHAPE, "M=%lld, K=%lld need %lld bytes of scratch; the static scratch holds %lld",
+                (long long)M, (long long)K, (long long)need, (long long)kScratchBytes);
+  void* ws = nullptr;
+  FN_TRY(scratch_for_current_device(&ws));
+  return adaln_ws_common(x, mod, idx, W_gate_packed, bias_gate, W_up_packed, bias_up, out, M, K, N, T, eps, ws,
+                         kScratchBytes, stream, true);
 }
 
 const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
