@@ -42,6 +42,23 @@ def assert_close(got, ref, dtype: str, what: str = ""):
     return err
 
 
+def stale_failures(outs, refs):
+    """The staleness check: every output must match its own input's oracle
+    within the tolerance, and differ from the previous call's oracle by more
+    than the tolerance (so a one-step-stale result is caught: the failure
+    mode of the two-stream FlashNorm bug).  Returns the failures."""
+    bad = []
+    for t, (got, ref) in enumerate(zip(outs, refs)):
+        err = np.max(np.abs(got - ref) / (np.abs(ref) + 1.0))
+        if not (np.all(np.isfinite(got)) and err <= TOL["bf16"]):
+            bad.append(f"call {t}: max |err|/(|ref|+1) = {err:.3e}")
+        if t > 0:
+            stale = np.max(np.abs(got - refs[t - 1]) / (np.abs(refs[t - 1]) + 1.0))
+            if not stale > TOL["bf16"]:
+                bad.append(f"call {t} indistinguishable from call {t - 1}")
+    return bad
+
+
 def storage_bits(values: np.ndarray, dtype: str) -> np.ndarray:
     """Bit patterns of storage-exact values."""
     f = np.ascontiguousarray(values, dtype=np.float32)

@@ -9,7 +9,7 @@ import pytest
 import oracle
 import workloads as W
 from tests import oracle_pins
-from tests.gpu_helpers import TOL, assert_close, pack_host, to_dev, to_f64, tdtype
+from tests.gpu_helpers import TOL, assert_close, pack_host, stale_failures, to_dev, to_f64, tdtype
 
 pytestmark = pytest.mark.gpu
 
@@ -212,10 +212,8 @@ def test_rne_store(gpu_lib):
 # ------------------------------------------------------ staleness (T5) --
 def test_back_to_back_calls_not_stale(gpu_lib):
     """256 consecutive calls with distinct x into one reused, NaN-poisoned y:
-    every output must match its own input's oracle, and differ from the
-    previous call's oracle by more than the tolerance (so a one-step-stale
-    result would be caught; the failure mode of the two-stream FlashNorm
-    bug)."""
+    every output must match its own input's oracle and not the previous
+    call's."""
     import torch
     M, K, N, T = 16, 1024, 512, 256
     base = W.random_inputs(M, K, N, "bf16", seed=15)
@@ -228,15 +226,47 @@ def test_back_to_back_calls_not_stale(gpu_lib):
         gpu_lib.norm_proj(xd[t], Wp, 1e-6, out=y)
         outs.append(y.clone())
     torch.cuda.synchronize()
-    prev_ref = None
+    refs = [oracle.norm_proj(xs[t], base.g, base.W, 1e-6) for t in range(T)]
+    bad = stale_failures([to_f64(o) for o in outs], refs)
+    assert not bad, bad[:5]
+
+
+def test_two_stream_chain_with_its_event_join_passes_the_check(gpu_lib):
+    """The pages' two-stream form of the deferred norm ([FlashNorm digest],
+    the bug / cause / fix bullets) in plain torch -- the product x @ W' on one
+    stream behind unrelated work, the sums of squares and the post-scale on
+    another that waits on the product's event (the fix) -- passes the
+    staleness check.  That the check flags the unjoined form's one-step-stale
+    outputs is shown on the CPU (tests/test_staleness_check.py): whether
+    two streams actually overlap depends on how they map to hardware queues,
+    so a GPU race is no dependable negative control."""
+    import torch
+    M, K, N, T = 16, 1024, 512, 8
+    base = W.random_inputs(M, K, N, "bf16", seed=15)
+    Wf = torch.from_numpy(oracle.fold_weights(base.g, base.W, "bf16").astype(np.float32)).cuda()
+    xs = [W.make_x(M, K, "bf16", seed=2000 + t) for t in range(T)]
+    xd = [torch.from_numpy(x).cuda() for x in xs]
+    s_mm, s_post = torch.cuda.Stream(), torch.cuda.Stream()
+    busy_a = torch.randn((2048, 2048), device="cuda")
+    h = torch.full((M, N), float("nan"), device="cuda")
+    outs = []
+    torch.cuda.synchronize()
     for t in range(T):
-        ref = oracle.norm_proj(xs[t], base.g, base.W, 1e-6)
-        got = to_f64(outs[t])
-        assert_close(got, ref, "bf16", f"call {t}")
-        if prev_ref is not None:
-            stale = np.max(np.abs(got - prev_ref) / (np.abs(prev_ref) + 1.0))
-            assert stale > TOL["bf16"], f"call {t} indistinguishable from call {t - 1}"
-        prev_ref = ref
+        done = torch.cuda.Event()
+        with torch.cuda.stream(s_mm):
+            for _ in range(20):                  # unrelated work ahead of the product
+                busy_a = busy_a @ busy_a * 1e-3
+            torch.matmul(xd[t], Wf, out=h)
+            done.record()
+        with torch.cuda.stream(s_post):
+            inv = torch.rsqrt(xd[t].pow(2).mean(dim=1, keepdim=True) + 1e-6)
+            s_post.wait_event(done)
+            y = (h * inv).to(torch.bfloat16)
+        torch.cuda.synchronize()
+        outs.append(y.to(torch.float64).cpu().numpy())
+    refs = [oracle.norm_proj(xs[t], base.g, base.W, 1e-6) for t in range(T)]
+    bad = stale_failures(outs, refs)
+    assert not bad, bad[:5]
 
 
 # ------------------------------------------------------ unfused chain ---
