@@ -520,16 +520,41 @@ typedef struct fn_step_s* fn_step;   /* opaque handle */
  * "call i: ..." in fn_last_error() and *out = NULL. */
 fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out);
 
-/* Replay the recorded calls on `stream` with one graph launch; allocates
- * nothing.  A step must not be replayed on two streams at once (its
- * replays share the outputs). */
+/* A step of independent calls run as ONE kernel launch: every column block
+ * of every call is a workgroup of the same grid, in call order, so the
+ * calls follow one another on the CUs with no drain and ramp between
+ * kernels (a graph replay still runs one kernel per call, each ending in a
+ * tail where CUs idle; [FlashNorm digest], summary bullets on the dozens
+ * of norm launches per decode step; [Fused kernels] closing summary, item
+ * 3).  Each block runs the one-wave whole-k decode tile: the same bits as
+ * the call's own entry point where that entry point takes this tile too
+ * (more than 256 column blocks for a projection, more than 512 for a SwiGLU
+ * pair); narrower calls, which the entry point splits over k across waves,
+ * agree with it to the fp32 sum order.  Takes FN_CALL_NORM_PROJ and
+ * FN_CALL_NORM_PROJ_SWIGLU calls with FN_BF16 and M <= 16 (FN_ERR_SHAPE
+ * otherwise), 1 <= n_calls <= 65535; calls with M == 0 or N == 0 add
+ * nothing (a step of only such calls launches nothing).  The calls run at
+ * the same time, so no call may write a buffer another call reads or
+ * writes: FN_ERR_ALIAS otherwise (a model's chained calls need the
+ * recorded graph of fn_step_create).  Allocates host memory for the handle
+ * and device memory for the call table (n_calls small records and two
+ * bytes per column block), copied synchronously here; launching allocates
+ * nothing. */
+fn_status fn_step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* out);
+
+/* Replay the recorded calls on `stream`: one graph launch, or for a
+ * grouped step one kernel launch; allocates nothing.  A step must not be
+ * replayed on two streams at once (its replays share the outputs). */
 fn_status fn_step_launch(fn_step step, hipStream_t stream);
 
-/* Number of calls recorded (the calls with M, N >= 1); -1 for NULL. */
+/* Kernel launches per replay of the step: the calls recorded (those with M,
+ * N >= 1), or 1 for a grouped step (0 if all its calls are empty); -1 for
+ * NULL. */
 int64_t fn_step_num_kernels(fn_step step);
 
-/* Release the graph and the handle; NULL is a no-op.  The caller makes
- * sure no replay is still running (e.g. synchronises its stream). */
+/* Release the graph (or the grouped step's device tables) and the handle;
+ * NULL is a no-op.  The caller makes sure no replay is still running (e.g.
+ * synchronises its stream). */
 fn_status fn_step_destroy(fn_step step);
 
 /* Static description of a status code. */

@@ -100,6 +100,7 @@ def load():
                                                       f32, vp, i64, vp]),
         "fn_kernel_name_adaln_q8": (ctypes.c_char_p, [i64, i64, i64, i64, i32]),
         "fn_step_create": (i32, [vp, i64, ctypes.POINTER(vp)]),
+        "fn_step_create_grouped": (i32, [vp, i64, ctypes.POINTER(vp)]),
         "fn_step_launch": (i32, [vp, vp]),
         "fn_step_num_kernels": (i64, [vp]),
         "fn_step_destroy": (i32, [vp]),
@@ -751,13 +752,16 @@ class Step:
                   Pu.scales.data_ptr(), codes, x.shape[0], Pg.K, Pg.N, eps, FN_BF16,
                   (x, Pg.data, Pg.scales, Pu.data, Pu.scales, codes, scales), scales)
 
-    def record(self):
-        """Validate and record the calls (fn_step_create)."""
+    def record(self, grouped: bool = False):
+        """Validate and record the calls: into a HIP graph (fn_step_create),
+        or, grouped=True, as one launch of independent calls
+        (fn_step_create_grouped)."""
         if self._handle is not None:
             raise RuntimeError("the step is already recorded")
         arr = (FnCall * len(self._calls))(*self._calls)
         h = ctypes.c_void_p()
-        _check(load().fn_step_create(arr, len(self._calls), ctypes.byref(h)))
+        create = load().fn_step_create_grouped if grouped else load().fn_step_create
+        _check(create(arr, len(self._calls), ctypes.byref(h)))
         self._handle = h
         return self
 
@@ -766,8 +770,9 @@ class Step:
         return load().fn_step_num_kernels(self._handle)
 
     def launch(self, stream=None):
-        """Replay every recorded call with one graph launch on `stream`
-        (default: the current stream of the first call's device)."""
+        """Replay every recorded call with one graph launch (one kernel
+        launch for a grouped step) on `stream` (default: the current stream
+        of the first call's device)."""
         if self._handle is None:
             raise RuntimeError("record() the step first")
         if stream is None:
@@ -775,7 +780,8 @@ class Step:
         _check(load().fn_step_launch(self._handle, stream))
 
     def close(self):
-        """Release the graph; the caller makes sure no replay is running."""
+        """Release the graph (or the grouped step's call table); the caller
+        makes sure no replay is running."""
         if self._handle is not None:
             _check(load().fn_step_destroy(self._handle))
             self._handle = None

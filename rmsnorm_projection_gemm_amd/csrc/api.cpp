@@ -6,8 +6,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "fn_launch.h"
 
@@ -420,6 +422,10 @@ struct fn_step_s {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   int64_t kernels = 0;
+  void* calls = nullptr;   // grouped: the call records (device)
+  void* items = nullptr;   // grouped: the call of each workgroup (device)
+  int64_t nitems = 0;      // grouped: workgroups of the one launch
+  bool grouped = false;
 };
 
 namespace fn {
@@ -845,9 +851,131 @@ fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out) {
   return st;
 }
 
+namespace {
+struct Span {
+  uintptr_t lo, hi;
+  bool out;
+  int64_t call;
+};
+
+// Furthest end reached so far, kept per call: the largest end, its call,
+// and the largest end among the other calls, so that the furthest reach of
+// every call but a given one is known.
+struct Reach {
+  uintptr_t end1 = 0, end2 = 0;
+  int64_t call1 = -1;
+  void add(uintptr_t e, int64_t c) {
+    if (c == call1) {
+      end1 = std::max(end1, e);
+    } else if (e > end1) {
+      end2 = end1;
+      end1 = e;
+      call1 = c;
+    } else {
+      end2 = std::max(end2, e);
+    }
+  }
+  uintptr_t other_than(int64_t c) const { return c == call1 ? end2 : end1; }
+};
+
+// True if an output of one call overlaps any buffer of another call: sorted
+// by start, a span overlaps an earlier span of another call exactly when it
+// starts before that call's furthest end; an output is checked against
+// every earlier span, any span against earlier outputs.
+bool outputs_overlap(std::vector<Span>& v) {
+  std::sort(v.begin(), v.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  Reach outs, any;
+  for (const Span& s : v) {
+    if (s.lo < outs.other_than(s.call)) return true;
+    if (s.out && s.lo < any.other_than(s.call)) return true;
+    if (s.out) outs.add(s.hi, s.call);
+    any.add(s.hi, s.call);
+  }
+  return false;
+}
+}  // namespace
+
+fn_status fn_step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* out) {
+  g_last_error[0] = '\0';
+  if (out == nullptr) return fail(FN_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  if (calls == nullptr) return fail(FN_ERR_NULL, "calls is NULL");
+  if (n_calls < 1 || n_calls > 65535) return fail(FN_ERR_SHAPE, "n_calls=%lld must be in [1, 65535]", (long long)n_calls);
+  std::vector<Span> spans;
+  int64_t items = 0;
+  for (int64_t i = 0; i < n_calls; ++i) {
+    const fn_call& c = calls[i];
+    const fn_status s = run_call(c, nullptr, true);
+    if (s != FN_OK) return call_failed(s, i);
+    if (c.kind != FN_CALL_NORM_PROJ && c.kind != FN_CALL_NORM_PROJ_SWIGLU)
+      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes fn_norm_proj and fn_norm_proj_swiglu calls"), i);
+    if (c.dt != FN_BF16 || c.M > 16)
+      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes bf16 calls of at most 16 rows (M=%lld)",
+                              (long long)c.M), i);
+    if (c.M == 0 || c.N == 0) continue;
+    const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU;
+    const int64_t wb = packed_bytes(c.K, c.N, FN_BF16);
+    auto add = [&](const void* p, int64_t bytes, bool o) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+      spans.push_back(Span{lo, lo + (uintptr_t)bytes, o, i});
+    };
+    add(c.x, c.M * c.K * 2, false);
+    add(c.w_gate, wb, false);
+    if (sw) add(c.w_up, wb, false);
+    add(c.y, c.M * c.N * 2, true);
+    items += (c.N + 15) / 16;
+  }
+  if (outputs_overlap(spans))
+    return fail(FN_ERR_ALIAS, "a grouped step runs its calls at once: no call may write a buffer another call uses");
+  if (items > INT32_MAX) return fail(FN_ERR_SHAPE, "a grouped step holds at most 2^31-1 column blocks");
+  const size_t rec = fn::grouped_call_bytes();
+  std::vector<uint8_t> host_calls((size_t)n_calls * rec);
+  std::vector<uint16_t> host_items((size_t)items);
+  int64_t first = 0;
+  for (int64_t i = 0; i < n_calls; ++i) {
+    const fn_call& c = calls[i];
+    const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU;
+    fn::grouped_call_fill(host_calls.data() + (size_t)i * rec, c.x, c.w_gate, sw ? c.w_up : nullptr, c.y, (int)c.M,
+                          (int)c.K, (int)c.N, c.eps, (int)first);
+    if (c.M == 0 || c.N == 0) continue;
+    const int64_t nb = (c.N + 15) / 16;
+    for (int64_t b = 0; b < nb; ++b) host_items[(size_t)(first + b)] = (uint16_t)i;
+    first += nb;
+  }
+  fn_step h = new (std::nothrow) fn_step_s;
+  if (h == nullptr) return fail(FN_ERR_HIP, "step: out of host memory");
+  h->grouped = true;
+  if (items == 0) {   // every call empty: the step launches nothing
+    *out = h;
+    return FN_OK;
+  }
+  fn_status st = hip_status(hipMalloc(&h->calls, host_calls.size()), "grouped step: allocate calls");
+  if (st == FN_OK) st = hip_status(hipMalloc(&h->items, host_items.size() * 2), "grouped step: allocate items");
+  if (st == FN_OK)
+    st = hip_status(hipMemcpy(h->calls, host_calls.data(), host_calls.size(), hipMemcpyHostToDevice),
+                    "grouped step: copy calls");
+  if (st == FN_OK)
+    st = hip_status(hipMemcpy(h->items, host_items.data(), host_items.size() * 2, hipMemcpyHostToDevice),
+                    "grouped step: copy items");
+  if (st != FN_OK) {
+    if (h->calls != nullptr) (void)hipFree(h->calls);
+    if (h->items != nullptr) (void)hipFree(h->items);
+    delete h;
+    return st;
+  }
+  h->nitems = items;
+  h->kernels = 1;
+  *out = h;
+  return FN_OK;
+}
+
 fn_status fn_step_launch(fn_step step, hipStream_t stream) {
   g_last_error[0] = '\0';
   if (step == nullptr) return fail(FN_ERR_NULL, "step is NULL");
+  if (step->grouped)
+    return step->nitems == 0 ? FN_OK
+                             : hip_status(fn::launch_decode_grouped(step->calls, step->items, (int)step->nitems, stream),
+                                          "grouped step: launch");
   return hip_status(hipGraphLaunch(step->exec, stream), "step: launch");
 }
 
@@ -856,9 +984,17 @@ int64_t fn_step_num_kernels(fn_step step) { return step == nullptr ? -1 : step->
 fn_status fn_step_destroy(fn_step step) {
   g_last_error[0] = '\0';
   if (step == nullptr) return FN_OK;
-  fn_status st = hip_status(hipGraphExecDestroy(step->exec), "step: destroy exec");
-  const fn_status s2 = hip_status(hipGraphDestroy(step->graph), "step: destroy graph");
-  if (st == FN_OK) st = s2;
+  fn_status st = FN_OK;
+  if (step->grouped) {
+    if (step->calls != nullptr) st = hip_status(hipFree(step->calls), "grouped step: free calls");
+    const fn_status s2 =
+        step->items == nullptr ? FN_OK : hip_status(hipFree(step->items), "grouped step: free items");
+    if (st == FN_OK) st = s2;
+  } else {
+    st = hip_status(hipGraphExecDestroy(step->exec), "step: destroy exec");
+    const fn_status s2 = hip_status(hipGraphDestroy(step->graph), "step: destroy graph");
+    if (st == FN_OK) st = s2;
+  }
   delete step;
   return st;
 }

@@ -47,8 +47,9 @@ struct DecodeArgs {
   float eps;
 };
 
+// One workgroup's tile: column-block group bx, row-block group by.
 template <typename T, int MF, int NF, bool SW, int WN, int WK, int U>
-__global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_tile(const DecodeArgs& a, int bx, int by) {
   constexpr int V = Geo<T>::V;
   constexpr int KB = Geo<T>::KB;
   constexpr int NMAT = SW ? 2 : 1;
@@ -59,8 +60,8 @@ __global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
   const int wk = wave / WN;         // k split of this wave
   const int lrow = lane & 15;       // operand row (x) / column (W') of this lane
   const int lgrp = lane >> 4;       // k group of this lane
-  const int nb0 = (blockIdx.x * WN + wn) * NF;
-  const int m0 = blockIdx.y * 16 * MF;
+  const int nb0 = (bx * WN + wn) * NF;
+  const int m0 = by * 16 * MF;
   const int kb_begin = (int)((int64_t)a.kblocks * wk / WK);
   const int kb_end = (int)((int64_t)a.kblocks * (wk + 1) / WK);
   const int kb_full = a.K / KB;     // k-blocks with no ragged tail
@@ -306,6 +307,65 @@ __global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
       }
     }
   }
+}
+
+template <typename T, int MF, int NF, bool SW, int WN, int WK, int U>
+__global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
+  decode_tile<T, MF, NF, SW, WN, WK, U>(a, blockIdx.x, blockIdx.y);
+}
+
+// Grouped launch: the column blocks of several independent calls (bf16, at
+// most 16 rows each) as the workgroups of one launch, in call order.  The
+// hardware starts each workgroup as a CU frees up, so the calls follow one
+// another with no drain and ramp between kernels -- what a launch per call
+// costs at the end and start of every call ([FlashNorm digest], summary
+// bullets on the dozens of norm launches per decode step).  Each
+// workgroup looks up its call (item -> call table) and runs the one-wave,
+// whole-k tile of the decode kernel on its column block.
+struct GroupCall {
+  DecodeArgs a;
+  int first;    // index of the call's first column block in the launch
+  int swiglu;
+};
+
+__global__ __launch_bounds__(kWave) void decode_grouped_kernel(const GroupCall* __restrict__ calls,
+                                                               const uint16_t* __restrict__ item_call) {
+  const int item = blockIdx.x;
+  const int c = __builtin_amdgcn_readfirstlane((int)item_call[item]);
+  const GroupCall& g = calls[c];
+  const int nb = item - g.first;
+  if (g.swiglu)
+    decode_tile<__bf16, 1, 1, true, 1, 1, 2>(g.a, nb, 0);
+  else
+    decode_tile<__bf16, 1, 1, false, 1, 1, 4>(g.a, nb, 0);
+}
+
+hipError_t launch_decode_grouped(const void* calls, const void* item_call, int items, hipStream_t stream) {
+  const GroupCall* c = static_cast<const GroupCall*>(calls);
+  const uint16_t* ic = static_cast<const uint16_t*>(item_call);
+  void* args[] = {&c, &ic};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_grouped_kernel), dim3((unsigned)items), dim3(kWave),
+                         args, 0, stream);
+}
+
+size_t grouped_call_bytes() { return sizeof(GroupCall); }
+
+void grouped_call_fill(void* dst, const void* x, const void* wg, const void* wu, void* y, int M, int K, int N,
+                       float eps, int first) {
+  GroupCall g{};
+  g.a.x = x;
+  g.a.wg = static_cast<const u32x4*>(wg);
+  g.a.wu = static_cast<const u32x4*>(wu);
+  g.a.y = y;
+  g.a.M = M;
+  g.a.K = K;
+  g.a.N = N;
+  g.a.kblocks = (int)ceil_div(K, k_per_block(DType::BF16));
+  g.a.nblocks = (int)ceil_div(N, 16);
+  g.a.eps = eps;
+  g.first = first;
+  g.swiglu = wu != nullptr;
+  *static_cast<GroupCall*>(dst) = g;
 }
 
 // Kernel instances.  The table maps (dtype, row capacity, SwiGLU) to a tile

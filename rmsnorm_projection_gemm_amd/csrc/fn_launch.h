@@ -92,6 +92,15 @@ hipError_t launch_decode_premod(const FusedPlan& plan, const void* u, const floa
                                 const float* sg, const void* wu, const float* su, void* y, int M, int K, int N,
                                 const AdalnArgs& ad, hipStream_t stream);
 
+// Grouped launch of independent bf16 calls of at most 16 rows: one
+// workgroup per column block of every call.  calls: device array of
+// grouped_call_bytes() records (grouped_call_fill on the host, then copied);
+// item_call: device array [items] of uint16 call indices.
+size_t grouped_call_bytes();
+void grouped_call_fill(void* dst, const void* x, const void* wg, const void* wu, void* y, int M, int K, int N,
+                       float eps, int first);
+hipError_t launch_decode_grouped(const void* calls, const void* item_call, int items, hipStream_t stream);
+
 hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
                        int K, int N, hipStream_t stream);
 

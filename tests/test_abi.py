@@ -276,6 +276,61 @@ def test_step_null_arguments(lib):
     assert lib.fn_step_destroy(None) == OK
 
 
+def _create_grouped(lib, calls, n=None):
+    arr = (fn.FnCall * max(1, len(calls)))(*calls)
+    h = ctypes.c_void_p(0x1234)
+    st = lib.fn_step_create_grouped(arr, len(calls) if n is None else n, ctypes.byref(h))
+    return st, h
+
+
+def test_grouped_step_validates_before_any_hip_call(lib):
+    # every rejection below is decided on the host, before the call table is
+    # allocated (no HIP call is possible without a GPU)
+    st, h = _create_grouped(lib, [_call(), _call(K=12)])
+    assert st == SHAPE and h.value is None and lib.fn_last_error().decode().startswith("call 1: K=12")
+    st, _ = _create_grouped(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_FP8, sg=0x30000)])
+    assert st == SHAPE and "grouped step takes fn_norm_proj" in lib.fn_last_error().decode()
+    st, _ = _create_grouped(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_SWIGLU_Q8, wu=0x30000, ys=0x50000)])
+    assert st == SHAPE
+    st, _ = _create_grouped(lib, [_call(dt=F32)])
+    assert st == SHAPE and "bf16 calls of at most 16 rows" in lib.fn_last_error().decode()
+    st, _ = _create_grouped(lib, [_call(M=17)])
+    assert st == SHAPE and "M=17" in lib.fn_last_error().decode()
+    st, _ = _create_grouped(lib, [])
+    assert st == SHAPE and "n_calls" in lib.fn_last_error().decode()
+    st, _ = _create_grouped(lib, [_call()], n=65536)
+    assert st == SHAPE
+    assert lib.fn_step_create_grouped(None, 1, ctypes.byref(ctypes.c_void_p())) == NULL
+    assert lib.fn_step_create_grouped((fn.FnCall * 1)(_call()), 1, None) == NULL
+
+
+def test_grouped_step_rejects_calls_that_share_a_written_buffer(lib):
+    # x 4x16 bf16 = 128 B, packed 16x16 weights, y 4x16 bf16 = 128 B
+    a = dict(x=0x1000, wg=0x20000, y=0x40000)
+    b = dict(x=0x2000, wg=0x20000, y=0x50000)            # same weights: read by both, fine
+    assert _create_grouped(lib, [_call(M=0, **a), _call(M=0, **b)])[0] == OK
+    st, _ = _create_grouped(lib, [_call(**a), _call(x=0x2000, wg=0x30000, y=0x40040)])
+    assert st == ALIAS and "at once" in lib.fn_last_error().decode()      # outputs overlap
+    st, _ = _create_grouped(lib, [_call(**a), _call(x=0x40000, wg=0x30000, y=0x50000)])
+    assert st == ALIAS                                                      # call 1 reads call 0's output
+    st, _ = _create_grouped(lib, [_call(**a), _call(x=0x2000, wg=0x30000, y=0x20010)])
+    assert st == ALIAS                                                      # call 1 writes call 0's weights
+    # a wide input of one call spanning another call's output, with a third
+    # call's buffers between them
+    st, _ = _create_grouped(lib, [_call(x=0x1000, M=16, K=1024, wg=0x90000, y=0xa0000),
+                                  _call(x=0x1100, wg=0x30000, y=0x3000, M=4, K=16, N=16),
+                                  _call(x=0x2800, wg=0xb0000, y=0xc0000)])
+    assert st == ALIAS
+
+
+def test_grouped_step_of_empty_calls_launches_nothing(lib):
+    st, h = _create_grouped(lib, [_call(M=0), _call(N=0, kind=fn.FN_CALL_NORM_PROJ_SWIGLU, wu=0x30000)])
+    assert st == OK and h.value is not None
+    assert lib.fn_step_num_kernels(h) == 0
+    assert lib.fn_step_launch(h, None) == OK
+    assert lib.fn_step_destroy(h) == OK
+
+
 def _q8(lib, x=0x1000, wg=0x20000, wu=0x30000, c=0x40000, s=0x50000, M=4, K=16, N=16, eps=1e-6):
     return lib.fn_norm_proj_swiglu_q8(x, wg, wu, c, s, M, K, N, eps, None)
 

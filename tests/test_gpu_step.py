@@ -2,7 +2,10 @@
 calls replayed with one HIP graph launch gives bit for bit what the same
 calls give launched one by one, on every replay, with inputs refreshed in
 place between replays; calls run in order, so a later call reads an earlier
-call's output; and the replay agrees with the float64 oracle."""
+call's output; and the replay agrees with the float64 oracle.  A grouped
+step (fn_step_create_grouped) runs independent calls as one launch: the
+same bits as the eager calls that take the same tile, the oracle's values
+within tolerance for every call."""
 import numpy as np
 import pytest
 
@@ -174,3 +177,106 @@ def test_step_binding_rejects(gpu_lib):
     with pytest.raises(fn.FlashNormError, match="call 0"):
         st.record()
     del y
+
+
+def test_grouped_decode_step_matches_eager(gpu_lib):
+    """The same four layers and head recorded as ONE grouped launch: every
+    call is wide enough that its own entry point takes the one-wave tile, so
+    each output equals the eager call's bit for bit, on every replay, with
+    the inputs refreshed in place between replays."""
+    import torch
+    fn = gpu_lib
+    calls = W.decode_step_calls(4)
+    st = fn.Step()
+    items = []
+    for c in calls:
+        x, g, Wm, Wu = W.make_inputs_device(c)
+        Pg = fn.fold_weights(g, Wm)
+        Pu = fn.fold_weights(g, Wu) if c.swiglu else None
+        out = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+        if c.swiglu:
+            st.norm_proj_swiglu(x, Pg, Pu, out, c.eps)
+        else:
+            st.norm_proj(x, Pg, out, c.eps)
+        items.append((x, Pg, Pu, out, c))
+        del Wm, Wu
+    st.record(grouped=True)
+    assert st.num_kernels == 1
+    gen = torch.Generator(device="cuda")
+    for replay in range(3):
+        if replay:
+            gen.manual_seed(300 + replay)
+            for x, *_r in items:
+                x.copy_(torch.randn(x.shape, generator=gen, device="cuda").to(x.dtype))
+        for *_r, out, _c in items:
+            out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        st.launch()
+        torch.cuda.synchronize()
+        for x, Pg, Pu, out, c in items:
+            want = fn.norm_proj_swiglu(x, Pg, Pu, c.eps) if c.swiglu else fn.norm_proj(x, Pg, c.eps)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {replay}: {c.name}"
+    st.close()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_grouped_ragged_calls_agree_with_oracle(gpu_lib, seed):
+    """Ragged calls in one grouped launch -- one row up to sixteen, K from 8
+    to 4104, N from 1 to 1100 (narrow ones, which their own entry points
+    split over k), an empty call between them -- each against the float64
+    oracle; and the outputs of a second replay are the first's bits."""
+    import torch
+    fn = gpu_lib
+    shapes = [(1, 8, 1, False), (16, 4104, 1100, True), (3, 264, 37, False), (0, 64, 32, False),
+              (7, 1032, 270, True), (16, 520, 16, False), (9, 40, 600, False), (12, 2056, 33, True),
+              (16, 4096, 530, False), (5, 136, 17, True)]
+    st = fn.Step()
+    cases = []
+    for i, (M, K, N, sw) in enumerate(shapes):
+        inp = W.random_inputs(M, K, N, "bf16", seed=400 + 20 * seed + i, swiglu=sw)
+        x = to_dev(inp.x, "bf16")
+        Pg = fn.fold_weights(to_dev(inp.g, "bf16"), to_dev(inp.W, "bf16"))
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if sw:
+            Pu = fn.fold_weights(to_dev(inp.g, "bf16"), to_dev(inp.W_up, "bf16"))
+            st.norm_proj_swiglu(x, Pg, Pu, out, 1e-6)
+            ref = oracle.norm_proj_swiglu(inp.x, inp.g, inp.W, inp.W_up, 1e-6)
+        else:
+            st.norm_proj(x, Pg, out, 1e-6)
+            ref = oracle.norm_proj(inp.x, inp.g, inp.W, 1e-6)
+        cases.append((out, ref, (M, K, N, sw)))
+    st.record(grouped=True)
+    st.launch()
+    torch.cuda.synchronize()
+    first = [out.clone() for out, _r, _s in cases]
+    for out, ref, shape in cases:
+        assert_close(to_f64(out), ref, "bf16", f"grouped call {shape}")
+        out.fill_(float("nan"))
+    st.launch()
+    torch.cuda.synchronize()
+    for (out, _r, shape), f in zip(cases, first):
+        assert torch.equal(out.view(torch.int16), f.view(torch.int16)), f"second replay differs: {shape}"
+    st.close()
+
+
+def test_grouped_step_rejects_chained_calls(gpu_lib):
+    """A call that reads another call's output cannot run at the same time
+    as it: the grouped form refuses it (the recorded graph takes it)."""
+    import torch
+    fn = gpu_lib
+    P1 = fn.fold_weights(None, torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda"))
+    P2 = fn.fold_weights(None, torch.zeros((64, 32), dtype=torch.bfloat16, device="cuda"))
+    x = torch.zeros((2, 64), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((2, 64), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((2, 32), dtype=torch.bfloat16, device="cuda")
+    st = fn.Step()
+    st.norm_proj(x, P1, h)
+    st.norm_proj(h, P2, y)
+    with pytest.raises(fn.FlashNormError, match="at once"):
+        st.record(grouped=True)
+    st2 = fn.Step()
+    st2.norm_proj(x, P1, h)
+    st2.norm_proj(h, P2, y)
+    st2.record()
+    st2.close()
