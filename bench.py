@@ -62,6 +62,8 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     p.add_argument("--no-measured-peak", dest="measured_peak", action="store_false",
                    help="skip measuring the attainable peak (roofline.measured_peak, frac_measured)")
+    p.add_argument("--no-plain-read", dest="plain_read", action="store_false",
+                   help="skip timing a plain streaming read of each HBM-bound call's bytes")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     p.add_argument("--configs", default=",".join(DEFAULT_CONFIGS),
                    help="other workloads to measure in the same run, comma-separated names from "
@@ -558,6 +560,34 @@ def measured_peak(torch, fn, bound):
     return round(work / pct(sorted(times), 0.5) / scale, 1), unit
 
 
+def plain_read_us(torch, fn, nbytes):
+    """The time of a plain streaming read of nbytes (fn_probe_hbm_read, 2048
+    workgroups) from cold buffers (rotated over >= 1 GiB, beyond the 256 MB
+    Infinity Cache): the floor a kernel that must read that many bytes meets
+    on this GPU, fixed launch and ramp costs included.  Median of ten blocks
+    of ten calls."""
+    n16 = max(16, nbytes // 16 * 16)
+    nbuf = max(2, -(-(1 << 30) // n16))
+    bufs = [torch.empty(n16, dtype=torch.uint8, device="cuda").fill_(3) for _ in range(nbuf)]
+    for i in range(nbuf):
+        fn.probe_hbm_read(bufs[i])
+    torch.cuda.synchronize()
+    times = []
+    j = 0
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn.probe_hbm_read(bufs[j % nbuf])
+            j += 1
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / 10)
+    del bufs
+    torch.cuda.empty_cache()
+    return pct(sorted(times), 0.5)
+
+
 def calibrate_copy(torch):
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -647,6 +677,12 @@ def measure(args, torch, fn, workloads):
             roof["frac_measured"] = round(roof["achieved"] / peak, 4)
             roof["measured_peak_probe"] = ("fn_probe_hbm_read over 1 GiB" if roof["bound"] == "hbm"
                                            else "fn_probe_mfma_bf16 (MFMA-only loop)")
+    if args.plain_read and roof["bound"] == "hbm" and unit != "us/call" and args.workload != "decode_step":
+        # the same bytes read by a plain streaming kernel, cold: what a kernel
+        # of this size can reach at all (launch and ramp included)
+        pr = plain_read_us(torch, fn, int(work))
+        roof["plain_read_same_bytes_us"] = round(pr, 3)
+        roof["frac_of_plain_read"] = round(pr / (med * 1e3), 4)
     out = {
         "value": round(value, 4), "unit": unit, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(r["ms"], 6), "dtype": dtype, "config": config, "roofline": roof,
