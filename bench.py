@@ -245,6 +245,7 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False, adaln=Fa
     x = inp.x[:rows]
     calls, t0 = 0, time.perf_counter()
     w8 = None
+    ref = None
     if fp8:
         # the AdaLN calls quantise the plain W (the gain goes into the table)
         gq = np.ones(call.K) if adaln else inp.g
@@ -264,26 +265,26 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False, adaln=Fa
         elif adaln and q8:
             oracle.adaln_norm_proj_swiglu_q8(x, inp.g, sc, sh, idx, inp.W, inp.W_up, call.eps)
         elif adaln and fp8 and call.swiglu:
-            oracle.adaln_norm_proj_swiglu_fp8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], mod, bias8[0], bias8[1], idx,
+            ref = oracle.adaln_norm_proj_swiglu_fp8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], mod, bias8[0], bias8[1], idx,
                                               call.eps)
         elif adaln and fp8:
-            oracle.adaln_norm_proj_fp8(x, w8[0][0], w8[0][1], mod, bias8[0], idx, call.eps)
+            ref = oracle.adaln_norm_proj_fp8(x, w8[0][0], w8[0][1], mod, bias8[0], idx, call.eps)
         elif adaln and call.swiglu:
-            oracle.adaln_norm_proj_swiglu(x, inp.g, sc, sh, idx, inp.W, inp.W_up, call.eps)
+            ref = oracle.adaln_norm_proj_swiglu(x, inp.g, sc, sh, idx, inp.W, inp.W_up, call.eps)
         elif adaln:
-            oracle.adaln_norm_proj(x, inp.g, sc, sh, idx, inp.W, call.eps)
+            ref = oracle.adaln_norm_proj(x, inp.g, sc, sh, idx, inp.W, call.eps)
         elif q8 and fp8:
             oracle.norm_proj_swiglu_fp8_q8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], call.eps)
         elif q8:
             oracle.norm_proj_swiglu_q8(x, inp.g, inp.W, inp.W_up, call.eps)
         elif fp8 and call.swiglu:
-            oracle.norm_proj_swiglu_fp8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], call.eps)
+            ref = oracle.norm_proj_swiglu_fp8(x, w8[0][0], w8[0][1], w8[1][0], w8[1][1], call.eps)
         elif fp8:
-            oracle.norm_proj_fp8(x, w8[0][0], w8[0][1], call.eps)
+            ref = oracle.norm_proj_fp8(x, w8[0][0], w8[0][1], call.eps)
         elif call.swiglu:
-            oracle.norm_proj_swiglu(x, inp.g, inp.W, inp.W_up, call.eps)
+            ref = oracle.norm_proj_swiglu(x, inp.g, inp.W, inp.W_up, call.eps)
         else:
-            oracle.norm_proj(x, inp.g, inp.W, call.eps)
+            ref = oracle.norm_proj(x, inp.g, inp.W, call.eps)
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -300,7 +301,22 @@ def cpu_baseline(call, inp, budget_s, metric_unit, fp8=False, q8=False, adaln=Fa
               f"{', E4M3 row-block output' if q8 else ''}{', AdaLN prologue' if adaln else ''}, float64, {el:.1f} s;"
               f" scaled by M/{rows}")
     return {"value": round(value, 4), "unit": metric_unit, "cores": cores, "kind": "oracle",
-            "sample": sample, "seconds_per_call": per_call, "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+            "sample": sample, "seconds_per_call": per_call, "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "_ref": ref}
+
+
+PARITY_ROWS = 512
+
+
+def parity_report(y_head, ref):
+    """The fused call's output against the oracle's on the sampled rows:
+    max |err| / (|ref| + 1) and mean |err| (the tests hold every output to
+    the tolerance; this reports the margin at the benchmarked size)."""
+    import numpy as np
+    n = min(y_head.shape[0], ref.shape[0])
+    err = np.abs(y_head[:n].astype(np.float64) - ref[:n])
+    return {"rows": int(n), "cols": int(ref.shape[1]), "max_err_rel": float(f"{(err / (np.abs(ref[:n]) + 1)).max():.3e}"),
+            "mean_abs_err": float(f"{err.mean():.3e}"), "reference": "float64 oracle, same seeded inputs"}
 
 
 # ---------------------------------------------------------- single calls --
@@ -383,6 +399,9 @@ def run_single(args, torch, fn, workloads):
     hot_ms = time_region(torch, lambda i: (proj_sw(x, Pg, Pu, eps, out=y) if call.swiglu
                                            else proj(x, Pg, eps, out=y)), args.steps, args.warmup)
     result = {"ms": ms, "blocks": blocks, "hot_ms": hot_ms, "rot": rot, "wbytes": wbytes}
+    if not q8:
+        torch.cuda.synchronize()
+        result["y_head"] = y[:PARITY_ROWS].float().cpu().numpy()   # the fused output's first rows, for the parity report
     if args.workload == "tiny":
         # launch-bound: the same call recorded TINY_STEP_CALLS times into one
         # step, replayed with one graph launch; reported per call
@@ -723,6 +742,9 @@ def measure(args, torch, fn, workloads):
         cb = cpu_baseline(cpu_call, cpu_inp, args.cpu_seconds, unit if unit != "us/call" else "us/call", fp8=fp8,
                           q8=q8, adaln=adaln, one_thread_s=getattr(args, "one_thread_s", 0.0))
         per_call = cb.pop("seconds_per_call")
+        ref = cb.pop("_ref", None)
+        if ref is not None and r.get("y_head") is not None:
+            out["parity"] = parity_report(r["y_head"], ref)
         if args.workload == "decode_step":
             # one head call sampled; scale to the whole step by algorithmic bytes
             step_s = per_call * bytes_step / (fp8_bytes(cpu_call) if fp8 else cpu_call.algorithmic_bytes())
