@@ -736,6 +736,10 @@ def measure(args, torch, fn, workloads):
             "fused_speedup_vs_own_chain": round(r["chain_own_ms"] / r["ms"], 3),
             "fused_speedup_vs_torch_chain": round(r["chain_torch_ms"] / r["ms"], 3),
         }
+    if args.no_cpu_baseline and getattr(args, "parity_only", False) and r.get("y_head") is not None:
+        cb = cpu_baseline(cpu_call, cpu_inp, 0.0, unit, fp8=fp8, q8=q8, adaln=adaln)
+        if cb.get("_ref") is not None:
+            out["parity"] = parity_report(r["y_head"], cb["_ref"])
     if not args.no_cpu_baseline:
         if cpu_inp is None:
             cpu_inp = workloads.make_inputs(cpu_call)
@@ -807,6 +811,7 @@ def main(argv=None):
         cargs.measured_peak = False
         if weights == "fp8":
             cargs.no_chain, cargs.no_cpu_baseline = True, True    # timing only; bf16 beside it in its own config
+            cargs.parity_only = True                              # one untimed oracle call for the parity report
         sub[name] = measure(cargs, torch, fn, workloads)
         torch.cuda.empty_cache()
 
