@@ -579,3 +579,29 @@ def test_adaln_q8_names_and_fp8(lib):
     assert f(*bad) == WORKSPACE
     assert f(None, None, None, None, None, None, None, None, None, None, None, 0, 16, 16, 2, 1e-6, None, 0,
              None) == OK
+
+
+def test_last_error_is_per_thread(lib):
+    """fn_last_error is thread-local: threads failing validation at the same
+    time each read their own message (the library is documented thread-safe
+    across streams; validation makes no HIP call, so this runs on the CPU)."""
+    import threading
+    errors = []
+    barrier = threading.Barrier(8)
+
+    def worker(k):
+        K = 8 * k + 4                       # not a multiple of 8: rejected with K in the message
+        barrier.wait()
+        for _ in range(200):
+            st = lib.fn_norm_proj(0x1000, 0x20000, 0x40000, 4, K, 16, 1e-6, BF16, None)
+            msg = lib.fn_last_error().decode()
+            if st != SHAPE or f"K={K}" not in msg:
+                errors.append((k, st, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(1, 9)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
