@@ -158,6 +158,27 @@ def test_nan_row_isolated(gpu_lib):
     assert_close(y[keep], ref[keep], "bf16", "rows beside a NaN row")
 
 
+@pytest.mark.parametrize("dtype,M,swiglu", [("bf16", 3, False), ("bf16", 40, True), ("bf16", 100, False),
+                                             ("bf16", 130, True), ("f32", 6, True)])
+def test_zero_row_eps0_and_inf_row_follow_the_formula(gpu_lib, dtype, M, swiglu):
+    """eps = 0 on an all-zero row: 1/RMS is 1/0 and the row's products are 0,
+    so every output of the row is NaN, as the formula (0/0) gives; an Inf in a
+    row makes that row's sum of squares Inf and its outputs NaN (Inf/Inf).
+    Every other row matches the oracle -- in each kernel family (register-x
+    decode, LDS-shared-x decode, prefill; SwiGLU and plain)."""
+    inp = W.random_inputs(M, 264, 70, dtype, seed=M + 31, swiglu=swiglu)
+    inp.x[1] = 0.0
+    inp.x[M - 1, 13] = np.inf
+    with np.errstate(invalid="ignore", divide="ignore"):
+        ref = reference(inp, eps=0.0)
+    assert np.all(np.isnan(ref[1])) and np.all(np.isnan(ref[M - 1]))
+    y = fused(gpu_lib, inp, 0.0)
+    assert np.all(np.isnan(y[1])), "zero row at eps = 0"
+    assert np.all(np.isnan(y[M - 1])), "row holding an Inf"
+    keep = [i for i in range(M) if i not in (1, M - 1)]
+    assert_close(y[keep], ref[keep], dtype, f"rows beside them, {dtype} M={M}")
+
+
 # ----------------------------------------------------------- invariants --
 def _fold_and_run(fn, x_np, g_np, W_np, dtype, eps):
     Wp = fn.fold_weights(to_dev(g_np, dtype), to_dev(W_np, dtype))
