@@ -125,17 +125,33 @@ def _torch():
     return torch
 
 
+_DTYPES = {}
+
+
 def _dt(dtype) -> int:
-    torch = _torch()
-    if dtype == torch.bfloat16:
-        return FN_BF16
-    if dtype == torch.float32:
-        return FN_F32
-    raise ValueError(f"dtype must be torch.bfloat16 or torch.float32, got {dtype}")
+    if not _DTYPES:
+        torch = _torch()
+        _DTYPES.update({torch.bfloat16: FN_BF16, torch.float32: FN_F32})
+    code = _DTYPES.get(dtype)
+    if code is None:
+        raise ValueError(f"dtype must be torch.bfloat16 or torch.float32, got {dtype}")
+    return code
+
+
+_raw_stream = None
 
 
 def _stream(t) -> int:
-    return _torch().cuda.current_stream(t.device).cuda_stream
+    """The current HIP stream of t's device, as an integer handle: torch's raw
+    getter when it has one (a tenth of the cost of building a Stream object
+    per call, which dominates a launch-bound call), else the public API."""
+    global _raw_stream
+    if _raw_stream is None:
+        torch = _torch()
+        getter = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _raw_stream = ((lambda d: getter(d.index)) if getter is not None
+                       else (lambda d: torch.cuda.current_stream(d).cuda_stream))
+    return _raw_stream(t.device)
 
 
 def _need_cuda(name, t):
