@@ -21,6 +21,10 @@
  *           library allocates nothing, frees nothing and never synchronises;
  *           each call enqueues its work on `stream` (0 = the null stream)
  *           and returns.  Results are ready when the stream reaches them.
+ *           Exceptions, each stated at its declaration: creating a recorded
+ *           or grouped step allocates (and copies its call table
+ *           synchronously), and fn_norm_proj_swiglu_adaln_static works in
+ *           the library's own static device array.
  * Layouts:  x[M,K], y[M,N], W[K,N] are dense row-major (leading dimensions
  *           K, N and N).  g[K] is a vector.  All tensors of one call share
  *           the storage dtype `dt`; y and out use it too.
@@ -48,7 +52,8 @@
  *           and h (the unfused helpers) need the alignment of their dtype.
  *           eps must be finite and >= 0.  An output may not overlap an input.
  * Threads:  the library holds no state between calls beyond the per-thread
- *           error text; calls on different streams may run concurrently.
+ *           error text (and the static array of the no-allocation call);
+ *           calls on different streams may run concurrently.
  */
 #ifndef FLASHNORM_H
 #define FLASHNORM_H
