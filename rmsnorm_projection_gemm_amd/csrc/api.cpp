@@ -895,8 +895,22 @@ bool outputs_overlap(std::vector<Span>& v) {
 }
 }  // namespace
 
+namespace {
+fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* out);
+}  // namespace
+
 fn_status fn_step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* out) {
   g_last_error[0] = '\0';
+  // host tables of up to 2^31 entries: allocation failure is a status, not an exception
+  try {
+    return step_create_grouped(calls, n_calls, out);
+  } catch (const std::bad_alloc&) {
+    return fail(FN_ERR_HIP, "grouped step: out of host memory");
+  }
+}
+
+namespace {
+fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* out) {
   if (out == nullptr) return fail(FN_ERR_NULL, "out is NULL");
   *out = nullptr;
   if (calls == nullptr) return fail(FN_ERR_NULL, "calls is NULL");
@@ -968,6 +982,7 @@ fn_status fn_step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step*
   *out = h;
   return FN_OK;
 }
+}  // namespace
 
 fn_status fn_step_launch(fn_step step, hipStream_t stream) {
   g_last_error[0] = '\0';
