@@ -525,16 +525,18 @@ typedef struct fn_step_s* fn_step;   /* opaque handle */
  * "call i: ..." in fn_last_error() and *out = NULL. */
 fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out);
 
-/* A step of independent calls run as ONE kernel launch: every column block
- * of every call is a workgroup of the same grid, in call order, so the
- * calls follow one another on the CUs with no drain and ramp between
- * kernels (a graph replay still runs one kernel per call, each ending in a
- * tail where CUs idle; [FlashNorm digest], summary bullets on the dozens
- * of norm launches per decode step; [Fused kernels] closing summary, item
- * 3).  Each block runs the one-wave whole-k decode tile: the same bits as
- * the call's own entry point where that entry point takes this tile too
- * (more than 256 column blocks for a projection, more than 512 for a SwiGLU
- * pair); narrower calls, which the entry point splits over k across waves,
+/* A step of independent calls run as ONE kernel launch: every pair of
+ * column blocks of every call is a workgroup of the same grid, in call
+ * order, so the calls follow one another on the CUs with no drain and ramp
+ * between kernels (a graph replay still runs one kernel per call, each
+ * ending in a tail where CUs idle; [FlashNorm digest], summary bullets on
+ * the dozens of norm launches per decode step; [Fused kernels] closing
+ * summary, item 3).  Each workgroup is one wave streaming the whole of k
+ * for its two column blocks (one x fragment load serves both): the same
+ * bits as the call's own entry point where that entry point also runs one
+ * wave over the whole of k (more than 256 column blocks for a projection,
+ * more than 512 for a SwiGLU pair); narrower calls, which the entry point
+ * splits over k across waves,
  * agree with it to the fp32 sum order.  Takes FN_CALL_NORM_PROJ and
  * FN_CALL_NORM_PROJ_SWIGLU calls with FN_BF16 and M <= 16 (FN_ERR_SHAPE
  * otherwise), 1 <= n_calls <= 65535; calls with M == 0 or N == 0 add
@@ -543,7 +545,7 @@ fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out);
  * writes: FN_ERR_ALIAS otherwise (a model's chained calls need the
  * recorded graph of fn_step_create).  Allocates host memory for the handle
  * and device memory for the call table (n_calls small records and two
- * bytes per column block), copied synchronously here; launching allocates
+ * bytes per workgroup), copied synchronously here; launching allocates
  * nothing. */
 fn_status fn_step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* out);
 

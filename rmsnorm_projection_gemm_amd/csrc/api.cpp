@@ -937,11 +937,11 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
     add(c.w_gate, wb, false);
     if (sw) add(c.w_up, wb, false);
     add(c.y, c.M * c.N * 2, true);
-    items += (c.N + 15) / 16;
+    items += ((c.N + 15) / 16 + fn::kGroupedBlocks - 1) / fn::kGroupedBlocks;
   }
   if (outputs_overlap(spans))
     return fail(FN_ERR_ALIAS, "a grouped step runs its calls at once: no call may write a buffer another call uses");
-  if (items > INT32_MAX) return fail(FN_ERR_SHAPE, "a grouped step holds at most 2^31-1 column blocks");
+  if (items > INT32_MAX) return fail(FN_ERR_SHAPE, "a grouped step holds at most 2^31-1 workgroups");
   const size_t rec = fn::grouped_call_bytes();
   std::vector<uint8_t> host_calls((size_t)n_calls * rec);
   std::vector<uint16_t> host_items((size_t)items);
@@ -952,7 +952,7 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
     fn::grouped_call_fill(host_calls.data() + (size_t)i * rec, c.x, c.w_gate, sw ? c.w_up : nullptr, c.y, (int)c.M,
                           (int)c.K, (int)c.N, c.eps, (int)first);
     if (c.M == 0 || c.N == 0) continue;
-    const int64_t nb = (c.N + 15) / 16;
+    const int64_t nb = ((c.N + 15) / 16 + fn::kGroupedBlocks - 1) / fn::kGroupedBlocks;   // workgroups of this call
     for (int64_t b = 0; b < nb; ++b) host_items[(size_t)(first + b)] = (uint16_t)i;
     first += nb;
   }

@@ -93,9 +93,11 @@ hipError_t launch_decode_premod(const FusedPlan& plan, const void* u, const floa
                                 const AdalnArgs& ad, hipStream_t stream);
 
 // Grouped launch of independent bf16 calls of at most 16 rows: one
-// workgroup per column block of every call.  calls: device array of
-// grouped_call_bytes() records (grouped_call_fill on the host, then copied);
-// item_call: device array [items] of uint16 call indices.
+// workgroup per kGroupedBlocks column blocks of every call.  calls: device
+// array of grouped_call_bytes() records (grouped_call_fill on the host,
+// then copied; first = the call's first workgroup); item_call: device array
+// [items] of uint16 call indices.
+constexpr int kGroupedBlocks = 2;
 size_t grouped_call_bytes();
 void grouped_call_fill(void* dst, const void* x, const void* wg, const void* wu, void* y, int M, int K, int N,
                        float eps, int first);
