@@ -508,20 +508,18 @@ def run_decode_step(args, torch, fn, workloads):
     graph_ms = time_region(torch, lambda _: step.launch(), args.steps, args.warmup)
     torch.cuda.synchronize()
     step.close()
-    # the calls are independent: one grouped launch runs them all (bf16)
-    grouped_ms = None
-    if not fp8:
-        gstep = fn.Step()
-        for it in items:
-            c = it["call"]
-            if c.swiglu:
-                gstep.norm_proj_swiglu(it["x"], it["Pg"], it["Pu"], it["y"], c.eps)
-            else:
-                gstep.norm_proj(it["x"], it["Pg"], it["y"], c.eps)
-        gstep.record(grouped=True)
-        grouped_ms = time_region(torch, lambda _: gstep.launch(), args.steps, args.warmup)
-        torch.cuda.synchronize()
-        gstep.close()
+    # the calls are independent: one grouped launch runs them all
+    gstep = fn.Step()
+    for it in items:
+        c = it["call"]
+        if c.swiglu:
+            (gstep.norm_proj_swiglu_fp8 if fp8 else gstep.norm_proj_swiglu)(it["x"], it["Pg"], it["Pu"], it["y"], c.eps)
+        else:
+            (gstep.norm_proj_fp8 if fp8 else gstep.norm_proj)(it["x"], it["Pg"], it["y"], c.eps)
+    gstep.record(grouped=True)
+    grouped_ms = time_region(torch, lambda _: gstep.launch(), args.steps, args.warmup)
+    torch.cuda.synchronize()
+    gstep.close()
     result = {"ms": ms, "blocks": blocks, "hot_ms": None, "rot": 1, "graph_ms": graph_ms, "grouped_ms": grouped_ms,
               "wbytes": sum((it["Pg"].data.numel() + (it["Pg"].scales.numel() * 4 if fp8 else 0)) * it["call"].mats
                             for it in items)}

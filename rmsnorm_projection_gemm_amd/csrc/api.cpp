@@ -426,6 +426,7 @@ struct fn_step_s {
   void* items = nullptr;   // grouped: the call of each workgroup (device)
   int64_t nitems = 0;      // grouped: workgroups of the one launch
   bool grouped = false;
+  bool fp8 = false;        // grouped: the calls take fp8 weights
 };
 
 namespace fn {
@@ -917,18 +918,25 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
   if (n_calls < 1 || n_calls > 65535) return fail(FN_ERR_SHAPE, "n_calls=%lld must be in [1, 65535]", (long long)n_calls);
   std::vector<Span> spans;
   int64_t items = 0;
+  const bool f8 = calls[0].kind == FN_CALL_NORM_PROJ_FP8 || calls[0].kind == FN_CALL_NORM_PROJ_SWIGLU_FP8;
   for (int64_t i = 0; i < n_calls; ++i) {
     const fn_call& c = calls[i];
     const fn_status s = run_call(c, nullptr, true);
     if (s != FN_OK) return call_failed(s, i);
-    if (c.kind != FN_CALL_NORM_PROJ && c.kind != FN_CALL_NORM_PROJ_SWIGLU)
-      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes fn_norm_proj and fn_norm_proj_swiglu calls"), i);
-    if (c.dt != FN_BF16 || c.M > 16)
-      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes bf16 calls of at most 16 rows (M=%lld)",
+    const bool bf = c.kind == FN_CALL_NORM_PROJ || c.kind == FN_CALL_NORM_PROJ_SWIGLU;
+    const bool c8 = c.kind == FN_CALL_NORM_PROJ_FP8 || c.kind == FN_CALL_NORM_PROJ_SWIGLU_FP8;
+    if (!bf && !c8)
+      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes fn_norm_proj, fn_norm_proj_swiglu and their fp8 "
+                                            "forms"), i);
+    if (c8 != f8)
+      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes calls of one weight type (all bf16 or all fp8)"),
+                         i);
+    if ((bf && c.dt != FN_BF16) || c.M > 16)
+      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes bf16 activations of at most 16 rows (M=%lld)",
                               (long long)c.M), i);
     if (c.M == 0 || c.N == 0) continue;
-    const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU;
-    const int64_t wb = packed_bytes(c.K, c.N, FN_BF16);
+    const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU || c.kind == FN_CALL_NORM_PROJ_SWIGLU_FP8;
+    const int64_t wb = f8 ? packed_fp8_bytes(c.K, c.N) : packed_bytes(c.K, c.N, FN_BF16);
     auto add = [&](const void* p, int64_t bytes, bool o) {
       const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
       spans.push_back(Span{lo, lo + (uintptr_t)bytes, o, i});
@@ -936,8 +944,13 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
     add(c.x, c.M * c.K * 2, false);
     add(c.w_gate, wb, false);
     if (sw) add(c.w_up, wb, false);
+    if (f8) {
+      add(c.s_gate, c.N * 4, false);
+      if (sw) add(c.s_up, c.N * 4, false);
+    }
     add(c.y, c.M * c.N * 2, true);
-    items += ((c.N + 15) / 16 + fn::kGroupedBlocks - 1) / fn::kGroupedBlocks;
+    const int per = fn::grouped_blocks(f8, sw);
+    items += ((c.N + 15) / 16 + per - 1) / per;
   }
   if (outputs_overlap(spans))
     return fail(FN_ERR_ALIAS, "a grouped step runs its calls at once: no call may write a buffer another call uses");
@@ -948,17 +961,20 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
   int64_t first = 0;
   for (int64_t i = 0; i < n_calls; ++i) {
     const fn_call& c = calls[i];
-    const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU;
-    fn::grouped_call_fill(host_calls.data() + (size_t)i * rec, c.x, c.w_gate, sw ? c.w_up : nullptr, c.y, (int)c.M,
-                          (int)c.K, (int)c.N, c.eps, (int)first);
+    const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU || c.kind == FN_CALL_NORM_PROJ_SWIGLU_FP8;
+    fn::grouped_call_fill(host_calls.data() + (size_t)i * rec, c.x, c.w_gate, sw ? c.w_up : nullptr,
+                          f8 ? c.s_gate : nullptr, f8 && sw ? c.s_up : nullptr, c.y, (int)c.M, (int)c.K, (int)c.N,
+                          c.eps, (int)first);
     if (c.M == 0 || c.N == 0) continue;
-    const int64_t nb = ((c.N + 15) / 16 + fn::kGroupedBlocks - 1) / fn::kGroupedBlocks;   // workgroups of this call
+    const int per = fn::grouped_blocks(f8, sw);
+    const int64_t nb = ((c.N + 15) / 16 + per - 1) / per;   // workgroups of this call
     for (int64_t b = 0; b < nb; ++b) host_items[(size_t)(first + b)] = (uint16_t)i;
     first += nb;
   }
   fn_step h = new (std::nothrow) fn_step_s;
   if (h == nullptr) return fail(FN_ERR_HIP, "step: out of host memory");
   h->grouped = true;
+  h->fp8 = f8;
   if (items == 0) {   // every call empty: the step launches nothing
     *out = h;
     return FN_OK;
@@ -989,7 +1005,8 @@ fn_status fn_step_launch(fn_step step, hipStream_t stream) {
   if (step == nullptr) return fail(FN_ERR_NULL, "step is NULL");
   if (step->grouped)
     return step->nitems == 0 ? FN_OK
-                             : hip_status(fn::launch_decode_grouped(step->calls, step->items, (int)step->nitems, stream),
+                             : hip_status(fn::launch_decode_grouped(step->calls, step->items, (int)step->nitems,
+                                                                    step->fp8, stream),
                                           "grouped step: launch");
   return hip_status(hipGraphLaunch(step->exec, stream), "step: launch");
 }

@@ -92,16 +92,23 @@ hipError_t launch_decode_premod(const FusedPlan& plan, const void* u, const floa
                                 const float* sg, const void* wu, const float* su, void* y, int M, int K, int N,
                                 const AdalnArgs& ad, hipStream_t stream);
 
-// Grouped launch of independent bf16 calls of at most 16 rows: one
-// workgroup per kGroupedBlocks column blocks of every call.  calls: device
-// array of grouped_call_bytes() records (grouped_call_fill on the host,
-// then copied; first = the call's first workgroup); item_call: device array
-// [items] of uint16 call indices.
-constexpr int kGroupedBlocks = 2;
+// Grouped launch of independent calls of at most 16 rows, all with bf16
+// weights or all with fp8 weights (sg, su: column scales): one one-wave
+// workgroup per grouped_blocks() column blocks of every call.  calls:
+// device array of grouped_call_bytes() records (grouped_call_fill on the
+// host, then copied; first = the call's first workgroup); item_call: device
+// array [items] of uint16 call indices.
+constexpr int kGroupedBlocks = 2;            // bf16 weights
+constexpr int kGroupedBlocksFp8 = 2;         // fp8 weights, projection
+constexpr int kGroupedBlocksFp8Swiglu = 2;   // fp8 weights, gate/up pair
+constexpr int kGroupedPairsFp8 = 4;          // fp8: k-block pairs per stage
+inline int grouped_blocks(bool fp8, bool swiglu) {
+  return fp8 ? (swiglu ? kGroupedBlocksFp8Swiglu : kGroupedBlocksFp8) : kGroupedBlocks;
+}
 size_t grouped_call_bytes();
-void grouped_call_fill(void* dst, const void* x, const void* wg, const void* wu, void* y, int M, int K, int N,
-                       float eps, int first);
-hipError_t launch_decode_grouped(const void* calls, const void* item_call, int items, hipStream_t stream);
+void grouped_call_fill(void* dst, const void* x, const void* wg, const void* wu, const float* sg, const float* su,
+                       void* y, int M, int K, int N, float eps, int first);
+hipError_t launch_decode_grouped(const void* calls, const void* item_call, int items, bool fp8, hipStream_t stream);
 
 hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
                        int K, int N, hipStream_t stream);

@@ -288,12 +288,17 @@ def test_grouped_step_validates_before_any_hip_call(lib):
     # allocated (no HIP call is possible without a GPU)
     st, h = _create_grouped(lib, [_call(), _call(K=12)])
     assert st == SHAPE and h.value is None and lib.fn_last_error().decode().startswith("call 1: K=12")
-    st, _ = _create_grouped(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_FP8, sg=0x30000)])
-    assert st == SHAPE and "grouped step takes fn_norm_proj" in lib.fn_last_error().decode()
+    st, _ = _create_grouped(lib, [_call(), _call(kind=fn.FN_CALL_NORM_PROJ_FP8, x=0x2000, sg=0x30000, y=0x50000)])
+    assert st == SHAPE and lib.fn_last_error().decode().startswith("call 1: a grouped step takes calls of one weight")
+    st, _ = _create_grouped(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_FP8, sg=0x30000), _call(x=0x2000, y=0x50000)])
+    assert st == SHAPE and "one weight type" in lib.fn_last_error().decode()
     st, _ = _create_grouped(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_SWIGLU_Q8, wu=0x30000, ys=0x50000)])
-    assert st == SHAPE
+    assert st == SHAPE and "their fp8 forms" in lib.fn_last_error().decode()
     st, _ = _create_grouped(lib, [_call(dt=F32)])
-    assert st == SHAPE and "bf16 calls of at most 16 rows" in lib.fn_last_error().decode()
+    assert st == SHAPE and "bf16 activations of at most 16 rows" in lib.fn_last_error().decode()
+    st, _ = _create_grouped(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_SWIGLU_FP8, wu=0x30000, sg=0x50000, su=0x60000,
+                                        M=17)])
+    assert st == SHAPE and "M=17" in lib.fn_last_error().decode()
     st, _ = _create_grouped(lib, [_call(M=17)])
     assert st == SHAPE and "M=17" in lib.fn_last_error().decode()
     st, _ = _create_grouped(lib, [])
@@ -321,6 +326,14 @@ def test_grouped_step_rejects_calls_that_share_a_written_buffer(lib):
                                   _call(x=0x1100, wg=0x30000, y=0x3000, M=4, K=16, N=16),
                                   _call(x=0x2800, wg=0xb0000, y=0xc0000)])
     assert st == ALIAS
+    # fp8 calls: the column scales are inputs too (16 columns: 64 B)
+    f8 = fn.FN_CALL_NORM_PROJ_FP8
+    st, _ = _create_grouped(lib, [_call(kind=f8, sg=0x30000, M=0),
+                                  _call(kind=f8, x=0x2000, sg=0x30000, y=0x50000, M=0)])
+    assert st == OK                                                         # shared scales, both read
+    st, _ = _create_grouped(lib, [_call(kind=f8, sg=0x30000),
+                                  _call(kind=f8, x=0x2000, wg=0x60000, sg=0x70000, y=0x30020)])
+    assert st == ALIAS and "at once" in lib.fn_last_error().decode()      # call 1 writes call 0's scales
 
 
 def test_grouped_step_of_empty_calls_launches_nothing(lib):

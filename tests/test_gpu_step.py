@@ -3,9 +3,10 @@ calls replayed with one HIP graph launch gives bit for bit what the same
 calls give launched one by one, on every replay, with inputs refreshed in
 place between replays; calls run in order, so a later call reads an earlier
 call's output; and the replay agrees with the float64 oracle.  A grouped
-step (fn_step_create_grouped) runs independent calls as one launch: the
-same bits as the eager calls that take the same tile, the oracle's values
-within tolerance for every call."""
+step (fn_step_create_grouped) runs independent calls as one launch: with
+bf16 weights the same bits as the eager calls that take the same tile, with
+fp8 weights the eager outputs up to the order of the sum of squares, and the
+oracle's values within tolerance for every call."""
 import numpy as np
 import pytest
 
@@ -257,6 +258,97 @@ def test_grouped_ragged_calls_agree_with_oracle(gpu_lib, seed):
     torch.cuda.synchronize()
     for (out, _r, shape), f in zip(cases, first):
         assert torch.equal(out.view(torch.int16), f.view(torch.int16)), f"second replay differs: {shape}"
+    st.close()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_grouped_fp8_ragged_calls_agree_with_oracle(gpu_lib, seed):
+    """fp8-weight calls in one grouped launch -- one row up to sixteen, K from
+    8 to 4104 (odd counts of k-blocks, so a last pair with one k-block, and
+    K % 32 != 0), N from 1 to 1100, an empty call between them -- each
+    against the float64 oracle on the codes and scales of the oracle's own
+    fold; a second replay gives the first's bits."""
+    import torch
+    fn = gpu_lib
+    shapes = [(1, 8, 1, False), (16, 4104, 1100, True), (3, 264, 37, False), (0, 64, 32, True),
+              (7, 1032, 270, True), (16, 520, 16, False), (9, 40, 600, False), (12, 2056, 33, True),
+              (16, 4096, 530, False), (5, 136, 17, True), (8, 96, 70, False), (2, 4096, 3000, False)]
+    st = fn.Step()
+    cases = []
+    for i, (M, K, N, sw) in enumerate(shapes):
+        inp = W.random_inputs(M, K, N, "bf16", seed=700 + 20 * seed + i, swiglu=sw)
+        x = to_dev(inp.x, "bf16")
+        Pg = fn.fold_weights_fp8(to_dev(inp.g, "bf16"), to_dev(inp.W, "bf16"))
+        cg, sg = oracle.fold_weights_fp8(inp.g, inp.W, "bf16")
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if sw:
+            Pu = fn.fold_weights_fp8(to_dev(inp.g, "bf16"), to_dev(inp.W_up, "bf16"))
+            cu, su = oracle.fold_weights_fp8(inp.g, inp.W_up, "bf16")
+            st.norm_proj_swiglu_fp8(x, Pg, Pu, out, 1e-6)
+            ref = oracle.norm_proj_swiglu_fp8(inp.x, cg, sg, cu, su, 1e-6)
+        else:
+            st.norm_proj_fp8(x, Pg, out, 1e-6)
+            ref = oracle.norm_proj_fp8(inp.x, cg, sg, 1e-6)
+        cases.append((out, ref, (M, K, N, sw)))
+    st.record(grouped=True)
+    assert st.num_kernels == 1
+    st.launch()
+    torch.cuda.synchronize()
+    first = [out.clone() for out, _r, _s in cases]
+    for out, ref, shape in cases:
+        assert_close(to_f64(out), ref, "bf16", f"grouped fp8 call {shape}")
+        out.fill_(float("nan"))
+    st.launch()
+    torch.cuda.synchronize()
+    for (out, _r, shape), f in zip(cases, first):
+        assert torch.equal(out.view(torch.int16), f.view(torch.int16)), f"second replay differs: {shape}"
+    st.close()
+
+
+def test_grouped_fp8_decode_step_agrees_with_eager(gpu_lib):
+    """Four layers and the head with fp8 weights as ONE grouped launch, on
+    three replays with the inputs refreshed in place: each output against
+    the eager call's.  The products follow the same k order; only the sum of
+    squares is added in another order (one chain over k here, per-wave
+    partials in the eager kernel), so 1/RMS may differ in its last fp32 bit
+    and an output by at most one bf16 step, rarely."""
+    import torch
+    fn = gpu_lib
+    calls = W.decode_step_calls(4)
+    st = fn.Step()
+    items = []
+    for c in calls:
+        x, g, Wm, Wu = W.make_inputs_device(c)
+        Pg = fn.fold_weights_fp8(g, Wm)
+        Pu = fn.fold_weights_fp8(g, Wu) if c.swiglu else None
+        out = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+        if c.swiglu:
+            st.norm_proj_swiglu_fp8(x, Pg, Pu, out, c.eps)
+        else:
+            st.norm_proj_fp8(x, Pg, out, c.eps)
+        items.append((x, Pg, Pu, out, c))
+        del Wm, Wu
+    st.record(grouped=True)
+    assert st.num_kernels == 1
+    gen = torch.Generator(device="cuda")
+    for replay in range(3):
+        if replay:
+            gen.manual_seed(500 + replay)
+            for x, *_r in items:
+                x.copy_(torch.randn(x.shape, generator=gen, device="cuda").to(x.dtype))
+        for *_r, out, _c in items:
+            out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        st.launch()
+        torch.cuda.synchronize()
+        for x, Pg, Pu, out, c in items:
+            want = fn.norm_proj_swiglu_fp8(x, Pg, Pu, c.eps) if c.swiglu else fn.norm_proj_fp8(x, Pg, c.eps)
+            torch.cuda.synchronize()
+            a, b = out.double(), want.double()
+            assert bool(torch.isfinite(a).all()), f"replay {replay}: {c.name} not finite"
+            same = float((out.view(torch.int16) == want.view(torch.int16)).double().mean())
+            assert same >= 0.999, f"replay {replay}: {c.name}: {same:.5f} of the outputs identical"
+            assert bool(((a - b).abs() <= b.abs() * 2.0 ** -7 + 1e-30).all()), f"replay {replay}: {c.name}"
     st.close()
 
 
