@@ -336,6 +336,55 @@ def test_grouped_step_rejects_calls_that_share_a_written_buffer(lib):
     assert st == ALIAS and "at once" in lib.fn_last_error().decode()      # call 1 writes call 0's scales
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_grouped_overlap_check_matches_brute_force(lib, fp8):
+    """Random groups of individually valid calls packed into a small address
+    range: the grouped step refuses them (FN_ERR_ALIAS) exactly when some
+    output of one call overlaps a buffer of another call, which a pairwise
+    comparison decides here.  Groups it accepts go on to allocate their
+    table (FN_ERR_HIP without a GPU, FN_OK with one)."""
+    import random
+    rng = random.Random(17 + fp8)
+    HIP = 7
+    base, arena = 0x100000, 1 << 16
+
+    def packed(K, N):
+        return (N + 15) // 16 * ((K + 63) // 64 if fp8 else (K + 31) // 32) * 1024
+
+    def hit(a, b):
+        return a[0] < b[0] + b[1] and b[0] < a[0] + a[1]
+
+    seen = {True: 0, False: 0}
+    for trial in range(400):
+        calls, spans = [], []
+        for i in range(rng.randint(2, 5)):
+            sw = rng.random() < 0.5
+            M, K, N = rng.randint(1, 16), 8 * rng.randint(1, 12), rng.randint(1, 40)
+            while True:
+                at = lambda: base + 16 * rng.randrange(arena // 16)
+                x, wg, wu, sg, su, y = at(), at(), at(), at(), at(), at()
+                ins = [(x, M * K * 2), (wg, packed(K, N))] + ([(wu, packed(K, N))] if sw else [])
+                if fp8:
+                    ins += [(sg, N * 4)] + ([(su, N * 4)] if sw else [])
+                out = (y, M * N * 2)
+                if not any(hit(out, b) for b in ins):   # each call valid on its own
+                    break
+            kind = ((fn.FN_CALL_NORM_PROJ_SWIGLU_FP8 if sw else fn.FN_CALL_NORM_PROJ_FP8) if fp8 else
+                    (fn.FN_CALL_NORM_PROJ_SWIGLU if sw else fn.FN_CALL_NORM_PROJ))
+            calls.append(_call(kind=kind, x=x, wg=wg, wu=wu if sw else None, sg=sg if fp8 else None,
+                               su=su if fp8 and sw else None, y=y, M=M, K=K, N=N))
+            spans.append((ins, out))
+        conflict = any(hit(spans[i][1], b) for i in range(len(spans)) for j in range(len(spans)) if i != j
+                       for b in spans[j][0] + [spans[j][1]])
+        st, h = _create_grouped(lib, calls)
+        if st == OK:
+            assert lib.fn_step_destroy(h) == OK
+        assert (st == ALIAS) == conflict, (trial, st, lib.fn_last_error())
+        assert st in (ALIAS, OK, HIP), (trial, st, lib.fn_last_error())
+        seen[conflict] += 1
+    assert min(seen.values()) >= 40, seen   # both outcomes well represented
+
+
 def test_grouped_step_of_empty_calls_launches_nothing(lib):
     st, h = _create_grouped(lib, [_call(M=0), _call(N=0, kind=fn.FN_CALL_NORM_PROJ_SWIGLU, wu=0x30000)])
     assert st == OK and h.value is not None
