@@ -348,20 +348,6 @@ __global__ __launch_bounds__(kWave) void decode_grouped_kernel(const GroupCall* 
     decode_tile<__bf16, 1, kGroupedBlocks, false, 1, 1, 4>(g.a, nb, 0);
 }
 
-// 16 E4M3 codes (a lane's chunk of a k-block pair) -> its two bf16 B
-// operands, bytes 0..7 for the first k-block and 8..15 for the second;
-// v_cvt_scalef32_pk_bf16_fp8 with scale 1 decodes two codes exactly (every
-// E4M3 value is a bf16 value).
-__device__ inline void e4m3_pair_to_bf16(u32x4 w, u32x4& lo, u32x4& hi) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    lo[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
-    lo[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
-    hi[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, false));
-    hi[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, true));
-  }
-}
-
 // The grouped tile for fp8 (E4M3) weights with column scales and bf16 x of
 // at most 16 rows: one wave streams the whole of k for NF column blocks
 // (each with its gate and up streams for SwiGLU), x in registers.  The
@@ -424,7 +410,7 @@ __device__ __forceinline__ void decode_tile_fp8(const DecodeArgs& a, const float
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int nf = 0; nf < NF; ++nf) e4m3_pair_to_bf16(w[m][nf], lo[m][nf], hi[m][nf]);
+      for (int nf = 0; nf < NF; ++nf) e4m3x16_to_bf16(w[m][nf], lo[m][nf], hi[m][nf]);
     gram = mfma_chunk<__bf16>(x0, x0, gram);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)

@@ -81,20 +81,6 @@ __device__ inline void wait_vmcnt_x() {
 
 constexpr uint32_t kOutOfRangeX = 0x80000000u;
 
-// 16 E4M3 codes (one 16-byte fp8 lane chunk) -> the lane's two bf16 B
-// operands: bytes 0..7 for the first k-block of the pair, 8..15 for the
-// second.  v_cvt_scalef32_pk_bf16_fp8 with scale 1 decodes two codes into
-// two bf16 exactly.
-__device__ inline void decode_e4m3x16(u32x4 w, u32x4& lo, u32x4& hi) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    lo[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
-    lo[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
-    hi[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, false));
-    hi[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, true));
-  }
-}
-
 // MF: 16-row blocks of x.  NC: 16-column blocks per wave (for SwiGLU each
 // with its gate and up stream).  NWV: waves, sharing the x fragments.  U:
 // k-blocks per stage.  F8: E4M3 weights.  Q8: E4M3 output with row-block
@@ -384,7 +370,7 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
     for (int c = 0; c < NST; ++c) {
       if constexpr (F8) {
 #pragma unroll
-        for (int p = 0; p < U / 2; ++p) decode_e4m3x16(wv[s][p][c], bw[2 * p][c], bw[2 * p + 1][c]);
+        for (int p = 0; p < U / 2; ++p) e4m3x16_to_bf16(wv[s][p][c], bw[2 * p][c], bw[2 * p + 1][c]);
       } else {
 #pragma unroll
         for (int u = 0; u < U; ++u) bw[u][c] = wv[s][u][c];

@@ -165,6 +165,21 @@ __device__ inline uint32_t e4m3_rne(float v) {
   return (a != a) ? 0x7Fu : (sign | code);
 }
 
+// 16 E4M3 codes (one 16-byte lane chunk of the packed fp8 weights: the
+// lane's 8 codes of each k-block of a pair) -> the lane's two bf16 B
+// operands, bytes 0..7 for the first k-block and 8..15 for the second.
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1 decodes two codes into two bf16
+// exactly (every E4M3 value is a bf16 value).
+__device__ inline void e4m3x16_to_bf16(u32x4 w, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    lo[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+    lo[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+    hi[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, false));
+    hi[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, true));
+  }
+}
+
 // Lane permutation inside each 16-lane row of the wave (DPP, no LDS).
 template <int CTRL>
 __device__ inline float dpp_move(float v) {
