@@ -80,8 +80,9 @@ def parse_args(argv=None):
 CONFIG_CHOICES = {"tiny": ("tiny", "native"), "qkv_decode": ("qkv_decode", "native"),
                   "ffn_decode": ("ffn_decode", "native"), "prefill_qkv": ("prefill_qkv", "native"),
                   "decode_step": ("decode_step", "native"), "qkv_decode_fp8": ("qkv_decode", "fp8"),
-                  "ffn_decode_fp8": ("ffn_decode", "fp8")}
-DEFAULT_CONFIGS = ("tiny", "ffn_decode", "prefill_qkv", "decode_step", "qkv_decode_fp8", "ffn_decode_fp8")
+                  "ffn_decode_fp8": ("ffn_decode", "fp8"), "decode_step_fp8": ("decode_step", "fp8")}
+DEFAULT_CONFIGS = ("tiny", "ffn_decode", "prefill_qkv", "decode_step", "qkv_decode_fp8", "ffn_decode_fp8",
+                   "decode_step_fp8")
 # steps and warmup of a config run: the headline's, capped where one step is long
 CONFIG_STEP_CAP = {"prefill_qkv": (50, 5), "decode_step": (20, 3)}
 
