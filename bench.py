@@ -50,6 +50,8 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qkv_decode",
                    choices=["tiny", "qkv_decode", "ffn_decode", "prefill_qkv", "decode_step"])
+    p.add_argument("--step-rows", type=int, default=8,
+                   help="decode_step: rows of every call (1..64; the step is quoted at 8)")
     p.add_argument("--weights", default="native", choices=["native", "fp8"],
                    help="weight storage: the activations' dtype, or E4M3 codes with per-column scales "
                         "(bf16 decode workloads only)")
@@ -470,7 +472,7 @@ def run_single(args, torch, fn, workloads):
 
 
 def run_decode_step(args, torch, fn, workloads):
-    calls = workloads.decode_step_calls()
+    calls = workloads.decode_step_calls(rows=getattr(args, "step_rows", 8))
     items = []
     fp8 = args.weights == "fp8"
     fold = fn.fold_weights_fp8 if fp8 else fn.fold_weights
@@ -629,14 +631,18 @@ def measure(args, torch, fn, workloads):
         calls, r = run_decode_step(args, torch, fn, workloads)
         bytes_step = sum((fp8_bytes(c) if fp8 else c.algorithmic_bytes()) for c in calls)
         flops_step = sum(c.flops() for c in calls)
-        name = "32-layer decode step, M=8: 32 x (norm+QKV 4096->12288, norm+gate/up SwiGLU 4096->2x11008) + norm+head 4096->32000"
-        config = {"workload": name, "calls_per_step": len(calls), "M": 8, "K": 4096,
+        rows = calls[0].M
+        name = (f"32-layer decode step, M={rows}: 32 x (norm+QKV 4096->12288, norm+gate/up SwiGLU 4096->2x11008) + "
+                "norm+head 4096->32000")
+        config = {"workload": name, "calls_per_step": len(calls), "M": rows, "K": 4096,
                   "weights_bytes": r["wbytes"], "cache": "cold (9.3 GB of distinct weights per step)"}
-        kernel = fn.kernel_name_fp8(8, 4096, 12288, False) if fp8 else fn.kernel_name(8, 4096, 12288, False, torch.bfloat16)
+        kernel = (fn.kernel_name_fp8(rows, 4096, 12288, False) if fp8 else
+                  fn.kernel_name(rows, 4096, 12288, False, torch.bfloat16))
         cpu_call, cpu_inp = calls[-1], None
         unit = "GB/s"
         work = bytes_step
-        roof = {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": counter_traffic("decode_step" + suffix)}
+        roof = {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "traffic": counter_traffic("decode_step" + suffix) if rows == 8 else None}
         dtype = "bf16"
         per_unit = {"algorithmic_bytes_per_step": bytes_step, "flops_per_step": flops_step}
     else:
@@ -786,6 +792,9 @@ def main(argv=None):
     adaln = args.prologue == "adaln"
     if adaln and args.workload not in ("qkv_decode", "ffn_decode", "prefill_qkv"):
         print("bench.py: --prologue adaln applies to qkv_decode, ffn_decode and prefill_qkv", file=sys.stderr)
+        return 2
+    if not 1 <= args.step_rows <= 64:
+        print("bench.py: --step-rows must be in 1..64", file=sys.stderr)
         return 2
     configs = [] if args.configs.strip() in ("", "none") else [c.strip() for c in args.configs.split(",")]
     bad = [c for c in configs if c not in CONFIG_CHOICES]

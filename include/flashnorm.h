@@ -525,30 +525,35 @@ typedef struct fn_step_s* fn_step;   /* opaque handle */
  * "call i: ..." in fn_last_error() and *out = NULL. */
 fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out);
 
-/* A step of independent calls run as ONE kernel launch: every pair of
- * column blocks of every call is a workgroup of the same grid, in call
- * order, so the calls follow one another on the CUs with no drain and ramp
- * between kernels (a graph replay still runs one kernel per call, each
- * ending in a tail where CUs idle; [FlashNorm digest], summary bullets on
- * the dozens of norm launches per decode step; [Fused kernels] closing
- * summary, item 3).  Each workgroup is one wave streaming the whole of k
- * for its two column blocks (one x fragment load serves both).  bf16
- * weights: the same bits as the call's own entry point where that entry
- * point also runs one wave over the whole of k (more than 256 column blocks
- * for a projection, more than 512 for a SwiGLU pair); narrower calls, which
- * the entry point splits over k across waves, agree with it to the fp32
- * sum order.  fp8 weights: the products in the entry point's k order, the
- * sum of squares as one chain over k (the entry point adds per-wave
+/* A step of independent calls run as ONE kernel launch: the column blocks
+ * of every call are the workgroups of the same grid, in call order, so the
+ * calls follow one another on the CUs with no drain and ramp between
+ * kernels (a graph replay still runs one kernel per call, each ending in a
+ * tail where CUs idle; [FlashNorm digest], summary bullets on the dozens of
+ * norm launches per decode step; [Fused kernels] closing summary, item 3).
+ * When every call has at most 16 rows, each workgroup
+ * is one wave streaming the whole of k for two column blocks of its call,
+ * x in registers (one x fragment load serves both); when some call has
+ * 17..64 rows, every call runs in workgroups of twelve waves, one column
+ * block each, sharing x through LDS (the entry point's 17..64-row kernel
+ * with more column blocks per workgroup than a single call could fill the
+ * GPU with).  The products follow the entry point's k order.  bf16 weights
+ * up to 16 rows: the same bits as the call's own entry point where that
+ * entry point also runs one wave over the whole of k (more than 256 column
+ * blocks for a projection, more than 512 for a SwiGLU pair); narrower
+ * calls, which the entry point splits over k across waves, agree with it
+ * to the fp32 sum order.  Otherwise the sum of squares may be added in
+ * another order than in the entry point (one chain, or other per-wave
  * partials), so an output can differ from the entry point's by one bf16
  * rounding step, rarely.  Takes FN_CALL_NORM_PROJ and
  * FN_CALL_NORM_PROJ_SWIGLU calls with FN_BF16, or FN_CALL_NORM_PROJ_FP8 and
  * FN_CALL_NORM_PROJ_SWIGLU_FP8 calls, all of one weight type, each with
- * M <= 16 (FN_ERR_SHAPE otherwise), 1 <= n_calls <= 65535; calls with
+ * M <= 64 (FN_ERR_SHAPE otherwise), 1 <= n_calls <= 65535; calls with
  * M == 0 or N == 0 add nothing (a step of only such calls launches
  * nothing).  The calls run at the same time, so no call may write a buffer
  * another call reads or writes (column scales included): FN_ERR_ALIAS
- * otherwise (a model's chained calls need the
- * recorded graph of fn_step_create).  Allocates host memory for the handle
+ * otherwise (a model's chained calls need the recorded graph of
+ * fn_step_create).  Allocates host memory for the handle
  * and device memory for the call table (n_calls small records and two
  * bytes per workgroup), copied synchronously here; launching allocates
  * nothing. */

@@ -427,6 +427,7 @@ struct fn_step_s {
   int64_t nitems = 0;      // grouped: workgroups of the one launch
   bool grouped = false;
   bool fp8 = false;        // grouped: the calls take fp8 weights
+  bool wide = false;       // grouped: some call has more than 16 rows (the LDS-shared-x tile)
 };
 
 namespace fn {
@@ -931,8 +932,8 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
     if (c8 != f8)
       return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes calls of one weight type (all bf16 or all fp8)"),
                          i);
-    if ((bf && c.dt != FN_BF16) || c.M > 16)
-      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes bf16 activations of at most 16 rows (M=%lld)",
+    if ((bf && c.dt != FN_BF16) || c.M > 64)
+      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes bf16 activations of at most 64 rows (M=%lld)",
                               (long long)c.M), i);
     if (c.M == 0 || c.N == 0) continue;
     const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU || c.kind == FN_CALL_NORM_PROJ_SWIGLU_FP8;
@@ -949,24 +950,35 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
       if (sw) add(c.s_up, c.N * 4, false);
     }
     add(c.y, c.M * c.N * 2, true);
-    const int per = fn::grouped_blocks(f8, sw);
-    items += ((c.N + 15) / 16 + per - 1) / per;
+  }
+  // up to 16 rows in every call: the one-wave register-x tiles; else every
+  // call takes the LDS-shared-x tile of 64 rows
+  bool wide = false;
+  for (int64_t i = 0; i < n_calls; ++i) wide = wide || (calls[i].N > 0 && calls[i].M > 16);
+  auto per_item = [&](const fn_call& c) {
+    const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU || c.kind == FN_CALL_NORM_PROJ_SWIGLU_FP8;
+    return wide ? fn::kGroupedXBlocks : fn::grouped_blocks(f8, sw);
+  };
+  for (int64_t i = 0; i < n_calls; ++i) {
+    const fn_call& c = calls[i];
+    if (c.M == 0 || c.N == 0) continue;
+    items += ((c.N + 15) / 16 + per_item(c) - 1) / per_item(c);
   }
   if (outputs_overlap(spans))
     return fail(FN_ERR_ALIAS, "a grouped step runs its calls at once: no call may write a buffer another call uses");
   if (items > INT32_MAX) return fail(FN_ERR_SHAPE, "a grouped step holds at most 2^31-1 workgroups");
-  const size_t rec = fn::grouped_call_bytes();
+  const size_t rec = wide ? fn::grouped_x_call_bytes() : fn::grouped_call_bytes();
   std::vector<uint8_t> host_calls((size_t)n_calls * rec);
   std::vector<uint16_t> host_items((size_t)items);
   int64_t first = 0;
   for (int64_t i = 0; i < n_calls; ++i) {
     const fn_call& c = calls[i];
     const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU || c.kind == FN_CALL_NORM_PROJ_SWIGLU_FP8;
-    fn::grouped_call_fill(host_calls.data() + (size_t)i * rec, c.x, c.w_gate, sw ? c.w_up : nullptr,
-                          f8 ? c.s_gate : nullptr, f8 && sw ? c.s_up : nullptr, c.y, (int)c.M, (int)c.K, (int)c.N,
-                          c.eps, (int)first);
+    (wide ? fn::grouped_x_call_fill : fn::grouped_call_fill)(
+        host_calls.data() + (size_t)i * rec, c.x, c.w_gate, sw ? c.w_up : nullptr, f8 ? c.s_gate : nullptr,
+        f8 && sw ? c.s_up : nullptr, c.y, (int)c.M, (int)c.K, (int)c.N, c.eps, (int)first);
     if (c.M == 0 || c.N == 0) continue;
-    const int per = fn::grouped_blocks(f8, sw);
+    const int per = per_item(c);
     const int64_t nb = ((c.N + 15) / 16 + per - 1) / per;   // workgroups of this call
     for (int64_t b = 0; b < nb; ++b) host_items[(size_t)(first + b)] = (uint16_t)i;
     first += nb;
@@ -975,6 +987,7 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
   if (h == nullptr) return fail(FN_ERR_HIP, "step: out of host memory");
   h->grouped = true;
   h->fp8 = f8;
+  h->wide = wide;
   if (items == 0) {   // every call empty: the step launches nothing
     *out = h;
     return FN_OK;
@@ -1005,9 +1018,11 @@ fn_status fn_step_launch(fn_step step, hipStream_t stream) {
   if (step == nullptr) return fail(FN_ERR_NULL, "step is NULL");
   if (step->grouped)
     return step->nitems == 0 ? FN_OK
-                             : hip_status(fn::launch_decode_grouped(step->calls, step->items, (int)step->nitems,
-                                                                    step->fp8, stream),
-                                          "grouped step: launch");
+           : hip_status(step->wide ? fn::launch_decode_x_grouped(step->calls, step->items, (int)step->nitems,
+                                                                 step->fp8, stream)
+                                   : fn::launch_decode_grouped(step->calls, step->items, (int)step->nitems,
+                                                               step->fp8, stream),
+                        "grouped step: launch");
   return hip_status(hipGraphLaunch(step->exec, stream), "step: launch");
 }
 

@@ -96,9 +96,12 @@ constexpr uint32_t kOutOfRangeX = 0x80000000u;
 // the unrounded operand (AD: split in registers, modulate8_split; EX: the
 // pre-pass's [2M, K] operand, row 2m the rounded part of x row m and row
 // 2m+1 the remainder, the remainder staged in LDS beside x).
+// One workgroup's tile: column-block group bx, row-block group by (the
+// kernel below takes them from the grid; the grouped launch from its call
+// table).
 template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false, int NS = 4, bool EX = false,
           bool LO = false>
-__global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
+__device__ __forceinline__ void decode_x_tile(const DecodeXArgs& a, int bx, int by) {
   static_assert(NS >= 3 && NS <= 6, "LDS ring slots");
   constexpr int D = NS - 1;                // stages in flight
   constexpr int NMAT = SW ? 2 : 1;
@@ -167,8 +170,8 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lrow = lane & 15, lgrp = lane >> 4;
-  const int nb0 = (blockIdx.x * NWV + w) * NC;   // first column block of this wave
-  const int m0 = blockIdx.y * MF * 16;           // first row of this workgroup
+  const int nb0 = (bx * NWV + w) * NC;   // first column block of this wave
+  const int m0 = by * MF * 16;           // first row of this workgroup
   // bytes of one packed column block: a fragment per k-block (bf16) or per
   // pair of k-blocks (fp8)
   const int64_t kfrag = (int64_t)(F8 ? (a.kblocks + 1) / 2 : a.kblocks) * kFragBytes;
@@ -523,6 +526,12 @@ __global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
   }
 }
 
+template <int MF, int NC, int NWV, bool SW, int U, bool F8, bool Q8, bool AD = false, int NS = 4, bool EX = false,
+          bool LO = false>
+__global__ __launch_bounds__(kWave * NWV) void decode_x_kernel(DecodeXArgs a) {
+  decode_x_tile<MF, NC, NWV, SW, U, F8, Q8, AD, NS, EX, LO>(a, blockIdx.x, blockIdx.y);
+}
+
 struct DecodeXInstance {
   const void* fn;
   int mf, nc, nwv, u;
@@ -787,5 +796,64 @@ hipError_t launch_fp8(const FusedPlan& p, const void* x, const void* wg, const f
   const DecodeXInstance* d = find_instance(kDecodeF8, p.mf, wu != nullptr);
   if (d == nullptr) return hipErrorInvalidValue;
   return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream, sg, su);
+}
+
+// Grouped launch of independent calls of up to 64 rows: every call's column
+// blocks in workgroups of the tile above at its 64-row capacity, one column
+// block per wave and kGroupedXWaves waves sharing x through the LDS ring.  A
+// single call cannot take that many column blocks per workgroup -- a QKV
+// projection would fill fewer workgroups than there are CUs -- but the
+// thousands of workgroups of a whole step can, and each x byte a workgroup
+// fetches then serves kGroupedXWaves weight streams instead of three or four.
+struct GroupCallX {
+  DecodeXArgs a;
+  int first;    // index of the call's first workgroup in the launch
+  int swiglu;
+};
+
+template <bool F8>
+__global__ __launch_bounds__(kWave * kGroupedXWaves) void decode_x_grouped_kernel(
+    const GroupCallX* __restrict__ calls, const uint16_t* __restrict__ item_call) {
+  const int item = blockIdx.x;
+  const int c = __builtin_amdgcn_readfirstlane((int)item_call[item]);
+  const GroupCallX& g = calls[c];
+  const int bx = item - g.first;
+  if (g.swiglu)
+    decode_x_tile<4, kGroupedXCols, kGroupedXWaves, true, kGroupedXStage, F8, false>(g.a, bx, 0);
+  else
+    decode_x_tile<4, kGroupedXCols, kGroupedXWaves, false, kGroupedXStage, F8, false>(g.a, bx, 0);
+}
+
+hipError_t launch_decode_x_grouped(const void* calls, const void* item_call, int items, bool fp8,
+                                   hipStream_t stream) {
+  const GroupCallX* c = static_cast<const GroupCallX*>(calls);
+  const uint16_t* ic = static_cast<const uint16_t*>(item_call);
+  void* args[] = {&c, &ic};
+  const void* k = fp8 ? reinterpret_cast<const void*>(&decode_x_grouped_kernel<true>)
+                      : reinterpret_cast<const void*>(&decode_x_grouped_kernel<false>);
+  return hipLaunchKernel(k, dim3((unsigned)items), dim3(kWave * kGroupedXWaves), args, 0, stream);
+}
+
+size_t grouped_x_call_bytes() { return sizeof(GroupCallX); }
+
+void grouped_x_call_fill(void* dst, const void* x, const void* wg, const void* wu, const float* sg, const float* su,
+                         void* y, int M, int K, int N, float eps, int first) {
+  GroupCallX g{};
+  g.a.x = x;
+  g.a.wg = wg;
+  g.a.wu = wu;
+  g.a.y = y;
+  g.a.M = M;
+  g.a.K = K;
+  g.a.N = N;
+  g.a.kblocks = (int)ceil_div(K, 32);
+  g.a.nblocks = (int)ceil_div(N, 16);
+  g.a.stages = (int)ceil_div(g.a.kblocks, kGroupedXStage);
+  g.a.eps = eps;
+  g.a.sg = sg;
+  g.a.su = su;
+  g.first = first;
+  g.swiglu = wu != nullptr;
+  *static_cast<GroupCallX*>(dst) = g;
 }
 }  // namespace fn

@@ -109,6 +109,19 @@ size_t grouped_call_bytes();
 void grouped_call_fill(void* dst, const void* x, const void* wg, const void* wu, const float* sg, const float* su,
                        void* y, int M, int K, int N, float eps, int first);
 hipError_t launch_decode_grouped(const void* calls, const void* item_call, int items, bool fp8, hipStream_t stream);
+// The same for steps with calls of 17..64 rows (decode_x.hip): every call in
+// workgroups of kGroupedXWaves waves of kGroupedXCols column blocks each,
+// sharing x through LDS, kGroupedXStage k-blocks per stage;
+// grouped_x_call_bytes() records.
+constexpr int kGroupedXWaves = 12;
+constexpr int kGroupedXCols = 1;
+constexpr int kGroupedXStage = 2;
+constexpr int kGroupedXBlocks = kGroupedXWaves * kGroupedXCols;   // column blocks per workgroup
+size_t grouped_x_call_bytes();
+void grouped_x_call_fill(void* dst, const void* x, const void* wg, const void* wu, const float* sg, const float* su,
+                         void* y, int M, int K, int N, float eps, int first);
+hipError_t launch_decode_x_grouped(const void* calls, const void* item_call, int items, bool fp8,
+                                   hipStream_t stream);
 
 hipError_t launch_fold(DType dt, const void* g, const void* W, void* W_packed,
                        int K, int N, hipStream_t stream);

@@ -352,6 +352,114 @@ def test_grouped_fp8_decode_step_agrees_with_eager(gpu_lib):
     st.close()
 
 
+def _fold_any(fn, g, Wm, fp8):
+    return fn.fold_weights_fp8(g, Wm) if fp8 else fn.fold_weights(g, Wm)
+
+
+def _add_call(st, x, Pg, Pu, out, eps, fp8):
+    if Pu is not None:
+        (st.norm_proj_swiglu_fp8 if fp8 else st.norm_proj_swiglu)(x, Pg, Pu, out, eps)
+    else:
+        (st.norm_proj_fp8 if fp8 else st.norm_proj)(x, Pg, out, eps)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_grouped_wide_ragged_calls_agree_with_oracle(gpu_lib, fp8, seed):
+    """A grouped step with calls of up to 64 rows takes the LDS-shared-x tile
+    for every call (rows 1 to 64 in one launch, K from 8 to 4104, N from 1 to
+    1100, an empty call): each output against the float64 oracle; a second
+    replay gives the first's bits."""
+    import torch
+    fn = gpu_lib
+    shapes = [(64, 4096, 530, True), (17, 8, 1, False), (3, 264, 37, True), (0, 64, 32, False),
+              (40, 1032, 270, False), (64, 4104, 1100, False), (33, 40, 600, True), (16, 2056, 33, False),
+              (1, 136, 17, True), (50, 96, 70, False)]
+    st = fn.Step()
+    cases = []
+    for i, (M, K, N, sw) in enumerate(shapes):
+        inp = W.random_inputs(M, K, N, "bf16", seed=900 + 20 * seed + i, swiglu=sw)
+        x = to_dev(inp.x, "bf16")
+        g = to_dev(inp.g, "bf16")
+        Pg = _fold_any(fn, g, to_dev(inp.W, "bf16"), fp8)
+        Pu = _fold_any(fn, g, to_dev(inp.W_up, "bf16"), fp8) if sw else None
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        _add_call(st, x, Pg, Pu, out, 1e-6, fp8)
+        if fp8:
+            cg, sg = oracle.fold_weights_fp8(inp.g, inp.W, "bf16")
+            if sw:
+                cu, su = oracle.fold_weights_fp8(inp.g, inp.W_up, "bf16")
+                ref = oracle.norm_proj_swiglu_fp8(inp.x, cg, sg, cu, su, 1e-6)
+            else:
+                ref = oracle.norm_proj_fp8(inp.x, cg, sg, 1e-6)
+        else:
+            ref = (oracle.norm_proj_swiglu(inp.x, inp.g, inp.W, inp.W_up, 1e-6) if sw else
+                   oracle.norm_proj(inp.x, inp.g, inp.W, 1e-6))
+        cases.append((out, ref, (M, K, N, sw)))
+    st.record(grouped=True)
+    assert st.num_kernels == 1
+    st.launch()
+    torch.cuda.synchronize()
+    first = [out.clone() for out, _r, _s in cases]
+    for out, ref, shape in cases:
+        assert_close(to_f64(out), ref, "bf16", f"wide grouped call {shape} fp8={fp8}")
+        out.fill_(float("nan"))
+    st.launch()
+    torch.cuda.synchronize()
+    for (out, _r, shape), f in zip(cases, first):
+        assert torch.equal(out.view(torch.int16), f.view(torch.int16)), f"second replay differs: {shape}"
+    st.close()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_grouped_wide_decode_step_agrees_with_eager(gpu_lib, fp8):
+    """Four layers and the head at 64 rows as one grouped launch (the
+    LDS-shared-x tile, eight column blocks per workgroup), on two replays
+    with the inputs refreshed in place: each output against the eager call's.
+    The products follow the same k order; the per-wave partial sums of
+    squares are grouped differently (eight waves against three or four), so
+    1/RMS may differ in its last fp32 bit and an output by one bf16 step,
+    rarely."""
+    import torch
+    fn = gpu_lib
+    calls = W.decode_step_calls(4)
+    st = fn.Step()
+    items = []
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(610 + fp8)
+    for c in calls:
+        _x8, g, Wm, Wu = W.make_inputs_device(c)
+        x = torch.randn((64, c.K), generator=gen, device="cuda").to(torch.bfloat16)
+        Pg = _fold_any(fn, g, Wm, fp8)
+        Pu = _fold_any(fn, g, Wu, fp8) if c.swiglu else None
+        out = torch.empty((64, c.N), dtype=torch.bfloat16, device="cuda")
+        _add_call(st, x, Pg, Pu, out, c.eps, fp8)
+        items.append((x, Pg, Pu, out, c))
+        del Wm, Wu
+    st.record(grouped=True)
+    for replay in range(2):
+        if replay:
+            for x, *_r in items:
+                x.copy_(torch.randn(x.shape, generator=gen, device="cuda").to(x.dtype))
+        for *_r, out, _c in items:
+            out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        st.launch()
+        torch.cuda.synchronize()
+        for x, Pg, Pu, out, c in items:
+            if fp8:
+                want = fn.norm_proj_swiglu_fp8(x, Pg, Pu, c.eps) if c.swiglu else fn.norm_proj_fp8(x, Pg, c.eps)
+            else:
+                want = fn.norm_proj_swiglu(x, Pg, Pu, c.eps) if c.swiglu else fn.norm_proj(x, Pg, c.eps)
+            torch.cuda.synchronize()
+            a, b = out.double(), want.double()
+            assert bool(torch.isfinite(a).all()), f"replay {replay}: {c.name} not finite"
+            same = float((out.view(torch.int16) == want.view(torch.int16)).double().mean())
+            assert same >= 0.999, f"replay {replay}: {c.name}: {same:.5f} of the outputs identical"
+            assert bool(((a - b).abs() <= b.abs() * 2.0 ** -7 + 1e-30).all()), f"replay {replay}: {c.name}"
+    st.close()
+
+
 def test_grouped_step_rejects_chained_calls(gpu_lib):
     """A call that reads another call's output cannot run at the same time
     as it: the grouped form refuses it (the recorded graph takes it)."""

@@ -88,15 +88,16 @@ DECODE_STEP_LAYERS = 32
 DECODE_STEP_M = 8
 
 
-def decode_step_calls(layers: int = DECODE_STEP_LAYERS) -> List[Call]:
-    """The 32-layer decode step at M=8: per layer an attention norm + QKV
-    projection and an FFN norm + gate/up SwiGLU; then the final norm + LM head.
-    Every call gets its own seeded x (calls are independent, not chained)."""
+def decode_step_calls(layers: int = DECODE_STEP_LAYERS, rows: int = DECODE_STEP_M) -> List[Call]:
+    """The 32-layer decode step at M=8 (``rows`` other batch sizes): per
+    layer an attention norm + QKV projection and an FFN norm + gate/up
+    SwiGLU; then the final norm + LM head.  Every call gets its own seeded x
+    (calls are independent, not chained)."""
     calls: List[Call] = []
     for l in range(layers):
-        calls.append(Call(f"layer{l}.attn_qkv", DECODE_STEP_M, 4096, 12288, False, "bf16", 5000 + 2 * l))
-        calls.append(Call(f"layer{l}.ffn_gate_up", DECODE_STEP_M, 4096, 11008, True, "bf16", 5001 + 2 * l))
-    calls.append(Call("head", DECODE_STEP_M, 4096, 32000, False, "bf16", 5064))
+        calls.append(Call(f"layer{l}.attn_qkv", rows, 4096, 12288, False, "bf16", 5000 + 2 * l))
+        calls.append(Call(f"layer{l}.ffn_gate_up", rows, 4096, 11008, True, "bf16", 5001 + 2 * l))
+    calls.append(Call("head", rows, 4096, 32000, False, "bf16", 5064))
     return calls
 
 
