@@ -105,6 +105,19 @@ fn_status fused_common(const void* x, const void* wg, const void* wu, void* y, i
 
 int64_t packed_fp8_bytes(int64_t K, int64_t N) { return ((N + 15) / 16) * ((K + 63) / 64) * 1024; }
 
+// Row counts just above the decode range on wide projections (at least 512
+// column blocks): the LDS-shared-x decode kernel with its 64-row blocks
+// tiled over grid.y instead of the prefill kernel, whose 256-row tiles leave
+// most of each tile empty and give too few workgroups (96 for 12288
+// columns).  Measured on MI355X, K = 4096: QKV 62 -> 40-44 us (bf16, 65-128
+// rows), 64 -> 28-32 us (fp8, 65-128 rows), 67 -> 61 us (fp8, 256 rows);
+// gate/up pairs 77 -> 66-68 us (bf16) and 81 -> 44-48 us (fp8) at 65-128
+// rows.  Beyond 128 rows with bf16 weights and 256 with fp8 the prefill
+// kernel is faster.
+bool decode_rows_tiled(int64_t M, int64_t N, bool f8) {
+  return M > 64 && M <= (f8 ? 256 : 128) && (N + 15) / 16 >= 512;
+}
+
 fn_status fp8_common(const void* x, const void* wg, const float* sg, const void* wu, const float* su, void* y,
                      int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream, bool swiglu,
                      bool check_only = false) {
@@ -128,7 +141,7 @@ fn_status fp8_common(const void* x, const void* wg, const float* sg, const void*
       (swiglu && (overlap(y, yb, wu, wb) || overlap(y, yb, su, sb))))
     return fail(FN_ERR_ALIAS, "output overlaps an input");
   if (check_only) return FN_OK;
-  if (M > 64) {
+  if (M > 64 && !decode_rows_tiled(M, N, true)) {
     const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, false, true);
     return hip_status(fn::launch_prefill_fp8(plan, x, wg, sg, swiglu ? wu : nullptr, swiglu ? su : nullptr, y, (int)M,
                                              (int)K, (int)N, eps, stream),
@@ -438,7 +451,7 @@ namespace fn {
 // (MFMA-bound).  fp32 at any M stays on the register decode kernel, tiled
 // over rows.
 FusedPlan plan_fused(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
-  if (dt == DType::BF16 && M > 64) return plan_prefill(dt, M, K, N, swiglu);
+  if (dt == DType::BF16 && M > 64 && !decode_rows_tiled(M, N, false)) return plan_prefill(dt, M, K, N, swiglu);
   // narrow SwiGLU pairs at 17-64 rows: the register-x kernel with a k-split
   if (dt == DType::BF16 && swiglu && M > 16 && (N + 15) / 16 <= 256) return plan_decode(dt, M, K, N, swiglu);
   if (dt == DType::BF16 && M > 16) return plan_decode_x(dt, M, K, N, swiglu);
@@ -1048,7 +1061,8 @@ fn_status fn_step_destroy(fn_step step) {
 
 const char* fn_kernel_name_fp8(int64_t M, int64_t K, int64_t N, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
-  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true).name;
+  if (M > 64 && !decode_rows_tiled(M, N, true))
+    return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true).name;
   return fn::plan_fp8(M, K, N, swiglu != 0).name;
 }
 

@@ -78,6 +78,17 @@ def test_fp8_parity(gpu_lib, swiglu, M, K, N):
     assert_close(y, ref, "bf16", f"fp8 {M}x{K}x{N} swiglu={swiglu}")
 
 
+@pytest.mark.parametrize("M,K,N,swiglu", [(65, 264, 8200, False), (130, 1032, 8192, True), (256, 136, 8200, False),
+                                          (200, 4104, 8200, True), (128, 4096, 12288, False)])
+def test_fp8_rows_tiled_decode_parity(gpu_lib, M, K, N, swiglu):
+    """65..256 rows of a wide projection with fp8 weights run the 64-row
+    decode kernel tiled over the rows: every output against the oracle."""
+    assert gpu_lib.kernel_name_fp8(M, K, N, swiglu).startswith("decode")
+    inp = W.random_inputs(M, K, N, "bf16", seed=M * 5 + K + N, swiglu=swiglu)
+    y, ref = _run(gpu_lib, inp, swiglu)
+    assert_close(y, ref, "bf16", f"fp8 rows tiled {M}x{K}x{N} swiglu={swiglu}")
+
+
 def test_fp8_qkv_decode_full(gpu_lib):
     inp = W.make_inputs(W.QKV_DECODE)
     y, ref = _run(gpu_lib, inp, False)

@@ -56,6 +56,20 @@ def test_fold_bit_exact(gpu_lib, dtype, K, N):
     assert np.array_equal(Wp1.data.cpu().numpy(), pack_host(inp.W, dtype))
 
 
+# ----------------------------- rows just past decode, wide projections ----
+@pytest.mark.parametrize("M,K,N,swiglu", [(65, 264, 8200, False), (100, 1032, 8192, True), (128, 136, 8208, False),
+                                          (97, 4104, 8200, True), (128, 4096, 12288, False)])
+def test_rows_tiled_decode_parity(gpu_lib, M, K, N, swiglu):
+    """65..128 rows of a projection with at least 512 column blocks run the
+    64-row LDS-shared-x decode kernel with its row blocks tiled over the grid
+    (a ragged last block of rows, ragged K and N): every output against the
+    oracle."""
+    inp = W.random_inputs(M, K, N, "bf16", seed=M + K + N + swiglu, swiglu=swiglu)
+    import torch
+    assert gpu_lib.kernel_name(M, K, N, swiglu, torch.bfloat16).startswith("decode")
+    assert_close(fused(gpu_lib, inp), reference(inp), "bf16", f"rows tiled {M}x{K}x{N} swiglu={swiglu}")
+
+
 # ------------------------------------------------------ hand-derived case --
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_hand_case_exact(gpu_lib, dtype):
