@@ -106,14 +106,14 @@ fn_status fused_common(const void* x, const void* wg, const void* wu, void* y, i
 int64_t packed_fp8_bytes(int64_t K, int64_t N) { return ((N + 15) / 16) * ((K + 63) / 64) * 1024; }
 
 // Row counts just above the decode range on wide projections (at least 512
-// column blocks): the LDS-shared-x decode kernel with its 64-row blocks
-// tiled over grid.y instead of the prefill kernel, whose 256-row tiles leave
-// most of each tile empty and give too few workgroups (96 for 12288
-// columns).  Measured on MI355X, K = 4096: QKV 62 -> 40-44 us (bf16, 65-128
-// rows), 64 -> 28-32 us (fp8, 65-128 rows), 67 -> 61 us (fp8, 256 rows);
-// gate/up pairs 77 -> 66-68 us (bf16) and 81 -> 44-48 us (fp8) at 65-128
-// rows.  Beyond 128 rows with bf16 weights and 256 with fp8 the prefill
-// kernel is faster.
+// column blocks): the LDS-shared-x decode kernel (a 128-row rung for bf16
+// weights; 64- or 128-row blocks tiled over grid.y for fp8) instead of the
+// prefill kernel, whose 256-row tiles leave most of each tile empty and give
+// too few workgroups (96 for 12288 columns).  Measured on MI355X, K = 4096:
+// QKV 62 -> 36 us (bf16, 65-128 rows), 64-67 -> 26-57 us (fp8, 65-256
+// rows); gate/up pairs 77 -> 47-51 us (bf16, 65-128 rows) and 81-87 ->
+// 39-64 us (fp8, 65-256 rows).  Beyond 128 rows with bf16 weights and 256
+// with fp8 the prefill kernel is faster.
 bool decode_rows_tiled(int64_t M, int64_t N, bool f8) {
   return M > 64 && M <= (f8 ? 256 : 128) && (N + 15) / 16 >= 512;
 }
@@ -447,7 +447,8 @@ namespace fn {
 
 // The row ladder.  bf16: up to 16 rows the skinny decode kernel with x in
 // registers; 17..64 rows the decode kernel that shares x through LDS (both
-// weight streaming, HBM-bound); more rows the tiled prefill kernel
+// weight streaming, HBM-bound), and its 128-row rung up to 128 rows of wide
+// projections (decode_rows_tiled); more rows the tiled prefill kernel
 // (MFMA-bound).  fp32 at any M stays on the register decode kernel, tiled
 // over rows.
 FusedPlan plan_fused(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {

@@ -128,7 +128,7 @@ __device__ __forceinline__ void decode_x_tile(const DecodeXArgs& a, int bx, int 
                 "AdaLN: one row block, bf16 weights and output, one column block per wave");
   // Epilogue through LDS (one lane per row, 16-byte stores): fp8 output
   // always, bf16 output when each wave owns one column block.
-  constexpr bool STAGE = Q8 || (NC == 1 && NWV <= NS);
+  constexpr bool STAGE = Q8 || (NC == 1 && NWV <= NS && MF <= 4);   // one lane per row
   static_assert(!STAGE || (NC == 1 && NWV <= NS && 16 * MF * 16 * 4 <= SLOT), "staging fits a ring slot");
   static_assert(!EX || (!AD && NC == 1), "pre-modulated operand: one column block per wave");
   constexpr bool BIAS = AD || EX;
@@ -598,6 +598,13 @@ static const DecodeXInstance kDecodeX[] = {
                     2, false, false, false, "decode_bf16_m64_xlds_w3_u2_s5"},
     FN_DECODE_X(2, 1, 3, true, 2, "decode_swiglu_bf16_m32_xlds_w3_u2"),
     FN_DECODE_X(4, 1, 3, true, 2, "decode_swiglu_bf16_m64_xlds_w3_u2"),
+    // 65..128 rows of wide projections (the row ladder sends them here
+    // instead of the prefill kernel): one workgroup holds all 128 rows, so
+    // each weight column block is requested once, not once per 64-row
+    // block -- measured against the 64-row rung tiled over the rows: QKV
+    // 39-43 -> 39-42 us, gate/up pairs 66-70 -> 51-53 us
+    FN_DECODE_X(8, 1, 3, false, 2, "decode_bf16_m128_xlds_w3_u2"),
+    FN_DECODE_X(8, 1, 3, true, 2, "decode_swiglu_bf16_m128_xlds_w3_u2"),
 };
 
 // fp8 weights, measured the same way: with half the weight bytes per stage
@@ -610,6 +617,10 @@ static const DecodeXInstance kDecodeF8[] = {
     FN_DECODE_X8(1, 1, 3, true, 4, "decode_swiglu_fp8_m16_xlds_w3_u4"),
     FN_DECODE_X8(2, 1, 3, true, 4, "decode_swiglu_fp8_m32_xlds_w3_u4"),
     FN_DECODE_X8(4, 1, 4, true, 2, "decode_swiglu_fp8_m64_xlds_w4_u2"),
+    // gate/up pairs of 65..256 rows: 128-row blocks (44-76 -> 42-68 us
+    // against the 64-row rung tiled over the rows); plain projections stay on
+    // 64-row blocks, which measured faster there (29-32 against 36-38 us)
+    FN_DECODE_X8(8, 1, 4, true, 2, "decode_swiglu_fp8_m128_xlds_w4_u2"),
 };
 
 // SwiGLU with fp8 output: the instances above with the row-block epilogue.
@@ -641,11 +652,12 @@ static FusedPlan plan_of(const DecodeXInstance* d, int kind, int64_t M, int64_t 
   return p;
 }
 
-// bf16 row ladder rungs 32 and 64 (one row of workgroups).
+// bf16 row ladder rungs 32, 64 and 128 (the last only for the wide
+// projections the row ladder sends here past 64 rows).
 FusedPlan plan_decode_x(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
   (void)dt;
   (void)K;
-  return plan_of(find_instance(kDecodeX, M <= 32 ? 2 : 4, swiglu), 2, M, N);
+  return plan_of(find_instance(kDecodeX, M <= 32 ? 2 : (M <= 64 ? 4 : 8), swiglu), 2, M, N);
 }
 
 hipError_t launch_decode_x(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
@@ -655,11 +667,12 @@ hipError_t launch_decode_x(DType dt, const FusedPlan& p, const void* x, const vo
   return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream);
 }
 
-// fp8 row ladder 16 / 32 / 64; past 64 rows the 64-row tiles repeat over
-// grid.y (each row tile streams the weights again: a decode design).
+// fp8 row ladder 16 / 32 / 64 (128 for SwiGLU pairs past 64 rows); past the
+// rung the row blocks repeat over grid.y (each streams the weights again: a
+// decode design, used up to 256 rows of wide projections).
 FusedPlan plan_fp8(int64_t M, int64_t K, int64_t N, bool swiglu) {
   (void)K;
-  return plan_of(find_instance(kDecodeF8, M <= 16 ? 1 : (M <= 32 ? 2 : 4), swiglu), 3, M, N);
+  return plan_of(find_instance(kDecodeF8, M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 || !swiglu ? 4 : 8)), swiglu), 3, M, N);
 }
 
 // AdaLN prologue (bf16), one launch, up to 16 rows: one modulation-table row

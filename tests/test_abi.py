@@ -50,10 +50,10 @@ def test_m_ladder(lib, M, name):
 
 
 def test_rows_just_past_decode_on_wide_projections(lib):
-    # 65..128 rows with at least 512 column blocks: the 64-row LDS-shared-x
-    # decode kernel tiled over the rows; more rows or narrower N: prefill
-    assert lib.fn_kernel_name(65, 4096, 12288, 0, BF16).decode().startswith("decode_bf16_m64")
-    assert lib.fn_kernel_name(128, 4096, 11008, 1, BF16).decode().startswith("decode_swiglu_bf16_m64")
+    # 65..128 rows with at least 512 column blocks: the 128-row rung of the
+    # LDS-shared-x decode kernel; more rows or narrower N: prefill
+    assert lib.fn_kernel_name(65, 4096, 12288, 0, BF16).decode().startswith("decode_bf16_m128")
+    assert lib.fn_kernel_name(128, 4096, 11008, 1, BF16).decode().startswith("decode_swiglu_bf16_m128")
     assert lib.fn_kernel_name(129, 4096, 12288, 0, BF16).decode().startswith("prefill")
     assert lib.fn_kernel_name(96, 4096, 8176, 0, BF16).decode().startswith("prefill")
     assert lib.fn_kernel_name(96, 4096, 8192, 0, F32).decode().startswith("decode_f32")
@@ -191,7 +191,8 @@ def test_fp8_kernel_names(lib):
     # 65..256 rows of a wide projection (>= 512 column blocks): the 64-row
     # decode kernel tiled over the rows; narrower ones stay on the prefill kernel
     assert lib.fn_kernel_name_fp8(65, 4096, 12288, 0).decode().startswith("decode_fp8_m64")
-    assert lib.fn_kernel_name_fp8(256, 4096, 8192, 1).decode().startswith("decode_swiglu_fp8_m64")
+    assert lib.fn_kernel_name_fp8(256, 4096, 8192, 1).decode().startswith("decode_swiglu_fp8_m128")
+    assert lib.fn_kernel_name_fp8(200, 4096, 8192, 0).decode().startswith("decode_fp8_m64")
     assert lib.fn_kernel_name_fp8(257, 4096, 12288, 0).decode().startswith("prefill_fp8")
     assert lib.fn_kernel_name_fp8(128, 4096, 8176, 0).decode().startswith("prefill_fp8")
     assert lib.fn_kernel_name_fp8(4096, 4096, 12288, 1).decode() == "prefill_swiglu_fp8_256x128_w4x2_xl"

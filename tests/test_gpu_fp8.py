@@ -81,8 +81,9 @@ def test_fp8_parity(gpu_lib, swiglu, M, K, N):
 @pytest.mark.parametrize("M,K,N,swiglu", [(65, 264, 8200, False), (130, 1032, 8192, True), (256, 136, 8200, False),
                                           (200, 4104, 8200, True), (128, 4096, 12288, False)])
 def test_fp8_rows_tiled_decode_parity(gpu_lib, M, K, N, swiglu):
-    """65..256 rows of a wide projection with fp8 weights run the 64-row
-    decode kernel tiled over the rows: every output against the oracle."""
+    """65..256 rows of a wide projection with fp8 weights run the decode
+    kernel's 64-row (projection) or 128-row (SwiGLU) blocks tiled over the
+    rows (a ragged last block): every output against the oracle."""
     assert gpu_lib.kernel_name_fp8(M, K, N, swiglu).startswith("decode")
     inp = W.random_inputs(M, K, N, "bf16", seed=M * 5 + K + N, swiglu=swiglu)
     y, ref = _run(gpu_lib, inp, swiglu)

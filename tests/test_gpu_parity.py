@@ -61,9 +61,8 @@ def test_fold_bit_exact(gpu_lib, dtype, K, N):
                                           (97, 4104, 8200, True), (128, 4096, 12288, False)])
 def test_rows_tiled_decode_parity(gpu_lib, M, K, N, swiglu):
     """65..128 rows of a projection with at least 512 column blocks run the
-    64-row LDS-shared-x decode kernel with its row blocks tiled over the grid
-    (a ragged last block of rows, ragged K and N): every output against the
-    oracle."""
+    128-row rung of the LDS-shared-x decode kernel (ragged rows, K and N):
+    every output against the oracle."""
     inp = W.random_inputs(M, K, N, "bf16", seed=M + K + N + swiglu, swiglu=swiglu)
     import torch
     assert gpu_lib.kernel_name(M, K, N, swiglu, torch.bfloat16).startswith("decode")
