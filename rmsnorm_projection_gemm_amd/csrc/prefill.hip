@@ -596,14 +596,21 @@ static const PrefillInstance kPrefill[] = {
     FN_PREFILL(4, 8, 4, 2, false, false, true, true, "prefill_fp8_premod_256x256_w4x2_xl"),
     FN_PREFILL_PAIR(true, "prefill_swiglu_fp8_premod_split_256x128_w4x2_xl"),
     FN_PREFILL(4, 4, 4, 2, true, true, true, true, "prefill_swiglu_fp8_q8_premod_256x128_w4x2_xl"),
+    // 129..256 rows of wide projections (at least 512 column blocks): 128-row
+    // tiles, twice the workgroups of 256-row tiles with half as many empty
+    // rows -- measured at K = 4096: QKV 64-66 -> 54-56 us, gate/up pairs
+    // 83 -> 72-74 us, the same bits; slower from 384 rows on
+    FN_PREFILL(2, 4, 4, 2, false, false, false, false, "prefill_bf16_128x128_w4x2"),
+    FN_PREFILL(2, 4, 4, 2, true, false, false, false, "prefill_swiglu_bf16_128x128_w4x2"),
 };
 
-// The first instance with exactly these flags (q8 implies SwiGLU) and, when
-// nf is given, 16-column fragments per tile; the plain projection when none
-// matches.
-static const PrefillInstance& pick(bool sw, bool q8 = false, bool ex = false, bool f8 = false, int nf = 0) {
+// The first instance with exactly these flags (q8 implies SwiGLU), mf
+// 16-row fragments per tile and, when nf is given, nf 16-column fragments;
+// the plain projection when none matches.
+static const PrefillInstance& pick(bool sw, bool q8 = false, bool ex = false, bool f8 = false, int nf = 0,
+                                   int mf = 16) {
   for (const PrefillInstance& d : kPrefill)
-    if (d.sw == (sw || q8) && d.q8 == q8 && d.ex == ex && d.f8 == f8 &&
+    if (d.sw == (sw || q8) && d.q8 == q8 && d.ex == ex && d.f8 == f8 && d.fm * d.wm == mf &&
         (nf == 0 || d.fn_ * d.wn == nf))
       return d;
   return kPrefill[0];
@@ -614,7 +621,8 @@ FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, b
   (void)K;
   const bool plain = !swiglu && !q8 && !ex;
   const bool narrow = plain && ceil_div(N, 256) * ceil_div(M, 256) < 128;
-  const PrefillInstance& d = pick(swiglu, q8, ex, f8, narrow ? 8 : 0);
+  const bool rows128 = !q8 && !ex && !f8 && M <= 256 && ceil_div(N, 16) >= 512;
+  const PrefillInstance& d = rows128 ? pick(swiglu, false, false, false, 8, 8) : pick(swiglu, q8, ex, f8, narrow ? 8 : 0);
   FusedPlan p{};
   p.kind = f8 ? 11 : (ex ? (q8 ? 10 : 8) : (q8 ? 5 : 1));
   p.mf = d.fm * d.wm;
@@ -630,7 +638,7 @@ FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, b
 hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
                           int M, int K, int N, float eps, hipStream_t stream, uint8_t* q, float* qs) {
   if (dt != DType::BF16 || (q != nullptr && wu == nullptr)) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, false, p.nf);
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, false, p.nf, p.mf);
   PrefillArgs a{};
   a.q = q;
   a.qs = qs;
@@ -655,7 +663,7 @@ hipError_t launch_prefill_fp8(const FusedPlan& p, const void* x, const void* wg,
                               const float* su, void* y, int M, int K, int N, float eps, hipStream_t stream, uint8_t* q,
                               float* qs) {
   if ((q != nullptr && wu == nullptr) || sg == nullptr || (wu != nullptr && su == nullptr)) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, true, p.nf);
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, true, p.nf, p.mf);
   PrefillArgs a{};
   a.x = x;
   a.wg = wg;

@@ -51,10 +51,13 @@ def test_m_ladder(lib, M, name):
 
 def test_rows_just_past_decode_on_wide_projections(lib):
     # 65..128 rows with at least 512 column blocks: the 128-row rung of the
-    # LDS-shared-x decode kernel; more rows or narrower N: prefill
+    # LDS-shared-x decode kernel; 129..256 rows: 128-row prefill tiles; more
+    # rows or narrower N: the 256-row prefill tiles
     assert lib.fn_kernel_name(65, 4096, 12288, 0, BF16).decode().startswith("decode_bf16_m128")
     assert lib.fn_kernel_name(128, 4096, 11008, 1, BF16).decode().startswith("decode_swiglu_bf16_m128")
-    assert lib.fn_kernel_name(129, 4096, 12288, 0, BF16).decode().startswith("prefill")
+    assert lib.fn_kernel_name(129, 4096, 12288, 0, BF16).decode() == "prefill_bf16_128x128_w4x2"
+    assert lib.fn_kernel_name(256, 4096, 11008, 1, BF16).decode() == "prefill_swiglu_bf16_128x128_w4x2"
+    assert lib.fn_kernel_name(257, 4096, 12288, 0, BF16).decode().startswith("prefill_bf16_256x")
     assert lib.fn_kernel_name(96, 4096, 8176, 0, BF16).decode().startswith("prefill")
     assert lib.fn_kernel_name(96, 4096, 8192, 0, F32).decode().startswith("decode_f32")
 

@@ -69,6 +69,17 @@ def test_rows_tiled_decode_parity(gpu_lib, M, K, N, swiglu):
     assert_close(fused(gpu_lib, inp), reference(inp), "bf16", f"rows tiled {M}x{K}x{N} swiglu={swiglu}")
 
 
+@pytest.mark.parametrize("M,K,N,swiglu", [(129, 264, 8200, False), (200, 1032, 8192, True), (256, 4096, 12288, False),
+                                          (161, 136, 8208, True)])
+def test_prefill_128_row_tiles_parity(gpu_lib, M, K, N, swiglu):
+    """129..256 rows of a wide projection take the prefill kernel's 128-row
+    tiles (ragged rows, K and N): every output against the oracle."""
+    import torch
+    assert "128x128" in gpu_lib.kernel_name(M, K, N, swiglu, torch.bfloat16)
+    inp = W.random_inputs(M, K, N, "bf16", seed=3 * M + K + N + swiglu, swiglu=swiglu)
+    assert_close(fused(gpu_lib, inp), reference(inp), "bf16", f"128-row tiles {M}x{K}x{N} swiglu={swiglu}")
+
+
 # ------------------------------------------------------ hand-derived case --
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_hand_case_exact(gpu_lib, dtype):
