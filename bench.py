@@ -51,7 +51,7 @@ def parse_args(argv=None):
     p.add_argument("--workload", default="qkv_decode",
                    choices=["tiny", "qkv_decode", "ffn_decode", "prefill_qkv", "decode_step"])
     p.add_argument("--step-rows", type=int, default=8,
-                   help="decode_step: rows of every call (1..64; the step is quoted at 8)")
+                   help="decode_step: rows of every call (1..128; the step is quoted at 8)")
     p.add_argument("--weights", default="native", choices=["native", "fp8"],
                    help="weight storage: the activations' dtype, or E4M3 codes with per-column scales "
                         "(bf16 decode workloads only)")
@@ -793,8 +793,8 @@ def main(argv=None):
     if adaln and args.workload not in ("qkv_decode", "ffn_decode", "prefill_qkv"):
         print("bench.py: --prologue adaln applies to qkv_decode, ffn_decode and prefill_qkv", file=sys.stderr)
         return 2
-    if not 1 <= args.step_rows <= 64:
-        print("bench.py: --step-rows must be in 1..64", file=sys.stderr)
+    if not 1 <= args.step_rows <= 128:
+        print("bench.py: --step-rows must be in 1..128", file=sys.stderr)
         return 2
     configs = [] if args.configs.strip() in ("", "none") else [c.strip() for c in args.configs.split(",")]
     bad = [c for c in configs if c not in CONFIG_CHOICES]

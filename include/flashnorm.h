@@ -534,10 +534,10 @@ fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out);
  * When every call has at most 16 rows, each workgroup
  * is one wave streaming the whole of k for two column blocks of its call,
  * x in registers (one x fragment load serves both); when some call has
- * 17..64 rows, every call runs in workgroups of twelve waves, one column
- * block each, sharing x through LDS (the entry point's 17..64-row kernel
- * with more column blocks per workgroup than a single call could fill the
- * GPU with).  The products follow the entry point's k order.  bf16 weights
+ * 17..128 rows, every call runs in workgroups of 64 rows and twelve waves,
+ * one column block each, sharing x through LDS (the entry point's
+ * 17..64-row kernel with more column blocks per workgroup than a single
+ * call could fill the GPU with).  The products follow the entry point's k order.  bf16 weights
  * up to 16 rows: the same bits as the call's own entry point where that
  * entry point also runs one wave over the whole of k (more than 256 column
  * blocks for a projection, more than 512 for a SwiGLU pair); narrower
@@ -548,7 +548,7 @@ fn_status fn_step_create(const fn_call* calls, int64_t n_calls, fn_step* out);
  * rounding step, rarely.  Takes FN_CALL_NORM_PROJ and
  * FN_CALL_NORM_PROJ_SWIGLU calls with FN_BF16, or FN_CALL_NORM_PROJ_FP8 and
  * FN_CALL_NORM_PROJ_SWIGLU_FP8 calls, all of one weight type, each with
- * M <= 64 (FN_ERR_SHAPE otherwise), 1 <= n_calls <= 65535; calls with
+ * M <= 128 (FN_ERR_SHAPE otherwise), 1 <= n_calls <= 65535; calls with
  * M == 0 or N == 0 add nothing (a step of only such calls launches
  * nothing).  The calls run at the same time, so no call may write a buffer
  * another call reads or writes (column scales included): FN_ERR_ALIAS

@@ -946,8 +946,8 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
     if (c8 != f8)
       return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes calls of one weight type (all bf16 or all fp8)"),
                          i);
-    if ((bf && c.dt != FN_BF16) || c.M > 64)
-      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes bf16 activations of at most 64 rows (M=%lld)",
+    if ((bf && c.dt != FN_BF16) || c.M > 128)
+      return call_failed(fail(FN_ERR_SHAPE, "a grouped step takes bf16 activations of at most 128 rows (M=%lld)",
                               (long long)c.M), i);
     if (c.M == 0 || c.N == 0) continue;
     const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU || c.kind == FN_CALL_NORM_PROJ_SWIGLU_FP8;
@@ -966,17 +966,26 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
     add(c.y, c.M * c.N * 2, true);
   }
   // up to 16 rows in every call: the one-wave register-x tiles; else every
-  // call takes the LDS-shared-x tile of 64 rows
+  // call takes the LDS-shared-x tile, 64 rows per workgroup (more rows in
+  // more workgroups)
   bool wide = false;
   for (int64_t i = 0; i < n_calls; ++i) wide = wide || (calls[i].N > 0 && calls[i].M > 16);
   auto per_item = [&](const fn_call& c) {
     const bool sw = c.kind == FN_CALL_NORM_PROJ_SWIGLU || c.kind == FN_CALL_NORM_PROJ_SWIGLU_FP8;
     return wide ? fn::kGroupedXBlocks : fn::grouped_blocks(f8, sw);
   };
+  // workgroups of a call: its column groups; in the wide tile with more than
+  // one 64-row block, the groups padded to a multiple of 8 times the row
+  // blocks (the kernel's XCD-aware order)
+  auto call_items = [&](const fn_call& c) -> int64_t {
+    const int64_t groups = ((c.N + 15) / 16 + per_item(c) - 1) / per_item(c);
+    const int64_t rowblocks = (c.M + 63) / 64;
+    return wide && rowblocks > 1 ? (groups + 7) / 8 * 8 * rowblocks : groups;
+  };
   for (int64_t i = 0; i < n_calls; ++i) {
     const fn_call& c = calls[i];
     if (c.M == 0 || c.N == 0) continue;
-    items += ((c.N + 15) / 16 + per_item(c) - 1) / per_item(c);
+    items += call_items(c);
   }
   if (outputs_overlap(spans))
     return fail(FN_ERR_ALIAS, "a grouped step runs its calls at once: no call may write a buffer another call uses");
@@ -992,8 +1001,7 @@ fn_status step_create_grouped(const fn_call* calls, int64_t n_calls, fn_step* ou
         host_calls.data() + (size_t)i * rec, c.x, c.w_gate, sw ? c.w_up : nullptr, f8 ? c.s_gate : nullptr,
         f8 && sw ? c.s_up : nullptr, c.y, (int)c.M, (int)c.K, (int)c.N, c.eps, (int)first);
     if (c.M == 0 || c.N == 0) continue;
-    const int per = per_item(c);
-    const int64_t nb = ((c.N + 15) / 16 + per - 1) / per;   // workgroups of this call
+    const int64_t nb = call_items(c);   // workgroups of this call
     for (int64_t b = 0; b < nb; ++b) host_items[(size_t)(first + b)] = (uint16_t)i;
     first += nb;
   }

@@ -820,9 +820,16 @@ hipError_t launch_fp8(const FusedPlan& p, const void* x, const void* wg, const f
 // fetches then serves kGroupedXWaves weight streams instead of three or four.
 struct GroupCallX {
   DecodeXArgs a;
-  int first;    // index of the call's first workgroup in the launch
+  int first;       // index of the call's first workgroup in the launch
   int swiglu;
+  int rowblocks;   // 64-row blocks of the call
 };
+// Workgroup r of a call with several row blocks: eight column groups side by
+// side, then the next row block of the same eight.  Workgroup L of the launch
+// runs on XCD L % 8, so the row blocks of one column group (r apart by
+// multiples of 8) share an XCD and its L2, and start close together: the
+// weights stream from HBM once.  Groups past the call's last (the padding of
+// its last eight) read nothing and store nothing.
 
 template <bool F8>
 __global__ __launch_bounds__(kWave * kGroupedXWaves) void decode_x_grouped_kernel(
@@ -830,11 +837,13 @@ __global__ __launch_bounds__(kWave * kGroupedXWaves) void decode_x_grouped_kerne
   const int item = blockIdx.x;
   const int c = __builtin_amdgcn_readfirstlane((int)item_call[item]);
   const GroupCallX& g = calls[c];
-  const int bx = item - g.first;
+  const int r = item - g.first;
+  const int oct = r / (8 * g.rowblocks), w8 = r - oct * 8 * g.rowblocks;
+  const int by = w8 >> 3, bx = oct * 8 + (w8 & 7);
   if (g.swiglu)
-    decode_x_tile<4, kGroupedXCols, kGroupedXWaves, true, kGroupedXStage, F8, false>(g.a, bx, 0);
+    decode_x_tile<4, kGroupedXCols, kGroupedXWaves, true, kGroupedXStage, F8, false>(g.a, bx, by);
   else
-    decode_x_tile<4, kGroupedXCols, kGroupedXWaves, false, kGroupedXStage, F8, false>(g.a, bx, 0);
+    decode_x_tile<4, kGroupedXCols, kGroupedXWaves, false, kGroupedXStage, F8, false>(g.a, bx, by);
 }
 
 hipError_t launch_decode_x_grouped(const void* calls, const void* item_call, int items, bool fp8,
@@ -867,6 +876,7 @@ void grouped_x_call_fill(void* dst, const void* x, const void* wg, const void* w
   g.a.su = su;
   g.first = first;
   g.swiglu = wu != nullptr;
+  g.rowblocks = (int)ceil_div(M, 64);
   *static_cast<GroupCallX*>(dst) = g;
 }
 }  // namespace fn

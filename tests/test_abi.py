@@ -315,12 +315,12 @@ def test_grouped_step_validates_before_any_hip_call(lib):
     st, _ = _create_grouped(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_SWIGLU_Q8, wu=0x30000, ys=0x50000)])
     assert st == SHAPE and "their fp8 forms" in lib.fn_last_error().decode()
     st, _ = _create_grouped(lib, [_call(dt=F32)])
-    assert st == SHAPE and "bf16 activations of at most 64 rows" in lib.fn_last_error().decode()
+    assert st == SHAPE and "bf16 activations of at most 128 rows" in lib.fn_last_error().decode()
     st, _ = _create_grouped(lib, [_call(kind=fn.FN_CALL_NORM_PROJ_SWIGLU_FP8, wu=0x30000, sg=0x50000, su=0x60000,
-                                        M=65)])
-    assert st == SHAPE and "M=65" in lib.fn_last_error().decode()
-    st, _ = _create_grouped(lib, [_call(M=65)])
-    assert st == SHAPE and "M=65" in lib.fn_last_error().decode()
+                                        M=129)])
+    assert st == SHAPE and "M=129" in lib.fn_last_error().decode()
+    st, _ = _create_grouped(lib, [_call(M=129)])
+    assert st == SHAPE and "M=129" in lib.fn_last_error().decode()
     st, _ = _create_grouped(lib, [])
     assert st == SHAPE and "n_calls" in lib.fn_last_error().decode()
     st, _ = _create_grouped(lib, [_call()], n=65536)
@@ -379,7 +379,7 @@ def test_grouped_overlap_check_matches_brute_force(lib, fp8):
         calls, spans = [], []
         for i in range(rng.randint(2, 5)):
             sw = rng.random() < 0.5
-            M, K, N = rng.randint(1, 64 if trial % 2 else 16), 8 * rng.randint(1, 12), rng.randint(1, 40)
+            M, K, N = rng.randint(1, 128 if trial % 2 else 16), 8 * rng.randint(1, 12), rng.randint(1, 40)
             while True:
                 at = lambda: base + 16 * rng.randrange(arena // 16)
                 x, wg, wu, sg, su, y = at(), at(), at(), at(), at(), at()

@@ -366,15 +366,16 @@ def _add_call(st, x, Pg, Pu, out, eps, fp8):
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("seed", [0, 1])
 def test_grouped_wide_ragged_calls_agree_with_oracle(gpu_lib, fp8, seed):
-    """A grouped step with calls of up to 64 rows takes the LDS-shared-x tile
-    for every call (rows 1 to 64 in one launch, K from 8 to 4104, N from 1 to
-    1100, an empty call): each output against the float64 oracle; a second
-    replay gives the first's bits."""
+    """A grouped step with calls of more than 16 rows takes the LDS-shared-x
+    tile for every call (rows 1 to 128 in one launch, two 64-row blocks for
+    the largest, K from 8 to 4104, N from 1 to 1100, an empty call): each
+    output against the float64 oracle; a second replay gives the first's
+    bits."""
     import torch
     fn = gpu_lib
     shapes = [(64, 4096, 530, True), (17, 8, 1, False), (3, 264, 37, True), (0, 64, 32, False),
               (40, 1032, 270, False), (64, 4104, 1100, False), (33, 40, 600, True), (16, 2056, 33, False),
-              (1, 136, 17, True), (50, 96, 70, False)]
+              (1, 136, 17, True), (50, 96, 70, False), (128, 1032, 270, True), (97, 264, 530, False)]
     st = fn.Step()
     cases = []
     for i, (M, K, N, sw) in enumerate(shapes):
@@ -411,28 +412,29 @@ def test_grouped_wide_ragged_calls_agree_with_oracle(gpu_lib, fp8, seed):
     st.close()
 
 
+@pytest.mark.parametrize("rows", [64, 128])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_grouped_wide_decode_step_agrees_with_eager(gpu_lib, fp8):
-    """Four layers and the head at 64 rows as one grouped launch (the
-    LDS-shared-x tile, eight column blocks per workgroup), on two replays
-    with the inputs refreshed in place: each output against the eager call's.
-    The products follow the same k order; the per-wave partial sums of
-    squares are grouped differently (eight waves against three or four), so
-    1/RMS may differ in its last fp32 bit and an output by one bf16 step,
-    rarely."""
+def test_grouped_wide_decode_step_agrees_with_eager(gpu_lib, fp8, rows):
+    """Four layers and the head at 64 or 128 rows as one grouped launch (the
+    LDS-shared-x tile, twelve column blocks and 64 rows per workgroup), on
+    two replays with the inputs refreshed in place: each output against the
+    eager call's, whichever kernel the row ladder gives it.  The products
+    follow the same k order; the per-wave partial sums of
+    squares are grouped differently, so 1/RMS may differ in its last fp32
+    bit and an output by one bf16 step, rarely."""
     import torch
     fn = gpu_lib
     calls = W.decode_step_calls(4)
     st = fn.Step()
     items = []
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(610 + fp8)
+    gen.manual_seed(610 + fp8 + rows)
     for c in calls:
         _x8, g, Wm, Wu = W.make_inputs_device(c)
-        x = torch.randn((64, c.K), generator=gen, device="cuda").to(torch.bfloat16)
+        x = torch.randn((rows, c.K), generator=gen, device="cuda").to(torch.bfloat16)
         Pg = _fold_any(fn, g, Wm, fp8)
         Pu = _fold_any(fn, g, Wu, fp8) if c.swiglu else None
-        out = torch.empty((64, c.N), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((rows, c.N), dtype=torch.bfloat16, device="cuda")
         _add_call(st, x, Pg, Pu, out, c.eps, fp8)
         items.append((x, Pg, Pu, out, c))
         del Wm, Wu
