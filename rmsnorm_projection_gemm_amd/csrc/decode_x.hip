@@ -811,13 +811,18 @@ hipError_t launch_fp8(const FusedPlan& p, const void* x, const void* wg, const f
   return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream, sg, su);
 }
 
-// Grouped launch of independent calls of up to 64 rows: every call's column
-// blocks in workgroups of the tile above at its 64-row capacity, one column
-// block per wave and kGroupedXWaves waves sharing x through the LDS ring.  A
-// single call cannot take that many column blocks per workgroup -- a QKV
-// projection would fill fewer workgroups than there are CUs -- but the
-// thousands of workgroups of a whole step can, and each x byte a workgroup
-// fetches then serves kGroupedXWaves weight streams instead of three or four.
+// Grouped launch of independent calls of up to 128 rows: every call's column
+// blocks in workgroups of the tile above at its 64-row capacity (one per
+// 64-row block of the call), one column block per wave and kGroupedXWaves
+// waves sharing x through the LDS ring.  A single call cannot take that many
+// column blocks per workgroup -- a QKV projection would fill fewer
+// workgroups than there are CUs -- but the thousands of workgroups of a
+// whole step can, and each x byte a workgroup fetches then serves
+// kGroupedXWaves weight streams instead of three or four.  Measured on the
+// 65 calls of a 32-layer step (speed-up over the calls launched one by one,
+// bf16 / fp8 weights): 1.06 / 1.38 at 32 rows, 1.15 / 1.76 at 64, 1.13 /
+// 1.66 at 128; eight waves per workgroup 1.13 / 1.68 at 64 rows, four 1.09 /
+// 1.52.
 struct GroupCallX {
   DecodeXArgs a;
   int first;       // index of the call's first workgroup in the launch
