@@ -580,13 +580,26 @@ static const DecodeInstance kDecode[] = {
     FN_DECODE(float, DType::F32, 1, 1, true, 1, 4, 2, "decode_swiglu_f32_m16_n16_k4_u2"),
     FN_DECODE(float, DType::F32, 2, 1, true, 1, 4, 2, "decode_swiglu_f32_m32_n16_k4_u2"),
     FN_DECODE(float, DType::F32, 4, 1, true, 1, 4, 2, "decode_swiglu_f32_m64_n16_k4_u2"),
+    // very wide projections (an LM head) at up to 16 rows: two column blocks
+    // per wave load each x fragment once for two weight fragments, and there
+    // are still three or more waves per CU -- measured 48.9 -> 43.9 us for
+    // 16 x 4096 -> 32000 and 200 -> 168 us for 16 x 4096 -> 128256 (at 8
+    // rows 43.0 -> 43.3 and 166 -> 162 us), the same bits
+    FN_DECODE(__bf16, DType::BF16, 1, 2, false, 1, 1, 4, "decode_bf16_m16_n32_k1_u4"),
+    FN_DECODE(__bf16, DType::BF16, 1, 2, true, 1, 1, 2, "decode_swiglu_bf16_m16_n32_k1_u2"),
 };
 
-// wk 0: the first instance of (dt, mf, sw) in the table (its default).
-static const DecodeInstance* find_decode(DType dt, int mf, bool sw, int wk = 0) {
+// wk 0: the first instance of (dt, mf, sw, nf) in the table (its default).
+static const DecodeInstance* find_decode(DType dt, int mf, bool sw, int wk = 0, int nf = 1) {
   for (const DecodeInstance& d : kDecode)
-    if (d.dt == dt && d.mf == mf && d.sw == sw && (wk == 0 || d.wk == wk)) return &d;
+    if (d.dt == dt && d.mf == mf && d.sw == sw && (wk == 0 || d.wk == wk) && d.nf == nf) return &d;
   return nullptr;
+}
+
+// Column blocks per wave: two at up to 16 rows of bf16 once there are at
+// least 1536 column blocks (768 two-block waves, three per CU).
+static int decode_blocks_per_wave(DType dt, int64_t M, int64_t N) {
+  return dt == DType::BF16 && M <= 16 && ceil_div(N, 16) >= 1536 ? 2 : 1;
 }
 
 // k-split for bf16: 4 waves when there are at most 256 workgroups of one
@@ -606,7 +619,9 @@ static int decode_k_split(DType dt, int64_t M, int64_t N, bool swiglu, int mf) {
 FusedPlan plan_decode(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
   (void)K;
   const int mf = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  const DecodeInstance* d = find_decode(dt, mf, swiglu, decode_k_split(dt, M, N, swiglu, mf));
+  const int nf = decode_blocks_per_wave(dt, M, N);
+  const DecodeInstance* d = nf > 1 ? find_decode(dt, 1, swiglu, 1, nf)
+                                   : find_decode(dt, mf, swiglu, decode_k_split(dt, M, N, swiglu, mf));
   if (d == nullptr) d = find_decode(dt, 1, swiglu, decode_k_split(dt, M, N, swiglu, 1));   // bf16 rows tiled
   if (d == nullptr) d = find_decode(dt, 1, swiglu);
   FusedPlan p{};
@@ -623,7 +638,7 @@ FusedPlan plan_decode(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
 
 hipError_t launch_decode(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
                          int M, int K, int N, float eps, hipStream_t stream) {
-  const DecodeInstance* d = find_decode(dt, p.mf, wu != nullptr, p.waves);   // one column group: waves = k-split
+  const DecodeInstance* d = find_decode(dt, p.mf, wu != nullptr, p.waves, p.nf);   // one column group: waves = k-split
   if (d == nullptr) return hipErrorInvalidValue;
   DecodeArgs a;
   a.x = x;

@@ -62,6 +62,17 @@ def test_rows_just_past_decode_on_wide_projections(lib):
     assert lib.fn_kernel_name(96, 4096, 8192, 0, F32).decode().startswith("decode_f32")
 
 
+def test_very_wide_projections_take_two_column_blocks_per_wave(lib):
+    # up to 16 rows of bf16 with at least 1536 column blocks (an LM head):
+    # the register-x decode kernel with two column blocks per wave
+    assert lib.fn_kernel_name(16, 4096, 32000, 0, BF16).decode() == "decode_bf16_m16_n32_k1_u4"
+    assert lib.fn_kernel_name(1, 4096, 128256, 0, BF16).decode() == "decode_bf16_m16_n32_k1_u4"
+    assert lib.fn_kernel_name(8, 4096, 24576, 1, BF16).decode() == "decode_swiglu_bf16_m16_n32_k1_u2"
+    assert lib.fn_kernel_name(16, 4096, 24560, 0, BF16).decode() == "decode_bf16_m16_n16_k1_u4"
+    assert lib.fn_kernel_name(17, 4096, 32000, 0, BF16).decode().startswith("decode_bf16_m32")
+    assert lib.fn_kernel_name(16, 4096, 32000, 0, F32).decode().startswith("decode_f32_m16_n16")
+
+
 def test_kernel_name_invalid(lib):
     assert lib.fn_kernel_name(0, 4096, 16, 0, BF16) == b"invalid"
     assert lib.fn_kernel_name(4, 12, 16, 0, BF16) == b"invalid"

@@ -69,6 +69,19 @@ def test_rows_tiled_decode_parity(gpu_lib, M, K, N, swiglu):
     assert_close(fused(gpu_lib, inp), reference(inp), "bf16", f"rows tiled {M}x{K}x{N} swiglu={swiglu}")
 
 
+@pytest.mark.parametrize("M,K,N,swiglu", [(16, 136, 24587, False), (1, 264, 32000, False), (11, 136, 24600, True),
+                                          (16, 72, 25000, True)])
+def test_two_block_decode_parity(gpu_lib, M, K, N, swiglu):
+    """Up to 16 rows of a projection with at least 1536 column blocks run
+    the register-x decode kernel with two column blocks per wave (an odd
+    block count leaves the last wave one block; ragged K and N): every
+    output against the oracle."""
+    import torch
+    assert "_n32_" in gpu_lib.kernel_name(M, K, N, swiglu, torch.bfloat16)
+    inp = W.random_inputs(M, K, N, "bf16", seed=5 * M + K + N + swiglu, swiglu=swiglu)
+    assert_close(fused(gpu_lib, inp), reference(inp), "bf16", f"two-block decode {M}x{K}x{N} swiglu={swiglu}")
+
+
 @pytest.mark.parametrize("M,K,N,swiglu", [(129, 264, 8200, False), (200, 1032, 8192, True), (256, 4096, 12288, False),
                                           (161, 136, 8208, True)])
 def test_prefill_128_row_tiles_parity(gpu_lib, M, K, N, swiglu):
