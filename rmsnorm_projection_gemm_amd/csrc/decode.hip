@@ -326,8 +326,9 @@ __global__ __launch_bounds__(kWave * WN * WK) void decode_kernel(DecodeArgs a) {
 // measured on MI355X over the 65 calls of a 32-layer step at 8 rows, 1.416
 // against 1.468 ms for one block (three: 1.427, four: 1.444), the same bits
 // (each column's k order does not depend on how many blocks a wave holds).
-// A single call does not gain from it: its few hundred waves would no
-// longer spread evenly over the CUs.
+// A single call of QKV or gate/up width does not gain from it: its few
+// hundred waves would no longer spread evenly over the CUs (an LM head's
+// thousands do, and take the decode kernel's two-block instances).
 struct GroupCall {
   DecodeArgs a;
   const float* sg;   // fp8 weights: column scales of W'_gate (else unused)
@@ -537,8 +538,9 @@ void grouped_call_fill(void* dst, const void* x, const void* wg, const void* wu,
   *static_cast<GroupCall*>(dst) = g;
 }
 
-// Kernel instances.  The table maps (dtype, row capacity, SwiGLU) to a tile
-// configuration; launch_decode looks the instance up by the same key.
+// Kernel instances.  The table maps (dtype, row capacity, SwiGLU, k-split,
+// column blocks per wave) to a tile configuration; launch_decode looks the
+// instance up by the same key.
 struct DecodeInstance {
   const void* fn;
   DType dt;

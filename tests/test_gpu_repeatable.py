@@ -42,6 +42,11 @@ CASES = {
     "decode_qkv": (16, 4096, 12288, False),
     "decode_ffn": (64, 4096, 11008, True),
     "decode_ffn_m32": (32, 4096, 11008, True),
+    "decode_head": (16, 4096, 32000, False),          # two column blocks per wave
+    "decode_qkv_m128": (128, 4096, 12288, False),     # the LDS-shared-x kernel's 128-row rung
+    "decode_ffn_m128": (128, 4096, 11008, True),
+    "prefill_qkv_m256": (256, 4096, 12288, False),    # 128 x 128 prefill tiles
+    "prefill_ffn_m200": (200, 4096, 11008, True),
 }
 
 
@@ -66,7 +71,7 @@ def test_fused_repeatable(gpu_lib, case):
     _repeat(call, lambda y: [y])
 
 
-@pytest.mark.parametrize("M", [16, 64, 4096])
+@pytest.mark.parametrize("M", [16, 64, 128, 256, 4096])
 def test_fp8_weights_repeatable(gpu_lib, M):
     import torch
     fn = gpu_lib
