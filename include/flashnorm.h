@@ -211,9 +211,10 @@ fn_status fn_fold_weights_fp8(const void* g, const void* W, void* W8_packed, flo
  *   y[m][n] = round_bf16( s[n] * (sum_k x[m][k] * q[k][n]) / sqrt(sum_k x[m][k]^2 / K + eps) )
  * x: [M,K] bf16; W8_packed, scales: from fn_fold_weights_fp8 for this K, N;
  * y: [M,N] bf16, fully overwritten.  scales must be 4-byte aligned.
- * Instances: the LDS-shared-x decode kernel up to 64 rows, the prefill
- * kernel with fp8 weights above (the codes decoded exactly to bf16 operands
- * inside the k loop). */
+ * Instances: the LDS-shared-x decode kernel up to 64 rows (up to 256 on
+ * projections of at least 512 column blocks, the row blocks tiled), the
+ * prefill kernel with fp8 weights above (the codes decoded exactly to bf16
+ * operands inside the k loop). */
 fn_status fn_norm_proj_fp8(const void* x, const void* W8_packed, const float* scales, void* y,
                            int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream);
 
@@ -254,8 +255,10 @@ const char* fn_kernel_name(int64_t M, int64_t K, int64_t N, int swiglu, fn_dtype
  * out_codes:  [M,N] row-major bytes, fully overwritten (no alignment needed).
  * out_scales: [M, ceil(N/16)] row-major fp32, 4-byte aligned, fully
  *             overwritten.
- * x is bf16.  Instances: the LDS-shared-x decode kernel up to 64 rows, the
- * prefill kernel above (bf16 or fp8 weights).
+ * x is bf16.  Instances: the LDS-shared-x decode kernel up to 64 rows (on
+ * projections of at least 512 column blocks up to 128 rows with bf16
+ * weights and 256 with fp8, 64-row blocks tiled), the prefill kernel above
+ * (bf16 or fp8 weights).
  * ------------------------------------------------------------------------- */
 
 /* bf16 packed weights (fn_fold_weights with FN_BF16). */
@@ -337,11 +340,13 @@ const char* fn_kernel_name_adaln(int64_t M, int64_t K, int64_t N, int64_t T, int
 /* Two-launch form of the two AdaLN calls above, any M.  A pre-pass
  * (fn_adaln_modulate below) writes the modulated operand and 1/RMS of each
  * raw row into a caller workspace; the plain projection kernel of the row
- * count (the LDS-shared-x decode kernel up to 64 rows, the prefill kernel
- * above) then projects that operand and applies the deferred 1/RMS and the
- * bias rows in its epilogue.  The modulation is done once per row, and any
- * T is served.  The page's own AdaLN FC1 kernel runs as two launches as well
- * ([FlashInfer #5521] "Fused Kernel on SM120").  Same arithmetic and
+ * count (the LDS-shared-x decode kernel up to 64 rows -- up to 128 rows,
+ * 64-row blocks tiled, on projections of at least 512 column blocks except
+ * for the SwiGLU pair -- the prefill kernel above) then projects that
+ * operand and applies the deferred 1/RMS and the bias rows in its
+ * epilogue.  The modulation is done once per row, and any T is served.  The
+ * page's own AdaLN FC1 kernel runs as two launches as well ([FlashInfer
+ * #5521] "Fused Kernel on SM120").  Same arithmetic and
  * arguments as fn_norm_proj_adaln / fn_norm_proj_swiglu_adaln, plus:
  * workspace: device memory of at least fn_adaln_workspace_bytes(M, K)
  *   bytes, 256-byte aligned, overlapping no other argument.  The call writes
@@ -399,7 +404,9 @@ const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, 
 /* AdaLN with fp8 weights (fn_fold_weights_fp8 of the plain W, g = NULL:
  * E4M3 codes, one scale per output column), in two launches for every M:
  * the pre-pass above, then the fp8-weight kernel of the row count on the
- * modulated operand (decode up to 64 rows, prefill above), with
+ * modulated operand (decode up to 64 rows -- on projections of at least
+ * 512 column blocks up to 256, 128 for the SwiGLU pair, 64-row blocks
+ * tiled -- prefill above), with
  *   y[m] = s * (u[m] * q) / RMS(x[m]) + bias[idx[m]].
  * The pages' AdaLN FC1 kernel is an fp8 kernel with pre-processed weights
  * and scales ([FlashInfer #5521] "Fused Kernel on SM120").  bias rows come
@@ -433,7 +440,9 @@ const char* fn_kernel_name_adaln_fp8(int64_t M, int64_t K, int64_t N, int64_t T,
  * codes, one fp32 scale per 16-column row block, as fn_norm_proj_swiglu_q8),
  * in two launches for every M: the pre-pass, then the q8 kernel of the row
  * count on the modulated operand (the LDS-shared-x decode kernel up to 64
- * rows, the prefill kernel above, with bf16 or fp8 weights).  The AdaLN FC1
+ * rows -- on projections of at least 512 column blocks up to 128 rows with
+ * bf16 weights and 256 with fp8, 64-row blocks tiled -- the prefill kernel
+ * above, with bf16 or fp8 weights).  The AdaLN FC1
  * block of [FlashInfer #5521] ("Segmented Chain": norm + AdaLN, FC1, SwiGLU,
  * quantisation for the next projection) with the output format of
  * [FlashInfer #4040] as read for fn_norm_proj_swiglu_q8.  The block values

@@ -118,6 +118,20 @@ bool decode_rows_tiled(int64_t M, int64_t N, bool f8) {
   return M > 64 && M <= (f8 ? 256 : 128) && (N + 15) / 16 >= 512;
 }
 
+// The same rows for the forms whose decode kernels have no 128-row rung --
+// SwiGLU with fp8 output and the AdaLN two-launch calls -- run its 64-row
+// instances tiled over the rows.  Measured on MI355X, K = 4096, 65-256 rows:
+// fp8 output 90-104 -> 45-75 us (fp8 weights) and 90-91 -> 65-67 us (bf16,
+// up to 128 rows); AdaLN QKV 87-93 -> 32-66 us (fp8) and 78-79 -> 43-52 us
+// (bf16); AdaLN with fp8 output 98-108 -> 50-82 us and 94-95 -> 70-74 us.
+// The AdaLN SwiGLU pair with bf16 output carries its operand as a hi + lo
+// pair, twice the x bytes per row block: with fp8 weights it gains up to 128
+// rows (86-89 -> 65-74 us) and loses beyond (95-101 -> 111-129 us), with bf16
+// weights it loses (81-86 -> 87-93 us), so those stay on the prefill kernel.
+bool premod_rows_tiled(int64_t M, int64_t N, bool f8, bool split) {
+  return decode_rows_tiled(M, N, f8) && (!split || (f8 && M <= 128));
+}
+
 fn_status fp8_common(const void* x, const void* wg, const float* sg, const void* wu, const float* su, void* y,
                      int64_t M, int64_t K, int64_t N, float eps, hipStream_t stream, bool swiglu,
                      bool check_only = false) {
@@ -183,7 +197,7 @@ fn_status q8_common(const void* x, const void* wg, const float* sg, const void* 
   if (overlap(codes, cb, scales, qb)) return fail(FN_ERR_ALIAS, "out_codes overlaps out_scales");
   if (check_only) return FN_OK;
   uint8_t* q = static_cast<uint8_t*>(codes);
-  if (M > 64) {
+  if (M > 64 && !decode_rows_tiled(M, N, f8)) {
     const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, f8);
     if (f8)
       return hip_status(fn::launch_prefill_fp8(plan, x, wg, sg, wu, su, nullptr, (int)M, (int)K, (int)N, eps, stream, q,
@@ -273,7 +287,7 @@ fn_status adaln_ws_common(const void* x, const float* mod, const int* idx, const
   FN_TRY(hip_status(fn::launch_adaln_modulate(x, mod, idx, (int)T, u, rs, (int)M, (int)K, eps, stream, swiglu),
                     "adaln_modulate"));
   const fn::AdalnArgs ad{nullptr, idx, bg, swiglu ? bu : nullptr, (int)T};
-  if (M <= 64) {
+  if (M <= 64 || premod_rows_tiled(M, N, false, swiglu)) {
     const fn::FusedPlan plan = fn::plan_decode_premod(M, N, swiglu);
     return hip_status(fn::launch_decode_premod(plan, u, rs, wg, nullptr, swiglu ? wu : nullptr, nullptr, y, (int)M,
                                                (int)K, (int)N, ad, stream),
@@ -286,7 +300,8 @@ fn_status adaln_ws_common(const void* x, const float* mod, const int* idx, const
 }
 
 // Two-launch AdaLN with fp8 weights (E4M3 codes + column scales), every M:
-// the pre-pass, then the fp8 decode kernel on the modulated operand.
+// the pre-pass, then the fp8 decode or prefill kernel on the modulated
+// operand.
 fn_status adaln_fp8_ws_common(const void* x, const float* mod, const int* idx, const void* wg, const float* sg,
                               const float* bg, const void* wu, const float* su, const float* bu, void* y, int64_t M,
                               int64_t K, int64_t N, int64_t T, float eps, void* ws, int64_t ws_bytes,
@@ -329,7 +344,7 @@ fn_status adaln_fp8_ws_common(const void* x, const float* mod, const int* idx, c
   FN_TRY(hip_status(fn::launch_adaln_modulate(x, mod, idx, (int)T, u, rs, (int)M, (int)K, eps, stream, swiglu),
                     "adaln_modulate"));
   const fn::AdalnArgs ad{nullptr, idx, bg, swiglu ? bu : nullptr, (int)T};
-  if (M > 64) {
+  if (M > 64 && !premod_rows_tiled(M, N, true, swiglu)) {
     const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu, false, true, true);
     return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, swiglu ? wu : nullptr, y, (int)M, (int)K, (int)N, ad,
                                                 stream, nullptr, nullptr, sg, swiglu ? su : nullptr),
@@ -387,7 +402,7 @@ fn_status adaln_q8_ws_common(const void* x, const float* mod, const int* idx, co
                     "adaln_modulate"));
   const fn::AdalnArgs ad{nullptr, idx, bg, bu, (int)T};
   uint8_t* q = static_cast<uint8_t*>(codes);
-  if (M > 64) {
+  if (M > 64 && !premod_rows_tiled(M, N, f8, false)) {
     const fn::FusedPlan plan = fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, true, f8);
     return hip_status(fn::launch_prefill_premod(plan, u, rs, wg, wu, nullptr, (int)M, (int)K, (int)N, ad, stream, q,
                                                 qscales, f8 ? sg : nullptr, f8 ? su : nullptr),
@@ -604,7 +619,8 @@ fn_status fn_norm_proj_swiglu_fp8_q8(const void* x, const void* W8_gate, const f
 
 const char* fn_kernel_name_q8(int64_t M, int64_t K, int64_t N, int fp8_weights) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
-  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, fp8_weights != 0).name;
+  if (M > 64 && !decode_rows_tiled(M, N, fp8_weights != 0))
+    return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, false, fp8_weights != 0).name;
   return fn::plan_decode_q8(fp8_weights != 0, M, N).name;
 }
 
@@ -739,7 +755,8 @@ fn_status fn_norm_proj_swiglu_adaln_static(const void* x, const float* mod, cons
 
 const char* fn_kernel_name_adaln_ws(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
-  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, true).name;
+  if (M > 64 && !premod_rows_tiled(M, N, false, swiglu != 0))
+    return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, true).name;
   if (M > kAdalnOneLaunchRows) return fn::plan_decode_premod(M, N, swiglu != 0).name;
   return fn_kernel_name_adaln(M, K, N, T, swiglu);
 }
@@ -768,7 +785,8 @@ fn_status fn_norm_proj_swiglu_adaln_fp8_ws(const void* x, const float* mod, cons
 
 const char* fn_kernel_name_adaln_fp8(int64_t M, int64_t K, int64_t N, int64_t T, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
-  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, true, true).name;
+  if (M > 64 && !premod_rows_tiled(M, N, true, swiglu != 0))
+    return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, true, true).name;
   return fn::plan_decode_premod(M, N, swiglu != 0, true).name;
 }
 
@@ -793,7 +811,8 @@ fn_status fn_norm_proj_swiglu_adaln_fp8_q8_ws(const void* x, const float* mod, c
 
 const char* fn_kernel_name_adaln_q8(int64_t M, int64_t K, int64_t N, int64_t T, int fp8_weights) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN || T < 1) return "invalid";
-  if (M > 64) return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, true, fp8_weights != 0).name;
+  if (M > 64 && !premod_rows_tiled(M, N, fp8_weights != 0, false))
+    return fn::plan_prefill(fn::DType::BF16, M, K, N, true, true, true, fp8_weights != 0).name;
   return fn::plan_decode_q8_premod(fp8_weights != 0, M, N).name;
 }
 

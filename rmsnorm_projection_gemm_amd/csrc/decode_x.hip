@@ -702,9 +702,10 @@ hipError_t launch_adaln(const FusedPlan& p, const void* x, const void* wg, const
   return launch_decode_x_instance(*d, x, wg, wu, y, M, K, N, eps, stream, nullptr, nullptr, nullptr, nullptr, &ad);
 }
 
-// Two-launch AdaLN, 17..64 rows: the plain 32- and 64-row rungs on the
-// operand the pre-pass modulated, 1/RMS from the pre-pass, bias rows added in
-// the epilogue (no Gram blocks).
+// Two-launch AdaLN, 17..64 rows (and, the 64-row tiles repeated over
+// grid.y, 65..128 rows of wide projections): the plain 32- and 64-row rungs
+// on the operand the pre-pass modulated, 1/RMS from the pre-pass, bias rows
+// added in the epilogue (no Gram blocks).
 // SwiGLU: the split operand (LO).
 #define FN_DECODE_XE(MF, SW, NS, NAME)                                                                          \
   DecodeXInstance {                                                                                            \
@@ -736,7 +737,7 @@ static const DecodeXInstance kDecodeF8Ex[] = {
 };
 
 // SwiGLU with fp8 output on the pre-modulated operand: the q8 rungs above
-// (bf16 weights up to 64 rows; fp8 weights every M).
+// (every M; past 64 rows the 64-row tiles repeat over grid.y).
 #define FN_DECODE_XQE(MF, NWV, U, F8, NAME)                                                                     \
   DecodeXInstance {                                                                                            \
     reinterpret_cast<const void*>(&decode_x_kernel<MF, 1, NWV, true, U, F8, true, false, 4, true>), MF, 1,     \
@@ -765,7 +766,7 @@ hipError_t launch_decode_q8_premod(bool f8_weights, const FusedPlan& p, const vo
                                    const void* wg, const float* sg, const void* wu, const float* su, uint8_t* q,
                                    float* qs, int M, int K, int N, const AdalnArgs& ad, hipStream_t stream) {
   const DecodeXInstance* d = find_q8_premod(f8_weights, p.mf);
-  if (d == nullptr || (!f8_weights && M > 16 * d->mf)) return hipErrorInvalidValue;
+  if (d == nullptr) return hipErrorInvalidValue;
   return launch_decode_x_instance(*d, u, wg, wu, nullptr, M, K, N, 0.f, stream, sg, su, q, qs, &ad, rs);
 }
 
@@ -780,12 +781,13 @@ hipError_t launch_decode_premod(const FusedPlan& p, const void* u, const float* 
   const bool f8 = sg != nullptr;
   const DecodeXInstance* d =
       f8 ? find_instance(kDecodeF8Ex, p.mf, wu != nullptr) : find_instance(kDecodeEx, p.mf, wu != nullptr);
-  if (d == nullptr || (!f8 && M > 16 * d->mf)) return hipErrorInvalidValue;
+  if (d == nullptr) return hipErrorInvalidValue;
   return launch_decode_x_instance(*d, u, wg, wu, y, M, K, N, 0.f, stream, sg, su, nullptr, nullptr, &ad, rs);
 }
 
-// SwiGLU with fp8 output, rows up to 64 (bf16 weights; larger M goes to the
-// prefill kernel) or any M (fp8 weights).
+// SwiGLU with fp8 output, every M (past 64 rows the 64-row tiles repeat over
+// grid.y; the API sends more than 128 rows with bf16 weights, 256 with fp8,
+// and more than 64 rows of narrow projections to the prefill kernel).
 static const DecodeXInstance* find_q8(bool f8, int mf) {
   for (const DecodeXInstance& d : kDecodeQ8)
     if (d.f8 == f8 && d.mf == mf) return &d;
@@ -800,7 +802,7 @@ hipError_t launch_decode_q8(bool f8_weights, const FusedPlan& p, const void* x, 
                             const void* wu, const float* su, uint8_t* q, float* qs, int M, int K, int N, float eps,
                             hipStream_t stream) {
   const DecodeXInstance* d = find_q8(f8_weights, p.mf);
-  if (d == nullptr || (!f8_weights && M > 16 * d->mf)) return hipErrorInvalidValue;
+  if (d == nullptr) return hipErrorInvalidValue;
   return launch_decode_x_instance(*d, x, wg, wu, nullptr, M, K, N, eps, stream, sg, su, q, qs);
 }
 

@@ -459,7 +459,15 @@ def test_swiglu_q8_codes_need_no_alignment_and_empty_is_ok(lib):
 def test_q8_kernel_names(lib):
     assert lib.fn_kernel_name_q8(16, 4096, 11008, 0).decode() == "decode_swiglu_bf16_q8_m16_xlds_w3_u2"
     assert lib.fn_kernel_name_q8(64, 4096, 11008, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
-    assert lib.fn_kernel_name_q8(65, 4096, 11008, 0).decode().startswith("prefill_swiglu_bf16_q8")
+    # past 64 rows of projections with at least 512 column blocks: the 64-row
+    # tiles repeated over the rows, up to 128 rows (bf16 weights) or 256 (fp8)
+    assert lib.fn_kernel_name_q8(65, 4096, 11008, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
+    assert lib.fn_kernel_name_q8(128, 4096, 8192, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
+    assert lib.fn_kernel_name_q8(129, 4096, 11008, 0).decode().startswith("prefill_swiglu_bf16_q8")
+    assert lib.fn_kernel_name_q8(65, 4096, 8176, 0).decode().startswith("prefill_swiglu_bf16_q8")
+    assert lib.fn_kernel_name_q8(256, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_q8_m64")
+    assert lib.fn_kernel_name_q8(257, 4096, 11008, 1).decode().startswith("prefill_swiglu_fp8_q8")
+    assert lib.fn_kernel_name_q8(65, 4096, 8176, 1).decode().startswith("prefill_swiglu_fp8_q8")
     assert lib.fn_kernel_name_q8(64, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_q8_m64")
     assert lib.fn_kernel_name_q8(4096, 4096, 11008, 1).decode() == "prefill_swiglu_fp8_q8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_q8(0, 4096, 16, 0) == b"invalid"
@@ -560,6 +568,12 @@ def test_adaln_ws_sizes_and_names(lib):
     assert (lib.fn_kernel_name_adaln_ws(65, 4096, 11008, 500, 1).decode() ==
             "prefill_swiglu_premod_split_bf16_256x128_w4x2_xl")
     assert lib.fn_kernel_name_adaln_ws(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_premod_split_bf16_m64_xlds_w3_u2"
+    # 65..128 rows of wide projections: the 64-row tiles repeated over the rows
+    # (not for the split SwiGLU operand)
+    assert lib.fn_kernel_name_adaln_ws(65, 4096, 12288, 4, 0).decode() == "decode_premod_bf16_m64_xlds_w3_u2_s5"
+    assert lib.fn_kernel_name_adaln_ws(128, 4096, 8192, 4, 0).decode() == "decode_premod_bf16_m64_xlds_w3_u2_s5"
+    assert lib.fn_kernel_name_adaln_ws(129, 4096, 12288, 4, 0).decode().startswith("prefill_premod_bf16")
+    assert lib.fn_kernel_name_adaln_ws(65, 4096, 8176, 4, 0).decode().startswith("prefill_premod_bf16")
     assert lib.fn_kernel_name_adaln_ws(16, 4096, 11008, 4, 1).decode() == "decode_swiglu_adaln_split_bf16_m16_xlds_w3_u2_s5"
     assert lib.fn_kernel_name_adaln_ws(17, 4096, 12288, 500, 0).decode() == "decode_premod_bf16_m32_xlds_w3_u2_s5"
     assert lib.fn_kernel_name_adaln_ws(16, 4096, 12288, 4, 0).decode() == "decode_adaln_bf16_m16_xlds_w3_u2_s5"
@@ -622,7 +636,13 @@ def test_adaln_fp8_sizes_and_names(lib):
             "decode_swiglu_fp8_premod_split_m64_xlds_w4_u2")
     assert (lib.fn_kernel_name_adaln_fp8(4096, 4096, 11008, 4, 1).decode() ==
             "prefill_swiglu_fp8_premod_split_256x128_w4x2_xl")
-    assert lib.fn_kernel_name_adaln_fp8(65, 4096, 12288, 4, 0).decode() == "prefill_fp8_premod_256x256_w4x2_xl"
+    assert lib.fn_kernel_name_adaln_fp8(65, 4096, 12288, 4, 0).decode() == "decode_fp8_premod_m64_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln_fp8(256, 4096, 12288, 4, 0).decode() == "decode_fp8_premod_m64_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln_fp8(257, 4096, 12288, 4, 0).decode() == "prefill_fp8_premod_256x256_w4x2_xl"
+    assert lib.fn_kernel_name_adaln_fp8(65, 4096, 8176, 4, 0).decode().startswith("prefill_fp8_premod")
+    assert (lib.fn_kernel_name_adaln_fp8(128, 4096, 11008, 4, 1).decode() ==
+            "decode_swiglu_fp8_premod_split_m64_xlds_w4_u2")
+    assert lib.fn_kernel_name_adaln_fp8(129, 4096, 11008, 4, 1).decode().startswith("prefill_swiglu_fp8_premod_split")
     assert lib.fn_kernel_name_adaln_fp8(0, 4096, 16, 4, 0) == b"invalid"
     sw = lib.fn_norm_proj_swiglu_adaln_fp8_ws
     assert sw(0x1000, 0x10000, 0x18000, 0x20000, 0x28000, 0x30000, 0x21000, None, 0x31000, 0x40000, 4, 16, 16, 2,
@@ -657,7 +677,11 @@ def test_norm_proj_swiglu_adaln_q8_ws_rejects(lib, kwargs, status, needle):
 def test_adaln_q8_names_and_fp8(lib):
     assert lib.fn_kernel_name_adaln_q8(16, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m16_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln_q8(64, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m64_xlds_w3_u2"
-    assert lib.fn_kernel_name_adaln_q8(65, 4096, 11008, 4, 0).decode() == "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"
+    assert lib.fn_kernel_name_adaln_q8(65, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m64_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln_q8(129, 4096, 11008, 4, 0).decode() == "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"
+    assert lib.fn_kernel_name_adaln_q8(65, 4096, 8176, 4, 0).decode().startswith("prefill_swiglu_bf16_q8_premod")
+    assert lib.fn_kernel_name_adaln_q8(256, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_q8_premod_m64_xlds_w4_u2"
+    assert lib.fn_kernel_name_adaln_q8(257, 4096, 11008, 4, 1).decode().startswith("prefill_swiglu_fp8_q8_premod")
     assert lib.fn_kernel_name_adaln_q8(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_q8_premod_m64_xlds_w4_u2"
     assert lib.fn_kernel_name_adaln_q8(4096, 4096, 11008, 4, 1).decode() == "prefill_swiglu_fp8_q8_premod_256x128_w4x2_xl"
     assert lib.fn_kernel_name_adaln_q8(0, 4096, 16, 4, 0) == b"invalid"

@@ -78,6 +78,19 @@ def test_adaln_ws_parity(gpu_lib, swiglu, M, K, N, T):
                        f"{'swiglu' if swiglu else 'proj'} adaln two launches {M}x{K}x{N} T={T}")
 
 
+@pytest.mark.parametrize("M,K,N,T", [(65, 264, 8200, 3), (128, 136, 8192, 40), (100, 4104, 8208, 5)])
+def test_adaln_ws_rows_tiled_parity(gpu_lib, M, K, N, T):
+    """65..128 rows of a projection with at least 512 column blocks: the
+    64-row decode tiles repeat over the rows on the modulated operand (the
+    SwiGLU pair, whose operand is split in two, stays on the prefill
+    kernel): every output."""
+    assert gpu_lib.kernel_name_adaln_ws(M, K, N, T, False).startswith("decode_premod_bf16_m64")
+    assert gpu_lib.kernel_name_adaln_ws(M, K, N, T, True).startswith("prefill_swiglu_premod_split")
+    c = AdalnCase(gpu_lib, M, K, N, T, False, seed=M * 3 + K + N + T, bad_idx=True)
+    y = to_f64(gpu_lib.norm_proj_adaln_ws(c.x, *c.args(), c.eps))
+    assert_adaln_close(y, c.reference(), c.value_error_bound(), f"proj adaln rows tiled {M}x{K}x{N} T={T}")
+
+
 @pytest.mark.parametrize("M,N,swiglu", [(16, 12288, False), (64, 11008, True), (64, 12288, False)])
 def test_adaln_decode_shapes(gpu_lib, M, N, swiglu):
     """The QKV and FFN decode shapes (K = 4096) with four table rows, every

@@ -28,6 +28,18 @@ def test_adaln_fp8_parity(gpu_lib, swiglu, M, K, N, T):
                        f"{'swiglu' if swiglu else 'proj'} adaln fp8 {M}x{K}x{N} T={T}")
 
 
+@pytest.mark.parametrize("M,K,N,T,swiglu", [(100, 264, 8200, 5, False), (256, 136, 8192, 3, False),
+                                             (65, 264, 8208, 7, True), (128, 72, 8200, 30, True)])
+def test_adaln_fp8_rows_tiled_parity(gpu_lib, M, K, N, T, swiglu):
+    """Past 64 rows of projections with at least 512 column blocks (up to
+    256 rows, 128 for the SwiGLU pair) the 64-row decode tiles repeat over
+    the rows on the modulated operand: every output."""
+    assert gpu_lib.kernel_name_adaln_fp8(M, K, N, T, swiglu).startswith(("decode_fp8", "decode_swiglu_fp8"))
+    y, c = _run(gpu_lib, M, K, N, T, swiglu, seed=M * 3 + K + N + T)
+    assert_adaln_close(y, c.reference(), c.value_error_bound(),
+                       f"{'swiglu' if swiglu else 'proj'} adaln fp8 rows tiled {M}x{K}x{N} T={T}")
+
+
 @pytest.mark.parametrize("M,N,swiglu", [(16, 12288, False), (64, 11008, True), (4096, 11008, True)])
 def test_adaln_fp8_decode_and_prefill_shapes(gpu_lib, M, N, swiglu):
     """The QKV and FFN decode shapes and the FFN prefill shape (K = 4096)

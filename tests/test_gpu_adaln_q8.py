@@ -33,6 +33,17 @@ def test_adaln_q8_parity(gpu_lib, weights, M, K, N, T):
     assert_q8_close(codes, scales, v, f"adaln q8 {weights} {M}x{K}x{N} T={T}", v_err=err)
 
 
+@pytest.mark.parametrize("weights,M,K,N,T", [("bf16", 96, 264, 8200, 4), ("bf16", 128, 72, 8192, 2),
+                                             ("fp8", 200, 136, 8208, 9), ("fp8", 256, 72, 8200, 3)])
+def test_adaln_q8_rows_tiled_parity(gpu_lib, weights, M, K, N, T):
+    """Past 64 rows of projections with at least 512 column blocks (up to
+    128 rows with bf16 weights, 256 with fp8) the 64-row decode tiles repeat
+    over the rows on the modulated operand: every output."""
+    assert gpu_lib.kernel_name_adaln_q8(M, K, N, T, weights == "fp8").startswith("decode_swiglu")
+    codes, scales, v, err = _run(gpu_lib, M, K, N, T, weights, seed=M * 7 + K + N + T)
+    assert_q8_close(codes, scales, v, f"adaln q8 rows tiled {weights} {M}x{K}x{N} T={T}", v_err=err)
+
+
 @pytest.mark.parametrize("weights", ["bf16", "fp8"])
 def test_adaln_q8_ffn_decode_shape(gpu_lib, weights):
     """The FFN decode shape (64 x 4096 -> 2 x 11008), four table rows."""

@@ -47,6 +47,18 @@ def test_q8_parity(gpu_lib, weights, M, K, N):
     assert_q8_close(codes, scales, v, f"q8 {weights} {M}x{K}x{N}")
 
 
+@pytest.mark.parametrize("weights,M,K,N", [("bf16", 65, 264, 8200), ("bf16", 128, 136, 8192), ("fp8", 100, 264, 8200),
+                                           ("fp8", 256, 72, 8208)])
+def test_q8_rows_tiled_parity(gpu_lib, weights, M, K, N):
+    """Past 64 rows of projections with at least 512 column blocks (up to
+    128 rows with bf16 weights, 256 with fp8) the 64-row decode tiles repeat
+    over the rows (ragged rows, K and N): every output against the oracle."""
+    assert gpu_lib.kernel_name_q8(M, K, N, weights == "fp8").startswith("decode_swiglu")
+    inp = W.random_inputs(M, K, N, "bf16", seed=M * 3 + K + N, swiglu=True)
+    codes, scales, v = (_bf16_case if weights == "bf16" else _fp8_case)(gpu_lib, inp)
+    assert_q8_close(codes, scales, v, f"q8 rows tiled {weights} {M}x{K}x{N}")
+
+
 @pytest.mark.parametrize("weights", ["bf16", "fp8"])
 def test_q8_ffn_decode_full(gpu_lib, weights):
     inp = W.make_inputs(W.FFN_DECODE)
