@@ -596,12 +596,17 @@ static const PrefillInstance kPrefill[] = {
     FN_PREFILL(4, 8, 4, 2, false, false, true, true, "prefill_fp8_premod_256x256_w4x2_xl"),
     FN_PREFILL_PAIR(true, "prefill_swiglu_fp8_premod_split_256x128_w4x2_xl"),
     FN_PREFILL(4, 4, 4, 2, true, true, true, true, "prefill_swiglu_fp8_q8_premod_256x128_w4x2_xl"),
-    // 129..256 rows of wide projections (at least 512 column blocks): 128-row
-    // tiles, twice the workgroups of 256-row tiles with half as many empty
-    // rows -- measured at K = 4096: QKV 64-66 -> 54-56 us, gate/up pairs
-    // 83 -> 72-74 us, the same bits; slower from 384 rows on
+    // 129..256 rows of wide projections (at least 512 column blocks) with
+    // bf16 weights: 128-row tiles, twice the workgroups of 256-row tiles with
+    // half as many empty rows -- measured at K = 4096: QKV 64-66 -> 54-56 us,
+    // gate/up pairs 83 -> 72-74 us (fp8 output 92-100 -> 75-79 us), AdaLN
+    // QKV on the modulated operand 78-86 -> 59-60 us (fp8 output 94-105 ->
+    // 81-86 us), the same bits; slower from 384 rows on
     FN_PREFILL(2, 4, 4, 2, false, false, false, false, "prefill_bf16_128x128_w4x2"),
     FN_PREFILL(2, 4, 4, 2, true, false, false, false, "prefill_swiglu_bf16_128x128_w4x2"),
+    FN_PREFILL(2, 4, 4, 2, true, true, false, false, "prefill_swiglu_bf16_q8_128x128_w4x2"),
+    FN_PREFILL(2, 4, 4, 2, false, false, true, false, "prefill_premod_bf16_128x128_w4x2"),
+    FN_PREFILL(2, 4, 4, 2, true, true, true, false, "prefill_swiglu_bf16_q8_premod_128x128_w4x2"),
 };
 
 // The first instance with exactly these flags (q8 implies SwiGLU), mf
@@ -621,8 +626,11 @@ FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, b
   (void)K;
   const bool plain = !swiglu && !q8 && !ex;
   const bool narrow = plain && ceil_div(N, 256) * ceil_div(M, 256) < 128;
-  const bool rows128 = !q8 && !ex && !f8 && M <= 256 && ceil_div(N, 16) >= 512;
-  const PrefillInstance& d = rows128 ? pick(swiglu, false, false, false, 8, 8) : pick(swiglu, q8, ex, f8, narrow ? 8 : 0);
+  // 128-row tiles: bf16 weights, not the split AdaLN operand (its tiles
+  // already hold 128 output rows)
+  const bool split = ex && swiglu && !q8;
+  const bool rows128 = !f8 && !split && M <= 256 && ceil_div(N, 16) >= 512;
+  const PrefillInstance& d = rows128 ? pick(swiglu, q8, ex, false, 8, 8) : pick(swiglu, q8, ex, f8, narrow ? 8 : 0);
   FusedPlan p{};
   p.kind = f8 ? 11 : (ex ? (q8 ? 10 : 8) : (q8 ? 5 : 1));
   p.mf = d.fm * d.wm;
@@ -689,7 +697,7 @@ hipError_t launch_prefill_premod(const FusedPlan& p, const void* u, const float*
   if (q != nullptr && wu == nullptr) return hipErrorInvalidValue;
   const bool f8 = sg != nullptr;
   if (f8 && wu != nullptr && su == nullptr) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, true, f8);
+  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, true, f8, p.nf, p.mf);
   PrefillArgs a{};
   a.sg = sg;
   a.su = su;

@@ -463,7 +463,8 @@ def test_q8_kernel_names(lib):
     # tiles repeated over the rows, up to 128 rows (bf16 weights) or 256 (fp8)
     assert lib.fn_kernel_name_q8(65, 4096, 11008, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
     assert lib.fn_kernel_name_q8(128, 4096, 8192, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
-    assert lib.fn_kernel_name_q8(129, 4096, 11008, 0).decode().startswith("prefill_swiglu_bf16_q8")
+    assert lib.fn_kernel_name_q8(129, 4096, 11008, 0).decode() == "prefill_swiglu_bf16_q8_128x128_w4x2"
+    assert lib.fn_kernel_name_q8(257, 4096, 11008, 0).decode() == "prefill_swiglu_bf16_q8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_q8(65, 4096, 8176, 0).decode().startswith("prefill_swiglu_bf16_q8")
     assert lib.fn_kernel_name_q8(256, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_q8_m64")
     assert lib.fn_kernel_name_q8(257, 4096, 11008, 1).decode().startswith("prefill_swiglu_fp8_q8")
@@ -572,7 +573,10 @@ def test_adaln_ws_sizes_and_names(lib):
     # (not for the split SwiGLU operand)
     assert lib.fn_kernel_name_adaln_ws(65, 4096, 12288, 4, 0).decode() == "decode_premod_bf16_m64_xlds_w3_u2_s5"
     assert lib.fn_kernel_name_adaln_ws(128, 4096, 8192, 4, 0).decode() == "decode_premod_bf16_m64_xlds_w3_u2_s5"
-    assert lib.fn_kernel_name_adaln_ws(129, 4096, 12288, 4, 0).decode().startswith("prefill_premod_bf16")
+    assert lib.fn_kernel_name_adaln_ws(129, 4096, 12288, 4, 0).decode() == "prefill_premod_bf16_128x128_w4x2"
+    assert lib.fn_kernel_name_adaln_ws(257, 4096, 12288, 4, 0).decode() == "prefill_premod_bf16_256x256_w4x2_xl"
+    assert (lib.fn_kernel_name_adaln_ws(200, 4096, 11008, 4, 1).decode() ==
+            "prefill_swiglu_premod_split_bf16_256x128_w4x2_xl")
     assert lib.fn_kernel_name_adaln_ws(65, 4096, 8176, 4, 0).decode().startswith("prefill_premod_bf16")
     assert lib.fn_kernel_name_adaln_ws(16, 4096, 11008, 4, 1).decode() == "decode_swiglu_adaln_split_bf16_m16_xlds_w3_u2_s5"
     assert lib.fn_kernel_name_adaln_ws(17, 4096, 12288, 500, 0).decode() == "decode_premod_bf16_m32_xlds_w3_u2_s5"
@@ -678,7 +682,8 @@ def test_adaln_q8_names_and_fp8(lib):
     assert lib.fn_kernel_name_adaln_q8(16, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m16_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln_q8(64, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m64_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln_q8(65, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m64_xlds_w3_u2"
-    assert lib.fn_kernel_name_adaln_q8(129, 4096, 11008, 4, 0).decode() == "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"
+    assert lib.fn_kernel_name_adaln_q8(129, 4096, 11008, 4, 0).decode() == "prefill_swiglu_bf16_q8_premod_128x128_w4x2"
+    assert lib.fn_kernel_name_adaln_q8(257, 4096, 11008, 4, 0).decode() == "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"
     assert lib.fn_kernel_name_adaln_q8(65, 4096, 8176, 4, 0).decode().startswith("prefill_swiglu_bf16_q8_premod")
     assert lib.fn_kernel_name_adaln_q8(256, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_q8_premod_m64_xlds_w4_u2"
     assert lib.fn_kernel_name_adaln_q8(257, 4096, 11008, 4, 1).decode().startswith("prefill_swiglu_fp8_q8_premod")

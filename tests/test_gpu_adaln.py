@@ -91,6 +91,16 @@ def test_adaln_ws_rows_tiled_parity(gpu_lib, M, K, N, T):
     assert_adaln_close(y, c.reference(), c.value_error_bound(), f"proj adaln rows tiled {M}x{K}x{N} T={T}")
 
 
+@pytest.mark.parametrize("M,K,N,T", [(129, 72, 8192, 2), (160, 264, 8200, 9)])
+def test_adaln_ws_prefill_128_row_tiles_parity(gpu_lib, M, K, N, T):
+    """129..256 rows of a wide projection: the prefill kernel's 128-row
+    tiles on the modulated operand, every output."""
+    assert gpu_lib.kernel_name_adaln_ws(M, K, N, T, False) == "prefill_premod_bf16_128x128_w4x2"
+    c = AdalnCase(gpu_lib, M, K, N, T, False, seed=M + K + N + T, bad_idx=True)
+    y = to_f64(gpu_lib.norm_proj_adaln_ws(c.x, *c.args(), c.eps))
+    assert_adaln_close(y, c.reference(), c.value_error_bound(), f"proj adaln 128-row tiles {M}x{K}x{N} T={T}")
+
+
 @pytest.mark.parametrize("M,N,swiglu", [(16, 12288, False), (64, 11008, True), (64, 12288, False)])
 def test_adaln_decode_shapes(gpu_lib, M, N, swiglu):
     """The QKV and FFN decode shapes (K = 4096) with four table rows, every

@@ -44,6 +44,15 @@ def test_adaln_q8_rows_tiled_parity(gpu_lib, weights, M, K, N, T):
     assert_q8_close(codes, scales, v, f"adaln q8 rows tiled {weights} {M}x{K}x{N} T={T}", v_err=err)
 
 
+def test_adaln_q8_prefill_128_row_tiles_parity(gpu_lib):
+    """129..256 rows of a wide projection with bf16 weights: the prefill
+    kernel's 128-row tiles on the modulated operand, every output."""
+    M, K, N, T = 256, 136, 8208, 6
+    assert "128x128" in gpu_lib.kernel_name_adaln_q8(M, K, N, T, False)
+    codes, scales, v, err = _run(gpu_lib, M, K, N, T, "bf16", seed=91)
+    assert_q8_close(codes, scales, v, f"adaln q8 128-row tiles {M}x{K}x{N}", v_err=err)
+
+
 @pytest.mark.parametrize("weights", ["bf16", "fp8"])
 def test_adaln_q8_ffn_decode_shape(gpu_lib, weights):
     """The FFN decode shape (64 x 4096 -> 2 x 11008), four table rows."""

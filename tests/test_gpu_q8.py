@@ -59,6 +59,16 @@ def test_q8_rows_tiled_parity(gpu_lib, weights, M, K, N):
     assert_q8_close(codes, scales, v, f"q8 rows tiled {weights} {M}x{K}x{N}")
 
 
+@pytest.mark.parametrize("M,K,N", [(129, 72, 8192), (200, 264, 8200)])
+def test_q8_prefill_128_row_tiles_parity(gpu_lib, M, K, N):
+    """129..256 rows of a wide projection with bf16 weights: the prefill
+    kernel's 128-row tiles with the fp8 epilogue, every output."""
+    assert "128x128" in gpu_lib.kernel_name_q8(M, K, N, False)
+    inp = W.random_inputs(M, K, N, "bf16", seed=M + K * 3 + N, swiglu=True)
+    codes, scales, v = _bf16_case(gpu_lib, inp)
+    assert_q8_close(codes, scales, v, f"q8 128-row tiles {M}x{K}x{N}")
+
+
 @pytest.mark.parametrize("weights", ["bf16", "fp8"])
 def test_q8_ffn_decode_full(gpu_lib, weights):
     inp = W.make_inputs(W.FFN_DECODE)
