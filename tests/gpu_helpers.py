@@ -251,7 +251,8 @@ class AdalnCase:
     def value_error_bound(self, rows=None, split=None):
         """Per-element bound on |kernel value - reference| before the output
         rounding, from the arithmetic: the bf16 operand x * mod rounded once
-        is within 2^-9 of its value (split in two bf16 parts: 2^-16), the
+        is within 2^-8 of its value (relative: an 8-bit significand rounded
+        to nearest; split in two bf16 parts, 2^-16), the
         weights are exact (bf16, or E4M3 codes decoded exactly), sums are
         fp32 (1e-5 of the sum of magnitudes), and the table itself is an fp32
         rounding of g * (1 + scale) (2^-24).  SwiGLU propagates the bounds on
@@ -265,7 +266,7 @@ class AdalnCase:
         r = oracle.rms(x, self.eps)[:, None]
         xm = np.abs(x * mod)
         ones = np.ones(self.K)
-        rel = (2.0 ** -16 if split else 2.0 ** -9) + 2.0 ** -23 + 1e-5
+        rel = (2.0 ** -16 if split else 2.0 ** -8) + 2.0 ** -23 + 1e-5
 
         def err(Wm):
             if self.weights == "bf16":

@@ -78,7 +78,7 @@ def test_adaln_ws_parity(gpu_lib, swiglu, M, K, N, T):
                        f"{'swiglu' if swiglu else 'proj'} adaln two launches {M}x{K}x{N} T={T}")
 
 
-@pytest.mark.parametrize("M,K,N,T", [(65, 264, 8200, 3), (128, 136, 8192, 40), (100, 4104, 8208, 5)])
+@pytest.mark.parametrize("M,K,N,T", [(65, 264, 8200, 3), (128, 136, 8192, 40), (100, 4104, 8208, 5), (90, 8, 8192, 2)])
 def test_adaln_ws_rows_tiled_parity(gpu_lib, M, K, N, T):
     """65..128 rows of a projection with at least 512 column blocks: the
     64-row decode tiles repeat over the rows on the modulated operand (the

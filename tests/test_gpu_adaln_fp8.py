@@ -29,7 +29,8 @@ def test_adaln_fp8_parity(gpu_lib, swiglu, M, K, N, T):
 
 
 @pytest.mark.parametrize("M,K,N,T,swiglu", [(100, 264, 8200, 5, False), (256, 136, 8192, 3, False),
-                                             (65, 264, 8208, 7, True), (128, 72, 8200, 30, True)])
+                                             (65, 264, 8208, 7, True), (128, 72, 8200, 30, True),
+                                             (150, 8, 8192, 2, False), (70, 8, 8200, 2, True)])
 def test_adaln_fp8_rows_tiled_parity(gpu_lib, M, K, N, T, swiglu):
     """Past 64 rows of projections with at least 512 column blocks (up to
     256 rows, 128 for the SwiGLU pair) the 64-row decode tiles repeat over

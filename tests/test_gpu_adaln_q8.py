@@ -34,7 +34,8 @@ def test_adaln_q8_parity(gpu_lib, weights, M, K, N, T):
 
 
 @pytest.mark.parametrize("weights,M,K,N,T", [("bf16", 96, 264, 8200, 4), ("bf16", 128, 72, 8192, 2),
-                                             ("fp8", 200, 136, 8208, 9), ("fp8", 256, 72, 8200, 3)])
+                                             ("fp8", 200, 136, 8208, 9), ("fp8", 256, 72, 8200, 3),
+                                             ("bf16", 77, 8, 8192, 2), ("fp8", 129, 8, 8200, 2)])
 def test_adaln_q8_rows_tiled_parity(gpu_lib, weights, M, K, N, T):
     """Past 64 rows of projections with at least 512 column blocks (up to
     128 rows with bf16 weights, 256 with fp8) the 64-row decode tiles repeat

@@ -47,8 +47,8 @@ def test_q8_parity(gpu_lib, weights, M, K, N):
     assert_q8_close(codes, scales, v, f"q8 {weights} {M}x{K}x{N}")
 
 
-@pytest.mark.parametrize("weights,M,K,N", [("bf16", 65, 264, 8200), ("bf16", 128, 136, 8192), ("fp8", 100, 264, 8200),
-                                           ("fp8", 256, 72, 8208)])
+@pytest.mark.parametrize("weights,M,K,N", [("bf16", 65, 264, 8200), ("bf16", 128, 136, 8192), ("bf16", 97, 8, 8192),
+                                           ("fp8", 100, 264, 8200), ("fp8", 256, 72, 8208), ("fp8", 200, 8, 8192)])
 def test_q8_rows_tiled_parity(gpu_lib, weights, M, K, N):
     """Past 64 rows of projections with at least 512 column blocks (up to
     128 rows with bf16 weights, 256 with fp8) the 64-row decode tiles repeat
