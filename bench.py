@@ -143,7 +143,8 @@ def pct(sorted_vals, q):
 # Sources each workload's dominant kernel is built from.
 KERNEL_SOURCES = {"prefill_qkv": ("prefill.hip", "fn_device.h"), "ffn_decode": ("decode_x.hip", "fn_device.h"),
                   "qkv_decode_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_fp8": ("decode_x.hip", "fn_device.h"),
-                  "decode_step_fp8": ("decode_x.hip", "fn_device.h"), "ffn_decode_q8": ("decode_x.hip", "fn_device.h"),
+                  # a decode step's HBM traffic is counted on its grouped launch (decode_grouped*_kernel)
+                  "decode_step_fp8": ("decode.hip", "fn_device.h"), "ffn_decode_q8": ("decode_x.hip", "fn_device.h"),
                   "ffn_decode_fp8_q8": ("decode_x.hip", "fn_device.h"), "qkv_decode_adaln": ("decode_x.hip", "fn_device.h"),
                   "qkv_decode_fp8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
                   "ffn_decode_fp8_adaln": ("decode_x.hip", "adaln.hip", "fn_device.h"),
