@@ -105,17 +105,36 @@ fn_status fused_common(const void* x, const void* wg, const void* wu, void* y, i
 
 int64_t packed_fp8_bytes(int64_t K, int64_t N) { return ((N + 15) / 16) * ((K + 63) / 64) * 1024; }
 
-// Row counts just above the decode range on wide projections (at least 512
-// column blocks): the LDS-shared-x decode kernel (a 128-row rung for bf16
-// weights; 64- or 128-row blocks tiled over grid.y for fp8) instead of the
-// prefill kernel, whose 256-row tiles leave most of each tile empty and give
-// too few workgroups (96 for 12288 columns).  Measured on MI355X, K = 4096:
-// QKV 62 -> 36 us (bf16, 65-128 rows), 64-67 -> 26-57 us (fp8, 65-256
-// rows); gate/up pairs 77 -> 47-51 us (bf16, 65-128 rows) and 81-87 ->
-// 39-64 us (fp8, 65-256 rows).  Beyond 128 rows with bf16 weights and 256
-// with fp8 the prefill kernel is faster.
+// Row counts past 64 that still take the LDS-shared-x decode kernel, its row
+// blocks tiled over grid.y (each streams the weights again, mostly from L2),
+// instead of the prefill kernel.
+// Wide projections (at least 512 column blocks): a 128-row rung for bf16
+// weights, 64- or 128-row blocks for fp8; the prefill kernel's 256-row tiles
+// would leave most of each tile empty and give too few workgroups (96 for
+// 12288 columns).  Measured on MI355X, K = 4096: QKV 62 -> 36 us (bf16,
+// 65-128 rows), 64-67 -> 26-57 us (fp8, 65-256 rows); gate/up pairs 77 ->
+// 47-51 us (bf16, 65-128 rows) and 81-87 -> 39-64 us (fp8, 65-256 rows).
+// Beyond 128 rows with bf16 weights and 256 with fp8 the prefill kernel is
+// faster.
+// Narrow projections (one GPU's share under tensor parallelism): the prefill
+// kernel gives them a few dozen 256 x 128 tiles, each streaming its x and
+// weight panels at one CU's request rate, 48-106 us whatever the row count
+// up to 1-2 thousand rows; the decode kernel's 64-row blocks spread them
+// over the CUs.  Measured, K = 4096, prefill -> tiled decode: 1536 columns
+// 59-61 -> 20-22 us (bf16, 65-512 rows), 54-65 -> 20-28 us (fp8, to 1024);
+// 2 x 1376 75-78 -> 24-40 us (bf16), 80-84 -> 39-44 us (fp8); 6144 columns
+// 61-64 -> 21-39 us (bf16, to 256 rows), 64-67 -> 21-54 us (fp8, to 512);
+// the fp8-output and AdaLN forms 1.2-3.7x.  The gain ends where the row
+// blocks' repeated weight streams catch up: with bf16 weights about 256 rows
+// (512 at 192 column blocks or fewer); with fp8 256 rows above 384 column
+// blocks (8176 columns at 384 rows: 67 against 71 us), 512 up to 384 and
+// 1024 up to 192.
 bool decode_rows_tiled(int64_t M, int64_t N, bool f8) {
-  return M > 64 && M <= (f8 ? 256 : 128) && (N + 15) / 16 >= 512;
+  const int64_t nb = (N + 15) / 16;
+  if (M <= 64) return false;
+  if (nb >= 512) return M <= (f8 ? 256 : 128);
+  if (!f8) return M <= (nb <= 192 ? 512 : 256);
+  return M <= (nb <= 192 ? 1024 : (nb <= 384 ? 512 : 256));
 }
 
 // The same rows for the forms whose decode kernels have no 128-row rung --
@@ -468,8 +487,13 @@ namespace fn {
 // over rows.
 FusedPlan plan_fused(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
   if (dt == DType::BF16 && M > 64 && !decode_rows_tiled(M, N, false)) return plan_prefill(dt, M, K, N, swiglu);
-  // narrow SwiGLU pairs at 17-64 rows: the register-x kernel with a k-split
-  if (dt == DType::BF16 && swiglu && M > 16 && (N + 15) / 16 <= 256) return plan_decode(dt, M, K, N, swiglu);
+  // narrow SwiGLU pairs at 17-64 rows, and past 64 rows while the 64-row
+  // blocks give at most 256 workgroups: the register-x kernel with a 4-wave
+  // k-split (2 x 1376 columns, 65-128 rows: 24 us against 27-28 on the
+  // LDS-shared-x kernel)
+  const int64_t nb = (N + 15) / 16;
+  if (dt == DType::BF16 && swiglu && M > 16 && nb <= 256 && (M <= 64 || nb * ((M + 63) / 64) <= 256))
+    return plan_decode(dt, M, K, N, swiglu);
   if (dt == DType::BF16 && M > 16) return plan_decode_x(dt, M, K, N, swiglu);
   return plan_decode(dt, M, K, N, swiglu);
 }

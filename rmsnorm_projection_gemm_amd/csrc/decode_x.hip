@@ -652,12 +652,14 @@ static FusedPlan plan_of(const DecodeXInstance* d, int kind, int64_t M, int64_t 
   return p;
 }
 
-// bf16 row ladder rungs 32, 64 and 128 (the last only for the wide
-// projections the row ladder sends here past 64 rows).
+// bf16 row ladder rungs 32, 64 and 128 (the last for the wide projections
+// the row ladder sends here past 64 rows; narrow ones repeat the 64-row rung
+// over grid.y, which keeps three or four times the workgroups).
 FusedPlan plan_decode_x(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu) {
   (void)dt;
   (void)K;
-  return plan_of(find_instance(kDecodeX, M <= 32 ? 2 : (M <= 64 ? 4 : 8), swiglu), 2, M, N);
+  const bool wide = ceil_div(N, 16) >= 512;
+  return plan_of(find_instance(kDecodeX, M <= 32 ? 2 : (M <= 64 || !wide ? 4 : 8), swiglu), 2, M, N);
 }
 
 hipError_t launch_decode_x(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,

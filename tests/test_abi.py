@@ -58,7 +58,18 @@ def test_rows_just_past_decode_on_wide_projections(lib):
     assert lib.fn_kernel_name(129, 4096, 12288, 0, BF16).decode() == "prefill_bf16_128x128_w4x2"
     assert lib.fn_kernel_name(256, 4096, 11008, 1, BF16).decode() == "prefill_swiglu_bf16_128x128_w4x2"
     assert lib.fn_kernel_name(257, 4096, 12288, 0, BF16).decode().startswith("prefill_bf16_256x")
-    assert lib.fn_kernel_name(96, 4096, 8176, 0, BF16).decode().startswith("prefill")
+    # narrow projections (< 512 column blocks): the 64-row rung tiled over the
+    # rows up to 256 rows (512 at 192 column blocks or fewer); a narrow SwiGLU
+    # pair whose 64-row blocks give at most 256 workgroups: the register-x
+    # kernel with a k-split
+    assert lib.fn_kernel_name(96, 4096, 8176, 0, BF16).decode() == "decode_bf16_m64_xlds_w3_u2_s5"
+    assert lib.fn_kernel_name(256, 4096, 8176, 0, BF16).decode() == "decode_bf16_m64_xlds_w3_u2_s5"
+    assert lib.fn_kernel_name(257, 4096, 8176, 0, BF16).decode().startswith("prefill_bf16_256x")
+    assert lib.fn_kernel_name(512, 4096, 3072, 0, BF16).decode() == "decode_bf16_m64_xlds_w3_u2_s5"
+    assert lib.fn_kernel_name(513, 4096, 3072, 0, BF16).decode().startswith("prefill_bf16_256x128")
+    assert lib.fn_kernel_name(128, 4096, 1376, 1, BF16).decode() == "decode_swiglu_bf16_m64_n16_k4_u2"
+    assert lib.fn_kernel_name(129, 4096, 1376, 1, BF16).decode() == "decode_swiglu_bf16_m64_xlds_w3_u2"
+    assert lib.fn_kernel_name(65, 4096, 2752, 1, BF16).decode() == "decode_swiglu_bf16_m64_xlds_w3_u2"
     assert lib.fn_kernel_name(96, 4096, 8192, 0, F32).decode().startswith("decode_f32")
 
 
@@ -203,12 +214,18 @@ def test_fp8_kernel_names(lib):
     # fewer than 128 tiles of 256 x 256: 256 x 128 tiles
     assert lib.fn_kernel_name_fp8(300, 4096, 12288, 0).decode() == "prefill_fp8_256x128_w4x2_xl"
     # 65..256 rows of a wide projection (>= 512 column blocks): the 64-row
-    # decode kernel tiled over the rows; narrower ones stay on the prefill kernel
+    # decode kernel tiled over the rows; narrower ones too, to 256, 512 or
+    # 1024 rows as they narrow
     assert lib.fn_kernel_name_fp8(65, 4096, 12288, 0).decode().startswith("decode_fp8_m64")
     assert lib.fn_kernel_name_fp8(256, 4096, 8192, 1).decode().startswith("decode_swiglu_fp8_m128")
     assert lib.fn_kernel_name_fp8(200, 4096, 8192, 0).decode().startswith("decode_fp8_m64")
     assert lib.fn_kernel_name_fp8(257, 4096, 12288, 0).decode().startswith("prefill_fp8")
-    assert lib.fn_kernel_name_fp8(128, 4096, 8176, 0).decode().startswith("prefill_fp8")
+    assert lib.fn_kernel_name_fp8(256, 4096, 8176, 0).decode().startswith("decode_fp8_m64")
+    assert lib.fn_kernel_name_fp8(257, 4096, 8176, 0).decode().startswith("prefill_fp8")
+    assert lib.fn_kernel_name_fp8(512, 4096, 6144, 0).decode().startswith("decode_fp8_m64")
+    assert lib.fn_kernel_name_fp8(513, 4096, 6144, 0).decode().startswith("prefill_fp8")
+    assert lib.fn_kernel_name_fp8(1024, 4096, 1376, 1).decode().startswith("decode_swiglu_fp8_m128")
+    assert lib.fn_kernel_name_fp8(1025, 4096, 1376, 1).decode().startswith("prefill_swiglu_fp8")
     assert lib.fn_kernel_name_fp8(4096, 4096, 12288, 1).decode() == "prefill_swiglu_fp8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_fp8(0, 4096, 16, 0) == b"invalid"
 
@@ -465,10 +482,13 @@ def test_q8_kernel_names(lib):
     assert lib.fn_kernel_name_q8(128, 4096, 8192, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
     assert lib.fn_kernel_name_q8(129, 4096, 11008, 0).decode() == "prefill_swiglu_bf16_q8_128x128_w4x2"
     assert lib.fn_kernel_name_q8(257, 4096, 11008, 0).decode() == "prefill_swiglu_bf16_q8_256x128_w4x2_xl"
-    assert lib.fn_kernel_name_q8(65, 4096, 8176, 0).decode().startswith("prefill_swiglu_bf16_q8")
+    assert lib.fn_kernel_name_q8(256, 4096, 8176, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
+    assert lib.fn_kernel_name_q8(257, 4096, 8176, 0).decode().startswith("prefill_swiglu_bf16_q8")
+    assert lib.fn_kernel_name_q8(512, 4096, 2752, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
     assert lib.fn_kernel_name_q8(256, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_q8_m64")
     assert lib.fn_kernel_name_q8(257, 4096, 11008, 1).decode().startswith("prefill_swiglu_fp8_q8")
-    assert lib.fn_kernel_name_q8(65, 4096, 8176, 1).decode().startswith("prefill_swiglu_fp8_q8")
+    assert lib.fn_kernel_name_q8(257, 4096, 8176, 1).decode().startswith("prefill_swiglu_fp8_q8")
+    assert lib.fn_kernel_name_q8(1024, 4096, 1376, 1).decode().startswith("decode_swiglu_fp8_q8_m64")
     assert lib.fn_kernel_name_q8(64, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_q8_m64")
     assert lib.fn_kernel_name_q8(4096, 4096, 11008, 1).decode() == "prefill_swiglu_fp8_q8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_q8(0, 4096, 16, 0) == b"invalid"
@@ -577,7 +597,9 @@ def test_adaln_ws_sizes_and_names(lib):
     assert lib.fn_kernel_name_adaln_ws(257, 4096, 12288, 4, 0).decode() == "prefill_premod_bf16_256x256_w4x2_xl"
     assert (lib.fn_kernel_name_adaln_ws(200, 4096, 11008, 4, 1).decode() ==
             "prefill_swiglu_premod_split_bf16_256x128_w4x2_xl")
-    assert lib.fn_kernel_name_adaln_ws(65, 4096, 8176, 4, 0).decode().startswith("prefill_premod_bf16")
+    assert lib.fn_kernel_name_adaln_ws(256, 4096, 8176, 4, 0).decode() == "decode_premod_bf16_m64_xlds_w3_u2_s5"
+    assert lib.fn_kernel_name_adaln_ws(257, 4096, 8176, 4, 0).decode().startswith("prefill_premod_bf16")
+    assert lib.fn_kernel_name_adaln_ws(65, 4096, 1376, 4, 1).decode().startswith("prefill_swiglu_premod_split")
     assert lib.fn_kernel_name_adaln_ws(16, 4096, 11008, 4, 1).decode() == "decode_swiglu_adaln_split_bf16_m16_xlds_w3_u2_s5"
     assert lib.fn_kernel_name_adaln_ws(17, 4096, 12288, 500, 0).decode() == "decode_premod_bf16_m32_xlds_w3_u2_s5"
     assert lib.fn_kernel_name_adaln_ws(16, 4096, 12288, 4, 0).decode() == "decode_adaln_bf16_m16_xlds_w3_u2_s5"
@@ -643,7 +665,11 @@ def test_adaln_fp8_sizes_and_names(lib):
     assert lib.fn_kernel_name_adaln_fp8(65, 4096, 12288, 4, 0).decode() == "decode_fp8_premod_m64_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln_fp8(256, 4096, 12288, 4, 0).decode() == "decode_fp8_premod_m64_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln_fp8(257, 4096, 12288, 4, 0).decode() == "prefill_fp8_premod_256x256_w4x2_xl"
-    assert lib.fn_kernel_name_adaln_fp8(65, 4096, 8176, 4, 0).decode().startswith("prefill_fp8_premod")
+    assert lib.fn_kernel_name_adaln_fp8(256, 4096, 8176, 4, 0).decode() == "decode_fp8_premod_m64_xlds_w3_u2"
+    assert lib.fn_kernel_name_adaln_fp8(257, 4096, 8176, 4, 0).decode().startswith("prefill_fp8_premod")
+    assert (lib.fn_kernel_name_adaln_fp8(128, 4096, 1376, 4, 1).decode() ==
+            "decode_swiglu_fp8_premod_split_m64_xlds_w4_u2")
+    assert lib.fn_kernel_name_adaln_fp8(129, 4096, 1376, 4, 1).decode().startswith("prefill_swiglu_fp8_premod_split")
     assert (lib.fn_kernel_name_adaln_fp8(128, 4096, 11008, 4, 1).decode() ==
             "decode_swiglu_fp8_premod_split_m64_xlds_w4_u2")
     assert lib.fn_kernel_name_adaln_fp8(129, 4096, 11008, 4, 1).decode().startswith("prefill_swiglu_fp8_premod_split")
@@ -684,7 +710,9 @@ def test_adaln_q8_names_and_fp8(lib):
     assert lib.fn_kernel_name_adaln_q8(65, 4096, 11008, 4, 0).decode() == "decode_swiglu_bf16_q8_premod_m64_xlds_w3_u2"
     assert lib.fn_kernel_name_adaln_q8(129, 4096, 11008, 4, 0).decode() == "prefill_swiglu_bf16_q8_premod_128x128_w4x2"
     assert lib.fn_kernel_name_adaln_q8(257, 4096, 11008, 4, 0).decode() == "prefill_swiglu_bf16_q8_premod_256x128_w4x2_xl"
-    assert lib.fn_kernel_name_adaln_q8(65, 4096, 8176, 4, 0).decode().startswith("prefill_swiglu_bf16_q8_premod")
+    assert lib.fn_kernel_name_adaln_q8(256, 4096, 8176, 4, 0).decode().startswith("decode_swiglu_bf16_q8_premod_m64")
+    assert lib.fn_kernel_name_adaln_q8(257, 4096, 8176, 4, 0).decode().startswith("prefill_swiglu_bf16_q8_premod")
+    assert lib.fn_kernel_name_adaln_q8(1024, 4096, 1376, 4, 1).decode().startswith("decode_swiglu_fp8_q8_premod_m64")
     assert lib.fn_kernel_name_adaln_q8(256, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_q8_premod_m64_xlds_w4_u2"
     assert lib.fn_kernel_name_adaln_q8(257, 4096, 11008, 4, 1).decode().startswith("prefill_swiglu_fp8_q8_premod")
     assert lib.fn_kernel_name_adaln_q8(64, 4096, 11008, 4, 1).decode() == "decode_swiglu_fp8_q8_premod_m64_xlds_w4_u2"

@@ -65,7 +65,9 @@ def test_adaln_one_launch_takes_at_most_16_rows(gpu_lib):
     # 17..64 rows: the LDS-shared-x decode kernel on the pre-modulated operand
     (17, 1032, 270, 23), (33, 4104, 530, 100), (40, 1032, 270, 4), (40, 1032, 270, 30), (64, 264, 1100, 3),
     (64, 4104, 530, 40),
-    # above: the prefill kernel
+    # above: the same kernel's 64-row blocks tiled over the rows (narrow
+    # projections up to 512 rows here; not the split SwiGLU operand), else
+    # the prefill kernel
     (65, 256, 160, 2), (130, 520, 33, 3), (300, 1032, 530, 5), (257, 264, 1100, 64), (520, 4104, 270, 63),
     (200, 1032, 300, 500), (777, 264, 48, 1)])
 def test_adaln_ws_parity(gpu_lib, swiglu, M, K, N, T):

@@ -90,6 +90,19 @@ def test_fp8_rows_tiled_decode_parity(gpu_lib, M, K, N, swiglu):
     assert_close(y, ref, "bf16", f"fp8 rows tiled {M}x{K}x{N} swiglu={swiglu}")
 
 
+@pytest.mark.parametrize("M,K,N,swiglu", [(1024, 72, 1380, True), (700, 136, 3000, False), (400, 136, 6000, False),
+                                          (256, 72, 8100, False), (333, 264, 5500, True)])
+def test_fp8_narrow_rows_tiled_parity(gpu_lib, M, K, N, swiglu):
+    """Narrow projections with fp8 weights keep the decode kernel's row
+    blocks tiled over the rows further: to 1024 rows at 192 column blocks or
+    fewer, 512 to 384 blocks, 256 above (ragged rows, K and N): every
+    output against the oracle."""
+    assert gpu_lib.kernel_name_fp8(M, K, N, swiglu).startswith("decode")
+    inp = W.random_inputs(M, K, N, "bf16", seed=M * 3 + K + N, swiglu=swiglu)
+    y, ref = _run(gpu_lib, inp, swiglu)
+    assert_close(y, ref, "bf16", f"fp8 narrow rows tiled {M}x{K}x{N} swiglu={swiglu}")
+
+
 def test_fp8_qkv_decode_full(gpu_lib):
     inp = W.make_inputs(W.QKV_DECODE)
     y, ref = _run(gpu_lib, inp, False)

@@ -69,6 +69,20 @@ def test_rows_tiled_decode_parity(gpu_lib, M, K, N, swiglu):
     assert_close(fused(gpu_lib, inp), reference(inp), "bf16", f"rows tiled {M}x{K}x{N} swiglu={swiglu}")
 
 
+@pytest.mark.parametrize("M,K,N,swiglu", [(96, 264, 1540, False), (300, 136, 3000, False), (200, 72, 8000, False),
+                                          (128, 264, 1380, True), (129, 136, 1380, True), (512, 72, 2750, True)])
+def test_narrow_rows_tiled_parity(gpu_lib, M, K, N, swiglu):
+    """Past 64 rows of a narrow projection (fewer than 512 column blocks: one
+    GPU's share under tensor parallelism) the decode kernels' 64-row blocks
+    repeat over the rows -- the LDS-shared-x kernel, or for a SwiGLU pair
+    whose row blocks give at most 256 workgroups the register-x kernel with
+    a k-split (ragged rows, K and N): every output against the oracle."""
+    import torch
+    assert gpu_lib.kernel_name(M, K, N, swiglu, torch.bfloat16).startswith("decode")
+    inp = W.random_inputs(M, K, N, "bf16", seed=7 * M + K + N + swiglu, swiglu=swiglu)
+    assert_close(fused(gpu_lib, inp), reference(inp), "bf16", f"narrow rows tiled {M}x{K}x{N} swiglu={swiglu}")
+
+
 @pytest.mark.parametrize("M,K,N,swiglu", [(16, 136, 24587, False), (1, 264, 32000, False), (11, 136, 24600, True),
                                           (16, 72, 25000, True)])
 def test_two_block_decode_parity(gpu_lib, M, K, N, swiglu):
@@ -357,7 +371,7 @@ def test_python_binding_rejects_bad_arguments(gpu_lib):
     assert tdtype("bf16") == torch.bfloat16
 
 
-@pytest.mark.parametrize("M,K,N,swiglu", [(2048, 264, 768, False), (1792, 136, 1024, True), (512, 72, 1024, False),
+@pytest.mark.parametrize("M,K,N,swiglu", [(2048, 264, 768, False), (1792, 136, 1024, True), (1024, 72, 1024, False),
                                           (4096, 40, 500, True)])
 def test_prefill_tile_order(gpu_lib, M, K, N, swiglu):
     """Tile counts that divide by 8 take the XCD-grouped tile order (groups of
@@ -365,6 +379,8 @@ def test_prefill_tile_order(gpu_lib, M, K, N, swiglu):
     oracle, so a tile computed twice or not at all would show.  The oracle
     takes the folded bf16 weights the kernel reads (the fold's rounding is
     not what this checks; the unfolded comparison is the other tests')."""
+    import torch
+    assert gpu_lib.kernel_name(M, K, N, swiglu, torch.bfloat16).startswith("prefill")
     inp = W.random_inputs(M, K, N, "bf16", seed=M + K + N, swiglu=swiglu)
     y = fused(gpu_lib, inp)
     assert np.all(np.isfinite(y))

@@ -47,6 +47,10 @@ CASES = {
     "decode_ffn_m128": (128, 4096, 11008, True),
     "prefill_qkv_m256": (256, 4096, 12288, False),    # 128 x 128 prefill tiles
     "prefill_ffn_m200": (200, 4096, 11008, True),
+    # narrow projections past 64 rows: the decode kernels' row blocks tiled
+    "narrow_qkv_m300": (300, 4096, 3072, False),
+    "narrow_ffn_m128": (128, 4096, 1376, True),       # register-x, 4-wave k-split
+    "narrow_ffn_m512": (512, 4096, 2752, True),
 }
 
 
@@ -71,7 +75,7 @@ def test_fused_repeatable(gpu_lib, case):
     _repeat(call, lambda y: [y])
 
 
-@pytest.mark.parametrize("M", [16, 64, 128, 256, 4096])
+@pytest.mark.parametrize("M", [16, 64, 128, 256, 1024, 4096])
 def test_fp8_weights_repeatable(gpu_lib, M):
     import torch
     fn = gpu_lib
