@@ -52,6 +52,9 @@ def parse_args(argv=None):
                    choices=["tiny", "qkv_decode", "ffn_decode", "prefill_qkv", "decode_step"])
     p.add_argument("--step-rows", type=int, default=8,
                    help="decode_step: rows of every call (1..128; the step is quoted at 8)")
+    p.add_argument("--step-shard", type=int, default=1, choices=[1, 2, 4, 8],
+                   help="decode_step: one GPU's column share of every projection under tensor parallelism over "
+                        "that many GPUs (1: the whole step)")
     p.add_argument("--weights", default="native", choices=["native", "fp8"],
                    help="weight storage: the activations' dtype, or E4M3 codes with per-column scales "
                         "(bf16 decode workloads only)")
@@ -473,7 +476,7 @@ def run_single(args, torch, fn, workloads):
 
 
 def run_decode_step(args, torch, fn, workloads):
-    calls = workloads.decode_step_calls(rows=getattr(args, "step_rows", 8))
+    calls = workloads.decode_step_calls(rows=getattr(args, "step_rows", 8), shard=getattr(args, "step_shard", 1))
     items = []
     fp8 = args.weights == "fp8"
     fold = fn.fold_weights_fp8 if fp8 else fn.fold_weights
@@ -632,18 +635,21 @@ def measure(args, torch, fn, workloads):
         calls, r = run_decode_step(args, torch, fn, workloads)
         bytes_step = sum((fp8_bytes(c) if fp8 else c.algorithmic_bytes()) for c in calls)
         flops_step = sum(c.flops() for c in calls)
-        rows = calls[0].M
-        name = (f"32-layer decode step, M={rows}: 32 x (norm+QKV 4096->12288, norm+gate/up SwiGLU 4096->2x11008) + "
-                "norm+head 4096->32000")
-        config = {"workload": name, "calls_per_step": len(calls), "M": rows, "K": 4096,
-                  "weights_bytes": r["wbytes"], "cache": "cold (9.3 GB of distinct weights per step)"}
-        kernel = (fn.kernel_name_fp8(rows, 4096, 12288, False) if fp8 else
-                  fn.kernel_name(rows, 4096, 12288, False, torch.bfloat16))
+        rows, shard = calls[0].M, args.step_shard
+        nq, nf, nh = calls[0].N, calls[1].N, calls[-1].N
+        name = (f"32-layer decode step, M={rows}: 32 x (norm+QKV 4096->{nq}, norm+gate/up SwiGLU 4096->2x{nf}) + "
+                f"norm+head 4096->{nh}" + (f" (one GPU's column share under {shard}-way tensor parallelism)"
+                                          if shard > 1 else ""))
+        config = {"workload": name, "calls_per_step": len(calls), "M": rows, "K": 4096, "shard": shard,
+                  "weights_bytes": r["wbytes"],
+                  "cache": f"cold ({r['wbytes'] / 1e9:.2f} GB of distinct weights per step)"}
+        kernel = (fn.kernel_name_fp8(rows, 4096, nq, False) if fp8 else
+                  fn.kernel_name(rows, 4096, nq, False, torch.bfloat16))
         cpu_call, cpu_inp = calls[-1], None
         unit = "GB/s"
         work = bytes_step
         roof = {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "traffic": counter_traffic("decode_step" + suffix) if rows == 8 else None}
+                "traffic": counter_traffic("decode_step" + suffix) if rows == 8 and shard == 1 else None}
         dtype = "bf16"
         per_unit = {"algorithmic_bytes_per_step": bytes_step, "flops_per_step": flops_step}
     else:

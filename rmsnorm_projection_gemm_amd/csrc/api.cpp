@@ -180,6 +180,12 @@ fn_status fp8_common(const void* x, const void* wg, const float* sg, const void*
                                              (int)K, (int)N, eps, stream),
                       plan.name);
   }
+  if (fn::fp8_k_split(M, N, swiglu) != 0) {
+    const fn::FusedPlan plan = fn::plan_fp8_ksplit(M, N, swiglu);
+    return hip_status(fn::launch_fp8_ksplit(plan, x, wg, sg, swiglu ? wu : nullptr, swiglu ? su : nullptr, y, (int)M,
+                                            (int)K, (int)N, eps, stream),
+                      plan.name);
+  }
   const fn::FusedPlan plan = fn::plan_fp8(M, K, N, swiglu);
   return hip_status(fn::launch_fp8(plan, x, wg, sg, swiglu ? wu : nullptr, swiglu ? su : nullptr, y, (int)M, (int)K,
                                    (int)N, eps, stream),
@@ -1115,6 +1121,7 @@ const char* fn_kernel_name_fp8(int64_t M, int64_t K, int64_t N, int swiglu) {
   if (K < 1 || K > kMaxK || K % 8 != 0 || M < 1 || M > kMaxM || N < 1 || N > kMaxN) return "invalid";
   if (M > 64 && !decode_rows_tiled(M, N, true))
     return fn::plan_prefill(fn::DType::BF16, M, K, N, swiglu != 0, false, false, true).name;
+  if (fn::fp8_k_split(M, N, swiglu != 0) != 0) return fn::plan_fp8_ksplit(M, N, swiglu != 0).name;
   return fn::plan_fp8(M, K, N, swiglu != 0).name;
 }
 

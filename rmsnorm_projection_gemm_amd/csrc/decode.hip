@@ -361,14 +361,21 @@ __global__ __launch_bounds__(kWave) void decode_grouped_kernel(const GroupCall* 
 // one Gram chain over k here, where the entry point adds per-wave partials,
 // so 1/RMS can differ from it in the last fp32 bit.  The column scale joins
 // 1/RMS in the epilogue.
-template <int NF, bool SW, int P>
+// WK > 1 (single narrow calls): WK waves split the k pairs of the same
+// column blocks, each a contiguous range in k order; wave 0 adds the other
+// waves' partial products and Gram blocks in wave order after its own (fixed
+// order, the same bits on every run) and runs the epilogue.
+template <int NF, bool SW, int P, int WK = 1>
 __device__ __forceinline__ void decode_tile_fp8(const DecodeArgs& a, const float* sg, const float* su, int bx) {
   constexpr int NMAT = SW ? 2 : 1;
   const int lane = threadIdx.x & (kWave - 1);
+  const int wk = WK == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int nb0 = bx * NF;
   const int kpairs = (a.kblocks + 1) / 2;
   const int full_pairs = a.K / 64;   // pairs whose two k-blocks lie inside K
+  const int p_begin = (int)((int64_t)kpairs * wk / WK), p_end = (int)((int64_t)kpairs * (wk + 1) / WK);
+  const int p_main_end = min(p_end, full_pairs);
   const __bf16* xrow = static_cast<const __bf16*>(a.x) + (size_t)min(lrow, a.M - 1) * a.K + lgrp * 8;
   const u32x4* wp[NMAT][NF];
   float sc[NMAT][NF];
@@ -429,11 +436,11 @@ __device__ __forceinline__ void decode_tile_fp8(const DecodeArgs& a, const float
   };
 
   // whole pairs, double-buffered as in decode_tile
-  int p = 0;
-  if (2 * P <= full_pairs) {
+  int p = p_begin;
+  if (p + 2 * P <= p_main_end) {
     Stage s0, s1;
-    load(s0, 0);
-    for (; p + 4 * P <= full_pairs; p += 2 * P) {
+    load(s0, p);
+    for (; p + 4 * P <= p_main_end; p += 2 * P) {
       load(s1, p + P);
       __builtin_amdgcn_sched_barrier(0);
       compute(s0);
@@ -451,7 +458,7 @@ __device__ __forceinline__ void decode_tile_fp8(const DecodeArgs& a, const float
   }
   // the remaining pairs one at a time; x past K (a ragged last k-block, the
   // missing half of an odd last pair) reads as zero, and its codes are zero
-  for (; p < kpairs; ++p) {
+  for (; p < p_end; ++p) {
     const bool in0 = (2 * p) * 32 + lgrp * 8 < a.K, in1 = (2 * p + 1) * 32 + lgrp * 8 < a.K;
     const u32x4 x0 = in0 ? *reinterpret_cast<const u32x4*>(xrow + (size_t)(2 * p) * 32) : u32x4{0u, 0u, 0u, 0u};
     const u32x4 x1 = in1 ? *reinterpret_cast<const u32x4*>(xrow + (size_t)(2 * p + 1) * 32) : u32x4{0u, 0u, 0u, 0u};
@@ -463,10 +470,32 @@ __device__ __forceinline__ void decode_tile_fp8(const DecodeArgs& a, const float
     pair(x0, x1, w);
   }
 
+  if constexpr (WK > 1) {
+    __shared__ f32x4 red[WK - 1][NMAT * NF + 1][kWave];
+    if (wk > 0) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) red[wk - 1][m * NF + nf][lane] = acc[m][nf];
+      red[wk - 1][NMAT * NF][lane] = gram;
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int w = 0; w < WK - 1; ++w) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) acc[m][nf] += red[w][m * NF + nf][lane];
+        gram += red[w][NMAT * NF][lane];
+      }
+    }
+  }
+
   // 1/RMS per row from the Gram diagonal (accumulator element r of lane l is
   // row 4*(l/16) + r, column l%16), shared through LDS
   __shared__ float inv_s[16];
-  if ((lrow >> 2) == lgrp) {
+  if (wk == 0 && (lrow >> 2) == lgrp) {
     const int r = lrow & 3;
     inv_s[lrow] = inv_rms(r == 0 ? gram[0] : (r == 1 ? gram[1] : (r == 2 ? gram[2] : gram[3])), (float)a.K, a.eps);
   }
@@ -477,7 +506,7 @@ __device__ __forceinline__ void decode_tile_fp8(const DecodeArgs& a, const float
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * lgrp + r;
-      if (row < a.M && col < a.N) {
+      if (wk == 0 && row < a.M && col < a.N) {
         const float inv = inv_s[row];
         const float ga = acc[0][nf][r] * (sc[0][nf] * inv);
         const float v = SW ? silu_times(ga, acc[NMAT - 1][nf][r] * (sc[NMAT - 1][nf] * inv)) : ga;
@@ -517,6 +546,77 @@ hipError_t launch_decode_grouped(const void* calls, const void* item_call, int i
 }
 
 size_t grouped_call_bytes() { return sizeof(GroupCall); }
+
+// Single fp8-weight calls of at most 16 rows on narrow projections (at most
+// 256 column blocks): the LDS-shared-x kernel gives them a workgroup per
+// three column blocks (32 for a 1536-column share) and each wave's chain
+// over k waits on memory at every stage; here one workgroup per column
+// block splits k over four waves.  Measured on MI355X, K = 4096, 1-16 rows:
+// 1536 columns 8.1-9.0 -> 6.2-7.3 us, 2 x 1376 11.8-12.8 -> 6.6-8.5 us,
+// 4000 columns 8.6-9.2 -> 5.9-7.9 us.  Two waves on wider projections
+// (6144-12288 columns) measured 0.7-1.2x, so those keep the LDS-shared-x
+// kernel.
+template <int SW, int P, int WK>
+__global__ __launch_bounds__(kWave * WK) void decode_fp8_ksplit_kernel(DecodeArgs a, const float* sg,
+                                                                      const float* su) {
+  decode_tile_fp8<1, SW != 0, P, WK>(a, sg, su, blockIdx.x);
+}
+
+struct DecodeFp8KInstance {
+  const void* fn;
+  int p, wk;
+  bool sw;
+  const char* name;
+};
+#define FN_DECODE_F8K(SW, P, WK, NAME) \
+  DecodeFp8KInstance { reinterpret_cast<const void*>(&decode_fp8_ksplit_kernel<SW, P, WK>), P, WK, SW != 0, NAME }
+static const DecodeFp8KInstance kDecodeFp8K[] = {
+    FN_DECODE_F8K(0, 4, 4, "decode_fp8_m16_n16_k4_p4"),
+    FN_DECODE_F8K(1, 2, 4, "decode_swiglu_fp8_m16_n16_k4_p2"),
+};
+
+int fp8_k_split(int64_t M, int64_t N, bool swiglu) {
+  (void)swiglu;
+  return M <= 16 && ceil_div(N, 16) <= 256 ? 4 : 0;
+}
+
+static const DecodeFp8KInstance* find_fp8k(bool sw, int wk) {
+  for (const DecodeFp8KInstance& d : kDecodeFp8K)
+    if (d.sw == sw && d.wk == wk) return &d;
+  return nullptr;
+}
+
+FusedPlan plan_fp8_ksplit(int64_t M, int64_t N, bool swiglu) {
+  const DecodeFp8KInstance* d = find_fp8k(swiglu, fp8_k_split(M, N, swiglu));
+  FusedPlan p{};
+  p.kind = 12;
+  p.mf = 1;
+  p.nf = 1;
+  p.waves = d != nullptr ? d->wk : 0;
+  p.grid = dim3((unsigned)ceil_div(N, 16), 1, 1);
+  p.block = dim3(kWave * p.waves, 1, 1);
+  p.name = d != nullptr ? d->name : "invalid";
+  return p;
+}
+
+hipError_t launch_fp8_ksplit(const FusedPlan& p, const void* x, const void* wg, const float* sg, const void* wu,
+                             const float* su, void* y, int M, int K, int N, float eps, hipStream_t stream) {
+  const DecodeFp8KInstance* d = find_fp8k(wu != nullptr, p.waves);
+  if (d == nullptr || M > 16 || sg == nullptr || (wu != nullptr && su == nullptr)) return hipErrorInvalidValue;
+  DecodeArgs a;
+  a.x = x;
+  a.wg = static_cast<const u32x4*>(wg);
+  a.wu = static_cast<const u32x4*>(wu);
+  a.y = y;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.kblocks = (int)ceil_div(K, k_per_block(DType::BF16));
+  a.nblocks = (int)ceil_div(N, 16);
+  a.eps = eps;
+  void* args[] = {&a, &sg, &su};
+  return hipLaunchKernel(d->fn, p.grid, p.block, args, 0, stream);
+}
 
 void grouped_call_fill(void* dst, const void* x, const void* wg, const void* wu, const float* sg, const float* su,
                        void* y, int M, int K, int N, float eps, int first) {

@@ -133,6 +133,14 @@ FusedPlan plan_fp8(int64_t M, int64_t K, int64_t N, bool swiglu);
 hipError_t launch_fp8(const FusedPlan& plan, const void* x, const void* wg, const float* sg,
                       const void* wu, const float* su, void* y, int M, int K, int N, float eps,
                       hipStream_t stream);
+// Narrow projections at up to 16 rows with fp8 weights: the register-x tile
+// with its k range split over waves (decode.hip); 0 when the call is not
+// such a case, else the waves per column block.
+int fp8_k_split(int64_t M, int64_t N, bool swiglu);
+FusedPlan plan_fp8_ksplit(int64_t M, int64_t N, bool swiglu);
+hipError_t launch_fp8_ksplit(const FusedPlan& plan, const void* x, const void* wg, const float* sg,
+                             const void* wu, const float* su, void* y, int M, int K, int N, float eps,
+                             hipStream_t stream);
 
 // SwiGLU with fp8 output (E4M3 codes, one scale per 16-column row block):
 // the LDS-shared-x decode kernel (bf16 weights up to 64 rows, fp8 weights

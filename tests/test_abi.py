@@ -207,6 +207,11 @@ def test_packed_fp8_bytes_invalid(lib, K, N):
 
 def test_fp8_kernel_names(lib):
     assert lib.fn_kernel_name_fp8(16, 4096, 12288, 0).decode().startswith("decode_fp8_m16")
+    # up to 16 rows of at most 256 column blocks: the register-x tile, k over four waves
+    assert lib.fn_kernel_name_fp8(16, 4096, 4096, 0).decode() == "decode_fp8_m16_n16_k4_p4"
+    assert lib.fn_kernel_name_fp8(1, 4096, 1376, 1).decode() == "decode_swiglu_fp8_m16_n16_k4_p2"
+    assert lib.fn_kernel_name_fp8(16, 4096, 4112, 0).decode().startswith("decode_fp8_m16_xlds")
+    assert lib.fn_kernel_name_fp8(17, 4096, 1536, 0).decode().startswith("decode_fp8_m32_xlds")
     assert lib.fn_kernel_name_fp8(17, 4096, 12288, 0).decode().startswith("decode_fp8_m32")
     assert lib.fn_kernel_name_fp8(64, 4096, 11008, 1).decode().startswith("decode_swiglu_fp8_m64")
     # above 64 rows the prefill kernel with fp8 weights

@@ -23,6 +23,24 @@ def test_algorithmic_bytes_and_flops_of_the_five_configs():
         assert bench.call_bytes(wl[name], fp8=False, q8=False) == wl[name].algorithmic_bytes()
 
 
+def test_decode_step_shards():
+    """One GPU's column share of the step under tensor parallelism: every
+    projection's N divided by the GPU count, x whole, the bytes summing to
+    the share of the weights plus each call's x and y."""
+    full, share = W.decode_step_calls(), W.decode_step_calls(shard=8)
+    assert len(share) == 65
+    assert [c.N for c in share[:2]] + [share[-1].N] == [1536, 1376, 4000]
+    assert all(c.K == 4096 and c.M == 8 for c in share)
+    w_full = sum(c.mats * c.K * c.N * 2 for c in full)
+    w_share = sum(c.mats * c.K * c.N * 2 for c in share)
+    assert w_share * 8 == w_full
+    assert sum(c.algorithmic_bytes() for c in share) == w_share + sum(2 * (c.M * c.K + c.M * c.N) for c in share)
+    import pytest
+    with pytest.raises(ValueError):
+        W.decode_step_calls(shard=3)
+    assert bench.parse_args(["--workload", "decode_step", "--step-shard", "8"]).step_shard == 8
+
+
 def test_fp8_and_fp8_output_bytes():
     c = W.WORKLOADS["qkv_decode"]            # 16 x 4096 -> 12288
     # codes (1 B each) and one fp32 scale per column, bf16 x and y

@@ -90,6 +90,18 @@ def test_fp8_rows_tiled_decode_parity(gpu_lib, M, K, N, swiglu):
     assert_close(y, ref, "bf16", f"fp8 rows tiled {M}x{K}x{N} swiglu={swiglu}")
 
 
+@pytest.mark.parametrize("M,K,N,swiglu", [(1, 8, 16, False), (16, 72, 1540, False), (9, 264, 4096, True),
+                                          (16, 4104, 1380, True), (5, 1032, 100, False), (12, 4096, 4000, False)])
+def test_fp8_narrow_ksplit_parity(gpu_lib, M, K, N, swiglu):
+    """Up to 16 rows of at most 256 column blocks with fp8 weights: the
+    register-x tile with k split over four waves (uneven and empty k ranges,
+    ragged K and N): every output against the oracle."""
+    assert "_k4_" in gpu_lib.kernel_name_fp8(M, K, N, swiglu)
+    inp = W.random_inputs(M, K, N, "bf16", seed=M * 11 + K + N, swiglu=swiglu)
+    y, ref = _run(gpu_lib, inp, swiglu)
+    assert_close(y, ref, "bf16", f"fp8 k-split {M}x{K}x{N} swiglu={swiglu}")
+
+
 @pytest.mark.parametrize("M,K,N,swiglu", [(1024, 72, 1380, True), (700, 136, 3000, False), (400, 136, 6000, False),
                                           (256, 72, 8100, False), (333, 264, 5500, True)])
 def test_fp8_narrow_rows_tiled_parity(gpu_lib, M, K, N, swiglu):

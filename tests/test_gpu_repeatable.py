@@ -87,6 +87,21 @@ def test_fp8_weights_repeatable(gpu_lib, M):
     _repeat(lambda: fn.norm_proj_swiglu_fp8(x, Pg, Pu, 1e-6), lambda y: [y])
 
 
+@pytest.mark.parametrize("N,swiglu", [(1536, False), (1376, True)])
+def test_fp8_narrow_ksplit_repeatable(gpu_lib, N, swiglu):
+    """fp8 weights, 16 rows of a tensor-parallel share: the four k-split
+    waves meet in LDS."""
+    import torch
+    fn = gpu_lib
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(21)
+    K = 4096
+    x = _rand((16, K), gen)
+    _, _, _, Pg, Pu = _weights(fn, K, N, swiglu, gen, fp8=True)
+    call = (lambda: fn.norm_proj_swiglu_fp8(x, Pg, Pu, 1e-6)) if swiglu else (lambda: fn.norm_proj_fp8(x, Pg, 1e-6))
+    _repeat(call, lambda y: [y])
+
+
 @pytest.mark.parametrize("M", [64, 4096])
 def test_q8_output_repeatable(gpu_lib, M):
     import torch

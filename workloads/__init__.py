@@ -88,16 +88,20 @@ DECODE_STEP_LAYERS = 32
 DECODE_STEP_M = 8
 
 
-def decode_step_calls(layers: int = DECODE_STEP_LAYERS, rows: int = DECODE_STEP_M) -> List[Call]:
+def decode_step_calls(layers: int = DECODE_STEP_LAYERS, rows: int = DECODE_STEP_M, shard: int = 1) -> List[Call]:
     """The 32-layer decode step at M=8 (``rows`` other batch sizes): per
     layer an attention norm + QKV projection and an FFN norm + gate/up
     SwiGLU; then the final norm + LM head.  Every call gets its own seeded x
-    (calls are independent, not chained)."""
+    (calls are independent, not chained).  ``shard`` > 1: one GPU's column
+    share of every projection under tensor parallelism over that many GPUs
+    (N / shard columns, the full x)."""
+    if shard < 1 or any(n % (16 * shard) for n in (12288, 11008, 32000)):
+        raise ValueError(f"shard={shard} must split every projection into 16-column blocks")
     calls: List[Call] = []
     for l in range(layers):
-        calls.append(Call(f"layer{l}.attn_qkv", rows, 4096, 12288, False, "bf16", 5000 + 2 * l))
-        calls.append(Call(f"layer{l}.ffn_gate_up", rows, 4096, 11008, True, "bf16", 5001 + 2 * l))
-    calls.append(Call("head", rows, 4096, 32000, False, "bf16", 5064))
+        calls.append(Call(f"layer{l}.attn_qkv", rows, 4096, 12288 // shard, False, "bf16", 5000 + 2 * l))
+        calls.append(Call(f"layer{l}.ffn_gate_up", rows, 4096, 11008 // shard, True, "bf16", 5001 + 2 * l))
+    calls.append(Call("head", rows, 4096, 32000 // shard, False, "bf16", 5064))
     return calls
 
 
