@@ -5,9 +5,11 @@
 // 16*FN*WN columns per weight matrix) with WM x WN waves, each owning a
 // 16*FM x 16*FN sub-tile whose fp32 accumulators stay in registers for the
 // whole k loop.  The instances use 256x256 tiles (256x128 per matrix for
-// SwiGLU) with eight waves of 64x128, two waves per SIMD: measured on MI355X
-// four waves of 128x128 (one per SIMD) ran 1.8x slower, nothing covering one
-// wave's barrier and memory latency.
+// SwiGLU) with eight waves, two per SIMD: of 64x128 where W' streams through
+// an LDS ring, of 128x64 where each wave loads its W' fragments straight
+// into registers (the large grids of plain and SwiGLU projections).
+// Measured on MI355X four waves of 128x128 (one per SIMD) ran 1.8x slower,
+// nothing covering one wave's barrier and memory latency.
 //
 // Schedule: ping-pong.  Waves 0-3 (one per SIMD) and waves
 // 4-7 alternate between a compute slot -- the k-block's MFMAs, operands
@@ -104,7 +106,8 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 // (v_cvt_scalef32_pk_bf16_fp8 with scale 1 is exact).  Per k-block a CU
 // moves 24 KiB of operands instead of 32 and its waves read 64 KiB of LDS
 // instead of 96; the column scale joins 1/RMS in the epilogue.
-template <int FM, int FN, int WM, int WN, bool SW, bool Q8, bool EX = false, bool F8 = false, bool PAIR = false>
+template <int FM, int FN, int WM, int WN, bool SW, bool Q8, bool EX = false, bool F8 = false, bool PAIR = false,
+          bool WD = false>
 __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = SW ? 2 : 1;
@@ -116,11 +119,12 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   constexpr int XPW = XFR / NW;                  // x loads per wave per pair
   constexpr int SSF = FM / WN;                   // row fragments whose squares this wave sums
   static_assert(WFR % NW == 0 && XFR % NW == 0 && FM % WN == 0, "tile shape");
-  constexpr int WSLOT = WFR * kFragBytes;
+  constexpr int WSLOT = WD ? 16 : WFR * kFragBytes;   // WD: no W' ring
   constexpr int XSLOT = XFR * kFragBytes;
   static_assert(4 * WSLOT + 2 * XSLOT + BMF * 64 <= 160 * 1024, "LDS budget");
   static_assert(NW == 8, "ping-pong: two groups of one wave per SIMD");
   static_assert(!PAIR || (EX && !Q8), "split operand: the two-launch AdaLN form, bf16 output");
+  static_assert(!WD || !F8, "W' fragments straight to registers: bf16 weights");
   constexpr bool BIAS = EX;
 
   __shared__ __attribute__((aligned(1024))) uint8_t wring0[WSLOT];
@@ -139,6 +143,13 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = wave / WN, wn = wave % WN;
   const int lrow = lane & 15, lgrp = lane >> 4;
+  // Row fragment of the tile held in the wave's i-th A operand.  WD: rotated
+  // by the wave's column group so that the fragments whose squares it sums
+  // (the SSF fragments from wn * SSF) sit first, at compile-time positions.
+  static_assert(!WD || (FM & (FM - 1)) == 0, "rotated fragment order");
+  auto rfrag = [&](int i) __attribute__((always_inline)) -> int {
+    return WD ? wm * FM + ((i + wn * SSF) & (FM - 1)) : wm * FM + i;
+  };
   // Tile order for the 8 XCDs: workgroup L = y * gridDim.x + x is placed on
   // XCD L % 8, and each XCD's L2 serves only its own workgroups.  When the
   // tile count divides by 8, XCD j takes the j-th eighth of a grouped order
@@ -247,7 +258,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
   u32x4 av[FM], bv[NB];                    // one k-block's operands
   auto read_a = [&](const uint8_t* base, int u) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) av[i] = *reinterpret_cast<const u32x4*>(base + x_at(u, wm * FM + i));
+    for (int i = 0; i < FM; ++i) av[i] = *reinterpret_cast<const u32x4*>(base + x_at(u, rfrag(i)));
   };
   auto read_b = [&](int j0, int j1, const uint8_t* base) __attribute__((always_inline)) {
 #pragma unroll
@@ -366,6 +377,113 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
       read_b8(wring0, 0);
       lgkm0();
       decode_b8();
+      for (int s = 0; s < a.kblocks; s += 4) {
+        stepA(std::integral_constant<int, 0>{}, s);
+        stepA(std::integral_constant<int, 1>{}, s + 1);
+        stepA(std::integral_constant<int, 2>{}, s + 2);
+        stepA(std::integral_constant<int, 3>{}, s + 3);
+      }
+    }
+  } else if constexpr (WD) {
+    // W' straight to registers.  A packed fragment (16 columns x 32 k) is
+    // 1 KiB of contiguous memory, the lane's 16 bytes its B operand, so each
+    // wave loads its own fragments with whole-line buffer loads instead of
+    // sharing them through an LDS ring; only x goes through LDS.  With waves
+    // of 128 x 64 (WM = 2, WN = 4) a k-block of a 256 x 256 tile then moves
+    // 16 KiB of DMA writes and 64 KiB of operand reads through the LDS
+    // instead of 32 + 96 KiB, while each W' fragment is fetched twice, by
+    // the waves of the two groups one slot apart.  (The same loads without
+    // the ping-pong -- every wave alike, one barrier per pair of k-blocks,
+    // a four-pair x ring -- gave the same bits 10-17% slower on every shape
+    // measured: the two groups' alternation is worth more than its barriers.)
+    //
+    // The slots are the ping-pong's above; x keeps its ring and issue
+    // order.  A wave's B operands of k-block s are loaded 3 slots before its
+    // compute slot: group A issues B(s+2) in the memory slot after
+    // computing s, group B issues B(s+1) in the memory slot before computing
+    // s.  The compiler's own counter waits cover the register loads; the
+    // explicit ones below cover x: when k-block q = s+1 opens a pair, the
+    // pair's loads have been followed by exactly two k-blocks of this
+    // wave's B loads in both groups' issue orders.
+    u32x4 bq[NB];   // the next k-block's B operands in flight
+    auto issue_wd = [&](int kb) __attribute__((always_inline)) {
+      const uint32_t win = (uint32_t)((kb - a.kblocks) >> 31);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int m = j / FN, ni = wn * FN + j % FN;
+        const uint32_t off = ((uint32_t)((ni * a.kblocks + kb) * kFragBytes + lane * 16) & win) | (kOutOfRange & ~win);
+        bq[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(m == 0 ? wr0 : wr1, off, 0, 0));
+      }
+    };
+    // with the rotated fragment order (rfrag) this wave's share of the
+    // squares is its first SSF fragments
+    auto squares_wd = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < SSF; ++t) gram[t] = mfma_chunk<__bf16>(av[t], av[t], gram[t]);
+    };
+    auto compute = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_cols(0, NB);
+      if constexpr (!EX) squares_wd();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto ready = [&](auto T4c) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T4c)::value;
+      if constexpr (T4 % 2 == 1) wait_vmcnt<2 * NB>();
+    };
+    auto stepA = [&](auto T4c, int s) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T4c)::value;
+      compute();
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bv[j] = bq[j];
+      ready(T4c);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(xslot(((T4 + 1) % 4) / 2), (T4 + 1) % 2);
+      if constexpr (T4 % 2 == 1) issue_x(xslot(((T4 + 3) / 2) % 2), (s + 3) / 2);
+      issue_wd(s + 2);
+      lgkm0();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+    };
+    auto stepB = [&](auto T4c, int s) __attribute__((always_inline)) {
+      constexpr int T4 = decltype(T4c)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      read_a(xslot(T4 / 2), T4 % 2);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bv[j] = bq[j];
+      if constexpr (T4 % 2 == 0) issue_x(xslot(((T4 + 2) / 2) % 2), (s + 2) / 2);
+      issue_wd(s + 1);
+      lgkm0();
+      ready(T4c);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      compute();
+      __builtin_amdgcn_s_barrier();
+    };
+    if (wave & 4) {
+      issue_x(xring0, 0);
+      issue_wd(0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<NB>();
+      __builtin_amdgcn_s_barrier();
+      for (int s = 0; s < a.kblocks; s += 4) {
+        stepB(std::integral_constant<int, 0>{}, s);
+        stepB(std::integral_constant<int, 1>{}, s + 1);
+        stepB(std::integral_constant<int, 2>{}, s + 2);
+        stepB(std::integral_constant<int, 3>{}, s + 3);
+      }
+    } else {
+      issue_x(xring0, 0);
+      issue_x(xring1, 1);
+      issue_wd(0);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bv[j] = bq[j];
+      issue_wd(1);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<XPW + 2 * NB>();
+      __builtin_amdgcn_s_barrier();
+      read_a(xring0, 0);
       for (int s = 0; s < a.kblocks; s += 4) {
         stepA(std::integral_constant<int, 0>{}, s);
         stepA(std::integral_constant<int, 1>{}, s + 1);
@@ -494,7 +612,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&ssbuf[(wm * FM + i) * 16 + 4 * lgrp]);
+    const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&ssbuf[rfrag(i) * 16 + 4 * lgrp]);
     // EX: the AdaLN bias values of this row fragment's outputs, all fetched
     // before its first store (the loads then overlap instead of each waiting
     // behind the previous store); where the index is outside the table or
@@ -503,7 +621,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     float bias[NMAT][4][FN];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = m0 + (wm * FM + i) * 16 + 4 * lgrp + r;
+      const int row = m0 + rfrag(i) * 16 + 4 * lgrp + r;
       const int trow = BIAS && row < a.M ? a.idx[PAIR ? row >> 1 : row] : -1;
       const bool tv = BIAS && (unsigned)trow < (unsigned)a.T;
       const size_t tb = (size_t)(tv ? trow : 0) * a.N;
@@ -520,7 +638,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void prefill_kernel(PrefillArgs a)
     }
 #pragma unroll
     for (int r = 0; r < 4; r += (PAIR ? 2 : 1)) {
-      const int rl = (wm * FM + i) * 16 + 4 * lgrp + r;   // row within the tile
+      const int rl = rfrag(i) * 16 + 4 * lgrp + r;   // row within the tile
       const int row = m0 + rl;
       const float inv = inv4[r];
       // PAIR: operand rows r and r+1 are one output row's two parts
@@ -563,6 +681,7 @@ struct PrefillInstance {
   int fm, fn_, wm, wn, ns;
   bool sw, q8, ex, f8, pair;
   const char* name;
+  bool wd;   // W' fragments straight to registers
 };
 
 #define FN_PREFILL(FM, FN_, WM, WN, SW, Q8, EX, F8, NAME)                                                   \
@@ -577,7 +696,25 @@ struct PrefillInstance {
         false, true, F8, true, NAME                                                                          \
   }
 
+// W' fragments straight to registers, waves of 128 x 64 (bf16 weights, no
+// AdaLN): listed first, so the plain and SwiGLU calls on 256-row tiles take
+// them when the grid has at least 128 tiles and K is at least 2048.
+// Measured against the LDS-ring instances below on the same inputs (the
+// same bits): 4096 x 4096 -> 12288 296 against 301 us, 8192 x 4096 -> 4096
+// 197-200 against 201-209 us, the gate/up pair 4096 x 4096 -> 2 x 11008
+// 546-560 against 547-566 us; slower on short k loops and small grids,
+// where each wave's own W' loads are latency it cannot hide: 2000 x 1064 ->
+// 4100 (136 tiles) 34.4 against 33.2 us, 1000 x 4000 -> 1000 (16 tiles) 81
+// against 76 us.
+#define FN_PREFILL_WD(FN_, SW, NAME)                                                                        \
+  PrefillInstance {                                                                                          \
+    reinterpret_cast<const void*>(&prefill_kernel<8, FN_, 2, 4, SW, false, false, false, false, true>), 8, FN_, 2, \
+        4, 4, SW, false, false, false, false, NAME, true                                                     \
+  }
+
 static const PrefillInstance kPrefill[] = {
+    FN_PREFILL_WD(4, false, "prefill_bf16_256x256_w2x4_wd"),
+    FN_PREFILL_WD(2, true, "prefill_swiglu_bf16_256x128_w2x4_wd"),
     FN_PREFILL(4, 8, 4, 2, false, false, false, false, "prefill_bf16_256x256_w4x2_xl"),
     // narrow projections (one GPU's column share under tensor parallelism):
     // fewer than 128 tiles of 256 x 256 leave most CUs idle; 256 x 128 tiles
@@ -613,24 +750,34 @@ static const PrefillInstance kPrefill[] = {
 // 16-row fragments per tile and, when nf is given, nf 16-column fragments;
 // the plain projection when none matches.
 static const PrefillInstance& pick(bool sw, bool q8 = false, bool ex = false, bool f8 = false, int nf = 0,
-                                   int mf = 16) {
+                                   int mf = 16, bool wd_ok = false) {
   for (const PrefillInstance& d : kPrefill)
     if (d.sw == (sw || q8) && d.q8 == q8 && d.ex == ex && d.f8 == f8 && d.fm * d.wm == mf &&
-        (nf == 0 || d.fn_ * d.wn == nf))
+        (nf == 0 || d.fn_ * d.wn == nf) && (wd_ok || !d.wd))
       return d;
-  return kPrefill[0];
+  return kPrefill[2];
+}
+
+// The instance a plan names (plans carry the table's own name pointers).
+static const PrefillInstance* by_name(const char* name) {
+  for (const PrefillInstance& d : kPrefill)
+    if (d.name == name) return &d;
+  return nullptr;
 }
 
 FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, bool q8, bool ex, bool f8) {
   (void)dt;
-  (void)K;
   const bool plain = !swiglu && !q8 && !ex;
   const bool narrow = plain && ceil_div(N, 256) * ceil_div(M, 256) < 128;
   // 128-row tiles: bf16 weights, not the split AdaLN operand (its tiles
   // already hold 128 output rows)
   const bool split = ex && swiglu && !q8;
   const bool rows128 = !f8 && !split && M <= 256 && ceil_div(N, 16) >= 512;
-  const PrefillInstance& d = rows128 ? pick(swiglu, q8, ex, false, 8, 8) : pick(swiglu, q8, ex, f8, narrow ? 8 : 0);
+  // W' straight to registers pays on long k loops over grids of at least
+  // 128 tiles
+  const int64_t tiles = ceil_div(M, 256) * ceil_div(N, swiglu ? 128 : 256);
+  const PrefillInstance& d = rows128 ? pick(swiglu, q8, ex, false, 8, 8)
+                                     : pick(swiglu, q8, ex, f8, narrow ? 8 : 0, 16, tiles >= 128 && K >= 2048);
   FusedPlan p{};
   p.kind = f8 ? 11 : (ex ? (q8 ? 10 : 8) : (q8 ? 5 : 1));
   p.mf = d.fm * d.wm;
@@ -646,7 +793,10 @@ FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, b
 hipError_t launch_prefill(DType dt, const FusedPlan& p, const void* x, const void* wg, const void* wu, void* y,
                           int M, int K, int N, float eps, hipStream_t stream, uint8_t* q, float* qs) {
   if (dt != DType::BF16 || (q != nullptr && wu == nullptr)) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, false, false, p.nf, p.mf);
+  const PrefillInstance* dp = by_name(p.name);
+  if (dp == nullptr || dp->ex || dp->f8 || dp->sw != (wu != nullptr) || dp->q8 != (q != nullptr))
+    return hipErrorInvalidValue;
+  const PrefillInstance& d = *dp;
   PrefillArgs a{};
   a.q = q;
   a.qs = qs;

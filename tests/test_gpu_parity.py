@@ -390,3 +390,25 @@ def test_prefill_tile_order(gpu_lib, M, K, N, swiglu):
     else:
         ref = oracle.norm_proj_folded(inp.x, Wg, inp.call.eps)
     assert_close(y, ref, "bf16", f"prefill tile order {M}x{K}x{N} swiglu={swiglu}")
+
+
+@pytest.mark.parametrize("M,K,N,swiglu", [(2000, 2056, 4100, False), (2000, 2056, 2100, True),
+                                          (1300, 2088, 5800, False), (1300, 2088, 3000, True)])
+def test_prefill_w_direct_ragged(gpu_lib, M, K, N, swiglu):
+    """Grids of at least 128 tiles with K >= 2048 take the instances that load
+    W' fragments straight into registers (rotated row-fragment order per
+    wave): ragged
+    rows, columns and k (a partial k-block, a k-block count that is not a
+    multiple of the unroll), tile counts with and without the XCD-grouped
+    order; every output against the oracle on the folded weights."""
+    import torch
+    assert gpu_lib.kernel_name(M, K, N, swiglu, torch.bfloat16).endswith("_wd")
+    inp = W.random_inputs(M, K, N, "bf16", seed=7 * M + K + N, swiglu=swiglu)
+    y = fused(gpu_lib, inp)
+    assert np.all(np.isfinite(y))
+    Wg = oracle.fold_weights(inp.g, inp.W, "bf16")
+    if swiglu:
+        ref = oracle.norm_proj_swiglu_folded(inp.x, Wg, oracle.fold_weights(inp.g, inp.W_up, "bf16"), inp.call.eps)
+    else:
+        ref = oracle.norm_proj_folded(inp.x, Wg, inp.call.eps)
+    assert_close(y, ref, "bf16", f"prefill W' direct {M}x{K}x{N} swiglu={swiglu}")
