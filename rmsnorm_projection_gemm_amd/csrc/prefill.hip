@@ -697,24 +697,28 @@ struct PrefillInstance {
   }
 
 // W' fragments straight to registers, waves of 128 x 64 (bf16 weights, no
-// AdaLN): listed first, so the plain and SwiGLU calls on 256-row tiles take
-// them when the grid has at least 128 tiles and K is at least 2048.
-// Measured against the LDS-ring instances below on the same inputs (the
-// same bits): 4096 x 4096 -> 12288 296 against 301 us, 8192 x 4096 -> 4096
-// 197-200 against 201-209 us, the gate/up pair 4096 x 4096 -> 2 x 11008
-// 546-560 against 547-566 us; slower on short k loops and small grids,
-// where each wave's own W' loads are latency it cannot hide: 2000 x 1064 ->
-// 4100 (136 tiles) 34.4 against 33.2 us, 1000 x 4000 -> 1000 (16 tiles) 81
-// against 76 us.
-#define FN_PREFILL_WD(FN_, SW, NAME)                                                                        \
+// AdaLN): listed first, so the plain, SwiGLU and fp8-output SwiGLU calls on
+// 256-row tiles take them when the grid has at least 128 tiles and K is at
+// least 4096.  Measured against the LDS-ring instances below on the same
+// inputs (the same bits): 4096 x 4096 -> 12288 296-303 against 301-308 us,
+// 8192 x 4096 -> 4096 197-200 against 201-209 us, the gate/up pair 4096 x
+// 4096 -> 2 x 11008 546-564 against 547-569 us (fp8 output 647 against
+// 653 us); slower on shorter k loops and small grids, where each wave's own
+// W' loads are latency it cannot hide: 2000 x 1064 -> 4100 (136 tiles)
+// 34.4 against 33.2 us, 2000 x 2056 -> 2 x 2100 with fp8 output 67.3
+// against 65.4 us, 1000 x 4000 -> 1000 (16 tiles) 81 against 76 us.  On
+// the AdaLN operand (no Gram blocks) it lost at every size (QKV 309 against
+// 295 us), so those instances keep the ring.
+#define FN_PREFILL_WD(FN_, SW, Q8, EX, NAME)                                                                \
   PrefillInstance {                                                                                          \
-    reinterpret_cast<const void*>(&prefill_kernel<8, FN_, 2, 4, SW, false, false, false, false, true>), 8, FN_, 2, \
-        4, 4, SW, false, false, false, false, NAME, true                                                     \
+    reinterpret_cast<const void*>(&prefill_kernel<8, FN_, 2, 4, SW, Q8, EX, false, false, true>), 8, FN_, 2, 4, 4, \
+        SW, Q8, EX, false, false, NAME, true                                                                 \
   }
 
 static const PrefillInstance kPrefill[] = {
-    FN_PREFILL_WD(4, false, "prefill_bf16_256x256_w2x4_wd"),
-    FN_PREFILL_WD(2, true, "prefill_swiglu_bf16_256x128_w2x4_wd"),
+    FN_PREFILL_WD(4, false, false, false, "prefill_bf16_256x256_w2x4_wd"),
+    FN_PREFILL_WD(2, true, false, false, "prefill_swiglu_bf16_256x128_w2x4_wd"),
+    FN_PREFILL_WD(2, true, true, false, "prefill_swiglu_bf16_q8_256x128_w2x4_wd"),
     FN_PREFILL(4, 8, 4, 2, false, false, false, false, "prefill_bf16_256x256_w4x2_xl"),
     // narrow projections (one GPU's column share under tensor parallelism):
     // fewer than 128 tiles of 256 x 256 leave most CUs idle; 256 x 128 tiles
@@ -755,7 +759,7 @@ static const PrefillInstance& pick(bool sw, bool q8 = false, bool ex = false, bo
     if (d.sw == (sw || q8) && d.q8 == q8 && d.ex == ex && d.f8 == f8 && d.fm * d.wm == mf &&
         (nf == 0 || d.fn_ * d.wn == nf) && (wd_ok || !d.wd))
       return d;
-  return kPrefill[2];
+  return kPrefill[3];
 }
 
 // The instance a plan names (plans carry the table's own name pointers).
@@ -777,7 +781,7 @@ FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, b
   // 128 tiles
   const int64_t tiles = ceil_div(M, 256) * ceil_div(N, swiglu ? 128 : 256);
   const PrefillInstance& d = rows128 ? pick(swiglu, q8, ex, false, 8, 8)
-                                     : pick(swiglu, q8, ex, f8, narrow ? 8 : 0, 16, tiles >= 128 && K >= 2048);
+                                     : pick(swiglu, q8, ex, f8, narrow ? 8 : 0, 16, tiles >= 128 && K >= 4096);
   FusedPlan p{};
   p.kind = f8 ? 11 : (ex ? (q8 ? 10 : 8) : (q8 ? 5 : 1));
   p.mf = d.fm * d.wm;
@@ -847,7 +851,10 @@ hipError_t launch_prefill_premod(const FusedPlan& p, const void* u, const float*
   if (q != nullptr && wu == nullptr) return hipErrorInvalidValue;
   const bool f8 = sg != nullptr;
   if (f8 && wu != nullptr && su == nullptr) return hipErrorInvalidValue;
-  const PrefillInstance& d = pick(wu != nullptr, q != nullptr, true, f8, p.nf, p.mf);
+  const PrefillInstance* dp = by_name(p.name);
+  if (dp == nullptr || !dp->ex || dp->f8 != f8 || dp->sw != (wu != nullptr) || dp->q8 != (q != nullptr))
+    return hipErrorInvalidValue;
+  const PrefillInstance& d = *dp;
   PrefillArgs a{};
   a.sg = sg;
   a.su = su;

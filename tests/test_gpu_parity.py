@@ -392,10 +392,10 @@ def test_prefill_tile_order(gpu_lib, M, K, N, swiglu):
     assert_close(y, ref, "bf16", f"prefill tile order {M}x{K}x{N} swiglu={swiglu}")
 
 
-@pytest.mark.parametrize("M,K,N,swiglu", [(2000, 2056, 4100, False), (2000, 2056, 2100, True),
-                                          (1300, 2088, 5800, False), (1300, 2088, 3000, True)])
+@pytest.mark.parametrize("M,K,N,swiglu", [(2000, 4104, 4100, False), (2000, 4104, 2100, True),
+                                          (1300, 4104, 5800, False), (1300, 4104, 3000, True)])
 def test_prefill_w_direct_ragged(gpu_lib, M, K, N, swiglu):
-    """Grids of at least 128 tiles with K >= 2048 take the instances that load
+    """Grids of at least 128 tiles with K >= 4096 take the instances that load
     W' fragments straight into registers (rotated row-fragment order per
     wave): ragged
     rows, columns and k (a partial k-block, a k-block count that is not a
