@@ -696,19 +696,20 @@ struct PrefillInstance {
         false, true, F8, true, NAME                                                                          \
   }
 
-// W' fragments straight to registers, waves of 128 x 64 (bf16 weights, no
-// AdaLN): listed first, so the plain, SwiGLU and fp8-output SwiGLU calls on
-// 256-row tiles take them when the grid has at least 128 tiles and K is at
-// least 4096.  Measured against the LDS-ring instances below on the same
-// inputs (the same bits): 4096 x 4096 -> 12288 296-303 against 301-308 us,
-// 8192 x 4096 -> 4096 197-200 against 201-209 us, the gate/up pair 4096 x
-// 4096 -> 2 x 11008 546-564 against 547-569 us (fp8 output 647 against
-// 653 us); slower on shorter k loops and small grids, where each wave's own
-// W' loads are latency it cannot hide: 2000 x 1064 -> 4100 (136 tiles)
-// 34.4 against 33.2 us, 2000 x 2056 -> 2 x 2100 with fp8 output 67.3
-// against 65.4 us, 1000 x 4000 -> 1000 (16 tiles) 81 against 76 us.  On
-// the AdaLN operand (no Gram blocks) it lost at every size (QKV 309 against
-// 295 us), so those instances keep the ring.
+// W' fragments straight to registers, waves of 128 x 64: listed first, so
+// plain projections on 256-row tiles take it when the grid has at least 128
+// tiles and K is at least 4096.  Measured against the LDS-ring instance on
+// the same inputs (the same bits), hot (one weight copy, cache-resident)
+// and cold (copies rotated over 1.2 GiB): 4096 x 4096 -> 12288 hot 291-303
+// against 296-308 us, cold 304-309 against 302-309 us; 8192 x 4096 -> 4096
+// hot 196-200 against 201-209 us, cold 198-201 against 202 us.  Each wave's
+// own W' loads are issued three slots ahead where the ring runs four
+// k-blocks ahead, so HBM latency shows more: on shorter k loops and small
+// grids it lost (2000 x 1064 -> 4100, 136 tiles: 34.4 against 33.2 us;
+// 1000 x 4000 -> 1000: 81 against 76 us), on the SwiGLU pair 4096 x 4096 ->
+// 2 x 11008 it won hot (547-564 against 551-569 us) and lost cold (565-567
+// against 559-560 us), and on the AdaLN operand (no Gram blocks) it lost at
+// every size (QKV 309 against 295 us); those keep the ring.
 #define FN_PREFILL_WD(FN_, SW, Q8, EX, NAME)                                                                \
   PrefillInstance {                                                                                          \
     reinterpret_cast<const void*>(&prefill_kernel<8, FN_, 2, 4, SW, Q8, EX, false, false, true>), 8, FN_, 2, 4, 4, \
@@ -717,8 +718,6 @@ struct PrefillInstance {
 
 static const PrefillInstance kPrefill[] = {
     FN_PREFILL_WD(4, false, false, false, "prefill_bf16_256x256_w2x4_wd"),
-    FN_PREFILL_WD(2, true, false, false, "prefill_swiglu_bf16_256x128_w2x4_wd"),
-    FN_PREFILL_WD(2, true, true, false, "prefill_swiglu_bf16_q8_256x128_w2x4_wd"),
     FN_PREFILL(4, 8, 4, 2, false, false, false, false, "prefill_bf16_256x256_w4x2_xl"),
     // narrow projections (one GPU's column share under tensor parallelism):
     // fewer than 128 tiles of 256 x 256 leave most CUs idle; 256 x 128 tiles
@@ -759,7 +758,7 @@ static const PrefillInstance& pick(bool sw, bool q8 = false, bool ex = false, bo
     if (d.sw == (sw || q8) && d.q8 == q8 && d.ex == ex && d.f8 == f8 && d.fm * d.wm == mf &&
         (nf == 0 || d.fn_ * d.wn == nf) && (wd_ok || !d.wd))
       return d;
-  return kPrefill[3];
+  return kPrefill[1];
 }
 
 // The instance a plan names (plans carry the table's own name pointers).

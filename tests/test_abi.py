@@ -73,17 +73,17 @@ def test_rows_just_past_decode_on_wide_projections(lib):
 
 
 def test_prefill_w_direct_selection(lib):
-    # plain, SwiGLU and fp8-output SwiGLU projections over at least 128 tiles
-    # of 256 rows with K >= 4096 load their W' fragments straight into
-    # registers; shorter k loops, smaller grids and AdaLN keep the LDS ring
+    # plain projections over at least 128 tiles of 256 rows with K >= 4096
+    # load their W' fragments straight into registers; shorter k loops,
+    # smaller grids, SwiGLU pairs and AdaLN keep the LDS ring
     assert lib.fn_kernel_name(4096, 4096, 12288, 0, BF16).decode() == "prefill_bf16_256x256_w2x4_wd"
-    assert lib.fn_kernel_name(4096, 4096, 11008, 1, BF16).decode() == "prefill_swiglu_bf16_256x128_w2x4_wd"
+    assert lib.fn_kernel_name(4096, 4096, 11008, 1, BF16).decode() == "prefill_swiglu_bf16_256x128_w4x2_xl"
     assert lib.fn_kernel_name(8192, 4096, 4096, 0, BF16).decode() == "prefill_bf16_256x256_w2x4_wd"
     assert lib.fn_kernel_name(2000, 1064, 4100, 0, BF16).decode() == "prefill_bf16_256x256_w4x2_xl"
     assert lib.fn_kernel_name(2000, 1064, 2100, 1, BF16).decode() == "prefill_swiglu_bf16_256x128_w4x2_xl"
     assert lib.fn_kernel_name(1000, 4000, 1000, 1, BF16).decode() == "prefill_swiglu_bf16_256x128_w4x2_xl"
     assert lib.fn_kernel_name(1000, 4000, 3000, 0, BF16).decode() == "prefill_bf16_256x128_w4x2_xl"
-    assert lib.fn_kernel_name_q8(4096, 4096, 11008, 0).decode() == "prefill_swiglu_bf16_q8_256x128_w2x4_wd"
+    assert lib.fn_kernel_name_q8(4096, 4096, 11008, 0).decode() == "prefill_swiglu_bf16_q8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_q8(2000, 2056, 2100, 0).decode() == "prefill_swiglu_bf16_q8_256x128_w4x2_xl"
     assert lib.fn_kernel_name(2000, 2056, 4100, 0, BF16).decode() == "prefill_bf16_256x256_w4x2_xl"
     assert lib.fn_kernel_name_adaln_ws(4096, 4096, 12288, 4, 0).decode() == "prefill_premod_bf16_256x256_w4x2_xl"
@@ -503,7 +503,7 @@ def test_q8_kernel_names(lib):
     assert lib.fn_kernel_name_q8(65, 4096, 11008, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
     assert lib.fn_kernel_name_q8(128, 4096, 8192, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
     assert lib.fn_kernel_name_q8(129, 4096, 11008, 0).decode() == "prefill_swiglu_bf16_q8_128x128_w4x2"
-    assert lib.fn_kernel_name_q8(257, 4096, 11008, 0).decode() == "prefill_swiglu_bf16_q8_256x128_w2x4_wd"
+    assert lib.fn_kernel_name_q8(257, 4096, 11008, 0).decode() == "prefill_swiglu_bf16_q8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_q8(256, 4096, 8176, 0).decode().startswith("decode_swiglu_bf16_q8_m64")
     assert lib.fn_kernel_name_q8(257, 4096, 8176, 0).decode().startswith("prefill_swiglu_bf16_q8")
     assert lib.fn_kernel_name_q8(512, 4096, 2752, 0).decode().startswith("decode_swiglu_bf16_q8_m64")

@@ -392,12 +392,12 @@ def test_prefill_tile_order(gpu_lib, M, K, N, swiglu):
     assert_close(y, ref, "bf16", f"prefill tile order {M}x{K}x{N} swiglu={swiglu}")
 
 
-@pytest.mark.parametrize("M,K,N,swiglu", [(2000, 4104, 4100, False), (2000, 4104, 2100, True),
-                                          (1300, 4104, 5800, False), (1300, 4104, 3000, True)])
+@pytest.mark.parametrize("M,K,N,swiglu", [(2000, 4104, 4100, False), (2048, 4104, 4096, False),
+                                          (1300, 4104, 5800, False), (1536, 4104, 8200, False)])
 def test_prefill_w_direct_ragged(gpu_lib, M, K, N, swiglu):
-    """Grids of at least 128 tiles with K >= 4096 take the instances that load
-    W' fragments straight into registers (rotated row-fragment order per
-    wave): ragged
+    """Plain projections over at least 128 tiles with K >= 4096 take the
+    instance that loads W' fragments straight into registers (rotated
+    row-fragment order per wave): ragged
     rows, columns and k (a partial k-block, a k-block count that is not a
     multiple of the unroll), tile counts with and without the XCD-grouped
     order; every output against the oracle on the folded weights."""
