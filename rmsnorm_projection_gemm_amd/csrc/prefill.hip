@@ -697,16 +697,17 @@ struct PrefillInstance {
   }
 
 // W' fragments straight to registers, waves of 128 x 64: listed first, so
-// plain projections on 256-row tiles take it when the grid has at least 128
-// tiles and K is at least 4096.  Measured against the LDS-ring instance on
+// plain projections on 256-row tiles take it when the grid has at least 256
+// tiles (one per CU or more) and K is at least 4096.  Measured against the LDS-ring instance on
 // the same inputs (the same bits), hot (one weight copy, cache-resident)
 // and cold (copies rotated over 1.2 GiB): 4096 x 4096 -> 12288 hot 291-303
 // against 296-308 us, cold 304-309 against 302-309 us; 8192 x 4096 -> 4096
 // hot 196-200 against 201-209 us, cold 198-201 against 202 us.  Each wave's
 // own W' loads are issued three slots ahead where the ring runs four
-// k-blocks ahead, so HBM latency shows more: on shorter k loops and small
-// grids it lost (2000 x 1064 -> 4100, 136 tiles: 34.4 against 33.2 us;
-// 1000 x 4000 -> 1000: 81 against 76 us), on the SwiGLU pair 4096 x 4096 ->
+// k-blocks ahead, so HBM latency shows more: on shorter k loops and grids
+// that leave CUs with a single tile it lost (2000 x 4104 -> 4100, 136
+// tiles: cold 104 against 91 us, hot 90 against 83 us; 2000 x 1064 ->
+// 4100: 34.4 against 33.2 us; 1000 x 4000 -> 1000: 81 against 76 us), on the SwiGLU pair 4096 x 4096 ->
 // 2 x 11008 it won hot (547-564 against 551-569 us) and lost cold (565-567
 // against 559-560 us), and on the AdaLN operand (no Gram blocks) it lost at
 // every size (QKV 309 against 295 us); those keep the ring.
@@ -776,11 +777,11 @@ FusedPlan plan_prefill(DType dt, int64_t M, int64_t K, int64_t N, bool swiglu, b
   // already hold 128 output rows)
   const bool split = ex && swiglu && !q8;
   const bool rows128 = !f8 && !split && M <= 256 && ceil_div(N, 16) >= 512;
-  // W' straight to registers pays on long k loops over grids of at least
-  // 128 tiles
+  // W' straight to registers pays on long k loops over grids that fill the
+  // chip at least once
   const int64_t tiles = ceil_div(M, 256) * ceil_div(N, swiglu ? 128 : 256);
   const PrefillInstance& d = rows128 ? pick(swiglu, q8, ex, false, 8, 8)
-                                     : pick(swiglu, q8, ex, f8, narrow ? 8 : 0, 16, tiles >= 128 && K >= 4096);
+                                     : pick(swiglu, q8, ex, f8, narrow ? 8 : 0, 16, tiles >= 256 && K >= 4096);
   FusedPlan p{};
   p.kind = f8 ? 11 : (ex ? (q8 ? 10 : 8) : (q8 ? 5 : 1));
   p.mf = d.fm * d.wm;

@@ -73,7 +73,7 @@ def test_rows_just_past_decode_on_wide_projections(lib):
 
 
 def test_prefill_w_direct_selection(lib):
-    # plain projections over at least 128 tiles of 256 rows with K >= 4096
+    # plain projections over at least 256 tiles of 256 rows with K >= 4096
     # load their W' fragments straight into registers; shorter k loops,
     # smaller grids, SwiGLU pairs and AdaLN keep the LDS ring
     assert lib.fn_kernel_name(4096, 4096, 12288, 0, BF16).decode() == "prefill_bf16_256x256_w2x4_wd"
@@ -86,6 +86,8 @@ def test_prefill_w_direct_selection(lib):
     assert lib.fn_kernel_name_q8(4096, 4096, 11008, 0).decode() == "prefill_swiglu_bf16_q8_256x128_w4x2_xl"
     assert lib.fn_kernel_name_q8(2000, 2056, 2100, 0).decode() == "prefill_swiglu_bf16_q8_256x128_w4x2_xl"
     assert lib.fn_kernel_name(2000, 2056, 4100, 0, BF16).decode() == "prefill_bf16_256x256_w4x2_xl"
+    assert lib.fn_kernel_name(2000, 4104, 4100, 0, BF16).decode() == "prefill_bf16_256x256_w4x2_xl"
+    assert lib.fn_kernel_name(4000, 4104, 4100, 0, BF16).decode() == "prefill_bf16_256x256_w2x4_wd"
     assert lib.fn_kernel_name_adaln_ws(4096, 4096, 12288, 4, 0).decode() == "prefill_premod_bf16_256x256_w4x2_xl"
     assert lib.fn_kernel_name(96, 4096, 8192, 0, F32).decode().startswith("decode_f32")
 

@@ -392,10 +392,10 @@ def test_prefill_tile_order(gpu_lib, M, K, N, swiglu):
     assert_close(y, ref, "bf16", f"prefill tile order {M}x{K}x{N} swiglu={swiglu}")
 
 
-@pytest.mark.parametrize("M,K,N,swiglu", [(2000, 4104, 4100, False), (2048, 4104, 4096, False),
-                                          (1300, 4104, 5800, False), (1536, 4104, 8200, False)])
+@pytest.mark.parametrize("M,K,N,swiglu", [(4000, 4104, 4100, False), (4100, 4104, 4200, False),
+                                          (2560, 4104, 6600, False)])
 def test_prefill_w_direct_ragged(gpu_lib, M, K, N, swiglu):
-    """Plain projections over at least 128 tiles with K >= 4096 take the
+    """Plain projections over at least 256 tiles with K >= 4096 take the
     instance that loads W' fragments straight into registers (rotated
     row-fragment order per wave): ragged
     rows, columns and k (a partial k-block, a k-block count that is not a
